@@ -1,0 +1,312 @@
+"""Plain CPU oracle of one xHC sublayer update (forward and backward).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+calls it and shares no code with it; it imports nothing but numpy.
+
+Everything is computed in float64 from the given inputs (bf16 inputs arrive
+already rounded, as float32, and are upcast exactly).  Nothing is blocked,
+fused or reordered beyond what the definition states: tokens are processed as
+one batch with numpy array operations, one step of the method at a time.
+
+Sources (three web pages on xHC, Expanded Hyper-Connections):
+
+  [R]  "xHC: Expanded Hyper-Connections" research retrospective
+       (qingkeai.online/archives/xHC, mirror of the first author's Zhihu post).
+       Sections used, by heading:
+         R-mHC   "把 N 调大以后，事情开始不太对了"   (the multi-stream state
+                  X in R^{N x C}; H_pre reads, H_post writes, H_res mixes;
+                  Sinkhorn makes H_res doubly stochastic)
+         R-one   "更多 streams，为什么仍然只写入一份信息？" (write-back as
+                  H_post times out^T; coefficients are dynamic, per stream)
+         R-TFA   "最便宜的新信息，可能就在相邻 token 里" (causal depthwise
+                  convolutions with kernel sizes 4, 8, 12 over the sublayer
+                  output, stacked with it into 4 components; zero init)
+         R-GS    "Conv 带来了新信息，也带来了新的麻烦" (the four components
+                  u_0..u_3; optional Gram-Schmidt, dropped under Muon)
+         R-cost  "N 从 4 扩展到 16，成本为什么涨得这么快？" (coefficients are
+                  generated from the flattened N*C state)
+         R-DRSW  "模型可以拥有 16 条 streams，但每层只更新 4 条" (dense read
+                  over all N streams, sparse write to k active streams, the
+                  xHC write formula, inactive streams unchanged)
+  [E]  explainer "xHC：把残差流扩到 N=16 的可扩展超连接"
+       (papers.ananclaw.com), section "核心方法" (wide state, narrow write;
+       k=4 of N=16 updated, the other 12 pass through).
+
+Readings where the pages are silent or their formulas were lost (each one is
+shared with the GPU library and listed in the design notes):
+
+  O1  coefficients: z = rms(xbar) ^-1 * xbar @ W + b, with xbar the token's
+      flattened state, xbar[i*C + c] = X[t, i, c], and
+      rms(xbar) = sqrt(mean(xbar^2) + eps).  All P = N + k*ncomp + k*k logits
+      come from the full N*C state.  Column layout of z:
+      [ pre (N) | post (k*ncomp, a-major) | res (k*k, a-major) ].
+  O2  gates: H_pre = sigmoid(z_pre), H_post = sigmoid(z_post); in "unit" gate
+      mode both are identically 1 (a test mode, used for the N=1 reduction).
+  O3  H_res = Sinkhorn(L) with L the k x k res logits: M = exp(L - rowmax(L)),
+      then `iters` times: divide each row by its sum, then each column by its
+      sum.  No epsilon in the denominators.
+  O4  TFA: U_0 = out; U_m[s, c] = sum_q w_m[c, q] * out[s - (K_m - 1) + q, c]
+      for K = 4, 8, 12, positions before the start of the sequence read 0 (no
+      leak between sequences of a batch); w_m[c, K_m - 1] multiplies the
+      current token.  No Gram-Schmidt.
+  O5  write: for active stream a (index i_a = active[a]):
+        X'[t, i_a] = sum_b H_res[a, b] X[t, i_b] + sum_c H_post[a, c] U_c[t];
+      every other stream is copied unchanged.  Dense read:
+        h_in[t] = sum_i H_pre[i] X[t, i].
+"""
+
+import numpy as np
+
+TFA_KERNEL_SIZES = (4, 8, 12)
+
+
+def n_logits(N, k, ncomp):
+    """P = N pre logits + k*ncomp post logits + k*k res logits (O1)."""
+    return N + k * ncomp + k * k
+
+
+# --------------------------------------------------------------------------
+# forward pieces
+# --------------------------------------------------------------------------
+
+def rms_projection(Xf, W, bias, eps):
+    """O1 / [R-cost], [R-DRSW]: logits from the RMS-normed flattened state.
+
+    Xf: [T, N*C] float64.  Returns z [T, P], r [T], xhat [T, N*C].
+    """
+    r = np.sqrt(np.mean(Xf * Xf, axis=1) + eps)
+    xhat = Xf / r[:, None]
+    z = xhat @ W + bias[None, :]
+    return z, r, xhat
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def split_logits(z, N, k, ncomp):
+    """Column layout of O1: pre | post (a-major) | res (a-major)."""
+    T = z.shape[0]
+    z_pre = z[:, :N]
+    z_post = z[:, N:N + k * ncomp].reshape(T, k, ncomp)
+    L = z[:, N + k * ncomp:N + k * ncomp + k * k].reshape(T, k, k)
+    return z_pre, z_post, L
+
+
+def sinkhorn(L, iters):
+    """O3 / [R-mHC]: Sinkhorn normalisation of exp(L), per token.
+
+    L: [T, k, k].  Returns H_res [T, k, k] and the list of iterates
+    (the matrix after every row step and every column step), which the
+    backward pass walks in reverse.
+    """
+    if iters < 1:
+        raise ValueError("sinkhorn needs at least one iteration")
+    M = np.exp(L - L.max(axis=2, keepdims=True))
+    states = [M]
+    for _ in range(iters):
+        M = M / M.sum(axis=2, keepdims=True)      # every row sums to 1
+        states.append(M)
+        M = M / M.sum(axis=1, keepdims=True)      # every column sums to 1
+        states.append(M)
+    return M, states
+
+
+def causal_depthwise_conv(out_bsc, w):
+    """O4 / [R-TFA]: one causal depthwise convolution along the sequence.
+
+    out_bsc: [B, S, C]; w: [C, K].  y[b, s, c] = sum_q w[c, q] *
+    out[b, s - (K-1) + q, c], reading zero before position 0.
+    """
+    B, S, C = out_bsc.shape
+    K = w.shape[1]
+    y = np.zeros_like(out_bsc)
+    for q in range(K):
+        shift = K - 1 - q                 # how many positions back tap q looks
+        if shift >= S:
+            continue
+        y[:, shift:, :] += w[None, None, :, q] * out_bsc[:, :S - shift, :]
+    return y
+
+
+def tfa_components(out, B, S, conv_ws):
+    """[R-TFA]: U = [out, conv4(out), conv8(out), conv12(out)] -> [T, ncomp, C].
+
+    conv_ws is () for the single-component (mHC-style) write-back.
+    """
+    T, C = out.shape
+    out_bsc = out.reshape(B, S, C)
+    comps = [out]
+    for w in conv_ws:
+        comps.append(causal_depthwise_conv(out_bsc, w).reshape(T, C))
+    return np.stack(comps, axis=1)
+
+
+def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
+            gate_mode="sigmoid"):
+    """One xHC sublayer update, forward ([R-DRSW] write formula, O1-O5).
+
+    X:      [B*S, N, C]  residual state before the update
+    out:    [B*S, C]     sublayer output
+    W:      [N*C, P]     projection weights, rows indexed i*C + c
+    bias:   [P] or None
+    active: k distinct stream ids; row/column a of H_res and row a of H_post
+            bind to active[a]
+    conv_ws: (w4, w8, w12) with shapes [C,4], [C,8], [C,12], or () for one
+            write-back component
+
+    Returns a dict with X_new, h_in and the intermediates (z, r, H_pre,
+    H_post, H_res, U).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    conv_ws = tuple(np.asarray(w, dtype=np.float64) for w in conv_ws)
+    T, N, C = X.shape
+    k = len(active)
+    ncomp = 1 + len(conv_ws)
+    P = n_logits(N, k, ncomp)
+    assert T == B * S and out.shape == (T, C) and W.shape == (N * C, P)
+    assert len(set(int(a) for a in active)) == k and all(0 <= a < N for a in active)
+    bias = np.zeros(P) if bias is None else np.asarray(bias, dtype=np.float64)
+
+    # coefficients from the full flattened state (dense read of all streams)
+    z, r, _ = rms_projection(X.reshape(T, N * C), W, bias, eps)
+    z_pre, z_post, L = split_logits(z, N, k, ncomp)
+    if gate_mode == "sigmoid":
+        H_pre, H_post = sigmoid(z_pre), sigmoid(z_post)
+    elif gate_mode == "unit":
+        H_pre, H_post = np.ones_like(z_pre), np.ones_like(z_post)
+    else:
+        raise ValueError(gate_mode)
+    H_res, _ = sinkhorn(L, iters)
+
+    # dense read: the sublayer input aggregates all N streams
+    h_in = np.einsum("ti,tic->tc", H_pre, X)
+
+    # temporal feature augmentation over the sublayer output
+    U = tfa_components(out, B, S, conv_ws)
+
+    # sparse write: only the k active streams are rewritten
+    X_new = X.copy()
+    Xa = X[:, list(active), :]                                    # [T, k, C]
+    X_new[:, list(active), :] = (np.einsum("tab,tbc->tac", H_res, Xa)
+                                 + np.einsum("tam,tmc->tac", H_post, U))
+    return dict(X_new=X_new, h_in=h_in, z=z, r=r, H_pre=H_pre,
+                H_post=H_post, H_res=H_res, U=U)
+
+
+# --------------------------------------------------------------------------
+# backward pieces (derived by hand from the forward above)
+# --------------------------------------------------------------------------
+
+def sinkhorn_backward(L, iters, dH):
+    """Gradient of O3 through the unrolled iterations.
+
+    A row step R = M / rowsum(M) has dM = (dR - rowsum(dR * R)) / rowsum(M);
+    a column step is the same along columns.  The row-max shift cancels in
+    the first row step, so it carries no gradient; dL = dM0 * M0.
+    """
+    _, states = sinkhorn(L, iters)
+    g = dH
+    for it in range(iters, 0, -1):
+        R = states[2 * it - 1]                      # after the row step
+        Mc = states[2 * it]                         # after the column step
+        colsum = R.sum(axis=1, keepdims=True)
+        g = (g - (g * Mc).sum(axis=1, keepdims=True)) / colsum
+        M = states[2 * it - 2]
+        rowsum = M.sum(axis=2, keepdims=True)
+        g = (g - (g * R).sum(axis=2, keepdims=True)) / rowsum
+    return g * states[0]
+
+
+def causal_depthwise_conv_backward(out_bsc, w, dy):
+    """Adjoint of causal_depthwise_conv: returns (d_out, d_w)."""
+    B, S, C = out_bsc.shape
+    K = w.shape[1]
+    d_out = np.zeros_like(out_bsc)
+    d_w = np.zeros_like(w)
+    for q in range(K):
+        shift = K - 1 - q
+        if shift >= S:
+            continue
+        # y[:, s] += w[q] * out[:, s - shift]   for s >= shift
+        d_out[:, :S - shift, :] += w[None, None, :, q] * dy[:, shift:, :]
+        d_w[:, q] += np.einsum("bsc,bsc->c", dy[:, shift:, :], out_bsc[:, :S - shift, :])
+    return d_out, d_w
+
+
+def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
+             iters=20, eps=1e-6, gate_mode="sigmoid"):
+    """Gradients of the forward above for upstream gradients dX_new, dh_in.
+
+    Returns dict(dX [T,N,C], dout [T,C], dW [N*C,P], db [P],
+    dconv [list of [C,K]], dz [T,P]).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    conv_ws = tuple(np.asarray(w, dtype=np.float64) for w in conv_ws)
+    dX_new = np.asarray(dX_new, dtype=np.float64)
+    dh_in = np.asarray(dh_in, dtype=np.float64)
+    T, N, C = X.shape
+    k = len(active)
+    ncomp = 1 + len(conv_ws)
+    P = n_logits(N, k, ncomp)
+    act = list(active)
+    bias = np.zeros(P) if bias is None else np.asarray(bias, dtype=np.float64)
+
+    Xf = X.reshape(T, N * C)
+    z, r, xhat = rms_projection(Xf, W, bias, eps)
+    z_pre, z_post, L = split_logits(z, N, k, ncomp)
+    if gate_mode == "sigmoid":
+        H_pre, H_post = sigmoid(z_pre), sigmoid(z_post)
+    else:
+        H_pre, H_post = np.ones_like(z_pre), np.ones_like(z_post)
+    H_res, _ = sinkhorn(L, iters)
+    U = tfa_components(out, B, S, conv_ws)
+
+    G = dX_new[:, act, :]                                         # [T, k, C]
+    Xa = X[:, act, :]
+
+    # pass-through rows keep their upstream gradient; rewritten rows do not
+    dX = dX_new.copy()
+    dX[:, act, :] = 0.0
+    # through the mixing term and the write-back term
+    dH_res = np.einsum("tac,tbc->tab", G, Xa)
+    dX[:, act, :] += np.einsum("tab,tac->tbc", H_res, G)
+    dH_post = np.einsum("tac,tmc->tam", G, U)
+    dU = np.einsum("tam,tac->tmc", H_post, G)
+    # through the dense read
+    dH_pre = np.einsum("tc,tic->ti", dh_in, X)
+    dX += H_pre[:, :, None] * dh_in[:, None, :]
+
+    # through the gates and Sinkhorn to the logits
+    if gate_mode == "sigmoid":
+        dz_pre = dH_pre * H_pre * (1.0 - H_pre)
+        dz_post = dH_post * H_post * (1.0 - H_post)
+    else:
+        dz_pre = np.zeros_like(dH_pre)
+        dz_post = np.zeros_like(dH_post)
+    dL = sinkhorn_backward(L, iters, dH_res)
+    dz = np.concatenate([dz_pre, dz_post.reshape(T, k * ncomp),
+                         dL.reshape(T, k * k)], axis=1)
+
+    # through the RMS-normed projection
+    db = dz.sum(axis=0)
+    dW = xhat.T @ dz
+    dxhat = dz @ W.T
+    n = N * C
+    dXf = (dxhat - xhat * (np.sum(dxhat * xhat, axis=1, keepdims=True) / n)) / r[:, None]
+    dX += dXf.reshape(T, N, C)
+
+    # through temporal feature augmentation
+    dout = dU[:, 0, :].copy()
+    out_bsc = out.reshape(B, S, C)
+    dconv = []
+    for m, w in enumerate(conv_ws):
+        d_o, d_w = causal_depthwise_conv_backward(out_bsc, w, dU[:, m + 1, :].reshape(B, S, C))
+        dout += d_o.reshape(T, C)
+        dconv.append(d_w)
+    return dict(dX=dX, dout=dout, dW=dW, db=db, dconv=dconv, dz=dz)
