@@ -1,0 +1,325 @@
+// C-ABI entry points of libxhc: validation, workspace planning, dispatch,
+// per-kernel timer.  Validation and planning are plain host code.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "xhc_launch.h"
+#include "xhc_plan.h"
+
+namespace xhc {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int make_plan(const xhc_desc* d, Plan* p) {
+  if (!d || !p) return XHC_ERR_NULL;
+  if (d->B < 1 || d->S < 1 || d->C < 8 || (d->C % 8) != 0) return XHC_ERR_SHAPE;
+  if (d->k < 1 || d->k > 4 || d->N < d->k || d->N > 16) return XHC_ERR_SHAPE;
+  if (d->ncomp != 1 && d->ncomp != 4) return XHC_ERR_SHAPE;
+  if (d->sinkhorn_iters < 1 || d->sinkhorn_iters > 64) return XHC_ERR_SHAPE;
+  if (!(d->rms_eps >= 0.f) || !std::isfinite(d->rms_eps)) return XHC_ERR_SHAPE;
+  if (d->dtype != XHC_F32 && d->dtype != XHC_BF16) return XHC_ERR_UNSUPPORTED;
+  if (d->gate_mode != XHC_GATE_SIGMOID && d->gate_mode != XHC_GATE_UNIT) return XHC_ERR_UNSUPPORTED;
+  const int64_t T = (int64_t)d->B * d->S;
+  if (T * d->N * (int64_t)d->C >= ((int64_t)1 << 31)) return XHC_ERR_SHAPE;
+
+  Plan& q = *p;
+  q.B = d->B; q.S = d->S; q.C = d->C; q.N = d->N; q.k = d->k; q.nc = d->ncomp;
+  q.P = q.N + q.k * q.nc + q.k * q.k;
+  q.NT = (int)cdiv(q.P, 16);
+  q.T = (int)T;
+  q.iters = d->sinkhorn_iters; q.dtype = d->dtype; q.gate = d->gate_mode; q.eps = d->rms_eps;
+  q.NC = (int64_t)q.N * q.C;
+  q.esz = q.dtype == XHC_BF16 ? 2 : 4;
+
+  // forward
+  q.SK = q.N;
+  q.ZST = q.NT * 16 + 4;
+  q.proj_tiles = (int)cdiv(T, PROJ_TOK);
+  q.mix_cblocks = (int)cdiv(q.C, MIX_THREADS * MIX_CH);
+  q.mix_segs = (int)cdiv(q.S, MIX_LSEG);
+
+  // backward: B1 segments sized for ~2048 waves
+  q.b1_cblocks = (int)cdiv(q.C, B1_WAVES * B1_WAVE_CH);
+  {
+    const int64_t waves_per_row = (int64_t)q.b1_cblocks * B1_WAVES;
+    const int64_t want_rows = std::max<int64_t>(1, cdiv(2048, waves_per_row));
+    const int64_t segs = std::max<int64_t>(1, cdiv(want_rows, q.B));
+    int64_t lseg = cdiv(cdiv(q.S, segs), 12) * 12;
+    lseg = std::max<int64_t>(lseg, 12);
+    q.b1_lseg = (int)lseg;
+    q.b1_segs = (int)cdiv(q.S, lseg);
+  }
+  q.b2_rowgroups = 1 + (int)cdiv(q.N - q.k, 4);
+  q.b2_cblocks = (int)cdiv(q.C, B2_CB);
+  q.Tpad = cdiv(T, B2_TT) * B2_TT;
+  {
+    const int64_t base = (int64_t)q.b2_rowgroups * q.b2_cblocks;
+    const int64_t tiles = q.Tpad / B2_TT;
+    int64_t ts = std::min<int64_t>(std::max<int64_t>(1, cdiv(512, base)), tiles);
+    const int64_t tiles_per = cdiv(tiles, ts);
+    q.b2_tok_per_split = (int)(tiles_per * B2_TT);
+    q.b2_ts = (int)cdiv(T, q.b2_tok_per_split);
+  }
+
+  // workspace layouts
+  size_t o = 0;
+  q.off_wt = o;     o = align256(o + (size_t)q.NT * 16 * q.NC * q.esz);
+  q.off_zpart = o;  o = align256(o + (size_t)q.SK * T * q.ZST * 4);
+  q.off_coef = o;   o = align256(o + (size_t)T * COEF_STRIDE * 4);
+  q.fwd_bytes = o;
+  // backward reuses the forward regions (projection recompute) and adds:
+  q.off_zbuf = o;   o = align256(o + (size_t)T * (q.P + 1) * 4);
+  q.off_wp = o;     o = align256(o + (size_t)q.NC * 64 * q.esz);
+  q.off_dpart = o;  o = align256(o + (size_t)q.b1_cblocks * T * DOT_STRIDE * 4);
+  q.off_dwpart = o; o = align256(o + (q.nc == 4 ? (size_t)q.B * q.b1_segs * q.C * 24 * 4 : 0));
+  q.off_dz = o;     o = align256(o + (size_t)T * 48 * 4);
+  q.off_dzr = o;    o = align256(o + (size_t)T * 64 * q.esz);
+  q.off_dzrt = o;   o = align256(o + (size_t)(q.dtype == XHC_BF16 ? 96 : 48) * q.Tpad * q.esz);
+  q.off_dwpart2 = o; o = align256(o + (size_t)q.b2_ts * q.NC * 48 * 4);
+  q.bwd_bytes = o;
+  return XHC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// validation helpers
+// ---------------------------------------------------------------------------
+struct Span { const char* lo; size_t n; };
+static Span span(const void* p, size_t n) { return Span{static_cast<const char*>(p), n}; }
+static bool overlap(Span a, Span b) {
+  if (!a.lo || !b.lo || !a.n || !b.n) return false;
+  return a.lo < b.lo + b.n && b.lo < a.lo + a.n;
+}
+static bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
+static int check_active(const Plan& p, const int32_t* act) {
+  if (!act) return XHC_ERR_NULL;
+  for (int a = 0; a < p.k; ++a) {
+    if (act[a] < 0 || act[a] >= p.N) return XHC_ERR_INDEX;
+    for (int b = 0; b < a; ++b)
+      if (act[a] == act[b]) return XHC_ERR_INDEX;
+  }
+  return XHC_OK;
+}
+
+// Outputs may not overlap each other nor any input, except the listed
+// permitted identity (same base, same size).
+static bool any_overlap(const std::vector<Span>& outs, const std::vector<Span>& ins, Span same_a, Span same_b) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlap(outs[i], outs[j])) return true;
+    for (const Span& in : ins) {
+      if (outs[i].lo == same_a.lo && in.lo == same_b.lo && same_a.lo == same_b.lo && same_a.n == same_b.n &&
+          outs[i].lo != nullptr)
+        continue;
+      if (overlap(outs[i], in)) return true;
+    }
+  }
+  return false;
+}
+
+static int validate_fwd(const Plan& p, const xhc_fwd_args* a) {
+  if (!a) return XHC_ERR_NULL;
+  if (!a->X || !a->out || !a->W || !a->X_new || !a->h_in) return XHC_ERR_NULL;
+  const bool has_conv = a->w4 || a->w8 || a->w12;
+  if (p.nc == 4 && (!a->w4 || !a->w8 || !a->w12)) return XHC_ERR_NULL;
+  if (p.nc == 1 && has_conv) return XHC_ERR_UNSUPPORTED;
+  int rc = check_active(p, a->active);
+  if (rc) return rc;
+  const void* ptrs[] = {a->X, a->out, a->w4, a->w8, a->w12, a->W, a->bias, a->X_new, a->h_in, a->z_save, a->xact_save};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return XHC_ERR_ALIGN;
+  const size_t T = p.T, e = p.esz;
+  const Span X = span(a->X, T * p.NC * e), Xn = span(a->X_new, T * p.NC * e);
+  const Span out = span(a->out, T * p.C * e), hin = span(a->h_in, T * p.C * e);
+  const Span W = span(a->W, (size_t)p.NC * p.P * e), bias = span(a->bias, a->bias ? (size_t)p.P * 4 : 0);
+  const Span w4 = span(a->w4, a->w4 ? (size_t)p.C * 16 : 0), w8 = span(a->w8, a->w8 ? (size_t)p.C * 32 : 0),
+             w12 = span(a->w12, a->w12 ? (size_t)p.C * 48 : 0);
+  const Span zs = span(a->z_save, a->z_save ? T * (p.P + 1) * 4 : 0);
+  const Span xs = span(a->xact_save, a->xact_save ? T * p.k * p.C * e : 0);
+  if (a->X_new != a->X && overlap(X, Xn)) return XHC_ERR_ALIAS;
+  std::vector<Span> outs = {Xn, hin, zs, xs};
+  std::vector<Span> ins = {X, out, W, bias, w4, w8, w12};
+  if (any_overlap(outs, ins, Xn, X)) return XHC_ERR_ALIAS;
+  return XHC_OK;
+}
+
+static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
+  if (!a) return XHC_ERR_NULL;
+  if (!a->X || !a->out || !a->W || !a->dX_new || !a->dh_in || !a->dX || !a->dout || !a->dW) return XHC_ERR_NULL;
+  if (p.nc == 4 && (!a->w4 || !a->w8 || !a->w12 || !a->dw4 || !a->dw8 || !a->dw12)) return XHC_ERR_NULL;
+  if (p.nc == 1 && (a->w4 || a->w8 || a->w12 || a->dw4 || a->dw8 || a->dw12)) return XHC_ERR_UNSUPPORTED;
+  if (a->accumulate != 0 && a->accumulate != 1) return XHC_ERR_UNSUPPORTED;
+  int rc = check_active(p, a->active);
+  if (rc) return rc;
+  const void* ptrs[] = {a->X, a->xact, a->out, a->w4, a->w8, a->w12, a->W, a->bias, a->z_save, a->dX_new,
+                        a->dh_in, a->dX, a->dout, a->dW, a->db, a->dw4, a->dw8, a->dw12};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return XHC_ERR_ALIGN;
+  const size_t T = p.T, e = p.esz;
+  const Span X = span(a->X, T * p.NC * e), xact = span(a->xact, a->xact ? T * p.k * p.C * e : 0);
+  const Span out = span(a->out, T * p.C * e), W = span(a->W, (size_t)p.NC * p.P * e);
+  const Span bias = span(a->bias, a->bias ? (size_t)p.P * 4 : 0);
+  const Span w4 = span(a->w4, a->w4 ? (size_t)p.C * 16 : 0), w8 = span(a->w8, a->w8 ? (size_t)p.C * 32 : 0),
+             w12 = span(a->w12, a->w12 ? (size_t)p.C * 48 : 0);
+  const Span zs = span(a->z_save, a->z_save ? T * (p.P + 1) * 4 : 0);
+  const Span dXn = span(a->dX_new, T * p.NC * e), dhin = span(a->dh_in, T * p.C * e);
+  const Span dX = span(a->dX, T * p.NC * e), dout = span(a->dout, T * p.C * e);
+  const Span dW = span(a->dW, (size_t)p.NC * p.P * 4), db = span(a->db, a->db ? (size_t)p.P * 4 : 0);
+  const Span dw4 = span(a->dw4, a->dw4 ? (size_t)p.C * 16 : 0), dw8 = span(a->dw8, a->dw8 ? (size_t)p.C * 32 : 0),
+             dw12 = span(a->dw12, a->dw12 ? (size_t)p.C * 48 : 0);
+  if (a->dX != a->dX_new && overlap(dX, dXn)) return XHC_ERR_ALIAS;
+  std::vector<Span> outs = {dX, dout, dW, db, dw4, dw8, dw12};
+  std::vector<Span> ins = {X, xact, out, W, bias, w4, w8, w12, zs, dXn, dhin};
+  if (any_overlap(outs, ins, dX, dXn)) return XHC_ERR_ALIAS;
+  return XHC_OK;
+}
+
+}  // namespace xhc
+
+// ---------------------------------------------------------------------------
+// timer
+// ---------------------------------------------------------------------------
+struct xhc_timer {
+  struct Rec { int kid; hipEvent_t start, stop; };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  hipEvent_t get() {
+    if (used == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+
+static const char* const kKernelNames[xhc::KID_COUNT] = {
+    "pack_wt", "proj", "coef", "mix", "pack_wp", "bdots", "bcoef", "bgrad", "breduce"};
+
+namespace xhc {
+void timer_mark(xhc_timer* tm, int kid, hipStream_t st, bool start) {
+  hipEvent_t e = tm->get();
+  if (!e) return;
+  hipEventRecord(e, st);
+  if (start) {
+    tm->recs.push_back({kid, e, nullptr});
+  } else {
+    for (size_t i = tm->recs.size(); i-- > 0;)
+      if (tm->recs[i].kid == kid && tm->recs[i].stop == nullptr) { tm->recs[i].stop = e; break; }
+  }
+}
+}  // namespace xhc
+
+extern "C" {
+
+size_t xhc_workspace_size(const xhc_desc* desc, int phase) {
+  xhc::Plan p;
+  if (xhc::make_plan(desc, &p) != XHC_OK) return 0;
+  if (phase == XHC_PHASE_FWD) return p.fwd_bytes;
+  if (phase == XHC_PHASE_BWD) return p.bwd_bytes;
+  return 0;
+}
+
+int xhc_validate(const xhc_desc* desc, const void* args, int phase) {
+  xhc::Plan p;
+  int rc = xhc::make_plan(desc, &p);
+  if (rc) return rc;
+  if (phase == XHC_PHASE_FWD) return xhc::validate_fwd(p, static_cast<const xhc_fwd_args*>(args));
+  if (phase == XHC_PHASE_BWD) return xhc::validate_bwd(p, static_cast<const xhc_bwd_args*>(args));
+  return XHC_ERR_UNSUPPORTED;
+}
+
+static int check_ws(const xhc::Plan& p, void* ws, size_t bytes, size_t need) {
+  (void)p;
+  if (!ws) return XHC_ERR_WORKSPACE;
+  if (bytes < need) return XHC_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return XHC_ERR_ALIGN;
+  return XHC_OK;
+}
+
+int xhc_forward(const xhc_desc* desc, const xhc_fwd_args* args, void* workspace, size_t workspace_bytes,
+                xhc_stream_t stream) {
+  xhc::Plan p;
+  int rc = xhc::make_plan(desc, &p);
+  if (rc) return rc;
+  rc = xhc::validate_fwd(p, args);
+  if (rc) return rc;
+  rc = check_ws(p, workspace, workspace_bytes, p.fwd_bytes);
+  if (rc) return rc;
+  return xhc::launch_forward(p, args, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+int xhc_backward(const xhc_desc* desc, const xhc_bwd_args* args, void* workspace, size_t workspace_bytes,
+                 xhc_stream_t stream) {
+  xhc::Plan p;
+  int rc = xhc::make_plan(desc, &p);
+  if (rc) return rc;
+  rc = xhc::validate_bwd(p, args);
+  if (rc) return rc;
+  rc = check_ws(p, workspace, workspace_bytes, p.bwd_bytes);
+  if (rc) return rc;
+  return xhc::launch_backward(p, args, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+const char* xhc_strerror(int code) {
+  switch (code) {
+    case XHC_OK: return "ok";
+    case XHC_ERR_NULL: return "a required pointer is NULL";
+    case XHC_ERR_SHAPE: return "sizes out of the supported range";
+    case XHC_ERR_INDEX: return "active stream index out of range or repeated";
+    case XHC_ERR_ALIAS: return "forbidden overlap between buffers";
+    case XHC_ERR_ALIGN: return "pointer not aligned (16 bytes; workspace 256 bytes)";
+    case XHC_ERR_UNSUPPORTED: return "mode not supported";
+    case XHC_ERR_WORKSPACE: return "workspace missing or too small";
+    case XHC_ERR_HIP: return "HIP call or kernel launch failed";
+    default: return "unknown xhc error";
+  }
+}
+
+xhc_timer* xhc_timer_create(void) { return new xhc_timer(); }
+
+void xhc_timer_destroy(xhc_timer* t) {
+  if (!t) return;
+  for (hipEvent_t e : t->pool) hipEventDestroy(e);
+  delete t;
+}
+
+void xhc_timer_reset(xhc_timer* t) {
+  if (!t) return;
+  t->recs.clear();
+  t->used = 0;
+}
+
+int xhc_timer_read(xhc_timer* t, const char* kernel, double* total_ms, int64_t* launches) {
+  if (!t || !kernel || !total_ms || !launches) return XHC_ERR_NULL;
+  int kid = -1;
+  for (int i = 0; i < xhc::KID_COUNT; ++i)
+    if (std::strcmp(kernel, kKernelNames[i]) == 0) kid = i;
+  if (kid < 0) return XHC_ERR_UNSUPPORTED;
+  double ms = 0.0;
+  int64_t n = 0;
+  for (const auto& r : t->recs) {
+    if (r.kid != kid || !r.stop) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return XHC_ERR_HIP;
+    float f = 0.f;
+    if (hipEventElapsedTime(&f, r.start, r.stop) != hipSuccess) return XHC_ERR_HIP;
+    ms += f;
+    ++n;
+  }
+  *total_ms = ms;
+  *launches = n;
+  return XHC_OK;
+}
+
+int xhc_kernel_count(void) { return xhc::KID_COUNT; }
+
+const char* xhc_kernel_name(int i) { return (i >= 0 && i < xhc::KID_COUNT) ? kKernelNames[i] : nullptr; }
+
+}  // extern "C"

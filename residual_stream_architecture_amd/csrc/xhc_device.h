@@ -1,0 +1,169 @@
+// Device-side helpers shared by the xHC kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xhc {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Storage element types.
+struct BF16 { static constexpr int bytes = 2; };
+struct F32 { static constexpr int bytes = 4; };
+
+// ---------------------------------------------------------------------------
+// W consecutive elements held by one lane, loaded and stored with one vector
+// access per 16 bytes.  V8 is also one lane's share of an MFMA K=32 step.
+// ---------------------------------------------------------------------------
+template <int BYTES> struct RawT;
+template <> struct RawT<4> { typedef unsigned type; };
+template <> struct RawT<8> { typedef u32x2 type; };
+template <> struct RawT<16> { typedef u32x4 type; };
+
+template <typename E, int W> struct Vec;
+
+template <int W> struct Vec<BF16, W> {
+  static constexpr int NW = W / 2;          // 32-bit words
+  unsigned w[NW];                           // element 2j in the low half of w[j]
+  __device__ static Vec zero() {
+    Vec v;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) v.w[j] = 0u;
+    return v;
+  }
+  __device__ static Vec load(const void* base, size_t elem) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + elem;
+    Vec v;
+    if constexpr (W == 8) {
+      u32x4 r = *reinterpret_cast<const u32x4*>(p);
+      v.w[0] = r[0]; v.w[1] = r[1]; v.w[2] = r[2]; v.w[3] = r[3];
+    } else if constexpr (W == 4) {
+      u32x2 r = *reinterpret_cast<const u32x2*>(p);
+      v.w[0] = r[0]; v.w[1] = r[1];
+    } else {
+      v.w[0] = *reinterpret_cast<const unsigned*>(p);
+    }
+    return v;
+  }
+  __device__ void store(void* base, size_t elem) const {
+    uint16_t* p = reinterpret_cast<uint16_t*>(base) + elem;
+    if constexpr (W == 8) {
+      *reinterpret_cast<u32x4*>(p) = u32x4{w[0], w[1], w[2], w[3]};
+    } else if constexpr (W == 4) {
+      *reinterpret_cast<u32x2*>(p) = u32x2{w[0], w[1]};
+    } else {
+      *reinterpret_cast<unsigned*>(p) = w[0];
+    }
+  }
+  __device__ float f(int j) const {
+    unsigned x = w[j >> 1];
+    return __uint_as_float((j & 1) ? (x & 0xffff0000u) : (x << 16));
+  }
+  __device__ void to_float(float* o) const {
+#pragma unroll
+    for (int j = 0; j < W; ++j) o[j] = f(j);
+  }
+  __device__ static Vec from_float(const float* x) {
+    Vec v;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      bf16x2 p = {(__bf16)x[2 * j], (__bf16)x[2 * j + 1]};   // RNE (v_cvt_pk_bf16_f32)
+      v.w[j] = __builtin_bit_cast(unsigned, p);
+    }
+    return v;
+  }
+};
+
+template <int W> struct Vec<F32, W> {
+  float x[W];
+  __device__ static Vec zero() {
+    Vec v;
+#pragma unroll
+    for (int j = 0; j < W; ++j) v.x[j] = 0.f;
+    return v;
+  }
+  __device__ static Vec load(const void* base, size_t elem) {
+    const float* p = reinterpret_cast<const float*>(base) + elem;
+    Vec v;
+#pragma unroll
+    for (int q = 0; q < W; q += 4) {
+      if constexpr (W >= 4) {
+        f32x4 r = *reinterpret_cast<const f32x4*>(p + q);
+        v.x[q] = r[0]; v.x[q + 1] = r[1]; v.x[q + 2] = r[2]; v.x[q + 3] = r[3];
+      }
+    }
+    if constexpr (W == 2) {
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      f32x2 r = *reinterpret_cast<const f32x2*>(p);
+      v.x[0] = r[0]; v.x[1] = r[1];
+    }
+    return v;
+  }
+  __device__ void store(void* base, size_t elem) const {
+    float* p = reinterpret_cast<float*>(base) + elem;
+    if constexpr (W >= 4) {
+#pragma unroll
+      for (int q = 0; q < W; q += 4)
+        *reinterpret_cast<f32x4*>(p + q) = f32x4{x[q], x[q + 1], x[q + 2], x[q + 3]};
+    } else {
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<f32x2*>(p) = f32x2{x[0], x[1]};
+    }
+  }
+  __device__ float f(int j) const { return x[j]; }
+  __device__ void to_float(float* o) const {
+#pragma unroll
+    for (int j = 0; j < W; ++j) o[j] = x[j];
+  }
+  __device__ static Vec from_float(const float* y) {
+    Vec v;
+#pragma unroll
+    for (int j = 0; j < W; ++j) v.x[j] = y[j];
+    return v;
+  }
+};
+
+template <typename E> using V8 = Vec<E, 8>;
+
+// One K=32 step of a 16x16 fp32-accumulating MFMA tile.  Lane l holds row
+// (A) or column (B) l%16 and the 8 K-elements of group l/16; the K order
+// inside a step is free as long as A and B use the same one.
+__device__ inline f32x4 mma32(const V8<BF16>& a, const V8<BF16>& b, f32x4 c) {
+  u32x4 ra = {a.w[0], a.w[1], a.w[2], a.w[3]};
+  u32x4 rb = {b.w[0], b.w[1], b.w[2], b.w[3]};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra),
+                                                 __builtin_bit_cast(bf16x8, rb), c, 0, 0, 0);
+}
+__device__ inline f32x4 mma32(const V8<F32>& a, const V8<F32>& b, f32x4 c) {
+  // eight 16x16x4 steps, step s taking element s of every lane's group
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f(s), b.f(s), c, 0, 0, 0);
+  return c;
+}
+
+// Split an fp32 value into bf16 hi + lo (hi = RNE(x), lo = RNE(x - hi)):
+// hi + lo carries ~16 significant bits, enough for fp32-accurate products.
+__device__ inline void split_bf16(float x, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
+
+__device__ inline float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+__device__ inline float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// XCD-aware remap of the linear workgroup id.  Workgroups are dispatched to
+// the 8 XCDs round-robin (id % 8); this returns a logical id such that each
+// XCD receives one contiguous range of logical ids, so neighbouring tiles
+// (which share operands) sit behind the same L2.  Requires nblocks % 8 == 0;
+// otherwise the id is returned unchanged.
+__device__ inline int xcd_logical_block(int bid, int nblocks) {
+  if (nblocks & 7) return bid;
+  return (bid & 7) * (nblocks >> 3) + (bid >> 3);
+}
+
+}  // namespace xhc

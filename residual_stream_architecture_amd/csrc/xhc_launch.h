@@ -1,0 +1,61 @@
+// Internal launch interface between the C-ABI entry points and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "xhc_plan.h"
+
+struct xhc_timer;   // defined in xhc_api.cpp
+
+namespace xhc {
+
+// Kernel ids reported by the timer (names in xhc_api.cpp).
+enum KernelId {
+  KID_PACK_WT = 0, KID_PROJ, KID_COEF, KID_MIX,
+  KID_PACK_WP, KID_BDOTS, KID_BCOEF, KID_BGRAD, KID_BREDUCE,
+  KID_COUNT
+};
+// Alias kept for the backward's coefficient recompute from z_save.
+constexpr KernelId KID_BCOEF_FWD = KID_COEF;
+
+// Records a start event before and a stop event after the launches in its
+// scope when a timer is attached (no-op otherwise).
+void timer_mark(xhc_timer* tm, int kid, hipStream_t st, bool start);
+struct TimedLaunch {
+  xhc_timer* tm; int kid; hipStream_t st;
+  TimedLaunch(xhc_timer* t, int k, hipStream_t s) : tm(t), kid(k), st(s) { if (tm) timer_mark(tm, kid, st, true); }
+  ~TimedLaunch() { if (tm) timer_mark(tm, kid, st, false); }
+};
+
+// Where each stream's rows of the pre-update state live: element pointer of
+// stream i's row for token 0 and the element stride between tokens.  Either
+// the state itself (base X + i*C, stride N*C) or, for the active streams
+// after an in-place forward, the saved rows (base xact + a*C, stride k*C).
+struct StreamRows {
+  const void* base[16];
+  int64_t stride[16];
+};
+
+inline StreamRows stream_rows(const Plan& p, const void* X, const void* xact, const int32_t* active) {
+  StreamRows s;
+  const char* xb = static_cast<const char*>(X);
+  for (int i = 0; i < 16; ++i) {
+    s.base[i] = xb + (size_t)(i < p.N ? i : 0) * p.C * p.esz;
+    s.stride[i] = p.NC;
+  }
+  if (xact) {
+    const char* ab = static_cast<const char*>(xact);
+    for (int a = 0; a < p.k; ++a) {
+      s.base[active[a]] = ab + (size_t)a * p.C * p.esz;
+      s.stride[active[a]] = (int64_t)p.k * p.C;
+    }
+  }
+  return s;
+}
+
+int launch_forward(const Plan& p, const xhc_fwd_args* a, void* ws, hipStream_t st);
+int launch_coef_bwd(const Plan& p, const void* X, const void* xact, const int32_t* active, const void* W,
+                    const float* bias, const float* z_save, void* ws, float* coef, float* z_out,
+                    hipStream_t st, xhc_timer* tm);
+int launch_backward(const Plan& p, const xhc_bwd_args* a, void* ws, hipStream_t st);
+
+}  // namespace xhc

@@ -1,0 +1,204 @@
+"""ctypes binding of libxhc (include/xhc.h), same names as the C ABI.
+
+Argument marshalling only: torch tensors provide device pointers and the
+current HIP stream; every step of the update runs in the library's kernels.
+Importing this module fails loudly when libxhc.so has not been built.
+"""
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libxhc.so")
+
+XHC_F32, XHC_BF16 = 0, 1
+XHC_GATE_SIGMOID, XHC_GATE_UNIT = 0, 1
+XHC_PHASE_FWD, XHC_PHASE_BWD = 0, 1
+ERRORS = {0: "XHC_OK", -1: "XHC_ERR_NULL", -2: "XHC_ERR_SHAPE", -3: "XHC_ERR_INDEX",
+          -4: "XHC_ERR_ALIAS", -5: "XHC_ERR_ALIGN", -6: "XHC_ERR_UNSUPPORTED",
+          -7: "XHC_ERR_WORKSPACE", -8: "XHC_ERR_HIP"}
+
+_vp = ctypes.c_void_p
+_fp = ctypes.POINTER(ctypes.c_float)
+
+
+class xhc_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("k", ctypes.c_int32), ("ncomp", ctypes.c_int32),
+                ("sinkhorn_iters", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("gate_mode", ctypes.c_int32)]
+
+
+class xhc_fwd_args(ctypes.Structure):
+    _fields_ = [("X", _vp), ("out", _vp), ("w4", _vp), ("w8", _vp), ("w12", _vp),
+                ("W", _vp), ("bias", _vp), ("active", ctypes.POINTER(ctypes.c_int32)),
+                ("X_new", _vp), ("h_in", _vp), ("z_save", _vp), ("xact_save", _vp),
+                ("timer", _vp)]
+
+
+class xhc_bwd_args(ctypes.Structure):
+    _fields_ = [("X", _vp), ("xact", _vp), ("out", _vp), ("w4", _vp), ("w8", _vp), ("w12", _vp),
+                ("W", _vp), ("bias", _vp), ("active", ctypes.POINTER(ctypes.c_int32)),
+                ("z_save", _vp), ("dX_new", _vp), ("dh_in", _vp), ("dX", _vp), ("dout", _vp),
+                ("dW", _vp), ("db", _vp), ("dw4", _vp), ("dw8", _vp), ("dw12", _vp),
+                ("accumulate", ctypes.c_int32), ("timer", _vp)]
+
+
+class XhcError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__(f"{what}: {ERRORS.get(code, code)} ({lib.xhc_strerror(code).decode()})")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m residual_stream_architecture_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.xhc_workspace_size.argtypes = [ctypes.POINTER(xhc_desc), ctypes.c_int]
+    L.xhc_workspace_size.restype = ctypes.c_size_t
+    L.xhc_validate.argtypes = [ctypes.POINTER(xhc_desc), _vp, ctypes.c_int]
+    L.xhc_validate.restype = ctypes.c_int
+    L.xhc_forward.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_fwd_args), _vp, ctypes.c_size_t, _vp]
+    L.xhc_forward.restype = ctypes.c_int
+    L.xhc_backward.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_bwd_args), _vp, ctypes.c_size_t, _vp]
+    L.xhc_backward.restype = ctypes.c_int
+    L.xhc_strerror.argtypes = [ctypes.c_int]
+    L.xhc_strerror.restype = ctypes.c_char_p
+    L.xhc_timer_create.argtypes = []
+    L.xhc_timer_create.restype = _vp
+    L.xhc_timer_destroy.argtypes = [_vp]
+    L.xhc_timer_destroy.restype = None
+    L.xhc_timer_reset.argtypes = [_vp]
+    L.xhc_timer_reset.restype = None
+    L.xhc_timer_read.argtypes = [_vp, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_int64)]
+    L.xhc_timer_read.restype = ctypes.c_int
+    L.xhc_kernel_count.argtypes = []
+    L.xhc_kernel_count.restype = ctypes.c_int
+    L.xhc_kernel_name.argtypes = [ctypes.c_int]
+    L.xhc_kernel_name.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def make_desc(B, S, C, N, k, ncomp, dtype, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID):
+    return xhc_desc(B, S, C, N, k, ncomp, iters, eps, dtype, gate_mode)
+
+
+def workspace_size(desc, phase):
+    return lib.xhc_workspace_size(ctypes.byref(desc), phase)
+
+
+def strerror(code):
+    return lib.xhc_strerror(code).decode()
+
+
+def kernel_names():
+    return [lib.xhc_kernel_name(i).decode() for i in range(lib.xhc_kernel_count())]
+
+
+class Timer:
+    """Per-kernel HIP-event timer (xhc_timer)."""
+
+    def __init__(self):
+        self.handle = lib.xhc_timer_create()
+
+    def reset(self):
+        lib.xhc_timer_reset(self.handle)
+
+    def read(self, kernel):
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        rc = lib.xhc_timer_read(self.handle, kernel.encode(), ctypes.byref(ms), ctypes.byref(n))
+        if rc:
+            raise XhcError(rc, "xhc_timer_read")
+        return ms.value, n.value
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib.xhc_timer_destroy(self.handle)
+            self.handle = None
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers (pointer and stream plumbing)
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return XHC_BF16
+    if t.dtype == torch.float32:
+        return XHC_F32
+    raise TypeError(f"unsupported state dtype {t.dtype}")
+
+
+def _stream_handle(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _workspace(desc, phase, device, workspace):
+    import torch
+    need = workspace_size(desc, phase)
+    if need == 0:
+        raise XhcError(-2, "xhc_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, need
+
+
+def _active_array(active):
+    arr = (ctypes.c_int32 * len(active))(*[int(a) for a in active])
+    return arr
+
+
+def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None, bias=None,
+            z_save=None, xact_save=None, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID,
+            workspace=None, stream=None, timer=None, desc=None):
+    """xhc_forward on torch device tensors.  X [B*S,N,C], out [B*S,C], W [N*C,P]."""
+    T, N, C = X.shape
+    ncomp = 4 if w4 is not None else 1
+    if desc is None:
+        desc = make_desc(B, S, C, N, len(active), ncomp, _dtype_code(X), iters, eps, gate_mode)
+    act = _active_array(active)
+    args = xhc_fwd_args(_ptr(X), _ptr(out), _ptr(w4), _ptr(w8), _ptr(w12), _ptr(W), _ptr(bias),
+                        ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(X_new), _ptr(h_in),
+                        _ptr(z_save), _ptr(xact_save), None if timer is None else timer.handle)
+    ws, need = _workspace(desc, XHC_PHASE_FWD, X.device, workspace)
+    rc = lib.xhc_forward(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
+                         _stream_handle(stream))
+    if rc:
+        raise XhcError(rc, "xhc_forward")
+
+
+def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None, w4=None, w8=None,
+             w12=None, bias=None, z_save=None, db=None, dw4=None, dw8=None, dw12=None, accumulate=False,
+             iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID, workspace=None, stream=None, timer=None,
+             desc=None):
+    """xhc_backward on torch device tensors."""
+    T, N, C = X.shape
+    ncomp = 4 if w4 is not None else 1
+    if desc is None:
+        desc = make_desc(B, S, C, N, len(active), ncomp, _dtype_code(X), iters, eps, gate_mode)
+    act = _active_array(active)
+    args = xhc_bwd_args(_ptr(X), _ptr(xact), _ptr(out), _ptr(w4), _ptr(w8), _ptr(w12), _ptr(W), _ptr(bias),
+                        ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(z_save), _ptr(dX_new),
+                        _ptr(dh_in), _ptr(dX), _ptr(dout), _ptr(dW), _ptr(db), _ptr(dw4), _ptr(dw8),
+                        _ptr(dw12), int(bool(accumulate)), None if timer is None else timer.handle)
+    ws, need = _workspace(desc, XHC_PHASE_BWD, X.device, workspace)
+    rc = lib.xhc_backward(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
+                          _stream_handle(stream))
+    if rc:
+        raise XhcError(rc, "xhc_backward")
+
+
+def validate(desc, args, phase):
+    """xhc_validate on an xhc_fwd_args / xhc_bwd_args structure (host only)."""
+    return lib.xhc_validate(ctypes.byref(desc), ctypes.cast(ctypes.byref(args), _vp), phase)

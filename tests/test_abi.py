@@ -1,0 +1,172 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every function
+include/xhc.h declares, sizes workspaces and rejects bad arguments before
+launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from residual_stream_architecture_amd import xhc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    txt = open(os.path.join(ROOT, "include", "xhc.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(xhc_[a-z_]+)\s*\(", txt)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert "xhc_forward" in names and "xhc_backward" in names and len(names) >= 11
+    for n in names:
+        assert hasattr(xhc.lib, n), n
+
+
+def test_kernel_names():
+    names = xhc.kernel_names()
+    assert names[:4] == ["pack_wt", "proj", "coef", "mix"]
+    assert "bgrad" in names and "bdots" in names
+
+
+BASE = 1 << 40          # fake, 256-aligned device addresses: validation never dereferences them
+
+
+def fake(i, off=0):
+    return BASE + (i << 32) + off
+
+
+def good_fwd(desc, inplace=True):
+    act = (ctypes.c_int32 * desc.k)(*range(desc.k))
+    a = xhc.xhc_fwd_args(
+        X=fake(1), out=fake(2), w4=fake(3) if desc.ncomp == 4 else None,
+        w8=fake(4) if desc.ncomp == 4 else None, w12=fake(5) if desc.ncomp == 4 else None,
+        W=fake(6), bias=None, active=ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)),
+        X_new=fake(1) if inplace else fake(7), h_in=fake(8), z_save=fake(9), xact_save=fake(10),
+        timer=None)
+    return a, act
+
+
+def good_bwd(desc):
+    act = (ctypes.c_int32 * desc.k)(*range(desc.k))
+    c4 = desc.ncomp == 4
+    a = xhc.xhc_bwd_args(
+        X=fake(1), xact=fake(2), out=fake(3), w4=fake(4) if c4 else None, w8=fake(5) if c4 else None,
+        w12=fake(6) if c4 else None, W=fake(7), bias=None,
+        active=ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), z_save=fake(8), dX_new=fake(9),
+        dh_in=fake(10), dX=fake(11), dout=fake(12), dW=fake(13), db=fake(14),
+        dw4=fake(15) if c4 else None, dw8=fake(16) if c4 else None, dw12=fake(17) if c4 else None,
+        accumulate=0, timer=None)
+    return a, act
+
+
+def desc16(**kw):
+    d = dict(B=2, S=100, C=256, N=16, k=4, ncomp=4, dtype=xhc.XHC_BF16)
+    d.update(kw)
+    return xhc.make_desc(**d)
+
+
+def test_workspace_sizes():
+    d = desc16()
+    f, b = xhc.workspace_size(d, 0), xhc.workspace_size(d, 1)
+    assert f > 0 and b > f and f % 256 == 0 and b % 256 == 0
+    assert xhc.workspace_size(desc16(C=7), 0) == 0
+    assert xhc.workspace_size(d, 5) == 0
+    # the headline workload: T=8192, C=4096; the workspace stays small next to the state
+    big = desc16(B=2, S=4096, C=4096)
+    assert xhc.workspace_size(big, 1) < 0.25 * 8192 * 16 * 4096 * 2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(C=12), -2), (dict(C=0), -2), (dict(k=5), -2), (dict(N=3), -2), (dict(N=17), -2),
+    (dict(ncomp=2), -2), (dict(B=0), -2), (dict(dtype=7), -6), (dict(iters=0), -2),
+    (dict(iters=65), -2), (dict(B=1 << 14, S=1 << 10, C=1024), -2)])
+def test_bad_descriptions(kw, code):
+    d = desc16(**kw)
+    a, _ = good_fwd(desc16())
+    assert xhc.validate(d, a, 0) == code
+
+
+def test_valid_arguments_pass():
+    for kw in [dict(), dict(ncomp=1, N=4), dict(N=1, k=1, ncomp=1, dtype=xhc.XHC_F32)]:
+        d = desc16(**kw)
+        a, keep = good_fwd(d)
+        assert xhc.validate(d, a, 0) == 0, kw
+        a2, keep2 = good_fwd(d, inplace=False)
+        assert xhc.validate(d, a2, 0) == 0, kw
+        b, keep3 = good_bwd(d)
+        assert xhc.validate(d, b, 1) == 0, kw
+
+
+def test_forward_error_paths():
+    d = desc16()
+    a, keep = good_fwd(d)
+    # null required pointers
+    for f in ("X", "out", "W", "X_new", "h_in", "w8"):
+        b, k2 = good_fwd(d)
+        setattr(b, f, None)
+        assert xhc.validate(d, b, 0) == -1, f
+    # indices: out of range, repeated
+    for bad in ([0, 1, 2, 16], [0, 1, 1, 3], [-1, 1, 2, 3]):
+        b, _ = good_fwd(d)
+        arr = (ctypes.c_int32 * 4)(*bad)
+        b.active = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+        assert xhc.validate(d, b, 0) == -3, bad
+    # alignment
+    b, _ = good_fwd(d)
+    b.out = fake(2, 8)
+    assert xhc.validate(d, b, 0) == -5
+    # partial overlap of X_new with X, h_in inside X, xact_save overlapping h_in
+    b, _ = good_fwd(d)
+    b.X_new = fake(1, 4096)
+    assert xhc.validate(d, b, 0) == -4
+    b, _ = good_fwd(d)
+    b.h_in = fake(1, 1024)
+    assert xhc.validate(d, b, 0) == -4
+    b, _ = good_fwd(d)
+    b.xact_save = fake(8, 256)
+    assert xhc.validate(d, b, 0) == -4
+    # conv weights given for a single-component call
+    d1 = desc16(ncomp=1)
+    b, _ = good_fwd(d1)
+    b.w4 = fake(3)
+    assert xhc.validate(d1, b, 0) == -6
+
+
+def test_backward_error_paths():
+    d = desc16()
+    for f in ("X", "dX_new", "dh_in", "dX", "dout", "dW", "dw12", "W"):
+        b, _ = good_bwd(d)
+        setattr(b, f, None)
+        assert xhc.validate(d, b, 1) == -1, f
+    b, _ = good_bwd(d)
+    b.dX = b.dX_new                      # in-place dX is allowed
+    assert xhc.validate(d, b, 1) == 0
+    b, _ = good_bwd(d)
+    b.dX = fake(9, 512)                  # partial overlap is not
+    assert xhc.validate(d, b, 1) == -4
+    b, _ = good_bwd(d)
+    b.dout = fake(3)                     # gradient written over an input
+    assert xhc.validate(d, b, 1) == -4
+    b, _ = good_bwd(d)
+    b.accumulate = 2
+    assert xhc.validate(d, b, 1) == -6
+
+
+def test_calls_fail_before_launch_without_workspace():
+    d = desc16()
+    a, keep = good_fwd(d)
+    rc = xhc.lib.xhc_forward(ctypes.byref(d), ctypes.byref(a), None, 0, None)
+    assert rc == -7
+    rc = xhc.lib.xhc_forward(ctypes.byref(d), ctypes.byref(a), fake(20), 16, None)
+    assert rc == -7
+    rc = xhc.lib.xhc_forward(ctypes.byref(d), ctypes.byref(a), fake(20, 128), 1 << 40, None)
+    assert rc == -5
+
+
+def test_strerror():
+    for c in range(0, -9, -1):
+        assert xhc.strerror(c)
+    assert "unknown" in xhc.strerror(-99)
