@@ -1,0 +1,266 @@
+"""Benchmark of the xHC sublayer forward+backward on one MI355X.
+
+One step = xhc_forward (in place, saving z and the old active rows) followed
+by xhc_backward, over one batch of the fwd+bwd workload (B=2, S=4096,
+C=4096, N=16 streams, k=4 active, TFA on, bf16 storage, fp32 arithmetic),
+with every input resident in HBM before the timed region starts.
+
+Prints one JSON line: tokens/s of the whole step, the roofline of the
+dominant kernel (algorithmic bytes per launch / its average duration from
+HIP events on the launch stream) and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "tokens/s and achieved HBM GB/s (% of peak), xHC N=16 k=4 sublayer fwd+bwd"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="fwdbwd4096")
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
+                    help="tokens of the CPU oracle sample (whole sequences, then a causal prefix)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-timer", action="store_true", help="skip the per-kernel event pass")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 2 GiB device copy (HBM counter calibration) and exit")
+    return ap.parse_args()
+
+
+def kernel_bytes(w, esz):
+    """Algorithmic HBM bytes per launch of each main kernel: every input and
+    output it must touch, once (per token, in units of C elements):
+      proj   reads the state                                   16C
+      mix    reads state 16C + out C; writes h_in C, 4 rows 4C,
+             saved old rows 4C                                 26C
+      bdots  reads state 16C (12 rows + 4 saved) + G 4C + dh_in C
+             + out C; writes dout C                            23C
+      bgrad  reads state 16C + dX_new 16C + dh_in C; writes dX 16C  49C
+    plus the projection weights (N*C x P) where a kernel reads them."""
+    T, C, N, k, P = w.T, w.C, w.N, w.k, w.P
+    unit = T * C * esz
+    wbytes = N * C * P * esz
+    return {
+        "proj": 16 * unit + wbytes,
+        "mix": (N + 1 + 1 + k + k) * unit,
+        "bdots": (N + k + 1 + 1 + 1) * unit,
+        "bgrad": (N + N + 1 + N) * unit + wbytes,
+    }
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "residual_stream_architecture_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"```json\n(.*?)\n```", txt, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_probe(torch):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.int16, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    reps = 10
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t) / reps
+    print(json.dumps({"copy_probe_bytes": 2 * n * 2, "ms": dt * 1e3, "GBps": 4 * n / dt / 1e9}), flush=True)
+
+
+def cpu_baseline(w, ntok):
+    """The oracle, as it stands, on `ntok` tokens of the workload: whole
+    sequences of it in turn (B=1 each, S=w.S), then a causally closed prefix
+    of the next one when ntok is not a multiple of S."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import xhc_oracle as xo
+    from residual_stream_architecture_amd import synth
+    active = synth.active_streams(0, w.N, w.k)
+    dt = 0.0
+    left = ntok
+    seq = 0
+    while left > 0:
+        S = min(left, w.S)
+        sw = synth.Workload("cpu-sample", 1, S, w.C, w.N, w.k, w.ncomp, w.dtype, "fwdbwd")
+        d = synth.make_inputs(sw, seed=seq, grads=True)
+        h = {k: synth.as_float(d, k) for k in d}
+        del d
+        convs = (h["w4"], h["w8"], h["w12"])
+        t = time.perf_counter()
+        xo.forward(h["X"], h["out"], h["W"], h["bias"], active, convs, B=1, S=S, iters=w.iters, eps=w.eps)
+        xo.backward(h["X"], h["out"], h["W"], h["bias"], active, convs, h["dX_new"], h["dh_in"], B=1, S=S,
+                    iters=w.iters, eps=w.eps)
+        dt += time.perf_counter() - t
+        del h
+        left -= S
+        seq += 1
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(ntok / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"numpy fp64 oracle forward+backward over {ntok} tokens ({seq} sequence(s) of at most "
+                      f"{w.S}) of the same workload (C={w.C}, N={w.N}, k={w.k}, TFA on): {dt:.1f} s of compute; "
+                      f"BLAS threads={threads}, host cpus={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from residual_stream_architecture_amd import synth
+    from residual_stream_architecture_amd import xhc
+
+    if args.copy_probe:
+        copy_probe(torch)
+        return
+
+    w = synth.WORKLOADS[args.workload]
+    assert w.phase == "fwdbwd", "the benchmark step is a forward+backward workload"
+    T, N, C, P, k = w.T, w.N, w.C, w.P, w.k
+    esz = 2 if w.dtype == "bf16" else 4
+    print(f"# workload {w}", file=sys.stderr, flush=True)
+
+    d = synth.make_inputs(w, seed=0, grads=True)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    X = dev(d.pop("X"))
+    dXn = dev(d.pop("dX_new"))
+    dhin = dev(d.pop("dh_in"))
+    out = dev(d["out"])
+    W = dev(d["W"])
+    bias = dev(d["bias"])
+    convs = dict(w4=dev(d["w4"]), w8=dev(d["w8"]), w12=dev(d["w12"]))
+    del d
+    sdt = X.dtype
+    h_in = torch.empty(T, C, dtype=sdt, device="cuda")
+    z_save = torch.empty(T, P + 1, device="cuda")
+    xact = torch.empty(T, k, C, dtype=sdt, device="cuda")
+    dX = torch.empty_like(dXn)
+    dout = torch.empty(T, C, dtype=sdt, device="cuda")
+    dW = torch.empty(N * C, P, device="cuda")
+    db = torch.empty(P, device="cuda")
+    dws = dict(dw4=torch.empty(C, 4, device="cuda"), dw8=torch.empty(C, 8, device="cuda"),
+               dw12=torch.empty(C, 12, device="cuda"))
+    desc = xhc.make_desc(w.B, w.S, C, N, k, w.ncomp, xhc.XHC_BF16 if w.dtype == "bf16" else xhc.XHC_F32,
+                         w.iters, w.eps)
+    ws_f = torch.empty(xhc.workspace_size(desc, 0), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(xhc.workspace_size(desc, 1), dtype=torch.uint8, device="cuda")
+    active = synth.active_streams(0, N, k)
+
+    def step(timer=None):
+        xhc.forward(X, out, W, active, X, h_in, B=w.B, S=w.S, bias=bias, z_save=z_save, xact_save=xact,
+                    workspace=ws_f, timer=timer, desc=desc, **convs)
+        xhc.backward(X, out, W, active, dXn, dhin, dX, dout, dW, B=w.B, S=w.S, xact=xact, bias=bias,
+                     z_save=z_save, db=db, workspace=ws_b, timer=timer, desc=desc, **convs, **dws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = T * args.steps / elapsed
+    print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # per-kernel durations from HIP events recorded on the launch stream
+    kernels = {}
+    roofline = None
+    if not args.no_timer:
+        timer = xhc.Timer()
+        for _ in range(args.steps):
+            step(timer)
+        torch.cuda.synchronize()
+        kb = kernel_bytes(w, esz)
+        for name in xhc.kernel_names():
+            ms, n = timer.read(name)
+            if n:
+                kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n}
+        for name, byts in kb.items():
+            if name in kernels:
+                avg_s = kernels[name]["avg_us"] * 1e-6
+                kernels[name]["alg_bytes"] = byts
+                kernels[name]["alg_GBps"] = round(byts / avg_s / 1e9, 1)
+        dom = max(kb, key=lambda n: kernels.get(n, {}).get("avg_us", 0.0))
+        achieved = kernels[dom]["alg_GBps"]
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(dom, w.name)}
+
+    # whole-step accounting in units of C per token (bf16)
+    alg_step_c = (N + 1 + 1 + k) + (N + N + 1 + 1 + N + 1)        # 22C forward + 51C backward
+    impl_step_c = 16 + 26 + 23 + 49                                 # what the kernels above touch
+    step_bytes = alg_step_c * T * C * esz
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"xHC sublayer fwd+bwd ({w.name}): B={w.B} S={w.S} C={C} N={N} k={k} "
+                               f"TFA K=4/8/12, 20 Sinkhorn iters, in-place forward + backward",
+                   "global_batch": w.B, "seq_len": w.S},
+        "step_hbm": {"alg_bytes_per_token_in_C": alg_step_c, "touched_bytes_per_token_in_C": impl_step_c,
+                     "alg_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                     "alg_frac_of_peak": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -445,16 +445,22 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpart, i
     for (int n = 0; n < 3; ++n) dz_out[t * 48 + e + 16 * n] = dzs[tok][e + 16 * n];
   }
   // MFMA operands: dzr [T][64] (B operand of dz W^T) and its transpose
-  // [48][Tpad] (operand of dW); t in [T, Tpad) is written as zero.
+  // [48][Tpad] (operand of dW); t in [T, Tpad) is written as zero.  In bf16
+  // mode each is stored as hi and lo halves (hi at offset 0, lo after it):
+  // the dz values of saturated Sinkhorn entries are large, and the products
+  // must keep fp32 accuracy.
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int p = e + 16 * n;
     const float v = tv ? dzs[tok][p] * inv_r : 0.f;
     if constexpr (E::bytes == 2) {
-      if (tv) reinterpret_cast<__bf16*>(dzr)[t * 64 + p] = (__bf16)v;
+      __bf16 hi, lo;
+      split_bf16(v, hi, lo);
+      if (tv) {
+        reinterpret_cast<__bf16*>(dzr)[t * 64 + p] = hi;
+        reinterpret_cast<__bf16*>(dzr)[((size_t)T + t) * 64 + p] = lo;
+      }
       if (p < 48 && t < Tpad) {
-        __bf16 hi, lo;
-        split_bf16(v, hi, lo);
         reinterpret_cast<__bf16*>(dzrt)[(size_t)p * Tpad + t] = hi;
         reinterpret_cast<__bf16*>(dzrt)[(size_t)(48 + p) * Tpad + t] = lo;
       }
@@ -532,15 +538,22 @@ __global__ __launch_bounds__(256) void k_bgrad(
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int tb = t0 + 16 * tt + r16;
-      V8<E> bz[2];
+      V8<E> bz[2], bzl[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 2; ++ks) {
         bz[ks] = tb < T ? V8<E>::load(dzr, (size_t)tb * 64 + 32 * ks + 8 * g4) : V8<E>::zero();
+        if constexpr (BF)
+          bzl[ks] = tb < T ? V8<E>::load(dzr, ((size_t)T + tb) * 64 + 32 * ks + 8 * g4) : V8<E>::zero();
+      }
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mma32(wa[jt][0], bz[0], acc);
         acc = mma32(wa[jt][1], bz[1], acc);
+        if constexpr (BF) {
+          acc = mma32(wa[jt][0], bzl[0], acc);
+          acc = mma32(wa[jt][1], bzl[1], acc);
+        }
         pj[jt][tt] = acc;
       }
     }
