@@ -42,7 +42,12 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.ZST = q.NT * 16 + 4;
   q.proj_tiles = (int)cdiv(T, PROJ_TOK);
   q.mix_cblocks = (int)cdiv(q.C, MIX_THREADS * MIX_CH);
-  q.mix_segs = (int)cdiv(q.S, MIX_LSEG);
+  {
+    const int64_t waves_per_row = cdiv(q.C, MIX_CH * 64) * q.B;
+    const int64_t segs = std::max<int64_t>(1, MIX_TARGET_WAVES / std::max<int64_t>(1, waves_per_row));
+    q.mix_lseg = (int)std::max<int64_t>(16, cdiv(q.S, segs));
+    q.mix_segs = (int)cdiv(q.S, q.mix_lseg);
+  }
 
   // backward: B1 segments sized for ~2048 waves
   q.b1_cblocks = (int)cdiv(q.C, B1_WAVES * B1_WAVE_CH);
@@ -61,7 +66,7 @@ int make_plan(const xhc_desc* d, Plan* p) {
   {
     const int64_t base = (int64_t)q.b2_rowgroups * q.b2_cblocks;
     const int64_t tiles = q.Tpad / B2_TT;
-    int64_t ts = std::min<int64_t>(std::max<int64_t>(1, cdiv(512, base)), tiles);
+    int64_t ts = std::min<int64_t>(std::max<int64_t>(1, (B2_TARGET_WG + base / 2) / base), tiles);
     const int64_t tiles_per = cdiv(tiles, ts);
     q.b2_tok_per_split = (int)(tiles_per * B2_TT);
     q.b2_ts = (int)cdiv(T, q.b2_tok_per_split);
@@ -69,7 +74,7 @@ int make_plan(const xhc_desc* d, Plan* p) {
 
   // workspace layouts
   size_t o = 0;
-  q.off_wt = o;     o = align256(o + (size_t)q.NT * 16 * q.NC * q.esz);
+  q.off_wt = o;     o = align256(o + (size_t)q.N * cdiv(q.C, 32) * 32 * q.NT * 16 * q.esz);
   q.off_zpart = o;  o = align256(o + (size_t)q.SK * T * q.ZST * 4);
   q.off_coef = o;   o = align256(o + (size_t)T * COEF_STRIDE * 4);
   q.fwd_bytes = o;

@@ -52,12 +52,15 @@ __global__ void k_pack_wp(const R* __restrict__ W, R* __restrict__ Wp, int64_t N
 //   * X dots on MFMA: A = the 16 state rows (K = the chunk's channels),
 //     B columns = [dh_in, G_0..G_{k-1}, 0...]; D[i][0] = dH_pre[i] and
 //     D[i_b][1+a] = dH_res[a][b] (partial over the chunk).
-//   * TFA part (lane = 2 channels): U_m from a 12-row ring of `out`,
-//     dH_post partials (wave-reduced), dU_m scattered into a 12-slot ring of
-//     dout accumulators (anti-causal), conv-weight partials.
+//   * TFA part (lane = 2 channels): U_m from a 12-row window of `out`,
+//     dH_post partials (wave-reduced), dU_m scattered into a 12-slot window
+//     of dout accumulators (anti-causal), conv-weight partials.
+// Both windows shift by one slot per token (slot 11 = current position).
 // The segment is followed by an 11-token lookahead that only scatters dU
 // into the segment's last dout positions.  The 4 waves' partial dots are
-// summed in LDS once per 12 tokens and written per channel block.
+// summed in LDS once per 12 tokens and written per channel block.  All
+// loads are unconditional (clamped addresses, masked values) and the next
+// token's loads are issued before the current token's arithmetic.
 // ---------------------------------------------------------------------------
 template <typename E, int NCOMP>
 __global__ __launch_bounds__(256) void k_bdots(
@@ -76,253 +79,267 @@ __global__ __launch_bounds__(256) void k_bdots(
   const int bseq = seg / segs_per_seq;
   const int s0 = (seg - bseq * segs_per_seq) * lseg;
   const int s1 = min(s0 + lseg, S);
+  const int tend = s1 + 11;
   const size_t tok0 = (size_t)bseq * S;
-  const int64_t NCs = (int64_t)N * C;
 
-  // TFA lane channels
-  const int cl = c0 + B1_CH * lane;
-  const bool cv = cl < C;
-  // MFMA lane roles
+  // TFA lane channels (clamped for idle lanes)
+  const int clraw = c0 + B1_CH * lane;
+  const bool cv = clraw < C;
+  const int cl = cv ? clraw : 0;
+  // MFMA lane roles: A row r16 = stream r16; B column r16: 0 = dh_in, 1..k = G
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int n_col = r16;   // B column: 0 = dh_in, 1..k = G_{n-1}
-  const void* arow_base = src.base[r16];
-  const int64_t arow_stride = src.stride[r16];
   const bool arow_valid = r16 < N;
+  const void* arow_base = src.base[arow_valid ? r16 : 0];
+  const int64_t arow_stride = src.stride[arow_valid ? r16 : 0];
+  const bool bcol_valid = r16 <= k;
+  const int bcol_row = (r16 >= 1 && r16 <= k) ? act.id[r16 - 1] : 0;
 
   float wk[B1_CH][24];
-  if (NCOMP == 4) {
+  if constexpr (NCOMP == 4) {
 #pragma unroll
     for (int ch = 0; ch < B1_CH; ++ch) {
-      const int cc = cv ? cl + ch : 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wk[ch][q] = w4[(size_t)cc * 4 + q];
+      for (int q = 0; q < 4; ++q) wk[ch][q] = w4[(size_t)(cl + ch) * 4 + q];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) wk[ch][4 + q] = w8[(size_t)cc * 8 + q];
+      for (int q = 0; q < 8; ++q) wk[ch][4 + q] = w8[(size_t)(cl + ch) * 8 + q];
 #pragma unroll
-      for (int q = 0; q < 12; ++q) wk[ch][12 + q] = w12[(size_t)cc * 12 + q];
+      for (int q = 0; q < 12; ++q) wk[ch][12 + q] = w12[(size_t)(cl + ch) * 12 + q];
     }
   }
-  float ring[12][B1_CH], dacc[12][B1_CH], dw[B1_CH][24];
+  float win[12][B1_CH], dacc[12][B1_CH], dw[B1_CH][24];
 #pragma unroll
-  for (int j = 0; j < 12; ++j) {
-    const int s = s0 - 12 + j;
+  for (int j = 0; j < 12; ++j)
 #pragma unroll
-    for (int ch = 0; ch < B1_CH; ++ch) { ring[j][ch] = 0.f; dacc[j][ch] = 0.f; }
-    if (NCOMP == 4 && j > 0 && s >= 0 && cv) {
-      V2 v = V2::load(out, (tok0 + s) * C + cl);
-      v.to_float(ring[j]);
-    }
-  }
+    for (int ch = 0; ch < B1_CH; ++ch) { win[j][ch] = 0.f; dacc[j][ch] = 0.f; }
 #pragma unroll
   for (int ch = 0; ch < B1_CH; ++ch)
 #pragma unroll
     for (int q = 0; q < 24; ++q) dw[ch][q] = 0.f;
+  if constexpr (NCOMP == 4) {
+#pragma unroll
+    for (int j = 0; j < 11; ++j) {
+      const int s = s0 - 11 + j;
+      V2 v = V2::load(out, (tok0 + (s >= 0 ? s : 0)) * C + cl);
+      float f[B1_CH];
+      v.to_float(f);
+#pragma unroll
+      for (int ch = 0; ch < B1_CH; ++ch) win[j + 1][ch] = s >= 0 ? f[ch] : 0.f;
+    }
+  }
 
-  const int tend = s1 + 11;
-  for (int g0 = s0; g0 < tend; g0 += 12) {
+  // loads of one token (clamped to the sequence)
+  V8<E> av[B1_WAVE_CH / 32], bv[B1_WAVE_CH / 32];
+  V2 gv[4], ov;
+  auto load_mfma = [&](int s) {
+    const size_t t = tok0 + min(s, S - 1);
 #pragma unroll
-    for (int j = 0; j < 12; ++j) {
-      const int s = g0 + j;
-      if (s < tend) {
-        const bool main_tok = s < s1;
-        const bool live = s < S;              // lookahead tokens exist
-        const size_t t = tok0 + (live ? s : 0);
-        const float* co = coef + t * COEF_STRIDE;
+    for (int ks = 0; ks < B1_WAVE_CH / 32; ++ks) {
+      const int cc = c0 + ks * 32 + 8 * g4;
+      const int ccl = cc < C ? cc : 0;
+      av[ks] = V8<E>::load(arow_base, t * arow_stride + ccl);
+      bv[ks] = (r16 == 0) ? V8<E>::load(dhin, t * C + ccl) : V8<E>::load(dXn, (t * N + bcol_row) * C + ccl);
+      if (!(cc < C && arow_valid)) av[ks] = V8<E>::zero();
+      if (!(cc < C && bcol_valid)) bv[ks] = V8<E>::zero();
+    }
+  };
+  auto load_tfa = [&](int s) {
+    const size_t t = tok0 + min(s, S - 1);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) gv[a] = V2::load(dXn, (t * N + act.id[a < k ? a : 0]) * C + cl);
+    ov = V2::load(out, t * C + cl);
+  };
+  load_mfma(s0);
+  load_tfa(s0);
 
-        if (main_tok) {
-          // ---- X dots on MFMA over this wave's 128 channels ----
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = s0; s < tend; ++s) {
+    const bool main_tok = s < s1;
+    const bool live = s < S;
+    const size_t t = tok0 + (live ? s : S - 1);
+    const int slot = (s - s0) % 12;
+
+    if (main_tok) {
+      // ---- X dots on MFMA ----
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < B1_WAVE_CH / 32; ++ks) {
-            const int cc = c0 + ks * 32 + 8 * g4;
-            const bool kv = cc < C;
-            V8<E> av = (kv && arow_valid) ? V8<E>::load(arow_base, t * arow_stride + cc) : V8<E>::zero();
-            V8<E> bv = V8<E>::zero();
-            if (kv) {
-              if (n_col == 0) bv = V8<E>::load(dhin, t * C + cc);
-              else if (n_col <= k) bv = V8<E>::load(dXn, (t * N + act.id[n_col - 1]) * C + cc);
-            }
-            acc = mma32(av, bv, acc);
-          }
-          // lane (n_col, g4) holds D[4*g4 + e][n_col]
-          if (n_col == 0) {
+      for (int ks = 0; ks < B1_WAVE_CH / 32; ++ks) acc = mma32(av[ks], bv[ks], acc);
+      load_mfma(s + 1);
+      // lane (r16, g4) holds D[4*g4 + e][r16]
+      if (r16 == 0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[wave][j][4 * g4 + e] = acc[e];
-          } else if (n_col <= 4) {
-            const int a = n_col - 1;
+        for (int e = 0; e < 4; ++e) red[wave][slot][4 * g4 + e] = acc[e];
+      } else if (r16 <= 4) {
+        const int a = r16 - 1;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const bool ok = a < k && b < k;
-              const int ib = ok ? act.id[b] : 0;
-              if (ok && (ib >> 2) == g4) {
-                const int e = ib & 3;
-                red[wave][j][16 + a * 4 + b] = e == 0 ? acc[0] : e == 1 ? acc[1] : e == 2 ? acc[2] : acc[3];
-              } else if (!ok && g4 == 0) {
-                red[wave][j][16 + a * 4 + b] = 0.f;
-              }
-            }
+        for (int b = 0; b < 4; ++b) {
+          const bool ok = a < k && b < k;
+          const int ib = ok ? act.id[b] : 0;
+          if (ok && (ib >> 2) == g4) {
+            const int e = ib & 3;
+            red[wave][slot][16 + a * 4 + b] = e == 0 ? acc[0] : e == 1 ? acc[1] : e == 2 ? acc[2] : acc[3];
+          } else if (!ok && g4 == 0) {
+            red[wave][slot][16 + a * 4 + b] = 0.f;
           }
         }
+      }
+    }
 
-        // ---- TFA part ----
-        float G[4][B1_CH];
-        if (live) {
+    // ---- TFA part ----
+    float G[4][B1_CH], of[B1_CH];
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            if (a < k && cv) {
-              V2 gv = V2::load(dXn, (t * N + act.id[a]) * C + cl);
-              gv.to_float(G[a]);
-            } else {
+    for (int a = 0; a < 4; ++a) {
+      gv[a].to_float(G[a]);
+      if (!(a < k && cv && live)) {
 #pragma unroll
-              for (int ch = 0; ch < B1_CH; ++ch) G[a][ch] = 0.f;
-            }
-          }
+        for (int ch = 0; ch < B1_CH; ++ch) G[a][ch] = 0.f;
+      }
+    }
+    ov.to_float(of);
+    load_tfa(s + 1);
+
+    float H[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) H[a][m] = coef[t * COEF_STRIDE + CO_POST + a * 4 + m];
+
+    if (main_tok) {
+#pragma unroll
+      for (int j = 0; j < 11; ++j)
+#pragma unroll
+        for (int ch = 0; ch < B1_CH; ++ch) win[j][ch] = win[j + 1][ch];
+#pragma unroll
+      for (int ch = 0; ch < B1_CH; ++ch) win[11][ch] = cv ? of[ch] : 0.f;
+      float U[4][B1_CH];
+#pragma unroll
+      for (int ch = 0; ch < B1_CH; ++ch) {
+        U[0][ch] = win[11][ch];
+        if constexpr (NCOMP == 4) {
+          float s4 = 0.f, s8 = 0.f, s12 = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) s4 = fmaf(wk[ch][q], win[8 + q][ch], s4);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) s8 = fmaf(wk[ch][4 + q], win[4 + q][ch], s8);
+#pragma unroll
+          for (int q = 0; q < 12; ++q) s12 = fmaf(wk[ch][12 + q], win[q][ch], s12);
+          U[1][ch] = s4; U[2][ch] = s8; U[3][ch] = s12;
         }
-        if (main_tok) {
-          if (cv) {
-            V2 ov = V2::load(out, t * C + cl);
-            ov.to_float(ring[j]);
-          } else {
+      }
+      // dH_post partials v[a*4+m], reduced over the wave by halving
+      float v[16];
 #pragma unroll
-            for (int ch = 0; ch < B1_CH; ++ch) ring[j][ch] = 0.f;
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          float d = 0.f;
+          if (m < NCOMP) {
+#pragma unroll
+            for (int ch = 0; ch < B1_CH; ++ch) d = fmaf(G[a][ch], U[m][ch], d);
           }
-          // U_m for this token
-          float U[4][B1_CH];
+          v[a * 4 + m] = d;
+        }
+      {
+        const bool h5 = lane & 32;
 #pragma unroll
-          for (int ch = 0; ch < B1_CH; ++ch) {
-            U[0][ch] = ring[j][ch];
-            if (NCOMP == 4) {
-              float s4 = 0.f, s8 = 0.f, s12 = 0.f;
+        for (int q = 0; q < 8; ++q) {
+          const float send = h5 ? v[q] : v[8 + q];
+          const float keep = h5 ? v[8 + q] : v[q];
+          v[q] = keep + shfl_xor(send, 32);
+        }
+        const bool h4 = lane & 16;
 #pragma unroll
-              for (int q = 0; q < 4; ++q) s4 = fmaf(wk[ch][q], ring[(j + 12 - 3 + q) % 12][ch], s4);
+        for (int q = 0; q < 4; ++q) {
+          const float send = h4 ? v[q] : v[4 + q];
+          const float keep = h4 ? v[4 + q] : v[q];
+          v[q] = keep + shfl_xor(send, 16);
+        }
+        const bool h3 = lane & 8;
 #pragma unroll
-              for (int q = 0; q < 8; ++q) s8 = fmaf(wk[ch][4 + q], ring[(j + 12 - 7 + q) % 12][ch], s8);
+        for (int q = 0; q < 2; ++q) {
+          const float send = h3 ? v[q] : v[2 + q];
+          const float keep = h3 ? v[2 + q] : v[q];
+          v[q] = keep + shfl_xor(send, 8);
+        }
+        const bool h2 = lane & 4;
+        {
+          const float send = h2 ? v[0] : v[1];
+          const float keep = h2 ? v[1] : v[0];
+          v[0] = keep + shfl_xor(send, 4);
+        }
+        v[0] += shfl_xor(v[0], 1);
+        v[0] += shfl_xor(v[0], 2);
+        if ((lane & 3) == 0) {
+          const int idx = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+          red[wave][slot][32 + idx] = v[0];
+        }
+      }
+    }
+    // dU_m for this token (zero for tokens past the sequence)
+    float dU[4][B1_CH];
 #pragma unroll
-              for (int q = 0; q < 12; ++q) s12 = fmaf(wk[ch][12 + q], ring[(j + 12 - 11 + q) % 12][ch], s12);
-              U[1][ch] = s4; U[2][ch] = s8; U[3][ch] = s12;
-            }
-          }
-          // dH_post partials v[a*4+m], reduced over the wave by halving
-          float v[16];
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int ch = 0; ch < B1_CH; ++ch) {
+        float d = 0.f;
+        if (m < NCOMP) {
 #pragma unroll
           for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              float d = 0.f;
-              if (m < NCOMP) {
-#pragma unroll
-                for (int ch = 0; ch < B1_CH; ++ch) d = fmaf(G[a][ch], U[m][ch], d);
-              }
-              v[a * 4 + m] = d;
-            }
-          {
-            const bool h5 = lane & 32;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const float send = h5 ? v[q] : v[8 + q];
-              const float keep = h5 ? v[8 + q] : v[q];
-              v[q] = keep + shfl_xor(send, 32);
-            }
-            const bool h4 = lane & 16;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float send = h4 ? v[q] : v[4 + q];
-              const float keep = h4 ? v[4 + q] : v[q];
-              v[q] = keep + shfl_xor(send, 16);
-            }
-            const bool h3 = lane & 8;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const float send = h3 ? v[q] : v[2 + q];
-              const float keep = h3 ? v[2 + q] : v[q];
-              v[q] = keep + shfl_xor(send, 8);
-            }
-            const bool h2 = lane & 4;
-            {
-              const float send = h2 ? v[0] : v[1];
-              const float keep = h2 ? v[1] : v[0];
-              v[0] = keep + shfl_xor(send, 4);
-            }
-            v[0] += shfl_xor(v[0], 1);
-            v[0] += shfl_xor(v[0], 2);
-            if ((lane & 3) == 0) {
-              const int idx = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
-              red[wave][j][32 + idx] = v[0];
-            }
-          }
-          // conv-weight partials: dw_m[c,q] += dU_m[t] * out[t-K_m+1+q]
+            if (a < k) d = fmaf(H[a][m], G[a][ch], d);
         }
-        if (live) {
-          float dU[4][B1_CH];
+        dU[m][ch] = d;
+      }
+    if (main_tok && NCOMP == 4) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
+      for (int ch = 0; ch < B1_CH; ++ch) {
 #pragma unroll
-            for (int ch = 0; ch < B1_CH; ++ch) {
-              float d = 0.f;
-              if (m < NCOMP) {
+        for (int q = 0; q < 4; ++q) dw[ch][q] = fmaf(dU[1][ch], win[8 + q][ch], dw[ch][q]);
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
-                  if (a < k) d = fmaf(co[CO_POST + a * 4 + m], G[a][ch], d);
-              }
-              dU[m][ch] = d;
-            }
-          if (main_tok && NCOMP == 4) {
+        for (int q = 0; q < 8; ++q) dw[ch][4 + q] = fmaf(dU[2][ch], win[4 + q][ch], dw[ch][4 + q]);
 #pragma unroll
-            for (int ch = 0; ch < B1_CH; ++ch) {
+        for (int q = 0; q < 12; ++q) dw[ch][12 + q] = fmaf(dU[3][ch], win[q][ch], dw[ch][12 + q]);
+      }
+    }
+    // scatter into the dout accumulators of positions s - lag (slot 11 - lag)
+    if (main_tok) {
 #pragma unroll
-              for (int q = 0; q < 4; ++q) dw[ch][q] = fmaf(dU[1][ch], ring[(j + 12 - 3 + q) % 12][ch], dw[ch][q]);
+      for (int ch = 0; ch < B1_CH; ++ch) dacc[11][ch] += dU[0][ch];
+    }
+    if constexpr (NCOMP == 4) {
 #pragma unroll
-              for (int q = 0; q < 8; ++q) dw[ch][4 + q] = fmaf(dU[2][ch], ring[(j + 12 - 7 + q) % 12][ch], dw[ch][4 + q]);
+      for (int lag = 0; lag < 12; ++lag) {
+        if (lag <= s - s0) {
 #pragma unroll
-              for (int q = 0; q < 12; ++q) dw[ch][12 + q] = fmaf(dU[3][ch], ring[(j + 12 - 11 + q) % 12][ch], dw[ch][12 + q]);
-            }
-          }
-          // scatter into dout accumulators of positions s - lag (lag < K_m)
-          if (main_tok) {
-#pragma unroll
-            for (int ch = 0; ch < B1_CH; ++ch) dacc[j][ch] += dU[0][ch];
-          }
-          if (NCOMP == 4) {
-#pragma unroll
-            for (int lag = 0; lag < 12; ++lag) {
-              const int pos = s - lag;
-              if (pos >= s0 && pos < s1) {
-                const int slot = (j + 12 - lag) % 12;
-#pragma unroll
-                for (int ch = 0; ch < B1_CH; ++ch) {
-                  float d = dacc[slot][ch];
-                  if (lag < 4) d = fmaf(wk[ch][3 - lag], dU[1][ch], d);
-                  if (lag < 8) d = fmaf(wk[ch][4 + 7 - lag], dU[2][ch], d);
-                  d = fmaf(wk[ch][12 + 11 - lag], dU[3][ch], d);
-                  dacc[slot][ch] = d;
-                }
-              }
-            }
-          }
-        }
-        // position s-11 is complete: emit it
-        {
-          const int pos = s - 11;
-          const int slot = (j + 1) % 12;
-          if (pos >= s0 && pos < s1) {
-            if (cv) V2::from_float(dacc[slot]).store(dout, (tok0 + pos) * C + cl);
-#pragma unroll
-            for (int ch = 0; ch < B1_CH; ++ch) dacc[slot][ch] = 0.f;
+          for (int ch = 0; ch < B1_CH; ++ch) {
+            float d = dacc[11 - lag][ch];
+            if (lag < 4) d = fmaf(wk[ch][3 - lag], dU[1][ch], d);
+            if (lag < 8) d = fmaf(wk[ch][4 + 7 - lag], dU[2][ch], d);
+            d = fmaf(wk[ch][12 + 11 - lag], dU[3][ch], d);
+            dacc[11 - lag][ch] = d;
           }
         }
       }
     }
-    // ---- sum the 4 waves' dots of this group's tokens ----
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 12 * DOT_STRIDE; idx += 256) {
-      const int jj = idx / DOT_STRIDE, q = idx - jj * DOT_STRIDE;
-      const int s = g0 + jj;
-      if (s < s1) {
+    // position s-11 is complete: emit it, then shift the window
+    {
+      const int pos = s - 11;
+      if (pos >= s0 && cv) V2::from_float(dacc[0]).store(dout, (tok0 + pos) * C + cl);
+#pragma unroll
+      for (int j = 0; j < 11; ++j)
+#pragma unroll
+        for (int ch = 0; ch < B1_CH; ++ch) dacc[j][ch] = dacc[j + 1][ch];
+#pragma unroll
+      for (int ch = 0; ch < B1_CH; ++ch) dacc[11][ch] = 0.f;
+    }
+    // ---- every 12 main tokens: sum the 4 waves' dots ----
+    if (main_tok && (slot == 11 || s == s1 - 1)) {
+      __syncthreads();
+      const int g0 = s - slot;
+      for (int idx = threadIdx.x; idx < (slot + 1) * DOT_STRIDE; idx += 256) {
+        const int jj = idx / DOT_STRIDE, q = idx - jj * DOT_STRIDE;
         const float sum = (red[0][jj][q] + red[1][jj][q]) + (red[2][jj][q] + red[3][jj][q]);
-        dpart[((size_t)cblock * T + tok0 + s) * DOT_STRIDE + q] = sum;
+        dpart[((size_t)cblock * T + tok0 + g0 + jj) * DOT_STRIDE + q] = sum;
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
   if (NCOMP == 4 && cv) {
 #pragma unroll
@@ -472,26 +489,48 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpart, i
 }
 
 // ---------------------------------------------------------------------------
-// B2.  Workgroup = (row group, 64 channels, token split); wave w handles the
-// group's row w.  Per 32-token tile:
-//   proj[c][t] = sum_p W[i*C+c, p] dzr[t, p] on MFMA, with A rows permuted so
-//   that lane (t = lane%16, g = lane/16) ends up owning channels 16g..16g+16
-//   of tokens t and t+16 -- the layout of its own vector loads;
+// B2.  Workgroup = (row group, B2_CB channels, token split); wave w handles
+// the group's row w.  Per tile of B2_TT = 16 tokens:
+//   proj[c][t] = sum_p W[i*C+c, p] dzr[t, p] on MFMA (dz/r as bf16 hi + lo),
+//   with A rows permuted so that lane (t = lane%16, g = lane/16) ends up
+//   owning channels 8g..8g+8 of token t -- the layout of its own loads;
 //   dX = pass + H_pre dh_in + proj - X gamma;
-//   dW[i*C+c][p] += sum_t X[t, c] dzr[t, p] on MFMA (A = X^T through LDS,
-//   dzr as bf16 hi + lo).
-// For the active group all rows are read before any is written (barrier), so
-// dX may alias dX_new.
+//   dW[i*C+c][p] += sum_t X[t, c] dzr[t, p] on MFMA (K = the tile's tokens,
+//   A = X^T through LDS).
+// The tile operands shared by the four rows (dz/r, its transpose, dh_in, the
+// coefficient records) are loaded cooperatively one tile ahead through
+// registers into a double-buffered LDS stage; each wave prefetches its own
+// state and dX_new rows one tile ahead.  The active rows' upstream gradients
+// G_a are exchanged through LDS, so every wave reads only its own dX_new row
+// from memory and all of a tile's rows are read (a tile earlier) before any
+// is written: dX may alias dX_new.
 // ---------------------------------------------------------------------------
+template <typename E> struct B2Stage;
+template <> struct B2Stage<BF16> {      // 16-byte chunks per region
+  static constexpr int DZR = 128, DZRT = 96, DH = 64, CO = 256;
+  static constexpr int o_dzr_hi = 0, o_dzr_lo = DZR, o_dzrt_hi = 2 * DZR, o_dzrt_lo = 2 * DZR + DZRT,
+                       o_dh = 2 * DZR + 2 * DZRT, o_co = o_dh + DH, total = o_co + CO;
+};
+template <> struct B2Stage<F32> {
+  static constexpr int DZR = 256, DZRT = 192, DH = 128, CO = 256;
+  static constexpr int o_dzr_hi = 0, o_dzr_lo = DZR, o_dzrt_hi = DZR, o_dzrt_lo = DZR + DZRT,
+                       o_dh = DZR + DZRT, o_co = o_dh + DH, total = o_co + CO;
+};
+
 template <typename E>
 __global__ __launch_bounds__(256) void k_bgrad(
     StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin,
     const float* __restrict__ coef, const void* __restrict__ Wp, const void* __restrict__ dzr,
     const void* __restrict__ dzrt, void* dX, float* __restrict__ dwp, int T, int64_t Tpad, int C, int N,
-    int k, Act4 act, RowTable rows, int nrg, int ncb, int tok_per_split) {
+    int k, RowTable rows, int nrg, int ncb, int tok_per_split) {
   constexpr bool BF = E::bytes == 2;
-  constexpr int XS_LD = B2_CB + 8;                         // padded LDS row (elements)
-  __shared__ __attribute__((aligned(16))) unsigned char xs_raw[4][B2_TT][XS_LD * E::bytes];
+  using SG = B2Stage<E>;
+  constexpr int NCHUNK = SG::total;
+  constexpr int NLOAD = (NCHUNK + 255) / 256;
+  constexpr int XS_LD = B2_CB + (BF ? 2 : 1);            // padded LDS row of the X^T staging (elements)
+  __shared__ __attribute__((aligned(16))) u32x4 stage[2][NCHUNK];
+  __shared__ __attribute__((aligned(16))) u32x4 gsh[4][B2_TT][B2_CB * E::bytes / 16];
+  __shared__ __attribute__((aligned(16))) unsigned char xsh[4][B2_TT][XS_LD * E::bytes];
 
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int rg = lb % nrg;
@@ -505,48 +544,117 @@ __global__ __launch_bounds__(256) void k_bgrad(
   const bool active_grp = rg == 0;
   const int c0 = cb * B2_CB;
   const int64_t NCs = (int64_t)N * C;
-  const size_t jbase = (size_t)srow * C + c0;   // flattened row index of channel c0
+  const size_t jbase = (size_t)srow * C + c0;
+  const int cl = c0 + 8 * g4;                   // this lane's 8 channels
+  const bool cv = wv && cl < C;
+  const int clc = cl < C ? cl : 0;
 
   // proj A operand: W rows, permuted: A row m of j-tile jt -> channel
-  // 16*(m/4) + 4*jt + m%4 ; K = 64 logits in two steps.
-  V8<E> wa[4][2];
+  // 8*(m/4) + 4*jt + m%4 ; K = 64 logits in two steps.
+  V8<E> wa[2][2];
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    const int ch = 16 * (r16 >> 2) + 4 * jt + (r16 & 3);
+  for (int jt = 0; jt < 2; ++jt) {
+    const int ch = 8 * (r16 >> 2) + 4 * jt + (r16 & 3);
+    const bool ok = wv && c0 + ch < C;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      wa[jt][ks] = (wv && c0 + ch < C) ? V8<E>::load(Wp, (jbase + ch) * 64 + 32 * ks + 8 * g4) : V8<E>::zero();
+    for (int ks = 0; ks < 2; ++ks) {
+      V8<E> v = V8<E>::load(Wp, ((ok ? jbase + ch : 0)) * 64 + 32 * ks + 8 * g4);
+      wa[jt][ks] = ok ? v : V8<E>::zero();
+    }
   }
-  f32x4 dwacc[4][3];
+  f32x4 dwacc[2][3];
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
+  for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
     for (int pt = 0; pt < 3; ++pt) dwacc[jt][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const void* xbase = src.base[srow];
   const int64_t xstride = src.stride[srow];
-  const int cl = c0 + 16 * g4;                  // this lane's 16 channels
-  const bool cv = wv && cl < C;                 // C % 8 == 0: 8-wide halves
-  const bool cv2 = wv && cl + 8 < C;
-  unsigned char (*xs)[XS_LD * E::bytes] = xs_raw[wave];
-
   const int tbeg = ts * tok_per_split;
   const int tfin = min(tbeg + tok_per_split, T);
-  for (int t0 = tbeg; t0 < tfin; t0 += B2_TT) {
-    // ---- proj on MFMA: D[c][t] for 4 j-tiles x 2 token tiles ----
-    f32x4 pj[4][2];
+
+  // cooperative loads of the shared operands of the tile at t0 (16-byte chunks)
+  u32x4 stg[NLOAD];
+  auto load_shared = [&](int t0) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int tb = t0 + 16 * tt + r16;
+    for (int r = 0; r < NLOAD; ++r) {
+      const int q = threadIdx.x + 256 * r;
+      const unsigned char* gp;
+      if (q < SG::o_dzrt_hi) {                          // dzr [T][64] (hi, then lo)
+        const int qq = BF ? (q < SG::o_dzr_lo ? q : q - SG::o_dzr_lo) : q;
+        const size_t lo_off = (BF && q >= SG::o_dzr_lo) ? (size_t)T * 64 : 0;
+        const int per_tok = 64 * E::bytes / 16;
+        const int t = min(t0 + qq / per_tok, T - 1);
+        gp = static_cast<const unsigned char*>(dzr) + (lo_off + (size_t)t * 64) * E::bytes + (qq % per_tok) * 16;
+      } else if (q < SG::o_dh) {                        // dzr^T [48][Tpad] (hi, then lo)
+        const int qq = q - SG::o_dzrt_hi;
+        const int per_row = B2_TT * E::bytes / 16;
+        const int prow = qq / per_row;                  // 0..47 (hi) or 48..95 (lo)
+        gp = static_cast<const unsigned char*>(dzrt) + ((size_t)prow * Tpad + t0) * E::bytes + (qq % per_row) * 16;
+      } else if (q < SG::o_co) {                        // dh_in [T][C], this block's channels
+        const int qq = q - SG::o_dh;
+        const int per_tok = B2_CB * E::bytes / 16;
+        const int t = min(t0 + qq / per_tok, T - 1);
+        const int c = c0 + (qq % per_tok) * (16 / E::bytes);
+        gp = static_cast<const unsigned char*>(dhin) + ((size_t)t * C + (c < C ? c : 0)) * E::bytes;
+      } else {                                          // coefficient records [T][64] floats
+        const int qq = min(q - SG::o_co, SG::CO - 1);
+        const int t = min(t0 + qq / 16, T - 1);
+        gp = reinterpret_cast<const unsigned char*>(coef + (size_t)t * COEF_STRIDE) + (qq % 16) * 16;
+      }
+      stg[r] = *reinterpret_cast<const u32x4*>(gp);
+    }
+  };
+  auto store_shared = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < NLOAD; ++r) {
+      const int q = threadIdx.x + 256 * r;
+      if (q < NCHUNK) stage[buf][q] = stg[r];
+    }
+  };
+  // own rows of the tile at t0
+  V8<E> xo, dvo;
+  auto load_own = [&](int t0) {
+    const int t = min(t0 + r16, T - 1);
+    xo = V8<E>::load(xbase, (size_t)t * xstride + clc);
+    dvo = V8<E>::load(dXn, ((size_t)t * N + srow) * C + clc);
+  };
+
+  if (tbeg < tfin) {
+    load_shared(tbeg);
+    load_own(tbeg);
+    store_shared(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int t0 = tbeg; t0 < tfin; t0 += B2_TT, buf ^= 1) {
+    const int tk = t0 + r16;
+    const bool tv = tk < T;
+    V8<E> xc = xo, dvc = dvo;
+    if (!(tv && cv)) { xc = V8<E>::zero(); dvc = V8<E>::zero(); }
+    const bool more = t0 + B2_TT < tfin;
+    if (more) {
+      load_shared(t0 + B2_TT);
+      load_own(t0 + B2_TT);
+    }
+    // publish this tile's G row (active group) and X row (for X^T)
+    if (active_grp) *reinterpret_cast<V8<E>*>(&gsh[wave][r16][g4 * (8 * E::bytes / 16)]) = dvc;
+    *reinterpret_cast<V8<E>*>(&xsh[wave][r16][8 * g4 * E::bytes]) = xc;
+    __syncthreads();
+
+    const u32x4* sg = stage[buf];
+    // ---- proj on MFMA: D[c][t], 2 j-tiles ----
+    f32x4 pj[2];
+    {
       V8<E> bz[2], bzl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        bz[ks] = tb < T ? V8<E>::load(dzr, (size_t)tb * 64 + 32 * ks + 8 * g4) : V8<E>::zero();
-        if constexpr (BF)
-          bzl[ks] = tb < T ? V8<E>::load(dzr, ((size_t)T + tb) * 64 + 32 * ks + 8 * g4) : V8<E>::zero();
+        const int off = r16 * (64 * E::bytes / 16) + (32 * ks + 8 * g4) * E::bytes / 16;
+        bz[ks] = *reinterpret_cast<const V8<E>*>(&sg[SG::o_dzr_hi + off]);
+        if constexpr (BF) bzl[ks] = *reinterpret_cast<const V8<E>*>(&sg[SG::o_dzr_lo + off]);
       }
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
+      for (int jt = 0; jt < 2; ++jt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mma32(wa[jt][0], bz[0], acc);
         acc = mma32(wa[jt][1], bz[1], acc);
@@ -554,128 +662,91 @@ __global__ __launch_bounds__(256) void k_bgrad(
           acc = mma32(wa[jt][0], bzl[0], acc);
           acc = mma32(wa[jt][1], bzl[1], acc);
         }
-        pj[jt][tt] = acc;
+        pj[jt] = acc;
       }
     }
-    // ---- loads for the elementwise assembly ----
-    V8<E> xv[2][2], dv[2][2], hv[2][2];
-    float hpre[2], gam[2], hres[2][4];
+    // ---- assemble dX for (token tk, channels cl..cl+8) ----
+    {
+      const float* cor = reinterpret_cast<const float*>(&sg[SG::o_co]) + r16 * COEF_STRIDE;
+      const float hpre = cor[CO_PRE + srow];
+      const float gam = cor[CO_GAMMA];
+      float pass[8];
+      if (active_grp) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int tk = t0 + 16 * tt + r16;
-      const bool tv = tk < T;
-      const size_t tkc = tv ? tk : 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bool ok = tv && (h ? cv2 : cv);
-        xv[tt][h] = ok ? V8<E>::load(xbase, tkc * xstride + cl + 8 * h) : V8<E>::zero();
-        hv[tt][h] = ok ? V8<E>::load(dhin, tkc * C + cl + 8 * h) : V8<E>::zero();
-        dv[tt][h] = (ok && !active_grp) ? V8<E>::load(dXn, (tkc * N + srow) * C + cl + 8 * h) : V8<E>::zero();
-      }
-      const float* co = coef + tkc * COEF_STRIDE;
-      hpre[tt] = co[CO_PRE + srow];
-      gam[tt] = co[CO_GAMMA];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) hres[tt][a] = (active_grp && a < k) ? co[CO_RES + a * 4 + wave] : 0.f;
-    }
-    // active group: pass term sum_a H_res[a][wave] G_a
-    float pass[2][16];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float d[8];
-        dv[tt][h].to_float(d);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) pass[tt][8 * h + q] = d[q];
-      }
-    }
-    if (active_grp) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int tk = t0 + 16 * tt + r16;
-        const bool tv = tk < T;
-        const size_t tkc = tv ? tk : 0;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) pass[tt][q] = 0.f;
+        for (int q = 0; q < 8; ++q) pass[q] = 0.f;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           if (a < k) {
+            const float h = cor[CO_RES + a * 4 + wave];
+            const V8<E> gv = *reinterpret_cast<const V8<E>*>(&gsh[a][r16][g4 * (8 * E::bytes / 16)]);
+            float gf[8];
+            gv.to_float(gf);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const bool ok = tv && (h ? cv2 : cv);
-              V8<E> gv = ok ? V8<E>::load(dXn, (tkc * N + act.id[a]) * C + cl + 8 * h) : V8<E>::zero();
-              float gf[8];
-              gv.to_float(gf);
-#pragma unroll
-              for (int q = 0; q < 8; ++q) pass[tt][8 * h + q] = fmaf(hres[tt][a], gf[q], pass[tt][8 * h + q]);
-            }
+            for (int q = 0; q < 8; ++q) pass[q] = fmaf(h, gf[q], pass[q]);
           }
         }
-      }
-      __syncthreads();   // every G row of the tile is read before any dX row is written
-    }
-    // ---- assemble and store dX; stage X into LDS for the dW operand ----
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int tk = t0 + 16 * tt + r16;
-      const bool tv = tk < T;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float xf[8], hf[8], o[8];
-        xv[tt][h].to_float(xf);
-        hv[tt][h].to_float(hf);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int cidx = 8 * h + q;                 // channel offset within the lane's 16
-          const int jt = (cidx >> 2) & 3, e = cidx & 3;
-          float v = pass[tt][cidx];
-          v = fmaf(hpre[tt], hf[q], v);
-          v += pj[jt][tt][e];
-          v = fmaf(-gam[tt], xf[q], v);
-          o[q] = v;
-        }
-        if (tv && (h ? cv2 : cv)) V8<E>::from_float(o).store(dX, ((size_t)tk * N + srow) * C + cl + 8 * h);
-        *reinterpret_cast<V8<E>*>(&xs[16 * tt + r16][(16 * g4 + 8 * h) * E::bytes]) = xv[tt][h];
-      }
-    }
-    __syncthreads();
-    // ---- dW on MFMA: A = X^T (rows = channels, K = 32 tokens) ----
-    V8<E> bh[3], bl[3];
-#pragma unroll
-    for (int pt = 0; pt < 3; ++pt) {
-      const size_t off = (size_t)(16 * pt + r16) * Tpad + t0 + 8 * g4;
-      bh[pt] = V8<E>::load(dzrt, off);
-      if constexpr (BF) bl[pt] = V8<E>::load(dzrt, off + (size_t)48 * Tpad);
-    }
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      V8<E> xa;
-      if constexpr (BF) {
-        const uint16_t* col = reinterpret_cast<const uint16_t*>(&xs[0][0]) + 16 * jt + r16;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const unsigned lo16 = col[(size_t)(8 * g4 + 2 * q) * XS_LD];
-          const unsigned hi16 = col[(size_t)(8 * g4 + 2 * q + 1) * XS_LD];
-          xa.w[q] = lo16 | (hi16 << 16);
-        }
       } else {
-        const float* col = reinterpret_cast<const float*>(&xs[0][0]) + 16 * jt + r16;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) reinterpret_cast<float*>(&xa)[q] = col[(size_t)(8 * g4 + q) * XS_LD];
+        dvc.to_float(pass);
       }
+      const V8<E> hv = *reinterpret_cast<const V8<E>*>(
+          &sg[SG::o_dh + r16 * (B2_CB * E::bytes / 16) + g4 * (8 * E::bytes / 16)]);
+      float xf[8], hf[8], o[8];
+      xc.to_float(xf);
+      hv.to_float(hf);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int jt = q >> 2, e = q & 3;              // channel 8*g4 + q = 8*g4 + 4*jt + e
+        float v = pass[q];
+        v = fmaf(hpre, hf[q], v);
+        v += pj[jt][e];
+        v = fmaf(-gam, xf[q], v);
+        o[q] = v;
+      }
+      if (tv && cv) V8<E>::from_float(o).store(dX, ((size_t)tk * N + srow) * C + cl);
+    }
+    // ---- dW on MFMA: A = X^T (rows = channels, K = 16 tokens) ----
+    {
+      Vec<E, 4> bh[3], bl[3];
 #pragma unroll
       for (int pt = 0; pt < 3; ++pt) {
-        dwacc[jt][pt] = mma32(xa, bh[pt], dwacc[jt][pt]);
-        if constexpr (BF) dwacc[jt][pt] = mma32(xa, bl[pt], dwacc[jt][pt]);
+        const int p = 16 * pt + r16;
+        const unsigned char* rowh = reinterpret_cast<const unsigned char*>(&sg[SG::o_dzrt_hi]) + (size_t)p * B2_TT * E::bytes;
+        bh[pt] = *reinterpret_cast<const Vec<E, 4>*>(rowh + 4 * g4 * E::bytes);
+        if constexpr (BF) {
+          const unsigned char* rowl = reinterpret_cast<const unsigned char*>(&sg[SG::o_dzrt_lo]) + (size_t)p * B2_TT * E::bytes;
+          bl[pt] = *reinterpret_cast<const Vec<E, 4>*>(rowl + 4 * g4 * E::bytes);
+        }
+      }
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        Vec<E, 4> xa;
+        if constexpr (BF) {
+          const uint16_t* col = reinterpret_cast<const uint16_t*>(&xsh[wave][0][0]) + 16 * jt + r16;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const unsigned lo16 = col[(size_t)(4 * g4 + 2 * q) * XS_LD];
+            const unsigned hi16 = col[(size_t)(4 * g4 + 2 * q + 1) * XS_LD];
+            xa.w[q] = lo16 | (hi16 << 16);
+          }
+        } else {
+          const float* col = reinterpret_cast<const float*>(&xsh[wave][0][0]) + 16 * jt + r16;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xa.x[q] = col[(size_t)(4 * g4 + q) * XS_LD];
+        }
+#pragma unroll
+        for (int pt = 0; pt < 3; ++pt) {
+          dwacc[jt][pt] = mma16(xa, bh[pt], dwacc[jt][pt]);
+          if constexpr (BF) dwacc[jt][pt] = mma16(xa, bl[pt], dwacc[jt][pt]);
+        }
       }
     }
+    if (more) store_shared(buf ^ 1);
     __syncthreads();
   }
   // dW partial rows: D row 4*g4+e of j-tile jt = channel 16*jt + 4*g4 + e
   if (wv) {
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
+    for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ch = 16 * jt + 4 * g4 + e;
@@ -790,7 +861,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
     }
     const int nb = p.b2_rowgroups * p.b2_cblocks * p.b2_ts;
     k_bgrad<E><<<nb, 256, 0, st>>>(src, a->dX_new, a->dh_in, coef, Wp, dzr, dzrt, a->dX, dwp, p.T, p.Tpad, p.C,
-                                   p.N, p.k, act, rows, p.b2_rowgroups, p.b2_cblocks, p.b2_tok_per_split);
+                                   p.N, p.k, rows, p.b2_rowgroups, p.b2_cblocks, p.b2_tok_per_split);
   }
   {
     TimedLaunch tl(tm, KID_BREDUCE, st);

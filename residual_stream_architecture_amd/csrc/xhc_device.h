@@ -145,6 +145,20 @@ __device__ inline f32x4 mma32(const V8<F32>& a, const V8<F32>& b, f32x4 c) {
   return c;
 }
 
+// One K=16 step of a 16x16 MFMA: lane l holds row/column l%16 and the 4
+// K-elements of group l/16 (bf16: 16x16x16; fp32: four 16x16x4 steps).
+__device__ inline f32x4 mma16(const Vec<BF16, 4>& a, const Vec<BF16, 4>& b, f32x4 c) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  u32x2 ra = {a.w[0], a.w[1]}, rb = {b.w[0], b.w[1]};
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, ra), __builtin_bit_cast(s16x4, rb), c,
+                                                   0, 0, 0);
+}
+__device__ inline f32x4 mma16(const Vec<F32, 4>& a, const Vec<F32, 4>& b, f32x4 c) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f(s), b.f(s), c, 0, 0, 0);
+  return c;
+}
+
 // Split an fp32 value into bf16 hi + lo (hi = RNE(x), lo = RNE(x - hi)):
 // hi + lo carries ~16 significant bits, enough for fp32-accurate products.
 __device__ inline void split_bf16(float x, __bf16& hi, __bf16& lo) {

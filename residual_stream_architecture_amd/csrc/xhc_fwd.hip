@@ -18,79 +18,131 @@
 namespace xhc {
 
 // ---------------------------------------------------------------------------
-// W [NC, P] (row j = i*C + c) -> Wt [NTP, NC], rows p >= P zero.
+// W [NC, P] (row j = i*C + c) -> Wf, the MFMA B operand in fragment order:
+// for stream i, K-step ks (channels ks*32 .. ks*32+32 of the stream) and
+// logit tile n, one 512-element block in which lane l holds the 8 channels
+// 8*(l/16) .. +8 of logit column 16n + l%16.  A wave then loads one B
+// fragment as one contiguous 1 KiB access.  Entries past C or P are zero.
 // ---------------------------------------------------------------------------
 template <typename R>
-__global__ void k_pack_wt(const R* __restrict__ W, R* __restrict__ Wt, int64_t NC, int P, int NTP) {
-  int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= NC) return;
-  for (int p = 0; p < NTP; ++p) Wt[(size_t)p * NC + j] = p < P ? W[(size_t)j * P + p] : R(0);
+__global__ void k_pack_wt(const R* __restrict__ W, R* __restrict__ Wf, int C, int P, int NT, int nks, int64_t nfrag) {
+  const int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (i, ks, n, lane)
+  if (f >= nfrag) return;
+  const int lane = (int)(f & 63);
+  const int64_t blk = f >> 6;
+  const int n = (int)(blk % NT);
+  const int64_t iks = blk / NT;
+  const int ks = (int)(iks % nks);
+  const int64_t i = iks / nks;
+  const int p = 16 * n + (lane & 15);
+  const int c0 = ks * 32 + 8 * (lane >> 4);
+  R* dst = Wf + f * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = c0 + e;
+    dst[e] = (p < P && c < C) ? W[((size_t)i * C + c) * P + p] : R(0);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Projection partials.  Workgroup = (stream `split`, tile of 64 tokens);
-// wave w owns tokens tile*64 + 16w .. +16 as MFMA rows; columns are the NT
-// 16-wide logit tiles.  The K loop runs over the stream's C channels in
-// steps of 32 (lane group g = lane/16 holds K elements 8g..8g+8 of a step).
+// Projection partials.  Workgroup = (stream `split`, tile of PROJ_TOK
+// tokens); wave w owns two 16-token MFMA row blocks (tokens base + 16f + l%16,
+// f = 0, 1).  The K loop walks the stream's channels 64 at a time (two
+// K=32 MFMA steps), loading the next 64 while the current ones multiply.
 // Stream rows come from `src` (the state, or after an in-place forward the
 // saved active rows for the active streams).
 // Output zpart[split][t][0..16NT) = sum_c X[t,split,c] W[split*C+c, p],
 //        zpart[split][t][16NT]    = sum_c X[t,split,c]^2.
 // ---------------------------------------------------------------------------
 template <typename E, int NT>
-__global__ __launch_bounds__(256) void k_proj(StreamRows src, const void* __restrict__ Wt,
-                                              float* __restrict__ zpart, int T, int C, int64_t NC,
-                                              int ZST, int ntiles) {
-  constexpr int U = 4;
+__global__ __launch_bounds__(256) void k_proj(StreamRows src, const void* __restrict__ Wf,
+                                              float* __restrict__ zpart, int T, int C, int ZST, int ntiles) {
+  constexpr int U = 2;                       // K=32 steps per stage
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int split = lb / ntiles;
   const int tile = lb - split * ntiles;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int t = tile * PROJ_TOK + wave * 16 + r;
-  const bool tv = t < T;
+  const int tbase = tile * PROJ_TOK + wave * 32;
   const void* X = src.base[split];
-  const size_t xrow = (size_t)(tv ? t : 0) * src.stride[split];
-  const size_t wcol = (size_t)split * C;
-
-  f32x4 acc[NT];
+  const int64_t xs = src.stride[split];
+  size_t xrow[2];
+  bool tv[2];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ss = 0.f;
-
-  const int nks = (C + 31) >> 5;
-  for (int ks = 0; ks < nks; ks += U) {
-    V8<E> a[U], b[U][NT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kb = (ks + u) * 32 + 8 * g;
-      const bool kv = (ks + u) < nks && kb < C;
-      a[u] = (kv && tv) ? V8<E>::load(X, xrow + kb) : V8<E>::zero();
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-        b[u][n] = kv ? V8<E>::load(Wt, (size_t)(16 * n + r) * NC + wcol + kb) : V8<E>::zero();
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) { const float v = a[u].f(j); ss = fmaf(v, v, ss); }
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] = mma32(a[u], b[u][n], acc[n]);
-    }
+  for (int f = 0; f < 2; ++f) {
+    const int t = tbase + 16 * f + r;
+    tv[f] = t < T;
+    xrow[f] = (size_t)(tv[f] ? t : 0) * xs;
   }
-  ss += shfl_xor(ss, 16);
-  ss += shfl_xor(ss, 32);
+  const int nks = (C + 31) >> 5;
+  const size_t wbase = (size_t)split * nks * NT * 512 + (size_t)lane * 8;
 
+  f32x4 acc[2][NT];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[f][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss[2] = {0.f, 0.f};
+
+  V8<E> a[2][U][2], b[2][U][NT];
+  auto load_stage = [&](int buf, int ks0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = ks0 + u;
+      const int kb = ks * 32 + 8 * g;
+      const bool kv = ks < nks && kb < C;
+      const int kc = kv ? kb : 0;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        V8<E> v = V8<E>::load(X, xrow[f] + kc);
+        a[buf][u][f] = (kv && tv[f]) ? v : V8<E>::zero();
+      }
+      const int kw = ks < nks ? ks : 0;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) b[buf][u][n] = V8<E>::load(Wf, wbase + ((size_t)kw * NT + n) * 512);
+    }
+  };
+  auto compute_stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { const float v = a[buf][u][f].f(j); ss[f] = fmaf(v, v, ss[f]); }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[f][n] = mma32(a[buf][u][f], b[buf][u][n], acc[f][n]);
+      }
+    }
+  };
+
+  load_stage(0, 0);
+  int ks0 = 0;
+  for (; ks0 + U < nks; ks0 += 2 * U) {
+    load_stage(1, ks0 + U);
+    compute_stage(0);
+    if (ks0 + 2 * U < nks) load_stage(0, ks0 + 2 * U);
+    compute_stage(1);
+  }
+  if (ks0 < nks) compute_stage(0);
+
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    ss[f] += shfl_xor(ss[f], 16);
+    ss[f] += shfl_xor(ss[f], 32);
+  }
   float* zp = zpart + (size_t)split * T * ZST;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int tt = tile * PROJ_TOK + wave * 16 + 4 * g + e;     // D row 4g+e
-    if (tt < T) {
+  for (int f = 0; f < 2; ++f) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n) zp[(size_t)tt * ZST + 16 * n + r] = acc[n][e];
+    for (int e = 0; e < 4; ++e) {
+      const int tt = tbase + 16 * f + 4 * g + e;     // D row 4g+e of block f
+      if (tt < T) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) zp[(size_t)tt * ZST + 16 * n + r] = acc[f][n][e];
+      }
     }
+    if (g == 0 && tv[f]) zp[(size_t)(tbase + 16 * f + r) * ZST + 16 * NT] = ss[f];
   }
-  if (g == 0 && tv) zp[(size_t)t * ZST + 16 * NT] = ss;
 }
 
 // ---------------------------------------------------------------------------
@@ -176,137 +228,140 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
 
 // ---------------------------------------------------------------------------
 // Dense read + TFA + sparse write.  Thread = MIX_CH consecutive channels of
-// one sequence segment of MIX_LSEG tokens, swept in order.  The last 12 rows
-// of `out` live in a register ring indexed by position mod 12 (segments start
-// at multiples of 12, so the index is a compile-time constant in the
-// 12-fold unrolled loop).  All reads of a token's rows happen before its
-// writes, so X_new == X (in place) is safe.
+// one sequence segment [s0, s1), swept in order.  The last 12 rows of `out`
+// live in a register window that shifts by one row per token (window[11] is
+// the current position, window[11-l] the position l back).  The next token's
+// rows are loaded before the current token is computed and stored: loads of
+// token s+1 never alias the rows written for token s, so X_new == X (in
+// place) stays safe and every load batch overlaps the previous token's work.
+// FULLN: N == 16 (rows unconditional); otherwise rows i >= N are skipped.
 // ---------------------------------------------------------------------------
 struct Active { int id[4]; };
 
-template <typename E, int NCOMP>
+template <typename E, int NCOMP, bool FULLN>
 __global__ __launch_bounds__(MIX_THREADS) void k_mix(
     const void* __restrict__ X, const void* __restrict__ out, const float* __restrict__ w4,
     const float* __restrict__ w8, const float* __restrict__ w12, const float* __restrict__ coef,
     void* Xnew, void* __restrict__ hin, void* __restrict__ xact, int S, int C, int N, int k,
-    Active act, int in_place, int segs_per_seq) {
+    Active act, int in_place, int lseg, int segs_per_seq) {
   using V = Vec<E, MIX_CH>;
-  const int c = (blockIdx.x * MIX_THREADS + threadIdx.x) * MIX_CH;
-  const bool cv = c < C;
+  const int craw = (blockIdx.x * MIX_THREADS + threadIdx.x) * MIX_CH;
+  const bool cv = craw < C;
+  const int c = cv ? craw : 0;                  // clamped: idle lanes read valid memory
   const int seg = blockIdx.y;
   const int bseq = seg / segs_per_seq;
-  const int s0 = (seg - bseq * segs_per_seq) * MIX_LSEG;
-  const int s1 = min(s0 + MIX_LSEG, S);
+  const int s0 = (seg - bseq * segs_per_seq) * lseg;
+  const int s1 = min(s0 + lseg, S);
   const size_t tok0 = (size_t)bseq * S;
+  const int NR = FULLN ? 16 : N;
 
-  float wa[MIX_CH][4], wb[MIX_CH][8], wc[MIX_CH][12];
-  if (NCOMP == 4) {
+  float wk[MIX_CH][24];
+  if constexpr (NCOMP == 4) {
 #pragma unroll
     for (int ch = 0; ch < MIX_CH; ++ch) {
-      const int cc = cv ? c + ch : 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wa[ch][q] = w4[(size_t)cc * 4 + q];
+      for (int q = 0; q < 4; ++q) wk[ch][q] = w4[(size_t)(c + ch) * 4 + q];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) wb[ch][q] = w8[(size_t)cc * 8 + q];
+      for (int q = 0; q < 8; ++q) wk[ch][4 + q] = w8[(size_t)(c + ch) * 8 + q];
 #pragma unroll
-      for (int q = 0; q < 12; ++q) wc[ch][q] = w12[(size_t)cc * 12 + q];
+      for (int q = 0; q < 12; ++q) wk[ch][12 + q] = w12[(size_t)(c + ch) * 12 + q];
     }
   }
-
-  float ring[12][MIX_CH];
+  // before the first shift, slot j+1 holds position s0-11+j (zero before the
+  // sequence start)
+  float win[12][MIX_CH];
 #pragma unroll
-  for (int j = 0; j < 12; ++j) {
-    const int s = s0 - 12 + j;
-    if (NCOMP == 4 && j > 0 && s >= 0 && cv) {
-      V v = V::load(out, (tok0 + s) * C + c);
-      v.to_float(ring[j]);
-    } else {
+  for (int ch = 0; ch < MIX_CH; ++ch) win[0][ch] = 0.f;
 #pragma unroll
-      for (int ch = 0; ch < MIX_CH; ++ch) ring[j][ch] = 0.f;
-    }
+  for (int j = 0; j < 11; ++j) {
+    const int s = s0 - 11 + j;
+    V v = (NCOMP == 4 && s >= 0) ? V::load(out, (tok0 + (s >= 0 ? s : 0)) * C + c) : V::zero();
+    v.to_float(win[j + 1]);
   }
 
-  for (int g0 = s0; g0 < s1; g0 += 12) {
+  // prefetch buffers: the 16 state rows and the out row of the next token
+  V xr[16], ov;
+  auto load_token = [&](int s) {
+    const size_t t = tok0 + s;
 #pragma unroll
-    for (int j = 0; j < 12; ++j) {
-      const int s = g0 + j;
-      if (s < s1) {
-        const size_t t = tok0 + s;
-        const float* co = coef + t * COEF_STRIDE;
-        if (cv) {
-          V ov = V::load(out, t * C + c);
-          ov.to_float(ring[j]);
-          float hacc[MIX_CH], o[4][MIX_CH], xa_keep[4][MIX_CH];
-          V xa_raw[4];
-#pragma unroll
-          for (int ch = 0; ch < MIX_CH; ++ch) {
-            hacc[ch] = 0.f;
-#pragma unroll
-            for (int a = 0; a < 4; ++a) o[a][ch] = 0.f;
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            if (i < N) {
-              V xv = V::load(X, (t * N + i) * C + c);
-              float xf[MIX_CH];
-              xv.to_float(xf);
-              const float hp = co[CO_PRE + i];
-#pragma unroll
-              for (int ch = 0; ch < MIX_CH; ++ch) hacc[ch] = fmaf(hp, xf[ch], hacc[ch]);
-#pragma unroll
-              for (int b = 0; b < 4; ++b) {
-                if (b < k && i == act.id[b]) {
-                  xa_raw[b] = xv;
-#pragma unroll
-                  for (int ch = 0; ch < MIX_CH; ++ch) xa_keep[b][ch] = xf[ch];
-                }
-              }
-              if (!in_place) {
-                bool is_act = false;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) is_act |= (b < k && i == act.id[b]);
-                if (!is_act) xv.store(Xnew, (t * N + i) * C + c);
-              }
-            }
-          }
-          V::from_float(hacc).store(hin, t * C + c);
+    for (int i = 0; i < 16; ++i)
+      if (FULLN || i < NR) xr[i] = V::load(X, (t * N + i) * C + c);
+    ov = V::load(out, t * C + c);
+  };
+  if (s0 < s1) load_token(s0);
 
-          // write-back components U_0..U_{NCOMP-1}
-          float u[4][MIX_CH];
+  for (int s = s0; s < s1; ++s) {
+    const size_t t = tok0 + s;
+    V cx[16], co_out = ov;
 #pragma unroll
-          for (int ch = 0; ch < MIX_CH; ++ch) {
-            u[0][ch] = ring[j][ch];
-            if (NCOMP == 4) {
-              float s4 = 0.f, s8 = 0.f, s12 = 0.f;
+    for (int i = 0; i < 16; ++i) cx[i] = xr[i];
+    load_token(s + 1 < s1 ? s + 1 : s);          // next token (the last iteration reloads, harmlessly)
+
+    const float* co = coef + t * COEF_STRIDE;
 #pragma unroll
-              for (int q = 0; q < 4; ++q) s4 = fmaf(wa[ch][q], ring[(j + 12 - 3 + q) % 12][ch], s4);
+    for (int j = 0; j < 11; ++j)
 #pragma unroll
-              for (int q = 0; q < 8; ++q) s8 = fmaf(wb[ch][q], ring[(j + 12 - 7 + q) % 12][ch], s8);
+      for (int ch = 0; ch < MIX_CH; ++ch) win[j][ch] = win[j + 1][ch];
+    co_out.to_float(win[11]);
+
+    float hacc[MIX_CH], xa[4][MIX_CH];
 #pragma unroll
-              for (int q = 0; q < 12; ++q) s12 = fmaf(wc[ch][q], ring[(j + 12 - 11 + q) % 12][ch], s12);
-              u[1][ch] = s4; u[2][ch] = s8; u[3][ch] = s12;
-            }
+    for (int ch = 0; ch < MIX_CH; ++ch) hacc[ch] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (FULLN || i < NR) {
+        float xf[MIX_CH];
+        cx[i].to_float(xf);
+        const float hp = co[CO_PRE + i];
+#pragma unroll
+        for (int ch = 0; ch < MIX_CH; ++ch) hacc[ch] = fmaf(hp, xf[ch], hacc[ch]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (b < k && i == act.id[b]) {
+#pragma unroll
+            for (int ch = 0; ch < MIX_CH; ++ch) xa[b][ch] = xf[ch];
+            if (xact && cv) cx[i].store(xact, (t * k + b) * C + c);
           }
-          // sparse write of the k active rows
+        if (!in_place && cv) {
+          bool is_act = false;
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            if (a < k) {
-              float res[MIX_CH];
-#pragma unroll
-              for (int ch = 0; ch < MIX_CH; ++ch) {
-                float v = 0.f;
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                  if (b < k) v = fmaf(co[CO_RES + a * 4 + b], xa_keep[b][ch], v);
-#pragma unroll
-                for (int m = 0; m < NCOMP; ++m) v = fmaf(co[CO_POST + a * 4 + m], u[m][ch], v);
-                res[ch] = v;
-              }
-              if (xact) xa_raw[a].store(xact, (t * k + a) * C + c);
-              V::from_float(res).store(Xnew, (t * N + act.id[a]) * C + c);
-            }
-          }
+          for (int b = 0; b < 4; ++b) is_act |= (b < k && i == act.id[b]);
+          if (!is_act) cx[i].store(Xnew, (t * N + i) * C + c);
         }
+      }
+    }
+    if (cv) V::from_float(hacc).store(hin, t * C + c);
+
+    float u[4][MIX_CH];
+#pragma unroll
+    for (int ch = 0; ch < MIX_CH; ++ch) {
+      u[0][ch] = win[11][ch];
+      if constexpr (NCOMP == 4) {
+        float s4 = 0.f, s8 = 0.f, s12 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s4 = fmaf(wk[ch][q], win[8 + q][ch], s4);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s8 = fmaf(wk[ch][4 + q], win[4 + q][ch], s8);
+#pragma unroll
+        for (int q = 0; q < 12; ++q) s12 = fmaf(wk[ch][12 + q], win[q][ch], s12);
+        u[1][ch] = s4; u[2][ch] = s8; u[3][ch] = s12;
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      if (a < k) {
+        float res[MIX_CH];
+#pragma unroll
+        for (int ch = 0; ch < MIX_CH; ++ch) {
+          float v = 0.f;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (b < k) v = fmaf(co[CO_RES + a * 4 + b], xa[b][ch], v);
+#pragma unroll
+          for (int m = 0; m < NCOMP; ++m) v = fmaf(co[CO_POST + a * 4 + m], u[m][ch], v);
+          res[ch] = v;
+        }
+        if (cv) V::from_float(res).store(Xnew, (t * N + act.id[a]) * C + c);
       }
     }
   }
@@ -316,23 +371,25 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
 // launchers
 // ---------------------------------------------------------------------------
 template <typename R>
-static void launch_pack_wt(const Plan& p, const void* W, void* Wt, hipStream_t st, xhc_timer* tm) {
+static void launch_pack_wt(const Plan& p, const void* W, void* Wf, hipStream_t st, xhc_timer* tm) {
   TimedLaunch tl(tm, KID_PACK_WT, st);
-  const int nb = (int)((p.NC + 255) / 256);
-  k_pack_wt<R><<<nb, 256, 0, st>>>(static_cast<const R*>(W), static_cast<R*>(Wt), p.NC, p.P, p.NT * 16);
+  const int nks = (p.C + 31) / 32;
+  const int64_t nfrag = (int64_t)p.N * nks * p.NT * 64;
+  k_pack_wt<R><<<(int)((nfrag + 255) / 256), 256, 0, st>>>(static_cast<const R*>(W), static_cast<R*>(Wf), p.C, p.P,
+                                                           p.NT, nks, nfrag);
 }
 
 template <typename E>
-static void launch_proj(const Plan& p, const StreamRows& src, const void* Wt, float* zpart, hipStream_t st,
+static void launch_proj(const Plan& p, const StreamRows& src, const void* Wf, float* zpart, hipStream_t st,
                         xhc_timer* tm) {
   TimedLaunch tl(tm, KID_PROJ, st);
   const int nb = p.proj_tiles * p.SK;
   if (p.NT == 1)
-    k_proj<E, 1><<<nb, 256, 0, st>>>(src, Wt, zpart, p.T, p.C, p.NC, p.ZST, p.proj_tiles);
+    k_proj<E, 1><<<nb, 256, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles);
   else if (p.NT == 2)
-    k_proj<E, 2><<<nb, 256, 0, st>>>(src, Wt, zpart, p.T, p.C, p.NC, p.ZST, p.proj_tiles);
+    k_proj<E, 2><<<nb, 256, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles);
   else
-    k_proj<E, 3><<<nb, 256, 0, st>>>(src, Wt, zpart, p.T, p.C, p.NC, p.ZST, p.proj_tiles);
+    k_proj<E, 3><<<nb, 256, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles);
 }
 
 template <typename E, typename R>
@@ -357,13 +414,16 @@ static int forward_impl(const Plan& p, const xhc_fwd_args* a, char* ws, hipStrea
     for (int b = 0; b < 4; ++b) act.id[b] = b < p.k ? a->active[b] : -1;
     dim3 grid(p.mix_cblocks, p.B * p.mix_segs);
     const int in_place = a->X_new == a->X;
-    if (p.nc == 4)
-      k_mix<E, 4><<<grid, MIX_THREADS, 0, st>>>(a->X, a->out, a->w4, a->w8, a->w12, coef, a->X_new, a->h_in,
-                                                a->xact_save, p.S, p.C, p.N, p.k, act, in_place, p.mix_segs);
-    else
-      k_mix<E, 1><<<grid, MIX_THREADS, 0, st>>>(a->X, a->out, nullptr, nullptr, nullptr, coef, a->X_new,
-                                                a->h_in, a->xact_save, p.S, p.C, p.N, p.k, act, in_place,
-                                                p.mix_segs);
+#define XHC_MIX(NCOMP, FULLN)                                                                              \
+  k_mix<E, NCOMP, FULLN><<<grid, MIX_THREADS, 0, st>>>(a->X, a->out, a->w4, a->w8, a->w12, coef, a->X_new, \
+                                                       a->h_in, a->xact_save, p.S, p.C, p.N, p.k, act,      \
+                                                       in_place, p.mix_lseg, p.mix_segs)
+    if (p.nc == 4) {
+      if (p.N == 16) XHC_MIX(4, true); else XHC_MIX(4, false);
+    } else {
+      if (p.N == 16) XHC_MIX(1, true); else XHC_MIX(1, false);
+    }
+#undef XHC_MIX
   }
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
 }

@@ -24,15 +24,16 @@ constexpr int CO_PRE = 0, CO_POST = 16, CO_RES = 32, CO_R = 48, CO_GAMMA = 49;
 //   [32, 48)  dH_post[a*4+m] = <G_a, U_m>
 constexpr int DOT_STRIDE = 48;
 
-constexpr int PROJ_TOK = 64;      // tokens per projection workgroup (4 waves x 16)
-constexpr int MIX_CH = 4;         // channels per thread in the mix kernel
-constexpr int MIX_THREADS = 128;
-constexpr int MIX_LSEG = 48;      // tokens per mix thread (multiple of 12)
+constexpr int PROJ_TOK = 128;     // tokens per projection workgroup (4 waves x 32)
+constexpr int MIX_CH = 2;         // channels per thread in the mix kernel
+constexpr int MIX_THREADS = 256;
+constexpr int MIX_TARGET_WAVES = 2560;   // grid size aimed at ~one resident round
 constexpr int B1_CH = 2;          // channels per lane in B1's TFA part
 constexpr int B1_WAVE_CH = 128;   // channels per B1 wave (64 lanes x 2)
 constexpr int B1_WAVES = 4;       // waves per B1 workgroup (consecutive chunks)
-constexpr int B2_CB = 64;         // channels per B2 wave row
-constexpr int B2_TT = 32;         // tokens per B2 tile
+constexpr int B2_CB = 32;         // channels per B2 wave row
+constexpr int B2_TT = 16;         // tokens per B2 tile
+constexpr int B2_TARGET_WG = 1536;  // B2 grid aimed at two rounds of 3 workgroups per CU
 
 struct Plan {
   int B, S, C, N, k, nc, P, NT, T, iters, dtype, gate;
@@ -44,6 +45,7 @@ struct Plan {
   int ZST;            // floats per (split, token) partial record
   int proj_tiles;     // token tiles of PROJ_TOK
   int mix_cblocks;    // channel blocks of MIX_THREADS*MIX_CH
+  int mix_lseg;       // tokens per mix segment
   int mix_segs;       // segments per sequence
   // backward
   int b1_cblocks;     // channel blocks of B1_WAVES*B1_WAVE_CH
