@@ -23,6 +23,7 @@ FLAGS = [
     # window index stays a compile-time register index
     "-mllvm", "-pragma-unroll-threshold=100000",
     "-Wno-unused-result",
+    "-I" + os.path.join(ROOT, "include"),
 ]
 
 

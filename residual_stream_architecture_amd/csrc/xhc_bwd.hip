@@ -62,15 +62,19 @@ __global__ void k_pack_wp(const R* __restrict__ W, R* __restrict__ Wp, int64_t N
 // loads are unconditional (clamped addresses, masked values) and the next
 // token's loads are issued before the current token's arithmetic.
 // ---------------------------------------------------------------------------
-template <typename E, int NCOMP>
+template <typename E, int NCOMP, bool FAST>
 __global__ __launch_bounds__(256) void k_bdots(
     StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin,
     const void* __restrict__ out, const float* __restrict__ w4, const float* __restrict__ w8,
     const float* __restrict__ w12, const float* __restrict__ coef, float* __restrict__ dpart,
-    void* __restrict__ dout, float* __restrict__ dwpart, int T, int S, int C, int N, int k, Act4 act,
+    void* __restrict__ dout, float* __restrict__ dwpart, int T, int S, int C, int N, int kk, Act4 act,
     int lseg, int segs_per_seq) {
   using V2 = Vec<E, B1_CH>;
+  constexpr int EB = E::bytes;
   __shared__ float red[B1_WAVES][12][DOT_STRIDE];
+  const int k = FAST ? 4 : kk;
+  (void)N;
+  const int NS = FAST ? 16 : N;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cblock = blockIdx.x;
@@ -81,18 +85,23 @@ __global__ __launch_bounds__(256) void k_bdots(
   const int s1 = min(s0 + lseg, S);
   const int tend = s1 + 11;
   const size_t tok0 = (size_t)bseq * S;
+  const uint32_t rowb = (uint32_t)C * EB;
+  const uint32_t tokb = (uint32_t)NS * rowb;
 
   // TFA lane channels (clamped for idle lanes)
   const int clraw = c0 + B1_CH * lane;
   const bool cv = clraw < C;
   const int cl = cv ? clraw : 0;
+  const uint32_t voff = (uint32_t)cl * EB;
   // MFMA lane roles: A row r16 = stream r16; B column r16: 0 = dh_in, 1..k = G
   const int r16 = lane & 15, g4 = lane >> 4;
-  const bool arow_valid = r16 < N;
-  const void* arow_base = src.base[arow_valid ? r16 : 0];
-  const int64_t arow_stride = src.stride[arow_valid ? r16 : 0];
+  const bool arow_valid = r16 < NS;
+  const char* abase = static_cast<const char*>(src.base[arow_valid ? r16 : 0]);
+  const size_t astride = (size_t)src.stride[arow_valid ? r16 : 0] * EB;
   const bool bcol_valid = r16 <= k;
   const int bcol_row = (r16 >= 1 && r16 <= k) ? act.id[r16 - 1] : 0;
+  const char* bbase = r16 == 0 ? static_cast<const char*>(dhin) : static_cast<const char*>(dXn) + (size_t)bcol_row * rowb;
+  const size_t bstride = r16 == 0 ? rowb : tokb;
 
   float wk[B1_CH][24];
   if constexpr (NCOMP == 4) {
@@ -106,6 +115,7 @@ __global__ __launch_bounds__(256) void k_bdots(
       for (int q = 0; q < 12; ++q) wk[ch][12 + q] = w12[(size_t)(cl + ch) * 12 + q];
     }
   }
+  const rsrc_t rout = make_rsrc(static_cast<const char*>(out) + tok0 * rowb, (uint32_t)S * rowb);
   float win[12][B1_CH], dacc[12][B1_CH], dw[B1_CH][24];
 #pragma unroll
   for (int j = 0; j < 12; ++j)
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(256) void k_bdots(
 #pragma unroll
     for (int j = 0; j < 11; ++j) {
       const int s = s0 - 11 + j;
-      V2 v = V2::load(out, (tok0 + (s >= 0 ? s : 0)) * C + cl);
+      V2 v = bload<E, B1_CH>(rout, voff, (uint32_t)(s >= 0 ? s : 0) * rowb);
       float f[B1_CH];
       v.to_float(f);
 #pragma unroll
@@ -132,21 +142,24 @@ __global__ __launch_bounds__(256) void k_bdots(
   V2 gv[4], ov;
   auto load_mfma = [&](int s) {
     const size_t t = tok0 + min(s, S - 1);
+    const char* ap = abase + t * astride;
+    const char* bp = bbase + t * bstride;
 #pragma unroll
     for (int ks = 0; ks < B1_WAVE_CH / 32; ++ks) {
       const int cc = c0 + ks * 32 + 8 * g4;
       const int ccl = cc < C ? cc : 0;
-      av[ks] = V8<E>::load(arow_base, t * arow_stride + ccl);
-      bv[ks] = (r16 == 0) ? V8<E>::load(dhin, t * C + ccl) : V8<E>::load(dXn, (t * N + bcol_row) * C + ccl);
+      av[ks] = *reinterpret_cast<const V8<E>*>(ap + (size_t)ccl * EB);
+      bv[ks] = *reinterpret_cast<const V8<E>*>(bp + (size_t)ccl * EB);
       if (!(cc < C && arow_valid)) av[ks] = V8<E>::zero();
       if (!(cc < C && bcol_valid)) bv[ks] = V8<E>::zero();
     }
   };
   auto load_tfa = [&](int s) {
     const size_t t = tok0 + min(s, S - 1);
+    const rsrc_t rg = make_rsrc(static_cast<const char*>(dXn) + t * tokb, tokb);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) gv[a] = V2::load(dXn, (t * N + act.id[a < k ? a : 0]) * C + cl);
-    ov = V2::load(out, t * C + cl);
+    for (int a = 0; a < 4; ++a) gv[a] = bload<E, B1_CH>(rg, voff, (uint32_t)act.id[a < k ? a : 0] * rowb);
+    ov = bload<E, B1_CH>(rout, voff, (uint32_t)min(s, S - 1) * rowb);
   };
   load_mfma(s0);
   load_tfa(s0);
@@ -197,10 +210,15 @@ __global__ __launch_bounds__(256) void k_bdots(
     load_tfa(s + 1);
 
     float H[4][4];
+    {
+      const f32x4* hp = reinterpret_cast<const f32x4*>(coef + t * COEF_STRIDE + CO_POST);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 v = hp[a];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) H[a][m] = coef[t * COEF_STRIDE + CO_POST + a * 4 + m];
+        for (int m = 0; m < 4; ++m) H[a][m] = v[m];
+      }
+    }
 
     if (main_tok) {
 #pragma unroll
@@ -498,23 +516,44 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpart, i
 //   dW[i*C+c][p] += sum_t X[t, c] dzr[t, p] on MFMA (K = the tile's tokens,
 //   A = X^T through LDS).
 // The tile operands shared by the four rows (dz/r, its transpose, dh_in, the
-// coefficient records) are loaded cooperatively one tile ahead through
-// registers into a double-buffered LDS stage; each wave prefetches its own
-// state and dX_new rows one tile ahead.  The active rows' upstream gradients
+// coefficient records) are loaded cooperatively one tile ahead into
+// registers and published to an LDS stage at the top of the next iteration;
+// each wave prefetches its own state and dX_new rows one tile ahead, so every
+// load has a whole iteration in flight.  The active rows' upstream gradients
 // G_a are exchanged through LDS, so every wave reads only its own dX_new row
 // from memory and all of a tile's rows are read (a tile earlier) before any
 // is written: dX may alias dX_new.
 // ---------------------------------------------------------------------------
 template <typename E> struct B2Stage;
-template <> struct B2Stage<BF16> {      // 16-byte chunks per region
+template <> struct B2Stage<BF16> {      // 16-byte global chunks per region
   static constexpr int DZR = 128, DZRT = 96, DH = 64, CO = 256;
-  static constexpr int o_dzr_hi = 0, o_dzr_lo = DZR, o_dzrt_hi = 2 * DZR, o_dzrt_lo = 2 * DZR + DZRT,
-                       o_dh = 2 * DZR + 2 * DZRT, o_co = o_dh + DH, total = o_co + CO;
+  static constexpr int o_dzrt = 2 * DZR, o_dh = 2 * DZR + 2 * DZRT, o_co = o_dh + DH, total = o_co + CO;
 };
 template <> struct B2Stage<F32> {
   static constexpr int DZR = 256, DZRT = 192, DH = 128, CO = 256;
-  static constexpr int o_dzr_hi = 0, o_dzr_lo = DZR, o_dzrt_hi = DZR, o_dzrt_lo = DZR + DZRT,
-                       o_dh = DZR + DZRT, o_co = o_dh + DH, total = o_co + CO;
+  static constexpr int o_dzrt = DZR, o_dh = DZR + DZRT, o_co = o_dh + DH, total = o_co + CO;
+};
+
+// LDS layout of one tile's shared operands, every region in the order the
+// lanes read it (lane l = g*16 + r reads entry [g][r]), so each wave-wide read
+// is contiguous and free of bank conflicts:
+//   dzr   [hi|lo][ks 2][g 4][t 16]  x 8 elements   (proj B fragments)
+//   dzrt  [hi|lo][pt 3][g 4][r 16]  x 4 elements   (dW B fragments)
+//   dh    [g 4][t 16]               x 8 elements
+//   co    [field 64][t 16]          floats         (coefficients, transposed)
+template <typename E> struct B2Lds {
+  static constexpr int EB = E::bytes;
+  static constexpr int NH = EB == 2 ? 2 : 1;           // hi/lo halves in bf16
+  static constexpr int DZR = 0;
+  static constexpr int DZR_HALF = 2 * 4 * 16 * 8 * EB;
+  static constexpr int DZRT = DZR + NH * DZR_HALF;
+  static constexpr int DZRT_HALF = 3 * 4 * 16 * 4 * EB;
+  static constexpr int DH = DZRT + NH * DZRT_HALF;
+  static constexpr int CO = DH + 4 * 16 * 8 * EB;
+  static constexpr int BYTES = CO + 64 * 16 * 4;
+  // per-wave row tiles ([g][t] x 8 elements, group stride padded by 16 B)
+  static constexpr int GSTRIDE = 16 * 8 * EB + 16;
+  static constexpr int ROWTILE = 4 * GSTRIDE;
 };
 
 template <typename E>
@@ -524,13 +563,14 @@ __global__ __launch_bounds__(256) void k_bgrad(
     const void* __restrict__ dzrt, void* dX, float* __restrict__ dwp, int T, int64_t Tpad, int C, int N,
     int k, RowTable rows, int nrg, int ncb, int tok_per_split) {
   constexpr bool BF = E::bytes == 2;
+  constexpr int EB = E::bytes;
   using SG = B2Stage<E>;
+  using LY = B2Lds<E>;
   constexpr int NCHUNK = SG::total;
   constexpr int NLOAD = (NCHUNK + 255) / 256;
-  constexpr int XS_LD = B2_CB + (BF ? 2 : 1);            // padded LDS row of the X^T staging (elements)
-  __shared__ __attribute__((aligned(16))) u32x4 stage[2][NCHUNK];
-  __shared__ __attribute__((aligned(16))) u32x4 gsh[4][B2_TT][B2_CB * E::bytes / 16];
-  __shared__ __attribute__((aligned(16))) unsigned char xsh[4][B2_TT][XS_LD * E::bytes];
+  __shared__ __attribute__((aligned(16))) unsigned char stage[LY::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char gsh[4][LY::ROWTILE];   // G rows (active group)
+  __shared__ __attribute__((aligned(16))) unsigned char xsh[4][LY::ROWTILE];   // X rows (for X^T)
 
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int rg = lb % nrg;
@@ -548,6 +588,7 @@ __global__ __launch_bounds__(256) void k_bgrad(
   const int cl = c0 + 8 * g4;                   // this lane's 8 channels
   const bool cv = wv && cl < C;
   const int clc = cl < C ? cl : 0;
+  const uint32_t tokb = (uint32_t)N * C * EB;   // bytes of one token's state
 
   // proj A operand: W rows, permuted: A row m of j-tile jt -> channel
   // 8*(m/4) + 4*jt + m%4 ; K = 64 logits in two steps.
@@ -580,23 +621,23 @@ __global__ __launch_bounds__(256) void k_bgrad(
     for (int r = 0; r < NLOAD; ++r) {
       const int q = threadIdx.x + 256 * r;
       const unsigned char* gp;
-      if (q < SG::o_dzrt_hi) {                          // dzr [T][64] (hi, then lo)
-        const int qq = BF ? (q < SG::o_dzr_lo ? q : q - SG::o_dzr_lo) : q;
-        const size_t lo_off = (BF && q >= SG::o_dzr_lo) ? (size_t)T * 64 : 0;
-        const int per_tok = 64 * E::bytes / 16;
+      if (q < SG::o_dzrt) {                             // dzr [T][64] (hi, then lo)
+        const int qq = q < SG::DZR ? q : q - SG::DZR;
+        const size_t lo_off = q < SG::DZR ? 0 : (size_t)T * 64;
+        const int per_tok = 64 * EB / 16;
         const int t = min(t0 + qq / per_tok, T - 1);
-        gp = static_cast<const unsigned char*>(dzr) + (lo_off + (size_t)t * 64) * E::bytes + (qq % per_tok) * 16;
-      } else if (q < SG::o_dh) {                        // dzr^T [48][Tpad] (hi, then lo)
-        const int qq = q - SG::o_dzrt_hi;
-        const int per_row = B2_TT * E::bytes / 16;
-        const int prow = qq / per_row;                  // 0..47 (hi) or 48..95 (lo)
-        gp = static_cast<const unsigned char*>(dzrt) + ((size_t)prow * Tpad + t0) * E::bytes + (qq % per_row) * 16;
+        gp = static_cast<const unsigned char*>(dzr) + (lo_off + (size_t)t * 64) * EB + (qq % per_tok) * 16;
+      } else if (q < SG::o_dh) {                        // dzr^T [48 or 96][Tpad]
+        const int qq = q - SG::o_dzrt;
+        const int per_row = B2_TT * EB / 16;
+        const int prow = qq / per_row;
+        gp = static_cast<const unsigned char*>(dzrt) + ((size_t)prow * Tpad + t0) * EB + (qq % per_row) * 16;
       } else if (q < SG::o_co) {                        // dh_in [T][C], this block's channels
         const int qq = q - SG::o_dh;
-        const int per_tok = B2_CB * E::bytes / 16;
+        const int per_tok = B2_CB * EB / 16;
         const int t = min(t0 + qq / per_tok, T - 1);
-        const int c = c0 + (qq % per_tok) * (16 / E::bytes);
-        gp = static_cast<const unsigned char*>(dhin) + ((size_t)t * C + (c < C ? c : 0)) * E::bytes;
+        const int c = c0 + (qq % per_tok) * (16 / EB);
+        gp = static_cast<const unsigned char*>(dhin) + ((size_t)t * C + (c < C ? c : 0)) * EB;
       } else {                                          // coefficient records [T][64] floats
         const int qq = min(q - SG::o_co, SG::CO - 1);
         const int t = min(t0 + qq / 16, T - 1);
@@ -605,11 +646,52 @@ __global__ __launch_bounds__(256) void k_bgrad(
       stg[r] = *reinterpret_cast<const u32x4*>(gp);
     }
   };
-  auto store_shared = [&](int buf) {
+  // scatter the staged chunks into the lane-ordered LDS layout
+  auto store_shared = [&]() {
 #pragma unroll
     for (int r = 0; r < NLOAD; ++r) {
       const int q = threadIdx.x + 256 * r;
-      if (q < NCHUNK) stage[buf][q] = stg[r];
+      const u32x4 v = stg[r];
+      if (q < SG::o_dzrt) {
+        const int half = q < SG::DZR ? 0 : 1;
+        const int qq = q - half * SG::DZR;
+        if constexpr (BF) {                             // chunk = one 8-element fragment piece
+          const int t = qq >> 3, j = qq & 7, ks = j >> 2, g = j & 3;
+          *reinterpret_cast<u32x4*>(&stage[LY::DZR + half * LY::DZR_HALF + (((ks * 4 + g) * 16 + t) * 16)]) = v;
+        } else {                                        // chunk = half of a 32-byte piece
+          const int t = qq >> 4, j = qq & 15, jp = j >> 1, h = j & 1, ks = jp >> 2, g = jp & 3;
+          *reinterpret_cast<u32x4*>(&stage[LY::DZR + (((ks * 4 + g) * 16 + t) * 32) + h * 16]) = v;
+        }
+      } else if (q < SG::o_dh) {
+        const int qq = q - SG::o_dzrt;
+        if constexpr (BF) {                             // row of 16 tokens = 2 chunks = 4 pieces
+          const int prow = qq >> 1, h = qq & 1;
+          const int half = prow >= 48 ? 1 : 0, p = prow - 48 * half, pt = p >> 4, rr = p & 15;
+          const int base = LY::DZRT + half * LY::DZRT_HALF;
+          *reinterpret_cast<u32x2*>(&stage[base + ((pt * 4 + 2 * h) * 16 + rr) * 8]) = u32x2{v[0], v[1]};
+          *reinterpret_cast<u32x2*>(&stage[base + ((pt * 4 + 2 * h + 1) * 16 + rr) * 8]) = u32x2{v[2], v[3]};
+        } else {                                        // row of 16 tokens = 4 chunks = 4 pieces
+          const int p = qq >> 2, g = qq & 3, pt = p >> 4, rr = p & 15;
+          *reinterpret_cast<u32x4*>(&stage[LY::DZRT + ((pt * 4 + g) * 16 + rr) * 16]) = v;
+        }
+      } else if (q < SG::o_co) {
+        const int qq = q - SG::o_dh;
+        if constexpr (BF) {
+          const int t = qq >> 2, g = qq & 3;
+          *reinterpret_cast<u32x4*>(&stage[LY::DH + (g * 16 + t) * 16]) = v;
+        } else {
+          const int t = qq >> 3, j = qq & 7, g = j >> 1, h = j & 1;
+          *reinterpret_cast<u32x4*>(&stage[LY::DH + (g * 16 + t) * 32 + h * 16]) = v;
+        }
+      } else if (q < NCHUNK) {
+        const int qq = q - SG::o_co;
+        const int t = qq >> 4, j = qq & 15;
+        float* co = reinterpret_cast<float*>(&stage[LY::CO]);
+        co[(4 * j + 0) * 16 + t] = __uint_as_float(v[0]);
+        co[(4 * j + 1) * 16 + t] = __uint_as_float(v[1]);
+        co[(4 * j + 2) * 16 + t] = __uint_as_float(v[2]);
+        co[(4 * j + 3) * 16 + t] = __uint_as_float(v[3]);
+      }
     }
   };
   // own rows of the tile at t0
@@ -619,39 +701,40 @@ __global__ __launch_bounds__(256) void k_bgrad(
     xo = V8<E>::load(xbase, (size_t)t * xstride + clc);
     dvo = V8<E>::load(dXn, ((size_t)t * N + srow) * C + clc);
   };
+  const int rowoff = g4 * LY::GSTRIDE + r16 * 8 * EB;      // this lane's slot in a row tile
 
   if (tbeg < tfin) {
     load_shared(tbeg);
     load_own(tbeg);
-    store_shared(0);
   }
-  __syncthreads();
-  int buf = 0;
-  for (int t0 = tbeg; t0 < tfin; t0 += B2_TT, buf ^= 1) {
+  for (int t0 = tbeg; t0 < tfin; t0 += B2_TT) {
     const int tk = t0 + r16;
     const bool tv = tk < T;
+    // this tile's operands were loaded one iteration ago: publish them, then
+    // start the next tile's loads before the arithmetic.  The loads are
+    // unconditional (the last tile reloads itself) so that the number of
+    // outstanding memory operations is static and waits stay exact.
+    store_shared();
     V8<E> xc = xo, dvc = dvo;
     if (!(tv && cv)) { xc = V8<E>::zero(); dvc = V8<E>::zero(); }
-    const bool more = t0 + B2_TT < tfin;
-    if (more) {
-      load_shared(t0 + B2_TT);
-      load_own(t0 + B2_TT);
+    {
+      const int tn = t0 + B2_TT < tfin ? t0 + B2_TT : t0;
+      load_shared(tn);
+      load_own(tn);
     }
-    // publish this tile's G row (active group) and X row (for X^T)
-    if (active_grp) *reinterpret_cast<V8<E>*>(&gsh[wave][r16][g4 * (8 * E::bytes / 16)]) = dvc;
-    *reinterpret_cast<V8<E>*>(&xsh[wave][r16][8 * g4 * E::bytes]) = xc;
+    if (active_grp) *reinterpret_cast<V8<E>*>(&gsh[wave][rowoff]) = dvc;
+    *reinterpret_cast<V8<E>*>(&xsh[wave][rowoff]) = xc;
     __syncthreads();
 
-    const u32x4* sg = stage[buf];
     // ---- proj on MFMA: D[c][t], 2 j-tiles ----
     f32x4 pj[2];
     {
       V8<E> bz[2], bzl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int off = r16 * (64 * E::bytes / 16) + (32 * ks + 8 * g4) * E::bytes / 16;
-        bz[ks] = *reinterpret_cast<const V8<E>*>(&sg[SG::o_dzr_hi + off]);
-        if constexpr (BF) bzl[ks] = *reinterpret_cast<const V8<E>*>(&sg[SG::o_dzr_lo + off]);
+        const int off = ((ks * 4 + g4) * 16 + r16) * 8 * EB;
+        bz[ks] = *reinterpret_cast<const V8<E>*>(&stage[LY::DZR + off]);
+        if constexpr (BF) bzl[ks] = *reinterpret_cast<const V8<E>*>(&stage[LY::DZR + LY::DZR_HALF + off]);
       }
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
@@ -667,9 +750,9 @@ __global__ __launch_bounds__(256) void k_bgrad(
     }
     // ---- assemble dX for (token tk, channels cl..cl+8) ----
     {
-      const float* cor = reinterpret_cast<const float*>(&sg[SG::o_co]) + r16 * COEF_STRIDE;
-      const float hpre = cor[CO_PRE + srow];
-      const float gam = cor[CO_GAMMA];
+      const float* co = reinterpret_cast<const float*>(&stage[LY::CO]);
+      const float hpre = co[(CO_PRE + srow) * 16 + r16];
+      const float gam = co[CO_GAMMA * 16 + r16];
       float pass[8];
       if (active_grp) {
 #pragma unroll
@@ -677,8 +760,8 @@ __global__ __launch_bounds__(256) void k_bgrad(
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           if (a < k) {
-            const float h = cor[CO_RES + a * 4 + wave];
-            const V8<E> gv = *reinterpret_cast<const V8<E>*>(&gsh[a][r16][g4 * (8 * E::bytes / 16)]);
+            const float h = co[(CO_RES + a * 4 + wave) * 16 + r16];
+            const V8<E> gv = *reinterpret_cast<const V8<E>*>(&gsh[a][rowoff]);
             float gf[8];
             gv.to_float(gf);
 #pragma unroll
@@ -688,8 +771,7 @@ __global__ __launch_bounds__(256) void k_bgrad(
       } else {
         dvc.to_float(pass);
       }
-      const V8<E> hv = *reinterpret_cast<const V8<E>*>(
-          &sg[SG::o_dh + r16 * (B2_CB * E::bytes / 16) + g4 * (8 * E::bytes / 16)]);
+      const V8<E> hv = *reinterpret_cast<const V8<E>*>(&stage[LY::DH + (g4 * 16 + r16) * 8 * EB]);
       float xf[8], hf[8], o[8];
       xc.to_float(xf);
       hv.to_float(hf);
@@ -702,36 +784,37 @@ __global__ __launch_bounds__(256) void k_bgrad(
         v = fmaf(-gam, xf[q], v);
         o[q] = v;
       }
-      if (tv && cv) V8<E>::from_float(o).store(dX, ((size_t)tk * N + srow) * C + cl);
+      // buffer store based at this tile; an out-of-range offset (ragged
+      // token or channel tail) is dropped by the hardware
+      const rsrc_t rdx = make_rsrc(static_cast<char*>(dX) + (size_t)t0 * tokb, (uint32_t)B2_TT * tokb);
+      const uint32_t voff = (tv && cv) ? ((uint32_t)r16 * N + srow) * (uint32_t)C * EB + cl * EB : 0x80000000u;
+      bstore<E, 8>(V8<E>::from_float(o), rdx, voff, 0);
     }
     // ---- dW on MFMA: A = X^T (rows = channels, K = 16 tokens) ----
     {
       Vec<E, 4> bh[3], bl[3];
 #pragma unroll
       for (int pt = 0; pt < 3; ++pt) {
-        const int p = 16 * pt + r16;
-        const unsigned char* rowh = reinterpret_cast<const unsigned char*>(&sg[SG::o_dzrt_hi]) + (size_t)p * B2_TT * E::bytes;
-        bh[pt] = *reinterpret_cast<const Vec<E, 4>*>(rowh + 4 * g4 * E::bytes);
-        if constexpr (BF) {
-          const unsigned char* rowl = reinterpret_cast<const unsigned char*>(&sg[SG::o_dzrt_lo]) + (size_t)p * B2_TT * E::bytes;
-          bl[pt] = *reinterpret_cast<const Vec<E, 4>*>(rowl + 4 * g4 * E::bytes);
-        }
+        const int off = ((pt * 4 + g4) * 16 + r16) * 4 * EB;
+        bh[pt] = *reinterpret_cast<const Vec<E, 4>*>(&stage[LY::DZRT + off]);
+        if constexpr (BF) bl[pt] = *reinterpret_cast<const Vec<E, 4>*>(&stage[LY::DZRT + LY::DZRT_HALF + off]);
       }
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
+        // channel cc = 16*jt + r16 of tokens 4*g4 .. 4*g4+3: entry [cc/8][t], element cc%8
+        const int cc = 16 * jt + r16;
+        const unsigned char* colp = &xsh[wave][(cc >> 3) * LY::GSTRIDE + (cc & 7) * EB];
         Vec<E, 4> xa;
         if constexpr (BF) {
-          const uint16_t* col = reinterpret_cast<const uint16_t*>(&xsh[wave][0][0]) + 16 * jt + r16;
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            const unsigned lo16 = col[(size_t)(4 * g4 + 2 * q) * XS_LD];
-            const unsigned hi16 = col[(size_t)(4 * g4 + 2 * q + 1) * XS_LD];
+            const unsigned lo16 = *reinterpret_cast<const uint16_t*>(colp + (4 * g4 + 2 * q) * 8 * EB);
+            const unsigned hi16 = *reinterpret_cast<const uint16_t*>(colp + (4 * g4 + 2 * q + 1) * 8 * EB);
             xa.w[q] = lo16 | (hi16 << 16);
           }
         } else {
-          const float* col = reinterpret_cast<const float*>(&xsh[wave][0][0]) + 16 * jt + r16;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) xa.x[q] = col[(size_t)(4 * g4 + q) * XS_LD];
+          for (int q = 0; q < 4; ++q) xa.x[q] = *reinterpret_cast<const float*>(colp + (4 * g4 + q) * 8 * EB);
         }
 #pragma unroll
         for (int pt = 0; pt < 3; ++pt) {
@@ -740,8 +823,7 @@ __global__ __launch_bounds__(256) void k_bgrad(
         }
       }
     }
-    if (more) store_shared(buf ^ 1);
-    __syncthreads();
+    __syncthreads();          // every read of the stage and of gsh/xsh is done
   }
   // dW partial rows: D row 4*g4+e of j-tile jt = channel 16*jt + 4*g4 + e
   if (wv) {
@@ -830,13 +912,17 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   {
     TimedLaunch tl(tm, KID_BDOTS, st);
     dim3 grid(p.b1_cblocks, p.B * p.b1_segs);
-    if (p.nc == 4)
-      k_bdots<E, 4><<<grid, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12, coef, dpart,
-                                          a->dout, dwpart, p.T, p.S, p.C, p.N, p.k, act, p.b1_lseg, p.b1_segs);
-    else
-      k_bdots<E, 1><<<grid, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, nullptr, nullptr, nullptr, coef,
-                                          dpart, a->dout, dwpart, p.T, p.S, p.C, p.N, p.k, act, p.b1_lseg,
-                                          p.b1_segs);
+    const bool fast = p.N == 16 && p.k == 4;
+#define XHC_BDOTS(NCOMP, FAST)                                                                                   \
+  k_bdots<E, NCOMP, FAST><<<grid, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12, coef,     \
+                                               dpart, a->dout, dwpart, p.T, p.S, p.C, p.N, p.k, act, p.b1_lseg, \
+                                               p.b1_segs)
+    if (p.nc == 4) {
+      if (fast) XHC_BDOTS(4, true); else XHC_BDOTS(4, false);
+    } else {
+      if (fast) XHC_BDOTS(1, true); else XHC_BDOTS(1, false);
+    }
+#undef XHC_BDOTS
   }
   {
     TimedLaunch tl(tm, KID_BCOEF, st);

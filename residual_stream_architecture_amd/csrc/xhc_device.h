@@ -19,11 +19,6 @@ struct F32 { static constexpr int bytes = 4; };
 // W consecutive elements held by one lane, loaded and stored with one vector
 // access per 16 bytes.  V8 is also one lane's share of an MFMA K=32 step.
 // ---------------------------------------------------------------------------
-template <int BYTES> struct RawT;
-template <> struct RawT<4> { typedef unsigned type; };
-template <> struct RawT<8> { typedef u32x2 type; };
-template <> struct RawT<16> { typedef u32x4 type; };
-
 template <typename E, int W> struct Vec;
 
 template <int W> struct Vec<BF16, W> {
@@ -128,6 +123,64 @@ template <int W> struct Vec<F32, W> {
 };
 
 template <typename E> using V8 = Vec<E, 8>;
+
+// ---------------------------------------------------------------------------
+// Raw buffer access: a 128-bit resource (base, byte size) in SGPRs, a per-lane
+// byte offset in a VGPR and a uniform byte offset in an SGPR.  Reads past the
+// resource's size return zero; writes past it are dropped.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+template <typename E, int W>
+__device__ inline Vec<E, W> bload(rsrc_t r, uint32_t voff, uint32_t soff) {
+  constexpr int B = W * E::bytes;
+  Vec<E, W> v;
+  if constexpr (B == 4) {
+    const unsigned x = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    __builtin_memcpy(&v, &x, 4);
+  } else if constexpr (B == 8) {
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    __builtin_memcpy(&v, &x, 8);
+  } else if constexpr (B == 16) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    __builtin_memcpy(&v, &x, 16);
+  } else {
+    static_assert(B == 32, "vector width");
+    const u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    const u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, 0);
+    __builtin_memcpy(&v, &x0, 16);
+    __builtin_memcpy(reinterpret_cast<char*>(&v) + 16, &x1, 16);
+  }
+  return v;
+}
+
+template <typename E, int W>
+__device__ inline void bstore(const Vec<E, W>& v, rsrc_t r, uint32_t voff, uint32_t soff) {
+  constexpr int B = W * E::bytes;
+  if constexpr (B == 4) {
+    unsigned x;
+    __builtin_memcpy(&x, &v, 4);
+    __builtin_amdgcn_raw_buffer_store_b32(x, r, voff, soff, 0);
+  } else if constexpr (B == 8) {
+    u32x2 x;
+    __builtin_memcpy(&x, &v, 8);
+    __builtin_amdgcn_raw_buffer_store_b64(x, r, voff, soff, 0);
+  } else if constexpr (B == 16) {
+    u32x4 x;
+    __builtin_memcpy(&x, &v, 16);
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
+  } else {
+    static_assert(B == 32, "vector width");
+    u32x4 x0, x1;
+    __builtin_memcpy(&x0, &v, 16);
+    __builtin_memcpy(&x1, reinterpret_cast<const char*>(&v) + 16, 16);
+    __builtin_amdgcn_raw_buffer_store_b128(x0, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(x1, r, voff + 16, soff, 0);
+  }
+}
 
 // One K=32 step of a 16x16 fp32-accumulating MFMA tile.  Lane l holds row
 // (A) or column (B) l%16 and the 8 K-elements of group l/16; the K order

@@ -234,26 +234,35 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
 // rows are loaded before the current token is computed and stored: loads of
 // token s+1 never alias the rows written for token s, so X_new == X (in
 // place) stays safe and every load batch overlaps the previous token's work.
-// FULLN: N == 16 (rows unconditional); otherwise rows i >= N are skipped.
+// FAST: N == 16 and k == 4 (all row and active-row loops compile-time);
+// otherwise rows i >= N and active slots a >= k are skipped at run time.
 // ---------------------------------------------------------------------------
 struct Active { int id[4]; };
 
-template <typename E, int NCOMP, bool FULLN>
+template <typename E, int NCOMP, bool FAST>
 __global__ __launch_bounds__(MIX_THREADS) void k_mix(
     const void* __restrict__ X, const void* __restrict__ out, const float* __restrict__ w4,
     const float* __restrict__ w8, const float* __restrict__ w12, const float* __restrict__ coef,
     void* Xnew, void* __restrict__ hin, void* __restrict__ xact, int S, int C, int N, int k,
     Active act, int in_place, int lseg, int segs_per_seq) {
   using V = Vec<E, MIX_CH>;
+  constexpr int EB = E::bytes;
   const int craw = (blockIdx.x * MIX_THREADS + threadIdx.x) * MIX_CH;
   const bool cv = craw < C;
   const int c = cv ? craw : 0;                  // clamped: idle lanes read valid memory
+  const uint32_t voff = (uint32_t)c * EB;       // this lane's byte offset inside a row
+  const uint32_t rowb = (uint32_t)C * EB;       // bytes per row
+  const uint32_t tokb = (uint32_t)N * rowb;     // bytes per token of state
   const int seg = blockIdx.y;
   const int bseq = seg / segs_per_seq;
   const int s0 = (seg - bseq * segs_per_seq) * lseg;
   const int s1 = min(s0 + lseg, S);
   const size_t tok0 = (size_t)bseq * S;
-  const int NR = FULLN ? 16 : N;
+  constexpr bool FULLN = FAST;
+  const int NR = FAST ? 16 : N;
+  const int K = FAST ? 4 : k;
+  const char* Xb = static_cast<const char*>(X);
+  char* Xnb = static_cast<char*>(Xnew);
 
   float wk[MIX_CH][24];
   if constexpr (NCOMP == 4) {
@@ -267,6 +276,8 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
       for (int q = 0; q < 12; ++q) wk[ch][12 + q] = w12[(size_t)(c + ch) * 12 + q];
     }
   }
+  // `out` rows of this sequence, addressed per position
+  const rsrc_t rout = make_rsrc(static_cast<const char*>(out) + tok0 * rowb, (uint32_t)S * rowb);
   // before the first shift, slot j+1 holds position s0-11+j (zero before the
   // sequence start)
   float win[12][MIX_CH];
@@ -275,36 +286,55 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
 #pragma unroll
   for (int j = 0; j < 11; ++j) {
     const int s = s0 - 11 + j;
-    V v = (NCOMP == 4 && s >= 0) ? V::load(out, (tok0 + (s >= 0 ? s : 0)) * C + c) : V::zero();
+    V v = bload<E, MIX_CH>(rout, voff, (uint32_t)(s >= 0 ? s : 0) * rowb);
     v.to_float(win[j + 1]);
+    if (NCOMP != 4 || s < 0) {
+#pragma unroll
+      for (int ch = 0; ch < MIX_CH; ++ch) win[j + 1][ch] = 0.f;
+    }
   }
 
-  // prefetch buffers: the 16 state rows and the out row of the next token
-  V xr[16], ov;
+  // prefetch buffers: the 16 state rows, the k active rows and the out row
+  // of the next token (one buffer resource per token: offsets stay small)
+  V xr[16], xa_r[4], ov;
   auto load_token = [&](int s) {
-    const size_t t = tok0 + s;
+    const rsrc_t rx = make_rsrc(Xb + (tok0 + s) * tokb, tokb);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (FULLN || i < NR) xr[i] = V::load(X, (t * N + i) * C + c);
-    ov = V::load(out, t * C + c);
+      if (FULLN || i < NR) xr[i] = bload<E, MIX_CH>(rx, voff, (uint32_t)i * rowb);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (b < K) xa_r[b] = bload<E, MIX_CH>(rx, voff, (uint32_t)act.id[b] * rowb);
+    ov = bload<E, MIX_CH>(rout, voff, (uint32_t)s * rowb);
   };
-  if (s0 < s1) load_token(s0);
+  load_token(s0);
 
   for (int s = s0; s < s1; ++s) {
     const size_t t = tok0 + s;
-    V cx[16], co_out = ov;
+    V cx[16], cxa[4], co_out = ov;
 #pragma unroll
     for (int i = 0; i < 16; ++i) cx[i] = xr[i];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) cxa[b] = xa_r[b];
     load_token(s + 1 < s1 ? s + 1 : s);          // next token (the last iteration reloads, harmlessly)
 
-    const float* co = coef + t * COEF_STRIDE;
+    // the token's coefficients: uniform 16-byte loads (scalar loads)
+    const f32x4* c4 = reinterpret_cast<const f32x4*>(coef + t * COEF_STRIDE);
+    float cpre[16], cpost[16], cres[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 a0 = c4[j], a1 = c4[4 + j], a2 = c4[8 + j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { cpre[4 * j + e] = a0[e]; cpost[4 * j + e] = a1[e]; cres[4 * j + e] = a2[e]; }
+    }
 #pragma unroll
     for (int j = 0; j < 11; ++j)
 #pragma unroll
       for (int ch = 0; ch < MIX_CH; ++ch) win[j][ch] = win[j + 1][ch];
     co_out.to_float(win[11]);
 
-    float hacc[MIX_CH], xa[4][MIX_CH];
+    // dense read
+    float hacc[MIX_CH];
 #pragma unroll
     for (int ch = 0; ch < MIX_CH; ++ch) hacc[ch] = 0.f;
 #pragma unroll
@@ -312,25 +342,13 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
       if (FULLN || i < NR) {
         float xf[MIX_CH];
         cx[i].to_float(xf);
-        const float hp = co[CO_PRE + i];
+        const float hp = cpre[i];
 #pragma unroll
         for (int ch = 0; ch < MIX_CH; ++ch) hacc[ch] = fmaf(hp, xf[ch], hacc[ch]);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          if (b < k && i == act.id[b]) {
-#pragma unroll
-            for (int ch = 0; ch < MIX_CH; ++ch) xa[b][ch] = xf[ch];
-            if (xact && cv) cx[i].store(xact, (t * k + b) * C + c);
-          }
-        if (!in_place && cv) {
-          bool is_act = false;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) is_act |= (b < k && i == act.id[b]);
-          if (!is_act) cx[i].store(Xnew, (t * N + i) * C + c);
-        }
       }
     }
-    if (cv) V::from_float(hacc).store(hin, t * C + c);
+    const rsrc_t rh = make_rsrc(static_cast<char*>(hin) + t * rowb, rowb);
+    if (cv) bstore<E, MIX_CH>(V::from_float(hacc), rh, voff, 0);
 
     float u[4][MIX_CH];
 #pragma unroll
@@ -347,21 +365,41 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
         u[1][ch] = s4; u[2][ch] = s8; u[3][ch] = s12;
       }
     }
+    if (cv) {
+      float xa[4][MIX_CH];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      if (a < k) {
-        float res[MIX_CH];
+      for (int b = 0; b < 4; ++b)
+        if (b < K) cxa[b].to_float(xa[b]);
+      const rsrc_t rxn = make_rsrc(Xnb + t * tokb, tokb);
+      const rsrc_t rxs = make_rsrc(static_cast<char*>(xact) + t * (uint32_t)K * rowb, (uint32_t)K * rowb);
 #pragma unroll
-        for (int ch = 0; ch < MIX_CH; ++ch) {
-          float v = 0.f;
+      for (int a = 0; a < 4; ++a) {
+        if (a < K) {
+          float res[MIX_CH];
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-            if (b < k) v = fmaf(co[CO_RES + a * 4 + b], xa[b][ch], v);
+          for (int ch = 0; ch < MIX_CH; ++ch) {
+            float v = 0.f;
 #pragma unroll
-          for (int m = 0; m < NCOMP; ++m) v = fmaf(co[CO_POST + a * 4 + m], u[m][ch], v);
-          res[ch] = v;
+            for (int b = 0; b < 4; ++b)
+              if (b < K) v = fmaf(cres[a * 4 + b], xa[b][ch], v);
+#pragma unroll
+            for (int m = 0; m < NCOMP; ++m) v = fmaf(cpost[a * 4 + m], u[m][ch], v);
+            res[ch] = v;
+          }
+          bstore<E, MIX_CH>(V::from_float(res), rxn, voff, (uint32_t)act.id[a] * rowb);
+          if (xact) bstore<E, MIX_CH>(cxa[a], rxs, voff, (uint32_t)a * rowb);
         }
-        if (cv) V::from_float(res).store(Xnew, (t * N + act.id[a]) * C + c);
+      }
+      if (!in_place) {                             // out of place: copy the untouched rows
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (FULLN || i < NR) {
+            bool is_act = false;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) is_act |= (b < K && i == act.id[b]);
+            if (!is_act) bstore<E, MIX_CH>(cx[i], rxn, voff, (uint32_t)i * rowb);
+          }
+        }
       }
     }
   }
@@ -418,10 +456,11 @@ static int forward_impl(const Plan& p, const xhc_fwd_args* a, char* ws, hipStrea
   k_mix<E, NCOMP, FULLN><<<grid, MIX_THREADS, 0, st>>>(a->X, a->out, a->w4, a->w8, a->w12, coef, a->X_new, \
                                                        a->h_in, a->xact_save, p.S, p.C, p.N, p.k, act,      \
                                                        in_place, p.mix_lseg, p.mix_segs)
+    const bool fast = p.N == 16 && p.k == 4;
     if (p.nc == 4) {
-      if (p.N == 16) XHC_MIX(4, true); else XHC_MIX(4, false);
+      if (fast) XHC_MIX(4, true); else XHC_MIX(4, false);
     } else {
-      if (p.N == 16) XHC_MIX(1, true); else XHC_MIX(1, false);
+      if (fast) XHC_MIX(1, true); else XHC_MIX(1, false);
     }
 #undef XHC_MIX
   }

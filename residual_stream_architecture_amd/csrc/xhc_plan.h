@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/xhc.h"
+#include "xhc.h"
 
 namespace xhc {
 
