@@ -84,8 +84,7 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.off_dpart = o;  o = align256(o + (size_t)q.b1_cblocks * T * DOT_STRIDE * 4);
   q.off_dwpart = o; o = align256(o + (q.nc == 4 ? (size_t)q.B * q.b1_segs * q.C * 24 * 4 : 0));
   q.off_dz = o;     o = align256(o + (size_t)T * 48 * 4);
-  q.off_dzr = o;    o = align256(o + (size_t)(q.dtype == XHC_BF16 ? 2 : 1) * T * 64 * q.esz);
-  q.off_dzrt = o;   o = align256(o + (size_t)(q.dtype == XHC_BF16 ? 96 : 48) * q.Tpad * q.esz);
+  q.off_rec = o;    o = align256(o + (size_t)(q.Tpad / B2_TT) * REC_BYTES);
   q.off_dwpart2 = o; o = align256(o + (size_t)q.b2_ts * q.NC * 48 * 4);
   q.bwd_bytes = o;
   return XHC_OK;

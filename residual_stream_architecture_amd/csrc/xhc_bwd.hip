@@ -382,9 +382,9 @@ constexpr int BCOEF_TOK = 4;
 
 template <typename E>
 __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpart, int ncb, const float* __restrict__ zin,
-                                              const float* __restrict__ bias, float* __restrict__ coef,
-                                              float* __restrict__ dz_out, void* __restrict__ dzr,
-                                              void* __restrict__ dzrt, int T, int64_t Tpad, int N, int k, int nc,
+                                              const float* __restrict__ bias, const float* __restrict__ coef,
+                                              float* __restrict__ dz_out, void* __restrict__ rec,
+                                              int T, int64_t Tpad, int N, int k, int nc,
                                               int P, float inv_nc_total, int iters, int unit_gates) {
   extern __shared__ float hist[];   // [BCOEF_TOK][iters+1][16]
   __shared__ float dzs[BCOEF_TOK][64];
@@ -475,120 +475,109 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpart, i
   al += shfl_xor(al, 8);
   const float inv_r = 1.f / r;
   if (tv) {
-    if (e == 0) coef[t * COEF_STRIDE + CO_GAMMA] = al * inv_nc_total * inv_r * inv_r;
 #pragma unroll
     for (int n = 0; n < 3; ++n) dz_out[t * 48 + e + 16 * n] = dzs[tok][e + 16 * n];
   }
-  // MFMA operands: dzr [T][64] (B operand of dz W^T) and its transpose
-  // [48][Tpad] (operand of dW); t in [T, Tpad) is written as zero.  In bf16
-  // mode each is stored as hi and lo halves (hi at offset 0, lo after it):
-  // the dz values of saturated Sinkhorn entries are large, and the products
-  // must keep fp32 accuracy.
+  // B2's tile record (layout next to REC_BYTES); t in [T, Tpad) is written
+  // as zeros.  In bf16 mode dz/r is stored as hi and lo bf16 halves: the dz
+  // values of saturated Sinkhorn entries are large, and the products must
+  // keep fp32 accuracy.
+  if (t < Tpad) {
+    constexpr int EB = E::bytes;
+    unsigned char* rb = static_cast<unsigned char*>(rec) + (size_t)(t / B2_TT) * REC_BYTES;
+    const int tt = (int)(t % B2_TT);
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int p = e + 16 * n;
-    const float v = tv ? dzs[tok][p] * inv_r : 0.f;
-    if constexpr (E::bytes == 2) {
-      __bf16 hi, lo;
-      split_bf16(v, hi, lo);
-      if (tv) {
-        reinterpret_cast<__bf16*>(dzr)[t * 64 + p] = hi;
-        reinterpret_cast<__bf16*>(dzr)[((size_t)T + t) * 64 + p] = lo;
+    for (int n = 0; n < 4; ++n) {
+      const int p = e + 16 * n;
+      const float v = tv ? dzs[tok][p] * inv_r : 0.f;
+      const int ks = p >> 5, g = (p >> 3) & 3, e8 = p & 7;
+      const size_t o_dzr = REC_DZR + ((size_t)((ks * 4 + g) * 16 + tt) * 8 + e8) * EB;
+      const int pt = p >> 4, rr = p & 15, gt = tt >> 2, e4 = tt & 3;
+      const size_t o_dzrt = REC_DZRT + ((size_t)((pt * 4 + gt) * 16 + rr) * 4 + e4) * EB;
+      if constexpr (EB == 2) {
+        __bf16 hi, lo;
+        split_bf16(v, hi, lo);
+        *reinterpret_cast<__bf16*>(rb + o_dzr) = hi;
+        *reinterpret_cast<__bf16*>(rb + o_dzr + rec_dzr_half(EB)) = lo;
+        if (p < 48) {
+          *reinterpret_cast<__bf16*>(rb + o_dzrt) = hi;
+          *reinterpret_cast<__bf16*>(rb + o_dzrt + rec_dzrt_half(EB)) = lo;
+        }
+      } else {
+        *reinterpret_cast<float*>(rb + o_dzr) = v;
+        if (p < 48) *reinterpret_cast<float*>(rb + o_dzrt) = v;
       }
-      if (p < 48 && t < Tpad) {
-        reinterpret_cast<__bf16*>(dzrt)[(size_t)p * Tpad + t] = hi;
-        reinterpret_cast<__bf16*>(dzrt)[(size_t)(48 + p) * Tpad + t] = lo;
-      }
-    } else {
-      if (tv) reinterpret_cast<float*>(dzr)[t * 64 + p] = v;
-      if (p < 48 && t < Tpad) reinterpret_cast<float*>(dzrt)[(size_t)p * Tpad + t] = v;
     }
+    float* rco = reinterpret_cast<float*>(rb + REC_CO);
+    rco[(RF_PRE + e) * B2_TT + tt] = tv ? co[CO_PRE + e] : 0.f;
+    rco[(RF_RES + e) * B2_TT + tt] = tv ? co[CO_RES + e] : 0.f;
+    if (e < REC_NF - RF_GAMMA)
+      rco[(RF_GAMMA + e) * B2_TT + tt] = (tv && e == 0) ? al * inv_nc_total * inv_r * inv_r : 0.f;
   }
 }
 
 // ---------------------------------------------------------------------------
-// B2.  Workgroup = (row group, B2_CB channels, token split); wave w handles
-// the group's row w.  Per tile of B2_TT = 16 tokens:
-//   proj[c][t] = sum_p W[i*C+c, p] dzr[t, p] on MFMA (dz/r as bf16 hi + lo),
+// B2.  Workgroup = (row group, B2_CB = 64 channels, token split), 8 waves:
+// wave w handles row w%4 of the group on channel half w/4, so the two halves
+// of every 128-byte line of a bf16 row are read by two waves of one
+// workgroup in the same tile.  Per tile of B2_TT = 16 tokens:
+//   proj[c][t] = sum_p W[i*C+c, p] dz_r[t, p] on MFMA (dz/r as bf16 hi + lo),
 //   with A rows permuted so that lane (t = lane%16, g = lane/16) ends up
 //   owning channels 8g..8g+8 of token t -- the layout of its own loads;
 //   dX = pass + H_pre dh_in + proj - X gamma;
-//   dW[i*C+c][p] += sum_t X[t, c] dzr[t, p] on MFMA (K = the tile's tokens,
+//   dW[i*C+c][p] += sum_t X[t, c] dz_r[t, p] on MFMA (K = the tile's tokens,
 //   A = X^T through LDS).
-// The tile operands shared by the four rows (dz/r, its transpose, dh_in, the
-// coefficient records) are loaded cooperatively one tile ahead into
-// registers and published to an LDS stage at the top of the next iteration;
-// each wave prefetches its own state and dX_new rows one tile ahead, so every
-// load has a whole iteration in flight.  The active rows' upstream gradients
-// G_a are exchanged through LDS, so every wave reads only its own dX_new row
-// from memory and all of a tile's rows are read (a tile earlier) before any
-// is written: dX may alias dX_new.
+// The tile's shared operands (dz/r in both fragment orders, the coefficients)
+// arrive as one contiguous record in LDS order, copied global -> LDS by the
+// LDS-DMA form of the load one tile ahead (double-buffered); each lane
+// prefetches its own state, dX_new and dh_in pieces one tile ahead.  A
+// tile's dX is stored at the start of the next iteration, ahead of that
+// iteration's prefetch, so the wait at the top of the loop never waits on a
+// store issued after the loads it needs.  The active rows' upstream
+// gradients G_a are exchanged through LDS; all of a tile's rows are read (a
+// tile earlier) before any is written, so dX may alias dX_new.
 // ---------------------------------------------------------------------------
-template <typename E> struct B2Stage;
-template <> struct B2Stage<BF16> {      // 16-byte global chunks per region
-  static constexpr int DZR = 128, DZRT = 96, DH = 64, CO = 256;
-  static constexpr int o_dzrt = 2 * DZR, o_dh = 2 * DZR + 2 * DZRT, o_co = o_dh + DH, total = o_co + CO;
-};
-template <> struct B2Stage<F32> {
-  static constexpr int DZR = 256, DZRT = 192, DH = 128, CO = 256;
-  static constexpr int o_dzrt = DZR, o_dh = DZR + DZRT, o_co = o_dh + DH, total = o_co + CO;
-};
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
 
-// LDS layout of one tile's shared operands, every region in the order the
-// lanes read it (lane l = g*16 + r reads entry [g][r]), so each wave-wide read
-// is contiguous and free of bank conflicts:
-//   dzr   [hi|lo][ks 2][g 4][t 16]  x 8 elements   (proj B fragments)
-//   dzrt  [hi|lo][pt 3][g 4][r 16]  x 4 elements   (dW B fragments)
-//   dh    [g 4][t 16]               x 8 elements
-//   co    [field 64][t 16]          floats         (coefficients, transposed)
 template <typename E> struct B2Lds {
   static constexpr int EB = E::bytes;
-  static constexpr int NH = EB == 2 ? 2 : 1;           // hi/lo halves in bf16
-  static constexpr int DZR = 0;
-  static constexpr int DZR_HALF = 2 * 4 * 16 * 8 * EB;
-  static constexpr int DZRT = DZR + NH * DZR_HALF;
-  static constexpr int DZRT_HALF = 3 * 4 * 16 * 4 * EB;
-  static constexpr int DH = DZRT + NH * DZRT_HALF;
-  static constexpr int CO = DH + 4 * 16 * 8 * EB;
-  static constexpr int BYTES = CO + 64 * 16 * 4;
   // per-wave row tiles ([g][t] x 8 elements, group stride padded by 16 B)
   static constexpr int GSTRIDE = 16 * 8 * EB + 16;
   static constexpr int ROWTILE = 4 * GSTRIDE;
 };
 
 template <typename E>
-__global__ __launch_bounds__(256) void k_bgrad(
-    StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin,
-    const float* __restrict__ coef, const void* __restrict__ Wp, const void* __restrict__ dzr,
-    const void* __restrict__ dzrt, void* dX, float* __restrict__ dwp, int T, int64_t Tpad, int C, int N,
-    int k, RowTable rows, int nrg, int ncb, int tok_per_split) {
+__global__ __launch_bounds__(512) void k_bgrad(
+    StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin, const void* __restrict__ Wp,
+    const unsigned char* __restrict__ rec, void* dX, float* __restrict__ dwp, int T, int C, int N, int k,
+    RowTable rows, int nrg, int ncb, int tok_per_split) {
   constexpr bool BF = E::bytes == 2;
   constexpr int EB = E::bytes;
-  using SG = B2Stage<E>;
   using LY = B2Lds<E>;
-  constexpr int NCHUNK = SG::total;
-  constexpr int NLOAD = (NCHUNK + 255) / 256;
-  __shared__ __attribute__((aligned(16))) unsigned char stage[LY::BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char gsh[4][LY::ROWTILE];   // G rows (active group)
-  __shared__ __attribute__((aligned(16))) unsigned char xsh[4][LY::ROWTILE];   // X rows (for X^T)
+  static_assert(REC_BYTES % 1024 == 0 && REC_BYTES / 1024 <= 2 * B2_WAVES, "record copy split");
+  __shared__ __attribute__((aligned(16))) unsigned char rbuf[2][REC_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char gsh[B2_WAVES][LY::ROWTILE];   // G rows (active group)
+  __shared__ __attribute__((aligned(16))) unsigned char xsh[B2_WAVES][LY::ROWTILE];   // X rows (for X^T)
 
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int rg = lb % nrg;
   const int cb = (lb / nrg) % ncb;
   const int ts = lb / (nrg * ncb);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = wave & 3, chalf = wave >> 2;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int stream = rows.stream[rg][wave];
+  const int stream = rows.stream[rg][slot];
   const bool wv = stream >= 0;
   const int srow = wv ? stream : 0;
   const bool active_grp = rg == 0;
-  const int c0 = cb * B2_CB;
+  const int c0 = cb * B2_CB + chalf * B2_WAVE_CH;   // this wave's channels c0 .. c0+32
   const int64_t NCs = (int64_t)N * C;
   const size_t jbase = (size_t)srow * C + c0;
-  const int cl = c0 + 8 * g4;                   // this lane's 8 channels
+  const int cl = c0 + 8 * g4;                        // this lane's 8 channels
   const bool cv = wv && cl < C;
   const int clc = cl < C ? cl : 0;
-  const uint32_t tokb = (uint32_t)N * C * EB;   // bytes of one token's state
+  const uint32_t tokb = (uint32_t)N * C * EB;        // bytes of one token's state
 
   // proj A operand: W rows, permuted: A row m of j-tile jt -> channel
   // 8*(m/4) + 4*jt + m%4 ; K = 64 logits in two steps.
@@ -614,117 +603,62 @@ __global__ __launch_bounds__(256) void k_bgrad(
   const int tbeg = ts * tok_per_split;
   const int tfin = min(tbeg + tok_per_split, T);
 
-  // cooperative loads of the shared operands of the tile at t0 (16-byte chunks)
-  u32x4 stg[NLOAD];
-  auto load_shared = [&](int t0) {
+  // record of the tile at t0 -> rbuf[b]: 1 KiB per wave-wide 16-byte copy
+  auto dma = [&](int t0, int b) {
+    const unsigned char* g = rec + (size_t)(t0 / B2_TT) * REC_BYTES + lane * 16;
 #pragma unroll
-    for (int r = 0; r < NLOAD; ++r) {
-      const int q = threadIdx.x + 256 * r;
-      const unsigned char* gp;
-      if (q < SG::o_dzrt) {                             // dzr [T][64] (hi, then lo)
-        const int qq = q < SG::DZR ? q : q - SG::DZR;
-        const size_t lo_off = q < SG::DZR ? 0 : (size_t)T * 64;
-        const int per_tok = 64 * EB / 16;
-        const int t = min(t0 + qq / per_tok, T - 1);
-        gp = static_cast<const unsigned char*>(dzr) + (lo_off + (size_t)t * 64) * EB + (qq % per_tok) * 16;
-      } else if (q < SG::o_dh) {                        // dzr^T [48 or 96][Tpad]
-        const int qq = q - SG::o_dzrt;
-        const int per_row = B2_TT * EB / 16;
-        const int prow = qq / per_row;
-        gp = static_cast<const unsigned char*>(dzrt) + ((size_t)prow * Tpad + t0) * EB + (qq % per_row) * 16;
-      } else if (q < SG::o_co) {                        // dh_in [T][C], this block's channels
-        const int qq = q - SG::o_dh;
-        const int per_tok = B2_CB * EB / 16;
-        const int t = min(t0 + qq / per_tok, T - 1);
-        const int c = c0 + (qq % per_tok) * (16 / EB);
-        gp = static_cast<const unsigned char*>(dhin) + ((size_t)t * C + (c < C ? c : 0)) * EB;
-      } else {                                          // coefficient records [T][64] floats
-        const int qq = min(q - SG::o_co, SG::CO - 1);
-        const int t = min(t0 + qq / 16, T - 1);
-        gp = reinterpret_cast<const unsigned char*>(coef + (size_t)t * COEF_STRIDE) + (qq % 16) * 16;
-      }
-      stg[r] = *reinterpret_cast<const u32x4*>(gp);
+    for (int q = 0; q < 2; ++q) {
+      const int c = wave + q * B2_WAVES;
+      if (q == 0 || c < REC_BYTES / 1024)
+        __builtin_amdgcn_global_load_lds((const gbl_void_t*)(g + c * 1024), (lds_void_t*)&rbuf[b][c * 1024], 16, 0, 0);
     }
   };
-  // scatter the staged chunks into the lane-ordered LDS layout
-  auto store_shared = [&]() {
-#pragma unroll
-    for (int r = 0; r < NLOAD; ++r) {
-      const int q = threadIdx.x + 256 * r;
-      const u32x4 v = stg[r];
-      if (q < SG::o_dzrt) {
-        const int half = q < SG::DZR ? 0 : 1;
-        const int qq = q - half * SG::DZR;
-        if constexpr (BF) {                             // chunk = one 8-element fragment piece
-          const int t = qq >> 3, j = qq & 7, ks = j >> 2, g = j & 3;
-          *reinterpret_cast<u32x4*>(&stage[LY::DZR + half * LY::DZR_HALF + (((ks * 4 + g) * 16 + t) * 16)]) = v;
-        } else {                                        // chunk = half of a 32-byte piece
-          const int t = qq >> 4, j = qq & 15, jp = j >> 1, h = j & 1, ks = jp >> 2, g = jp & 3;
-          *reinterpret_cast<u32x4*>(&stage[LY::DZR + (((ks * 4 + g) * 16 + t) * 32) + h * 16]) = v;
-        }
-      } else if (q < SG::o_dh) {
-        const int qq = q - SG::o_dzrt;
-        if constexpr (BF) {                             // row of 16 tokens = 2 chunks = 4 pieces
-          const int prow = qq >> 1, h = qq & 1;
-          const int half = prow >= 48 ? 1 : 0, p = prow - 48 * half, pt = p >> 4, rr = p & 15;
-          const int base = LY::DZRT + half * LY::DZRT_HALF;
-          *reinterpret_cast<u32x2*>(&stage[base + ((pt * 4 + 2 * h) * 16 + rr) * 8]) = u32x2{v[0], v[1]};
-          *reinterpret_cast<u32x2*>(&stage[base + ((pt * 4 + 2 * h + 1) * 16 + rr) * 8]) = u32x2{v[2], v[3]};
-        } else {                                        // row of 16 tokens = 4 chunks = 4 pieces
-          const int p = qq >> 2, g = qq & 3, pt = p >> 4, rr = p & 15;
-          *reinterpret_cast<u32x4*>(&stage[LY::DZRT + ((pt * 4 + g) * 16 + rr) * 16]) = v;
-        }
-      } else if (q < SG::o_co) {
-        const int qq = q - SG::o_dh;
-        if constexpr (BF) {
-          const int t = qq >> 2, g = qq & 3;
-          *reinterpret_cast<u32x4*>(&stage[LY::DH + (g * 16 + t) * 16]) = v;
-        } else {
-          const int t = qq >> 3, j = qq & 7, g = j >> 1, h = j & 1;
-          *reinterpret_cast<u32x4*>(&stage[LY::DH + (g * 16 + t) * 32 + h * 16]) = v;
-        }
-      } else if (q < NCHUNK) {
-        const int qq = q - SG::o_co;
-        const int t = qq >> 4, j = qq & 15;
-        float* co = reinterpret_cast<float*>(&stage[LY::CO]);
-        co[(4 * j + 0) * 16 + t] = __uint_as_float(v[0]);
-        co[(4 * j + 1) * 16 + t] = __uint_as_float(v[1]);
-        co[(4 * j + 2) * 16 + t] = __uint_as_float(v[2]);
-        co[(4 * j + 3) * 16 + t] = __uint_as_float(v[3]);
-      }
-    }
-  };
-  // own rows of the tile at t0
-  V8<E> xo, dvo;
+  // own pieces of the tile at t0
+  V8<E> xo, dvo, dho;
   auto load_own = [&](int t0) {
     const int t = min(t0 + r16, T - 1);
     xo = V8<E>::load(xbase, (size_t)t * xstride + clc);
     dvo = V8<E>::load(dXn, ((size_t)t * N + srow) * C + clc);
+    dho = V8<E>::load(dhin, (size_t)t * C + clc);
+  };
+  // dX of a finished tile, by a buffer store based at that tile: an
+  // out-of-range offset (ragged token or channel tail, or no tile yet) is
+  // dropped by the hardware
+  V8<E> res = V8<E>::zero();
+  uint32_t res_off = 0x80000000u;
+  int res_t0 = 0;
+  auto store_res = [&]() {
+    const rsrc_t rdx = make_rsrc(static_cast<char*>(dX) + (size_t)res_t0 * tokb, (uint32_t)B2_TT * tokb);
+    bstore<E, 8>(res, rdx, res_off, 0);
   };
   const int rowoff = g4 * LY::GSTRIDE + r16 * 8 * EB;      // this lane's slot in a row tile
 
   if (tbeg < tfin) {
-    load_shared(tbeg);
+    dma(tbeg, 0);
     load_own(tbeg);
   }
+  int buf = 0;
   for (int t0 = tbeg; t0 < tfin; t0 += B2_TT) {
     const int tk = t0 + r16;
     const bool tv = tk < T;
-    // this tile's operands were loaded one iteration ago: publish them, then
-    // start the next tile's loads before the arithmetic.  The loads are
-    // unconditional (the last tile reloads itself) so that the number of
-    // outstanding memory operations is static and waits stay exact.
-    store_shared();
+    // this tile's record copy and own loads (issued one iteration ago) have
+    // landed; the other waves' copies are covered by the barrier below
+    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0)
     V8<E> xc = xo, dvc = dvo;
+    const V8<E> dhc = dho;
     if (!(tv && cv)) { xc = V8<E>::zero(); dvc = V8<E>::zero(); }
-    {
-      const int tn = t0 + B2_TT < tfin ? t0 + B2_TT : t0;
-      load_shared(tn);
-      load_own(tn);
-    }
+    store_res();
     if (active_grp) *reinterpret_cast<V8<E>*>(&gsh[wave][rowoff]) = dvc;
     *reinterpret_cast<V8<E>*>(&xsh[wave][rowoff]) = xc;
+    {
+      // next tile's loads; the last tile reloads itself so that every wave
+      // issues the same memory operations in every iteration
+      const int tn = t0 + B2_TT < tfin ? t0 + B2_TT : t0;
+      dma(tn, buf ^ 1);
+      load_own(tn);
+    }
     __syncthreads();
+    const unsigned char* rb = rbuf[buf];
 
     // ---- proj on MFMA: D[c][t], 2 j-tiles ----
     f32x4 pj[2];
@@ -732,9 +666,9 @@ __global__ __launch_bounds__(256) void k_bgrad(
       V8<E> bz[2], bzl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int off = ((ks * 4 + g4) * 16 + r16) * 8 * EB;
-        bz[ks] = *reinterpret_cast<const V8<E>*>(&stage[LY::DZR + off]);
-        if constexpr (BF) bzl[ks] = *reinterpret_cast<const V8<E>*>(&stage[LY::DZR + LY::DZR_HALF + off]);
+        const int off = REC_DZR + ((ks * 4 + g4) * 16 + r16) * 8 * EB;
+        bz[ks] = *reinterpret_cast<const V8<E>*>(rb + off);
+        if constexpr (BF) bzl[ks] = *reinterpret_cast<const V8<E>*>(rb + off + rec_dzr_half(EB));
       }
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
@@ -750,9 +684,9 @@ __global__ __launch_bounds__(256) void k_bgrad(
     }
     // ---- assemble dX for (token tk, channels cl..cl+8) ----
     {
-      const float* co = reinterpret_cast<const float*>(&stage[LY::CO]);
-      const float hpre = co[(CO_PRE + srow) * 16 + r16];
-      const float gam = co[CO_GAMMA * 16 + r16];
+      const float* co = reinterpret_cast<const float*>(rb + REC_CO);
+      const float hpre = co[(RF_PRE + srow) * B2_TT + r16];
+      const float gam = co[RF_GAMMA * B2_TT + r16];
       float pass[8];
       if (active_grp) {
 #pragma unroll
@@ -760,8 +694,8 @@ __global__ __launch_bounds__(256) void k_bgrad(
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           if (a < k) {
-            const float h = co[(CO_RES + a * 4 + wave) * 16 + r16];
-            const V8<E> gv = *reinterpret_cast<const V8<E>*>(&gsh[a][rowoff]);
+            const float h = co[(RF_RES + a * 4 + slot) * B2_TT + r16];
+            const V8<E> gv = *reinterpret_cast<const V8<E>*>(&gsh[a + 4 * chalf][rowoff]);
             float gf[8];
             gv.to_float(gf);
 #pragma unroll
@@ -771,10 +705,9 @@ __global__ __launch_bounds__(256) void k_bgrad(
       } else {
         dvc.to_float(pass);
       }
-      const V8<E> hv = *reinterpret_cast<const V8<E>*>(&stage[LY::DH + (g4 * 16 + r16) * 8 * EB]);
       float xf[8], hf[8], o[8];
       xc.to_float(xf);
-      hv.to_float(hf);
+      dhc.to_float(hf);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int jt = q >> 2, e = q & 3;              // channel 8*g4 + q = 8*g4 + 4*jt + e
@@ -784,20 +717,18 @@ __global__ __launch_bounds__(256) void k_bgrad(
         v = fmaf(-gam, xf[q], v);
         o[q] = v;
       }
-      // buffer store based at this tile; an out-of-range offset (ragged
-      // token or channel tail) is dropped by the hardware
-      const rsrc_t rdx = make_rsrc(static_cast<char*>(dX) + (size_t)t0 * tokb, (uint32_t)B2_TT * tokb);
-      const uint32_t voff = (tv && cv) ? ((uint32_t)r16 * N + srow) * (uint32_t)C * EB + cl * EB : 0x80000000u;
-      bstore<E, 8>(V8<E>::from_float(o), rdx, voff, 0);
+      res = V8<E>::from_float(o);
+      res_t0 = t0;
+      res_off = (tv && cv) ? ((uint32_t)r16 * N + srow) * (uint32_t)C * EB + cl * EB : 0x80000000u;
     }
     // ---- dW on MFMA: A = X^T (rows = channels, K = 16 tokens) ----
     {
       Vec<E, 4> bh[3], bl[3];
 #pragma unroll
       for (int pt = 0; pt < 3; ++pt) {
-        const int off = ((pt * 4 + g4) * 16 + r16) * 4 * EB;
-        bh[pt] = *reinterpret_cast<const Vec<E, 4>*>(&stage[LY::DZRT + off]);
-        if constexpr (BF) bl[pt] = *reinterpret_cast<const Vec<E, 4>*>(&stage[LY::DZRT + LY::DZRT_HALF + off]);
+        const int off = REC_DZRT + ((pt * 4 + g4) * 16 + r16) * 4 * EB;
+        bh[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off);
+        if constexpr (BF) bl[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off + rec_dzrt_half(EB));
       }
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
@@ -823,8 +754,10 @@ __global__ __launch_bounds__(256) void k_bgrad(
         }
       }
     }
-    __syncthreads();          // every read of the stage and of gsh/xsh is done
+    __syncthreads();          // every read of rbuf[buf] and of gsh/xsh is done
+    buf ^= 1;
   }
+  store_res();
   // dW partial rows: D row 4*g4+e of j-tile jt = channel 16*jt + 4*g4 + e
   if (wv) {
 #pragma unroll
@@ -897,8 +830,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   float* dpart = reinterpret_cast<float*>(ws + p.off_dpart);
   float* dwpart = reinterpret_cast<float*>(ws + p.off_dwpart);
   float* dz = reinterpret_cast<float*>(ws + p.off_dz);
-  void* dzr = ws + p.off_dzr;
-  void* dzrt = ws + p.off_dzrt;
+  unsigned char* rec = reinterpret_cast<unsigned char*>(ws + p.off_rec);
   float* dwp = reinterpret_cast<float*>(ws + p.off_dwpart2);
   const StreamRows src = stream_rows(p, a->X, a->xact, a->active);
   Act4 act;
@@ -928,7 +860,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
     TimedLaunch tl(tm, KID_BCOEF, st);
     const int nb = (int)((p.Tpad + BCOEF_TOK - 1) / BCOEF_TOK);
     const size_t shm = (size_t)BCOEF_TOK * (p.iters + 1) * 16 * sizeof(float);
-    k_bcoef<E><<<nb, 64, shm, st>>>(dpart, p.b1_cblocks, zin, a->bias, coef, dz, dzr, dzrt, p.T, p.Tpad, p.N,
+    k_bcoef<E><<<nb, 64, shm, st>>>(dpart, p.b1_cblocks, zin, a->bias, coef, dz, rec, p.T, p.Tpad, p.N,
                                     p.k, p.nc, p.P, 1.0f / (float)p.NC, p.iters, p.gate == XHC_GATE_UNIT);
   }
   {
@@ -946,8 +878,8 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
       ++nxt;
     }
     const int nb = p.b2_rowgroups * p.b2_cblocks * p.b2_ts;
-    k_bgrad<E><<<nb, 256, 0, st>>>(src, a->dX_new, a->dh_in, coef, Wp, dzr, dzrt, a->dX, dwp, p.T, p.Tpad, p.C,
-                                   p.N, p.k, rows, p.b2_rowgroups, p.b2_cblocks, p.b2_tok_per_split);
+    k_bgrad<E><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, a->dX, dwp, p.T, p.C, p.N, p.k,
+                                             rows, p.b2_rowgroups, p.b2_cblocks, p.b2_tok_per_split);
   }
   {
     TimedLaunch tl(tm, KID_BREDUCE, st);

@@ -14,9 +14,8 @@ namespace xhc {
 //   [16, 32)  H_post[a*4 + m]
 //   [32, 48)  H_res[a*4 + b]
 //   48        r (RMS of the flattened state)
-//   49        gamma = (dz . (z - bias)) / (N*C*r^2), backward only
 constexpr int COEF_STRIDE = 64;
-constexpr int CO_PRE = 0, CO_POST = 16, CO_RES = 32, CO_R = 48, CO_GAMMA = 49;
+constexpr int CO_PRE = 0, CO_POST = 16, CO_RES = 32, CO_R = 48;
 
 // Per-token backward dot record (floats, per channel block of B1):
 //   [0, 16)   dH_pre[i]      = <dh_in, X_i>
@@ -31,9 +30,26 @@ constexpr int MIX_TARGET_WAVES = 2560;   // grid size aimed at ~one resident rou
 constexpr int B1_CH = 2;          // channels per lane in B1's TFA part
 constexpr int B1_WAVE_CH = 128;   // channels per B1 wave (64 lanes x 2)
 constexpr int B1_WAVES = 4;       // waves per B1 workgroup (consecutive chunks)
-constexpr int B2_CB = 32;         // channels per B2 wave row
+constexpr int B2_WAVE_CH = 32;    // channels per B2 wave (one state row)
+constexpr int B2_CB = 64;         // channels per B2 workgroup: whole 128-byte lines of a bf16 row
+constexpr int B2_WAVES = 8;       // 4 rows x 2 channel halves
 constexpr int B2_TT = 16;         // tokens per B2 tile
-constexpr int B2_TARGET_WG = 1536;  // B2 grid aimed at two rounds of 3 workgroups per CU
+constexpr int B2_TARGET_WG = 512;   // B2 grid aimed at one resident round of 2 workgroups per CU
+
+// Per-tile backward record (B2_TT tokens), written by the coefficient
+// backward kernel and copied verbatim into LDS by B2, so its layout is the
+// order in which B2's lanes read it (lane = g*16 + r):
+//   [REC_DZR,  +4096)  dz/r as the projection MFMA's B fragments:
+//                      [half][ks 2][g 4][t 16] x 8 elements, logit p = 32ks + 8g + e
+//   [REC_DZRT, +3072)  dz/r as the dW MFMA's B fragments:
+//                      [half][pt 3][g 4][r 16] x 4 elements, logit 16pt + r, token 4g + e
+//   [REC_CO,   +2304)  coefficients [field 36][t 16] floats: H_pre[16], H_res[16], gamma
+// half = bf16 hi and lo parts (bf16 storage) or one fp32 part (fp32 storage).
+constexpr int REC_BYTES = 10240;
+constexpr int REC_DZR = 0, REC_DZRT = 4096, REC_CO = 7168;
+constexpr int RF_PRE = 0, RF_RES = 16, RF_GAMMA = 32, REC_NF = 36;
+constexpr int rec_dzr_half(int esz) { return 2 * 4 * 16 * 8 * esz; }
+constexpr int rec_dzrt_half(int esz) { return 3 * 4 * 16 * 4 * esz; }
 
 struct Plan {
   int B, S, C, N, k, nc, P, NT, T, iters, dtype, gate;
@@ -58,7 +74,7 @@ struct Plan {
   int64_t Tpad;       // T rounded up to B2_TT
   // workspace layout (byte offsets; every region 256-byte aligned)
   size_t off_wt, off_zpart, off_coef, fwd_bytes;
-  size_t off_zbuf, off_wp, off_dpart, off_dwpart, off_dz, off_dzr, off_dzrt, off_dwpart2, bwd_bytes;
+  size_t off_zbuf, off_wp, off_dpart, off_dwpart, off_dz, off_rec, off_dwpart2, bwd_bytes;
 };
 
 // Fills `p` from `d`; returns XHC_OK or an XHC_ERR_* code for an
