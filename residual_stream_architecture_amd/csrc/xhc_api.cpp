@@ -65,10 +65,10 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.Tpad = cdiv(T, B2_TT) * B2_TT;
   {
     const int64_t base = (int64_t)q.b2_rowgroups * q.b2_cblocks;
-    const int64_t tiles = q.Tpad / B2_TT;
-    int64_t ts = std::min<int64_t>(std::max<int64_t>(1, (B2_TARGET_WG + base / 2) / base), tiles);
-    const int64_t tiles_per = cdiv(tiles, ts);
-    q.b2_tok_per_split = (int)(tiles_per * B2_TT);
+    const int64_t steps = cdiv(T, B2_TT * B2_SUB);            // iterations of B2_SUB tiles
+    int64_t ts = std::min<int64_t>(std::max<int64_t>(1, (B2_TARGET_WG + base / 2) / base), steps);
+    const int64_t steps_per = cdiv(steps, ts);
+    q.b2_tok_per_split = (int)(steps_per * B2_TT * B2_SUB);
     q.b2_ts = (int)cdiv(T, q.b2_tok_per_split);
   }
 

@@ -550,21 +550,27 @@ template <typename E> struct B2Lds {
 template <typename E>
 __global__ __launch_bounds__(512) void k_bgrad(
     StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin, const void* __restrict__ Wp,
-    const unsigned char* __restrict__ rec, void* dX, float* __restrict__ dwp, int T, int C, int N, int k,
+    const unsigned char* __restrict__ rec, int ntiles, void* dX, float* __restrict__ dwp, int T, int C, int N, int k,
     RowTable rows, int nrg, int ncb, int tok_per_split) {
   constexpr bool BF = E::bytes == 2;
   constexpr int EB = E::bytes;
   using LY = B2Lds<E>;
-  static_assert(REC_BYTES % 1024 == 0 && REC_BYTES / 1024 <= 2 * B2_WAVES, "record copy split");
-  __shared__ __attribute__((aligned(16))) unsigned char rbuf[2][REC_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char gsh[B2_WAVES][LY::ROWTILE];   // G rows (active group)
-  __shared__ __attribute__((aligned(16))) unsigned char xsh[B2_WAVES][LY::ROWTILE];   // X rows (for X^T)
+  constexpr int DHB = B2_TT * B2_CB * EB;              // dh_in block of one tile ([t][B2_CB])
+  constexpr int SBUF = REC_USED + DHB;                 // LDS bytes of one tile's shared operands
+  constexpr int NREC = (REC_USED + 1023) / 1024;       // wave-wide copies of the record (last one partial)
+  constexpr int NCH = NREC + DHB / 1024;
+  constexpr int STEP = B2_TT * B2_SUB;
+  static_assert(REC_USED % 16 == 0 && DHB % 1024 == 0 && REC_USED <= REC_BYTES, "record copy split");
+  __shared__ __attribute__((aligned(16))) unsigned char rbuf[2][B2_SUB][SBUF];
+  __shared__ __attribute__((aligned(16))) unsigned char gsh[B2_SUB][B2_WAVES][LY::ROWTILE];   // dX_new rows
+  __shared__ __attribute__((aligned(16))) unsigned char xsh[B2_SUB][B2_WAVES][LY::ROWTILE];   // X rows
 
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int rg = lb % nrg;
   const int cb = (lb / nrg) % ncb;
   const int ts = lb / (nrg * ncb);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: rsrc and M0 stay scalar
   const int slot = wave & 3, chalf = wave >> 2;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int stream = rows.stream[rg][slot];
@@ -603,32 +609,64 @@ __global__ __launch_bounds__(512) void k_bgrad(
   const int tbeg = ts * tok_per_split;
   const int tfin = min(tbeg + tok_per_split, T);
 
-  // record of the tile at t0 -> rbuf[b]: 1 KiB per wave-wide 16-byte copy
+  // The B2_SUB tiles from t0 -> rbuf[b]: each tile's record, then this
+  // workgroup's dh_in block, by wave-wide 16-byte LDS-DMA copies of 1 KiB
+  // (the record's last copy is partial).  Every copy goes through a buffer
+  // resource based at its tile whose size ends at the data's end, so tiles
+  // and tokens past the end read zeros.
+  const uint32_t dhrowb = (uint32_t)C * EB;
   auto dma = [&](int t0, int b) {
-    const unsigned char* g = rec + (size_t)(t0 / B2_TT) * REC_BYTES + lane * 16;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int c = wave + q * B2_WAVES;
-      if (q == 0 || c < REC_BYTES / 1024)
-        __builtin_amdgcn_global_load_lds((const gbl_void_t*)(g + c * 1024), (lds_void_t*)&rbuf[b][c * 1024], 16, 0, 0);
+    for (int s = 0; s < B2_SUB; ++s) {
+      const int ta = t0 + s * B2_TT;
+      const int tile = ta / B2_TT;
+      const rsrc_t rrec = make_rsrc(rec + (size_t)tile * REC_BYTES, tile < ntiles ? REC_BYTES : 0u);
+      const rsrc_t rdh = make_rsrc(static_cast<const char*>(dhin) + (size_t)ta * dhrowb,
+                                   clamp_bytes(ta < T ? T - ta : 0, dhrowb));
+#pragma unroll
+      for (int q = 0; q < (NCH + B2_WAVES - 1) / B2_WAVES; ++q) {
+        const int c = wave + q * B2_WAVES;
+        if (c < NREC) {
+          if (c * 1024 + lane * 16 < REC_USED)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rrec, (lds_void_t*)&rbuf[b][s][c * 1024], 16,
+                                                     c * 1024 + lane * 16, 0, 0, 0);
+        } else if (c < NCH) {
+          constexpr int PPT = B2_CB * EB / 16;             // 16-byte pieces per token
+          const int e = (c - NREC) * 64 + lane;
+          const uint32_t voff = ((uint32_t)(e / PPT) * C + cb * B2_CB + (e % PPT) * (16 / EB)) * EB;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rdh, (lds_void_t*)&rbuf[b][s][REC_USED + (c - NREC) * 1024], 16,
+                                                   voff, 0, 0, 0);
+        }
+      }
     }
   };
-  // own pieces of the tile at t0
-  V8<E> xo, dvo, dho;
+  // own rows of the B2_SUB tiles from t0, through buffer resources based at
+  // each tile (tokens past the end read zeros)
+  V8<E> xo[B2_SUB], dvo[B2_SUB];
+  const uint32_t xrowb = (uint32_t)xstride * EB;
+  const uint32_t vx = ((uint32_t)r16 * (uint32_t)xstride + clc) * EB;
+  const uint32_t vd = (((uint32_t)r16 * N + srow) * (uint32_t)C + clc) * EB;
   auto load_own = [&](int t0) {
-    const int t = min(t0 + r16, T - 1);
-    xo = V8<E>::load(xbase, (size_t)t * xstride + clc);
-    dvo = V8<E>::load(dXn, ((size_t)t * N + srow) * C + clc);
-    dho = V8<E>::load(dhin, (size_t)t * C + clc);
+#pragma unroll
+    for (int s = 0; s < B2_SUB; ++s) {
+      const int ta = t0 + s * B2_TT;
+      const int left = ta < T ? T - ta : 0;
+      const rsrc_t rx = make_rsrc(static_cast<const char*>(xbase) + (size_t)ta * xrowb, clamp_bytes(left, xrowb));
+      const rsrc_t rd = make_rsrc(static_cast<const char*>(dXn) + (size_t)ta * tokb, clamp_bytes(left, tokb));
+      xo[s] = bload<E, 8>(rx, vx, 0);
+      dvo[s] = bload<E, 8>(rd, vd, 0);
+    }
   };
-  // dX of a finished tile, by a buffer store based at that tile: an
+  // dX of finished tiles, by buffer stores based at each tile: an
   // out-of-range offset (ragged token or channel tail, or no tile yet) is
-  // dropped by the hardware
+  // dropped by the hardware.  The last tile of a step is stored at the top
+  // of the next step, ahead of its prefetch.
   V8<E> res = V8<E>::zero();
   uint32_t res_off = 0x80000000u;
   int res_t0 = 0;
   auto store_res = [&]() {
-    const rsrc_t rdx = make_rsrc(static_cast<char*>(dX) + (size_t)res_t0 * tokb, (uint32_t)B2_TT * tokb);
+    const rsrc_t rdx =
+        make_rsrc(static_cast<char*>(dX) + (size_t)(res_t0 + (B2_SUB - 1) * B2_TT) * tokb, (uint32_t)B2_TT * tokb);
     bstore<E, 8>(res, rdx, res_off, 0);
   };
   const int rowoff = g4 * LY::GSTRIDE + r16 * 8 * EB;      // this lane's slot in a row tile
@@ -638,123 +676,143 @@ __global__ __launch_bounds__(512) void k_bgrad(
     load_own(tbeg);
   }
   int buf = 0;
-  for (int t0 = tbeg; t0 < tfin; t0 += B2_TT) {
-    const int tk = t0 + r16;
-    const bool tv = tk < T;
-    // this tile's record copy and own loads (issued one iteration ago) have
+  for (int t0 = tbeg; t0 < tfin; t0 += STEP) {
+    // these tiles' copies and own loads (issued one iteration ago) have
     // landed; the other waves' copies are covered by the barrier below
     __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0)
-    V8<E> xc = xo, dvc = dvo;
-    const V8<E> dhc = dho;
-    if (!(tv && cv)) { xc = V8<E>::zero(); dvc = V8<E>::zero(); }
+    // publish the own rows (zero outside the sequence or the channels), which
+    // frees their registers for the next prefetch
+#pragma unroll
+    for (int s = 0; s < B2_SUB; ++s) {
+      const bool ok = t0 + s * B2_TT + r16 < T && cv;
+      *reinterpret_cast<V8<E>*>(&xsh[s][wave][rowoff]) = ok ? xo[s] : V8<E>::zero();
+      *reinterpret_cast<V8<E>*>(&gsh[s][wave][rowoff]) = ok ? dvo[s] : V8<E>::zero();
+    }
     store_res();
-    if (active_grp) *reinterpret_cast<V8<E>*>(&gsh[wave][rowoff]) = dvc;
-    *reinterpret_cast<V8<E>*>(&xsh[wave][rowoff]) = xc;
     {
-      // next tile's loads; the last tile reloads itself so that every wave
+      // next tiles' loads; the last step reloads itself so that every wave
       // issues the same memory operations in every iteration
-      const int tn = t0 + B2_TT < tfin ? t0 + B2_TT : t0;
+      const int tn = t0 + STEP < tfin ? t0 + STEP : t0;
       dma(tn, buf ^ 1);
       load_own(tn);
     }
+    res_t0 = t0;
     __syncthreads();
-    const unsigned char* rb = rbuf[buf];
+#pragma unroll
+    for (int s = 0; s < B2_SUB; ++s) {
+      __builtin_amdgcn_sched_barrier(0);      // keep the tiles' live ranges apart
+      const int tk = t0 + s * B2_TT + r16;
+      const bool tv = tk < T;
+      const unsigned char* rb = rbuf[buf][s];
 
-    // ---- proj on MFMA: D[c][t], 2 j-tiles ----
-    f32x4 pj[2];
-    {
-      V8<E> bz[2], bzl[2];
+      // ---- proj on MFMA: D[c][t], 2 j-tiles ----
+      f32x4 pj[2];
+      {
+        V8<E> bz[2], bzl[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int off = REC_DZR + ((ks * 4 + g4) * 16 + r16) * 8 * EB;
-        bz[ks] = *reinterpret_cast<const V8<E>*>(rb + off);
-        if constexpr (BF) bzl[ks] = *reinterpret_cast<const V8<E>*>(rb + off + rec_dzr_half(EB));
-      }
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma32(wa[jt][0], bz[0], acc);
-        acc = mma32(wa[jt][1], bz[1], acc);
-        if constexpr (BF) {
-          acc = mma32(wa[jt][0], bzl[0], acc);
-          acc = mma32(wa[jt][1], bzl[1], acc);
+        for (int ks = 0; ks < 2; ++ks) {
+          const int off = REC_DZR + ((ks * 4 + g4) * 16 + r16) * 8 * EB;
+          bz[ks] = *reinterpret_cast<const V8<E>*>(rb + off);
+          if constexpr (BF) bzl[ks] = *reinterpret_cast<const V8<E>*>(rb + off + rec_dzr_half(EB));
         }
-        pj[jt] = acc;
-      }
-    }
-    // ---- assemble dX for (token tk, channels cl..cl+8) ----
-    {
-      const float* co = reinterpret_cast<const float*>(rb + REC_CO);
-      const float hpre = co[(RF_PRE + srow) * B2_TT + r16];
-      const float gam = co[RF_GAMMA * B2_TT + r16];
-      float pass[8];
-      if (active_grp) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) pass[q] = 0.f;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          if (a < k) {
-            const float h = co[(RF_RES + a * 4 + slot) * B2_TT + r16];
-            const V8<E> gv = *reinterpret_cast<const V8<E>*>(&gsh[a + 4 * chalf][rowoff]);
-            float gf[8];
-            gv.to_float(gf);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) pass[q] = fmaf(h, gf[q], pass[q]);
+        for (int jt = 0; jt < 2; ++jt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mma32(wa[jt][0], bz[0], acc);
+          acc = mma32(wa[jt][1], bz[1], acc);
+          if constexpr (BF) {
+            acc = mma32(wa[jt][0], bzl[0], acc);
+            acc = mma32(wa[jt][1], bzl[1], acc);
           }
+          pj[jt] = acc;
         }
-      } else {
-        dvc.to_float(pass);
       }
-      float xf[8], hf[8], o[8];
-      xc.to_float(xf);
-      dhc.to_float(hf);
+      // ---- assemble dX for (token tk, channels cl..cl+8) ----
+      {
+        const float* co = reinterpret_cast<const float*>(rb + REC_CO);
+        const float hpre = co[(RF_PRE + srow) * B2_TT + r16];
+        const float gam = co[RF_GAMMA * B2_TT + r16];
+        float pass[8];
+        if (active_grp) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int jt = q >> 2, e = q & 3;              // channel 8*g4 + q = 8*g4 + 4*jt + e
-        float v = pass[q];
-        v = fmaf(hpre, hf[q], v);
-        v += pj[jt][e];
-        v = fmaf(-gam, xf[q], v);
-        o[q] = v;
-      }
-      res = V8<E>::from_float(o);
-      res_t0 = t0;
-      res_off = (tv && cv) ? ((uint32_t)r16 * N + srow) * (uint32_t)C * EB + cl * EB : 0x80000000u;
-    }
-    // ---- dW on MFMA: A = X^T (rows = channels, K = 16 tokens) ----
-    {
-      Vec<E, 4> bh[3], bl[3];
+          for (int q = 0; q < 8; ++q) pass[q] = 0.f;
 #pragma unroll
-      for (int pt = 0; pt < 3; ++pt) {
-        const int off = REC_DZRT + ((pt * 4 + g4) * 16 + r16) * 4 * EB;
-        bh[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off);
-        if constexpr (BF) bl[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off + rec_dzrt_half(EB));
-      }
+          for (int a = 0; a < 4; ++a) {
+            if (a < k) {
+              const float h = co[(RF_RES + a * 4 + slot) * B2_TT + r16];
+              const V8<E> gv = *reinterpret_cast<const V8<E>*>(&gsh[s][a + 4 * chalf][rowoff]);
+              float gf[8];
+              gv.to_float(gf);
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        // channel cc = 16*jt + r16 of tokens 4*g4 .. 4*g4+3: entry [cc/8][t], element cc%8
-        const int cc = 16 * jt + r16;
-        const unsigned char* colp = &xsh[wave][(cc >> 3) * LY::GSTRIDE + (cc & 7) * EB];
-        Vec<E, 4> xa;
-        if constexpr (BF) {
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const unsigned lo16 = *reinterpret_cast<const uint16_t*>(colp + (4 * g4 + 2 * q) * 8 * EB);
-            const unsigned hi16 = *reinterpret_cast<const uint16_t*>(colp + (4 * g4 + 2 * q + 1) * 8 * EB);
-            xa.w[q] = lo16 | (hi16 << 16);
+              for (int q = 0; q < 8; ++q) pass[q] = fmaf(h, gf[q], pass[q]);
+            }
           }
         } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) xa.x[q] = *reinterpret_cast<const float*>(colp + (4 * g4 + q) * 8 * EB);
+          const V8<E> gv = *reinterpret_cast<const V8<E>*>(&gsh[s][wave][rowoff]);
+          gv.to_float(pass);
         }
+        const V8<E> hv =
+            *reinterpret_cast<const V8<E>*>(rb + REC_USED + (r16 * B2_CB + chalf * B2_WAVE_CH + 8 * g4) * EB);
+        const V8<E> xv = *reinterpret_cast<const V8<E>*>(&xsh[s][wave][rowoff]);
+        float xf[8], hf[8], o[8];
+        xv.to_float(xf);
+        hv.to_float(hf);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int jt = q >> 2, e = q & 3;              // channel 8*g4 + q = 8*g4 + 4*jt + e
+          float v = pass[q];
+          v = fmaf(hpre, hf[q], v);
+          v += pj[jt][e];
+          v = fmaf(-gam, xf[q], v);
+          o[q] = v;
+        }
+        const V8<E> ov = V8<E>::from_float(o);
+        const uint32_t off = (tv && cv) ? ((uint32_t)r16 * N + srow) * (uint32_t)C * EB + cl * EB : 0x80000000u;
+        if (s + 1 < B2_SUB) {
+          // stored now: it completes well before the next top-of-loop wait
+          const rsrc_t rdx =
+              make_rsrc(static_cast<char*>(dX) + (size_t)(t0 + s * B2_TT) * tokb, (uint32_t)B2_TT * tokb);
+          bstore<E, 8>(ov, rdx, off, 0);
+        } else {
+          res = ov;          // the last tile's store is issued at the top of the next step
+          res_off = off;
+        }
+      }
+      // ---- dW on MFMA: A = X^T (rows = channels, K = 16 tokens) ----
+      {
+        Vec<E, 4> bh[3], bl[3];
 #pragma unroll
         for (int pt = 0; pt < 3; ++pt) {
-          dwacc[jt][pt] = mma16(xa, bh[pt], dwacc[jt][pt]);
-          if constexpr (BF) dwacc[jt][pt] = mma16(xa, bl[pt], dwacc[jt][pt]);
+          const int off = REC_DZRT + ((pt * 4 + g4) * 16 + r16) * 4 * EB;
+          bh[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off);
+          if constexpr (BF) bl[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off + rec_dzrt_half(EB));
+        }
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          // channel cc = 16*jt + r16 of tokens 4*g4 .. 4*g4+3: entry [cc/8][t], element cc%8
+          const int cc = 16 * jt + r16;
+          const unsigned char* colp = &xsh[s][wave][(cc >> 3) * LY::GSTRIDE + (cc & 7) * EB];
+          Vec<E, 4> xa;
+          if constexpr (BF) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const unsigned lo16 = *reinterpret_cast<const uint16_t*>(colp + (4 * g4 + 2 * q) * 8 * EB);
+              const unsigned hi16 = *reinterpret_cast<const uint16_t*>(colp + (4 * g4 + 2 * q + 1) * 8 * EB);
+              xa.w[q] = lo16 | (hi16 << 16);
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xa.x[q] = *reinterpret_cast<const float*>(colp + (4 * g4 + q) * 8 * EB);
+          }
+#pragma unroll
+          for (int pt = 0; pt < 3; ++pt) {
+            dwacc[jt][pt] = mma16(xa, bh[pt], dwacc[jt][pt]);
+            if constexpr (BF) dwacc[jt][pt] = mma16(xa, bl[pt], dwacc[jt][pt]);
+          }
         }
       }
     }
-    __syncthreads();          // every read of rbuf[buf] and of gsh/xsh is done
+    __syncthreads();          // every read of this step's buffers and row tiles is done
     buf ^= 1;
   }
   store_res();
@@ -878,7 +936,8 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
       ++nxt;
     }
     const int nb = p.b2_rowgroups * p.b2_cblocks * p.b2_ts;
-    k_bgrad<E><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, a->dX, dwp, p.T, p.C, p.N, p.k,
+    k_bgrad<E><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, (int)(p.Tpad / B2_TT), a->dX, dwp,
+                                             p.T, p.C, p.N, p.k,
                                              rows, p.b2_rowgroups, p.b2_cblocks, p.b2_tok_per_split);
   }
   {

@@ -130,6 +130,12 @@ template <typename E> using V8 = Vec<E, 8>;
 // resource's size return zero; writes past it are dropped.
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// rows * row_bytes as a buffer size, saturated below 4 GiB
+__device__ inline uint32_t clamp_bytes(int rows, uint32_t row_bytes) {
+  const uint64_t b = (uint64_t)(uint32_t)rows * row_bytes;
+  return b > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)b;
+}
+
 __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }

@@ -33,7 +33,8 @@ constexpr int B1_WAVES = 4;       // waves per B1 workgroup (consecutive chunks)
 constexpr int B2_WAVE_CH = 32;    // channels per B2 wave (one state row)
 constexpr int B2_CB = 64;         // channels per B2 workgroup: whole 128-byte lines of a bf16 row
 constexpr int B2_WAVES = 8;       // 4 rows x 2 channel halves
-constexpr int B2_TT = 16;         // tokens per B2 tile
+constexpr int B2_TT = 16;         // tokens per B2 tile (one MFMA K / N extent)
+constexpr int B2_SUB = 2;         // tiles per B2 iteration (loaded together, one iteration ahead)
 constexpr int B2_TARGET_WG = 512;   // B2 grid aimed at one resident round of 2 workgroups per CU
 
 // Per-tile backward record (B2_TT tokens), written by the coefficient
@@ -46,6 +47,7 @@ constexpr int B2_TARGET_WG = 512;   // B2 grid aimed at one resident round of 2 
 //   [REC_CO,   +2304)  coefficients [field 36][t 16] floats: H_pre[16], H_res[16], gamma
 // half = bf16 hi and lo parts (bf16 storage) or one fp32 part (fp32 storage).
 constexpr int REC_BYTES = 10240;
+constexpr int REC_USED = 9472;   // bytes of a record that carry data (the rest pads to 1 KiB)
 constexpr int REC_DZR = 0, REC_DZRT = 4096, REC_CO = 7168;
 constexpr int RF_PRE = 0, RF_RES = 16, RF_GAMMA = 32, REC_NF = 36;
 constexpr int rec_dzr_half(int esz) { return 2 * 4 * 16 * 8 * esz; }
