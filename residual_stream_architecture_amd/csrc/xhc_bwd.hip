@@ -537,9 +537,6 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpart, i
 // gradients G_a are exchanged through LDS; all of a tile's rows are read (a
 // tile earlier) before any is written, so dX may alias dX_new.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void gbl_void_t;
-
 template <typename E> struct B2Lds {
   static constexpr int EB = E::bytes;
   // per-wave row tiles ([g][t] x 8 elements, group stride padded by 16 B)
@@ -679,7 +676,7 @@ __global__ __launch_bounds__(512) void k_bgrad(
   for (int t0 = tbeg; t0 < tfin; t0 += STEP) {
     // these tiles' copies and own loads (issued one iteration ago) have
     // landed; the other waves' copies are covered by the barrier below
-    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0)
+    wait_vmcnt<0>();
     // publish the own rows (zero outside the sequence or the channels), which
     // frees their registers for the next prefetch
 #pragma unroll

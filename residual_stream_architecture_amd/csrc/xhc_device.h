@@ -129,6 +129,19 @@ template <typename E> using V8 = Vec<E, 8>;
 // byte offset in a VGPR and a uniform byte offset in an SGPR.  Reads past the
 // resource's size return zero; writes past it are dropped.
 // ---------------------------------------------------------------------------
+// LDS and global address-space pointers for the LDS-DMA loads (the LDS
+// destination must be an address-space-3 pointer for the compiler to see
+// the write)
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
+template <int n>
+__device__ inline void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // rows * row_bytes as a buffer size, saturated below 4 GiB
 __device__ inline uint32_t clamp_bytes(int rows, uint32_t row_bytes) {

@@ -46,22 +46,40 @@ __global__ void k_pack_wt(const R* __restrict__ W, R* __restrict__ Wf, int C, in
 
 // ---------------------------------------------------------------------------
 // Projection partials.  Workgroup = (stream `split`, tile of PROJ_TOK
-// tokens); wave w owns two 16-token MFMA row blocks (tokens base + 16f + l%16,
-// f = 0, 1).  The K loop walks the stream's channels 64 at a time (two
-// K=32 MFMA steps), loading the next 64 while the current ones multiply.
+// tokens), PROJ_WAVES waves; wave w owns two 16-token MFMA row blocks
+// (tokens base + 32w + 16f + l%16, f = 0, 1).  The K loop walks the stream's
+// channels in stages of PU K-steps of 32:
+//   * the stage's W fragments (the same for every wave) are copied once per
+//     workgroup into an LDS ring by LDS-DMA loads;
+//   * each lane's state pieces go to a register ring;
+// and the ring keeps PNS-1 stages in flight ahead of the one being
+// multiplied.  The loop holds no stores, so loads complete in order and the
+// per-stage waits count only the younger stages' loads.
 // Stream rows come from `src` (the state, or after an in-place forward the
 // saved active rows for the active streams).
 // Output zpart[split][t][0..16NT) = sum_c X[t,split,c] W[split*C+c, p],
 //        zpart[split][t][16NT]    = sum_c X[t,split,c]^2.
 // ---------------------------------------------------------------------------
+constexpr int PU = 2;     // K-steps per stage
+constexpr int PNS = 4;    // stages in the ring
+
 template <typename E, int NT>
-__global__ __launch_bounds__(256) void k_proj(StreamRows src, const void* __restrict__ Wf,
-                                              float* __restrict__ zpart, int T, int C, int ZST, int ntiles) {
-  constexpr int U = 2;                       // K=32 steps per stage
+__global__ __launch_bounds__(64 * PROJ_WAVES) void k_proj(StreamRows src, const void* __restrict__ Wf,
+                                                          float* __restrict__ zpart, int T, int C, int ZST,
+                                                          int ntiles) {
+  constexpr int EB = E::bytes;
+  constexpr int FB = 512 * EB;                       // bytes of one W fragment
+  constexpr int WST = PU * NT * FB;                  // W bytes per stage
+  constexpr int NCH = WST / 1024;                    // wave-wide 1 KiB copies per stage
+  constexpr int XOPS = PU * 2 * (EB == 2 ? 1 : 2);  // state loads per lane per stage
+  static_assert(WST % 1024 == 0, "stage copy split");
+  __shared__ __attribute__((aligned(16))) unsigned char wring[PNS][WST];
+
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int split = lb / ntiles;
   const int tile = lb - split * ntiles;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int tbase = tile * PROJ_TOK + wave * 32;
   const void* X = src.base[split];
@@ -75,7 +93,10 @@ __global__ __launch_bounds__(256) void k_proj(StreamRows src, const void* __rest
     xrow[f] = (size_t)(tv[f] ? t : 0) * xs;
   }
   const int nks = (C + 31) >> 5;
-  const size_t wbase = (size_t)split * nks * NT * 512 + (size_t)lane * 8;
+  const int nst = (nks + PU - 1) / PU;                 // stages
+  const unsigned char* wsplit = static_cast<const unsigned char*>(Wf) + (size_t)split * nks * NT * FB;
+  // this wave's share of each stage's W copies: chunks wave, wave + PROJ_WAVES, ...
+  const int nmine = NCH > wave ? (NCH - wave + PROJ_WAVES - 1) / PROJ_WAVES : 0;
 
   f32x4 acc[2][NT];
 #pragma unroll
@@ -84,46 +105,82 @@ __global__ __launch_bounds__(256) void k_proj(StreamRows src, const void* __rest
     for (int n = 0; n < NT; ++n) acc[f][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss[2] = {0.f, 0.f};
 
-  V8<E> a[2][U][2], b[2][U][NT];
-  auto load_stage = [&](int buf, int ks0) {
+  V8<E> a[PNS][PU][2];
+  // stage j -> ring slot q: W copies, then this lane's state pieces.  Stages
+  // past the end reload K-step 0 (valid addresses); their data is unused.
+  // Workgroups start their K walk at different stages (and wrap), so that
+  // at any moment the chip reads many different column offsets of the
+  // token rows instead of one column of every row.
+  const int jofs = (int)(((unsigned)tile * 5u + (unsigned)split * 3u) % (unsigned)nst);
+  auto issue = [&](int jv, int q) {
+    const int j = jv + jofs < nst ? jv + jofs : jv + jofs - nst;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ks = ks0 + u;
+    for (int i = 0; i < (NCH + PROJ_WAVES - 1) / PROJ_WAVES; ++i) {
+      const int c = wave + i * PROJ_WAVES;
+      if (c < NCH) {
+        const int fr = c * 1024 / FB;                    // fragment (u, n) of the stage
+        const int u = fr / NT, n = fr - u * NT;
+        const int ks = j * PU + u;
+        const int kw = ks < nks ? ks : 0;
+        const unsigned char* gsrc = wsplit + ((size_t)kw * NT + n) * FB + (c * 1024 - fr * FB) + lane * 16;
+        __builtin_amdgcn_global_load_lds((const gbl_void_t*)gsrc, (lds_void_t*)&wring[q][c * 1024], 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PU; ++u) {
+      const int ks = j * PU + u;
       const int kb = ks * 32 + 8 * g;
       const bool kv = ks < nks && kb < C;
       const int kc = kv ? kb : 0;
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         V8<E> v = V8<E>::load(X, xrow[f] + kc);
-        a[buf][u][f] = (kv && tv[f]) ? v : V8<E>::zero();
+        a[q][u][f] = (kv && tv[f]) ? v : V8<E>::zero();
       }
-      const int kw = ks < nks ? ks : 0;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) b[buf][u][n] = V8<E>::load(Wf, wbase + ((size_t)kw * NT + n) * 512);
     }
   };
-  auto compute_stage = [&](int buf) {
+  auto compute = [&](int q) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < PU; ++u) {
+      V8<E> b[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) b[n] = *reinterpret_cast<const V8<E>*>(&wring[q][(u * NT + n) * FB + lane * 8 * EB]);
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { const float v = a[buf][u][f].f(j); ss[f] = fmaf(v, v, ss[f]); }
+        for (int j = 0; j < 8; ++j) { const float v = a[q][u][f].f(j); ss[f] = fmaf(v, v, ss[f]); }
 #pragma unroll
-        for (int n = 0; n < NT; ++n) acc[f][n] = mma32(a[buf][u][f], b[buf][u][n], acc[f][n]);
+        for (int n = 0; n < NT; ++n) acc[f][n] = mma32(a[q][u][f], b[n], acc[f][n]);
       }
     }
   };
+  // wait for stage j's loads with `younger` later stages issued after it
+  auto wait_stage = [&]() {
+    // per stage this wave issued nmine W copies and XOPS state loads;
+    // PNS - 2 younger stages are in flight when a stage is consumed
+    static_assert(PNS >= 3 && (PNS - 2) * (XOPS + 2) < 64, "ring depth");
+    if (nmine == 2) wait_vmcnt<(PNS - 2) * (XOPS + 2)>();
+    else if (nmine == 1) wait_vmcnt<(PNS - 2) * (XOPS + 1)>();
+    else wait_vmcnt<(PNS - 2) * XOPS>();
+  };
 
-  load_stage(0, 0);
-  int ks0 = 0;
-  for (; ks0 + U < nks; ks0 += 2 * U) {
-    load_stage(1, ks0 + U);
-    compute_stage(0);
-    if (ks0 + 2 * U < nks) load_stage(0, ks0 + 2 * U);
-    compute_stage(1);
+#pragma unroll
+  for (int q = 0; q < PNS - 1; ++q) issue(q < nst ? q : 0, q);
+  // steady state, unrolled by the ring size so that ring slots are static
+  for (int j = 0; j < nst; j += PNS) {
+#pragma unroll
+    for (int q = 0; q < PNS; ++q) {
+      const int jj = j + q;
+      if (jj < nst) {
+        wait_stage();
+        __syncthreads();                           // stage jj's W copies from every wave are in LDS;
+                                                   // every wave is done with slot (q-1)%PNS
+        issue(jj + PNS - 1 < nst ? jj + PNS - 1 : 0, (q + PNS - 1) % PNS);
+        compute(q);
+      }
+    }
   }
-  if (ks0 < nks) compute_stage(0);
+  wait_vmcnt<0>();
 
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
@@ -423,11 +480,11 @@ static void launch_proj(const Plan& p, const StreamRows& src, const void* Wf, fl
   TimedLaunch tl(tm, KID_PROJ, st);
   const int nb = p.proj_tiles * p.SK;
   if (p.NT == 1)
-    k_proj<E, 1><<<nb, 256, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles);
+    k_proj<E, 1><<<nb, 64 * PROJ_WAVES, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles);
   else if (p.NT == 2)
-    k_proj<E, 2><<<nb, 256, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles);
+    k_proj<E, 2><<<nb, 64 * PROJ_WAVES, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles);
   else
-    k_proj<E, 3><<<nb, 256, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles);
+    k_proj<E, 3><<<nb, 64 * PROJ_WAVES, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles);
 }
 
 template <typename E, typename R>

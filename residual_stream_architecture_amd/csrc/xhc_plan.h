@@ -23,7 +23,8 @@ constexpr int CO_PRE = 0, CO_POST = 16, CO_RES = 32, CO_R = 48;
 //   [32, 48)  dH_post[a*4+m] = <G_a, U_m>
 constexpr int DOT_STRIDE = 48;
 
-constexpr int PROJ_TOK = 128;     // tokens per projection workgroup (4 waves x 32)
+constexpr int PROJ_WAVES = 8;     // waves per projection workgroup
+constexpr int PROJ_TOK = 32 * PROJ_WAVES;   // tokens per projection workgroup (32 per wave)
 constexpr int MIX_CH = 2;         // channels per thread in the mix kernel
 constexpr int MIX_THREADS = 256;
 constexpr int MIX_TARGET_WAVES = 2560;   // grid size aimed at ~one resident round
