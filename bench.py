@@ -44,12 +44,12 @@ def parse():
 def kernel_bytes(w, esz):
     """Algorithmic HBM bytes per launch of each main kernel: every input and
     output it must touch, once (per token, in units of C elements):
-      proj   reads the state                                   16C
-      mix    reads state 16C + out C; writes h_in C, 4 rows 4C,
-             saved old rows 4C                                 26C
-      bdots  reads state 16C (12 rows + 4 saved) + G 4C + dh_in C
-             + out C; writes dout C                            23C
-      bgrad  reads state 16C + dX_new 16C + dh_in C; writes dX 16C  49C
+      proj    reads the state                                  16C
+      mix     reads state 16C + out C; writes h_in C, 4 rows 4C,
+              saved old rows 4C                                26C
+      bxdots  reads state 16C (12 rows + 4 saved) + dh_in C + G 4C  21C
+      bdots   reads G 4C + out C; writes dout C                 6C
+      bgrad   reads state 16C + dX_new 16C + dh_in C; writes dX 16C  49C
     plus the projection weights (N*C x P) where a kernel reads them."""
     T, C, N, k, P = w.T, w.C, w.N, w.k, w.P
     unit = T * C * esz
@@ -57,7 +57,8 @@ def kernel_bytes(w, esz):
     return {
         "proj": 16 * unit + wbytes,
         "mix": (N + 1 + 1 + k + k) * unit,
-        "bdots": (N + k + 1 + 1 + 1) * unit,
+        "bxdots": (N + 1 + k) * unit,
+        "bdots": (k + 1 + 1) * unit,
         "bgrad": (N + N + 1 + N) * unit + wbytes,
     }
 
@@ -232,7 +233,7 @@ def main():
 
     # whole-step accounting in units of C per token (bf16)
     alg_step_c = (N + 1 + 1 + k) + (N + N + 1 + 1 + N + 1)        # 22C forward + 51C backward
-    impl_step_c = 16 + 26 + 23 + 49                                 # what the kernels above touch
+    impl_step_c = 16 + 26 + 21 + 6 + 49                             # what the kernels above touch
     step_bytes = alg_step_c * T * C * esz
     result = {
         "metric": METRIC,

@@ -60,6 +60,8 @@ int make_plan(const xhc_desc* d, Plan* p) {
     q.b1_lseg = (int)lseg;
     q.b1_segs = (int)cdiv(q.S, lseg);
   }
+  q.bx_cblocks = (int)cdiv(q.C, BX_CB);
+  q.bx_tiles = (int)cdiv(T, BX_TOK);
   q.b2_rowgroups = 1 + (int)cdiv(q.N - q.k, 4);
   q.b2_cblocks = (int)cdiv(q.C, B2_CB);
   q.Tpad = cdiv(T, B2_TT) * B2_TT;
@@ -82,6 +84,7 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.off_zbuf = o;   o = align256(o + (size_t)T * (q.P + 1) * 4);
   q.off_wp = o;     o = align256(o + (size_t)q.NC * 64 * q.esz);
   q.off_dpart = o;  o = align256(o + (size_t)q.b1_cblocks * T * DOT_STRIDE * 4);
+  q.off_dpa = o;    o = align256(o + (size_t)q.bx_cblocks * T * BX_OUT * 4);
   q.off_dwpart = o; o = align256(o + (q.nc == 4 ? (size_t)q.B * q.b1_segs * q.C * 24 * 4 : 0));
   q.off_dz = o;     o = align256(o + (size_t)T * 48 * 4);
   q.off_rec = o;    o = align256(o + (size_t)(q.Tpad / B2_TT) * REC_BYTES);
@@ -205,7 +208,7 @@ struct xhc_timer {
 };
 
 static const char* const kKernelNames[xhc::KID_COUNT] = {
-    "pack_wt", "proj", "coef", "mix", "pack_wp", "bdots", "bcoef", "bgrad", "breduce"};
+    "pack_wt", "proj", "coef", "mix", "pack_wp", "bdots", "bcoef", "bgrad", "breduce", "bxdots"};
 
 namespace xhc {
 void timer_mark(xhc_timer* tm, int kid, hipStream_t st, bool start) {

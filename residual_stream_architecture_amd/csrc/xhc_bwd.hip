@@ -47,17 +47,113 @@ __global__ void k_pack_wp(const R* __restrict__ W, R* __restrict__ Wp, int64_t N
 }
 
 // ---------------------------------------------------------------------------
-// B1.  Workgroup = 4 waves on 4 consecutive 128-channel chunks of one
-// sequence segment [s0, s1).  Per token:
-//   * X dots on MFMA: A = the 16 state rows (K = the chunk's channels),
-//     B columns = [dh_in, G_0..G_{k-1}, 0...]; D[i][0] = dH_pre[i] and
-//     D[i_b][1+a] = dH_res[a][b] (partial over the chunk).
-//   * TFA part (lane = 2 channels): U_m from a 12-row window of `out`,
-//     dH_post partials (wave-reduced), dU_m scattered into a 12-slot window
-//     of dout accumulators (anti-causal), conv-weight partials.
+// B1x.  The backward's state dots on MFMA.  Workgroup = (channel block of
+// BX_CB = 8 x 64 channels, tile of BX_TOK tokens); wave w owns channels
+// cb*BX_CB + 64w .. +64 (two K=32 steps).  Per token:
+//   D[i][col] = sum_c X[t, i, c] B[c][col],  B columns = [dh_in, G_0..G_{k-1}, ...]
+// so D[i][0] = dH_pre[i] and D[i_b][1+a] = dH_res[a][b] over the wave's
+// channels (columns past k and rows past N are never read).  Each wave keeps
+// the loads of RING-1 tokens in flight; the loop holds no global stores, so
+// loads complete in order and the waits are exact.  Every BX_GRP tokens the
+// 8 waves' partials are summed in LDS in a fixed order (deterministic) into
+// the tile's result buffer, written out once at the end:
+//   dpa[cb][t][0..16) = dH_pre,  dpa[cb][t][16 + a*4 + b] = dH_res[a][b].
+// ---------------------------------------------------------------------------
+template <typename E>
+__global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const void* __restrict__ dXn,
+                                                          const void* __restrict__ dhin, float* __restrict__ dpa,
+                                                          int T, int C, int N, int k, Act4 act, int ncb) {
+  constexpr int EB = E::bytes;
+  constexpr int RING = EB == 2 ? 4 : 2;
+  static_assert(BX_GRP % RING == 0 && BX_TOK % BX_GRP == 0, "ring slots must be static in a group");
+  __shared__ float red[BX_GRP][BX_WAVES][80];
+  __shared__ float res[BX_TOK][BX_OUT];
+
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int cb = lb % ncb;
+  const int tile = lb / ncb;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int c0 = cb * BX_CB + wave * BX_WCH;
+  const int t0 = tile * BX_TOK;
+  const int tn = min(BX_TOK, T - t0);
+
+  // A row r = stream r; B column r = dh_in (r = 0) or G_{r-1}
+  const bool arow = r < N;
+  const void* abase = src.base[arow ? r : 0];
+  const int64_t astr = src.stride[arow ? r : 0];
+  const int brow = (r >= 1 && r <= k) ? act.id[r - 1] : 0;
+  const void* bbase = r == 0 ? dhin : dXn;
+  const int64_t bstr = r == 0 ? (int64_t)C : (int64_t)N * C;
+  const int64_t boff = r == 0 ? 0 : (int64_t)brow * C;
+  int cofs[2];
+  bool kv[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int cc = c0 + 32 * ks + 8 * g;
+    kv[ks] = cc < C;
+    cofs[ks] = kv[ks] ? cc : 0;
+  }
+
+  V8<E> av[RING][2], bv[RING][2];
+  // token t0 + tt (clamped to the tile) -> ring slot q; channels past C are
+  // zeroed in A so that they add nothing
+  auto load = [&](int tt, int q) {
+    const int64_t t = t0 + min(tt, tn - 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const V8<E> x = V8<E>::load(abase, (size_t)(t * astr + cofs[ks]));
+      av[q][ks] = kv[ks] ? x : V8<E>::zero();
+      bv[q][ks] = V8<E>::load(bbase, (size_t)(t * bstr + boff + cofs[ks]));
+    }
+  };
+
+#pragma unroll
+  for (int q = 0; q < RING - 1; ++q) load(q, q);
+  for (int tg = 0; tg < tn; tg += BX_GRP) {
+#pragma unroll
+    for (int u = 0; u < BX_GRP; ++u) {
+      const int q = u % RING;
+      load(tg + u + RING - 1, (u + RING - 1) % RING);
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      d = mma32(av[q][0], bv[q][0], d);
+      d = mma32(av[q][1], bv[q][1], d);
+      // lane (r, g) holds D[4g + e][r]: column r, rows 4g..4g+3
+      if (r <= 4) *reinterpret_cast<f32x4*>(&red[u][wave][r * 16 + 4 * g]) = d;
+    }
+    __syncthreads();
+    if (threadIdx.x < BX_GRP * BX_OUT) {
+      const int u = threadIdx.x / BX_OUT, o = threadIdx.x % BX_OUT;
+      int idx = -1;
+      if (o < 16) {
+        idx = o < N ? o : -1;                                  // D[i][0]
+      } else {
+        const int a = (o - 16) >> 2, b = (o - 16) & 3;
+        if (a < k && b < k) idx = (1 + a) * 16 + act.id[b];    // D[i_b][1 + a]
+      }
+      float sum = 0.f;
+      if (idx >= 0) {
+#pragma unroll
+        for (int w = 0; w < BX_WAVES; ++w) sum += red[u][w][idx];
+      }
+      res[tg + u][o] = sum;
+    }
+    __syncthreads();
+  }
+  for (int j = threadIdx.x; j < tn * BX_OUT; j += 64 * BX_WAVES)
+    dpa[((size_t)cb * T + t0 + j / BX_OUT) * BX_OUT + j % BX_OUT] = res[j / BX_OUT][j % BX_OUT];
+}
+
+// ---------------------------------------------------------------------------
+// B1.  TFA backward.  Workgroup = 4 waves on 4 consecutive 128-channel
+// chunks of one sequence segment [s0, s1).  Per token (lane = 2 channels):
+//   U_m from a 12-row window of `out`, dH_post partials (wave-reduced),
+//   dU_m scattered into a 12-slot window of dout accumulators (anti-causal),
+//   conv-weight partials.
 // Both windows shift by one slot per token (slot 11 = current position).
 // The segment is followed by an 11-token lookahead that only scatters dU
-// into the segment's last dout positions.  The 4 waves' partial dots are
+// into the segment's last dout positions.  The 4 waves' partial dH_post are
 // summed in LDS once per 12 tokens and written per channel block.  All
 // loads are unconditional (clamped addresses, masked values) and the next
 // token's loads are issued before the current token's arithmetic.
@@ -71,7 +167,7 @@ __global__ __launch_bounds__(256) void k_bdots(
     int lseg, int segs_per_seq) {
   using V2 = Vec<E, B1_CH>;
   constexpr int EB = E::bytes;
-  __shared__ float red[B1_WAVES][12][DOT_STRIDE];
+  __shared__ float red[B1_WAVES][12][16];
   const int k = FAST ? 4 : kk;
   (void)N;
   const int NS = FAST ? 16 : N;
@@ -93,15 +189,6 @@ __global__ __launch_bounds__(256) void k_bdots(
   const bool cv = clraw < C;
   const int cl = cv ? clraw : 0;
   const uint32_t voff = (uint32_t)cl * EB;
-  // MFMA lane roles: A row r16 = stream r16; B column r16: 0 = dh_in, 1..k = G
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const bool arow_valid = r16 < NS;
-  const char* abase = static_cast<const char*>(src.base[arow_valid ? r16 : 0]);
-  const size_t astride = (size_t)src.stride[arow_valid ? r16 : 0] * EB;
-  const bool bcol_valid = r16 <= k;
-  const int bcol_row = (r16 >= 1 && r16 <= k) ? act.id[r16 - 1] : 0;
-  const char* bbase = r16 == 0 ? static_cast<const char*>(dhin) : static_cast<const char*>(dXn) + (size_t)bcol_row * rowb;
-  const size_t bstride = r16 == 0 ? rowb : tokb;
 
   float wk[B1_CH][24];
   if constexpr (NCOMP == 4) {
@@ -138,22 +225,7 @@ __global__ __launch_bounds__(256) void k_bdots(
   }
 
   // loads of one token (clamped to the sequence)
-  V8<E> av[B1_WAVE_CH / 32], bv[B1_WAVE_CH / 32];
   V2 gv[4], ov;
-  auto load_mfma = [&](int s) {
-    const size_t t = tok0 + min(s, S - 1);
-    const char* ap = abase + t * astride;
-    const char* bp = bbase + t * bstride;
-#pragma unroll
-    for (int ks = 0; ks < B1_WAVE_CH / 32; ++ks) {
-      const int cc = c0 + ks * 32 + 8 * g4;
-      const int ccl = cc < C ? cc : 0;
-      av[ks] = *reinterpret_cast<const V8<E>*>(ap + (size_t)ccl * EB);
-      bv[ks] = *reinterpret_cast<const V8<E>*>(bp + (size_t)ccl * EB);
-      if (!(cc < C && arow_valid)) av[ks] = V8<E>::zero();
-      if (!(cc < C && bcol_valid)) bv[ks] = V8<E>::zero();
-    }
-  };
   auto load_tfa = [&](int s) {
     const size_t t = tok0 + min(s, S - 1);
     const rsrc_t rg = make_rsrc(static_cast<const char*>(dXn) + t * tokb, tokb);
@@ -161,7 +233,6 @@ __global__ __launch_bounds__(256) void k_bdots(
     for (int a = 0; a < 4; ++a) gv[a] = bload<E, B1_CH>(rg, voff, (uint32_t)act.id[a < k ? a : 0] * rowb);
     ov = bload<E, B1_CH>(rout, voff, (uint32_t)min(s, S - 1) * rowb);
   };
-  load_mfma(s0);
   load_tfa(s0);
 
   for (int s = s0; s < tend; ++s) {
@@ -169,32 +240,6 @@ __global__ __launch_bounds__(256) void k_bdots(
     const bool live = s < S;
     const size_t t = tok0 + (live ? s : S - 1);
     const int slot = (s - s0) % 12;
-
-    if (main_tok) {
-      // ---- X dots on MFMA ----
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < B1_WAVE_CH / 32; ++ks) acc = mma32(av[ks], bv[ks], acc);
-      load_mfma(s + 1);
-      // lane (r16, g4) holds D[4*g4 + e][r16]
-      if (r16 == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) red[wave][slot][4 * g4 + e] = acc[e];
-      } else if (r16 <= 4) {
-        const int a = r16 - 1;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const bool ok = a < k && b < k;
-          const int ib = ok ? act.id[b] : 0;
-          if (ok && (ib >> 2) == g4) {
-            const int e = ib & 3;
-            red[wave][slot][16 + a * 4 + b] = e == 0 ? acc[0] : e == 1 ? acc[1] : e == 2 ? acc[2] : acc[3];
-          } else if (!ok && g4 == 0) {
-            red[wave][slot][16 + a * 4 + b] = 0.f;
-          }
-        }
-      }
-    }
 
     // ---- TFA part ----
     float G[4][B1_CH], of[B1_CH];
@@ -256,38 +301,31 @@ __global__ __launch_bounds__(256) void k_bdots(
           v[a * 4 + m] = d;
         }
       {
-        const bool h5 = lane & 32;
+        // halving exchange over the wave: after the steps on lane bits 5, 4,
+        // 3, 2 a lane holds one of the 16 sums, the one its bits select
+        // (lanes are paired by xor 32, 16, 15, 7, then quads are summed)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float send = h5 ? v[q] : v[8 + q];
-          const float keep = h5 ? v[8 + q] : v[q];
-          v[q] = keep + shfl_xor(send, 32);
-        }
-        const bool h4 = lane & 16;
+        for (int q = 0; q < 8; ++q) v[q] = halve32(v[q], v[8 + q]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float send = h4 ? v[q] : v[4 + q];
-          const float keep = h4 ? v[4 + q] : v[q];
-          v[q] = keep + shfl_xor(send, 16);
-        }
+        for (int q = 0; q < 4; ++q) v[q] = halve16(v[q], v[4 + q]);
         const bool h3 = lane & 8;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const float send = h3 ? v[q] : v[2 + q];
           const float keep = h3 ? v[2 + q] : v[q];
-          v[q] = keep + shfl_xor(send, 8);
+          v[q] = keep + dpp_xor15(send);
         }
         const bool h2 = lane & 4;
         {
           const float send = h2 ? v[0] : v[1];
           const float keep = h2 ? v[1] : v[0];
-          v[0] = keep + shfl_xor(send, 4);
+          v[0] = keep + dpp_xor7(send);
         }
-        v[0] += shfl_xor(v[0], 1);
-        v[0] += shfl_xor(v[0], 2);
+        v[0] += dpp_xor1(v[0]);
+        v[0] += dpp_xor2(v[0]);
         if ((lane & 3) == 0) {
           const int idx = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
-          red[wave][slot][32 + idx] = v[0];
+          red[wave][slot][idx] = v[0];
         }
       }
     }
@@ -347,14 +385,14 @@ __global__ __launch_bounds__(256) void k_bdots(
 #pragma unroll
       for (int ch = 0; ch < B1_CH; ++ch) dacc[11][ch] = 0.f;
     }
-    // ---- every 12 main tokens: sum the 4 waves' dots ----
+    // ---- every 12 main tokens: sum the 4 waves' dH_post ----
     if (main_tok && (slot == 11 || s == s1 - 1)) {
       __syncthreads();
       const int g0 = s - slot;
-      for (int idx = threadIdx.x; idx < (slot + 1) * DOT_STRIDE; idx += 256) {
-        const int jj = idx / DOT_STRIDE, q = idx - jj * DOT_STRIDE;
+      for (int idx = threadIdx.x; idx < (slot + 1) * 16; idx += 256) {
+        const int jj = idx >> 4, q = idx & 15;
         const float sum = (red[0][jj][q] + red[1][jj][q]) + (red[2][jj][q] + red[3][jj][q]);
-        dpart[((size_t)cblock * T + tok0 + g0 + jj) * DOT_STRIDE + q] = sum;
+        dpart[((size_t)cblock * T + tok0 + g0 + jj) * DOT_STRIDE + 32 + q] = sum;
       }
       __syncthreads();
     }
@@ -381,7 +419,8 @@ __global__ __launch_bounds__(256) void k_bdots(
 constexpr int BCOEF_TOK = 4;
 
 template <typename E>
-__global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpart, int ncb, const float* __restrict__ zin,
+__global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int ncba, const float* __restrict__ dpart,
+                                              int ncb, const float* __restrict__ zin,
                                               const float* __restrict__ bias, const float* __restrict__ coef,
                                               float* __restrict__ dz_out, void* __restrict__ rec,
                                               int T, int64_t Tpad, int N, int k, int nc,
@@ -396,12 +435,12 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpart, i
 
   // reduce the per-chunk dots
   float dpre = 0.f, dres = 0.f, dpost = 0.f;
-  for (int cb = 0; cb < ncb; ++cb) {
-    const float* d = dpart + ((size_t)cb * T + tc) * DOT_STRIDE;
+  for (int cb = 0; cb < ncba; ++cb) {
+    const float* d = dpa + ((size_t)cb * T + tc) * BX_OUT;
     dpre += d[e];
     dres += d[16 + e];
-    dpost += d[32 + e];
   }
+  for (int cb = 0; cb < ncb; ++cb) dpost += dpart[((size_t)cb * T + tc) * DOT_STRIDE + 32 + e];
   const float* co = coef + tc * COEF_STRIDE;
   const float* z = zin + tc * (P + 1);
   const float r = co[CO_R];
@@ -420,16 +459,16 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpart, i
   const bool valid = a < k && b < k;
   {
     const float L = valid ? z[N + k * nc + a * k + b] : -INFINITY;
-    float mx = fmaxf(L, shfl_xor(L, 1));
-    mx = fmaxf(mx, shfl_xor(mx, 2));
+    float mx = fmaxf(L, row_xor<1>(L));
+    mx = fmaxf(mx, row_xor<2>(mx));
     float M = valid ? expf(L - mx) : 0.f;
     H[e] = M;
     for (int it = 0; it < iters; ++it) {
-      float rs = M + shfl_xor(M, 1);
-      rs += shfl_xor(rs, 2);
+      float rs = M + row_xor<1>(M);
+      rs += row_xor<2>(rs);
       M = valid ? M / rs : 0.f;
-      float cs = M + shfl_xor(M, 4);
-      cs += shfl_xor(cs, 8);
+      float cs = M + row_xor<4>(M);
+      cs += row_xor<8>(cs);
       M = valid ? M / cs : 0.f;
       H[(it + 1) * 16 + e] = M;
     }
@@ -437,19 +476,19 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpart, i
   float g = valid ? dres : 0.f;
   for (int it = iters; it >= 1; --it) {
     const float Mp = H[(it - 1) * 16 + e];
-    float rs = Mp + shfl_xor(Mp, 1);
-    rs += shfl_xor(rs, 2);
+    float rs = Mp + row_xor<1>(Mp);
+    rs += row_xor<2>(rs);
     const float R = valid ? Mp / rs : 0.f;
-    float cs = R + shfl_xor(R, 4);
-    cs += shfl_xor(cs, 8);
+    float cs = R + row_xor<4>(R);
+    cs += row_xor<8>(cs);
     const float Mc = valid ? R / cs : 0.f;
     float t1 = g * Mc;
-    t1 += shfl_xor(t1, 4);
-    t1 += shfl_xor(t1, 8);
+    t1 += row_xor<4>(t1);
+    t1 += row_xor<8>(t1);
     const float gR = valid ? (g - t1) / cs : 0.f;
     float t2 = gR * R;
-    t2 += shfl_xor(t2, 1);
-    t2 += shfl_xor(t2, 2);
+    t2 += row_xor<1>(t2);
+    t2 += row_xor<2>(t2);
     g = valid ? (gR - t2) / rs : 0.f;
   }
   const float dL = g * H[e];
@@ -469,10 +508,10 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpart, i
     const int p = e + 16 * n;
     if (p < P) al = fmaf(dzs[tok][p], z[p] - (bias ? bias[p] : 0.f), al);
   }
-  al += shfl_xor(al, 1);
-  al += shfl_xor(al, 2);
-  al += shfl_xor(al, 4);
-  al += shfl_xor(al, 8);
+  al += row_xor<1>(al);
+  al += row_xor<2>(al);
+  al += row_xor<4>(al);
+  al += row_xor<8>(al);
   const float inv_r = 1.f / r;
   if (tv) {
 #pragma unroll
@@ -883,6 +922,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
 
   void* Wp = ws + p.off_wp;
   float* dpart = reinterpret_cast<float*>(ws + p.off_dpart);
+  float* dpa = reinterpret_cast<float*>(ws + p.off_dpa);
   float* dwpart = reinterpret_cast<float*>(ws + p.off_dwpart);
   float* dz = reinterpret_cast<float*>(ws + p.off_dz);
   unsigned char* rec = reinterpret_cast<unsigned char*>(ws + p.off_rec);
@@ -895,6 +935,11 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
     TimedLaunch tl(tm, KID_PACK_WP, st);
     const int64_t n = p.NC * 64;
     k_pack_wp<R><<<(int)((n + 255) / 256), 256, 0, st>>>(static_cast<const R*>(a->W), static_cast<R*>(Wp), p.NC, p.P);
+  }
+  {
+    TimedLaunch tl(tm, KID_BXDOTS, st);
+    k_bxdots<E><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N,
+                                                                     p.k, act, p.bx_cblocks);
   }
   {
     TimedLaunch tl(tm, KID_BDOTS, st);
@@ -915,7 +960,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
     TimedLaunch tl(tm, KID_BCOEF, st);
     const int nb = (int)((p.Tpad + BCOEF_TOK - 1) / BCOEF_TOK);
     const size_t shm = (size_t)BCOEF_TOK * (p.iters + 1) * 16 * sizeof(float);
-    k_bcoef<E><<<nb, 64, shm, st>>>(dpart, p.b1_cblocks, zin, a->bias, coef, dz, rec, p.T, p.Tpad, p.N,
+    k_bcoef<E><<<nb, 64, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, coef, dz, rec, p.T, p.Tpad, p.N,
                                     p.k, p.nc, p.P, 1.0f / (float)p.NC, p.iters, p.gate == XHC_GATE_UNIT);
   }
   {

@@ -242,6 +242,55 @@ __device__ inline float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 __device__ inline float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Cross-lane steps on the VALU (gfx950), for wave-wide reductions:
+// swap32(x, y) / swap16(x, y) return x + y' where the permlane swap moves
+// y's values of the lower half (lanes 0..31, or rows 0 and 2) to the upper
+// half and x's values of the upper half to the lower half.  With x = the
+// values a lane keeps when its bit (5, resp. 4) is 0 and y = those it keeps
+// when the bit is 1, the result is the lane's kept value summed with its
+// partner's (lane ^ 32, resp. lane ^ 16): one step of a halving exchange.
+__device__ inline float halve32(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float halve16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// DPP lane moves within rows of 16: value of lane (l ^ 15), of lane (l ^ 7),
+// of lane (l ^ 2) and of lane (l ^ 1)
+__device__ inline float dpp_xor15(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+}
+__device__ inline float dpp_xor7(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+}
+__device__ inline float dpp_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ inline float dpp_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+// value of lane (l ^ 8) and of lane (l ^ 4) within rows of 16 (rotations by
+// 8, and by 4 or 12 depending on lane bit 2)
+__device__ inline float dpp_xor8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+__device__ inline float dpp_xor4(float v) {
+  const float a = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+  const float b = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x12C, 0xF, 0xF, false));
+  return (__lane_id() & 4) ? a : b;
+}
+// exact xor-partner exchange within 16-lane rows, m in {1, 2, 4, 8}
+template <int m>
+__device__ inline float row_xor(float v) {
+  static_assert(m == 1 || m == 2 || m == 4 || m == 8, "row xor mask");
+  if constexpr (m == 1) return dpp_xor1(v);
+  else if constexpr (m == 2) return dpp_xor2(v);
+  else if constexpr (m == 4) return dpp_xor4(v);
+  else return dpp_xor8(v);
+}
+
 // XCD-aware remap of the linear workgroup id.  Workgroups are dispatched to
 // the 8 XCDs round-robin (id % 8); this returns a logical id such that each
 // XCD receives one contiguous range of logical ids, so neighbouring tiles

@@ -221,10 +221,10 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
   float r = 0.f;
   if (zpart) {
     float ss = (tv && e < SK) ? zpart[((size_t)e * T + t) * ZST + NTP] : 0.f;
-    ss += shfl_xor(ss, 1);
-    ss += shfl_xor(ss, 2);
-    ss += shfl_xor(ss, 4);
-    ss += shfl_xor(ss, 8);
+    ss += row_xor<1>(ss);
+    ss += row_xor<2>(ss);
+    ss += row_xor<4>(ss);
+    ss += row_xor<8>(ss);
     r = sqrtf(ss * inv_nc_total + eps);
 #pragma unroll
     for (int n = 0; n < 3; ++n) {
@@ -259,15 +259,15 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
     const int a = e >> 2, b = e & 3;
     const bool valid = a < k && b < k;
     const float L = valid ? zs[tok][N + k * nc + a * k + b] : -INFINITY;
-    float mx = fmaxf(L, shfl_xor(L, 1));
-    mx = fmaxf(mx, shfl_xor(mx, 2));
+    float mx = fmaxf(L, row_xor<1>(L));
+    mx = fmaxf(mx, row_xor<2>(mx));
     float M = valid ? expf(L - mx) : 0.f;
     for (int it = 0; it < iters; ++it) {
-      float rs = M + shfl_xor(M, 1);
-      rs += shfl_xor(rs, 2);
+      float rs = M + row_xor<1>(M);
+      rs += row_xor<2>(rs);
       M = valid ? M / rs : 0.f;
-      float cs = M + shfl_xor(M, 4);
-      cs += shfl_xor(cs, 8);
+      float cs = M + row_xor<4>(M);
+      cs += row_xor<8>(cs);
       M = valid ? M / cs : 0.f;
     }
     co[CO_RES + e] = M;

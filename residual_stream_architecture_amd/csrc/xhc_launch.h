@@ -11,7 +11,7 @@ namespace xhc {
 // Kernel ids reported by the timer (names in xhc_api.cpp).
 enum KernelId {
   KID_PACK_WT = 0, KID_PROJ, KID_COEF, KID_MIX,
-  KID_PACK_WP, KID_BDOTS, KID_BCOEF, KID_BGRAD, KID_BREDUCE,
+  KID_PACK_WP, KID_BDOTS, KID_BCOEF, KID_BGRAD, KID_BREDUCE, KID_BXDOTS,
   KID_COUNT
 };
 // Alias kept for the backward's coefficient recompute from z_save.

@@ -17,11 +17,12 @@ namespace xhc {
 constexpr int COEF_STRIDE = 64;
 constexpr int CO_PRE = 0, CO_POST = 16, CO_RES = 32, CO_R = 48;
 
-// Per-token backward dot record (floats, per channel block of B1):
-//   [0, 16)   dH_pre[i]      = <dh_in, X_i>
-//   [16, 32)  dH_res[a*4+b]  = <G_a, X_{i_b}>
-//   [32, 48)  dH_post[a*4+m] = <G_a, U_m>
+// Per-token backward dot records (floats):
+//   B1x, per channel block of BX_CB:   [0, 16)  dH_pre[i]      = <dh_in, X_i>
+//                                      [16, 32) dH_res[a*4+b]  = <G_a, X_{i_b}>
+//   B1, per channel block of B1:       [32, 48) dH_post[a*4+m] = <G_a, U_m>
 constexpr int DOT_STRIDE = 48;
+constexpr int BX_OUT = 32;
 
 constexpr int PROJ_WAVES = 8;     // waves per projection workgroup
 constexpr int PROJ_TOK = 32 * PROJ_WAVES;   // tokens per projection workgroup (32 per wave)
@@ -31,6 +32,11 @@ constexpr int MIX_TARGET_WAVES = 2560;   // grid size aimed at ~one resident rou
 constexpr int B1_CH = 2;          // channels per lane in B1's TFA part
 constexpr int B1_WAVE_CH = 128;   // channels per B1 wave (64 lanes x 2)
 constexpr int B1_WAVES = 4;       // waves per B1 workgroup (consecutive chunks)
+constexpr int BX_WAVES = 8;       // waves per B1x workgroup
+constexpr int BX_WCH = 64;        // channels per B1x wave (two K=32 steps)
+constexpr int BX_CB = BX_WAVES * BX_WCH;
+constexpr int BX_TOK = 64;        // tokens per B1x workgroup
+constexpr int BX_GRP = 8;         // tokens per B1x cross-wave reduction
 constexpr int B2_WAVE_CH = 32;    // channels per B2 wave (one state row)
 constexpr int B2_CB = 64;         // channels per B2 workgroup: whole 128-byte lines of a bf16 row
 constexpr int B2_WAVES = 8;       // 4 rows x 2 channel halves
@@ -70,6 +76,8 @@ struct Plan {
   int b1_cblocks;     // channel blocks of B1_WAVES*B1_WAVE_CH
   int b1_lseg;        // tokens per B1 segment (multiple of 12)
   int b1_segs;        // segments per sequence
+  int bx_cblocks;     // channel blocks of BX_CB
+  int bx_tiles;       // token tiles of BX_TOK
   int b2_rowgroups;   // 1 active group + ceil((N-k)/4) inactive groups
   int b2_cblocks;     // channel blocks of B2_CB
   int b2_ts;          // token splits
@@ -77,7 +85,7 @@ struct Plan {
   int64_t Tpad;       // T rounded up to B2_TT
   // workspace layout (byte offsets; every region 256-byte aligned)
   size_t off_wt, off_zpart, off_coef, fwd_bytes;
-  size_t off_zbuf, off_wp, off_dpart, off_dwpart, off_dz, off_rec, off_dwpart2, bwd_bytes;
+  size_t off_zbuf, off_wp, off_dpart, off_dpa, off_dwpart, off_dz, off_rec, off_dwpart2, bwd_bytes;
 };
 
 // Fills `p` from `d`; returns XHC_OK or an XHC_ERR_* code for an
