@@ -62,7 +62,9 @@ __global__ void k_pack_wp(const R* __restrict__ W, R* __restrict__ Wp, int64_t N
 template <typename E>
 __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const void* __restrict__ dXn,
                                                           const void* __restrict__ dhin, float* __restrict__ dpa,
-                                                          int T, int C, int N, int k, Act4 act, int ncb) {
+                                                          int T, int C, int N, int k, Act4 act, int ncb,
+                                                          const float* __restrict__ zin, float* __restrict__ hpost,
+                                                          int P, int nc, int unit_gates) {
   constexpr int EB = E::bytes;
   constexpr int RING = EB == 2 ? 4 : 2;
   static_assert(BX_GRP % RING == 0 && BX_TOK % BX_GRP == 0, "ring slots must be static in a group");
@@ -78,6 +80,17 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
   const int c0 = cb * BX_CB + wave * BX_WCH;
   const int t0 = tile * BX_TOK;
   const int tn = min(BX_TOK, T - t0);
+
+  // the tile's post gates for B1 (H_post[a*4 + m], recomputed from the saved
+  // logits as the forward computed them), written by channel block 0
+  if (cb == 0) {
+    for (int j = threadIdx.x; j < tn * 16; j += 64 * BX_WAVES) {
+      const int tt = j >> 4, e = j & 15, a = e >> 2, m = e & 3;
+      float h = 0.f;
+      if (a < k && m < nc) h = unit_gates ? 1.f : sigmoid(zin[(size_t)(t0 + tt) * (P + 1) + N + a * nc + m]);
+      hpost[(size_t)(t0 + tt) * 16 + e] = h;
+    }
+  }
 
   // A row r = stream r; B column r = dh_in (r = 0) or G_{r-1}
   const bool arow = r < N;
@@ -162,7 +175,7 @@ template <typename E, int NCOMP, bool FAST>
 __global__ __launch_bounds__(256) void k_bdots(
     StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin,
     const void* __restrict__ out, const float* __restrict__ w4, const float* __restrict__ w8,
-    const float* __restrict__ w12, const float* __restrict__ coef, float* __restrict__ dpart,
+    const float* __restrict__ w12, const float* __restrict__ hpost, float* __restrict__ dpart,
     void* __restrict__ dout, float* __restrict__ dwpart, int T, int S, int C, int N, int kk, Act4 act,
     int lseg, int segs_per_seq) {
   using V2 = Vec<E, B1_CH>;
@@ -256,7 +269,7 @@ __global__ __launch_bounds__(256) void k_bdots(
 
     float H[4][4];
     {
-      const f32x4* hp = reinterpret_cast<const f32x4*>(coef + t * COEF_STRIDE + CO_POST);
+      const f32x4* hp = reinterpret_cast<const f32x4*>(hpost + t * 16);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const f32x4 v = hp[a];
@@ -421,7 +434,7 @@ constexpr int BCOEF_TOK = 4;
 template <typename E>
 __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int ncba, const float* __restrict__ dpart,
                                               int ncb, const float* __restrict__ zin,
-                                              const float* __restrict__ bias, const float* __restrict__ coef,
+                                              const float* __restrict__ bias,
                                               float* __restrict__ dz_out, void* __restrict__ rec,
                                               int T, int64_t Tpad, int N, int k, int nc,
                                               int P, float inv_nc_total, int iters, int unit_gates) {
@@ -441,17 +454,18 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
     dres += d[16 + e];
   }
   for (int cb = 0; cb < ncb; ++cb) dpost += dpart[((size_t)cb * T + tc) * DOT_STRIDE + 32 + e];
-  const float* co = coef + tc * COEF_STRIDE;
   const float* z = zin + tc * (P + 1);
-  const float r = co[CO_R];
+  const float r = z[P];
 
-  // gates
+  // gates (recomputed from the logits, as the forward computed them)
+  const bool pre_ok = e < N;
+  const bool post_ok = (e >> 2) < k && (e & 3) < nc;
+  const float hp = pre_ok ? (unit_gates ? 1.f : sigmoid(z[e])) : 0.f;
+  const float hq = post_ok ? (unit_gates ? 1.f : sigmoid(z[N + (e >> 2) * nc + (e & 3)])) : 0.f;
   float dz_pre = 0.f, dz_post = 0.f;
   if (!unit_gates) {
-    const float hp = co[CO_PRE + e];
-    dz_pre = e < N ? dpre * hp * (1.f - hp) : 0.f;
-    const float hq = co[CO_POST + e];
-    dz_post = ((e >> 2) < k && (e & 3) < nc) ? dpost * hq * (1.f - hq) : 0.f;
+    dz_pre = pre_ok ? dpre * hp * (1.f - hp) : 0.f;
+    dz_post = post_ok ? dpost * hq * (1.f - hq) : 0.f;
   }
 
   // Sinkhorn backward
@@ -548,8 +562,8 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
       }
     }
     float* rco = reinterpret_cast<float*>(rb + REC_CO);
-    rco[(RF_PRE + e) * B2_TT + tt] = tv ? co[CO_PRE + e] : 0.f;
-    rco[(RF_RES + e) * B2_TT + tt] = tv ? co[CO_RES + e] : 0.f;
+    rco[(RF_PRE + e) * B2_TT + tt] = tv ? hp : 0.f;
+    rco[(RF_RES + e) * B2_TT + tt] = tv ? H[iters * 16 + e] : 0.f;
     if (e < REC_NF - RF_GAMMA)
       rco[(RF_GAMMA + e) * B2_TT + tt] = (tv && e == 0) ? al * inv_nc_total * inv_r * inv_r : 0.f;
   }
@@ -871,40 +885,58 @@ __global__ __launch_bounds__(512) void k_bgrad(
 // ---------------------------------------------------------------------------
 // Deterministic reductions (fixed order, no atomics).
 // ---------------------------------------------------------------------------
-__global__ void k_red_dw(const float* __restrict__ part, int nsplit, int64_t NC, int P, float* __restrict__ dW,
-                         int accumulate) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= NC * P) return;
-  const int64_t j = idx / P;
-  const int p = (int)(idx - j * P);
-  float s = accumulate ? dW[idx] : 0.f;
-  for (int q = 0; q < nsplit; ++q) s += part[((size_t)q * NC + j) * 48 + p];
-  dW[idx] = s;
-}
+constexpr int RED_CONV_LANES = 4;   // threads per conv-weight gradient (quad, summed with DPP)
 
-__global__ void k_red_db(const float* __restrict__ dz, int T, float* __restrict__ db, int accumulate) {
+// One launch for the three parameter-gradient reductions; workgroup ranges:
+//   [0, nb_dw)              dW[j][p] = sum over token splits (B2 partials)
+//   [nb_dw, nb_dw + P)      db[p]    = sum over tokens of dz (one block per p)
+//   [nb_dw + P, ...)        dconv    = sum over sequence segments (B1 partials),
+//                            4 threads per output, each summing every 4th segment
+__global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, int nsplit, int64_t NC, int P,
+                                                float* __restrict__ dW, const float* __restrict__ dz, int T,
+                                                float* __restrict__ db, const float* __restrict__ cpart, int nseg,
+                                                int C, float* __restrict__ dw4, float* __restrict__ dw8,
+                                                float* __restrict__ dw12, int nb_dw, int accumulate) {
   __shared__ float sm[256];
-  const int p = blockIdx.x;
-  float s = 0.f;
-  for (int t = threadIdx.x; t < T; t += 256) s += dz[(size_t)t * 48 + p];
-  sm[threadIdx.x] = s;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) sm[threadIdx.x] += sm[threadIdx.x + w];
-    __syncthreads();
+  const int bid = blockIdx.x;
+  if (bid < nb_dw) {
+    const int64_t idx = (int64_t)bid * 256 + threadIdx.x;
+    if (idx >= NC * P) return;
+    const int64_t j = idx / P;
+    const int p = (int)(idx - j * P);
+    float s = accumulate ? dW[idx] : 0.f;
+    for (int q = 0; q < nsplit; ++q) s += dwp[((size_t)q * NC + j) * 48 + p];
+    dW[idx] = s;
+    return;
   }
-  if (threadIdx.x == 0) db[p] = (accumulate ? db[p] : 0.f) + sm[0];
-}
-
-__global__ void k_red_conv(const float* __restrict__ part, int nseg, int C, float* __restrict__ dw4,
-                           float* __restrict__ dw8, float* __restrict__ dw12, int accumulate) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)C * 24) return;
-  const int c = (int)(idx / 24), q = (int)(idx - (int64_t)c * 24);
+  if (bid < nb_dw + P) {
+    if (!db) return;
+    const int p = bid - nb_dw;
+    float s = 0.f;
+    for (int t = threadIdx.x; t < T; t += 256) s += dz[(size_t)t * 48 + p];
+    sm[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (threadIdx.x < w) sm[threadIdx.x] += sm[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) db[p] = (accumulate ? db[p] : 0.f) + sm[0];
+    return;
+  }
+  if (!cpart) return;
+  const int64_t oid = ((int64_t)(bid - nb_dw - P) * 256 + threadIdx.x) / RED_CONV_LANES;
+  const int sub = threadIdx.x % RED_CONV_LANES;
+  const bool ok = oid < (int64_t)C * 24;
+  const int c = ok ? (int)(oid / 24) : 0, q = ok ? (int)(oid - (int64_t)c * 24) : 0;
   float s = 0.f;
-  for (int g = 0; g < nseg; ++g) s += part[((size_t)g * C + c) * 24 + q];
-  float* dst = q < 4 ? dw4 + (size_t)c * 4 + q : q < 12 ? dw8 + (size_t)c * 8 + (q - 4) : dw12 + (size_t)c * 12 + (q - 12);
-  *dst = (accumulate ? *dst : 0.f) + s;
+  if (ok)
+    for (int g = sub; g < nseg; g += RED_CONV_LANES) s += cpart[((size_t)g * C + c) * 24 + q];
+  s += dpp_xor1(s);
+  s += dpp_xor2(s);
+  if (ok && sub == 0) {
+    float* dst = q < 4 ? dw4 + (size_t)c * 4 + q : q < 12 ? dw8 + (size_t)c * 8 + (q - 4) : dw12 + (size_t)c * 12 + (q - 12);
+    *dst = (accumulate ? *dst : 0.f) + s;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -913,16 +945,20 @@ __global__ void k_red_conv(const float* __restrict__ part, int nseg, int C, floa
 template <typename E, typename R>
 static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStream_t st) {
   xhc_timer* tm = a->timer;
-  float* coef = reinterpret_cast<float*>(ws + p.off_coef);
   const float* zin = a->z_save;
-  if (!zin) zin = reinterpret_cast<const float*>(ws + p.off_zbuf);
-  int rc = launch_coef_bwd(p, a->X, a->xact, a->active, a->W, a->bias, a->z_save, ws, coef,
-                           a->z_save ? nullptr : reinterpret_cast<float*>(ws + p.off_zbuf), st, tm);
-  if (rc) return rc;
+  if (!zin) {
+    // no saved logits: recompute them (projection and coefficient passes)
+    float* zbuf = reinterpret_cast<float*>(ws + p.off_zbuf);
+    float* coef = reinterpret_cast<float*>(ws + p.off_coef);
+    const int rc = launch_coef_bwd(p, a->X, a->xact, a->active, a->W, a->bias, nullptr, ws, coef, zbuf, st, tm);
+    if (rc) return rc;
+    zin = zbuf;
+  }
 
   void* Wp = ws + p.off_wp;
   float* dpart = reinterpret_cast<float*>(ws + p.off_dpart);
   float* dpa = reinterpret_cast<float*>(ws + p.off_dpa);
+  float* hpost = reinterpret_cast<float*>(ws + p.off_coef);     // [T][16] post gates for B1
   float* dwpart = reinterpret_cast<float*>(ws + p.off_dwpart);
   float* dz = reinterpret_cast<float*>(ws + p.off_dz);
   unsigned char* rec = reinterpret_cast<unsigned char*>(ws + p.off_rec);
@@ -939,14 +975,15 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   {
     TimedLaunch tl(tm, KID_BXDOTS, st);
     k_bxdots<E><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N,
-                                                                     p.k, act, p.bx_cblocks);
+                                                                     p.k, act, p.bx_cblocks, zin, hpost, p.P, p.nc,
+                                                                     p.gate == XHC_GATE_UNIT);
   }
   {
     TimedLaunch tl(tm, KID_BDOTS, st);
     dim3 grid(p.b1_cblocks, p.B * p.b1_segs);
     const bool fast = p.N == 16 && p.k == 4;
 #define XHC_BDOTS(NCOMP, FAST)                                                                                   \
-  k_bdots<E, NCOMP, FAST><<<grid, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12, coef,     \
+  k_bdots<E, NCOMP, FAST><<<grid, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12, hpost,    \
                                                dpart, a->dout, dwpart, p.T, p.S, p.C, p.N, p.k, act, p.b1_lseg, \
                                                p.b1_segs)
     if (p.nc == 4) {
@@ -960,7 +997,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
     TimedLaunch tl(tm, KID_BCOEF, st);
     const int nb = (int)((p.Tpad + BCOEF_TOK - 1) / BCOEF_TOK);
     const size_t shm = (size_t)BCOEF_TOK * (p.iters + 1) * 16 * sizeof(float);
-    k_bcoef<E><<<nb, 64, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, coef, dz, rec, p.T, p.Tpad, p.N,
+    k_bcoef<E><<<nb, 64, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T, p.Tpad, p.N,
                                     p.k, p.nc, p.P, 1.0f / (float)p.NC, p.iters, p.gate == XHC_GATE_UNIT);
   }
   {
@@ -984,14 +1021,11 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   }
   {
     TimedLaunch tl(tm, KID_BREDUCE, st);
-    const int64_t n = p.NC * p.P;
-    k_red_dw<<<(int)((n + 255) / 256), 256, 0, st>>>(dwp, p.b2_ts, p.NC, p.P, a->dW, a->accumulate);
-    if (a->db) k_red_db<<<p.P, 256, 0, st>>>(dz, p.T, a->db, a->accumulate);
-    if (p.nc == 4) {
-      const int64_t m = (int64_t)p.C * 24;
-      k_red_conv<<<(int)((m + 255) / 256), 256, 0, st>>>(dwpart, p.B * p.b1_segs, p.C, a->dw4, a->dw8, a->dw12,
-                                                          a->accumulate);
-    }
+    const int nb_dw = (int)((p.NC * p.P + 255) / 256);
+    const int nb_conv = p.nc == 4 ? (int)(((int64_t)p.C * 24 * RED_CONV_LANES + 255) / 256) : 0;
+    k_reduce<<<nb_dw + p.P + nb_conv, 256, 0, st>>>(dwp, p.b2_ts, p.NC, p.P, a->dW, dz, p.T, a->db,
+                                                     p.nc == 4 ? dwpart : nullptr, p.B * p.b1_segs, p.C, a->dw4,
+                                                     a->dw8, a->dw12, nb_dw, a->accumulate);
   }
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
 }
