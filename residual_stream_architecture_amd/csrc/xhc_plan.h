@@ -28,7 +28,7 @@ constexpr int PROJ_WAVES = 8;     // waves per projection workgroup
 constexpr int PROJ_TOK = 32 * PROJ_WAVES;   // tokens per projection workgroup (32 per wave)
 constexpr int MIX_CH = 2;         // channels per thread in the mix kernel
 constexpr int MIX_THREADS = 256;
-constexpr int MIX_TARGET_WAVES = 2560;   // grid size aimed at ~one resident round
+constexpr int MIX_TARGET_WAVES = 10240;  // grid size: several rounds of short token segments
 constexpr int B1_CH = 2;          // channels per lane in B1's TFA part
 constexpr int B1_WAVE_CH = 128;   // channels per B1 wave (64 lanes x 2)
 constexpr int B1_WAVES = 4;       // waves per B1 workgroup (consecutive chunks)
@@ -42,7 +42,7 @@ constexpr int B2_CB = 64;         // channels per B2 workgroup: whole 128-byte l
 constexpr int B2_WAVES = 8;       // 4 rows x 2 channel halves
 constexpr int B2_TT = 16;         // tokens per B2 tile (one MFMA K / N extent)
 constexpr int B2_SUB = 2;         // tiles per B2 iteration (loaded together, one iteration ahead)
-constexpr int B2_TARGET_WG = 512;   // B2 grid aimed at one resident round of 2 workgroups per CU
+constexpr int B2_TARGET_WG = 2048;  // B2 grid: four rounds of 2 workgroups per CU (later rounds balance the load)
 
 // Per-tile backward record (B2_TT tokens), written by the coefficient
 // backward kernel and copied verbatim into LDS by B2, so its layout is the
