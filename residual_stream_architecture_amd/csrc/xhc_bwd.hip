@@ -16,16 +16,16 @@
 //   dw_m[c,q] = sum_t dU_m[t,c] out[t-K_m+1+q, c]
 //
 // Pipeline of one backward call:
-//   k_coef (shared)  coefficients from z_save (or a fresh projection)
-//   k_pack_wp        W [N*C, P] -> Wp [N*C, 64] zero-padded A operand
-//   k_bdots  (B1)    per (channel block, segment): the 48 dots per token
-//                    (MFMA for the X dots, VALU for the TFA part), dout,
-//                    conv-weight partials
-//   k_bcoef          per token: reduce dots, gates' and Sinkhorn's backward,
-//                    dz, dz/r (MFMA operands), gamma
+//   (k_coef path)    only when no logits were saved: a fresh projection
+//   k_bxdots (B1x)   per (512 channels, 64 tokens): dH_pre and dH_res on MFMA;
+//                    also packs W for B2 and writes the post gates for B1
+//   k_bdots  (B1)    per (512 channels, sequence segment): TFA backward --
+//                    dH_post partials, dout, conv-weight partials
+//   k_bcoef          per token: reduce the dots, gates' and Sinkhorn's
+//                    backward, dz, B2's per-tile record (dz/r, gates, gamma)
 //   k_bgrad  (B2)    per (row group, 64 channels, token split): dX assembly
 //                    with the dz W^T term on MFMA, dW partials on MFMA
-//   k_red_*          deterministic reductions of dW, db and dw partials
+//   k_reduce         deterministic reductions of the dW, db and dconv partials
 #include "xhc_device.h"
 #include "xhc_launch.h"
 
@@ -37,14 +37,6 @@ struct RowTable { int stream[5][4]; };   // row group -> 4 stream ids (-1 = none
 // ---------------------------------------------------------------------------
 // W [NC, P] -> Wp [NC, 64], columns p >= P zero.
 // ---------------------------------------------------------------------------
-template <typename R>
-__global__ void k_pack_wp(const R* __restrict__ W, R* __restrict__ Wp, int64_t NC, int P) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= NC * 64) return;
-  const int64_t j = idx >> 6;
-  const int p = (int)(idx & 63);
-  Wp[idx] = p < P ? W[(size_t)j * P + p] : R(0);
-}
 
 // ---------------------------------------------------------------------------
 // B1x.  The backward's state dots on MFMA.  Workgroup = (channel block of
@@ -59,12 +51,13 @@ __global__ void k_pack_wp(const R* __restrict__ W, R* __restrict__ Wp, int64_t N
 // the tile's result buffer, written out once at the end:
 //   dpa[cb][t][0..16) = dH_pre,  dpa[cb][t][16 + a*4 + b] = dH_res[a][b].
 // ---------------------------------------------------------------------------
-template <typename E>
+template <typename E, typename R>
 __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const void* __restrict__ dXn,
                                                           const void* __restrict__ dhin, float* __restrict__ dpa,
                                                           int T, int C, int N, int k, Act4 act, int ncb,
                                                           const float* __restrict__ zin, float* __restrict__ hpost,
-                                                          int P, int nc, int unit_gates) {
+                                                          int P, int nc, int unit_gates, const R* __restrict__ W,
+                                                          R* __restrict__ Wp, int64_t NC) {
   constexpr int EB = E::bytes;
   constexpr int RING = EB == 2 ? 4 : 2;
   static_assert(BX_GRP % RING == 0 && BX_TOK % BX_GRP == 0, "ring slots must be static in a group");
@@ -81,6 +74,18 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
   const int t0 = tile * BX_TOK;
   const int tn = min(BX_TOK, T - t0);
 
+  // B2's projection operand: this workgroup's slice of W -> Wp [NC][64]
+  // (zero padded past P); nothing reads it before B2
+  {
+    const int64_t nwp = NC * 64;
+    const int64_t per = (nwp + gridDim.x - 1) / gridDim.x;
+    const int64_t beg = (int64_t)lb * per, end = min(beg + per, nwp);
+    for (int64_t idx = beg + threadIdx.x; idx < end; idx += 64 * BX_WAVES) {
+      const int64_t j = idx >> 6;
+      const int pp = (int)(idx & 63);
+      Wp[idx] = pp < P ? W[(size_t)j * P + pp] : R(0);
+    }
+  }
   // the tile's post gates for B1 (H_post[a*4 + m], recomputed from the saved
   // logits as the forward computed them), written by channel block 0
   if (cb == 0) {
@@ -900,13 +905,22 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, i
   __shared__ float sm[256];
   const int bid = blockIdx.x;
   if (bid < nb_dw) {
-    const int64_t idx = (int64_t)bid * 256 + threadIdx.x;
-    if (idx >= NC * P) return;
-    const int64_t j = idx / P;
-    const int p = (int)(idx - j * P);
-    float s = accumulate ? dW[idx] : 0.f;
-    for (int q = 0; q < nsplit; ++q) s += dwp[((size_t)q * NC + j) * 48 + p];
-    dW[idx] = s;
+    // four consecutive logits of one row per thread (P <= 48 and the
+    // partial rows are 48 floats, so a group of 4 never crosses a row)
+    const int64_t g = (int64_t)bid * 256 + threadIdx.x;
+    const int gpr = (P + 3) >> 2;                   // groups per row
+    if (g >= NC * gpr) return;
+    const int64_t j = g / gpr;
+    const int p0 = (int)(g - j * gpr) * 4;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < nsplit; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(dwp + ((size_t)q * NC + j) * 48 + p0);
+      s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+    }
+    float* dst = dW + (size_t)j * P + p0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (p0 + e < P) dst[e] = (accumulate ? dst[e] : 0.f) + s[e];
     return;
   }
   if (bid < nb_dw + P) {
@@ -968,15 +982,10 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   for (int b = 0; b < 4; ++b) act.id[b] = b < p.k ? a->active[b] : 0;
 
   {
-    TimedLaunch tl(tm, KID_PACK_WP, st);
-    const int64_t n = p.NC * 64;
-    k_pack_wp<R><<<(int)((n + 255) / 256), 256, 0, st>>>(static_cast<const R*>(a->W), static_cast<R*>(Wp), p.NC, p.P);
-  }
-  {
     TimedLaunch tl(tm, KID_BXDOTS, st);
-    k_bxdots<E><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N,
-                                                                     p.k, act, p.bx_cblocks, zin, hpost, p.P, p.nc,
-                                                                     p.gate == XHC_GATE_UNIT);
+    k_bxdots<E, R><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(
+        src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, zin, hpost, p.P, p.nc,
+        p.gate == XHC_GATE_UNIT, static_cast<const R*>(a->W), static_cast<R*>(Wp), p.NC);
   }
   {
     TimedLaunch tl(tm, KID_BDOTS, st);
@@ -1021,7 +1030,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   }
   {
     TimedLaunch tl(tm, KID_BREDUCE, st);
-    const int nb_dw = (int)((p.NC * p.P + 255) / 256);
+    const int nb_dw = (int)((p.NC * ((p.P + 3) / 4) + 255) / 256);
     const int nb_conv = p.nc == 4 ? (int)(((int64_t)p.C * 24 * RED_CONV_LANES + 255) / 256) : 0;
     k_reduce<<<nb_dw + p.P + nb_conv, 256, 0, st>>>(dwp, p.b2_ts, p.NC, p.P, a->dW, dz, p.T, a->db,
                                                      p.nc == 4 ? dwpart : nullptr, p.B * p.b1_segs, p.C, a->dw4,
