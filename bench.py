@@ -41,7 +41,7 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_bytes(w, esz):
+def kernel_bytes(w, esz, save_rows=True):
     """Algorithmic HBM bytes per launch of each main kernel: every input and
     output it must touch, once (per token, in units of C elements):
       proj    reads the state                                  16C
@@ -55,8 +55,8 @@ def kernel_bytes(w, esz):
     unit = T * C * esz
     wbytes = N * C * P * esz
     return {
-        "proj": 16 * unit + wbytes,
-        "mix": (N + 1 + 1 + k + k) * unit,
+        "proj": N * unit + wbytes,
+        "mix": (N + 1 + 1 + k + (k if save_rows else 0)) * unit,
         "bxdots": (N + 1 + k) * unit,
         "bdots": (k + 1 + 1) * unit,
         "bgrad": (N + N + 1 + N) * unit + wbytes,
@@ -138,6 +138,82 @@ def cpu_baseline(w, ntok):
                       f"BLAS threads={threads}, host cpus={os.cpu_count()}"}
 
 
+def forward_bench(args, w, np, torch, synth, xhc):
+    """Forward-only workloads (extra measurements; the default line is the
+    fwd+bwd one).  One step = one in-place forward of every layer of the
+    workload (48 for the stacked one, each with its own parameters and its
+    rotating active set).  The state comes from the seeded generator; the
+    per-layer parameters of the stack are drawn on the device from torch's
+    generator seeded 1000 + layer (same shapes and distributions; the run
+    time does not depend on the values)."""
+    T, N, C, P, k = w.T, w.N, w.C, w.P, w.k
+    esz = 2 if w.dtype == "bf16" else 4
+    sdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    print(f"# workload {w}", file=sys.stderr, flush=True)
+    d = synth.make_inputs(w, seed=0, state=True)
+    X = torch.from_numpy(d.pop("X").view(np.int16)).cuda().view(torch.bfloat16) if esz == 2 else \
+        torch.from_numpy(d.pop("X")).cuda()
+    layers = []
+    for l in range(w.layers):
+        if w.layers == 1:
+            p = {key: (torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16) if a.dtype == np.uint16
+                       else torch.from_numpy(a).cuda()) for key, a in d.items()}
+        else:
+            g = torch.Generator(device="cuda")
+            g.manual_seed(synth.stack_layer_seed(l))
+            p = {"out": torch.randn(T, C, generator=g, device="cuda").to(sdt),
+                 "w4": torch.randn(C, 4, generator=g, device="cuda") * 0.02,
+                 "w8": torch.randn(C, 8, generator=g, device="cuda") * 0.02,
+                 "w12": torch.randn(C, 12, generator=g, device="cuda") * 0.02,
+                 "W": (torch.randn(N * C, P, generator=g, device="cuda") * 0.02).to(sdt),
+                 "bias": torch.zeros(P, device="cuda")}
+        layers.append((p, synth.active_streams(l, N, k)))
+    del d
+    h_in = torch.empty(T, C, dtype=sdt, device="cuda")
+    desc = xhc.make_desc(w.B, w.S, C, N, k, w.ncomp, xhc.XHC_BF16 if esz == 2 else xhc.XHC_F32, w.iters, w.eps)
+    ws_f = torch.empty(xhc.workspace_size(desc, 0), dtype=torch.uint8, device="cuda")
+
+    def step(timer=None):
+        for p, active in layers:
+            conv = dict(w4=p["w4"], w8=p["w8"], w12=p["w12"]) if w.ncomp == 4 else {}
+            xhc.forward(X, p["out"], p["W"], active, X, h_in, B=w.B, S=w.S, bias=p["bias"], workspace=ws_f,
+                        timer=timer, desc=desc, **conv)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    kernels = {}
+    timer = xhc.Timer()
+    for _ in range(max(1, min(args.steps, 5))):
+        step(timer)
+    torch.cuda.synchronize()
+    kb = kernel_bytes(w, esz, save_rows=False)
+    for name in xhc.kernel_names():
+        ms, n = timer.read(name)
+        if n:
+            kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n}
+            if name in ("proj", "mix"):
+                kernels[name]["alg_GBps"] = round(kb[name] / (ms * 1e-3 / n) / 1e9, 1)
+    alg_c = (N + 1 + 1 + k) * w.layers          # per token: state, out, h_in, k rows
+    result = {"metric": f"tokens/s, xHC sublayer forward ({w.name})", "value": round(T * args.steps / elapsed, 1),
+              "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+              "config": {"workload": f"{w.name}: B={w.B} S={w.S} C={C} N={N} k={k} ncomp={w.ncomp} "
+                                     f"layers={w.layers}, in-place forward"},
+              "layer_tokens_per_s": round(T * w.layers * args.steps / elapsed, 1),
+              "step_hbm": {"alg_bytes_per_token_in_C": alg_c,
+                           "alg_GBps": round(alg_c * T * C * esz / (ms_per_step * 1e-3) / 1e9, 1)},
+              "kernels": kernels}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -154,7 +230,9 @@ def main():
         return
 
     w = synth.WORKLOADS[args.workload]
-    assert w.phase == "fwdbwd", "the benchmark step is a forward+backward workload"
+    if w.phase != "fwdbwd":
+        forward_bench(args, w, np, torch, synth, xhc)
+        return
     T, N, C, P, k = w.T, w.N, w.C, w.P, w.k
     esz = 2 if w.dtype == "bf16" else 4
     print(f"# workload {w}", file=sys.stderr, flush=True)
