@@ -32,6 +32,15 @@
 namespace xhc {
 
 struct Act4 { int id[4]; };
+
+// compile-time loop: f(std::integral_constant<int, I>) for I in [I0, I1)
+template <int I0, int I1, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < I1) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, I1>(f);
+  }
+}
 struct RowTable { int stream[5][4]; };   // row group -> 4 stream ids (-1 = none)
 
 // ---------------------------------------------------------------------------
@@ -238,179 +247,202 @@ __global__ __launch_bounds__(256) void k_bdots(
       float f[B1_CH];
       v.to_float(f);
 #pragma unroll
-      for (int ch = 0; ch < B1_CH; ++ch) win[j + 1][ch] = s >= 0 ? f[ch] : 0.f;
+      for (int ch = 0; ch < B1_CH; ++ch) win[j][ch] = s >= 0 ? f[ch] : 0.f;   // ring slot of position s0-11+j
     }
   }
 
-  // loads of one token (clamped to the sequence)
-  V2 gv[4], ov;
-  auto load_tfa = [&](int s) {
+  // loads of one token (clamped to the sequence) into ring slot q; the ring
+  // keeps PF tokens of loads in flight
+  constexpr int PF = 3;
+  V2 gq[PF + 1][4], oq[PF + 1];
+  auto load_tok = [&](int s, int q) {
     const size_t t = tok0 + min(s, S - 1);
     const rsrc_t rg = make_rsrc(static_cast<const char*>(dXn) + t * tokb, tokb);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) gv[a] = bload<E, B1_CH>(rg, voff, (uint32_t)act.id[a < k ? a : 0] * rowb);
-    ov = bload<E, B1_CH>(rout, voff, (uint32_t)min(s, S - 1) * rowb);
+    for (int a = 0; a < 4; ++a) gq[q][a] = bload<E, B1_CH>(rg, voff, (uint32_t)act.id[a < k ? a : 0] * rowb);
+    oq[q] = bload<E, B1_CH>(rout, voff, (uint32_t)min(s, S - 1) * rowb);
   };
-  load_tfa(s0);
-
-  for (int s = s0; s < tend; ++s) {
-    const bool main_tok = s < s1;
-    const bool live = s < S;
-    const size_t t = tok0 + (live ? s : S - 1);
-    const int slot = (s - s0) % 12;
-
-    // ---- TFA part ----
-    float G[4][B1_CH], of[B1_CH];
+  // post gates of one token (uniform: scalar loads), one token ahead
+  float Hn[4][4];
+  auto load_h = [&](int s) {
+    const f32x4* hp = reinterpret_cast<const f32x4*>(hpost + (tok0 + min(s, S - 1)) * 16);
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      gv[a].to_float(G[a]);
-      if (!(a < k && cv && live)) {
+      const f32x4 v = hp[a];
 #pragma unroll
-        for (int ch = 0; ch < B1_CH; ++ch) G[a][ch] = 0.f;
-      }
+      for (int m = 0; m < 4; ++m) Hn[a][m] = v[m];
     }
-    ov.to_float(of);
-    load_tfa(s + 1);
+  };
+#pragma unroll
+  for (int q = 0; q < PF; ++q) load_tok(s0 + q, q);
+  load_h(s0);
 
-    float H[4][4];
-    {
-      const f32x4* hp = reinterpret_cast<const f32x4*>(hpost + t * 16);
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 v = hp[a];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) H[a][m] = v[m];
-      }
-    }
-
-    if (main_tok) {
-#pragma unroll
-      for (int j = 0; j < 11; ++j)
-#pragma unroll
-        for (int ch = 0; ch < B1_CH; ++ch) win[j][ch] = win[j + 1][ch];
-#pragma unroll
-      for (int ch = 0; ch < B1_CH; ++ch) win[11][ch] = cv ? of[ch] : 0.f;
-      float U[4][B1_CH];
-#pragma unroll
-      for (int ch = 0; ch < B1_CH; ++ch) {
-        U[0][ch] = win[11][ch];
-        if constexpr (NCOMP == 4) {
-          float s4 = 0.f, s8 = 0.f, s12 = 0.f;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) s4 = fmaf(wk[ch][q], win[8 + q][ch], s4);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) s8 = fmaf(wk[ch][4 + q], win[4 + q][ch], s8);
-#pragma unroll
-          for (int q = 0; q < 12; ++q) s12 = fmaf(wk[ch][12 + q], win[q][ch], s12);
-          U[1][ch] = s4; U[2][ch] = s8; U[3][ch] = s12;
-        }
-      }
-      // dH_post partials v[a*4+m], reduced over the wave by halving
-      float v[16];
+  // Tokens go in groups of 12 aligned to s0, fully unrolled, so that both
+  // 12-slot windows are rings with static slots: at group position j,
+  //   `out` of position s - 11 + i sits in win[(j + i) % 12]  (i = 11: s)
+  //   the dout accumulator of position s - 11 + i in dacc[(j + 1 + i) % 12].
+  // Positions completed during a group are held in registers and stored at
+  // the group's end, so that the loop issues no store between a load and its
+  // use (loads and stores share one completion counter).
+  for (int sg = s0; sg < tend; sg += 12) {
+    V2 pend[12];
+    static_for<0, 12>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      constexpr int q = j % (PF + 1);
+      const int s = sg + j;
+      const bool main_tok = s < s1;
+      const bool in_seg = s < tend;
+      const bool live = s < S;
+      load_tok(s + PF, (j + PF) % (PF + 1));
+      float H[4][4];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < 4; ++m) H[a][m] = Hn[a][m];
+      load_h(s + 1);
+
+      float G[4][B1_CH], of[B1_CH];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        gq[q][a].to_float(G[a]);
+        if (!(a < k && cv && live)) {
+#pragma unroll
+          for (int ch = 0; ch < B1_CH; ++ch) G[a][ch] = 0.f;
+        }
+      }
+      oq[q].to_float(of);
+
+      if (main_tok) {
+#pragma unroll
+        for (int ch = 0; ch < B1_CH; ++ch) win[(j + 11) % 12][ch] = cv ? of[ch] : 0.f;
+        float U[4][B1_CH];
+#pragma unroll
+        for (int ch = 0; ch < B1_CH; ++ch) {
+          U[0][ch] = win[(j + 11) % 12][ch];
+          if constexpr (NCOMP == 4) {
+            float s4 = 0.f, s8 = 0.f, s12 = 0.f;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) s4 = fmaf(wk[ch][qq], win[(j + 8 + qq) % 12][ch], s4);
+#pragma unroll
+            for (int qq = 0; qq < 8; ++qq) s8 = fmaf(wk[ch][4 + qq], win[(j + 4 + qq) % 12][ch], s8);
+#pragma unroll
+            for (int qq = 0; qq < 12; ++qq) s12 = fmaf(wk[ch][12 + qq], win[(j + qq) % 12][ch], s12);
+            U[1][ch] = s4; U[2][ch] = s8; U[3][ch] = s12;
+          }
+        }
+        // dH_post partials v[a*4+m], reduced over the wave by halving
+        float v[16];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            float d = 0.f;
+            if (m < NCOMP) {
+#pragma unroll
+              for (int ch = 0; ch < B1_CH; ++ch) d = fmaf(G[a][ch], U[m][ch], d);
+            }
+            v[a * 4 + m] = d;
+          }
+        {
+          // halving exchange over the wave: after the steps on lane bits 5,
+          // 4, 3, 2 a lane holds one of the 16 sums, the one its bits select
+          // (lanes are paired by xor 32, 16, 15, 7, then quads are summed)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = halve32(v[i], v[8 + i]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = halve16(v[i], v[4 + i]);
+          const bool h3 = lane & 8;
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const float send = h3 ? v[i] : v[2 + i];
+            const float keep = h3 ? v[2 + i] : v[i];
+            v[i] = keep + dpp_xor15(send);
+          }
+          const bool h2 = lane & 4;
+          {
+            const float send = h2 ? v[0] : v[1];
+            const float keep = h2 ? v[1] : v[0];
+            v[0] = keep + dpp_xor7(send);
+          }
+          v[0] += dpp_xor1(v[0]);
+          v[0] += dpp_xor2(v[0]);
+          if ((lane & 3) == 0) {
+            const int idx = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+            red[wave][j][idx] = v[0];
+          }
+        }
+      }
+      // dU_m for this token (zero for tokens past the sequence)
+      float dU[4][B1_CH];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int ch = 0; ch < B1_CH; ++ch) {
           float d = 0.f;
           if (m < NCOMP) {
 #pragma unroll
-            for (int ch = 0; ch < B1_CH; ++ch) d = fmaf(G[a][ch], U[m][ch], d);
+            for (int a = 0; a < 4; ++a)
+              if (a < k) d = fmaf(H[a][m], G[a][ch], d);
           }
-          v[a * 4 + m] = d;
+          dU[m][ch] = d;
         }
-      {
-        // halving exchange over the wave: after the steps on lane bits 5, 4,
-        // 3, 2 a lane holds one of the 16 sums, the one its bits select
-        // (lanes are paired by xor 32, 16, 15, 7, then quads are summed)
+      if (main_tok && NCOMP == 4) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = halve32(v[q], v[8 + q]);
+        for (int ch = 0; ch < B1_CH; ++ch) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = halve16(v[q], v[4 + q]);
-        const bool h3 = lane & 8;
+          for (int qq = 0; qq < 4; ++qq) dw[ch][qq] = fmaf(dU[1][ch], win[(j + 8 + qq) % 12][ch], dw[ch][qq]);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const float send = h3 ? v[q] : v[2 + q];
-          const float keep = h3 ? v[2 + q] : v[q];
-          v[q] = keep + dpp_xor15(send);
-        }
-        const bool h2 = lane & 4;
-        {
-          const float send = h2 ? v[0] : v[1];
-          const float keep = h2 ? v[1] : v[0];
-          v[0] = keep + dpp_xor7(send);
-        }
-        v[0] += dpp_xor1(v[0]);
-        v[0] += dpp_xor2(v[0]);
-        if ((lane & 3) == 0) {
-          const int idx = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
-          red[wave][slot][idx] = v[0];
+          for (int qq = 0; qq < 8; ++qq)
+            dw[ch][4 + qq] = fmaf(dU[2][ch], win[(j + 4 + qq) % 12][ch], dw[ch][4 + qq]);
+#pragma unroll
+          for (int qq = 0; qq < 12; ++qq)
+            dw[ch][12 + qq] = fmaf(dU[3][ch], win[(j + qq) % 12][ch], dw[ch][12 + qq]);
         }
       }
-    }
-    // dU_m for this token (zero for tokens past the sequence)
-    float dU[4][B1_CH];
+      if (in_seg) {
+        // scatter into the dout accumulators of positions s - lag (positions
+        // before s0 receive terms too; they are never emitted)
+        if (main_tok) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int ch = 0; ch < B1_CH; ++ch) {
-        float d = 0.f;
-        if (m < NCOMP) {
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-            if (a < k) d = fmaf(H[a][m], G[a][ch], d);
+          for (int ch = 0; ch < B1_CH; ++ch) dacc[j % 12][ch] += dU[0][ch];
         }
-        dU[m][ch] = d;
-      }
-    if (main_tok && NCOMP == 4) {
+        if constexpr (NCOMP == 4) {
 #pragma unroll
-      for (int ch = 0; ch < B1_CH; ++ch) {
+          for (int lag = 0; lag < 12; ++lag) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dw[ch][q] = fmaf(dU[1][ch], win[8 + q][ch], dw[ch][q]);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) dw[ch][4 + q] = fmaf(dU[2][ch], win[4 + q][ch], dw[ch][4 + q]);
-#pragma unroll
-        for (int q = 0; q < 12; ++q) dw[ch][12 + q] = fmaf(dU[3][ch], win[q][ch], dw[ch][12 + q]);
-      }
-    }
-    // scatter into the dout accumulators of positions s - lag (slot 11 - lag)
-    if (main_tok) {
-#pragma unroll
-      for (int ch = 0; ch < B1_CH; ++ch) dacc[11][ch] += dU[0][ch];
-    }
-    if constexpr (NCOMP == 4) {
-#pragma unroll
-      for (int lag = 0; lag < 12; ++lag) {
-        if (lag <= s - s0) {
-#pragma unroll
-          for (int ch = 0; ch < B1_CH; ++ch) {
-            float d = dacc[11 - lag][ch];
-            if (lag < 4) d = fmaf(wk[ch][3 - lag], dU[1][ch], d);
-            if (lag < 8) d = fmaf(wk[ch][4 + 7 - lag], dU[2][ch], d);
-            d = fmaf(wk[ch][12 + 11 - lag], dU[3][ch], d);
-            dacc[11 - lag][ch] = d;
+            for (int ch = 0; ch < B1_CH; ++ch) {
+              float d = dacc[(j + 12 - lag) % 12][ch];
+              if (lag < 4) d = fmaf(wk[ch][3 - lag], dU[1][ch], d);
+              if (lag < 8) d = fmaf(wk[ch][4 + 7 - lag], dU[2][ch], d);
+              d = fmaf(wk[ch][12 + 11 - lag], dU[3][ch], d);
+              dacc[(j + 12 - lag) % 12][ch] = d;
+            }
           }
         }
       }
+      // position s - 11 is complete: hold it for the group's store, clear its slot
+      pend[j] = V2::from_float(dacc[(j + 1) % 12]);
+#pragma unroll
+      for (int ch = 0; ch < B1_CH; ++ch) dacc[(j + 1) % 12][ch] = 0.f;
+    });
+    // group end: completed positions sg - 11 .. sg (those in [s0, s1)) and
+    // the 8 waves' dH_post sums of the group's main tokens
+    if (cv) {
+#pragma unroll
+      for (int j = 0; j < 12; ++j) {
+        const int pos = sg + j - 11;
+        if (pos >= s0 && pos < s1) pend[j].store(dout, (tok0 + pos) * C + cl);
+      }
     }
-    // position s-11 is complete: emit it, then shift the window
-    {
-      const int pos = s - 11;
-      if (pos >= s0 && cv) V2::from_float(dacc[0]).store(dout, (tok0 + pos) * C + cl);
-#pragma unroll
-      for (int j = 0; j < 11; ++j)
-#pragma unroll
-        for (int ch = 0; ch < B1_CH; ++ch) dacc[j][ch] = dacc[j + 1][ch];
-#pragma unroll
-      for (int ch = 0; ch < B1_CH; ++ch) dacc[11][ch] = 0.f;
-    }
-    // ---- every 12 main tokens: sum the 4 waves' dH_post ----
-    if (main_tok && (slot == 11 || s == s1 - 1)) {
+    if (sg < s1) {
       __syncthreads();
-      const int g0 = s - slot;
-      for (int idx = threadIdx.x; idx < (slot + 1) * 16; idx += 256) {
+      const int nmain = min(12, s1 - sg);
+      for (int idx = threadIdx.x; idx < nmain * 16; idx += 64 * B1_WAVES) {
         const int jj = idx >> 4, q = idx & 15;
-        const float sum = (red[0][jj][q] + red[1][jj][q]) + (red[2][jj][q] + red[3][jj][q]);
-        dpart[((size_t)cblock * T + tok0 + g0 + jj) * DOT_STRIDE + 32 + q] = sum;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < B1_WAVES; ++w) sum += red[w][jj][q];
+        dpart[((size_t)cblock * T + tok0 + sg + jj) * DOT_STRIDE + 32 + q] = sum;
       }
       __syncthreads();
     }
