@@ -577,25 +577,29 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
     unsigned char* rb = static_cast<unsigned char*>(rec) + (size_t)(t / B2_TT) * REC_BYTES;
     const int tt = (int)(t % B2_TT);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int p = e + 16 * n;
+    for (int n = 0; n < 3; ++n) {
+      const int p = e + 16 * n;                      // logits 0..47
       const float v = tv ? dzs[tok][p] * inv_r : 0.f;
-      const int ks = p >> 5, g = (p >> 3) & 3, e8 = p & 7;
-      const size_t o_dzr = REC_DZR + ((size_t)((ks * 4 + g) * 16 + tt) * 8 + e8) * EB;
+      size_t o_dzr, dzr_half;
+      if (p < 32) {
+        o_dzr = REC_DZR0 + ((size_t)(((p >> 3) * 16 + tt) * 8 + (p & 7))) * EB;
+        dzr_half = rec_dzr0_half(EB);
+      } else {
+        o_dzr = REC_DZR1 + ((size_t)((((p - 32) >> 2) * 16 + tt) * 4 + ((p - 32) & 3))) * EB;
+        dzr_half = rec_dzr1_half(EB);
+      }
       const int pt = p >> 4, rr = p & 15, gt = tt >> 2, e4 = tt & 3;
       const size_t o_dzrt = REC_DZRT + ((size_t)((pt * 4 + gt) * 16 + rr) * 4 + e4) * EB;
       if constexpr (EB == 2) {
         __bf16 hi, lo;
         split_bf16(v, hi, lo);
         *reinterpret_cast<__bf16*>(rb + o_dzr) = hi;
-        *reinterpret_cast<__bf16*>(rb + o_dzr + rec_dzr_half(EB)) = lo;
-        if (p < 48) {
-          *reinterpret_cast<__bf16*>(rb + o_dzrt) = hi;
-          *reinterpret_cast<__bf16*>(rb + o_dzrt + rec_dzrt_half(EB)) = lo;
-        }
+        *reinterpret_cast<__bf16*>(rb + o_dzr + dzr_half) = lo;
+        *reinterpret_cast<__bf16*>(rb + o_dzrt) = hi;
+        *reinterpret_cast<__bf16*>(rb + o_dzrt + rec_dzrt_half(EB)) = lo;
       } else {
         *reinterpret_cast<float*>(rb + o_dzr) = v;
-        if (p < 48) *reinterpret_cast<float*>(rb + o_dzrt) = v;
+        *reinterpret_cast<float*>(rb + o_dzrt) = v;
       }
     }
     float* rco = reinterpret_cast<float*>(rb + REC_CO);
@@ -673,17 +677,19 @@ __global__ __launch_bounds__(512) void k_bgrad(
   const uint32_t tokb = (uint32_t)N * C * EB;        // bytes of one token's state
 
   // proj A operand: W rows, permuted: A row m of j-tile jt -> channel
-  // 8*(m/4) + 4*jt + m%4 ; K = 64 logits in two steps.
-  V8<E> wa[2][2];
+  // 8*(m/4) + 4*jt + m%4 ; K = 48 logits as a K=32 step (wa) and a K=16
+  // step (wb)
+  V8<E> wa[2];
+  Vec<E, 4> wb[2];
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt) {
     const int ch = 8 * (r16 >> 2) + 4 * jt + (r16 & 3);
     const bool ok = wv && c0 + ch < C;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      V8<E> v = V8<E>::load(Wp, ((ok ? jbase + ch : 0)) * 64 + 32 * ks + 8 * g4);
-      wa[jt][ks] = ok ? v : V8<E>::zero();
-    }
+    const size_t row = (ok ? jbase + ch : 0) * 64;
+    const V8<E> va = V8<E>::load(Wp, row + 8 * g4);
+    const Vec<E, 4> vb = Vec<E, 4>::load(Wp, row + 32 + 4 * g4);
+    wa[jt] = ok ? va : V8<E>::zero();
+    wb[jt] = ok ? vb : Vec<E, 4>::zero();
   }
   f32x4 dwacc[2][3];
 #pragma unroll
@@ -792,24 +798,29 @@ __global__ __launch_bounds__(512) void k_bgrad(
       const bool tv = tk < T;
       const unsigned char* rb = rbuf[buf][s];
 
-      // ---- proj on MFMA: D[c][t], 2 j-tiles ----
+      // ---- proj on MFMA: D[c][t], 2 j-tiles; K = 48 logits as 32 + 16 ----
       f32x4 pj[2];
       {
-        V8<E> bz[2], bzl[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int off = REC_DZR + ((ks * 4 + g4) * 16 + r16) * 8 * EB;
-          bz[ks] = *reinterpret_cast<const V8<E>*>(rb + off);
-          if constexpr (BF) bzl[ks] = *reinterpret_cast<const V8<E>*>(rb + off + rec_dzr_half(EB));
+        V8<E> bz0, bz0l;
+        Vec<E, 4> bz1, bz1l;
+        {
+          const int off0 = REC_DZR0 + (g4 * 16 + r16) * 8 * EB;
+          const int off1 = REC_DZR1 + (g4 * 16 + r16) * 4 * EB;
+          bz0 = *reinterpret_cast<const V8<E>*>(rb + off0);
+          bz1 = *reinterpret_cast<const Vec<E, 4>*>(rb + off1);
+          if constexpr (BF) {
+            bz0l = *reinterpret_cast<const V8<E>*>(rb + off0 + rec_dzr0_half(EB));
+            bz1l = *reinterpret_cast<const Vec<E, 4>*>(rb + off1 + rec_dzr1_half(EB));
+          }
         }
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          acc = mma32(wa[jt][0], bz[0], acc);
-          acc = mma32(wa[jt][1], bz[1], acc);
+          acc = mma32(wa[jt], bz0, acc);
+          acc = mma16(wb[jt], bz1, acc);
           if constexpr (BF) {
-            acc = mma32(wa[jt][0], bzl[0], acc);
-            acc = mma32(wa[jt][1], bzl[1], acc);
+            acc = mma32(wa[jt], bz0l, acc);
+            acc = mma16(wb[jt], bz1l, acc);
           }
           pj[jt] = acc;
         }

@@ -47,17 +47,21 @@ constexpr int B2_TARGET_WG = 2048;  // B2 grid: four rounds of 2 workgroups per 
 // Per-tile backward record (B2_TT tokens), written by the coefficient
 // backward kernel and copied verbatim into LDS by B2, so its layout is the
 // order in which B2's lanes read it (lane = g*16 + r):
-//   [REC_DZR,  +4096)  dz/r as the projection MFMA's B fragments:
-//                      [half][ks 2][g 4][t 16] x 8 elements, logit p = 32ks + 8g + e
-//   [REC_DZRT, +3072)  dz/r as the dW MFMA's B fragments:
-//                      [half][pt 3][g 4][r 16] x 4 elements, logit 16pt + r, token 4g + e
-//   [REC_CO,   +2304)  coefficients [field 36][t 16] floats: H_pre[16], H_res[16], gamma
-// half = bf16 hi and lo parts (bf16 storage) or one fp32 part (fp32 storage).
-constexpr int REC_BYTES = 10240;
-constexpr int REC_USED = 9472;   // bytes of a record that carry data (the rest pads to 1 KiB)
-constexpr int REC_DZR = 0, REC_DZRT = 4096, REC_CO = 7168;
+//   [REC_DZR0, ..)    dz/r logits 0..31, B fragments of the projection's
+//                     K=32 MFMA: [half][g 4][t 16] x 8 elements, p = 8g + e
+//   [REC_DZR1, ..)    dz/r logits 32..47, B fragments of its K=16 MFMA:
+//                     [half][g 4][t 16] x 4 elements, p = 32 + 4g + e
+//   [REC_DZRT, ..)    dz/r as the dW MFMA's B fragments:
+//                     [half][pt 3][g 4][r 16] x 4 elements, logit 16pt + r, token 4g + e
+//   [REC_CO, +2304)   coefficients [field 36][t 16] floats: H_pre[16], H_res[16], gamma
+// half = bf16 hi and lo parts (bf16 storage) or one fp32 part (fp32 storage);
+// each region has the same size in both storages.
+constexpr int REC_BYTES = 9216;
+constexpr int REC_USED = 8448;   // bytes of a record that carry data (the rest pads to 1 KiB)
+constexpr int REC_DZR0 = 0, REC_DZR1 = 2048, REC_DZRT = 3072, REC_CO = 6144;
 constexpr int RF_PRE = 0, RF_RES = 16, RF_GAMMA = 32, REC_NF = 36;
-constexpr int rec_dzr_half(int esz) { return 2 * 4 * 16 * 8 * esz; }
+constexpr int rec_dzr0_half(int esz) { return 4 * 16 * 8 * esz; }
+constexpr int rec_dzr1_half(int esz) { return 4 * 16 * 4 * esz; }
 constexpr int rec_dzrt_half(int esz) { return 3 * 4 * 16 * 4 * esz; }
 
 struct Plan {
