@@ -155,6 +155,40 @@ int xhc_forward(const xhc_desc* desc, const xhc_fwd_args* args,
 int xhc_backward(const xhc_desc* desc, const xhc_bwd_args* args,
                  void* workspace, size_t workspace_bytes, xhc_stream_t stream);
 
+/* Chained forward of a stack of sublayers with the same description
+ * (source: the closing section of the retrospective, which names an exactly
+ * equivalent dense-read correction beyond the sparse write without giving
+ * its mechanism; this is a reading of it).  Sublayer l's write pass reads
+ * every row of its state and writes the k active rows, so the next
+ * sublayer's state differs only in those rows; the pass also forms the next
+ * sublayer's projection partials (x'.W' and sum x'^2 over each block of
+ * channels, x' = X_new as stored), and the next call starts from them
+ * instead of reading its state a second time.  Results equal those of
+ * xhc_forward called layer by layer, up to the order of fp32 sums. */
+typedef struct {
+  const void* carry_in;   /* NULL: project X here as xhc_forward does; else the
+                             carry_out of the previous call, whose X_new is
+                             this call's X (args->W is then not read)      */
+  const void* W_next;     /* [N*C,P] projection weights of the next sublayer,
+                             or NULL (no carry out: the last sublayer)      */
+  void* carry_out;        /* xhc_carry_size(desc) bytes, or NULL iff W_next is
+                             NULL; may be == carry_in (it is consumed before
+                             it is written), otherwise no overlap with any
+                             other buffer of the call                       */
+} xhc_chain_args;
+
+/* Bytes of one carry buffer (fp32 partials per token and channel block);
+ * 0 for an invalid description.  Pure host code. */
+size_t xhc_carry_size(const xhc_desc* desc);
+
+/* xhc_forward with the chaining of xhc_chain_args.  chain == NULL behaves
+ * as xhc_forward.  Same workspace as xhc_forward; the carry buffers are the
+ * caller's.  Errors as xhc_forward, plus XHC_ERR_NULL for W_next without
+ * carry_out and XHC_ERR_ALIAS for a carry overlapping another buffer. */
+int xhc_forward_chain(const xhc_desc* desc, const xhc_fwd_args* args,
+                      const xhc_chain_args* chain, void* workspace,
+                      size_t workspace_bytes, xhc_stream_t stream);
+
 /* Message of an XHC_* code (static string). */
 const char* xhc_strerror(int code);
 

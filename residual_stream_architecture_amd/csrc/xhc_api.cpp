@@ -74,6 +74,17 @@ int make_plan(const xhc_desc* d, Plan* p) {
     q.b2_ts = (int)cdiv(T, q.b2_tok_per_split);
   }
 
+  // chained forward: channel blocks of whole chunks, at most 16 of them
+  {
+    const int cw = q.dtype == XHC_BF16 ? 64 : 32;
+    q.mp_nch = (int)cdiv(q.C, cw);
+    const int ncb = std::min(16, q.mp_nch);
+    q.mp_cpw = (int)cdiv(q.mp_nch, ncb);
+    q.mp_ncb = (int)cdiv(q.mp_nch, q.mp_cpw);
+    q.mp_nbatch = (int)cdiv(T, 128);
+    q.carry_bytes = (size_t)q.mp_ncb * T * q.ZST * 4;
+  }
+
   // workspace layouts
   size_t o = 0;
   q.off_wt = o;     o = align256(o + (size_t)q.N * cdiv(q.C, 32) * 32 * q.NT * 16 * q.esz);
@@ -130,9 +141,9 @@ static bool any_overlap(const std::vector<Span>& outs, const std::vector<Span>& 
   return false;
 }
 
-static int validate_fwd(const Plan& p, const xhc_fwd_args* a) {
+static int validate_fwd(const Plan& p, const xhc_fwd_args* a, bool need_W = true) {
   if (!a) return XHC_ERR_NULL;
-  if (!a->X || !a->out || !a->W || !a->X_new || !a->h_in) return XHC_ERR_NULL;
+  if (!a->X || !a->out || (need_W && !a->W) || !a->X_new || !a->h_in) return XHC_ERR_NULL;
   const bool has_conv = a->w4 || a->w8 || a->w12;
   if (p.nc == 4 && (!a->w4 || !a->w8 || !a->w12)) return XHC_ERR_NULL;
   if (p.nc == 1 && has_conv) return XHC_ERR_UNSUPPORTED;
@@ -153,6 +164,42 @@ static int validate_fwd(const Plan& p, const xhc_fwd_args* a) {
   std::vector<Span> outs = {Xn, hin, zs, xs};
   std::vector<Span> ins = {X, out, W, bias, w4, w8, w12};
   if (any_overlap(outs, ins, Xn, X)) return XHC_ERR_ALIAS;
+  return XHC_OK;
+}
+
+// Chained forward: the carry buffers and the next sublayer's weights.
+static int validate_chain(const Plan& p, const xhc_fwd_args* a, const xhc_chain_args* c) {
+  if (!c) return XHC_OK;
+  if ((c->W_next == nullptr) != (c->carry_out == nullptr)) return XHC_ERR_NULL;
+  if (misaligned(c->carry_in) || misaligned(c->carry_out) || misaligned(c->W_next)) return XHC_ERR_ALIGN;
+  const size_t T = p.T, e = p.esz;
+  const Span cin = span(c->carry_in, c->carry_in ? p.carry_bytes : 0);
+  const Span cout = span(c->carry_out, c->carry_out ? p.carry_bytes : 0);
+  const Span Wn = span(c->W_next, c->W_next ? (size_t)p.NC * p.P * e : 0);
+  const Span X = span(a->X, T * p.NC * e), Xn = span(a->X_new, T * p.NC * e);
+  const Span out = span(a->out, T * p.C * e), hin = span(a->h_in, T * p.C * e);
+  const Span W = span(a->W, a->W ? (size_t)p.NC * p.P * e : 0);
+  const Span bias = span(a->bias, a->bias ? (size_t)p.P * 4 : 0);
+  const Span w4 = span(a->w4, a->w4 ? (size_t)p.C * 16 : 0), w8 = span(a->w8, a->w8 ? (size_t)p.C * 32 : 0),
+             w12 = span(a->w12, a->w12 ? (size_t)p.C * 48 : 0);
+  const Span zs = span(a->z_save, a->z_save ? T * (p.P + 1) * 4 : 0);
+  const Span xs = span(a->xact_save, a->xact_save ? T * p.k * p.C * e : 0);
+  const Span outs[] = {Xn, hin, zs, xs};
+  const Span ins[] = {X, out, W, bias, w4, w8, w12};
+  // carry_out: an output (carry_in identical to it is permitted)
+  if (c->carry_out) {
+    for (const Span& o : outs)
+      if (overlap(cout, o)) return XHC_ERR_ALIAS;
+    for (const Span& i : ins)
+      if (overlap(cout, i)) return XHC_ERR_ALIAS;
+    if (overlap(cout, Wn)) return XHC_ERR_ALIAS;
+    if (c->carry_in && c->carry_in != c->carry_out && overlap(cout, cin)) return XHC_ERR_ALIAS;
+  }
+  // carry_in and W_next: inputs, no overlap with the call's outputs
+  for (const Span& o : outs) {
+    if (overlap(cin, o)) return XHC_ERR_ALIAS;
+    if (overlap(Wn, o)) return XHC_ERR_ALIAS;
+  }
   return XHC_OK;
 }
 
@@ -208,7 +255,7 @@ struct xhc_timer {
 };
 
 static const char* const kKernelNames[xhc::KID_COUNT] = {
-    "pack_wt", "proj", "coef", "mix", "pack_wp", "bdots", "bcoef", "bgrad", "breduce", "bxdots"};
+    "pack_wt", "proj", "coef", "mix", "pack_wp", "bdots", "bcoef", "bgrad", "breduce", "bxdots", "mixproj"};
 
 namespace xhc {
 void timer_mark(xhc_timer* tm, int kid, hipStream_t st, bool start) {
@@ -261,6 +308,26 @@ int xhc_forward(const xhc_desc* desc, const xhc_fwd_args* args, void* workspace,
   rc = check_ws(p, workspace, workspace_bytes, p.fwd_bytes);
   if (rc) return rc;
   return xhc::launch_forward(p, args, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t xhc_carry_size(const xhc_desc* desc) {
+  xhc::Plan p;
+  if (xhc::make_plan(desc, &p) != XHC_OK) return 0;
+  return p.carry_bytes;
+}
+
+int xhc_forward_chain(const xhc_desc* desc, const xhc_fwd_args* args, const xhc_chain_args* chain, void* workspace,
+                      size_t workspace_bytes, xhc_stream_t stream) {
+  xhc::Plan p;
+  int rc = xhc::make_plan(desc, &p);
+  if (rc) return rc;
+  rc = xhc::validate_fwd(p, args, !(chain && chain->carry_in));
+  if (rc) return rc;
+  rc = xhc::validate_chain(p, args, chain);
+  if (rc) return rc;
+  rc = check_ws(p, workspace, workspace_bytes, p.fwd_bytes);
+  if (rc) return rc;
+  return xhc::launch_forward_chain(p, args, chain, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
 int xhc_backward(const xhc_desc* desc, const xhc_bwd_args* args, void* workspace, size_t workspace_bytes,

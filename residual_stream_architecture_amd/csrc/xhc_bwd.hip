@@ -33,14 +33,6 @@ namespace xhc {
 
 struct Act4 { int id[4]; };
 
-// compile-time loop: f(std::integral_constant<int, I>) for I in [I0, I1)
-template <int I0, int I1, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I0 < I1) {
-    f(std::integral_constant<int, I0>{});
-    static_for<I0 + 1, I1>(f);
-  }
-}
 struct RowTable { int stream[5][4]; };   // row group -> 4 stream ids (-1 = none)
 
 // ---------------------------------------------------------------------------

@@ -1,0 +1,443 @@
+// Fused write pass of one sublayer and projection of the next one (gfx950).
+//
+// Source: "xHC: Expanded Hyper-Connections" retrospective (qingkeai.online),
+// closing section on going further than the sparse write, which mentions a
+// dense-read correction that is exactly equivalent but gives no mechanism.
+// The reading implemented here: the write pass of sublayer l reads every row
+// of the pre-update state X and produces the k new active rows, and the
+// state after the update, X', equals X in every other row.  Sublayer l+1's
+// projection partials
+//     sum_c X'[t,i,c] W'[i*C + c, p]   and   sum_{i,c} X'[t,i,c]^2
+// are therefore formed in the same pass, on MFMA, from rows already in
+// registers: the untouched rows as read and the active rows as written
+// (after rounding to the storage type).  Sublayer l+1 then starts from
+// these partials and never reads X' for its projection, so a stacked
+// forward reads the state once per sublayer instead of twice.
+//
+// Workgroup = (channel block of cpw chunks, batch of MP_TOK tokens), eight
+// waves; wave w owns the batch's tokens 16w .. 16w+15 for every chunk.  A
+// chunk is 32*KS channels (64 for bf16 storage, 32 for fp32): lane
+// (r = lane%16, g = lane/16) holds token r and channels 32u + 8g .. +8 of
+// K-step u, which is at once the MFMA operand layout and a 128-byte read of
+// every token row per K-step pair.  A chunk is walked in steps of MP_RPS
+// rows, the k active rows first:
+//   * the step's rows of the next chunk position are loaded into registers
+//     one step ahead;
+//   * the W' fragments of the step's rows are copied from L2 into a
+//     two-slot LDS ring by LDS-DMA (shared by the eight waves);
+//   * the first step of a chunk forms the TFA components (the 11 earlier
+//     positions of `out` come from the lane's 15 row neighbours by DPP
+//     rotations and from the previous 16 tokens' tile) and the new rows;
+//   * every step accumulates h_in (old rows), the sum of squares and the
+//     projection (new state) and issues its stores.
+// Each step starts with a full wait and a barrier, so loads, LDS-DMA and
+// stores never need exact counts.
+//
+// Output: the write pass's X_new, h_in, xact_save as k_mix writes them, and
+//   carry[cb][t][0 .. 16*NT)  = partial x'.W' over the block's channels
+//   carry[cb][t][16*NT]       = partial sum of x'^2
+// which k_coef of the next sublayer sums over the ncb channel blocks.
+#include "xhc_device.h"
+#include "xhc_launch.h"
+
+namespace xhc {
+
+constexpr int MP_WAVES = 8;
+constexpr int MP_TOK = 16 * MP_WAVES;     // tokens per workgroup
+constexpr int MP_RPS = 4;                 // state rows per step
+constexpr int MP_WSLOT = MP_RPS * 6144;   // W' bytes per step (NT = 3)
+
+// value of lane (l - n) mod 16 within the lane's row of 16
+template <int n>
+__device__ inline unsigned ror16(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + n, 0xF, 0xF, false);
+}
+
+// `out` n positions back: the lane's token is r of a 16-token tile, `cur`
+// holds the tile's values and `halo` those of the 16 tokens before it.
+template <int n, typename E>
+__device__ inline V8<E> window_back(const V8<E>& cur, const V8<E>& halo, bool from_cur) {
+  constexpr int NWD = (int)sizeof(V8<E>) / 4;
+  unsigned cw[NWD], hw[NWD], ow[NWD];
+  __builtin_memcpy(cw, &cur, sizeof(cw));
+  __builtin_memcpy(hw, &halo, sizeof(hw));
+#pragma unroll
+  for (int j = 0; j < NWD; ++j) {
+    const unsigned a = ror16<n>(cw[j]), b = ror16<n>(hw[j]);
+    ow[j] = from_cur ? a : b;
+  }
+  V8<E> o;
+  __builtin_memcpy(&o, ow, sizeof(ow));
+  return o;
+}
+
+template <typename E, int NT, int NCOMP>
+__global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
+    const void* __restrict__ X, const void* __restrict__ out, const float* __restrict__ w4,
+    const float* __restrict__ w8, const float* __restrict__ w12, const float* __restrict__ coef,
+    const void* __restrict__ Wf, void* Xnew, void* __restrict__ hin, void* __restrict__ xact,
+    float* __restrict__ carry, RowOrder ro, int T, int S, int C, int N, int k, int in_place, int cpw,
+    int nch, int nbatch, int ZST) {
+  constexpr int EB = E::bytes;
+  constexpr int KS = EB == 2 ? 2 : 1;        // MFMA K-steps of 32 channels per chunk
+  constexpr int CW = 32 * KS;                // channels per chunk
+  constexpr int FB = 512 * EB;               // bytes of one W' fragment
+  constexpr int SLOTB = KS * NT * FB;        // W' bytes of one row and chunk
+  constexpr int PPR = SLOTB / 1024;          // 1 KiB copies per row
+  static_assert(MP_RPS * SLOTB <= MP_WSLOT && SLOTB % 1024 == 0, "W' step slot");
+  __shared__ __attribute__((aligned(16))) unsigned char wst[2][MP_WSLOT];
+  __shared__ __attribute__((aligned(16))) float cwl[2][24][64];
+  __shared__ __attribute__((aligned(16))) float cl[MP_TOK][48];
+
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int cb = lb / nbatch, bt = lb - cb * nbatch;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int tb = bt * MP_TOK, t0 = tb + 16 * wave, t = t0 + r;
+  const int spos = (t < T ? t : 0) % S;                 // position in the sequence
+  const int nq = (N + MP_RPS - 1) / MP_RPS;             // steps per chunk
+  const int c0 = cb * cpw, c1 = min(c0 + cpw, nch);
+  const int nsteps = (c1 - c0) * nq;
+  const int nks = (C + 31) >> 5;                        // K-steps of the packed W'
+  const uint32_t rowb = (uint32_t)C * EB, tokb = (uint32_t)N * rowb;
+  const int tc = min(t0, T);
+  const int ntile = min(max(T - t0, 0), 16);
+  // `out` of the tile and of the 16 tokens before it in one resource; the
+  // first tile (t0 = 0) has no halo and reads its own rows there, which the
+  // position mask discards
+  const int th = max(t0 - 16, 0);
+  const uint32_t cur_soff = (uint32_t)(t0 - th) * ((uint32_t)C * EB);
+  const rsrc_t rx = make_rsrc(static_cast<const char*>(X) + (size_t)tc * tokb, clamp_bytes(ntile, tokb));
+  const rsrc_t rxn = make_rsrc(static_cast<char*>(Xnew) + (size_t)tc * tokb, clamp_bytes(ntile, tokb));
+  const rsrc_t rout = make_rsrc(static_cast<const char*>(out) + (size_t)min(th, T) * rowb,
+                                clamp_bytes(min(max(T - th, 0), 32), rowb));
+  const rsrc_t rh = make_rsrc(static_cast<char*>(hin) + (size_t)tc * rowb, clamp_bytes(ntile, rowb));
+  const uint32_t xsb = (uint32_t)k * rowb;              // bytes per token of xact
+  const rsrc_t rxs = make_rsrc(xact ? static_cast<char*>(xact) + (size_t)tc * xsb : Xnew,
+                               xact ? clamp_bytes(ntile, xsb) : 0u);
+
+  // lane byte offset of (chunk c, K-step u) in a row of `stride` bytes per
+  // token; channels past C get an offset the buffer range check drops
+  auto lane_off = [&](int c, int u, uint32_t stride) -> uint32_t {
+    const int ch = c * CW + 32 * u + 8 * g;
+    return ch < C ? (uint32_t)r * stride + (uint32_t)ch * EB : 0x80000000u;
+  };
+
+  // coefficients of the batch's tokens -> cl[token][pre 16 | post 16 | res 16]
+  {
+    const int ntok = min(max(T - tb, 0), MP_TOK);
+    const rsrc_t rco = make_rsrc(coef + (size_t)min(tb, T) * COEF_STRIDE, clamp_bytes(ntok, COEF_STRIDE * 4));
+#pragma unroll
+    for (int j = 0; j < MP_TOK * 12 / (64 * MP_WAVES); ++j) {
+      const int id = j * 64 * MP_WAVES + tid;            // 16-byte piece: token id/12, part id%12
+      const int tk = id / 12, part = id - tk * 12;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rco, (lds_void_t*)(reinterpret_cast<unsigned char*>(&cl[0][0]) + (j * 64 * MP_WAVES + wave * 64) * 16), 16,
+          (uint32_t)(tk * COEF_STRIDE + part * 4) * 4, 0, 0, 0);
+    }
+  }
+
+  // conv weights of chunk c: thread-strided over the chunk's [w4 | w8 | w12]
+  // source ranges (contiguous in memory), stored transposed as cwl[tap][ch]
+  float cwr[3];
+  auto conv_src = [&](int c, int f, int& tap, int& cc) -> const float* {
+    if (f < 4 * CW) { cc = f >> 2; tap = f & 3; return w4 + (size_t)c * CW * 4 + f; }
+    if (f < 12 * CW) { const int f2 = f - 4 * CW; cc = f2 >> 3; tap = 4 + (f2 & 7); return w8 + (size_t)c * CW * 8 + f2; }
+    const int f3 = f - 12 * CW;
+    cc = f3 / 12; tap = 12 + (f3 - cc * 12);
+    return w12 + (size_t)c * CW * 12 + f3;
+  };
+  auto load_conv = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int f = tid + i * 64 * MP_WAVES;
+      float v = 0.f;
+      if (f < 24 * CW) {
+        int tap, cc;
+        const float* src = conv_src(c, f, tap, cc);
+        if (c * CW + cc < C) v = *src;
+      }
+      cwr[i] = v;
+    }
+  };
+  auto store_conv = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int f = tid + i * 64 * MP_WAVES;
+      if (f < 24 * CW) {
+        int tap, cc;
+        (void)conv_src(c, f, tap, cc);
+        cwl[c & 1][tap][cc] = cwr[i];
+      }
+    }
+  };
+
+  // W' fragments of step s's rows -> wst[s & 1][slot j][u][n]
+  auto w_dma = [&](int s) {
+    const int cq = s / nq, q = s - cq * nq, c = c0 + cq;
+    const int ksb = c * KS;
+    const int valid_bytes = min(nks - ksb, KS) * NT * FB;
+#pragma unroll
+    for (int i = 0; i < (MP_RPS * PPR + MP_WAVES - 1) / MP_WAVES; ++i) {
+      const int pc = wave + MP_WAVES * i;
+      if (pc < MP_RPS * PPR) {
+        const int j = pc / PPR, o = pc - j * PPR;
+        const int slot = q * MP_RPS + j;
+        if (slot < N && o * 1024 < valid_bytes) {
+          const unsigned char* src = static_cast<const unsigned char*>(Wf) +
+                                     ((size_t)row_of(ro, slot) * nks + ksb) * NT * FB + o * 1024 + lane * 16;
+          __builtin_amdgcn_global_load_lds((const gbl_void_t*)src, (lds_void_t*)&wst[s & 1][j * SLOTB + o * 1024], 16,
+                                           0, 0);
+        }
+      }
+    }
+  };
+
+  // register state
+  V8<E> xc[MP_RPS][KS], xn[MP_RPS][KS];       // rows of the current step; of the next (in flight)
+  V8<E> oc[KS], oh[KS];                       // out and its halo of the chunk (loaded after the
+                                              // previous chunk's first step consumed them)
+  auto load_rows = [&](int c, int q, V8<E> (&x)[MP_RPS][KS]) {
+#pragma unroll
+    for (int j = 0; j < MP_RPS; ++j) {
+      const uint32_t soff = (uint32_t)row_of(ro, q * MP_RPS + j) * rowb;    // rows past N repeat a valid row
+#pragma unroll
+      for (int u = 0; u < KS; ++u) x[j][u] = bload<E, 8>(rx, lane_off(c, u, tokb), soff);
+    }
+  };
+  auto load_out = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+      oc[u] = bload<E, 8>(rout, lane_off(c, u, rowb), cur_soff);
+      oh[u] = bload<E, 8>(rout, lane_off(c, u, rowb), 0);
+    }
+  };
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  float hacc[KS][8];
+#pragma unroll
+  for (int u = 0; u < KS; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hacc[u][e] = 0.f;
+  const float* co = &cl[16 * wave + r][0];
+
+  // one row of the step: h_in from the old values, sum of squares and the
+  // projection from `xv` (the row of the new state), K-step u
+  auto row_work = [&](const unsigned char* wsl, int j, int u, int c, float hp, const V8<E>& xold, const V8<E>& xv) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hacc[u][e] = fmaf(hp, xold.f(e), hacc[u][e]);
+      const float y = xv.f(e);
+      ss = fmaf(y, y, ss);
+    }
+    if (c * KS + u < nks) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const V8<E> wv = *reinterpret_cast<const V8<E>*>(wsl + j * SLOTB + (u * NT + n) * FB + lane * 8 * EB);
+        acc[n] = mma32(wv, xv, acc[n]);
+      }
+    }
+  };
+
+  // step (chunk cq, quarter q): rows 4q .. 4q+4 of the row order.  FIRST:
+  // q == 0, which also forms the new active rows.
+  auto step = [&](auto FI, int cq, int q) {
+    constexpr bool FIRST = decltype(FI)::value;
+    auto& x = xc;
+    const int c = c0 + cq;
+    const int s = cq * nq + q;
+    wait_vmcnt<0>();
+    if constexpr (FIRST && NCOMP == 4) store_conv(c);
+    __syncthreads();            // W' of step s, conv weights and coefficients visible; step s-1 consumed
+    // the next step's loads: issued at once, except in a chunk's first step,
+    // which issues them after its TFA part (that part needs many registers)
+    auto issue_next = [&]() {
+      if (q + 1 < nq) {
+        w_dma(s + 1);
+        load_rows(c, q + 1, xn);
+      } else if (cq + 1 < c1 - c0) {
+        w_dma(s + 1);
+        load_rows(c + 1, 0, xn);
+        if constexpr (NCOMP == 4) load_conv(c + 1);
+      }
+    };
+    if constexpr (!FIRST) issue_next();
+    const unsigned char* wsl = wst[s & 1];
+
+    if constexpr (FIRST) {
+      // TFA components and the new active rows, one K-step and one half of
+      // the lane's 8 channels at a time (keeps the live registers low)
+#pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        unsigned nvw[4][sizeof(V8<E>) / 4];     // packed new rows: [a][dword] (bf16 pairs or fp32 bits)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float u0[4], u1[4], u2[4], u3[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) u0[e] = oc[u].f(4 * h + e);
+          if constexpr (NCOMP == 4) {
+            const float* wl = &cwl[c & 1][0][32 * u + 8 * g + 4 * h];
+            auto tap4 = [&](int tap) { return *reinterpret_cast<const f32x4*>(wl + tap * 64); };
+            {
+              const f32x4 wa = tap4(3), wb = tap4(4 + 7), wc = tap4(12 + 11);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) { u1[e] = wa[e] * u0[e]; u2[e] = wb[e] * u0[e]; u3[e] = wc[e] * u0[e]; }
+            }
+            // U_m = sum_{n < K_m} w_m[c, K_m - 1 - n] * out[t - n]
+            static_for<1, 12>([&](auto NI) {
+              constexpr int n = decltype(NI)::value;
+              const V8<E> ob = window_back<n, E>(oc[u], oh[u], r >= n);
+              float of[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) of[e] = spos < n ? 0.f : ob.f(4 * h + e);
+              if constexpr (n < 4) {
+                const f32x4 w = tap4(3 - n);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u1[e] = fmaf(w[e], of[e], u1[e]);
+              }
+              if constexpr (n < 8) {
+                const f32x4 w = tap4(4 + 7 - n);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u2[e] = fmaf(w[e], of[e], u2[e]);
+              }
+              {
+                const f32x4 w = tap4(12 + 11 - n);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u3[e] = fmaf(w[e], of[e], u3[e]);
+              }
+            });
+          }
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            if (a < k) {
+              const f32x4 res = *reinterpret_cast<const f32x4*>(co + 32 + 4 * a);
+              const f32x4 post = *reinterpret_cast<const f32x4*>(co + 16 + 4 * a);
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float y = 0.f;
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                  if (b < k) y = fmaf(res[b], x[b][u].f(4 * h + e), y);
+                y = fmaf(post[0], u0[e], y);
+                if constexpr (NCOMP == 4) {
+                  y = fmaf(post[1], u1[e], y);
+                  y = fmaf(post[2], u2[e], y);
+                  y = fmaf(post[3], u3[e], y);
+                }
+                v[e] = y;
+              }
+              const Vec<E, 4> hv = Vec<E, 4>::from_float(v);
+              __builtin_memcpy(&nvw[a][h * (int)sizeof(Vec<E, 4>) / 4], &hv, sizeof(hv));
+            }
+          }
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          if (a < k) {
+            V8<E> nv;
+            __builtin_memcpy(&nv, &nvw[a][0], sizeof(nv));
+            const int row = row_of(ro, a);
+            bstore<E, 8>(nv, rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
+            if (xact) bstore<E, 8>(x[a][u], rxs, lane_off(c, u, xsb), (uint32_t)a * rowb);
+            row_work(wsl, a, u, c, co[row], x[a][u], nv);
+          }
+        }
+      }
+    }
+    // `out` of the next chunk (this chunk's has been consumed)
+    if constexpr (FIRST) {
+      issue_next();
+      if (cq + 1 < c1 - c0) load_out(c + 1);
+    }
+    // the step's other rows (untouched by the update)
+#pragma unroll
+    for (int j = 0; j < MP_RPS; ++j) {
+      const int slot = q * MP_RPS + j;
+      if (slot < N && (!FIRST || j >= k)) {
+        const int row = row_of(ro, slot);
+        const float hp = co[row];
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+          row_work(wsl, j, u, c, hp, x[j][u], x[j][u]);
+          if (!in_place) bstore<E, 8>(x[j][u], rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
+        }
+      }
+    }
+    if (q + 1 == nq) {
+#pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        bstore<E, 8>(V8<E>::from_float(hacc[u]), rh, lane_off(c, u, rowb), 0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hacc[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < MP_RPS; ++j)
+#pragma unroll
+      for (int u = 0; u < KS; ++u) xc[j][u] = xn[j][u];
+  };
+
+  if constexpr (NCOMP == 4) load_conv(c0);
+  if (c1 > c0) {
+    w_dma(0);
+    load_rows(c0, 0, xc);
+    load_out(c0);
+  }
+  for (int cq = 0; cq < c1 - c0; ++cq) {
+    step(std::true_type{}, cq, 0);
+    for (int q = 1; q < nq; ++q) step(std::false_type{}, cq, q);
+  }
+  wait_vmcnt<0>();
+
+  ss += shfl_xor(ss, 16);
+  ss += shfl_xor(ss, 32);
+  if (t < T) {
+    float* zp = carry + ((size_t)cb * T + t) * ZST;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(zp + 16 * n + 4 * g) = acc[n];
+    if (g == 0) zp[16 * NT] = ss;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------
+template <typename E>
+static void launch_mixproj_e(const Plan& p, const xhc_fwd_args* a, const float* coef, const void* Wf,
+                             float* carry, hipStream_t st) {
+  RowOrder ro{0};
+  {
+    bool used[16] = {false};
+    int order[16], n = 0;
+    for (int b = 0; b < p.k; ++b) { order[n++] = a->active[b]; used[a->active[b]] = true; }
+    for (int i = 0; i < p.N; ++i)
+      if (!used[i]) order[n++] = i;
+    for (; n < 16; ++n) order[n] = order[0];
+    for (int i = 0; i < 16; ++i) ro.bits |= (uint64_t)order[i] << (4 * i);
+  }
+  const int in_place = a->X_new == a->X;
+  const dim3 grid(p.mp_ncb * p.mp_nbatch);
+#define XHC_MP(NT, NC)                                                                                            \
+  k_mixproj<E, NT, NC><<<grid, 64 * MP_WAVES, 0, st>>>(a->X, a->out, a->w4, a->w8, a->w12, coef, Wf, a->X_new,    \
+                                                       a->h_in, a->xact_save, carry, ro, p.T, p.S, p.C, p.N, p.k, \
+                                                       in_place, p.mp_cpw, p.mp_nch, p.mp_nbatch, p.ZST)
+  if (p.nc == 4) {
+    if (p.NT == 3) XHC_MP(3, 4); else if (p.NT == 2) XHC_MP(2, 4); else XHC_MP(1, 4);
+  } else {
+    if (p.NT == 3) XHC_MP(3, 1); else if (p.NT == 2) XHC_MP(2, 1); else XHC_MP(1, 1);
+  }
+#undef XHC_MP
+}
+
+void launch_mixproj(const Plan& p, const xhc_fwd_args* a, const float* coef, const void* Wf, float* carry,
+                    hipStream_t st) {
+  if (p.dtype == XHC_BF16) launch_mixproj_e<BF16>(p, a, coef, Wf, carry, st);
+  else launch_mixproj_e<F32>(p, a, coef, Wf, carry, st);
+}
+
+}  // namespace xhc

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace xhc {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -289,6 +291,15 @@ __device__ inline float row_xor(float v) {
   else if constexpr (m == 2) return dpp_xor2(v);
   else if constexpr (m == 4) return dpp_xor4(v);
   else return dpp_xor8(v);
+}
+
+// compile-time loop: f(std::integral_constant<int, I>) for I in [I0, I1)
+template <int I0, int I1, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < I1) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, I1>(f);
+  }
 }
 
 // XCD-aware remap of the linear workgroup id.  Workgroups are dispatched to

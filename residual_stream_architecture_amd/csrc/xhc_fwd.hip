@@ -488,20 +488,32 @@ static void launch_proj(const Plan& p, const StreamRows& src, const void* Wf, fl
 }
 
 template <typename E, typename R>
-static int forward_impl(const Plan& p, const xhc_fwd_args* a, char* ws, hipStream_t st, xhc_timer* tm) {
+static int forward_impl(const Plan& p, const xhc_fwd_args* a, const xhc_chain_args* ch, char* ws, hipStream_t st,
+                        xhc_timer* tm) {
   void* Wt = ws + p.off_wt;
   float* zpart = reinterpret_cast<float*>(ws + p.off_zpart);
   float* coef = reinterpret_cast<float*>(ws + p.off_coef);
   const int NTP = p.NT * 16;
-  (void)sizeof(R);
+  const float* carry_in = ch ? static_cast<const float*>(ch->carry_in) : nullptr;
+  const bool carry_out = ch && ch->W_next;
 
-  launch_pack_wt<R>(p, a->W, Wt, st, tm);
-  launch_proj<E>(p, stream_rows(p, a->X, nullptr, a->active), Wt, zpart, st, tm);
+  if (!carry_in) {
+    launch_pack_wt<R>(p, a->W, Wt, st, tm);
+    launch_proj<E>(p, stream_rows(p, a->X, nullptr, a->active), Wt, zpart, st, tm);
+  }
   {
     TimedLaunch tl(tm, KID_COEF, st);
-    k_coef<<<(p.T + 15) / 16, 256, 0, st>>>(zpart, p.SK, p.ZST, NTP, nullptr, a->bias, coef, a->z_save,
-                                            p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps,
-                                            p.iters, p.gate == XHC_GATE_UNIT);
+    k_coef<<<(p.T + 15) / 16, 256, 0, st>>>(carry_in ? carry_in : zpart, carry_in ? p.mp_ncb : p.SK, p.ZST, NTP,
+                                            nullptr, a->bias, coef, a->z_save, p.T, p.N, p.k, p.nc, p.P,
+                                            1.0f / (float)p.NC, p.eps, p.iters, p.gate == XHC_GATE_UNIT);
+  }
+  if (carry_out) {
+    // the next sublayer's weights in the MFMA fragment order, then the fused
+    // write pass with its projection
+    launch_pack_wt<R>(p, ch->W_next, Wt, st, tm);
+    TimedLaunch tl(tm, KID_MIXPROJ, st);
+    launch_mixproj(p, a, coef, Wt, static_cast<float*>(ch->carry_out), st);
+    return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
   }
   {
     TimedLaunch tl(tm, KID_MIX, st);
@@ -525,9 +537,13 @@ static int forward_impl(const Plan& p, const xhc_fwd_args* a, char* ws, hipStrea
 }
 
 int launch_forward(const Plan& p, const xhc_fwd_args* a, void* ws, hipStream_t st) {
+  return launch_forward_chain(p, a, nullptr, ws, st);
+}
+
+int launch_forward_chain(const Plan& p, const xhc_fwd_args* a, const xhc_chain_args* c, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
-  if (p.dtype == XHC_BF16) return forward_impl<BF16, uint16_t>(p, a, w, st, a->timer);
-  return forward_impl<F32, float>(p, a, w, st, a->timer);
+  if (p.dtype == XHC_BF16) return forward_impl<BF16, uint16_t>(p, a, c, w, st, a->timer);
+  return forward_impl<F32, float>(p, a, c, w, st, a->timer);
 }
 
 // Backward helper: coefficients either from a forward's z_save or, when it

@@ -12,6 +12,7 @@ namespace xhc {
 enum KernelId {
   KID_PACK_WT = 0, KID_PROJ, KID_COEF, KID_MIX,
   KID_PACK_WP, KID_BDOTS, KID_BCOEF, KID_BGRAD, KID_BREDUCE, KID_BXDOTS,
+  KID_MIXPROJ,
   KID_COUNT
 };
 // Alias kept for the backward's coefficient recompute from z_save.
@@ -52,7 +53,19 @@ inline StreamRows stream_rows(const Plan& p, const void* X, const void* xact, co
   return s;
 }
 
+// Order in which the fused write + next-projection pass visits the state
+// rows: the k active rows (in the order of `active`), then the other rows
+// ascending; entries past N repeat the first.  Slot s in bits 4s .. 4s+3.
+struct RowOrder { uint64_t bits; };
+__host__ __device__ inline int row_of(const RowOrder& o, int slot) { return (int)((o.bits >> (4 * slot)) & 15u); }
+
 int launch_forward(const Plan& p, const xhc_fwd_args* a, void* ws, hipStream_t st);
+// Forward with an optional projection carried in from the previous sublayer
+// (carry_in) and an optional projection of X_new for the next sublayer
+// (W_next -> carry_out).
+int launch_forward_chain(const Plan& p, const xhc_fwd_args* a, const xhc_chain_args* c, void* ws, hipStream_t st);
+void launch_mixproj(const Plan& p, const xhc_fwd_args* a, const float* coef, const void* Wf, float* carry,
+                    hipStream_t st);
 int launch_coef_bwd(const Plan& p, const void* X, const void* xact, const int32_t* active, const void* W,
                     const float* bias, const float* z_save, void* ws, float* coef, float* z_out,
                     hipStream_t st, xhc_timer* tm);

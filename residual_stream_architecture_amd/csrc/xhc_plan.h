@@ -87,6 +87,12 @@ struct Plan {
   int b2_ts;          // token splits
   int b2_tok_per_split;
   int64_t Tpad;       // T rounded up to B2_TT
+  // fused write + next-sublayer projection (chained forward)
+  int mp_nch;         // channel chunks (64 channels for bf16 storage, 32 for fp32)
+  int mp_cpw;         // chunks per workgroup
+  int mp_ncb;         // channel blocks = projection partials per token (<= 16)
+  int mp_nbatch;      // token batches of 128
+  size_t carry_bytes; // [mp_ncb][T][ZST] floats
   // workspace layout (byte offsets; every region 256-byte aligned)
   size_t off_wt, off_zpart, off_coef, fwd_bytes;
   size_t off_zbuf, off_wp, off_dpart, off_dpa, off_dwpart, off_dz, off_rec, off_dwpart2, bwd_bytes;

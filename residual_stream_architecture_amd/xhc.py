@@ -43,6 +43,10 @@ class xhc_bwd_args(ctypes.Structure):
                 ("accumulate", ctypes.c_int32), ("timer", _vp)]
 
 
+class xhc_chain_args(ctypes.Structure):
+    _fields_ = [("carry_in", _vp), ("W_next", _vp), ("carry_out", _vp)]
+
+
 class XhcError(RuntimeError):
     def __init__(self, code, what):
         super().__init__(f"{what}: {ERRORS.get(code, code)} ({lib.xhc_strerror(code).decode()})")
@@ -60,6 +64,11 @@ def _load():
     L.xhc_validate.restype = ctypes.c_int
     L.xhc_forward.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_fwd_args), _vp, ctypes.c_size_t, _vp]
     L.xhc_forward.restype = ctypes.c_int
+    L.xhc_carry_size.argtypes = [ctypes.POINTER(xhc_desc)]
+    L.xhc_carry_size.restype = ctypes.c_size_t
+    L.xhc_forward_chain.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_fwd_args),
+                                    ctypes.POINTER(xhc_chain_args), _vp, ctypes.c_size_t, _vp]
+    L.xhc_forward_chain.restype = ctypes.c_int
     L.xhc_backward.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_bwd_args), _vp, ctypes.c_size_t, _vp]
     L.xhc_backward.restype = ctypes.c_int
     L.xhc_strerror.argtypes = [ctypes.c_int]
@@ -89,6 +98,10 @@ def make_desc(B, S, C, N, k, ncomp, dtype, iters=20, eps=1e-6, gate_mode=XHC_GAT
 
 def workspace_size(desc, phase):
     return lib.xhc_workspace_size(ctypes.byref(desc), phase)
+
+
+def carry_size(desc):
+    return lib.xhc_carry_size(ctypes.byref(desc))
 
 
 def strerror(code):
@@ -161,8 +174,14 @@ def _active_array(active):
 
 def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None, bias=None,
             z_save=None, xact_save=None, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID,
-            workspace=None, stream=None, timer=None, desc=None):
-    """xhc_forward on torch device tensors.  X [B*S,N,C], out [B*S,C], W [N*C,P]."""
+            workspace=None, stream=None, timer=None, desc=None, carry_in=None, W_next=None,
+            carry_out=None):
+    """xhc_forward on torch device tensors.  X [B*S,N,C], out [B*S,C], W [N*C,P].
+
+    With carry_in, W_next or carry_out given, calls xhc_forward_chain: carry_in
+    is the previous call's carry_out (X is then not projected and W may be
+    None); W_next [N*C,P] with carry_out (xhc_carry_size bytes) forms the next
+    sublayer's projection partials from X_new."""
     T, N, C = X.shape
     ncomp = 4 if w4 is not None else 1
     if desc is None:
@@ -172,10 +191,17 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
                         ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(X_new), _ptr(h_in),
                         _ptr(z_save), _ptr(xact_save), None if timer is None else timer.handle)
     ws, need = _workspace(desc, XHC_PHASE_FWD, X.device, workspace)
-    rc = lib.xhc_forward(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
-                         _stream_handle(stream))
+    if carry_in is None and W_next is None and carry_out is None:
+        rc = lib.xhc_forward(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
+                             _stream_handle(stream))
+        if rc:
+            raise XhcError(rc, "xhc_forward")
+        return
+    chain = xhc_chain_args(_ptr(carry_in), _ptr(W_next), _ptr(carry_out))
+    rc = lib.xhc_forward_chain(ctypes.byref(desc), ctypes.byref(args), ctypes.byref(chain), ws.data_ptr(),
+                               ws.numel(), _stream_handle(stream))
     if rc:
-        raise XhcError(rc, "xhc_forward")
+        raise XhcError(rc, "xhc_forward_chain")
 
 
 def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None, w4=None, w8=None,

@@ -28,7 +28,7 @@ def test_every_declared_function_is_exported():
 def test_kernel_names():
     names = xhc.kernel_names()
     assert names[:4] == ["pack_wt", "proj", "coef", "mix"]
-    assert "bgrad" in names and "bdots" in names
+    assert "bgrad" in names and "bdots" in names and "mixproj" in names
 
 
 BASE = 1 << 40          # fake, 256-aligned device addresses: validation never dereferences them
@@ -164,6 +164,61 @@ def test_calls_fail_before_launch_without_workspace():
     assert rc == -7
     rc = xhc.lib.xhc_forward(ctypes.byref(d), ctypes.byref(a), fake(20, 128), 1 << 40, None)
     assert rc == -5
+
+
+def good_chain():
+    return xhc.xhc_chain_args(carry_in=fake(21), W_next=fake(22), carry_out=fake(23))
+
+
+def chain_call(d, a, c, ws=None, nbytes=0):
+    return xhc.lib.xhc_forward_chain(ctypes.byref(d), ctypes.byref(a), ctypes.byref(c), ws, nbytes, None)
+
+
+def test_carry_size():
+    # one partial record of 16*NT + 4 floats per token and channel block; blocks
+    # are 64 channels (bf16) or 32 (fp32) wide, at most 16 of them
+    d = desc16()                                 # C = 256 bf16: 4 blocks, P = 48 (NT = 3)
+    assert xhc.carry_size(d) == 4 * 200 * 52 * 4
+    assert xhc.carry_size(desc16(dtype=xhc.XHC_F32)) == 8 * 200 * 52 * 4
+    assert xhc.carry_size(desc16(C=7168)) == 16 * 200 * 52 * 4
+    assert xhc.carry_size(desc16(N=4, ncomp=1)) == 4 * 200 * 36 * 4      # P = 24 (NT = 2)
+    assert xhc.carry_size(desc16(C=7)) == 0
+
+
+def test_chain_error_paths():
+    d = desc16()
+    a, keep = good_fwd(d)
+    # valid chain arguments get as far as the workspace check
+    assert chain_call(d, a, good_chain()) == -7
+    # no chain structure behaves as xhc_forward
+    assert xhc.lib.xhc_forward_chain(ctypes.byref(d), ctypes.byref(a), None, None, 0, None) == -7
+    # with carry_in the state is not projected: W may be NULL
+    b, _ = good_fwd(d)
+    b.W = None
+    assert chain_call(d, b, good_chain()) == -7
+    c = good_chain()
+    c.carry_in = None
+    assert chain_call(d, b, c) == -1
+    # W_next and carry_out come together
+    for f in ("W_next", "carry_out"):
+        c = good_chain()
+        setattr(c, f, None)
+        assert chain_call(d, a, c) == -1, f
+    # the same buffer for carry in and out is allowed; a partial overlap is not
+    c = good_chain()
+    c.carry_out = c.carry_in
+    assert chain_call(d, a, c) == -7
+    c = good_chain()
+    c.carry_out = fake(21, 256)
+    assert chain_call(d, a, c) == -4
+    # carries may not overlap the call's buffers
+    for f, v in (("carry_out", fake(1)), ("carry_out", fake(6, 512)), ("carry_in", fake(8)), ("W_next", fake(9))):
+        c = good_chain()
+        setattr(c, f, v)
+        assert chain_call(d, a, c) == -4, f
+    c = good_chain()
+    c.carry_out = fake(23, 8)
+    assert chain_call(d, a, c) == -5
 
 
 def test_strerror():
