@@ -36,6 +36,9 @@ def parse():
                     help="tokens of the CPU oracle sample (whole sequences, then a causal prefix)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timer", action="store_true", help="skip the per-kernel event pass")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="stacked workloads: project every sublayer's state in its own pass instead of "
+                         "carrying the projection from the previous sublayer's write pass")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 2 GiB device copy (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -50,6 +53,9 @@ def kernel_bytes(w, esz, save_rows=True):
       bxdots  reads state 16C (12 rows + 4 saved) + dh_in C + G 4C  21C
       bdots   reads G 4C + out C; writes dout C                 6C
       bgrad   reads state 16C + dX_new 16C + dh_in C; writes dX 16C  49C
+      mixproj reads state 16C + out C; writes h_in C, 4 rows 4C  22C
+              (the write pass that also projects the state it writes
+              for the next sublayer)
     plus the projection weights (N*C x P) where a kernel reads them."""
     T, C, N, k, P = w.T, w.C, w.N, w.k, w.P
     unit = T * C * esz
@@ -60,6 +66,7 @@ def kernel_bytes(w, esz, save_rows=True):
         "bxdots": (N + 1 + k) * unit,
         "bdots": (k + 1 + 1) * unit,
         "bgrad": (N + N + 1 + N) * unit + wbytes,
+        "mixproj": (N + 1 + 1 + k) * unit + wbytes,
     }
 
 
@@ -145,11 +152,15 @@ def forward_bench(args, w, np, torch, synth, xhc):
     rotating active set).  The state comes from the seeded generator; the
     per-layer parameters of the stack are drawn on the device from torch's
     generator seeded 1000 + layer (same shapes and distributions; the run
-    time does not depend on the values)."""
+    time does not depend on the values).  A stack is chained by default:
+    every sublayer but the last also projects the state it writes for the
+    next one (xhc_forward_chain), so only the first sublayer reads its state
+    twice."""
     T, N, C, P, k = w.T, w.N, w.C, w.P, w.k
     esz = 2 if w.dtype == "bf16" else 4
     sdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    print(f"# workload {w}", file=sys.stderr, flush=True)
+    chain = w.layers > 1 and not args.no_chain
+    print(f"# workload {w} chain={chain}", file=sys.stderr, flush=True)
     d = synth.make_inputs(w, seed=0, state=True)
     X = torch.from_numpy(d.pop("X").view(np.int16)).cuda().view(torch.bfloat16) if esz == 2 else \
         torch.from_numpy(d.pop("X")).cuda()
@@ -172,12 +183,19 @@ def forward_bench(args, w, np, torch, synth, xhc):
     h_in = torch.empty(T, C, dtype=sdt, device="cuda")
     desc = xhc.make_desc(w.B, w.S, C, N, k, w.ncomp, xhc.XHC_BF16 if esz == 2 else xhc.XHC_F32, w.iters, w.eps)
     ws_f = torch.empty(xhc.workspace_size(desc, 0), dtype=torch.uint8, device="cuda")
+    carries = [torch.empty(xhc.carry_size(desc) // 4, device="cuda") for _ in range(2)] if chain else None
 
     def step(timer=None):
-        for p, active in layers:
+        for l, (p, active) in enumerate(layers):
             conv = dict(w4=p["w4"], w8=p["w8"], w12=p["w12"]) if w.ncomp == 4 else {}
+            extra = {}
+            if chain:
+                last = l + 1 == len(layers)
+                extra = dict(carry_in=carries[l % 2] if l > 0 else None,
+                             W_next=None if last else layers[l + 1][0]["W"],
+                             carry_out=None if last else carries[(l + 1) % 2])
             xhc.forward(X, p["out"], p["W"], active, X, h_in, B=w.B, S=w.S, bias=p["bias"], workspace=ws_f,
-                        timer=timer, desc=desc, **conv)
+                        timer=timer, desc=desc, **conv, **extra)
 
     for _ in range(args.warmup):
         step()
@@ -198,17 +216,22 @@ def forward_bench(args, w, np, torch, synth, xhc):
         ms, n = timer.read(name)
         if n:
             kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n}
-            if name in ("proj", "mix"):
+            if name in ("proj", "mix", "mixproj"):
                 kernels[name]["alg_GBps"] = round(kb[name] / (ms * 1e-3 / n) / 1e9, 1)
-    alg_c = (N + 1 + 1 + k) * w.layers          # per token: state, out, h_in, k rows
+    # per token and step, in units of C: every sublayer reads its state, out
+    # and writes h_in and k rows (22C at N = 16); without the chain every
+    # sublayer also reads its state for the projection, with it only the first
+    alg_c = (N + 1 + 1 + k) * w.layers
+    touched_c = alg_c + N * (1 if chain else w.layers)
     result = {"metric": f"tokens/s, xHC sublayer forward ({w.name})", "value": round(T * args.steps / elapsed, 1),
               "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
               "config": {"workload": f"{w.name}: B={w.B} S={w.S} C={C} N={N} k={k} ncomp={w.ncomp} "
-                                     f"layers={w.layers}, in-place forward"},
+                                     f"layers={w.layers}, in-place forward"
+                                     + (", chained projection" if chain else "")},
               "layer_tokens_per_s": round(T * w.layers * args.steps / elapsed, 1),
-              "step_hbm": {"alg_bytes_per_token_in_C": alg_c,
+              "step_hbm": {"alg_bytes_per_token_in_C": alg_c, "touched_bytes_per_token_in_C": touched_c,
                            "alg_GBps": round(alg_c * T * C * esz / (ms_per_step * 1e-3) / 1e9, 1)},
               "kernels": kernels}
     print(json.dumps(result), flush=True)

@@ -50,8 +50,25 @@ def build(verbose=False):
                 print(out)
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
+    _check_kernel_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_kernel_stubs(lib):
+    """A kernel template whose host-side instantiation fails (a deferred
+    device-code diagnostic) leaves its launch stub undefined: the library
+    links but cannot be loaded.  Fail the build instead."""
+    try:
+        out = subprocess.run(["nm", "-D", "--undefined-only", lib], stdout=subprocess.PIPE,
+                             stderr=subprocess.DEVNULL, text=True).stdout
+    except FileNotFoundError:
+        return
+    missing = [l.split()[-1] for l in out.splitlines() if "__device_stub__" in l]
+    if missing:
+        os.remove(lib)
+        raise RuntimeError("kernel launch stubs missing from the library (host-side instantiation failed):\n  "
+                           + "\n  ".join(missing))
 
 
 if __name__ == "__main__":

@@ -46,6 +46,7 @@ constexpr int MP_WAVES = 8;
 constexpr int MP_TOK = 16 * MP_WAVES;     // tokens per workgroup
 constexpr int MP_RPS = 4;                 // state rows per step
 constexpr int MP_WSLOT = MP_RPS * 6144;   // W' bytes per step (NT = 3)
+constexpr int CL_STRIDE = 52;             // floats per token of the LDS coefficient rows
 
 // value of lane (l - n) mod 16 within the lane's row of 16
 template <int n>
@@ -87,7 +88,8 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
   static_assert(MP_RPS * SLOTB <= MP_WSLOT && SLOTB % 1024 == 0, "W' step slot");
   __shared__ __attribute__((aligned(16))) unsigned char wst[2][MP_WSLOT];
   __shared__ __attribute__((aligned(16))) float cwl[2][24][64];
-  __shared__ __attribute__((aligned(16))) float cl[MP_TOK][48];
+  __shared__ __attribute__((aligned(16))) float cl[MP_TOK][CL_STRIDE];
+  __shared__ __attribute__((aligned(16))) unsigned char xbuf[MP_WAVES][MP_RPS * 1024 * KS * (EB / 2)];
 
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int cb = lb / nbatch, bt = lb - cb * nbatch;
@@ -108,13 +110,13 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
   // position mask discards
   const int th = max(t0 - 16, 0);
   const uint32_t cur_soff = (uint32_t)(t0 - th) * ((uint32_t)C * EB);
-  const rsrc_t rx = make_rsrc(static_cast<const char*>(X) + (size_t)tc * tokb, clamp_bytes(ntile, tokb));
-  const rsrc_t rxn = make_rsrc(static_cast<char*>(Xnew) + (size_t)tc * tokb, clamp_bytes(ntile, tokb));
-  const rsrc_t rout = make_rsrc(static_cast<const char*>(out) + (size_t)min(th, T) * rowb,
+  const rsrc_t rx = make_rsrc_u(static_cast<const char*>(X) + (size_t)tc * tokb, clamp_bytes(ntile, tokb));
+  const rsrc_t rxn = make_rsrc_u(static_cast<char*>(Xnew) + (size_t)tc * tokb, clamp_bytes(ntile, tokb));
+  const rsrc_t rout = make_rsrc_u(static_cast<const char*>(out) + (size_t)min(th, T) * rowb,
                                 clamp_bytes(min(max(T - th, 0), 32), rowb));
-  const rsrc_t rh = make_rsrc(static_cast<char*>(hin) + (size_t)tc * rowb, clamp_bytes(ntile, rowb));
+  const rsrc_t rh = make_rsrc_u(static_cast<char*>(hin) + (size_t)tc * rowb, clamp_bytes(ntile, rowb));
   const uint32_t xsb = (uint32_t)k * rowb;              // bytes per token of xact
-  const rsrc_t rxs = make_rsrc(xact ? static_cast<char*>(xact) + (size_t)tc * xsb : Xnew,
+  const rsrc_t rxs = make_rsrc_u(xact ? static_cast<char*>(xact) + (size_t)tc * xsb : Xnew,
                                xact ? clamp_bytes(ntile, xsb) : 0u);
 
   // lane byte offset of (chunk c, K-step u) in a row of `stride` bytes per
@@ -124,17 +126,21 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     return ch < C ? (uint32_t)r * stride + (uint32_t)ch * EB : 0x80000000u;
   };
 
-  // coefficients of the batch's tokens -> cl[token][pre 16 | post 16 | res 16]
+  // coefficients of the batch's tokens -> cl[token][pre 16 | post 16 | res 16 | r, pad]
+  // (13 pieces of 16 bytes per token: the padded row stride spreads the 16
+  // tokens a wave reads over the LDS banks)
   {
+    constexpr int PIECES = CL_STRIDE / 4;
     const int ntok = min(max(T - tb, 0), MP_TOK);
-    const rsrc_t rco = make_rsrc(coef + (size_t)min(tb, T) * COEF_STRIDE, clamp_bytes(ntok, COEF_STRIDE * 4));
+    const rsrc_t rco = make_rsrc_u(coef + (size_t)min(tb, T) * COEF_STRIDE, clamp_bytes(ntok, COEF_STRIDE * 4));
 #pragma unroll
-    for (int j = 0; j < MP_TOK * 12 / (64 * MP_WAVES); ++j) {
-      const int id = j * 64 * MP_WAVES + tid;            // 16-byte piece: token id/12, part id%12
-      const int tk = id / 12, part = id - tk * 12;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rco, (lds_void_t*)(reinterpret_cast<unsigned char*>(&cl[0][0]) + (j * 64 * MP_WAVES + wave * 64) * 16), 16,
-          (uint32_t)(tk * COEF_STRIDE + part * 4) * 4, 0, 0, 0);
+    for (int j = 0; j < (MP_TOK * PIECES + 64 * MP_WAVES - 1) / (64 * MP_WAVES); ++j) {
+      const int id = j * 64 * MP_WAVES + tid;            // 16-byte piece: token id/PIECES, part id%PIECES
+      const int tk = id / PIECES, part = id - tk * PIECES;
+      if (j * 64 * MP_WAVES + wave * 64 < MP_TOK * PIECES)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rco, (lds_void_t*)(reinterpret_cast<unsigned char*>(&cl[0][0]) + (j * 64 * MP_WAVES + wave * 64) * 16),
+            16, (uint32_t)(tk * COEF_STRIDE + part * 4) * 4, 0, 0, 0);
     }
   }
 
@@ -195,16 +201,42 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
   };
 
   // register state
-  V8<E> xc[MP_RPS][KS], xn[MP_RPS][KS];       // rows of the current step; of the next (in flight)
+  V8<E> xc[MP_RPS][KS];                       // rows of the current step
   V8<E> oc[KS], oh[KS];                       // out and its halo of the chunk (loaded after the
                                               // previous chunk's first step consumed them)
-  auto load_rows = [&](int c, int q, V8<E> (&x)[MP_RPS][KS]) {
+  // the next step's rows go to the wave's LDS buffer by LDS-DMA (16 bytes
+  // per lane and copy, lane-ordered), so that prefetching costs no
+  // registers; the step reads them back into registers at its start
+  constexpr int PP = EB / 2;                  // 16-byte pieces per lane and V8
+  auto dma_rows = [&](int c, int q) {
 #pragma unroll
     for (int j = 0; j < MP_RPS; ++j) {
       const uint32_t soff = (uint32_t)row_of(ro, q * MP_RPS + j) * rowb;    // rows past N repeat a valid row
 #pragma unroll
-      for (int u = 0; u < KS; ++u) x[j][u] = bload<E, 8>(rx, lane_off(c, u, tokb), soff);
+      for (int u = 0; u < KS; ++u) {
+        const uint32_t vo = lane_off(c, u, tokb);
+#pragma unroll
+        for (int pp = 0; pp < PP; ++pp)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)&xbuf[wave][((j * KS + u) * PP + pp) * 1024], 16,
+                                                   (int)(vo + pp * 16), (int)soff, 0, 0);
+      }
     }
+  };
+  auto read_rows = [&]() {
+#pragma unroll
+    for (int j = 0; j < MP_RPS; ++j)
+#pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        unsigned w[4 * PP];
+#pragma unroll
+        for (int pp = 0; pp < PP; ++pp) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&xbuf[wave][((j * KS + u) * PP + pp) * 1024 + lane * 16]);
+          w[4 * pp] = v[0]; w[4 * pp + 1] = v[1]; w[4 * pp + 2] = v[2]; w[4 * pp + 3] = v[3];
+        }
+        __builtin_memcpy(&xc[j][u], w, sizeof(w));
+      }
+    // the buffer is refilled right after: every read must have completed
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
   };
   auto load_out = [&](int c) {
 #pragma unroll
@@ -253,19 +285,16 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     wait_vmcnt<0>();
     if constexpr (FIRST && NCOMP == 4) store_conv(c);
     __syncthreads();            // W' of step s, conv weights and coefficients visible; step s-1 consumed
-    // the next step's loads: issued at once, except in a chunk's first step,
-    // which issues them after its TFA part (that part needs many registers)
-    auto issue_next = [&]() {
-      if (q + 1 < nq) {
-        w_dma(s + 1);
-        load_rows(c, q + 1, xn);
-      } else if (cq + 1 < c1 - c0) {
-        w_dma(s + 1);
-        load_rows(c + 1, 0, xn);
-        if constexpr (NCOMP == 4) load_conv(c + 1);
-      }
-    };
-    if constexpr (!FIRST) issue_next();
+    read_rows();
+    // the next step's copies
+    if (q + 1 < nq) {
+      w_dma(s + 1);
+      dma_rows(c, q + 1);
+    } else if (cq + 1 < c1 - c0) {
+      w_dma(s + 1);
+      dma_rows(c + 1, 0);
+      if constexpr (NCOMP == 4) load_conv(c + 1);
+    }
     const unsigned char* wsl = wst[s & 1];
 
     if constexpr (FIRST) {
@@ -351,7 +380,6 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     }
     // `out` of the next chunk (this chunk's has been consumed)
     if constexpr (FIRST) {
-      issue_next();
       if (cq + 1 < c1 - c0) load_out(c + 1);
     }
     // the step's other rows (untouched by the update)
@@ -376,16 +404,12 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
         for (int e = 0; e < 8; ++e) hacc[u][e] = 0.f;
       }
     }
-#pragma unroll
-    for (int j = 0; j < MP_RPS; ++j)
-#pragma unroll
-      for (int u = 0; u < KS; ++u) xc[j][u] = xn[j][u];
   };
 
   if constexpr (NCOMP == 4) load_conv(c0);
   if (c1 > c0) {
     w_dma(0);
-    load_rows(c0, 0, xc);
+    dma_rows(c0, 0);
     load_out(c0);
   }
   for (int cq = 0; cq < c1 - c0; ++cq) {

@@ -155,6 +155,18 @@ __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
+// make_rsrc with the base address and size read from the first lane: the
+// compiler keeps the resource in scalar registers even where it cannot prove
+// the operands uniform (a resource in vector registers turns every access
+// into a loop over the distinct values).  The operands must be uniform.
+__device__ inline rsrc_t make_rsrc_u(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint32_t n = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);
+  return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), n);
+}
+
 template <typename E, int W>
 __device__ inline Vec<E, W> bload(rsrc_t r, uint32_t voff, uint32_t soff) {
   constexpr int B = W * E::bytes;
