@@ -261,10 +261,20 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
   // projection from `xv` (the row of the new state), K-step u
   auto row_work = [&](const unsigned char* wsl, int j, int u, int c, float hp, const V8<E>& xold, const V8<E>& xv) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      hacc[u][e] = fmaf(hp, xold.f(e), hacc[u][e]);
-      const float y = xv.f(e);
-      ss = fmaf(y, y, ss);
+    for (int e = 0; e < 8; ++e) hacc[u][e] = fmaf(hp, xold.f(e), hacc[u][e]);
+    if constexpr (EB == 2) {
+      // bf16 pairs: the products are exact in fp32
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16x2 p2 = __builtin_bit_cast(bf16x2, xv.w[d]);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, ss, false);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = xv.f(e);
+        ss = fmaf(y, y, ss);
+      }
     }
     if (c * KS + u < nks) {
 #pragma unroll
