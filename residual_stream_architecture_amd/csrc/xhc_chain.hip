@@ -48,37 +48,36 @@ constexpr int MP_RPS = 4;                 // state rows per step
 constexpr int MP_WSLOT = MP_RPS * 6144;   // W' bytes per step (NT = 3)
 constexpr int CL_STRIDE = 52;             // floats per token of the LDS coefficient rows
 
-// value of lane (l - n) mod 16 within the lane's row of 16
-template <int n>
-__device__ inline unsigned ror16(unsigned v) {
-  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + n, 0xF, 0xF, false);
-}
-
 // `out` n positions back: the lane's token is r of a 16-token tile, `cur`
 // holds the tile's values and `halo` those of the 16 tokens before it.
+// Lanes r >= n take lane r - n of `cur` (a row shift, whose source lanes
+// r < n are out of the row and keep the destination's old value); lanes
+// r < n take lane r - n + 16 of `halo` (a row rotation), placed first.
 template <int n, typename E>
-__device__ inline V8<E> window_back(const V8<E>& cur, const V8<E>& halo, bool from_cur) {
+__device__ inline V8<E> window_back(const V8<E>& cur, const V8<E>& halo) {
   constexpr int NWD = (int)sizeof(V8<E>) / 4;
   unsigned cw[NWD], hw[NWD], ow[NWD];
   __builtin_memcpy(cw, &cur, sizeof(cw));
   __builtin_memcpy(hw, &halo, sizeof(hw));
 #pragma unroll
   for (int j = 0; j < NWD; ++j) {
-    const unsigned a = ror16<n>(cw[j]), b = ror16<n>(hw[j]);
-    ow[j] = from_cur ? a : b;
+    const int rot = __builtin_amdgcn_update_dpp(0, (int)hw[j], 0x120 + n, 0xF, 0xF, false);    // row_ror:n
+    ow[j] = (unsigned)__builtin_amdgcn_update_dpp(rot, (int)cw[j], 0x110 + n, 0xF, 0xF, false); // row_shr:n
   }
   V8<E> o;
   __builtin_memcpy(&o, ow, sizeof(ow));
   return o;
 }
 
-template <typename E, int NT, int NCOMP>
+template <typename E, int NT, int NCOMP, bool FAST>
 __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     const void* __restrict__ X, const void* __restrict__ out, const float* __restrict__ w4,
     const float* __restrict__ w8, const float* __restrict__ w12, const float* __restrict__ coef,
     const void* __restrict__ Wf, void* Xnew, void* __restrict__ hin, void* __restrict__ xact,
-    float* __restrict__ carry, RowOrder ro, int T, int S, int C, int N, int k, int in_place, int cpw,
+    float* __restrict__ carry, RowOrder ro, int T, int S, int C, int N_, int k_, int in_place, int cpw,
     int nch, int nbatch, int ZST) {
+  const int N = FAST ? 16 : N_;
+  const int k = FAST ? 4 : k_;
   constexpr int EB = E::bytes;
   constexpr int KS = EB == 2 ? 2 : 1;        // MFMA K-steps of 32 channels per chunk
   constexpr int CW = 32 * KS;                // channels per chunk
@@ -329,7 +328,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
             // U_m = sum_{n < K_m} w_m[c, K_m - 1 - n] * out[t - n]
             static_for<1, 12>([&](auto NI) {
               constexpr int n = decltype(NI)::value;
-              const V8<E> ob = window_back<n, E>(oc[u], oh[u], r >= n);
+              const V8<E> ob = window_back<n, E>(oc[u], oh[u]);
               float of[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) of[e] = spos < n ? 0.f : ob.f(4 * h + e);
@@ -457,7 +456,7 @@ static void launch_mixproj_e(const Plan& p, const xhc_fwd_args* a, const float* 
   const int in_place = a->X_new == a->X;
   const dim3 grid(p.mp_ncb * p.mp_nbatch);
 #define XHC_MP(NT, NC)                                                                                            \
-  k_mixproj<E, NT, NC><<<grid, 64 * MP_WAVES, 0, st>>>(a->X, a->out, a->w4, a->w8, a->w12, coef, Wf, a->X_new,    \
+  k_mixproj<E, NT, NC, false><<<grid, 64 * MP_WAVES, 0, st>>>(a->X, a->out, a->w4, a->w8, a->w12, coef, Wf, a->X_new,    \
                                                        a->h_in, a->xact_save, carry, ro, p.T, p.S, p.C, p.N, p.k, \
                                                        in_place, p.mp_cpw, p.mp_nch, p.mp_nbatch, p.ZST)
   if (p.nc == 4) {
