@@ -86,7 +86,9 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
   constexpr int PPR = SLOTB / 1024;          // 1 KiB copies per row
   static_assert(MP_RPS * SLOTB <= MP_WSLOT && SLOTB % 1024 == 0, "W' step slot");
   __shared__ __attribute__((aligned(16))) unsigned char wst[2][MP_WSLOT];
-  __shared__ __attribute__((aligned(16))) float cwl[2][24][64];
+  // the active rows' K-step-1 fragments, kept from a chunk's first step to its third
+  __shared__ __attribute__((aligned(16))) unsigned char wa1[MP_RPS * 3 * 1024];
+  __shared__ __attribute__((aligned(16))) float cwl[24][64];
   __shared__ __attribute__((aligned(16))) float cl[MP_TOK][CL_STRIDE];
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[MP_WAVES][MP_RPS * 1024 * KS * (EB / 2)];
 
@@ -98,6 +100,10 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
   const int tb = bt * MP_TOK, t0 = tb + 16 * wave, t = t0 + r;
   const int spos = (t < T ? t : 0) % S;                 // position in the sequence
   const int nq = (N + MP_RPS - 1) / MP_RPS;             // steps per chunk
+  // bf16 chunks hold two K-steps; with four steps per chunk the active rows'
+  // second K-step (TFA, new rows, their projection) moves to the third step,
+  // so that the arithmetic of the first step is split over two steps
+  const bool split = KS == 2 && nq == 4;
   const int c0 = cb * cpw, c1 = min(c0 + cpw, nch);
   const int nsteps = (c1 - c0) * nq;
   const int nks = (C + 31) >> 5;                        // K-steps of the packed W'
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
       if (f < 24 * CW) {
         int tap, cc;
         (void)conv_src(c, f, tap, cc);
-        cwl[c & 1][tap][cc] = cwr[i];
+        cwl[tap][cc] = cwr[i];
       }
     }
   };
@@ -192,8 +198,12 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
         if (slot < N && o * 1024 < valid_bytes) {
           const unsigned char* src = static_cast<const unsigned char*>(Wf) +
                                      ((size_t)row_of(ro, slot) * nks + ksb) * NT * FB + o * 1024 + lane * 16;
-          __builtin_amdgcn_global_load_lds((const gbl_void_t*)src, (lds_void_t*)&wst[s & 1][j * SLOTB + o * 1024], 16,
-                                           0, 0);
+          if (split && q == 0 && o >= PPR / 2)        // K-step 1 of an active row
+            __builtin_amdgcn_global_load_lds((const gbl_void_t*)src,
+                                             (lds_void_t*)&wa1[j * (PPR / 2) * 1024 + (o - PPR / 2) * 1024], 16, 0, 0);
+          else
+            __builtin_amdgcn_global_load_lds((const gbl_void_t*)src, (lds_void_t*)&wst[s & 1][j * SLOTB + o * 1024],
+                                             16, 0, 0);
         }
       }
     }
@@ -258,7 +268,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
 
   // one row of the step: h_in from the old values, sum of squares and the
   // projection from `xv` (the row of the new state), K-step u
-  auto row_work = [&](const unsigned char* wsl, int j, int u, int c, float hp, const V8<E>& xold, const V8<E>& xv) {
+  auto row_work = [&](const unsigned char* wfr, int u, int c, float hp, const V8<E>& xold, const V8<E>& xv) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) hacc[u][e] = fmaf(hp, xold.f(e), hacc[u][e]);
     if constexpr (EB == 2) {
@@ -278,21 +288,106 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     if (c * KS + u < nks) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const V8<E> wv = *reinterpret_cast<const V8<E>*>(wsl + j * SLOTB + (u * NT + n) * FB + lane * 8 * EB);
+        const V8<E> wv = *reinterpret_cast<const V8<E>*>(wfr + n * FB + lane * 8 * EB);
         acc[n] = mma32(wv, xv, acc[n]);
       }
     }
   };
 
+  // K-step u of chunk c for the active rows: TFA components, the new rows
+  // (stored, and projected with the fragments at wact + row j * wstride),
+  // h_in and sum of squares.  xs[b] holds active row b's K-step u.
+  auto active_u = [&](int c, int u, const V8<E>* xs, const unsigned char* wact, int wstride) {
+    unsigned nvw[4][sizeof(V8<E>) / 4];       // packed new rows: [a][dword] (bf16 pairs or fp32 bits)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float u0[4], u1[4], u2[4], u3[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u0[e] = oc[u].f(4 * h + e);
+      if constexpr (NCOMP == 4) {
+        const float* wl = &cwl[0][32 * u + 8 * g + 4 * h];
+        auto tap4 = [&](int tap) { return *reinterpret_cast<const f32x4*>(wl + tap * 64); };
+        {
+          const f32x4 wa = tap4(3), wb = tap4(4 + 7), wc = tap4(12 + 11);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { u1[e] = wa[e] * u0[e]; u2[e] = wb[e] * u0[e]; u3[e] = wc[e] * u0[e]; }
+        }
+        // U_m = sum_{n < K_m} w_m[c, K_m - 1 - n] * out[t - n]
+        static_for<1, 12>([&](auto NI) {
+          constexpr int n = decltype(NI)::value;
+          const V8<E> ob = window_back<n, E>(oc[u], oh[u]);
+          float of[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) of[e] = spos < n ? 0.f : ob.f(4 * h + e);
+          if constexpr (n < 4) {
+            const f32x4 w = tap4(3 - n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u1[e] = fmaf(w[e], of[e], u1[e]);
+          }
+          if constexpr (n < 8) {
+            const f32x4 w = tap4(4 + 7 - n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u2[e] = fmaf(w[e], of[e], u2[e]);
+          }
+          {
+            const f32x4 w = tap4(12 + 11 - n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u3[e] = fmaf(w[e], of[e], u3[e]);
+          }
+        });
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        if (a < k) {
+          const f32x4 res = *reinterpret_cast<const f32x4*>(co + 32 + 4 * a);
+          const f32x4 post = *reinterpret_cast<const f32x4*>(co + 16 + 4 * a);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float y = 0.f;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              if (b < k) y = fmaf(res[b], xs[b].f(4 * h + e), y);
+            y = fmaf(post[0], u0[e], y);
+            if constexpr (NCOMP == 4) {
+              y = fmaf(post[1], u1[e], y);
+              y = fmaf(post[2], u2[e], y);
+              y = fmaf(post[3], u3[e], y);
+            }
+            v[e] = y;
+          }
+          const Vec<E, 4> hv = Vec<E, 4>::from_float(v);
+          __builtin_memcpy(&nvw[a][h * (int)sizeof(Vec<E, 4>) / 4], &hv, sizeof(hv));
+        }
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      if (a < k) {
+        V8<E> nv;
+        __builtin_memcpy(&nv, &nvw[a][0], sizeof(nv));
+        const int row = row_of(ro, a);
+        bstore<E, 8>(nv, rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
+        if (xact) bstore<E, 8>(xs[a], rxs, lane_off(c, u, xsb), (uint32_t)a * rowb);
+        row_work(wact + a * wstride, u, c, co[row], xs[a], nv);
+      }
+    }
+  };
+  V8<E> xa1[4];                               // active rows' K-step 1, first to third step
+
   // step (chunk cq, quarter q): rows 4q .. 4q+4 of the row order.  FIRST:
-  // q == 0, which also forms the new active rows.
+  // q == 0, which also forms the new active rows (both K-steps, or K-step 0
+  // when split, K-step 1 then following in the third step).
   auto step = [&](auto FI, int cq, int q) {
     constexpr bool FIRST = decltype(FI)::value;
     auto& x = xc;
     const int c = c0 + cq;
     const int s = cq * nq + q;
     wait_vmcnt<0>();
-    if constexpr (FIRST && NCOMP == 4) store_conv(c);
+    if constexpr (FIRST && NCOMP == 4) {
+      if (nq == 1) __syncthreads();     // one step per chunk: every wave is done with the last conv weights
+      store_conv(c);
+    }
     __syncthreads();            // W' of step s, conv weights and coefficients visible; step s-1 consumed
     read_rows();
     // the next step's copies
@@ -307,89 +402,26 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     const unsigned char* wsl = wst[s & 1];
 
     if constexpr (FIRST) {
-      // TFA components and the new active rows, one K-step and one half of
-      // the lane's 8 channels at a time (keeps the live registers low)
+      if (split) {
+        V8<E> xs0[4];
 #pragma unroll
-      for (int u = 0; u < KS; ++u) {
-        unsigned nvw[4][sizeof(V8<E>) / 4];     // packed new rows: [a][dword] (bf16 pairs or fp32 bits)
+        for (int b = 0; b < 4; ++b) { xs0[b] = x[b][0]; xa1[b] = x[b][KS - 1]; }
+        active_u(c, 0, xs0, wsl, SLOTB);
+      } else {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float u0[4], u1[4], u2[4], u3[4];
+        for (int u = 0; u < KS; ++u) {
+          V8<E> xs[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) u0[e] = oc[u].f(4 * h + e);
-          if constexpr (NCOMP == 4) {
-            const float* wl = &cwl[c & 1][0][32 * u + 8 * g + 4 * h];
-            auto tap4 = [&](int tap) { return *reinterpret_cast<const f32x4*>(wl + tap * 64); };
-            {
-              const f32x4 wa = tap4(3), wb = tap4(4 + 7), wc = tap4(12 + 11);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) { u1[e] = wa[e] * u0[e]; u2[e] = wb[e] * u0[e]; u3[e] = wc[e] * u0[e]; }
-            }
-            // U_m = sum_{n < K_m} w_m[c, K_m - 1 - n] * out[t - n]
-            static_for<1, 12>([&](auto NI) {
-              constexpr int n = decltype(NI)::value;
-              const V8<E> ob = window_back<n, E>(oc[u], oh[u]);
-              float of[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) of[e] = spos < n ? 0.f : ob.f(4 * h + e);
-              if constexpr (n < 4) {
-                const f32x4 w = tap4(3 - n);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) u1[e] = fmaf(w[e], of[e], u1[e]);
-              }
-              if constexpr (n < 8) {
-                const f32x4 w = tap4(4 + 7 - n);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) u2[e] = fmaf(w[e], of[e], u2[e]);
-              }
-              {
-                const f32x4 w = tap4(12 + 11 - n);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) u3[e] = fmaf(w[e], of[e], u3[e]);
-              }
-            });
-          }
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            if (a < k) {
-              const f32x4 res = *reinterpret_cast<const f32x4*>(co + 32 + 4 * a);
-              const f32x4 post = *reinterpret_cast<const f32x4*>(co + 16 + 4 * a);
-              float v[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                float y = 0.f;
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                  if (b < k) y = fmaf(res[b], x[b][u].f(4 * h + e), y);
-                y = fmaf(post[0], u0[e], y);
-                if constexpr (NCOMP == 4) {
-                  y = fmaf(post[1], u1[e], y);
-                  y = fmaf(post[2], u2[e], y);
-                  y = fmaf(post[3], u3[e], y);
-                }
-                v[e] = y;
-              }
-              const Vec<E, 4> hv = Vec<E, 4>::from_float(v);
-              __builtin_memcpy(&nvw[a][h * (int)sizeof(Vec<E, 4>) / 4], &hv, sizeof(hv));
-            }
-          }
+          for (int b = 0; b < 4; ++b) xs[b] = x[b][u];
+          active_u(c, u, xs, wsl + u * NT * FB, SLOTB);
         }
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          if (a < k) {
-            V8<E> nv;
-            __builtin_memcpy(&nv, &nvw[a][0], sizeof(nv));
-            const int row = row_of(ro, a);
-            bstore<E, 8>(nv, rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
-            if (xact) bstore<E, 8>(x[a][u], rxs, lane_off(c, u, xsb), (uint32_t)a * rowb);
-            row_work(wsl, a, u, c, co[row], x[a][u], nv);
-          }
-        }
+        if (cq + 1 < c1 - c0) load_out(c + 1);      // this chunk's `out` has been consumed
       }
-    }
-    // `out` of the next chunk (this chunk's has been consumed)
-    if constexpr (FIRST) {
-      if (cq + 1 < c1 - c0) load_out(c + 1);
+    } else {
+      if (split && q == 2) {
+        active_u(c, KS - 1, xa1, wa1, NT * FB);
+        if (cq + 1 < c1 - c0) load_out(c + 1);
+      }
     }
     // the step's other rows (untouched by the update)
 #pragma unroll
@@ -400,7 +432,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
         const float hp = co[row];
 #pragma unroll
         for (int u = 0; u < KS; ++u) {
-          row_work(wsl, j, u, c, hp, x[j][u], x[j][u]);
+          row_work(wsl + j * SLOTB + u * NT * FB, u, c, hp, x[j][u], x[j][u]);
           if (!in_place) bstore<E, 8>(x[j][u], rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
         }
       }
