@@ -70,9 +70,21 @@ def kernel_bytes(w, esz, save_rows=True):
     }
 
 
-def source_digest():
+# the source file that holds each kernel (the shared headers count for all)
+KERNEL_SOURCE = {"proj": "xhc_fwd.hip", "mix": "xhc_fwd.hip", "bxdots": "xhc_bwd.hip", "bdots": "xhc_bwd.hip",
+                 "bgrad": "xhc_bwd.hip", "mixproj": "xhc_chain.hip"}
+
+
+def source_digest(kernel=None):
+    """sha256 (first 16 hex digits) of the sources a kernel is built from:
+    the shared headers and the kernel's own file (every source when kernel
+    is None)."""
+    csrc = os.path.join(ROOT, "residual_stream_architecture_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "*")))
+    if kernel is not None:
+        files = [f for f in files if f.endswith(".h") or os.path.basename(f) == KERNEL_SOURCE[kernel]]
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "residual_stream_architecture_amd", "csrc", "*"))):
+    for f in files:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -89,7 +101,7 @@ def measured_traffic(kernel, workload):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("source_digest") != source_digest():
+    if rec.get("source_digest") != source_digest(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
