@@ -49,11 +49,23 @@ shared with the GPU library and listed in the design notes):
   O4  TFA: U_0 = out; U_m[s, c] = sum_q w_m[c, q] * out[s - (K_m - 1) + q, c]
       for K = 4, 8, 12, positions before the start of the sequence read 0 (no
       leak between sequences of a batch); w_m[c, K_m - 1] multiplies the
-      current token.  No Gram-Schmidt.
+      current token.
   O5  write: for active stream a (index i_a = active[a]):
         X'[t, i_a] = sum_b H_res[a, b] X[t, i_b] + sum_c H_post[a, c] U_c[t];
       every other stream is copied unchanged.  Dense read:
         h_in[t] = sum_i H_pre[i] X[t, i].
+  O6  Gram-Schmidt (optional, [R-GS]; off by default, the form the pages
+      keep when the backbone trains with Muon): per token, over the C
+      channels, u~_0 = U_0 and for c = 1, 2, 3 in turn the component keeps
+      its own direction minus its projections on the components already
+      produced, removed one after another (modified Gram-Schmidt):
+        v = U_c;  for j < c:  v -= <v, u~_j> / (<u~_j, u~_j> + C*gs_eps) u~_j
+        u~_c = v.
+      No normalisation (the output keeps its magnitude).  gs_eps (1e-6 by
+      default, the RMS epsilon scaled to a sum over C) keeps a zero
+      component -- the zero-initialised conv branches at the start of
+      training -- from dividing 0 by 0; with it such a component stays 0.
+      The write uses u~ in place of U.
 """
 
 import numpy as np
@@ -143,8 +155,30 @@ def tfa_components(out, B, S, conv_ws):
     return np.stack(comps, axis=1)
 
 
+def gram_schmidt(U, gs_eps):
+    """O6 / [R-GS]: modified Gram-Schmidt over the components, per token.
+
+    U: [T, m, C].  Returns (Ut [T, m, C], steps), steps = the list of
+    (c, j, v_before, alpha, den) of every projection removal, in order,
+    which the backward walks in reverse.
+    """
+    T, m, C = U.shape
+    Ut = U.copy()
+    steps = []
+    for c in range(1, m):
+        v = U[:, c, :].copy()
+        for j in range(c):
+            uj = Ut[:, j, :]
+            den = np.sum(uj * uj, axis=1) + C * gs_eps
+            alpha = np.sum(v * uj, axis=1) / den
+            steps.append((c, j, v, alpha, den))
+            v = v - alpha[:, None] * uj
+        Ut[:, c, :] = v
+    return Ut, steps
+
+
 def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
-            gate_mode="sigmoid"):
+            gate_mode="sigmoid", gram_schmidt_on=False, gs_eps=1e-6):
     """One xHC sublayer update, forward ([R-DRSW] write formula, O1-O5).
 
     X:      [B*S, N, C]  residual state before the update
@@ -187,6 +221,8 @@ def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
 
     # temporal feature augmentation over the sublayer output
     U = tfa_components(out, B, S, conv_ws)
+    if gram_schmidt_on:
+        U, _ = gram_schmidt(U, gs_eps)
 
     # sparse write: only the k active streams are rewritten
     X_new = X.copy()
@@ -237,8 +273,40 @@ def causal_depthwise_conv_backward(out_bsc, w, dy):
     return d_out, d_w
 
 
+def gram_schmidt_backward(U, gs_eps, dUt):
+    """Adjoint of gram_schmidt: dU from dUt, walking the removals backwards.
+
+    One removal v' = v - alpha u~_j with alpha = <v, u~_j> / den_j and
+    den_j = <u~_j, u~_j> + C*gs_eps gives, for the gradient dv' of v':
+      dalpha = -<dv', u~_j>
+      dv     = dv' + dalpha / den_j * u~_j
+      du~_j += -alpha dv' + dalpha / den_j * (v - 2 alpha u~_j).
+    u~_c = v after the last removal of component c, and the removals of
+    later components only read u~_c, so u~_c's gradient is complete when
+    its own removals are walked; it then flows to U_c.
+    """
+    Ut, steps = gram_schmidt(U, gs_eps)
+    g = dUt.copy()                        # running gradient of every u~
+    dU = np.zeros_like(U)
+    c_cur, dv = None, None
+    for c, j, v, alpha, den in reversed(steps):
+        if c != c_cur:
+            if c_cur is not None:
+                dU[:, c_cur, :] = dv
+            c_cur, dv = c, g[:, c, :].copy()
+        uj = Ut[:, j, :]
+        dalpha = -np.sum(dv * uj, axis=1)
+        q = dalpha / den
+        g[:, j, :] += -alpha[:, None] * dv + q[:, None] * (v - 2.0 * alpha[:, None] * uj)
+        dv = dv + q[:, None] * uj
+    if c_cur is not None:
+        dU[:, c_cur, :] = dv
+    dU[:, 0, :] = g[:, 0, :]
+    return dU
+
+
 def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
-             iters=20, eps=1e-6, gate_mode="sigmoid"):
+             iters=20, eps=1e-6, gate_mode="sigmoid", gram_schmidt_on=False, gs_eps=1e-6):
     """Gradients of the forward above for upstream gradients dX_new, dh_in.
 
     Returns dict(dX [T,N,C], dout [T,C], dW [N*C,P], db [P],
@@ -265,7 +333,8 @@ def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
     else:
         H_pre, H_post = np.ones_like(z_pre), np.ones_like(z_post)
     H_res, _ = sinkhorn(L, iters)
-    U = tfa_components(out, B, S, conv_ws)
+    U_raw = tfa_components(out, B, S, conv_ws)
+    U = gram_schmidt(U_raw, gs_eps)[0] if gram_schmidt_on else U_raw
 
     G = dX_new[:, act, :]                                         # [T, k, C]
     Xa = X[:, act, :]
@@ -301,7 +370,9 @@ def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
     dXf = (dxhat - xhat * (np.sum(dxhat * xhat, axis=1, keepdims=True) / n)) / r[:, None]
     dX += dXf.reshape(T, N, C)
 
-    # through temporal feature augmentation
+    # through Gram-Schmidt, then temporal feature augmentation
+    if gram_schmidt_on:
+        dU = gram_schmidt_backward(U_raw, gs_eps, dU)
     dout = dU[:, 0, :].copy()
     out_bsc = out.reshape(B, S, C)
     dconv = []

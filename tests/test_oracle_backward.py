@@ -57,8 +57,21 @@ def test_backward_matches_central_differences(ncomp, gate_mode):
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
 
 
-def torch_forward(X, out, W, bias, active, convs, B, S, iters=20, eps=1e-6):
-    """A separately written float64 forward in torch, for autograd."""
+def torch_mgs(U, gs_eps):
+    """Modified Gram-Schmidt over dim 1 of [T, m, C], written apart from the oracle."""
+    C = U.shape[2]
+    done = [U[:, 0]]
+    for c in range(1, U.shape[1]):
+        v = U[:, c]
+        for q in done:
+            v = v - ((v * q).sum(dim=1) / ((q * q).sum(dim=1) + C * gs_eps))[:, None] * q
+        done.append(v)
+    return torch.stack(done, dim=1)
+
+
+def torch_forward(X, out, W, bias, active, convs, B, S, iters=20, eps=1e-6, gs_eps=None):
+    """A separately written float64 forward in torch, for autograd (gs_eps:
+    None, or the epsilon of Gram-Schmidt over the components)."""
     T, N, C = X.shape
     k = len(active)
     nc = 1 + len(convs)
@@ -79,6 +92,8 @@ def torch_forward(X, out, W, bias, active, convs, B, S, iters=20, eps=1e-6):
         y = torch.nn.functional.conv1d(torch.nn.functional.pad(seq, (K - 1, 0)), w[:, None, :], groups=C)
         comps.append(y.permute(0, 2, 1).reshape(T, C))
     U = torch.stack(comps, dim=1)
+    if gs_eps is not None:
+        U = torch_mgs(U, gs_eps)
     rows = []
     idx = list(active)
     for i in range(N):
