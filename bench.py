@@ -47,32 +47,41 @@ def parse():
 def kernel_bytes(w, esz, save_rows=True):
     """Algorithmic HBM bytes per launch of each main kernel: every input and
     output it must touch, once (per token, in units of C elements):
-      proj    reads the state                                  16C
-      mix     reads state 16C + out C; writes h_in C, 4 rows 4C,
-              saved old rows 4C                                26C
-      bxdots  reads state 16C (12 rows + 4 saved) + dh_in C + G 4C  21C
-      bdots   reads G 4C + out C; writes dout C                 6C
-      bgrad   reads state 16C + dX_new 16C + dh_in C; writes dX 16C  49C
-      mixproj reads state 16C + out C; writes h_in C, 4 rows 4C  22C
-              (the write pass that also projects the state it writes
-              for the next sublayer)
+      proj     reads the state                                  16C
+      mix      reads state 16C + out C; writes h_in C, 4 rows 4C,
+               saved old rows 4C                                26C
+      bxdots   reads state 16C (12 rows + 4 saved) + dh_in C + G 4C  21C
+      bdots    reads G 4C + out C; writes dout C                 6C
+               (with Gram-Schmidt: the dots pass, reads G 4C + out C  5C)
+      bgrad    reads state 16C + dX_new 16C + dh_in C; writes dX 16C  49C
+      mixproj  reads state 16C + out C; writes h_in C, 4 rows 4C  22C
+               (the write pass that also projects the state it writes
+               for the next sublayer)
+      gram     (Gram-Schmidt) reads out C
+      bdots_gs (Gram-Schmidt) reads G 4C + out C; writes dout C  6C
     plus the projection weights (N*C x P) where a kernel reads them."""
     T, C, N, k, P = w.T, w.C, w.N, w.k, w.P
     unit = T * C * esz
     wbytes = N * C * P * esz
-    return {
+    gs = getattr(w, "gs", False)
+    kb = {
         "proj": N * unit + wbytes,
         "mix": (N + 1 + 1 + k + (k if save_rows else 0)) * unit,
         "bxdots": (N + 1 + k) * unit,
-        "bdots": (k + 1 + 1) * unit,
+        "bdots": (k + 1 + (0 if gs else 1)) * unit,
         "bgrad": (N + N + 1 + N) * unit + wbytes,
         "mixproj": (N + 1 + 1 + k) * unit + wbytes,
     }
+    if gs:
+        kb["gram"] = unit
+        kb["bdots_gs"] = (k + 1 + 1) * unit
+    return kb
 
 
 # the source file that holds each kernel (the shared headers count for all)
 KERNEL_SOURCE = {"proj": "xhc_fwd.hip", "mix": "xhc_fwd.hip", "bxdots": "xhc_bwd.hip", "bdots": "xhc_bwd.hip",
-                 "bgrad": "xhc_bwd.hip", "mixproj": "xhc_chain.hip"}
+                 "bgrad": "xhc_bwd.hip", "mixproj": "xhc_chain.hip", "gram": "xhc_bwd.hip",
+                 "bdots_gs": "xhc_bwd.hip"}
 
 
 def source_digest(kernel=None):
@@ -143,9 +152,10 @@ def cpu_baseline(w, ntok):
         del d
         convs = (h["w4"], h["w8"], h["w12"])
         t = time.perf_counter()
-        xo.forward(h["X"], h["out"], h["W"], h["bias"], active, convs, B=1, S=S, iters=w.iters, eps=w.eps)
+        xo.forward(h["X"], h["out"], h["W"], h["bias"], active, convs, B=1, S=S, iters=w.iters, eps=w.eps,
+                   gram_schmidt_on=w.gs)
         xo.backward(h["X"], h["out"], h["W"], h["bias"], active, convs, h["dX_new"], h["dh_in"], B=1, S=S,
-                    iters=w.iters, eps=w.eps)
+                    iters=w.iters, eps=w.eps, gram_schmidt_on=w.gs)
         dt += time.perf_counter() - t
         del h
         left -= S
@@ -153,7 +163,8 @@ def cpu_baseline(w, ntok):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": round(ntok / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"numpy fp64 oracle forward+backward over {ntok} tokens ({seq} sequence(s) of at most "
-                      f"{w.S}) of the same workload (C={w.C}, N={w.N}, k={w.k}, TFA on): {dt:.1f} s of compute; "
+                      f"{w.S}) of the same workload (C={w.C}, N={w.N}, k={w.k}, TFA on"
+                      f"{', Gram-Schmidt on' if w.gs else ''}): {dt:.1f} s of compute; "
                       f"BLAS threads={threads}, host cpus={os.cpu_count()}"}
 
 
@@ -193,7 +204,8 @@ def forward_bench(args, w, np, torch, synth, xhc):
         layers.append((p, synth.active_streams(l, N, k)))
     del d
     h_in = torch.empty(T, C, dtype=sdt, device="cuda")
-    desc = xhc.make_desc(w.B, w.S, C, N, k, w.ncomp, xhc.XHC_BF16 if esz == 2 else xhc.XHC_F32, w.iters, w.eps)
+    desc = xhc.make_desc(w.B, w.S, C, N, k, w.ncomp, xhc.XHC_BF16 if esz == 2 else xhc.XHC_F32, w.iters, w.eps,
+                         gram_schmidt=w.gs)
     ws_f = torch.empty(xhc.workspace_size(desc, 0), dtype=torch.uint8, device="cuda")
     carries = [torch.empty(xhc.carry_size(desc) // 4, device="cuda") for _ in range(2)] if chain else None
 
@@ -298,7 +310,7 @@ def main():
     dws = dict(dw4=torch.empty(C, 4, device="cuda"), dw8=torch.empty(C, 8, device="cuda"),
                dw12=torch.empty(C, 12, device="cuda"))
     desc = xhc.make_desc(w.B, w.S, C, N, k, w.ncomp, xhc.XHC_BF16 if w.dtype == "bf16" else xhc.XHC_F32,
-                         w.iters, w.eps)
+                         w.iters, w.eps, gram_schmidt=w.gs)
     ws_f = torch.empty(xhc.workspace_size(desc, 0), dtype=torch.uint8, device="cuda")
     ws_b = torch.empty(xhc.workspace_size(desc, 1), dtype=torch.uint8, device="cuda")
     active = synth.active_streams(0, N, k)
@@ -347,6 +359,8 @@ def main():
     # whole-step accounting in units of C per token (bf16)
     alg_step_c = (N + 1 + 1 + k) + (N + N + 1 + 1 + N + 1)        # 22C forward + 51C backward
     impl_step_c = 16 + 26 + 21 + 6 + 49                             # what the kernels above touch
+    if w.gs:
+        impl_step_c += 1 + 5                                        # gram pass, the dots pass of B1
     step_bytes = alg_step_c * T * C * esz
     result = {
         "metric": METRIC,
@@ -362,7 +376,8 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": f"xHC sublayer fwd+bwd ({w.name}): B={w.B} S={w.S} C={C} N={N} k={k} "
-                               f"TFA K=4/8/12, 20 Sinkhorn iters, in-place forward + backward",
+                               f"TFA K=4/8/12{', Gram-Schmidt' if w.gs else ''}, 20 Sinkhorn iters, "
+                               f"in-place forward + backward",
                    "global_batch": w.B, "seq_len": w.S},
         "step_hbm": {"alg_bytes_per_token_in_C": alg_step_c, "touched_bytes_per_token_in_C": impl_step_c,
                      "alg_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),

@@ -77,7 +77,18 @@ enum {
 /* Problem description.  Supported: B, S >= 1; 1 <= k <= 4; k <= N <= 16;
  * ncomp in {1, 4} (4 = TFA on: out plus three causal convolutions; 1 = out
  * only, the mHC-style write-back); C >= 8 with C % 8 == 0;
- * 1 <= sinkhorn_iters <= 64; rms_eps >= 0; B*S*N*C < 2^31. */
+ * 1 <= sinkhorn_iters <= 64; rms_eps >= 0; B*S*N*C < 2^31.
+ *
+ * Gram-Schmidt (gram_schmidt = 1; source: the retrospective's section
+ * "Conv 带来了新信息，也带来了新的麻烦", which removes from each conv
+ * component its projections on the components before it and keeps the
+ * output as it is): per token, over the C channels, U~_0 = U_0 and for
+ * c = 1, 2, 3, starting from v = U_c, for j = 0 .. c-1 in turn
+ *   v -= <v, U~_j> / (<U~_j, U~_j> + C * gs_eps) * U~_j,   U~_c = v;
+ * the write then uses U~ in place of U.  No normalisation.  gs_eps > 0 keeps
+ * a zero component (zero conv weights) at 0.  With ncomp == 1 it is the
+ * identity.  A description with gram_schmidt = 0 (a zero-filled tail) is the
+ * form without it, which the pages use when the backbone trains with Muon. */
 typedef struct {
   int32_t B, S, C, N, k, ncomp;
   int32_t sinkhorn_iters;   /* Sinkhorn row+column steps (20 by default)    */
@@ -85,6 +96,8 @@ typedef struct {
   int32_t dtype;            /* XHC_F32 or XHC_BF16                          */
   int32_t gate_mode;        /* XHC_GATE_SIGMOID, or XHC_GATE_UNIT (test mode:
                                H_pre = H_post = 1, no gate gradient)        */
+  int32_t gram_schmidt;     /* 0: off; 1: modified Gram-Schmidt over U      */
+  float gs_eps;             /* > 0 and finite when gram_schmidt = 1 (1e-6)  */
 } xhc_desc;
 
 /* Optional per-kernel timer (HIP events around every kernel a call

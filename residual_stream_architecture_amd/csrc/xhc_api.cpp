@@ -25,6 +25,8 @@ int make_plan(const xhc_desc* d, Plan* p) {
   if (!(d->rms_eps >= 0.f) || !std::isfinite(d->rms_eps)) return XHC_ERR_SHAPE;
   if (d->dtype != XHC_F32 && d->dtype != XHC_BF16) return XHC_ERR_UNSUPPORTED;
   if (d->gate_mode != XHC_GATE_SIGMOID && d->gate_mode != XHC_GATE_UNIT) return XHC_ERR_UNSUPPORTED;
+  if (d->gram_schmidt != 0 && d->gram_schmidt != 1) return XHC_ERR_UNSUPPORTED;
+  if (d->gram_schmidt && !(d->gs_eps > 0.f && std::isfinite(d->gs_eps))) return XHC_ERR_SHAPE;
   const int64_t T = (int64_t)d->B * d->S;
   if (T * d->N * (int64_t)d->C >= ((int64_t)1 << 31)) return XHC_ERR_SHAPE;
 
@@ -36,6 +38,8 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.iters = d->sinkhorn_iters; q.dtype = d->dtype; q.gate = d->gate_mode; q.eps = d->rms_eps;
   q.NC = (int64_t)q.N * q.C;
   q.esz = q.dtype == XHC_BF16 ? 2 : 4;
+  q.gs = d->gram_schmidt == 1 && q.nc == 4;
+  q.gs_ceps = q.gs ? (float)q.C * d->gs_eps : 0.f;
 
   // forward
   q.SK = q.N;
@@ -90,6 +94,7 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.off_wt = o;     o = align256(o + (size_t)q.N * cdiv(q.C, 32) * 32 * q.NT * 16 * q.esz);
   q.off_zpart = o;  o = align256(o + (size_t)q.SK * T * q.ZST * 4);
   q.off_coef = o;   o = align256(o + (size_t)T * COEF_STRIDE * 4);
+  q.off_gram = o;   o = align256(o + (q.gs ? (size_t)q.b1_cblocks * T * 16 * 4 : 0));
   q.fwd_bytes = o;
   // backward reuses the forward regions (projection recompute) and adds:
   q.off_zbuf = o;   o = align256(o + (size_t)T * (q.P + 1) * 4);
@@ -100,6 +105,7 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.off_dz = o;     o = align256(o + (size_t)T * 48 * 4);
   q.off_rec = o;    o = align256(o + (size_t)(q.Tpad / B2_TT) * REC_BYTES);
   q.off_dwpart2 = o; o = align256(o + (size_t)q.b2_ts * q.NC * 48 * 4);
+  q.off_gss = o;    o = align256(o + (q.gs ? (size_t)T * 16 * 4 : 0));
   q.bwd_bytes = o;
   return XHC_OK;
 }
@@ -255,7 +261,8 @@ struct xhc_timer {
 };
 
 static const char* const kKernelNames[xhc::KID_COUNT] = {
-    "pack_wt", "proj", "coef", "mix", "pack_wp", "bdots", "bcoef", "bgrad", "breduce", "bxdots", "mixproj"};
+    "pack_wt", "proj", "coef", "mix", "pack_wp", "bdots", "bcoef", "bgrad", "breduce", "bxdots", "mixproj", "gram",
+    "bdots_gs"};
 
 namespace xhc {
 void timer_mark(xhc_timer* tm, int kid, hipStream_t st, bool start) {

@@ -27,6 +27,7 @@
 //                    with the dz W^T term on MFMA, dW partials on MFMA
 //   k_reduce         deterministic reductions of the dW, db and dconv partials
 #include "xhc_device.h"
+#include "xhc_gs.h"
 #include "xhc_launch.h"
 
 namespace xhc {
@@ -176,17 +177,69 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
 // summed in LDS once per 12 tokens and written per channel block.  All
 // loads are unconditional (clamped addresses, masked values) and the next
 // token's loads are issued before the current token's arithmetic.
+//
+// MODE selects the pass (Gram-Schmidt over the components, xhc_gs.h, needs
+// the full-C inner products of the components before any gradient of them):
+//   BD_FULL    no Gram-Schmidt: all of the above in one pass
+//   BD_GSDOTS  <G_a, U_m> and the Gram record <U_m, U_n> only
+//   BD_GSGRAD  dout and conv-weight partials from
+//              dU_m = sum_a Ht[a][m] G_a + sum_n Sg[m][n] U_n,
+//              Ht = H_post T and Sg from the coefficient backward; U is then
+//              also formed for the lookahead tokens
+//   BD_GRAM    (forward) the Gram record only; G is not read
+// Dot records: dpart[cb][t][DOT_STRIDE] with <G_a, U_m> at 32 + 4a + m and
+// the Gram record at 0..10 (BD_GRAM: dpart[cb][t][16], Gram at 0..10).
 // ---------------------------------------------------------------------------
-template <typename E, int NCOMP, bool FAST>
+enum { BD_FULL = 0, BD_GSDOTS = 1, BD_GSGRAD = 2, BD_GRAM = 3 };
+
+// Sum of 16 per-lane values over the wave by halving exchanges (lanes are
+// paired by xor 32, 16, 15, 7, then quads are summed): afterwards lane l with
+// l % 4 == 0 holds the sum of value reduce16_slot(l).
+__device__ inline float wave_reduce16(float (&v)[16], int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = halve32(v[i], v[8 + i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = halve16(v[i], v[4 + i]);
+  const bool h3 = lane & 8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float send = h3 ? v[i] : v[2 + i];
+    const float keep = h3 ? v[2 + i] : v[i];
+    v[i] = keep + dpp_xor15(send);
+  }
+  const bool h2 = lane & 4;
+  {
+    const float send = h2 ? v[0] : v[1];
+    const float keep = h2 ? v[1] : v[0];
+    v[0] = keep + dpp_xor7(send);
+  }
+  v[0] += dpp_xor1(v[0]);
+  v[0] += dpp_xor2(v[0]);
+  return v[0];
+}
+__device__ inline int reduce16_slot(int lane) {
+  return ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+}
+
+template <typename E, int NCOMP, bool FAST, int MODE>
 __global__ __launch_bounds__(256) void k_bdots(
     StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin,
     const void* __restrict__ out, const float* __restrict__ w4, const float* __restrict__ w8,
-    const float* __restrict__ w12, const float* __restrict__ hpost, float* __restrict__ dpart,
-    void* __restrict__ dout, float* __restrict__ dwpart, int T, int S, int C, int N, int kk, Act4 act,
-    int lseg, int segs_per_seq) {
+    const float* __restrict__ w12, const float* __restrict__ hpost, const float* __restrict__ gsS,
+    float* __restrict__ dpart, void* __restrict__ dout, float* __restrict__ dwpart, int T, int S, int C, int N,
+    int kk, Act4 act, int lseg, int segs_per_seq) {
   using V2 = Vec<E, B1_CH>;
   constexpr int EB = E::bytes;
-  __shared__ float red[B1_WAVES][12][16];
+  constexpr bool GS = MODE != BD_FULL;
+  constexpr bool NEED_G = MODE != BD_GRAM;
+  constexpr bool NEED_H = MODE == BD_FULL || MODE == BD_GSGRAD;
+  constexpr bool DOTS = MODE == BD_FULL || MODE == BD_GSDOTS;       // <G_a, U_m>
+  constexpr bool GRAMR = MODE == BD_GSDOTS || MODE == BD_GRAM;      // <U_m, U_n>
+  constexpr bool GRAD = MODE == BD_FULL || MODE == BD_GSGRAD;       // dout, dw
+  constexpr int NRED = (DOTS ? 16 : 0) + (GRAMR ? 16 : 0);
+  constexpr int RSTRIDE = MODE == BD_GRAM ? 16 : DOT_STRIDE;
+  static_assert(!GS || NCOMP == 4, "Gram-Schmidt needs the four components");
+  __shared__ float red[B1_WAVES][12][NRED > 0 ? NRED : 1];
   const int k = FAST ? 4 : kk;
   (void)N;
   const int NS = FAST ? 16 : N;
@@ -198,7 +251,7 @@ __global__ __launch_bounds__(256) void k_bdots(
   const int bseq = seg / segs_per_seq;
   const int s0 = (seg - bseq * segs_per_seq) * lseg;
   const int s1 = min(s0 + lseg, S);
-  const int tend = s1 + 11;
+  const int tend = GRAD ? s1 + 11 : s1;
   const size_t tok0 = (size_t)bseq * S;
   const uint32_t rowb = (uint32_t)C * EB;
   const uint32_t tokb = (uint32_t)NS * rowb;
@@ -239,7 +292,9 @@ __global__ __launch_bounds__(256) void k_bdots(
       float f[B1_CH];
       v.to_float(f);
 #pragma unroll
-      for (int ch = 0; ch < B1_CH; ++ch) win[j][ch] = s >= 0 ? f[ch] : 0.f;   // ring slot of position s0-11+j
+      // ring slot of position s0-11+j; lanes past C hold zeros, as in the
+      // loop, so that their components vanish in the Gram record
+      for (int ch = 0; ch < B1_CH; ++ch) win[j][ch] = (s >= 0 && cv) ? f[ch] : 0.f;
     }
   }
 
@@ -249,20 +304,34 @@ __global__ __launch_bounds__(256) void k_bdots(
   V2 gq[PF + 1][4], oq[PF + 1];
   auto load_tok = [&](int s, int q) {
     const size_t t = tok0 + min(s, S - 1);
-    const rsrc_t rg = make_rsrc(static_cast<const char*>(dXn) + t * tokb, tokb);
+    if constexpr (NEED_G) {
+      const rsrc_t rg = make_rsrc(static_cast<const char*>(dXn) + t * tokb, tokb);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) gq[q][a] = bload<E, B1_CH>(rg, voff, (uint32_t)act.id[a < k ? a : 0] * rowb);
+      for (int a = 0; a < 4; ++a) gq[q][a] = bload<E, B1_CH>(rg, voff, (uint32_t)act.id[a < k ? a : 0] * rowb);
+    }
     oq[q] = bload<E, B1_CH>(rout, voff, (uint32_t)min(s, S - 1) * rowb);
   };
-  // post gates of one token (uniform: scalar loads), one token ahead
-  float Hn[4][4];
+  // post coefficients (and Sg) of one token (uniform: scalar loads), one token ahead
+  float Hn[4][4], Sn[4][4];
   auto load_h = [&](int s) {
-    const f32x4* hp = reinterpret_cast<const f32x4*>(hpost + (tok0 + min(s, S - 1)) * 16);
+    if constexpr (NEED_H) {
+      const size_t t = tok0 + min(s, S - 1);
+      const f32x4* hp = reinterpret_cast<const f32x4*>(hpost + t * 16);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const f32x4 v = hp[a];
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 v = hp[a];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) Hn[a][m] = v[m];
+        for (int m = 0; m < 4; ++m) Hn[a][m] = v[m];
+      }
+      if constexpr (MODE == BD_GSGRAD) {
+        const f32x4* sp = reinterpret_cast<const f32x4*>(gsS + t * 16);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 v = sp[m];
+#pragma unroll
+          for (int n = 0; n < 4; ++n) Sn[m][n] = v[n];
+        }
+      }
     }
   };
 #pragma unroll
@@ -286,28 +355,41 @@ __global__ __launch_bounds__(256) void k_bdots(
       const bool in_seg = s < tend;
       const bool live = s < S;
       load_tok(s + PF, (j + PF) % (PF + 1));
-      float H[4][4];
+      float H[4][4], Sg[4][4];
+      if constexpr (NEED_H) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) H[a][m] = Hn[a][m];
-      load_h(s + 1);
+          for (int m = 0; m < 4; ++m) {
+            H[a][m] = Hn[a][m];
+            if constexpr (MODE == BD_GSGRAD) Sg[a][m] = Sn[a][m];
+          }
+        load_h(s + 1);
+      }
 
       float G[4][B1_CH], of[B1_CH];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        gq[q][a].to_float(G[a]);
-        if (!(a < k && cv && live)) {
+        if constexpr (NEED_G) {
+          gq[q][a].to_float(G[a]);
+        }
+        if (!NEED_G || !(a < k && cv && live)) {
 #pragma unroll
           for (int ch = 0; ch < B1_CH; ++ch) G[a][ch] = 0.f;
         }
       }
       oq[q].to_float(of);
 
-      if (main_tok) {
+      // U of this token: main tokens, and in BD_GSGRAD the lookahead too
+      const bool need_u = MODE == BD_GSGRAD ? in_seg : main_tok;
+      float U[4][B1_CH];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int ch = 0; ch < B1_CH; ++ch) U[m][ch] = 0.f;
+      if (need_u) {
 #pragma unroll
         for (int ch = 0; ch < B1_CH; ++ch) win[(j + 11) % 12][ch] = cv ? of[ch] : 0.f;
-        float U[4][B1_CH];
 #pragma unroll
         for (int ch = 0; ch < B1_CH; ++ch) {
           U[0][ch] = win[(j + 11) % 12][ch];
@@ -322,130 +404,142 @@ __global__ __launch_bounds__(256) void k_bdots(
             U[1][ch] = s4; U[2][ch] = s8; U[3][ch] = s12;
           }
         }
-        // dH_post partials v[a*4+m], reduced over the wave by halving
-        float v[16];
+      }
+      if (main_tok) {
+        if constexpr (DOTS) {
+          // dH_post partials v[a*4+m]
+          float v[16];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+          for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
+            for (int m = 0; m < 4; ++m) {
+              float d = 0.f;
+              if (m < NCOMP) {
+#pragma unroll
+                for (int ch = 0; ch < B1_CH; ++ch) d = fmaf(G[a][ch], U[m][ch], d);
+              }
+              v[a * 4 + m] = d;
+            }
+          const float r = wave_reduce16(v, lane);
+          if ((lane & 3) == 0) red[wave][j][reduce16_slot(lane)] = r;
+        }
+        if constexpr (GRAMR) {
+          // Gram record partials (entries 10..15 are zero)
+          float v[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = 0.f;
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int n = m; n < 4; ++n) {
+              float d = 0.f;
+#pragma unroll
+              for (int ch = 0; ch < B1_CH; ++ch) d = fmaf(U[m][ch], U[n][ch], d);
+              v[gram_idx(m, n)] = d;
+            }
+          const float r = wave_reduce16(v, lane);
+          if ((lane & 3) == 0) red[wave][j][(DOTS ? 16 : 0) + reduce16_slot(lane)] = r;
+        }
+      }
+      if constexpr (GRAD) {
+        // dU_m for this token (zero for tokens past the sequence)
+        float dU[4][B1_CH];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int ch = 0; ch < B1_CH; ++ch) {
             float d = 0.f;
             if (m < NCOMP) {
 #pragma unroll
-              for (int ch = 0; ch < B1_CH; ++ch) d = fmaf(G[a][ch], U[m][ch], d);
+              for (int a = 0; a < 4; ++a)
+                if (a < k) d = fmaf(H[a][m], G[a][ch], d);
+              if constexpr (MODE == BD_GSGRAD) {
+                float e = 0.f;
+#pragma unroll
+                for (int n = 0; n < 4; ++n) e = fmaf(Sg[m][n], U[n][ch], e);
+                d += (live && cv) ? e : 0.f;
+              }
             }
-            v[a * 4 + m] = d;
+            dU[m][ch] = d;
           }
-        {
-          // halving exchange over the wave: after the steps on lane bits 5,
-          // 4, 3, 2 a lane holds one of the 16 sums, the one its bits select
-          // (lanes are paired by xor 32, 16, 15, 7, then quads are summed)
+        if (main_tok && NCOMP == 4) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = halve32(v[i], v[8 + i]);
+          for (int ch = 0; ch < B1_CH; ++ch) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = halve16(v[i], v[4 + i]);
-          const bool h3 = lane & 8;
+            for (int qq = 0; qq < 4; ++qq) dw[ch][qq] = fmaf(dU[1][ch], win[(j + 8 + qq) % 12][ch], dw[ch][qq]);
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const float send = h3 ? v[i] : v[2 + i];
-            const float keep = h3 ? v[2 + i] : v[i];
-            v[i] = keep + dpp_xor15(send);
-          }
-          const bool h2 = lane & 4;
-          {
-            const float send = h2 ? v[0] : v[1];
-            const float keep = h2 ? v[1] : v[0];
-            v[0] = keep + dpp_xor7(send);
-          }
-          v[0] += dpp_xor1(v[0]);
-          v[0] += dpp_xor2(v[0]);
-          if ((lane & 3) == 0) {
-            const int idx = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
-            red[wave][j][idx] = v[0];
+            for (int qq = 0; qq < 8; ++qq)
+              dw[ch][4 + qq] = fmaf(dU[2][ch], win[(j + 4 + qq) % 12][ch], dw[ch][4 + qq]);
+#pragma unroll
+            for (int qq = 0; qq < 12; ++qq)
+              dw[ch][12 + qq] = fmaf(dU[3][ch], win[(j + qq) % 12][ch], dw[ch][12 + qq]);
           }
         }
-      }
-      // dU_m for this token (zero for tokens past the sequence)
-      float dU[4][B1_CH];
+        if (in_seg) {
+          // scatter into the dout accumulators of positions s - lag (positions
+          // before s0 receive terms too; they are never emitted)
+          if (main_tok) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int ch = 0; ch < B1_CH; ++ch) {
-          float d = 0.f;
-          if (m < NCOMP) {
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-              if (a < k) d = fmaf(H[a][m], G[a][ch], d);
+            for (int ch = 0; ch < B1_CH; ++ch) dacc[j % 12][ch] += dU[0][ch];
           }
-          dU[m][ch] = d;
-        }
-      if (main_tok && NCOMP == 4) {
+          if constexpr (NCOMP == 4) {
 #pragma unroll
-        for (int ch = 0; ch < B1_CH; ++ch) {
+            for (int lag = 0; lag < 12; ++lag) {
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) dw[ch][qq] = fmaf(dU[1][ch], win[(j + 8 + qq) % 12][ch], dw[ch][qq]);
-#pragma unroll
-          for (int qq = 0; qq < 8; ++qq)
-            dw[ch][4 + qq] = fmaf(dU[2][ch], win[(j + 4 + qq) % 12][ch], dw[ch][4 + qq]);
-#pragma unroll
-          for (int qq = 0; qq < 12; ++qq)
-            dw[ch][12 + qq] = fmaf(dU[3][ch], win[(j + qq) % 12][ch], dw[ch][12 + qq]);
-        }
-      }
-      if (in_seg) {
-        // scatter into the dout accumulators of positions s - lag (positions
-        // before s0 receive terms too; they are never emitted)
-        if (main_tok) {
-#pragma unroll
-          for (int ch = 0; ch < B1_CH; ++ch) dacc[j % 12][ch] += dU[0][ch];
-        }
-        if constexpr (NCOMP == 4) {
-#pragma unroll
-          for (int lag = 0; lag < 12; ++lag) {
-#pragma unroll
-            for (int ch = 0; ch < B1_CH; ++ch) {
-              float d = dacc[(j + 12 - lag) % 12][ch];
-              if (lag < 4) d = fmaf(wk[ch][3 - lag], dU[1][ch], d);
-              if (lag < 8) d = fmaf(wk[ch][4 + 7 - lag], dU[2][ch], d);
-              d = fmaf(wk[ch][12 + 11 - lag], dU[3][ch], d);
-              dacc[(j + 12 - lag) % 12][ch] = d;
+              for (int ch = 0; ch < B1_CH; ++ch) {
+                float d = dacc[(j + 12 - lag) % 12][ch];
+                if (lag < 4) d = fmaf(wk[ch][3 - lag], dU[1][ch], d);
+                if (lag < 8) d = fmaf(wk[ch][4 + 7 - lag], dU[2][ch], d);
+                d = fmaf(wk[ch][12 + 11 - lag], dU[3][ch], d);
+                dacc[(j + 12 - lag) % 12][ch] = d;
+              }
             }
           }
         }
-      }
-      // position s - 11 is complete: hold it for the group's store, clear its slot
-      pend[j] = V2::from_float(dacc[(j + 1) % 12]);
+        // position s - 11 is complete: hold it for the group's store, clear its slot
+        pend[j] = V2::from_float(dacc[(j + 1) % 12]);
 #pragma unroll
-      for (int ch = 0; ch < B1_CH; ++ch) dacc[(j + 1) % 12][ch] = 0.f;
+        for (int ch = 0; ch < B1_CH; ++ch) dacc[(j + 1) % 12][ch] = 0.f;
+      }
     });
     // group end: completed positions sg - 11 .. sg (those in [s0, s1)) and
-    // the 8 waves' dH_post sums of the group's main tokens
-    if (cv) {
+    // the waves' dot sums of the group's main tokens
+    if constexpr (GRAD) {
+      if (cv) {
 #pragma unroll
-      for (int j = 0; j < 12; ++j) {
-        const int pos = sg + j - 11;
-        if (pos >= s0 && pos < s1) pend[j].store(dout, (tok0 + pos) * C + cl);
+        for (int j = 0; j < 12; ++j) {
+          const int pos = sg + j - 11;
+          if (pos >= s0 && pos < s1) pend[j].store(dout, (tok0 + pos) * C + cl);
+        }
       }
     }
-    if (sg < s1) {
-      __syncthreads();
-      const int nmain = min(12, s1 - sg);
-      for (int idx = threadIdx.x; idx < nmain * 16; idx += 64 * B1_WAVES) {
-        const int jj = idx >> 4, q = idx & 15;
-        float sum = 0.f;
+    if constexpr (NRED > 0) {
+      if (sg < s1) {
+        __syncthreads();
+        const int nmain = min(12, s1 - sg);
+        for (int idx = threadIdx.x; idx < nmain * NRED; idx += 64 * B1_WAVES) {
+          const int jj = idx / NRED, q = idx - jj * NRED;
+          float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < B1_WAVES; ++w) sum += red[w][jj][q];
-        dpart[((size_t)cblock * T + tok0 + sg + jj) * DOT_STRIDE + 32 + q] = sum;
+          for (int w = 0; w < B1_WAVES; ++w) sum += red[w][jj][q];
+          // q < 16 with DOTS: <G_a, U_m>; otherwise the Gram record
+          const int col = (DOTS && q < 16) ? 32 + q : q - (DOTS ? 16 : 0);
+          if (!(GRAMR && col < 16 && col >= 10))
+            dpart[((size_t)cblock * T + tok0 + sg + jj) * RSTRIDE + col] = sum;
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
-  if (NCOMP == 4 && cv) {
+  if constexpr (GRAD) {
+    if (NCOMP == 4 && cv) {
 #pragma unroll
-    for (int ch = 0; ch < B1_CH; ++ch) {
-      float* dst = dwpart + ((size_t)seg * C + cl + ch) * 24;
+      for (int ch = 0; ch < B1_CH; ++ch) {
+        float* dst = dwpart + ((size_t)seg * C + cl + ch) * 24;
 #pragma unroll
-      for (int q = 0; q < 24; q += 4)
-        *reinterpret_cast<f32x4*>(dst + q) = f32x4{dw[ch][q], dw[ch][q + 1], dw[ch][q + 2], dw[ch][q + 3]};
+        for (int q = 0; q < 24; q += 4)
+          *reinterpret_cast<f32x4*>(dst + q) = f32x4{dw[ch][q], dw[ch][q + 1], dw[ch][q + 2], dw[ch][q + 3]};
+      }
     }
   }
 }
@@ -457,16 +551,24 @@ __global__ __launch_bounds__(256) void k_bdots(
 //   column step Mc = R / colsum(R):  dR = (dMc - colsum(dMc*Mc)) / colsum(R)
 //   row step    R  = M / rowsum(M):  dM = (dR - rowsum(dR*R))  / rowsum(M)
 //   dL = dM_0 * M_0 (the row-max shift cancels in the first row step).
+// With Gram-Schmidt (GS, xhc_gs.h) the B1 dots are D[a][m] = <G_a, U_m> over
+// the raw components, and with u~ = T U:
+//   dH_post[a][c] = sum_m T[c][m] D[a][m]
+//   dT[c][m]      = sum_a H_post[a][c] D[a][m]   -> Sg = dg + dg^T
+// and the kernel writes, for the second B1 pass, Ht = H_post T over hpost
+// and Sg to gss ([T][16] each), so that dU_m = sum_a Ht[a][m] G_a +
+// sum_n Sg[m][n] U_n.
 // ---------------------------------------------------------------------------
 constexpr int BCOEF_TOK = 4;
 
-template <typename E>
+template <typename E, bool GS>
 __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int ncba, const float* __restrict__ dpart,
                                               int ncb, const float* __restrict__ zin,
                                               const float* __restrict__ bias,
                                               float* __restrict__ dz_out, void* __restrict__ rec,
                                               int T, int64_t Tpad, int N, int k, int nc,
-                                              int P, float inv_nc_total, int iters, int unit_gates) {
+                                              int P, float inv_nc_total, int iters, int unit_gates,
+                                              float gs_ceps, float* __restrict__ hpost, float* __restrict__ gss) {
   extern __shared__ float hist[];   // [BCOEF_TOK][iters+1][16]
   __shared__ float dzs[BCOEF_TOK][64];
   const int e = threadIdx.x & 15, tok = threadIdx.x >> 4;
@@ -491,6 +593,57 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
   const bool post_ok = (e >> 2) < k && (e & 3) < nc;
   const float hp = pre_ok ? (unit_gates ? 1.f : sigmoid(z[e])) : 0.f;
   const float hq = post_ok ? (unit_gates ? 1.f : sigmoid(z[N + (e >> 2) * nc + (e & 3)])) : 0.f;
+  if constexpr (GS) {
+    // the token's 16 lanes share one wave: gather its records
+    float gsum = 0.f;
+    if (e < 10)
+      for (int cb = 0; cb < ncb; ++cb) gsum += dpart[((size_t)cb * T + tc) * DOT_STRIDE + e];
+    const int base = (threadIdx.x & 63) & ~15;
+    float g[4][4], D[4][4], Hp[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        if (n >= m) {
+          g[m][n] = __shfl(gsum, base + gram_idx(m, n), 64);
+          g[n][m] = g[m][n];
+        }
+        D[m][n] = __shfl(dpost, base + m * 4 + n, 64);
+        Hp[m][n] = __shfl(hq, base + m * 4 + n, 64);
+      }
+    GsFwd f;
+    gs_forward(g, gs_ceps, f);
+    float dT[4][4], Sg[4][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float v = 0.f;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) v = fmaf(Hp[a][c], D[a][m], v);
+        dT[c][m] = v;
+      }
+    gs_backward(g, f, dT, Sg);
+    const int a = e >> 2, q = e & 3;
+    float dh = 0.f, ht = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dh = fmaf(f.T[q][m], D[a][m], dh);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ht = fmaf(Hp[a][c], f.T[c][q], ht);
+    float sv = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        if (m == a && n == q) sv = Sg[m][n];
+    dpost = dh;
+    if (tv) {
+      hpost[t * 16 + e] = ht;
+      gss[t * 16 + e] = sv;
+    }
+  } else {
+    (void)gs_ceps; (void)hpost; (void)gss;
+  }
   float dz_pre = 0.f, dz_post = 0.f;
   if (!unit_gates) {
     dz_pre = pre_ok ? dpre * hp * (1.f - hp) : 0.f;
@@ -1022,28 +1175,41 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
         src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, zin, hpost, p.P, p.nc,
         p.gate == XHC_GATE_UNIT, static_cast<const R*>(a->W), static_cast<R*>(Wp), p.NC);
   }
+  float* gss = reinterpret_cast<float*>(ws + p.off_gss);        // [T][16] Sg (Gram-Schmidt)
+  const dim3 b1grid(p.b1_cblocks, p.B * p.b1_segs);
+  const bool fast = p.N == 16 && p.k == 4;
+#define XHC_BDOTS(NCOMP, FAST, MODE)                                                                              \
+  k_bdots<E, NCOMP, FAST, MODE><<<b1grid, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12,    \
+                                                        hpost, gss, dpart, a->dout, dwpart, p.T, p.S, p.C, p.N, p.k, \
+                                                        act, p.b1_lseg, p.b1_segs)
   {
     TimedLaunch tl(tm, KID_BDOTS, st);
-    dim3 grid(p.b1_cblocks, p.B * p.b1_segs);
-    const bool fast = p.N == 16 && p.k == 4;
-#define XHC_BDOTS(NCOMP, FAST)                                                                                   \
-  k_bdots<E, NCOMP, FAST><<<grid, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12, hpost,    \
-                                               dpart, a->dout, dwpart, p.T, p.S, p.C, p.N, p.k, act, p.b1_lseg, \
-                                               p.b1_segs)
-    if (p.nc == 4) {
-      if (fast) XHC_BDOTS(4, true); else XHC_BDOTS(4, false);
+    if (p.gs) {
+      if (fast) XHC_BDOTS(4, true, BD_GSDOTS); else XHC_BDOTS(4, false, BD_GSDOTS);
+    } else if (p.nc == 4) {
+      if (fast) XHC_BDOTS(4, true, BD_FULL); else XHC_BDOTS(4, false, BD_FULL);
     } else {
-      if (fast) XHC_BDOTS(1, true); else XHC_BDOTS(1, false);
+      if (fast) XHC_BDOTS(1, true, BD_FULL); else XHC_BDOTS(1, false, BD_FULL);
     }
-#undef XHC_BDOTS
   }
   {
     TimedLaunch tl(tm, KID_BCOEF, st);
     const int nb = (int)((p.Tpad + BCOEF_TOK - 1) / BCOEF_TOK);
     const size_t shm = (size_t)BCOEF_TOK * (p.iters + 1) * 16 * sizeof(float);
-    k_bcoef<E><<<nb, 64, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T, p.Tpad, p.N,
-                                    p.k, p.nc, p.P, 1.0f / (float)p.NC, p.iters, p.gate == XHC_GATE_UNIT);
+    if (p.gs)
+      k_bcoef<E, true><<<nb, 64, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T,
+                                            p.Tpad, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.iters,
+                                            p.gate == XHC_GATE_UNIT, p.gs_ceps, hpost, gss);
+    else
+      k_bcoef<E, false><<<nb, 64, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T,
+                                             p.Tpad, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.iters,
+                                             p.gate == XHC_GATE_UNIT, 0.f, nullptr, nullptr);
   }
+  if (p.gs) {
+    TimedLaunch tl(tm, KID_BDOTS_GS, st);
+    if (fast) XHC_BDOTS(4, true, BD_GSGRAD); else XHC_BDOTS(4, false, BD_GSGRAD);
+  }
+#undef XHC_BDOTS
   {
     TimedLaunch tl(tm, KID_BGRAD, st);
     RowTable rows;
@@ -1072,6 +1238,21 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
                                                      a->dw8, a->dw12, nb_dw, a->accumulate);
   }
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
+}
+
+void launch_gram(const Plan& p, const void* out, const float* w4, const float* w8, const float* w12, float* gram,
+                 hipStream_t st) {
+  const dim3 grid(p.b1_cblocks, p.B * p.b1_segs);
+  StreamRows none{};
+  Act4 act{};
+  if (p.dtype == XHC_BF16)
+    k_bdots<BF16, 4, false, BD_GRAM><<<grid, 256, 0, st>>>(none, nullptr, nullptr, out, w4, w8, w12, nullptr, nullptr,
+                                                           gram, nullptr, nullptr, p.T, p.S, p.C, p.N, p.k, act,
+                                                           p.b1_lseg, p.b1_segs);
+  else
+    k_bdots<F32, 4, false, BD_GRAM><<<grid, 256, 0, st>>>(none, nullptr, nullptr, out, w4, w8, w12, nullptr, nullptr,
+                                                          gram, nullptr, nullptr, p.T, p.S, p.C, p.N, p.k, act,
+                                                          p.b1_lseg, p.b1_segs);
 }
 
 int launch_backward(const Plan& p, const xhc_bwd_args* a, void* ws, hipStream_t st) {

@@ -13,6 +13,7 @@
 //   k_mix      per (sequence segment, channel block): dense read h_in, TFA
 //              over a 12-row causal window, sparse write of the k rows
 #include "xhc_device.h"
+#include "xhc_gs.h"
 #include "xhc_launch.h"
 
 namespace xhc {
@@ -207,13 +208,18 @@ __global__ __launch_bounds__(64 * PROJ_WAVES) void k_proj(StreamRows src, const 
 // and entry (a, b) = (e/4, e%4) of the k x k Sinkhorn matrix, whose row sums
 // are quad reductions (xor 1, 2) and column sums xor 4, 8 reductions.
 // Either reduces projection partials (zpart != NULL) or reloads z and r from
-// z_in (a forward's z_save).
+// z_in (a forward's z_save).  With gram != NULL (Gram-Schmidt on, four
+// components) the token's Gram record is summed over its ngram channel-block
+// partials, and the post coefficients become H_post T (u~ = T U, see
+// xhc_gs.h), so the write pass combines the raw components.
 // ---------------------------------------------------------------------------
+template <bool GS>
 __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, int SK, int ZST, int NTP,
                                               const float* __restrict__ z_in, const float* __restrict__ bias,
                                               float* __restrict__ coef, float* __restrict__ z_out, int T,
                                               int N, int k, int nc, int P, float inv_nc_total, float eps,
-                                              int iters, int unit_gates) {
+                                              int iters, int unit_gates, const float* __restrict__ gram,
+                                              int ngram, float gs_ceps) {
   __shared__ float zs[16][COEF_STRIDE];
   const int e = threadIdx.x & 15, tok = threadIdx.x >> 4;
   const int t = blockIdx.x * 16 + tok;
@@ -250,9 +256,37 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
 
   // gates
   co[CO_PRE + e] = e < N ? (unit_gates ? 1.f : sigmoid(zs[tok][e])) : 0.f;
-  {
+  if constexpr (!GS) {
+    (void)gram; (void)ngram; (void)gs_ceps;
     const int a = e >> 2, m = e & 3;
     co[CO_POST + e] = (a < k && m < nc) ? (unit_gates ? 1.f : sigmoid(zs[tok][N + a * nc + m])) : 0.f;
+  } else {
+    // Gram-Schmidt folded into the post coefficients (nc == 4)
+    float gsum = 0.f;
+    if (e < 10)
+      for (int b = 0; b < ngram; ++b) gsum += gram[((size_t)b * T + t) * 16 + e];
+    // the token's 16 lanes share one wave: every lane gathers the record
+    const int base = (threadIdx.x & 63) & ~15;
+    float g[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = m; n < 4; ++n) {
+        g[m][n] = __shfl(gsum, base + gram_idx(m, n), 64);
+        g[n][m] = g[m][n];
+      }
+    GsFwd f;
+    gs_forward(g, gs_ceps, f);
+    const int a = e >> 2, m = e & 3;
+    float h = 0.f;
+    if (a < k) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float hp = unit_gates ? 1.f : sigmoid(zs[tok][N + a * 4 + c]);
+        h = fmaf(hp, f.T[c][m], h);
+      }
+    }
+    co[CO_POST + e] = h;
   }
   // Sinkhorn on the k x k res logits
   {
@@ -501,11 +535,24 @@ static int forward_impl(const Plan& p, const xhc_fwd_args* a, const xhc_chain_ar
     launch_pack_wt<R>(p, a->W, Wt, st, tm);
     launch_proj<E>(p, stream_rows(p, a->X, nullptr, a->active), Wt, zpart, st, tm);
   }
+  float* gram = reinterpret_cast<float*>(ws + p.off_gram);
+  if (p.gs) {
+    TimedLaunch tl(tm, KID_GRAM, st);
+    launch_gram(p, a->out, a->w4, a->w8, a->w12, gram, st);
+  }
   {
     TimedLaunch tl(tm, KID_COEF, st);
-    k_coef<<<(p.T + 15) / 16, 256, 0, st>>>(carry_in ? carry_in : zpart, carry_in ? p.mp_ncb : p.SK, p.ZST, NTP,
-                                            nullptr, a->bias, coef, a->z_save, p.T, p.N, p.k, p.nc, p.P,
-                                            1.0f / (float)p.NC, p.eps, p.iters, p.gate == XHC_GATE_UNIT);
+    const float* zp = carry_in ? carry_in : zpart;
+    const int sk = carry_in ? p.mp_ncb : p.SK;
+    const int unit = p.gate == XHC_GATE_UNIT;
+    if (p.gs)
+      k_coef<true><<<(p.T + 15) / 16, 256, 0, st>>>(zp, sk, p.ZST, NTP, nullptr, a->bias, coef, a->z_save, p.T, p.N,
+                                                    p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps, p.iters, unit, gram,
+                                                    p.b1_cblocks, p.gs_ceps);
+    else
+      k_coef<false><<<(p.T + 15) / 16, 256, 0, st>>>(zp, sk, p.ZST, NTP, nullptr, a->bias, coef, a->z_save, p.T,
+                                                     p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps, p.iters, unit,
+                                                     nullptr, 0, 0.f);
   }
   if (carry_out) {
     // the next sublayer's weights in the MFMA fragment order, then the fused
@@ -566,9 +613,10 @@ int launch_coef_bwd(const Plan& p, const void* X, const void* xact, const int32_
     }
   }
   TimedLaunch tl(tm, KID_COEF, st);
-  k_coef<<<(p.T + 15) / 16, 256, 0, st>>>(zpart, p.SK, p.ZST, p.NT * 16, z_save, bias, coef, z_out, p.T,
-                                          p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps, p.iters,
-                                          p.gate == XHC_GATE_UNIT);
+  // the backward needs z (and r) only: its post coefficients come from z
+  k_coef<false><<<(p.T + 15) / 16, 256, 0, st>>>(zpart, p.SK, p.ZST, p.NT * 16, z_save, bias, coef, z_out, p.T,
+                                                 p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps, p.iters,
+                                                 p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f);
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
 }
 

@@ -12,7 +12,7 @@ namespace xhc {
 enum KernelId {
   KID_PACK_WT = 0, KID_PROJ, KID_COEF, KID_MIX,
   KID_PACK_WP, KID_BDOTS, KID_BCOEF, KID_BGRAD, KID_BREDUCE, KID_BXDOTS,
-  KID_MIXPROJ,
+  KID_MIXPROJ, KID_GRAM, KID_BDOTS_GS,
   KID_COUNT
 };
 // Alias kept for the backward's coefficient recompute from z_save.
@@ -70,5 +70,9 @@ int launch_coef_bwd(const Plan& p, const void* X, const void* xact, const int32_
                     const float* bias, const float* z_save, void* ws, float* coef, float* z_out,
                     hipStream_t st, xhc_timer* tm);
 int launch_backward(const Plan& p, const xhc_bwd_args* a, void* ws, hipStream_t st);
+// Gram-Schmidt's Gram records of the components (forward): gram[cb][t][16]
+// partials over channel blocks of B1_WAVES * B1_WAVE_CH.
+void launch_gram(const Plan& p, const void* out, const float* w4, const float* w8, const float* w12, float* gram,
+                 hipStream_t st);
 
 }  // namespace xhc

@@ -20,7 +20,10 @@ constexpr int CO_PRE = 0, CO_POST = 16, CO_RES = 32, CO_R = 48;
 // Per-token backward dot records (floats):
 //   B1x, per channel block of BX_CB:   [0, 16)  dH_pre[i]      = <dh_in, X_i>
 //                                      [16, 32) dH_res[a*4+b]  = <G_a, X_{i_b}>
-//   B1, per channel block of B1:       [32, 48) dH_post[a*4+m] = <G_a, U_m>
+//   B1, per channel block of B1:       [32, 48) <G_a, U_m> (dH_post[a*4+m]
+//                                      without Gram-Schmidt)
+//                                      [0, 10)  Gram record <U_m, U_n>, m <= n
+//                                      (with Gram-Schmidt)
 constexpr int DOT_STRIDE = 48;
 constexpr int BX_OUT = 32;
 
@@ -67,6 +70,8 @@ constexpr int rec_dzrt_half(int esz) { return 3 * 4 * 16 * 4 * esz; }
 struct Plan {
   int B, S, C, N, k, nc, P, NT, T, iters, dtype, gate;
   float eps;
+  bool gs;            // Gram-Schmidt over the four components (nc == 4)
+  float gs_ceps;      // C * gs_eps
   int64_t NC;
   int esz;            // bytes per storage element
   // forward
@@ -94,8 +99,8 @@ struct Plan {
   int mp_nbatch;      // token batches of 128
   size_t carry_bytes; // [mp_ncb][T][ZST] floats
   // workspace layout (byte offsets; every region 256-byte aligned)
-  size_t off_wt, off_zpart, off_coef, fwd_bytes;
-  size_t off_zbuf, off_wp, off_dpart, off_dpa, off_dwpart, off_dz, off_rec, off_dwpart2, bwd_bytes;
+  size_t off_wt, off_zpart, off_coef, off_gram, fwd_bytes;
+  size_t off_zbuf, off_wp, off_dpart, off_dpa, off_dwpart, off_dz, off_rec, off_dwpart2, off_gss, bwd_bytes;
 };
 
 // Fills `p` from `d`; returns XHC_OK or an XHC_ERR_* code for an

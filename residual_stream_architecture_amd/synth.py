@@ -33,6 +33,7 @@ class Workload:
     layers: int = 1
     iters: int = 20
     eps: float = 1e-6
+    gs: bool = False      # Gram-Schmidt over the write-back components
 
     @property
     def T(self):
@@ -52,6 +53,8 @@ WORKLOADS = {
     "mhc4": Workload("mhc4", 4, 4096, 4096, 4, 4, 1, "bf16", "fwd"),
     # bf16 sublayer forward + backward (the headline workload)
     "fwdbwd4096": Workload("fwdbwd4096", 2, 4096, 4096, 16, 4, 4, "bf16", "fwdbwd"),
+    # the same with Gram-Schmidt over the four write-back components
+    "fwdbwd4096_gs": Workload("fwdbwd4096_gs", 2, 4096, 4096, 16, 4, 4, "bf16", "fwdbwd", gs=True),
     # 48 stacked sublayer updates, state carried in HBM
     "stack48": Workload("stack48", 1, 8192, 7168, 16, 4, 4, "bf16", "stack", layers=48),
 }

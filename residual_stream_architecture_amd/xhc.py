@@ -25,7 +25,8 @@ class xhc_desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("C", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("k", ctypes.c_int32), ("ncomp", ctypes.c_int32),
                 ("sinkhorn_iters", ctypes.c_int32), ("rms_eps", ctypes.c_float),
-                ("dtype", ctypes.c_int32), ("gate_mode", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
+                ("gram_schmidt", ctypes.c_int32), ("gs_eps", ctypes.c_float)]
 
 
 class xhc_fwd_args(ctypes.Structure):
@@ -92,8 +93,9 @@ def _load():
 lib = _load()
 
 
-def make_desc(B, S, C, N, k, ncomp, dtype, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID):
-    return xhc_desc(B, S, C, N, k, ncomp, iters, eps, dtype, gate_mode)
+def make_desc(B, S, C, N, k, ncomp, dtype, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID,
+              gram_schmidt=False, gs_eps=1e-6):
+    return xhc_desc(B, S, C, N, k, ncomp, iters, eps, dtype, gate_mode, int(gram_schmidt), gs_eps)
 
 
 def workspace_size(desc, phase):
@@ -175,17 +177,19 @@ def _active_array(active):
 def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None, bias=None,
             z_save=None, xact_save=None, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID,
             workspace=None, stream=None, timer=None, desc=None, carry_in=None, W_next=None,
-            carry_out=None):
+            carry_out=None, gram_schmidt=False, gs_eps=1e-6):
     """xhc_forward on torch device tensors.  X [B*S,N,C], out [B*S,C], W [N*C,P].
 
     With carry_in, W_next or carry_out given, calls xhc_forward_chain: carry_in
     is the previous call's carry_out (X is then not projected and W may be
     None); W_next [N*C,P] with carry_out (xhc_carry_size bytes) forms the next
-    sublayer's projection partials from X_new."""
+    sublayer's projection partials from X_new.  gram_schmidt=True orthogonalises
+    the write-back components (modified Gram-Schmidt, epsilon gs_eps)."""
     T, N, C = X.shape
     ncomp = 4 if w4 is not None else 1
     if desc is None:
-        desc = make_desc(B, S, C, N, len(active), ncomp, _dtype_code(X), iters, eps, gate_mode)
+        desc = make_desc(B, S, C, N, len(active), ncomp, _dtype_code(X), iters, eps, gate_mode,
+                         gram_schmidt, gs_eps)
     act = _active_array(active)
     args = xhc_fwd_args(_ptr(X), _ptr(out), _ptr(w4), _ptr(w8), _ptr(w12), _ptr(W), _ptr(bias),
                         ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(X_new), _ptr(h_in),
@@ -207,12 +211,13 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
 def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None, w4=None, w8=None,
              w12=None, bias=None, z_save=None, db=None, dw4=None, dw8=None, dw12=None, accumulate=False,
              iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID, workspace=None, stream=None, timer=None,
-             desc=None):
+             desc=None, gram_schmidt=False, gs_eps=1e-6):
     """xhc_backward on torch device tensors."""
     T, N, C = X.shape
     ncomp = 4 if w4 is not None else 1
     if desc is None:
-        desc = make_desc(B, S, C, N, len(active), ncomp, _dtype_code(X), iters, eps, gate_mode)
+        desc = make_desc(B, S, C, N, len(active), ncomp, _dtype_code(X), iters, eps, gate_mode,
+                         gram_schmidt, gs_eps)
     act = _active_array(active)
     args = xhc_bwd_args(_ptr(X), _ptr(xact), _ptr(out), _ptr(w4), _ptr(w8), _ptr(w12), _ptr(W), _ptr(bias),
                         ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(z_save), _ptr(dX_new),

@@ -29,6 +29,7 @@ def test_kernel_names():
     names = xhc.kernel_names()
     assert names[:4] == ["pack_wt", "proj", "coef", "mix"]
     assert "bgrad" in names and "bdots" in names and "mixproj" in names
+    assert "gram" in names and "bdots_gs" in names
 
 
 BASE = 1 << 40          # fake, 256-aligned device addresses: validation never dereferences them
@@ -82,15 +83,29 @@ def test_workspace_sizes():
 @pytest.mark.parametrize("kw,code", [
     (dict(C=12), -2), (dict(C=0), -2), (dict(k=5), -2), (dict(N=3), -2), (dict(N=17), -2),
     (dict(ncomp=2), -2), (dict(B=0), -2), (dict(dtype=7), -6), (dict(iters=0), -2),
-    (dict(iters=65), -2), (dict(B=1 << 14, S=1 << 10, C=1024), -2)])
+    (dict(iters=65), -2), (dict(B=1 << 14, S=1 << 10, C=1024), -2),
+    (dict(gram_schmidt=2), -6), (dict(gram_schmidt=True, gs_eps=0.0), -2),
+    (dict(gram_schmidt=True, gs_eps=float("nan")), -2), (dict(gram_schmidt=True, gs_eps=-1e-6), -2)])
 def test_bad_descriptions(kw, code):
     d = desc16(**kw)
     a, _ = good_fwd(desc16())
     assert xhc.validate(d, a, 0) == code
 
 
+def test_gram_schmidt_workspace():
+    # Gram-Schmidt adds the Gram partials (forward) and the Sg records
+    # (backward); with one component it is the identity and adds nothing
+    d, g = desc16(), desc16(gram_schmidt=True)
+    T, ncb = 200, 1                                  # C = 256: one channel block of 512
+    assert xhc.workspace_size(g, 0) - xhc.workspace_size(d, 0) == -(-ncb * T * 16 * 4 // 256) * 256
+    assert xhc.workspace_size(g, 1) > xhc.workspace_size(d, 1)
+    d1, g1 = desc16(ncomp=1, N=4), desc16(ncomp=1, N=4, gram_schmidt=True)
+    assert xhc.workspace_size(g1, 0) == xhc.workspace_size(d1, 0)
+    assert xhc.workspace_size(g1, 1) == xhc.workspace_size(d1, 1)
+
+
 def test_valid_arguments_pass():
-    for kw in [dict(), dict(ncomp=1, N=4), dict(N=1, k=1, ncomp=1, dtype=xhc.XHC_F32)]:
+    for kw in [dict(), dict(ncomp=1, N=4), dict(N=1, k=1, ncomp=1, dtype=xhc.XHC_F32), dict(gram_schmidt=True)]:
         d = desc16(**kw)
         a, keep = good_fwd(d)
         assert xhc.validate(d, a, 0) == 0, kw

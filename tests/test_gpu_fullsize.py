@@ -159,6 +159,59 @@ def test_fwdbwd4096_full_backward():
         check_close(key, to_host(dws[key]), dconv_ref[m], 1e-2, 1e-2)
 
 
+@pytest.mark.timeout(600)
+def test_fwdbwd4096_gs_sampled():
+    # the Gram-Schmidt form at the full fwd+bwd size, in the launch
+    # configuration the benchmark times.  Tokens interact only through the
+    # 11-token TFA window: a block with 11 tokens of lead-in gives exact
+    # forward outputs and dX; one with 11 more tokens after it gives exact
+    # dout (the gradients of later positions flow back through the window).
+    w = synth.WORKLOADS["fwdbwd4096_gs"]
+    say(f"[fullsize] fwdbwd4096_gs B={w.B} S={w.S} C={w.C}")
+    d = synth.make_inputs(w, seed=7, grads=True)
+    r = np.random.default_rng(8)
+    for key, K in (("w4", 4), ("w8", 8), ("w12", 12)):       # components leaning on the output
+        v = (r.standard_normal((w.C, K)) * 0.3).astype(np.float32)
+        v[:, K - 1] += 0.6
+        d[key] = v
+    p = dev_params(d)
+    X = to_dev(d["X"], True)
+    dXn = to_dev(d["dX_new"], True)
+    dhin = to_dev(d["dh_in"], True)
+    active = [0, 1, 2, 3]
+    T, N, C, P = w.T, w.N, w.C, w.P
+    h_in = torch.empty(T, C, dtype=torch.bfloat16, device="cuda")
+    z_save = torch.empty(T, P + 1, device="cuda")
+    xact = torch.empty(T, 4, C, dtype=torch.bfloat16, device="cuda")
+    xhc.forward(X, p["out"], p["W"], active, X, h_in, B=w.B, S=w.S, bias=p["bias"], z_save=z_save,
+                xact_save=xact, gram_schmidt=True, **conv_kw(p, 4))
+    dX = torch.empty_like(dXn)
+    dout = torch.empty(T, C, dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty(N * C, P, device="cuda")
+    dws = dict(dw4=torch.empty(C, 4, device="cuda"), dw8=torch.empty(C, 8, device="cuda"),
+               dw12=torch.empty(C, 12, device="cuda"))
+    xhc.backward(X, p["out"], p["W"], active, dXn, dhin, dX, dout, dW, B=w.B, S=w.S, xact=xact, bias=p["bias"],
+                 z_save=z_save, gram_schmidt=True, **conv_kw(p, 4), **dws)
+    torch.cuda.synchronize()
+    Xh = synth.bf16_to_f32(d["X"])
+    outh, hW = synth.as_float(d, "out"), synth.as_float(d, "W")
+    dXnh, dhinh = synth.bf16_to_f32(d["dX_new"]), synth.bf16_to_f32(d["dh_in"])
+    convs = (d["w4"], d["w8"], d["w12"])
+    n = 24
+    for (b, s) in sample_blocks(w, n):
+        lo, hi = max(0, s - LEAD), min(w.S, s + n + LEAD)
+        rows = slice(b * w.S + lo, b * w.S + hi)
+        kw = dict(B=1, S=hi - lo, iters=w.iters, eps=w.eps, gram_schmidt_on=True)
+        ref = xo.forward(Xh[rows], outh[rows], hW, d["bias"], active, convs, **kw)
+        g = xo.backward(Xh[rows], outh[rows], hW, d["bias"], active, convs, dXnh[rows], dhinh[rows], **kw)
+        k0, t0 = s - lo, b * w.S + s
+        check_close(f"X_new[b={b},s={s}]", to_host(X[t0:t0 + n])[:, active], ref["X_new"][k0:k0 + n, active],
+                    1e-2, 1e-2)
+        check_close(f"h_in[b={b},s={s}]", to_host(h_in[t0:t0 + n]), ref["h_in"][k0:k0 + n], 1e-2, 1e-2)
+        check_close(f"dX[b={b},s={s}]", to_host(dX[t0:t0 + n]), g["dX"][k0:k0 + n], 1e-2, 1e-2)
+        check_close(f"dout[b={b},s={s}]", to_host(dout[t0:t0 + n]), g["dout"][k0:k0 + n], 1e-2, 1e-2)
+
+
 @pytest.mark.timeout(1200)
 def test_stack48_teacher_forced():
     w = synth.WORKLOADS["stack48"]
