@@ -168,10 +168,14 @@ int xhc_forward(const xhc_desc* desc, const xhc_fwd_args* args,
 int xhc_backward(const xhc_desc* desc, const xhc_bwd_args* args,
                  void* workspace, size_t workspace_bytes, xhc_stream_t stream);
 
-/* Chained forward of a stack of sublayers with the same description
- * (source: the closing section of the retrospective, which names an exactly
- * equivalent dense-read correction beyond the sparse write without giving
- * its mechanism; this is a reading of it).  Sublayer l's write pass reads
+/* Chained forward of a stack of sublayers (source: the closing section of
+ * the retrospective, which names an exactly equivalent dense-read correction
+ * beyond the sparse write without giving its mechanism; this is a reading of
+ * it).  The next sublayer may differ in k, ncomp, gates, Sinkhorn steps,
+ * epsilons and Gram-Schmidt -- a stack alternates attention-side sublayers
+ * with one write-back component and MLP-side ones with TFA (section
+ * "最便宜的新信息，可能就在相邻 token 里" keeps TFA on the MLP side only) --
+ * but shares B, S, C, N and the storage type.  Sublayer l's write pass reads
  * every row of its state and writes the k active rows, so the next
  * sublayer's state differs only in those rows; the pass also forms the next
  * sublayer's projection partials (x'.W' and sum x'^2 over each block of
@@ -184,10 +188,14 @@ typedef struct {
                              this call's X (args->W is then not read)      */
   const void* W_next;     /* [N*C,P] projection weights of the next sublayer,
                              or NULL (no carry out: the last sublayer)      */
-  void* carry_out;        /* xhc_carry_size(desc) bytes, or NULL iff W_next is
-                             NULL; may be == carry_in (it is consumed before
-                             it is written), otherwise no overlap with any
-                             other buffer of the call                       */
+  void* carry_out;        /* xhc_carry_size(next description) bytes, or NULL
+                             iff W_next is NULL; may be == carry_in (it is
+                             consumed before it is written), otherwise no
+                             overlap with any other buffer of the call      */
+  const xhc_desc* desc_next; /* HOST; the next sublayer's description, or
+                             NULL: the same as this call's.  W_next is then
+                             [N*C, P of desc_next].  XHC_ERR_SHAPE when B, S,
+                             C, N or dtype differ from this call's          */
 } xhc_chain_args;
 
 /* Bytes of one carry buffer (fp32 partials per token and channel block);

@@ -91,7 +91,9 @@ int make_plan(const xhc_desc* d, Plan* p) {
 
   // workspace layouts
   size_t o = 0;
-  q.off_wt = o;     o = align256(o + (size_t)q.N * cdiv(q.C, 32) * 32 * q.NT * 16 * q.esz);
+  // sized for the largest tile count: a chained call packs the next
+  // sublayer's W there, whose P may differ
+  q.off_wt = o;     o = align256(o + (size_t)q.N * cdiv(q.C, 32) * 32 * NT_MAX * 16 * q.esz);
   q.off_zpart = o;  o = align256(o + (size_t)q.SK * T * q.ZST * 4);
   q.off_coef = o;   o = align256(o + (size_t)T * COEF_STRIDE * 4);
   q.off_gram = o;   o = align256(o + (q.gs ? (size_t)q.b1_cblocks * T * 16 * 4 : 0));
@@ -174,14 +176,16 @@ static int validate_fwd(const Plan& p, const xhc_fwd_args* a, bool need_W = true
 }
 
 // Chained forward: the carry buffers and the next sublayer's weights.
-static int validate_chain(const Plan& p, const xhc_fwd_args* a, const xhc_chain_args* c) {
+// pn: the next sublayer's plan (== p without desc_next)
+static int validate_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const xhc_chain_args* c) {
   if (!c) return XHC_OK;
   if ((c->W_next == nullptr) != (c->carry_out == nullptr)) return XHC_ERR_NULL;
   if (misaligned(c->carry_in) || misaligned(c->carry_out) || misaligned(c->W_next)) return XHC_ERR_ALIGN;
+  if (pn.B != p.B || pn.S != p.S || pn.C != p.C || pn.N != p.N || pn.dtype != p.dtype) return XHC_ERR_SHAPE;
   const size_t T = p.T, e = p.esz;
   const Span cin = span(c->carry_in, c->carry_in ? p.carry_bytes : 0);
-  const Span cout = span(c->carry_out, c->carry_out ? p.carry_bytes : 0);
-  const Span Wn = span(c->W_next, c->W_next ? (size_t)p.NC * p.P * e : 0);
+  const Span cout = span(c->carry_out, c->carry_out ? pn.carry_bytes : 0);
+  const Span Wn = span(c->W_next, c->W_next ? (size_t)pn.NC * pn.P * e : 0);
   const Span X = span(a->X, T * p.NC * e), Xn = span(a->X_new, T * p.NC * e);
   const Span out = span(a->out, T * p.C * e), hin = span(a->h_in, T * p.C * e);
   const Span W = span(a->W, a->W ? (size_t)p.NC * p.P * e : 0);
@@ -330,11 +334,16 @@ int xhc_forward_chain(const xhc_desc* desc, const xhc_fwd_args* args, const xhc_
   if (rc) return rc;
   rc = xhc::validate_fwd(p, args, !(chain && chain->carry_in));
   if (rc) return rc;
-  rc = xhc::validate_chain(p, args, chain);
+  xhc::Plan pn = p;
+  if (chain && chain->desc_next) {
+    rc = xhc::make_plan(chain->desc_next, &pn);
+    if (rc) return rc;
+  }
+  rc = xhc::validate_chain(p, pn, args, chain);
   if (rc) return rc;
   rc = check_ws(p, workspace, workspace_bytes, p.fwd_bytes);
   if (rc) return rc;
-  return xhc::launch_forward_chain(p, args, chain, workspace, reinterpret_cast<hipStream_t>(stream));
+  return xhc::launch_forward_chain(p, pn, args, chain, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
 int xhc_backward(const xhc_desc* desc, const xhc_bwd_args* args, void* workspace, size_t workspace_bytes,

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
         if (slot < N && o * 1024 < valid_bytes) {
           const unsigned char* src = static_cast<const unsigned char*>(Wf) +
                                      ((size_t)row_of(ro, slot) * nks + ksb) * NT * FB + o * 1024 + lane * 16;
-          if (split && q == 0 && o >= PPR / 2)        // K-step 1 of an active row
+          if (split && q == 0 && j < k && o >= PPR / 2)   // K-step 1 of an active row
             __builtin_amdgcn_global_load_lds((const gbl_void_t*)src,
                                              (lds_void_t*)&wa1[j * (PPR / 2) * 1024 + (o - PPR / 2) * 1024], 16, 0, 0);
           else
@@ -472,9 +472,11 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
+// pn: the next sublayer's plan; its tile count and partial-record stride
+// shape the projection and the carry.
 template <typename E>
-static void launch_mixproj_e(const Plan& p, const xhc_fwd_args* a, const float* coef, const void* Wf,
-                             float* carry, hipStream_t st) {
+static void launch_mixproj_e(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const float* coef,
+                             const void* Wf, float* carry, hipStream_t st) {
   RowOrder ro{0};
   {
     bool used[16] = {false};
@@ -490,19 +492,19 @@ static void launch_mixproj_e(const Plan& p, const xhc_fwd_args* a, const float* 
 #define XHC_MP(NT, NC)                                                                                            \
   k_mixproj<E, NT, NC, false><<<grid, 64 * MP_WAVES, 0, st>>>(a->X, a->out, a->w4, a->w8, a->w12, coef, Wf, a->X_new,    \
                                                        a->h_in, a->xact_save, carry, ro, p.T, p.S, p.C, p.N, p.k, \
-                                                       in_place, p.mp_cpw, p.mp_nch, p.mp_nbatch, p.ZST)
+                                                       in_place, p.mp_cpw, p.mp_nch, p.mp_nbatch, pn.ZST)
   if (p.nc == 4) {
-    if (p.NT == 3) XHC_MP(3, 4); else if (p.NT == 2) XHC_MP(2, 4); else XHC_MP(1, 4);
+    if (pn.NT == 3) XHC_MP(3, 4); else if (pn.NT == 2) XHC_MP(2, 4); else XHC_MP(1, 4);
   } else {
-    if (p.NT == 3) XHC_MP(3, 1); else if (p.NT == 2) XHC_MP(2, 1); else XHC_MP(1, 1);
+    if (pn.NT == 3) XHC_MP(3, 1); else if (pn.NT == 2) XHC_MP(2, 1); else XHC_MP(1, 1);
   }
 #undef XHC_MP
 }
 
-void launch_mixproj(const Plan& p, const xhc_fwd_args* a, const float* coef, const void* Wf, float* carry,
-                    hipStream_t st) {
-  if (p.dtype == XHC_BF16) launch_mixproj_e<BF16>(p, a, coef, Wf, carry, st);
-  else launch_mixproj_e<F32>(p, a, coef, Wf, carry, st);
+void launch_mixproj(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const float* coef, const void* Wf,
+                    float* carry, hipStream_t st) {
+  if (p.dtype == XHC_BF16) launch_mixproj_e<BF16>(p, pn, a, coef, Wf, carry, st);
+  else launch_mixproj_e<F32>(p, pn, a, coef, Wf, carry, st);
 }
 
 }  // namespace xhc

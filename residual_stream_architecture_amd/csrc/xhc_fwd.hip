@@ -522,8 +522,8 @@ static void launch_proj(const Plan& p, const StreamRows& src, const void* Wf, fl
 }
 
 template <typename E, typename R>
-static int forward_impl(const Plan& p, const xhc_fwd_args* a, const xhc_chain_args* ch, char* ws, hipStream_t st,
-                        xhc_timer* tm) {
+static int forward_impl(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const xhc_chain_args* ch, char* ws,
+                        hipStream_t st, xhc_timer* tm) {
   void* Wt = ws + p.off_wt;
   float* zpart = reinterpret_cast<float*>(ws + p.off_zpart);
   float* coef = reinterpret_cast<float*>(ws + p.off_coef);
@@ -557,9 +557,9 @@ static int forward_impl(const Plan& p, const xhc_fwd_args* a, const xhc_chain_ar
   if (carry_out) {
     // the next sublayer's weights in the MFMA fragment order, then the fused
     // write pass with its projection
-    launch_pack_wt<R>(p, ch->W_next, Wt, st, tm);
+    launch_pack_wt<R>(pn, ch->W_next, Wt, st, tm);
     TimedLaunch tl(tm, KID_MIXPROJ, st);
-    launch_mixproj(p, a, coef, Wt, static_cast<float*>(ch->carry_out), st);
+    launch_mixproj(p, pn, a, coef, Wt, static_cast<float*>(ch->carry_out), st);
     return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
   }
   {
@@ -584,13 +584,14 @@ static int forward_impl(const Plan& p, const xhc_fwd_args* a, const xhc_chain_ar
 }
 
 int launch_forward(const Plan& p, const xhc_fwd_args* a, void* ws, hipStream_t st) {
-  return launch_forward_chain(p, a, nullptr, ws, st);
+  return launch_forward_chain(p, p, a, nullptr, ws, st);
 }
 
-int launch_forward_chain(const Plan& p, const xhc_fwd_args* a, const xhc_chain_args* c, void* ws, hipStream_t st) {
+int launch_forward_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const xhc_chain_args* c, void* ws,
+                         hipStream_t st) {
   char* w = static_cast<char*>(ws);
-  if (p.dtype == XHC_BF16) return forward_impl<BF16, uint16_t>(p, a, c, w, st, a->timer);
-  return forward_impl<F32, float>(p, a, c, w, st, a->timer);
+  if (p.dtype == XHC_BF16) return forward_impl<BF16, uint16_t>(p, pn, a, c, w, st, a->timer);
+  return forward_impl<F32, float>(p, pn, a, c, w, st, a->timer);
 }
 
 // Backward helper: coefficients either from a forward's z_save or, when it

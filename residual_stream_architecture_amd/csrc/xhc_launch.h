@@ -63,9 +63,11 @@ int launch_forward(const Plan& p, const xhc_fwd_args* a, void* ws, hipStream_t s
 // Forward with an optional projection carried in from the previous sublayer
 // (carry_in) and an optional projection of X_new for the next sublayer
 // (W_next -> carry_out).
-int launch_forward_chain(const Plan& p, const xhc_fwd_args* a, const xhc_chain_args* c, void* ws, hipStream_t st);
-void launch_mixproj(const Plan& p, const xhc_fwd_args* a, const float* coef, const void* Wf, float* carry,
-                    hipStream_t st);
+// pn: the next sublayer's plan (its P, tile count and carry layout).
+int launch_forward_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const xhc_chain_args* c, void* ws,
+                         hipStream_t st);
+void launch_mixproj(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const float* coef, const void* Wf,
+                    float* carry, hipStream_t st);
 int launch_coef_bwd(const Plan& p, const void* X, const void* xact, const int32_t* active, const void* W,
                     const float* bias, const float* z_save, void* ws, float* coef, float* z_out,
                     hipStream_t st, xhc_timer* tm);

@@ -67,6 +67,8 @@ constexpr int rec_dzr0_half(int esz) { return 4 * 16 * 8 * esz; }
 constexpr int rec_dzr1_half(int esz) { return 4 * 16 * 4 * esz; }
 constexpr int rec_dzrt_half(int esz) { return 3 * 4 * 16 * 4 * esz; }
 
+constexpr int NT_MAX = 3;   // logit tiles of 16: P = N + k*nc + k*k <= 48
+
 struct Plan {
   int B, S, C, N, k, nc, P, NT, T, iters, dtype, gate;
   float eps;

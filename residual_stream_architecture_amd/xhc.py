@@ -45,7 +45,8 @@ class xhc_bwd_args(ctypes.Structure):
 
 
 class xhc_chain_args(ctypes.Structure):
-    _fields_ = [("carry_in", _vp), ("W_next", _vp), ("carry_out", _vp)]
+    _fields_ = [("carry_in", _vp), ("W_next", _vp), ("carry_out", _vp),
+                ("desc_next", ctypes.POINTER(xhc_desc))]
 
 
 class XhcError(RuntimeError):
@@ -177,14 +178,15 @@ def _active_array(active):
 def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None, bias=None,
             z_save=None, xact_save=None, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID,
             workspace=None, stream=None, timer=None, desc=None, carry_in=None, W_next=None,
-            carry_out=None, gram_schmidt=False, gs_eps=1e-6):
+            carry_out=None, gram_schmidt=False, gs_eps=1e-6, desc_next=None):
     """xhc_forward on torch device tensors.  X [B*S,N,C], out [B*S,C], W [N*C,P].
 
     With carry_in, W_next or carry_out given, calls xhc_forward_chain: carry_in
     is the previous call's carry_out (X is then not projected and W may be
     None); W_next [N*C,P] with carry_out (xhc_carry_size bytes) forms the next
-    sublayer's projection partials from X_new.  gram_schmidt=True orthogonalises
-    the write-back components (modified Gram-Schmidt, epsilon gs_eps)."""
+    sublayer's projection partials from X_new; desc_next (an xhc_desc) describes
+    that sublayer when it differs from this one (k, ncomp, ...).  gram_schmidt=True
+    orthogonalises the write-back components (modified Gram-Schmidt, epsilon gs_eps)."""
     T, N, C = X.shape
     ncomp = 4 if w4 is not None else 1
     if desc is None:
@@ -195,13 +197,14 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
                         ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(X_new), _ptr(h_in),
                         _ptr(z_save), _ptr(xact_save), None if timer is None else timer.handle)
     ws, need = _workspace(desc, XHC_PHASE_FWD, X.device, workspace)
-    if carry_in is None and W_next is None and carry_out is None:
+    if carry_in is None and W_next is None and carry_out is None and desc_next is None:
         rc = lib.xhc_forward(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
                              _stream_handle(stream))
         if rc:
             raise XhcError(rc, "xhc_forward")
         return
-    chain = xhc_chain_args(_ptr(carry_in), _ptr(W_next), _ptr(carry_out))
+    chain = xhc_chain_args(_ptr(carry_in), _ptr(W_next), _ptr(carry_out),
+                           None if desc_next is None else ctypes.pointer(desc_next))
     rc = lib.xhc_forward_chain(ctypes.byref(desc), ctypes.byref(args), ctypes.byref(chain), ws.data_ptr(),
                                ws.numel(), _stream_handle(stream))
     if rc:

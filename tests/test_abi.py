@@ -234,6 +234,14 @@ def test_chain_error_paths():
     c = good_chain()
     c.carry_out = fake(23, 8)
     assert chain_call(d, a, c) == -5
+    # the next sublayer may differ in k and ncomp, not in B, S, C, N or dtype
+    for kw, code in ((dict(ncomp=1), -7), (dict(k=2), -7), (dict(ncomp=1, gram_schmidt=True), -7),
+                     (dict(C=512), -2), (dict(N=8), -2), (dict(S=99), -2), (dict(dtype=xhc.XHC_F32), -2),
+                     (dict(k=5), -2)):
+        dn = desc16(**kw)
+        c = good_chain()
+        c.desc_next = ctypes.pointer(dn)
+        assert chain_call(d, a, c) == code, kw
 
 
 def test_strerror():

@@ -35,6 +35,9 @@ CHAIN_CASES = [
     ("bf16_mhc_n4", W_("cm", 2, 40, 136, 4, 4, 1, "bf16", "stack", layers=3), True, False, True, 0.0),
     ("f32_n6_k2_nc1", W_("cf", 3, 33, 72, 6, 2, 1, "f32", "stack", layers=2), False, False, False, 0.5),
     ("f32_n16_many_blocks", W_("cg", 1, 300, 608, 16, 4, 4, "f32", "stack", layers=2), True, True, False, 0.0),
+    # N = 16 with k < 4: a chunk's first step holds active and untouched rows
+    ("bf16_n16_k2", W_("ck", 2, 70, 192, 16, 2, 4, "bf16", "stack", layers=3), True, True, False, 0.1),
+    ("bf16_n16_k3_nc1", W_("cl", 1, 100, 128, 16, 3, 1, "bf16", "stack", layers=2), False, False, True, 0.0),
 ]
 
 
@@ -138,3 +141,50 @@ def test_chain_stack48_shape_sampled():
             check_close(f"L{layer} h_in[s={s}]", to_host(h_in[s:s + n]), ref["h_in"][k0:], 1e-2, 1e-2)
             check_close(f"L{layer} z[s={s}]", to_host(z_save[s:s + n])[:, :P], ref["z"][k0:], 1e-2, 1e-2)
         say(f" layer {layer} ok at {time.time() - t_start:.1f}s")
+
+
+# name, base workload, per-layer (k, ncomp): the chain between sublayers of
+# different descriptions (attention-side sublayers with one component,
+# MLP-side ones with TFA, different k), so P and the tile count change
+ALT_CASES = [
+    ("bf16_attn_mlp", W_("ca", 2, 45, 200, 16, 4, 4, "bf16", "stack"), [(4, 1), (4, 4), (4, 1), (4, 4)]),
+    ("f32_n4_tiles_change", W_("cb", 3, 33, 72, 4, 4, 4, "f32", "stack"), [(4, 4), (4, 1), (2, 4), (3, 1)]),
+    ("bf16_k_varies", W_("cc", 1, 130, 128, 16, 4, 4, "bf16", "stack"), [(4, 4), (2, 4), (3, 1)]),
+]
+
+
+@pytest.mark.parametrize("name,w,spec", ALT_CASES, ids=[c[0] for c in ALT_CASES])
+def test_chain_across_different_descriptions(name, w, spec):
+    import dataclasses
+    say(f"[chain alt] {name} B={w.B} S={w.S} C={w.C} N={w.N} layers={spec}")
+    bf16 = w.dtype == "bf16"
+    dt = torch.bfloat16 if bf16 else torch.float32
+    T, N, C = w.T, w.N, w.C
+    code = xhc.XHC_BF16 if bf16 else xhc.XHC_F32
+    ws = [dataclasses.replace(w, k=k, ncomp=nc, layers=1) for k, nc in spec]
+    descs = [xhc.make_desc(w.B, w.S, C, N, k, nc, code) for k, nc in spec]
+    params = [layer_params(wl, l, 0.2) for l, wl in enumerate(ws)]
+    X = to_dev(synth.make_inputs(w, seed=0)["X"], bf16)
+    nbytes = max(xhc.carry_size(dsc) for dsc in descs)
+    carries = [torch.empty(nbytes // 4, device="cuda") for _ in range(2)]
+    h_in = torch.empty(T, C, dtype=dt, device="cuda")
+    for l, wl in enumerate(ws):
+        p, h = params[l]
+        atol, rtol = tol(wl)
+        active = synth.active_streams(l, N, wl.k)
+        last = l + 1 == len(ws)
+        z_save = torch.empty(T, wl.P + 1, device="cuda")
+        Xh = to_host(X)
+        xhc.forward(X, p["out"], p["W"], active, X, h_in, B=w.B, S=w.S, bias=p["bias"], z_save=z_save,
+                    desc=descs[l], carry_in=carries[l % 2] if l > 0 else None,
+                    W_next=None if last else params[l + 1][0]["W"],
+                    carry_out=None if last else carries[(l + 1) % 2],
+                    desc_next=None if last else descs[l + 1], **conv_kw(p, wl))
+        torch.cuda.synchronize()
+        ref = xo.forward(Xh, h["out"], h["W"], h["bias"], active, h["convs"], B=w.B, S=w.S)
+        got = to_host(X)
+        inactive = [i for i in range(N) if i not in active]
+        assert np.array_equal(got[:, inactive], Xh[:, inactive]), f"layer {l}: pass-through rows differ"
+        check_close(f"L{l} X_new[active]", got[:, active], ref["X_new"][:, active], atol, rtol)
+        check_close(f"L{l} h_in", to_host(h_in), ref["h_in"], atol, rtol)
+        check_close(f"L{l} z", to_host(z_save)[:, :wl.P], ref["z"], atol, rtol)
