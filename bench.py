@@ -187,37 +187,42 @@ def forward_bench(args, w, np, torch, synth, xhc):
     d = synth.make_inputs(w, seed=0, state=True)
     X = torch.from_numpy(d.pop("X").view(np.int16)).cuda().view(torch.bfloat16) if esz == 2 else \
         torch.from_numpy(d.pop("X")).cuda()
+    code = xhc.XHC_BF16 if esz == 2 else xhc.XHC_F32
     layers = []
     for l in range(w.layers):
+        nc = synth.layer_ncomp(w, l)
+        Pl = N + k * nc + k * k
         if w.layers == 1:
             p = {key: (torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16) if a.dtype == np.uint16
                        else torch.from_numpy(a).cuda()) for key, a in d.items()}
         else:
             g = torch.Generator(device="cuda")
             g.manual_seed(synth.stack_layer_seed(l))
-            p = {"out": torch.randn(T, C, generator=g, device="cuda").to(sdt),
-                 "w4": torch.randn(C, 4, generator=g, device="cuda") * 0.02,
-                 "w8": torch.randn(C, 8, generator=g, device="cuda") * 0.02,
-                 "w12": torch.randn(C, 12, generator=g, device="cuda") * 0.02,
-                 "W": (torch.randn(N * C, P, generator=g, device="cuda") * 0.02).to(sdt),
-                 "bias": torch.zeros(P, device="cuda")}
-        layers.append((p, synth.active_streams(l, N, k)))
+            p = {"out": torch.randn(T, C, generator=g, device="cuda").to(sdt)}
+            if nc == 4:
+                p.update(w4=torch.randn(C, 4, generator=g, device="cuda") * 0.02,
+                         w8=torch.randn(C, 8, generator=g, device="cuda") * 0.02,
+                         w12=torch.randn(C, 12, generator=g, device="cuda") * 0.02)
+            p.update(W=(torch.randn(N * C, Pl, generator=g, device="cuda") * 0.02).to(sdt),
+                     bias=torch.zeros(Pl, device="cuda"))
+        desc = xhc.make_desc(w.B, w.S, C, N, k, nc, code, w.iters, w.eps, gram_schmidt=w.gs)
+        layers.append((p, synth.active_streams(l, N, k), desc, nc))
     del d
     h_in = torch.empty(T, C, dtype=sdt, device="cuda")
-    desc = xhc.make_desc(w.B, w.S, C, N, k, w.ncomp, xhc.XHC_BF16 if esz == 2 else xhc.XHC_F32, w.iters, w.eps,
-                         gram_schmidt=w.gs)
-    ws_f = torch.empty(xhc.workspace_size(desc, 0), dtype=torch.uint8, device="cuda")
-    carries = [torch.empty(xhc.carry_size(desc) // 4, device="cuda") for _ in range(2)] if chain else None
+    ws_f = torch.empty(max(xhc.workspace_size(L[2], 0) for L in layers), dtype=torch.uint8, device="cuda")
+    carries = ([torch.empty(max(xhc.carry_size(L[2]) for L in layers) // 4, device="cuda") for _ in range(2)]
+               if chain else None)
 
     def step(timer=None):
-        for l, (p, active) in enumerate(layers):
-            conv = dict(w4=p["w4"], w8=p["w8"], w12=p["w12"]) if w.ncomp == 4 else {}
+        for l, (p, active, desc, nc) in enumerate(layers):
+            conv = dict(w4=p["w4"], w8=p["w8"], w12=p["w12"]) if nc == 4 else {}
             extra = {}
             if chain:
                 last = l + 1 == len(layers)
                 extra = dict(carry_in=carries[l % 2] if l > 0 else None,
                              W_next=None if last else layers[l + 1][0]["W"],
-                             carry_out=None if last else carries[(l + 1) % 2])
+                             carry_out=None if last else carries[(l + 1) % 2],
+                             desc_next=None if last else layers[l + 1][2])
             xhc.forward(X, p["out"], p["W"], active, X, h_in, B=w.B, S=w.S, bias=p["bias"], workspace=ws_f,
                         timer=timer, desc=desc, **conv, **extra)
 
@@ -252,7 +257,9 @@ def forward_bench(args, w, np, torch, synth, xhc):
               "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
               "config": {"workload": f"{w.name}: B={w.B} S={w.S} C={C} N={N} k={k} ncomp={w.ncomp} "
-                                     f"layers={w.layers}, in-place forward"
+                                     f"layers={w.layers}"
+                                     + (" (even sublayers attention-side: ncomp=1)" if w.alt else "")
+                                     + ", in-place forward"
                                      + (", chained projection" if chain else "")},
               "layer_tokens_per_s": round(T * w.layers * args.steps / elapsed, 1),
               "step_hbm": {"alg_bytes_per_token_in_C": alg_c, "touched_bytes_per_token_in_C": touched_c,

@@ -34,6 +34,7 @@ class Workload:
     iters: int = 20
     eps: float = 1e-6
     gs: bool = False      # Gram-Schmidt over the write-back components
+    alt: bool = False     # stack: even sublayers attention-side (one component, no TFA)
 
     @property
     def T(self):
@@ -57,7 +58,15 @@ WORKLOADS = {
     "fwdbwd4096_gs": Workload("fwdbwd4096_gs", 2, 4096, 4096, 16, 4, 4, "bf16", "fwdbwd", gs=True),
     # 48 stacked sublayer updates, state carried in HBM
     "stack48": Workload("stack48", 1, 8192, 7168, 16, 4, 4, "bf16", "stack", layers=48),
+    # the same stack alternating attention-side sublayers (out only) with
+    # MLP-side ones (TFA), as the pages place TFA after the MLP/MoE only
+    "stack48_alt": Workload("stack48_alt", 1, 8192, 7168, 16, 4, 4, "bf16", "stack", layers=48, alt=True),
 }
+
+
+def layer_ncomp(w, layer):
+    """Write-back components of sublayer `layer` of a stack."""
+    return 1 if (w.alt and layer % 2 == 0) else w.ncomp
 
 
 def active_streams(layer, N, k):

@@ -103,31 +103,37 @@ def test_chain_matches_oracle_per_layer(name, w, in_place, save_rows, one_carry,
 
 
 @pytest.mark.timeout(900)
-def test_chain_stack48_shape_sampled():
-    """The stacked workload's shape (S = 8192, C = 7168) for four chained
+@pytest.mark.parametrize("wname", ["stack48", "stack48_alt"])
+def test_chain_stack48_shape_sampled(wname):
+    """The stacked workloads' shape (S = 8192, C = 7168) for four chained
     layers, teacher-forced, on sampled token blocks (an 11-token lead-in
-    makes each block's outputs exact)."""
-    w = synth.WORKLOADS["stack48"]
+    makes each block's outputs exact).  stack48_alt alternates sublayers with
+    one component and with TFA."""
+    import dataclasses
+    w = synth.WORKLOADS[wname]
     layers, n, lead = 4, 16, 11
-    say(f"[chain] stack48 shape S={w.S} C={w.C} layers={layers}")
+    say(f"[chain] {wname} shape S={w.S} C={w.C} layers={layers}")
     t_start = time.time()
-    T, N, C, P = w.T, w.N, w.C, w.P
+    T, N, C = w.T, w.N, w.C
     X = to_dev(synth.make_inputs(w, seed=0)["X"], True)
-    desc = xhc.make_desc(w.B, w.S, C, N, w.k, w.ncomp, xhc.XHC_BF16)
-    carries = [torch.empty(xhc.carry_size(desc) // 4, device="cuda") for _ in range(2)]
-    params = [layer_params(w, layer, 0.0) for layer in range(layers)]
+    lw = [dataclasses.replace(w, ncomp=synth.layer_ncomp(w, layer), layers=1) for layer in range(layers)]
+    descs = [xhc.make_desc(w.B, w.S, C, N, w.k, wl.ncomp, xhc.XHC_BF16) for wl in lw]
+    carries = [torch.empty(max(xhc.carry_size(dsc) for dsc in descs) // 4, device="cuda") for _ in range(2)]
+    params = [layer_params(lw[layer], layer, 0.0) for layer in range(layers)]
     h_in = torch.empty(T, C, dtype=torch.bfloat16, device="cuda")
-    z_save = torch.empty(T, P + 1, device="cuda")
     blocks = [0, 4096 - 5, w.S - n]
     for layer in range(layers):
         p, h = params[layer]
+        P = lw[layer].P
+        z_save = torch.empty(T, P + 1, device="cuda")
         active = synth.active_streams(layer, N, w.k)
         before = {s: to_host(X[max(0, s - lead):s + n]) for s in blocks}
         last = layer + 1 == layers
-        xhc.forward(X, p["out"], p["W"], active, X, h_in, B=w.B, S=w.S, bias=p["bias"], z_save=z_save, desc=desc,
-                    carry_in=carries[layer % 2] if layer > 0 else None,
+        xhc.forward(X, p["out"], p["W"], active, X, h_in, B=w.B, S=w.S, bias=p["bias"], z_save=z_save,
+                    desc=descs[layer], carry_in=carries[layer % 2] if layer > 0 else None,
                     W_next=None if last else params[layer + 1][0]["W"],
-                    carry_out=None if last else carries[(layer + 1) % 2], **conv_kw(p, w))
+                    carry_out=None if last else carries[(layer + 1) % 2],
+                    desc_next=None if last else descs[layer + 1], **conv_kw(p, lw[layer]))
         torch.cuda.synchronize()
         for s in blocks:
             lo = max(0, s - lead)

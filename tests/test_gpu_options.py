@@ -30,7 +30,20 @@ OPTION_CASES = [
     ("iters1_f32", synth.Workload("i1", 1, 50, 64, 8, 4, 4, "f32", "fwd", iters=1), [7, 6, 5, 4], "sigmoid", 0.0),
     ("iters64_eps_f32", synth.Workload("i64", 1, 50, 64, 16, 4, 1, "f32", "fwd", iters=64, eps=1e-3),
      [0, 1, 2, 3], "sigmoid", 0.3),
+    # H_res logits from the k active rows only: W's res columns are zero on
+    # the rows of the untouched streams (the pages' O(k^3 C) generation)
+    ("hres_active_bf16", synth.Workload("ha", 2, 60, 136, 16, 4, 4, "bf16", "fwd"), [3, 9, 12, 14], "sigmoid", 0.2),
+    ("hres_active_f32", synth.Workload("hf", 1, 50, 40, 9, 3, 1, "f32", "fwd"), [8, 0, 5], "sigmoid", 0.0),
 ]
+RES_FROM_ACTIVE = {"hres_active_bf16", "hres_active_f32"}
+
+
+def zero_res_rows(d, w, active):
+    """Zero the res-logit columns of W on the rows of the untouched streams."""
+    P0 = w.N + w.k * w.ncomp
+    for i in range(w.N):
+        if i not in active:
+            d["W"][i * w.C:(i + 1) * w.C, P0:] = 0       # +0 in fp32 and in bf16 bits
 
 
 def _inputs(w, bias_scale, seed):
@@ -56,6 +69,8 @@ def _gate(gate):
 def test_options_forward_backward(name, w, active, gate, bias_scale):
     say(f"[options] {name} B={w.B} S={w.S} C={w.C} N={w.N} k={w.k} nc={w.ncomp} iters={w.iters} eps={w.eps}")
     d = _inputs(w, bias_scale, seed=11)
+    if name in RES_FROM_ACTIVE:
+        zero_res_rows(d, w, active)
     h = host_inputs(d)
     dev = device_inputs(d, w.dtype == "bf16")
     T, N, C, P = w.T, w.N, w.C, w.P

@@ -407,3 +407,29 @@ def test_active_rows_mixing_conserves_the_sum():
     lhs = res["X_new"][:, act].sum(axis=1) - wb
     np.testing.assert_allclose(lhs, c["X"][:, act].sum(axis=1), atol=1e-11)
     assert np.abs(res["H_res"].sum(axis=2) - 1).max() > 1e-3   # the test has teeth
+
+
+# ---------------------------------------------------------------------------
+# H_res generated from the k active rows only (retrospective section
+# "模型可以拥有 16 条 streams，但每层只更新 4 条": the cubic generation cost
+# falls from N^3 C to k^3 C): with W's res columns zero on the rows of the
+# untouched streams, the un-normalised res logits r * (z_res - b) depend on
+# the active rows alone, while the pre logits still see every stream
+# ---------------------------------------------------------------------------
+
+def test_res_logits_from_active_rows_only():
+    c = rand_case(N=10, k=3, C=5, seed=31)
+    N, k, C = 10, 3, 5
+    P0 = N + k * 4
+    inactive = [i for i in range(N) if i not in c["active"]]
+    for i in inactive:
+        c["W"][i * C:(i + 1) * C, P0:] = 0.0
+    a = fwd(c)
+    c2 = dict(c)
+    c2["X"] = c["X"].copy()
+    c2["X"][:, inactive] = RNG.standard_normal(c2["X"][:, inactive].shape)
+    b = fwd(c2)
+    un_a = a["r"][:, None] * (a["z"][:, P0:] - c["bias"][P0:])
+    un_b = b["r"][:, None] * (b["z"][:, P0:] - c["bias"][P0:])
+    np.testing.assert_allclose(un_a, un_b, rtol=1e-12, atol=1e-12)
+    assert np.abs(a["z"][:, :N] - b["z"][:, :N]).max() > 1e-3
