@@ -301,6 +301,13 @@ int xhc_validate(const xhc_desc* desc, const void* args, int phase) {
   return XHC_ERR_UNSUPPORTED;
 }
 
+// The launchers report a failed launch through hipGetLastError(), which
+// returns the last error of ANY HIP call made on the calling thread.  Other
+// code on that thread (a framework probing pointer attributes, say) may
+// leave an error pending that it chose to ignore; clear it before this
+// call's launches so that only their errors are reported as XHC_ERR_HIP.
+static void clear_pending_hip_error() { (void)hipGetLastError(); }
+
 static int check_ws(const xhc::Plan& p, void* ws, size_t bytes, size_t need) {
   (void)p;
   if (!ws) return XHC_ERR_WORKSPACE;
@@ -318,6 +325,7 @@ int xhc_forward(const xhc_desc* desc, const xhc_fwd_args* args, void* workspace,
   if (rc) return rc;
   rc = check_ws(p, workspace, workspace_bytes, p.fwd_bytes);
   if (rc) return rc;
+  clear_pending_hip_error();
   return xhc::launch_forward(p, args, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -343,6 +351,7 @@ int xhc_forward_chain(const xhc_desc* desc, const xhc_fwd_args* args, const xhc_
   if (rc) return rc;
   rc = check_ws(p, workspace, workspace_bytes, p.fwd_bytes);
   if (rc) return rc;
+  clear_pending_hip_error();
   return xhc::launch_forward_chain(p, pn, args, chain, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -355,6 +364,7 @@ int xhc_backward(const xhc_desc* desc, const xhc_bwd_args* args, void* workspace
   if (rc) return rc;
   rc = check_ws(p, workspace, workspace_bytes, p.bwd_bytes);
   if (rc) return rc;
+  clear_pending_hip_error();
   return xhc::launch_backward(p, args, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -579,11 +579,13 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
 
   // reduce the per-chunk dots
   float dpre = 0.f, dres = 0.f, dpost = 0.f;
+  #pragma unroll 8
   for (int cb = 0; cb < ncba; ++cb) {
     const float* d = dpa + ((size_t)cb * T + tc) * BX_OUT;
     dpre += d[e];
     dres += d[16 + e];
   }
+  #pragma unroll 8
   for (int cb = 0; cb < ncb; ++cb) dpost += dpart[((size_t)cb * T + tc) * DOT_STRIDE + 32 + e];
   const float* z = zin + tc * (P + 1);
   const float r = z[P];
@@ -597,6 +599,7 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
     // the token's 16 lanes share one wave: gather its records
     float gsum = 0.f;
     if (e < 10)
+      #pragma unroll 8
       for (int cb = 0; cb < ncb; ++cb) gsum += dpart[((size_t)cb * T + tc) * DOT_STRIDE + e];
     const int base = (threadIdx.x & 63) & ~15;
     float g[4][4], D[4][4], Hp[4][4];
@@ -1101,6 +1104,7 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, i
     const int64_t j = g / gpr;
     const int p0 = (int)(g - j * gpr) * 4;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll 8
     for (int q = 0; q < nsplit; ++q) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(dwp + ((size_t)q * NC + j) * 48 + p0);
       s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
@@ -1115,6 +1119,7 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, i
     if (!db) return;
     const int p = bid - nb_dw;
     float s = 0.f;
+    #pragma unroll 8
     for (int t = threadIdx.x; t < T; t += 256) s += dz[(size_t)t * 48 + p];
     sm[threadIdx.x] = s;
     __syncthreads();
@@ -1132,6 +1137,7 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, i
   const int c = ok ? (int)(oid / 24) : 0, q = ok ? (int)(oid - (int64_t)c * 24) : 0;
   float s = 0.f;
   if (ok)
+    #pragma unroll 8
     for (int g = sub; g < nseg; g += RED_CONV_LANES) s += cpart[((size_t)g * C + c) * 24 + q];
   s += dpp_xor1(s);
   s += dpp_xor2(s);

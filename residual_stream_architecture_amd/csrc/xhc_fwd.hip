@@ -232,15 +232,23 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
     ss += row_xor<4>(ss);
     ss += row_xor<8>(ss);
     r = sqrtf(ss * inv_nc_total + eps);
+    // all partial loads issued together (SK <= 16; clamped indices, masked
+    // values), summed in split order
+    float z[3] = {0.f, 0.f, 0.f};
+    const int tcl = tv ? t : 0;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const float* zr = zpart + ((size_t)min(s, SK - 1) * T + tcl) * ZST;
+      float v[3];
+#pragma unroll
+      for (int n = 0; n < 3; ++n) v[n] = zr[min(e + 16 * n, ZST - 1)];
+#pragma unroll
+      for (int n = 0; n < 3; ++n) z[n] += s < SK ? v[n] : 0.f;
+    }
 #pragma unroll
     for (int n = 0; n < 3; ++n) {
       const int p = e + 16 * n;
-      float z = 0.f;
-      if (tv && p < P) {
-        for (int s = 0; s < SK; ++s) z += zpart[((size_t)s * T + t) * ZST + p];
-        z = z / r + (bias ? bias[p] : 0.f);
-      }
-      zs[tok][p] = z;
+      zs[tok][p] = (tv && p < P) ? z[n] / r + (bias ? bias[p] : 0.f) : 0.f;
     }
   } else {
     r = tv ? z_in[(size_t)t * (P + 1) + P] : 1.f;
@@ -264,6 +272,7 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
     // Gram-Schmidt folded into the post coefficients (nc == 4)
     float gsum = 0.f;
     if (e < 10)
+#pragma unroll 8
       for (int b = 0; b < ngram; ++b) gsum += gram[((size_t)b * T + t) * 16 + e];
     // the token's 16 lanes share one wave: every lane gathers the record
     const int base = (threadIdx.x & 63) & ~15;

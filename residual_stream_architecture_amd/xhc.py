@@ -59,6 +59,13 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m residual_stream_architecture_amd.build`")
+    # torch's HIP runtime must be in the process before the library: torch
+    # ships its own libamdhip64 and asks for it under another name, so when
+    # the library comes first and binds the system runtime, torch loads a
+    # second one, and the library's launches then run in a runtime that does
+    # not own torch's streams and memory.  Loaded after torch, the library's
+    # libamdhip64.so.7 resolves to the one already there.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     L.xhc_workspace_size.argtypes = [ctypes.POINTER(xhc_desc), ctypes.c_int]
     L.xhc_workspace_size.restype = ctypes.c_size_t
