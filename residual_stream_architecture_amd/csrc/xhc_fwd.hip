@@ -61,8 +61,8 @@ __global__ void k_pack_wt(const R* __restrict__ W, R* __restrict__ Wf, int C, in
 // Output zpart[split][t][0..16NT) = sum_c X[t,split,c] W[split*C+c, p],
 //        zpart[split][t][16NT]    = sum_c X[t,split,c]^2.
 // ---------------------------------------------------------------------------
-constexpr int PU = 2;     // K-steps per stage
-constexpr int PNS = 4;    // stages in the ring
+constexpr int PU = 1;     // K-steps per stage
+constexpr int PNS = 6;    // stages in the ring
 
 template <typename E, int NT>
 __global__ __launch_bounds__(64 * PROJ_WAVES) void k_proj(StreamRows src, const void* __restrict__ Wf,
