@@ -28,6 +28,8 @@ CASES = [
     ("k3_n7_f32", W_("g", 3, 30, 40, 7, 3, 4, "f32", "fwd"), [6, 1, 4], "sigmoid", "leaning"),
     ("wide_bf16", W_("g", 1, 130, 1040, 16, 4, 4, "bf16", "fwd"), [4, 5, 6, 7], "sigmoid", "leaning"),
     ("unit_f32", W_("g", 2, 25, 48, 6, 2, 4, "f32", "fwd"), [2, 5], "unit", "leaning"),
+    ("edge_c8_s1_f32", W_("g", 4, 1, 8, 16, 4, 4, "f32", "fwd"), [0, 1, 2, 3], "sigmoid", "leaning"),
+    ("edge_c8_s5_bf16", W_("g", 3, 5, 8, 4, 3, 4, "bf16", "fwd"), [3, 1, 2], "sigmoid", "leaning"),
 ]
 
 

@@ -24,6 +24,11 @@ CASES = [
     ("k2_f32", synth.Workload("k2", 3, 30, 40, 7, 2, 4, "f32", "fwd"), [6, 1], "sigmoid"),
     ("wide_bf16", synth.Workload("w", 1, 130, 1040, 16, 4, 4, "bf16", "fwd"), [4, 5, 6, 7], "sigmoid"),
     ("vanilla_f32", synth.Workload("v", 2, 20, 16, 1, 1, 1, "f32", "fwd"), [0], "unit"),
+    # edge shapes: the smallest C, one-token sequences (no TFA history), a
+    # two-token tail with two streams
+    ("edge_c8_s1_f32", synth.Workload("e1", 5, 1, 8, 16, 4, 4, "f32", "fwd"), [0, 5, 10, 15], "sigmoid"),
+    ("edge_c8_s3_bf16", synth.Workload("e2", 3, 3, 8, 2, 2, 4, "bf16", "fwd"), [1, 0], "sigmoid"),
+    ("edge_c24_s13_bf16", synth.Workload("e3", 1, 13, 24, 16, 4, 4, "bf16", "fwd"), [12, 13, 14, 15], "sigmoid"),
 ]
 
 
