@@ -271,7 +271,7 @@ def forward_bench(args, w, np, torch, synth, xhc):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no multi-GPU path.",
               file=sys.stderr, flush=True)
         sys.exit(2)
     import numpy as np
