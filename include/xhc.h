@@ -69,7 +69,7 @@ enum {
   XHC_ERR_INDEX = -3,        /* active index out of range or repeated       */
   XHC_ERR_ALIAS = -4,        /* forbidden overlap between buffers           */
   XHC_ERR_ALIGN = -5,        /* a pointer is not 16-byte aligned            */
-  XHC_ERR_UNSUPPORTED = -6,  /* a mode this build does not implement        */
+  XHC_ERR_UNSUPPORTED = -6,  /* a mode the library does not implement       */
   XHC_ERR_WORKSPACE = -7,    /* workspace NULL or smaller than required     */
   XHC_ERR_HIP = -8           /* a HIP call or kernel launch failed          */
 };
