@@ -159,6 +159,8 @@ ALT_CASES = [
     ("bf16_attn_mlp", W_("ca", 2, 45, 200, 16, 4, 4, "bf16", "stack"), [(4, 1), (4, 4), (4, 1), (4, 4)]),
     ("f32_n4_tiles_change", W_("cb", 3, 33, 72, 4, 4, 4, "f32", "stack"), [(4, 4), (4, 1), (2, 4), (3, 1)]),
     ("bf16_k_varies", W_("cc", 1, 130, 128, 16, 4, 4, "bf16", "stack"), [(4, 4), (2, 4), (3, 1)]),
+    # MLP-side sublayers with Gram-Schmidt over their four components
+    ("bf16_attn_mlp_gs", W_("cd", 2, 40, 136, 16, 4, 4, "bf16", "stack"), [(4, 1), (4, 4, True), (4, 1), (4, 4, True)]),
 ]
 
 
@@ -170,8 +172,9 @@ def test_chain_across_different_descriptions(name, w, spec):
     dt = torch.bfloat16 if bf16 else torch.float32
     T, N, C = w.T, w.N, w.C
     code = xhc.XHC_BF16 if bf16 else xhc.XHC_F32
-    ws = [dataclasses.replace(w, k=k, ncomp=nc, layers=1) for k, nc in spec]
-    descs = [xhc.make_desc(w.B, w.S, C, N, k, nc, code) for k, nc in spec]
+    spec = [tuple(sp) + (False,) * (3 - len(sp)) for sp in spec]
+    ws = [dataclasses.replace(w, k=k, ncomp=nc, layers=1, gs=gs) for k, nc, gs in spec]
+    descs = [xhc.make_desc(w.B, w.S, C, N, k, nc, code, gram_schmidt=gs) for k, nc, gs in spec]
     params = [layer_params(wl, l, 0.2) for l, wl in enumerate(ws)]
     X = to_dev(synth.make_inputs(w, seed=0)["X"], bf16)
     nbytes = max(xhc.carry_size(dsc) for dsc in descs)
@@ -190,7 +193,8 @@ def test_chain_across_different_descriptions(name, w, spec):
                     carry_out=None if last else carries[(l + 1) % 2],
                     desc_next=None if last else descs[l + 1], **conv_kw(p, wl))
         torch.cuda.synchronize()
-        ref = xo.forward(Xh, h["out"], h["W"], h["bias"], active, h["convs"], B=w.B, S=w.S)
+        ref = xo.forward(Xh, h["out"], h["W"], h["bias"], active, h["convs"], B=w.B, S=w.S,
+                         gram_schmidt_on=wl.gs)
         got = to_host(X)
         inactive = [i for i in range(N) if i not in active]
         assert np.array_equal(got[:, inactive], Xh[:, inactive]), f"layer {l}: pass-through rows differ"
