@@ -24,24 +24,31 @@ namespace xhc {
 // logit tile n, one 512-element block in which lane l holds the 8 channels
 // 8*(l/16) .. +8 of logit column 16n + l%16.  A wave then loads one B
 // fragment as one contiguous 1 KiB access.  Entries past C or P are zero.
+// One workgroup per (i, ks): the 32 x P source rows are one contiguous run
+// of W, read coalesced into LDS, and the NT fragments are written from there
+// as 8-element vectors.
 // ---------------------------------------------------------------------------
 template <typename R>
-__global__ void k_pack_wt(const R* __restrict__ W, R* __restrict__ Wf, int C, int P, int NT, int nks, int64_t nfrag) {
-  const int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (i, ks, n, lane)
-  if (f >= nfrag) return;
-  const int lane = (int)(f & 63);
-  const int64_t blk = f >> 6;
-  const int n = (int)(blk % NT);
-  const int64_t iks = blk / NT;
-  const int ks = (int)(iks % nks);
-  const int64_t i = iks / nks;
-  const int p = 16 * n + (lane & 15);
-  const int c0 = ks * 32 + 8 * (lane >> 4);
-  R* dst = Wf + f * 8;
+__global__ __launch_bounds__(256) void k_pack_wt(const R* __restrict__ W, R* __restrict__ Wf, int C, int P, int NT,
+                                                 int nks) {
+  __shared__ R tile[32][16 * NT_MAX + 1];
+  const int i = blockIdx.x / nks, ks = blockIdx.x - (blockIdx.x / nks) * nks;
+  const int c0 = ks * 32;
+  const int rows = min(32, C - c0);
+  const R* src = W + ((size_t)i * C + c0) * P;
+  for (int idx = threadIdx.x; idx < 32 * P; idx += 256) {
+    const int rr = idx / P, pp = idx - (idx / P) * P;
+    tile[rr][pp] = rr < rows ? src[idx] : R(0);
+  }
+  __syncthreads();
+  R* dst = Wf + (size_t)blockIdx.x * NT * 512;
+  for (int idx = threadIdx.x; idx < NT * 64; idx += 256) {
+    const int n = idx >> 6, l = idx & 63;
+    const int p = 16 * n + (l & 15), r0 = 8 * (l >> 4);
+    R v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = c0 + e;
-    dst[e] = (p < P && c < C) ? W[((size_t)i * C + c) * P + p] : R(0);
+    for (int e = 0; e < 8; ++e) v[e] = p < P ? tile[r0 + e][p] : R(0);
+    __builtin_memcpy(dst + (size_t)idx * 8, v, sizeof(v));
   }
 }
 
@@ -512,9 +519,7 @@ template <typename R>
 static void launch_pack_wt(const Plan& p, const void* W, void* Wf, hipStream_t st, xhc_timer* tm) {
   TimedLaunch tl(tm, KID_PACK_WT, st);
   const int nks = (p.C + 31) / 32;
-  const int64_t nfrag = (int64_t)p.N * nks * p.NT * 64;
-  k_pack_wt<R><<<(int)((nfrag + 255) / 256), 256, 0, st>>>(static_cast<const R*>(W), static_cast<R*>(Wf), p.C, p.P,
-                                                           p.NT, nks, nfrag);
+  k_pack_wt<R><<<p.N * nks, 256, 0, st>>>(static_cast<const R*>(W), static_cast<R*>(Wf), p.C, p.P, p.NT, nks);
 }
 
 template <typename E>
