@@ -191,6 +191,7 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
 // the Gram record at 0..10 (BD_GRAM: dpart[cb][t][16], Gram at 0..10).
 // ---------------------------------------------------------------------------
 enum { BD_FULL = 0, BD_GSDOTS = 1, BD_GSGRAD = 2, BD_GRAM = 3 };
+constexpr int GRAM_SPLIT = 8;   // segments of the forward Gram pass per backward segment
 
 // Sum of 16 per-lane values over the wave by halving exchanges (lanes are
 // paired by xor 32, 16, 15, 7, then quads are summed): afterwards lane l with
@@ -1248,17 +1249,21 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
 
 void launch_gram(const Plan& p, const void* out, const float* w4, const float* w8, const float* w12, float* gram,
                  hipStream_t st) {
-  const dim3 grid(p.b1_cblocks, p.B * p.b1_segs);
+  // GRAM_SPLIT times the backward's segments: the pass needs few registers,
+  // and more, shorter segments keep more waves in flight
+  const int lseg = std::max(12, (p.b1_lseg / GRAM_SPLIT + 11) / 12 * 12);
+  const int segs = (p.S + lseg - 1) / lseg;
+  const dim3 grid(p.b1_cblocks, p.B * segs);
   StreamRows none{};
   Act4 act{};
   if (p.dtype == XHC_BF16)
     k_bdots<BF16, 4, false, BD_GRAM><<<grid, 256, 0, st>>>(none, nullptr, nullptr, out, w4, w8, w12, nullptr, nullptr,
                                                            gram, nullptr, nullptr, p.T, p.S, p.C, p.N, p.k, act,
-                                                           p.b1_lseg, p.b1_segs);
+                                                           lseg, segs);
   else
     k_bdots<F32, 4, false, BD_GRAM><<<grid, 256, 0, st>>>(none, nullptr, nullptr, out, w4, w8, w12, nullptr, nullptr,
                                                           gram, nullptr, nullptr, p.T, p.S, p.C, p.N, p.k, act,
-                                                          p.b1_lseg, p.b1_segs);
+                                                          lseg, segs);
 }
 
 int launch_backward(const Plan& p, const xhc_bwd_args* a, void* ws, hipStream_t st) {
