@@ -1151,6 +1151,8 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, i
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
+static void dots_segments(const Plan& p, int& lseg, int& segs);
+
 template <typename E, typename R>
 static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStream_t st) {
   xhc_timer* tm = a->timer;
@@ -1192,7 +1194,17 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   {
     TimedLaunch tl(tm, KID_BDOTS, st);
     if (p.gs) {
-      if (fast) XHC_BDOTS(4, true, BD_GSDOTS); else XHC_BDOTS(4, false, BD_GSDOTS);
+      int lseg, segs;
+      dots_segments(p, lseg, segs);
+      const dim3 g2(p.b1_cblocks, p.B * segs);
+      if (fast)
+        k_bdots<E, 4, true, BD_GSDOTS><<<g2, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12,
+                                                           hpost, gss, dpart, a->dout, dwpart, p.T, p.S, p.C, p.N,
+                                                           p.k, act, lseg, segs);
+      else
+        k_bdots<E, 4, false, BD_GSDOTS><<<g2, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12,
+                                                            hpost, gss, dpart, a->dout, dwpart, p.T, p.S, p.C, p.N,
+                                                            p.k, act, lseg, segs);
     } else if (p.nc == 4) {
       if (fast) XHC_BDOTS(4, true, BD_FULL); else XHC_BDOTS(4, false, BD_FULL);
     } else {
@@ -1247,12 +1259,18 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
 }
 
+// Segments of the passes that write per-token records only (BD_GRAM,
+// BD_GSDOTS): GRAM_SPLIT times the backward's, as these passes need few
+// registers and more, shorter segments keep more waves in flight.
+static void dots_segments(const Plan& p, int& lseg, int& segs) {
+  lseg = std::max(12, (p.b1_lseg / GRAM_SPLIT + 11) / 12 * 12);
+  segs = (p.S + lseg - 1) / lseg;
+}
+
 void launch_gram(const Plan& p, const void* out, const float* w4, const float* w8, const float* w12, float* gram,
                  hipStream_t st) {
-  // GRAM_SPLIT times the backward's segments: the pass needs few registers,
-  // and more, shorter segments keep more waves in flight
-  const int lseg = std::max(12, (p.b1_lseg / GRAM_SPLIT + 11) / 12 * 12);
-  const int segs = (p.S + lseg - 1) / lseg;
+  int lseg, segs;
+  dots_segments(p, lseg, segs);
   const dim3 grid(p.b1_cblocks, p.B * segs);
   StreamRows none{};
   Act4 act{};
