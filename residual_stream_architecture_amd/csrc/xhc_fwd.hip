@@ -68,10 +68,10 @@ __global__ __launch_bounds__(256) void k_pack_wt(const R* __restrict__ W, R* __r
 // Output zpart[split][t][0..16NT) = sum_c X[t,split,c] W[split*C+c, p],
 //        zpart[split][t][16NT]    = sum_c X[t,split,c]^2.
 // ---------------------------------------------------------------------------
-constexpr int PU = 1;     // K-steps per stage
-constexpr int PNS = 6;    // stages in the ring
-
-template <typename E, int NT>
+// PU K-steps per stage, PNS stages in the ring: one K-step in a six-deep ring
+// when the grid has several workgroups per CU (N >= 8 stream splits), two in
+// a four-deep ring when it has one (more bytes in flight per workgroup).
+template <typename E, int NT, int PU, int PNS>
 __global__ __launch_bounds__(64 * PROJ_WAVES) void k_proj(StreamRows src, const void* __restrict__ Wf,
                                                           float* __restrict__ zpart, int T, int C, int ZST,
                                                           int ntiles) {
@@ -527,12 +527,14 @@ static void launch_proj(const Plan& p, const StreamRows& src, const void* Wf, fl
                         xhc_timer* tm) {
   TimedLaunch tl(tm, KID_PROJ, st);
   const int nb = p.proj_tiles * p.SK;
-  if (p.NT == 1)
-    k_proj<E, 1><<<nb, 64 * PROJ_WAVES, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles);
-  else if (p.NT == 2)
-    k_proj<E, 2><<<nb, 64 * PROJ_WAVES, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles);
-  else
-    k_proj<E, 3><<<nb, 64 * PROJ_WAVES, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles);
+#define XHC_PROJ(NT, PU, PNS) \
+  k_proj<E, NT, PU, PNS><<<nb, 64 * PROJ_WAVES, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles)
+  if (p.SK >= 8) {
+    if (p.NT == 1) XHC_PROJ(1, 1, 6); else if (p.NT == 2) XHC_PROJ(2, 1, 6); else XHC_PROJ(3, 1, 6);
+  } else {
+    if (p.NT == 1) XHC_PROJ(1, 2, 4); else if (p.NT == 2) XHC_PROJ(2, 2, 4); else XHC_PROJ(3, 2, 4);
+  }
+#undef XHC_PROJ
 }
 
 template <typename E, typename R>
