@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-chain", action="store_true",
                     help="stacked workloads: project every sublayer's state in its own pass instead of "
                          "carrying the projection from the previous sublayer's write pass")
+    ap.add_argument("--graph", action="store_true",
+                    help="fwd+bwd: capture one step in a HIP graph (torch.cuda.CUDAGraph) and time its replays")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 2 GiB device copy (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -331,14 +333,33 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # the library launches only kernels on the current stream, so one
+        # step captures whole; replays redo the same work on the same buffers
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T * args.steps / elapsed
-    print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    print(f"# timed {args.steps} steps{' (graph replays)' if args.graph else ''}: {ms_per_step:.3f} ms/step",
+          file=sys.stderr, flush=True)
 
     # per-kernel durations from HIP events recorded on the launch stream
     kernels = {}
