@@ -27,7 +27,8 @@
  *             w_m[c, K_m - 1] multiplies the current token)     (TFA)
  *     X_new[t, i_a]  = sum_b H_res[a, b] X[t, i_b] + sum_m H_post[a, m] U_m[t]
  *     X_new[t, i]    = X[t, i] for i not active        (sparse write, bitwise)
- *   with i_a = active[a], a < k.
+ *   with i_a = active[a], a < k.  With desc->gram_schmidt = 1 the write uses
+ *   the orthogonalised components U~ (see xhc_desc) in place of U.
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless a field says HOST.  The caller owns
@@ -203,9 +204,11 @@ typedef struct {
 size_t xhc_carry_size(const xhc_desc* desc);
 
 /* xhc_forward with the chaining of xhc_chain_args.  chain == NULL behaves
- * as xhc_forward.  Same workspace as xhc_forward; the carry buffers are the
- * caller's.  Errors as xhc_forward, plus XHC_ERR_NULL for W_next without
- * carry_out and XHC_ERR_ALIAS for a carry overlapping another buffer. */
+ * as xhc_forward.  Same workspace as xhc_forward (whatever desc_next is); the
+ * carry buffers are the caller's.  Errors as xhc_forward, plus XHC_ERR_NULL
+ * for W_next without carry_out, XHC_ERR_ALIAS for a carry overlapping another
+ * buffer and XHC_ERR_SHAPE for a desc_next that does not describe the same
+ * state (B, S, C, N, dtype) or is invalid. */
 int xhc_forward_chain(const xhc_desc* desc, const xhc_fwd_args* args,
                       const xhc_chain_args* chain, void* workspace,
                       size_t workspace_bytes, xhc_stream_t stream);
