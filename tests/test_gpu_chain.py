@@ -38,6 +38,7 @@ CHAIN_CASES = [
     # N = 16 with k < 4: a chunk's first step holds active and untouched rows
     ("bf16_n16_k2", W_("ck", 2, 70, 192, 16, 2, 4, "bf16", "stack", layers=3), True, True, False, 0.1),
     ("bf16_n16_k3_nc1", W_("cl", 1, 100, 128, 16, 3, 1, "bf16", "stack", layers=2), False, False, True, 0.0),
+    ("bf16_n16_k1", W_("cu", 2, 60, 128, 16, 1, 4, "bf16", "stack", layers=3), True, True, False, 0.2),
     # edge shapes: the smallest C, one-token sequences
     ("f32_c8_s1", W_("cs", 6, 1, 8, 16, 4, 4, "f32", "stack", layers=3), True, True, False, 0.0),
     ("bf16_c8_s2", W_("ct", 3, 2, 8, 5, 2, 4, "bf16", "stack", layers=2), False, True, True, 0.1),

@@ -29,6 +29,8 @@ CASES = [
     ("edge_c8_s1_f32", synth.Workload("e1", 5, 1, 8, 16, 4, 4, "f32", "fwd"), [0, 5, 10, 15], "sigmoid"),
     ("edge_c8_s3_bf16", synth.Workload("e2", 3, 3, 8, 2, 2, 4, "bf16", "fwd"), [1, 0], "sigmoid"),
     ("edge_c24_s13_bf16", synth.Workload("e3", 1, 13, 24, 16, 4, 4, "bf16", "fwd"), [12, 13, 14, 15], "sigmoid"),
+    # one active stream of 16
+    ("k1_n16_bf16", synth.Workload("k1", 2, 50, 192, 16, 1, 4, "bf16", "fwd"), [9], "sigmoid"),
     # a wide, ragged C: many channel blocks, a partial last block everywhere
     ("wide_c8200_bf16", synth.Workload("wc", 1, 40, 8200, 16, 4, 4, "bf16", "fwd"), [1, 6, 11, 14], "sigmoid"),
 ]
