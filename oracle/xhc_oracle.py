@@ -66,6 +66,22 @@ shared with the GPU library and listed in the design notes):
       component -- the zero-initialised conv branches at the start of
       training -- from dividing 0 by 0; with it such a component stays 0.
       The write uses u~ in place of U.
+  O7  router (optional, [R-DRSW], the paragraphs on fixed and routed
+      streams, the sigmoid router and its gradient): the first k - R
+      entries of `active` are fixed streams, written at every token; the
+      other R slots are chosen per token.  The router reads the flattened
+      state through a LayerNorm without affine parameters (a gain and a
+      shift fold into W_route and b_route):
+        y = (xbar - mean(xbar)) / sqrt(var(xbar) + eps),  var the population
+        variance, eps the RMS epsilon;  rho = y @ W_route + b_route  (N scores)
+      and s = sigmoid(rho).  Slot k - R + j (j = 0 .. R-1) takes the stream
+      with the (j+1)-th largest rho among the streams that are not fixed;
+      equal scores go to the lower stream id first.  A routed slot's
+      write-back is scaled by its score:
+        X'[t, i_a] = sum_b H_res[a, b] X[t, i_b] + s_a sum_c H_post[a, c] u~_c
+      (s_a = 1 for a fixed slot).  The choice itself is discrete: only the
+      chosen streams' scores receive a gradient, through s_a.  R = 0 is the
+      fixed active list of O5.
 """
 
 import numpy as np
@@ -177,8 +193,56 @@ def gram_schmidt(U, gs_eps):
     return Ut, steps
 
 
+def layer_norm_flat(Xf, eps):
+    """O7: LayerNorm of each token's flattened state, no affine parameters.
+
+    Xf: [T, N*C].  Returns y [T, N*C], mean [T], sd [T]
+    (sd = sqrt(population variance + eps)).
+    """
+    mu = Xf.mean(axis=1)
+    d = Xf - mu[:, None]
+    sd = np.sqrt(np.mean(d * d, axis=1) + eps)
+    return d / sd[:, None], mu, sd
+
+
+def route_select(rho, fixed, R):
+    """O7: per-token active list -- the fixed streams, then the R streams
+    that are not fixed with the largest router scores, largest first, equal
+    scores to the lower stream id.  rho: [T, N].  Returns idx [T, k]."""
+    T, N = rho.shape
+    fixed = [int(i) for i in fixed]
+    cand = np.array([i for i in range(N) if i not in fixed], dtype=np.int64)
+    order = np.argsort(-rho[:, cand], axis=1, kind="stable")[:, :R]
+    idx = np.empty((T, len(fixed) + R), dtype=np.int64)
+    idx[:, :len(fixed)] = fixed
+    idx[:, len(fixed):] = cand[order]
+    return idx
+
+
+def router(Xf, W_route, b_route, active, R, eps, route_idx=None):
+    """O7: router scores, per-token active lists and write-back scales.
+
+    Returns dict(idx [T,k], rho [T,N], s [T,k], y, mu, sd).  route_idx, if
+    given, replaces the top-R choice (for checking another implementation's
+    choice at near ties); the scores still come from rho.
+    """
+    T = Xf.shape[0]
+    k = len(active)
+    y, mu, sd = layer_norm_flat(Xf, eps)
+    rho = y @ W_route + b_route[None, :]
+    if route_idx is None:
+        idx = route_select(rho, list(active)[:k - R], R)
+    else:
+        idx = np.asarray(route_idx, dtype=np.int64).reshape(T, k)
+    s = np.ones((T, k))
+    if R:
+        s[:, k - R:] = sigmoid(np.take_along_axis(rho, idx[:, k - R:], axis=1))
+    return dict(idx=idx, rho=rho, s=s, y=y, mu=mu, sd=sd)
+
+
 def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
-            gate_mode="sigmoid", gram_schmidt_on=False, gs_eps=1e-6):
+            gate_mode="sigmoid", gram_schmidt_on=False, gs_eps=1e-6,
+            route=0, W_route=None, b_route=None, route_idx=None):
     """One xHC sublayer update, forward ([R-DRSW] write formula, O1-O5).
 
     X:      [B*S, N, C]  residual state before the update
@@ -186,12 +250,16 @@ def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
     W:      [N*C, P]     projection weights, rows indexed i*C + c
     bias:   [P] or None
     active: k distinct stream ids; row/column a of H_res and row a of H_post
-            bind to active[a]
+            bind to active[a] (with route = R > 0 only the first k - R are
+            used: the fixed streams of O7)
     conv_ws: (w4, w8, w12) with shapes [C,4], [C,8], [C,12], or () for one
             write-back component
+    route, W_route [N*C, N], b_route [N] or None, route_idx: the router of
+            O7 (route = number of routed slots)
 
     Returns a dict with X_new, h_in and the intermediates (z, r, H_pre,
-    H_post, H_res, U).
+    H_post, H_res, U, idx [T, k] the per-token active list, s [T, k] the
+    write-back scales, and with a router rho, mu, sd).
     """
     X = np.asarray(X, dtype=np.float64)
     out = np.asarray(out, dtype=np.float64)
@@ -224,13 +292,35 @@ def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
     if gram_schmidt_on:
         U, _ = gram_schmidt(U, gs_eps)
 
+    # the per-token active list: fixed, or fixed + routed (O7)
+    rt = _route(X.reshape(T, N * C), active, route, W_route, b_route, eps, route_idx)
+    idx, s = rt["idx"], rt["s"]
+
     # sparse write: only the k active streams are rewritten
     X_new = X.copy()
-    Xa = X[:, list(active), :]                                    # [T, k, C]
-    X_new[:, list(active), :] = (np.einsum("tab,tbc->tac", H_res, Xa)
-                                 + np.einsum("tam,tmc->tac", H_post, U))
-    return dict(X_new=X_new, h_in=h_in, z=z, r=r, H_pre=H_pre,
-                H_post=H_post, H_res=H_res, U=U)
+    tok = np.arange(T)[:, None]
+    Xa = X[tok, idx, :]                                           # [T, k, C]
+    X_new[tok, idx, :] = (np.einsum("tab,tbc->tac", H_res, Xa)
+                          + s[:, :, None] * np.einsum("tam,tmc->tac", H_post, U))
+    res = dict(X_new=X_new, h_in=h_in, z=z, r=r, H_pre=H_pre,
+               H_post=H_post, H_res=H_res, U=U)
+    res.update(rt)
+    return res
+
+
+def _route(Xf, active, route, W_route, b_route, eps, route_idx):
+    """The per-token active list and scales: O5's fixed list (route = 0) or
+    O7's router."""
+    T, NC = Xf.shape
+    k = len(active)
+    if not route:
+        return dict(idx=np.tile(np.asarray(active, dtype=np.int64), (T, 1)), s=np.ones((T, k)))
+    assert 0 < route <= k
+    W_route = np.asarray(W_route, dtype=np.float64)
+    N = W_route.shape[1]
+    assert W_route.shape == (NC, N) and route <= N - (k - route)
+    b_route = np.zeros(N) if b_route is None else np.asarray(b_route, dtype=np.float64)
+    return router(Xf, W_route, b_route, active, route, eps, route_idx)
 
 
 # --------------------------------------------------------------------------
@@ -306,11 +396,13 @@ def gram_schmidt_backward(U, gs_eps, dUt):
 
 
 def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
-             iters=20, eps=1e-6, gate_mode="sigmoid", gram_schmidt_on=False, gs_eps=1e-6):
+             iters=20, eps=1e-6, gate_mode="sigmoid", gram_schmidt_on=False, gs_eps=1e-6,
+             route=0, W_route=None, b_route=None, route_idx=None):
     """Gradients of the forward above for upstream gradients dX_new, dh_in.
 
     Returns dict(dX [T,N,C], dout [T,C], dW [N*C,P], db [P],
-    dconv [list of [C,K]], dz [T,P]).
+    dconv [list of [C,K]], dz [T,P]; with a router also dW_route [N*C,N],
+    db_route [N], drho [T,N] and idx).
     """
     X = np.asarray(X, dtype=np.float64)
     out = np.asarray(out, dtype=np.float64)
@@ -336,17 +428,21 @@ def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
     U_raw = tfa_components(out, B, S, conv_ws)
     U = gram_schmidt(U_raw, gs_eps)[0] if gram_schmidt_on else U_raw
 
-    G = dX_new[:, act, :]                                         # [T, k, C]
-    Xa = X[:, act, :]
+    rt = _route(Xf, act, route, W_route, b_route, eps, route_idx)
+    idx, s = rt["idx"], rt["s"]
+    tok = np.arange(T)[:, None]
+    G = dX_new[tok, idx, :]                                       # [T, k, C]
+    Xa = X[tok, idx, :]
 
     # pass-through rows keep their upstream gradient; rewritten rows do not
     dX = dX_new.copy()
-    dX[:, act, :] = 0.0
-    # through the mixing term and the write-back term
+    dX[tok, idx, :] = 0.0
+    # through the mixing term and the write-back term (scaled by s)
     dH_res = np.einsum("tac,tbc->tab", G, Xa)
-    dX[:, act, :] += np.einsum("tab,tac->tbc", H_res, G)
-    dH_post = np.einsum("tac,tmc->tam", G, U)
-    dU = np.einsum("tam,tac->tmc", H_post, G)
+    dX[tok, idx, :] += np.einsum("tab,tac->tbc", H_res, G)
+    dq = np.einsum("tac,tmc->tam", G, U)            # gradient of s_a H_post[a, m]
+    dH_post = s[:, :, None] * dq
+    dU = np.einsum("tam,tac->tmc", s[:, :, None] * H_post, G)
     # through the dense read
     dH_pre = np.einsum("tc,tic->ti", dh_in, X)
     dX += H_pre[:, :, None] * dh_in[:, None, :]
@@ -370,6 +466,21 @@ def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
     dXf = (dxhat - xhat * (np.sum(dxhat * xhat, axis=1, keepdims=True) / n)) / r[:, None]
     dX += dXf.reshape(T, N, C)
 
+    # through the router's scales, then its LayerNorm (O7)
+    extra = {}
+    if route:
+        ds = np.sum(H_post * dq, axis=2)                         # [T, k]
+        drho = np.zeros((T, N))
+        sr = s[:, k - route:]
+        drho[tok, idx[:, k - route:]] = ds[:, k - route:] * sr * (1.0 - sr)
+        Wr = np.asarray(W_route, dtype=np.float64)
+        y, sd = rt["y"], rt["sd"]
+        dy = drho @ Wr.T
+        dXr = (dy - dy.mean(axis=1, keepdims=True)
+               - y * np.mean(dy * y, axis=1, keepdims=True)) / sd[:, None]
+        dX += dXr.reshape(T, N, C)
+        extra = dict(dW_route=y.T @ drho, db_route=drho.sum(axis=0), drho=drho, idx=idx)
+
     # through Gram-Schmidt, then temporal feature augmentation
     if gram_schmidt_on:
         dU = gram_schmidt_backward(U_raw, gs_eps, dU)
@@ -380,4 +491,6 @@ def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
         d_o, d_w = causal_depthwise_conv_backward(out_bsc, w, dU[:, m + 1, :].reshape(B, S, C))
         dout += d_o.reshape(T, C)
         dconv.append(d_w)
-    return dict(dX=dX, dout=dout, dW=dW, db=db, dconv=dconv, dz=dz)
+    res = dict(dX=dX, dout=dout, dW=dW, db=db, dconv=dconv, dz=dz)
+    res.update(extra)
+    return res
