@@ -28,7 +28,9 @@
  *     X_new[t, i_a]  = sum_b H_res[a, b] X[t, i_b] + sum_m H_post[a, m] U_m[t]
  *     X_new[t, i]    = X[t, i] for i not active        (sparse write, bitwise)
  *   with i_a = active[a], a < k.  With desc->gram_schmidt = 1 the write uses
- *   the orthogonalised components U~ (see xhc_desc) in place of U.
+ *   the orthogonalised components U~ (see xhc_desc) in place of U.  With
+ *   desc->route = R > 0 the last R of the k active streams are chosen per
+ *   token by a router and their write-back term is scaled (see xhc_desc).
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless a field says HOST.  The caller owns
@@ -89,7 +91,24 @@ enum {
  * the write then uses U~ in place of U.  No normalisation.  gs_eps > 0 keeps
  * a zero component (zero conv weights) at 0.  With ncomp == 1 it is the
  * identity.  A description with gram_schmidt = 0 (a zero-filled tail) is the
- * form without it, which the pages use when the backbone trains with Muon. */
+ * form without it, which the pages use when the backbone trains with Muon.
+ *
+ * Router (route = R > 0; source: the retrospective's section "模型可以拥有
+ * 16 条 streams，但每层只更新 4 条", the paragraphs on fixed and routed
+ * streams and on the sigmoid router): active[0 .. k-R) are fixed streams,
+ * written at every token; slots k-R .. k-1 are chosen per token.  Scores
+ *   y   = (xbar - mean(xbar)) / sqrt(var(xbar) + rms_eps)  (LayerNorm of the
+ *         flattened state, population variance, no affine parameters: a gain
+ *         and a shift fold into W_route and b_route)
+ *   rho = y @ W_route + b_route                             rho in R^N
+ * slot k-R+j takes the stream with the (j+1)-th largest rho among the
+ * N-(k-R) streams that are not fixed (equal scores: lower stream id first;
+ * the choice is made on fp32 scores), and its write-back term is scaled by
+ * s = sigmoid(rho):  X_new[t, i_a] = sum_b H_res[a,b] X[t, i_b]
+ * + s_a sum_m H_post[a,m] U_m.  The choice is discrete: the gradient reaches
+ * the chosen streams' scores through s only.  Supported with at most 15
+ * candidate streams (N - (k-R) <= 15, so at N = 16 at least one fixed
+ * stream) and 1 <= R <= k; not with the chained forward. */
 typedef struct {
   int32_t B, S, C, N, k, ncomp;
   int32_t sinkhorn_iters;   /* Sinkhorn row+column steps (20 by default)    */
@@ -99,6 +118,9 @@ typedef struct {
                                H_pre = H_post = 1, no gate gradient)        */
   int32_t gram_schmidt;     /* 0: off; 1: modified Gram-Schmidt over U      */
   float gs_eps;             /* > 0 and finite when gram_schmidt = 1 (1e-6)  */
+  int32_t route;            /* 0: the active list of every token is `active`;
+                               R > 0: R routed slots (the retrospective's
+                               setting is k = 4, R = 2)                     */
 } xhc_desc;
 
 /* Optional per-kernel timer (HIP events around every kernel a call
@@ -113,17 +135,25 @@ typedef struct {
   const float* w12;    /* [C,12] }                                            */
   const void* W;       /* [N*C,P] projection weights, row i*C + c             */
   const float* bias;   /* [P] or NULL (zero)                                  */
-  const int32_t* active; /* HOST [k] distinct stream ids; order binds row a   */
+  const int32_t* active; /* HOST [k] distinct stream ids; order binds row a.
+                          With route = R > 0 only the first k-R are read    */
   void* X_new;         /* [T,N,C]; == X: in place, only the k active rows are
                           written; otherwise must not overlap X and all N rows
                           are written (inactive rows copied bitwise)          */
   void* h_in;          /* [T,C] dense-read sublayer input; no overlap with X,
                           X_new, out                                          */
-  float* z_save;       /* [T,P+1] logits z and r per token, or NULL; the
+  float* z_save;       /* [T, xhc_zsave_stride(desc)] per token: logits z, r
+                          (and with a router its record), or NULL; the
                           backward needs it                                   */
-  void* xact_save;     /* [T,k,C] the k active rows of X before the update, or
-                          NULL; the backward needs it after an in-place call  */
+  void* xact_save;     /* [T,k,C] the k active rows of X before the update
+                          (slot order), or NULL; the backward needs it after
+                          an in-place call without a router                   */
   xhc_timer* timer;    /* NULL, or a timer from xhc_timer_create             */
+  /* router (read only when desc->route > 0) */
+  const void* W_route; /* [N*C,N] router weights, storage type, row i*C + c   */
+  const float* b_route;  /* [N] or NULL (zero)                                */
+  int32_t* route_idx;  /* [T,k] per-token active list (output), or NULL; the
+                          backward needs it                                   */
 } xhc_fwd_args;
 
 typedef struct {
@@ -135,7 +165,8 @@ typedef struct {
   const void* W;       /* [N*C,P]                                             */
   const float* bias;   /* [P] or NULL                                         */
   const int32_t* active;  /* HOST [k], the forward's active list              */
-  const float* z_save; /* [T,P+1] from the forward, or NULL (recomputed)      */
+  const float* z_save; /* [T, xhc_zsave_stride(desc)] from the forward, or
+                          NULL (recomputed; not with a router)                */
   const void* dX_new;  /* [T,N,C] gradient w.r.t. X_new                       */
   const void* dh_in;   /* [T,C] gradient w.r.t. h_in                          */
   void* dX;            /* [T,N,C] gradient w.r.t. X; may be == dX_new, must
@@ -144,13 +175,26 @@ typedef struct {
   float* dW;           /* [N*C,P] fp32                                        */
   float* db;           /* [P] fp32, or NULL                                   */
   float *dw4, *dw8, *dw12;  /* fp32 conv-weight gradients; NULL iff ncomp == 1 */
-  int32_t accumulate;  /* 0: overwrite dW/db/dw*; 1: add to them              */
+  int32_t accumulate;  /* 0: overwrite dW/db/dw* (and dW_route/db_route);
+                          1: add to them                                      */
   xhc_timer* timer;
+  /* router (read only when desc->route > 0; then X must be the forward's
+     input, xact NULL and z_save the forward's) */
+  const void* W_route; /* [N*C,N]                                             */
+  const int32_t* route_idx;  /* [T,k] the forward's per-token active list     */
+  float* dW_route;     /* [N*C,N] fp32                                        */
+  float* db_route;     /* [N] fp32, or NULL                                   */
 } xhc_bwd_args;
 
 /* Bytes of device workspace the call needs (phase XHC_PHASE_FWD or
  * XHC_PHASE_BWD); 0 for an invalid description.  Pure host code. */
 size_t xhc_workspace_size(const xhc_desc* desc, int phase);
+
+/* Floats per token of z_save: P + 1 (logits, r) without a router; with
+ * route = R > 0, P + 3 + 3R: logits, r, the LayerNorm mean and sd, then per
+ * routed slot its score rho, rho - b_route and the column sum of W_route of
+ * the chosen stream.  0 for an invalid description.  Pure host code. */
+int32_t xhc_zsave_stride(const xhc_desc* desc);
 
 /* Checks desc and args (an xhc_fwd_args* or xhc_bwd_args* per phase):
  * NULLs, shapes, indices, aliasing, alignment.  Pure host code, no HIP

@@ -270,7 +270,8 @@ def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
     ncomp = 1 + len(conv_ws)
     P = n_logits(N, k, ncomp)
     assert T == B * S and out.shape == (T, C) and W.shape == (N * C, P)
-    assert len(set(int(a) for a in active)) == k and all(0 <= a < N for a in active)
+    fixed = list(active)[:k - route]          # with a router only the fixed prefix is read
+    assert len(set(int(a) for a in fixed)) == len(fixed) and all(0 <= a < N for a in fixed)
     bias = np.zeros(P) if bias is None else np.asarray(bias, dtype=np.float64)
 
     # coefficients from the full flattened state (dense read of all streams)

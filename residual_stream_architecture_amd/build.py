@@ -10,7 +10,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["xhc_api.cpp", "xhc_fwd.hip", "xhc_bwd.hip", "xhc_chain.hip"]
+SOURCES = ["xhc_api.cpp", "xhc_fwd.hip", "xhc_bwd.hip", "xhc_chain.hip", "xhc_route.hip"]
 LIB = os.path.join(PKG, "libxhc.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 

@@ -29,6 +29,9 @@ int make_plan(const xhc_desc* d, Plan* p) {
   if (d->gram_schmidt && !(d->gs_eps > 0.f && std::isfinite(d->gs_eps))) return XHC_ERR_SHAPE;
   const int64_t T = (int64_t)d->B * d->S;
   if (T * d->N * (int64_t)d->C >= ((int64_t)1 << 31)) return XHC_ERR_SHAPE;
+  if (d->route < 0 || d->route > d->k) return XHC_ERR_SHAPE;
+  // the router's candidates and the LayerNorm sum share one logit tile
+  if (d->route > 0 && d->N - (d->k - d->route) > 15) return XHC_ERR_UNSUPPORTED;
 
   Plan& q = *p;
   q.B = d->B; q.S = d->S; q.C = d->C; q.N = d->N; q.k = d->k; q.nc = d->ncomp;
@@ -40,6 +43,14 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.esz = q.dtype == XHC_BF16 ? 2 : 4;
   q.gs = d->gram_schmidt == 1 && q.nc == 4;
   q.gs_ceps = q.gs ? (float)q.C * d->gs_eps : 0.f;
+  q.R = d->route;
+  q.nfix = q.k - q.R;
+  q.ncand = q.R ? q.N - q.nfix : 0;
+  if (q.R) q.NT = 4;                       // tile 3: router candidates + sum(x)
+  q.zsv = q.R ? q.P + 3 + 3 * q.R : q.P + 1;
+  q.dzs = q.R ? DZ_R : 48;
+  q.dwr = q.R ? 64 : 48;
+  q.rec_bytes = q.R ? REC_R_BYTES : REC_BYTES;
 
   // forward
   q.SK = q.N;
@@ -66,7 +77,8 @@ int make_plan(const xhc_desc* d, Plan* p) {
   }
   q.bx_cblocks = (int)cdiv(q.C, BX_CB);
   q.bx_tiles = (int)cdiv(T, BX_TOK);
-  q.b2_rowgroups = 1 + (int)cdiv(q.N - q.k, 4);
+  // with a router the active rows change per token: all rows in groups of 4
+  q.b2_rowgroups = q.R ? (int)cdiv(q.N, 4) : 1 + (int)cdiv(q.N - q.k, 4);
   q.b2_cblocks = (int)cdiv(q.C, B2_CB);
   q.Tpad = cdiv(T, B2_TT) * B2_TT;
   {
@@ -97,17 +109,21 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.off_zpart = o;  o = align256(o + (size_t)q.SK * T * q.ZST * 4);
   q.off_coef = o;   o = align256(o + (size_t)T * COEF_STRIDE * 4);
   q.off_gram = o;   o = align256(o + (q.gs ? (size_t)q.b1_cblocks * T * 16 * 4 : 0));
+  q.off_rcs = o;    o = align256(o + (q.R ? (size_t)RCS_BLK * 16 * 4 : 0));
   q.fwd_bytes = o;
   // backward reuses the forward regions (projection recompute) and adds:
-  q.off_zbuf = o;   o = align256(o + (size_t)T * (q.P + 1) * 4);
+  q.off_zbuf = o;   o = align256(o + (size_t)T * q.zsv * 4);
   q.off_wp = o;     o = align256(o + (size_t)q.NC * 64 * q.esz);
   q.off_dpart = o;  o = align256(o + (size_t)q.b1_cblocks * T * DOT_STRIDE * 4);
   q.off_dpa = o;    o = align256(o + (size_t)q.bx_cblocks * T * BX_OUT * 4);
   q.off_dwpart = o; o = align256(o + (q.nc == 4 ? (size_t)q.B * q.b1_segs * q.C * 24 * 4 : 0));
-  q.off_dz = o;     o = align256(o + (size_t)T * 48 * 4);
-  q.off_rec = o;    o = align256(o + (size_t)(q.Tpad / B2_TT) * REC_BYTES);
-  q.off_dwpart2 = o; o = align256(o + (size_t)q.b2_ts * q.NC * 48 * 4);
+  q.off_dz = o;     o = align256(o + (size_t)T * q.dzs * 4);
+  q.off_rec = o;    o = align256(o + (size_t)(q.Tpad / B2_TT) * q.rec_bytes);
+  q.off_dwpart2 = o; o = align256(o + (size_t)q.b2_ts * q.NC * q.dwr * 4);
   q.off_gss = o;    o = align256(o + (q.gs ? (size_t)T * 16 * 4 : 0));
+  q.off_hres = o;   o = align256(o + (q.R ? (size_t)T * 16 * 4 : 0));
+  q.off_pass = o;   o = align256(o + (q.R ? (size_t)T * q.k * q.C * q.esz : 0));
+  q.off_rred = o;   o = align256(o + (q.R ? (size_t)16 * 4 : 0));
   q.bwd_bytes = o;
   return XHC_OK;
 }
@@ -123,9 +139,10 @@ static bool overlap(Span a, Span b) {
 }
 static bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
 
+// The host active list: all k entries, or with a router the k - R fixed ones.
 static int check_active(const Plan& p, const int32_t* act) {
   if (!act) return XHC_ERR_NULL;
-  for (int a = 0; a < p.k; ++a) {
+  for (int a = 0; a < p.nfix; ++a) {
     if (act[a] < 0 || act[a] >= p.N) return XHC_ERR_INDEX;
     for (int b = 0; b < a; ++b)
       if (act[a] == act[b]) return XHC_ERR_INDEX;
@@ -155,9 +172,11 @@ static int validate_fwd(const Plan& p, const xhc_fwd_args* a, bool need_W = true
   const bool has_conv = a->w4 || a->w8 || a->w12;
   if (p.nc == 4 && (!a->w4 || !a->w8 || !a->w12)) return XHC_ERR_NULL;
   if (p.nc == 1 && has_conv) return XHC_ERR_UNSUPPORTED;
+  if (p.R && !a->W_route) return XHC_ERR_NULL;
   int rc = check_active(p, a->active);
   if (rc) return rc;
-  const void* ptrs[] = {a->X, a->out, a->w4, a->w8, a->w12, a->W, a->bias, a->X_new, a->h_in, a->z_save, a->xact_save};
+  const void* ptrs[] = {a->X, a->out, a->w4, a->w8, a->w12, a->W, a->bias, a->X_new, a->h_in, a->z_save, a->xact_save,
+                        p.R ? a->W_route : nullptr, p.R ? a->b_route : nullptr, p.R ? a->route_idx : nullptr};
   for (const void* q : ptrs)
     if (misaligned(q)) return XHC_ERR_ALIGN;
   const size_t T = p.T, e = p.esz;
@@ -166,11 +185,14 @@ static int validate_fwd(const Plan& p, const xhc_fwd_args* a, bool need_W = true
   const Span W = span(a->W, (size_t)p.NC * p.P * e), bias = span(a->bias, a->bias ? (size_t)p.P * 4 : 0);
   const Span w4 = span(a->w4, a->w4 ? (size_t)p.C * 16 : 0), w8 = span(a->w8, a->w8 ? (size_t)p.C * 32 : 0),
              w12 = span(a->w12, a->w12 ? (size_t)p.C * 48 : 0);
-  const Span zs = span(a->z_save, a->z_save ? T * (p.P + 1) * 4 : 0);
+  const Span zs = span(a->z_save, a->z_save ? T * p.zsv * 4 : 0);
   const Span xs = span(a->xact_save, a->xact_save ? T * p.k * p.C * e : 0);
+  const Span Wr = span(p.R ? a->W_route : nullptr, (size_t)p.NC * p.N * e);
+  const Span br = span(p.R ? a->b_route : nullptr, (size_t)p.N * 4);
+  const Span ri = span(p.R ? a->route_idx : nullptr, T * p.k * 4);
   if (a->X_new != a->X && overlap(X, Xn)) return XHC_ERR_ALIAS;
-  std::vector<Span> outs = {Xn, hin, zs, xs};
-  std::vector<Span> ins = {X, out, W, bias, w4, w8, w12};
+  std::vector<Span> outs = {Xn, hin, zs, xs, ri};
+  std::vector<Span> ins = {X, out, W, bias, w4, w8, w12, Wr, br};
   if (any_overlap(outs, ins, Xn, X)) return XHC_ERR_ALIAS;
   return XHC_OK;
 }
@@ -179,6 +201,7 @@ static int validate_fwd(const Plan& p, const xhc_fwd_args* a, bool need_W = true
 // pn: the next sublayer's plan (== p without desc_next)
 static int validate_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const xhc_chain_args* c) {
   if (!c) return XHC_OK;
+  if (p.R || pn.R) return XHC_ERR_UNSUPPORTED;
   if ((c->W_next == nullptr) != (c->carry_out == nullptr)) return XHC_ERR_NULL;
   if (misaligned(c->carry_in) || misaligned(c->carry_out) || misaligned(c->W_next)) return XHC_ERR_ALIGN;
   if (pn.B != p.B || pn.S != p.S || pn.C != p.C || pn.N != p.N || pn.dtype != p.dtype) return XHC_ERR_SHAPE;
@@ -192,7 +215,7 @@ static int validate_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, 
   const Span bias = span(a->bias, a->bias ? (size_t)p.P * 4 : 0);
   const Span w4 = span(a->w4, a->w4 ? (size_t)p.C * 16 : 0), w8 = span(a->w8, a->w8 ? (size_t)p.C * 32 : 0),
              w12 = span(a->w12, a->w12 ? (size_t)p.C * 48 : 0);
-  const Span zs = span(a->z_save, a->z_save ? T * (p.P + 1) * 4 : 0);
+  const Span zs = span(a->z_save, a->z_save ? T * p.zsv * 4 : 0);
   const Span xs = span(a->xact_save, a->xact_save ? T * p.k * p.C * e : 0);
   const Span outs[] = {Xn, hin, zs, xs};
   const Span ins[] = {X, out, W, bias, w4, w8, w12};
@@ -219,10 +242,17 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
   if (p.nc == 4 && (!a->w4 || !a->w8 || !a->w12 || !a->dw4 || !a->dw8 || !a->dw12)) return XHC_ERR_NULL;
   if (p.nc == 1 && (a->w4 || a->w8 || a->w12 || a->dw4 || a->dw8 || a->dw12)) return XHC_ERR_UNSUPPORTED;
   if (a->accumulate != 0 && a->accumulate != 1) return XHC_ERR_UNSUPPORTED;
+  if (p.R) {
+    // the router's choice and scores come from the forward's records
+    if (!a->z_save || !a->route_idx || !a->W_route || !a->dW_route) return XHC_ERR_NULL;
+    if (a->xact) return XHC_ERR_UNSUPPORTED;
+  }
   int rc = check_active(p, a->active);
   if (rc) return rc;
   const void* ptrs[] = {a->X, a->xact, a->out, a->w4, a->w8, a->w12, a->W, a->bias, a->z_save, a->dX_new,
-                        a->dh_in, a->dX, a->dout, a->dW, a->db, a->dw4, a->dw8, a->dw12};
+                        a->dh_in, a->dX, a->dout, a->dW, a->db, a->dw4, a->dw8, a->dw12,
+                        p.R ? a->W_route : nullptr, p.R ? a->route_idx : nullptr,
+                        p.R ? a->dW_route : nullptr, p.R ? a->db_route : nullptr};
   for (const void* q : ptrs)
     if (misaligned(q)) return XHC_ERR_ALIGN;
   const size_t T = p.T, e = p.esz;
@@ -231,15 +261,19 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
   const Span bias = span(a->bias, a->bias ? (size_t)p.P * 4 : 0);
   const Span w4 = span(a->w4, a->w4 ? (size_t)p.C * 16 : 0), w8 = span(a->w8, a->w8 ? (size_t)p.C * 32 : 0),
              w12 = span(a->w12, a->w12 ? (size_t)p.C * 48 : 0);
-  const Span zs = span(a->z_save, a->z_save ? T * (p.P + 1) * 4 : 0);
+  const Span zs = span(a->z_save, a->z_save ? T * p.zsv * 4 : 0);
+  const Span Wr = span(p.R ? a->W_route : nullptr, (size_t)p.NC * p.N * e);
+  const Span ri = span(p.R ? a->route_idx : nullptr, T * p.k * 4);
+  const Span dWr = span(p.R ? a->dW_route : nullptr, (size_t)p.NC * p.N * 4);
+  const Span dbr = span(p.R ? a->db_route : nullptr, (size_t)p.N * 4);
   const Span dXn = span(a->dX_new, T * p.NC * e), dhin = span(a->dh_in, T * p.C * e);
   const Span dX = span(a->dX, T * p.NC * e), dout = span(a->dout, T * p.C * e);
   const Span dW = span(a->dW, (size_t)p.NC * p.P * 4), db = span(a->db, a->db ? (size_t)p.P * 4 : 0);
   const Span dw4 = span(a->dw4, a->dw4 ? (size_t)p.C * 16 : 0), dw8 = span(a->dw8, a->dw8 ? (size_t)p.C * 32 : 0),
              dw12 = span(a->dw12, a->dw12 ? (size_t)p.C * 48 : 0);
   if (a->dX != a->dX_new && overlap(dX, dXn)) return XHC_ERR_ALIAS;
-  std::vector<Span> outs = {dX, dout, dW, db, dw4, dw8, dw12};
-  std::vector<Span> ins = {X, xact, out, W, bias, w4, w8, w12, zs, dXn, dhin};
+  std::vector<Span> outs = {dX, dout, dW, db, dw4, dw8, dw12, dWr, dbr};
+  std::vector<Span> ins = {X, xact, out, W, bias, w4, w8, w12, zs, dXn, dhin, Wr, ri};
   if (any_overlap(outs, ins, dX, dXn)) return XHC_ERR_ALIAS;
   return XHC_OK;
 }
@@ -266,7 +300,7 @@ struct xhc_timer {
 
 static const char* const kKernelNames[xhc::KID_COUNT] = {
     "pack_wt", "proj", "coef", "mix", "pack_wp", "bdots", "bcoef", "bgrad", "breduce", "bxdots", "mixproj", "gram",
-    "bdots_gs"};
+    "bdots_gs", "route_colsum", "route_pass", "route_dwr"};
 
 namespace xhc {
 void timer_mark(xhc_timer* tm, int kid, hipStream_t st, bool start) {
@@ -327,6 +361,12 @@ int xhc_forward(const xhc_desc* desc, const xhc_fwd_args* args, void* workspace,
   if (rc) return rc;
   clear_pending_hip_error();
   return xhc::launch_forward(p, args, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+int32_t xhc_zsave_stride(const xhc_desc* desc) {
+  xhc::Plan p;
+  if (xhc::make_plan(desc, &p) != XHC_OK) return 0;
+  return p.zsv;
 }
 
 size_t xhc_carry_size(const xhc_desc* desc) {

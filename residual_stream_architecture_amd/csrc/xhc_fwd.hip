@@ -27,10 +27,19 @@ namespace xhc {
 // One workgroup per (i, ks): the 32 x P source rows are one contiguous run
 // of W, read coalesced into LDS, and the NT fragments are written from there
 // as 8-element vectors.
+// With a router (Wr != NULL, NT == 4) logit tile 3 holds the router's
+// candidate columns, column 48 + e = Wr column cand(e) for e < ncand, then a
+// column of ones (its dot with the state row is the row's sum, for the
+// LayerNorm mean), then zeros.
 // ---------------------------------------------------------------------------
+template <typename R> __device__ inline R one_of();
+template <> __device__ inline uint16_t one_of<uint16_t>() { return (uint16_t)0x3F80u; }   // bf16 1.0
+template <> __device__ inline float one_of<float>() { return 1.0f; }
+
 template <typename R>
 __global__ __launch_bounds__(256) void k_pack_wt(const R* __restrict__ W, R* __restrict__ Wf, int C, int P, int NT,
-                                                 int nks) {
+                                                 int nks, const R* __restrict__ Wr, int N, RowOrder cand,
+                                                 int ncand) {
   __shared__ R tile[32][16 * NT_MAX + 1];
   const int i = blockIdx.x / nks, ks = blockIdx.x - (blockIdx.x / nks) * nks;
   const int c0 = ks * 32;
@@ -40,6 +49,16 @@ __global__ __launch_bounds__(256) void k_pack_wt(const R* __restrict__ W, R* __r
     const int rr = idx / P, pp = idx - (idx / P) * P;
     tile[rr][pp] = rr < rows ? src[idx] : R(0);
   }
+  if (Wr) {
+    const R* rsrc = Wr + ((size_t)i * C + c0) * N;
+    for (int idx = threadIdx.x; idx < 32 * 16; idx += 256) {
+      const int rr = idx >> 4, e = idx & 15;
+      R v = R(0);
+      if (rr < rows) v = e < ncand ? rsrc[(size_t)rr * N + row_of(cand, e)] : e == ncand ? one_of<R>() : R(0);
+      tile[rr][48 + e] = v;
+    }
+  }
+  const int PW = Wr ? 64 : P;    // columns held in the tile
   __syncthreads();
   R* dst = Wf + (size_t)blockIdx.x * NT * 512;
   for (int idx = threadIdx.x; idx < NT * 64; idx += 256) {
@@ -47,7 +66,7 @@ __global__ __launch_bounds__(256) void k_pack_wt(const R* __restrict__ W, R* __r
     const int p = 16 * n + (l & 15), r0 = 8 * (l >> 4);
     R v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = p < P ? tile[r0 + e][p] : R(0);
+    for (int e = 0; e < 8; ++e) v[e] = (p < P || (p >= 48 && p < PW)) ? tile[r0 + e][p] : R(0);
     __builtin_memcpy(dst + (size_t)idx * 8, v, sizeof(v));
   }
 }
@@ -219,62 +238,163 @@ __global__ __launch_bounds__(64 * PROJ_WAVES) void k_proj(StreamRows src, const 
 // components) the token's Gram record is summed over its ngram channel-block
 // partials, and the post coefficients become H_post T (u~ = T U, see
 // xhc_gs.h), so the write pass combines the raw components.
+// ROUTE (projection partials only): logit tile 3 holds x.Wr for the router's
+// candidates and sum(x); the token's scores, its top-R choice (R argmax
+// rounds over the 16 lanes on fp32 scores, equal scores to the lower
+// candidate, that is the lower stream id) and the scaling of the routed
+// slots' post coefficients by s = sigmoid(rho) happen here; the active list
+// goes to the coefficient record (CO_IDX), route_idx and z_save's router
+// record.
 // ---------------------------------------------------------------------------
-template <bool GS>
+struct RouteArgs {
+  const float* rcs;       // [RCS_BLK][16] partial column sums of W_route
+  const float* b_route;   // [N] or NULL
+  int32_t* route_idx;     // [T][k] or NULL
+  RowOrder cand;          // candidate e -> stream id
+  int ncand, nfix, R;
+  int fixed[4];           // stream ids of the fixed slots
+};
+
+template <bool GS, bool ROUTE>
 __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, int SK, int ZST, int NTP,
                                               const float* __restrict__ z_in, const float* __restrict__ bias,
-                                              float* __restrict__ coef, float* __restrict__ z_out, int T,
+                                              float* __restrict__ coef, float* __restrict__ z_out, int zsv, int T,
                                               int N, int k, int nc, int P, float inv_nc_total, float eps,
                                               int iters, int unit_gates, const float* __restrict__ gram,
-                                              int ngram, float gs_ceps) {
+                                              int ngram, float gs_ceps, RouteArgs ra) {
   __shared__ float zs[16][COEF_STRIDE];
+  __shared__ float csum[16];
   const int e = threadIdx.x & 15, tok = threadIdx.x >> 4;
   const int t = blockIdx.x * 16 + tok;
   const bool tv = t < T;
   float r = 0.f;
+  float zr = 0.f, ssum = 0.f;   // ROUTE: raw x.Wr of candidate e (or sum(x) at e == ncand), sum(x^2)
+  if constexpr (ROUTE) {
+    // W_route's column sums, in a fixed order
+    if (threadIdx.x < 16) {
+      float a = 0.f;
+      for (int b = 0; b < RCS_BLK; ++b) a += ra.rcs[b * 16 + threadIdx.x];
+      csum[threadIdx.x] = a;
+    }
+  }
   if (zpart) {
     float ss = (tv && e < SK) ? zpart[((size_t)e * T + t) * ZST + NTP] : 0.f;
     ss += row_xor<1>(ss);
     ss += row_xor<2>(ss);
     ss += row_xor<4>(ss);
     ss += row_xor<8>(ss);
+    ssum = ss;
     r = sqrtf(ss * inv_nc_total + eps);
     // all partial loads issued together (SK <= 16; clamped indices, masked
     // values), summed in split order
-    float z[3] = {0.f, 0.f, 0.f};
+    constexpr int NZ = ROUTE ? 4 : 3;
+    float z[NZ];
+#pragma unroll
+    for (int n = 0; n < NZ; ++n) z[n] = 0.f;
     const int tcl = tv ? t : 0;
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      const float* zr = zpart + ((size_t)min(s, SK - 1) * T + tcl) * ZST;
-      float v[3];
+      const float* zp = zpart + ((size_t)min(s, SK - 1) * T + tcl) * ZST;
+      float v[NZ];
 #pragma unroll
-      for (int n = 0; n < 3; ++n) v[n] = zr[min(e + 16 * n, ZST - 1)];
+      for (int n = 0; n < NZ; ++n) v[n] = zp[min(e + 16 * n, ZST - 1)];
 #pragma unroll
-      for (int n = 0; n < 3; ++n) z[n] += s < SK ? v[n] : 0.f;
+      for (int n = 0; n < NZ; ++n) z[n] += s < SK ? v[n] : 0.f;
     }
+    if constexpr (ROUTE) zr = z[3];
 #pragma unroll
     for (int n = 0; n < 3; ++n) {
       const int p = e + 16 * n;
       zs[tok][p] = (tv && p < P) ? z[n] / r + (bias ? bias[p] : 0.f) : 0.f;
     }
   } else {
-    r = tv ? z_in[(size_t)t * (P + 1) + P] : 1.f;
+    r = tv ? z_in[(size_t)t * zsv + P] : 1.f;
 #pragma unroll
     for (int n = 0; n < 3; ++n) {
       const int p = e + 16 * n;
-      zs[tok][p] = (tv && p < P) ? z_in[(size_t)t * (P + 1) + p] : 0.f;
+      zs[tok][p] = (tv && p < P) ? z_in[(size_t)t * zsv + p] : 0.f;
     }
   }
   __syncthreads();
   if (!tv) return;
   float* co = coef + (size_t)t * COEF_STRIDE;
 
+  // router: scores of the candidates, top-R choice, write-back scales
+  int sel[4];
+  float sscale[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) { sel[a] = a < k && a < ra.nfix ? ra.fixed[a] : 0; sscale[a] = 1.f; }
+  if constexpr (ROUTE) {
+    const int base = (threadIdx.x & 63) & ~15;
+    const float inv_nc = inv_nc_total;
+    const float mu = __shfl(zr, base + ra.ncand, 64) * inv_nc;
+    const float var = fmaxf(ssum * inv_nc - mu * mu, 0.f);
+    const float sd = sqrtf(var + eps);
+    const bool cand = e < ra.ncand;
+    const int sid = cand ? row_of(ra.cand, e) : 0;                    // the candidate's stream
+    const float csm = cand ? csum[sid] : 0.f;
+    const float ys = cand ? (zr - mu * csm) / sd : 0.f;               // rho - b_route
+    const float rho = cand ? ys + (ra.b_route ? ra.b_route[sid] : 0.f) : 0.f;
+    float key = (cand && rho == rho) ? rho : -INFINITY;
+    int lk = cand ? e : 32 + e;                                      // equal keys: lower lane wins
+    float* zo = z_out ? z_out + (size_t)t * zsv : nullptr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j >= ra.R) break;
+      float bv = key;
+      int bl = lk;
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        float ov;
+        int ol;
+        if (m == 1) { ov = row_xor<1>(bv); ol = __float_as_int(row_xor<1>(__int_as_float(bl))); }
+        else if (m == 2) { ov = row_xor<2>(bv); ol = __float_as_int(row_xor<2>(__int_as_float(bl))); }
+        else if (m == 4) { ov = row_xor<4>(bv); ol = __float_as_int(row_xor<4>(__int_as_float(bl))); }
+        else { ov = row_xor<8>(bv); ol = __float_as_int(row_xor<8>(__int_as_float(bl))); }
+        const bool take = ov > bv || (ov == bv && ol < bl);
+        bv = take ? ov : bv;
+        bl = take ? ol : bl;
+      }
+      const int lw = bl & 15;                      // a candidate lane: R <= ncand
+      const float rho_w = __shfl(rho, base + lw, 64);
+      const float y_w = __shfl(ys, base + lw, 64);
+      const float cs_w = __shfl(csm, base + lw, 64);
+      const int a = ra.nfix + j;
+      const int sw = row_of(ra.cand, lw);
+      const float sg = sigmoid(rho_w);
+#pragma unroll
+      for (int a2 = 0; a2 < 4; ++a2)
+        if (a2 == a) { sel[a2] = sw; sscale[a2] = sg; }
+      if (e == lw) { key = -INFINITY; lk = 64 + e; }   // taken
+      if (zo && e == 0) {
+        zo[P + 3 + 3 * j] = rho_w;
+        zo[P + 4 + 3 * j] = y_w;
+        zo[P + 5 + 3 * j] = cs_w;
+      }
+    }
+    if (zo && e == 0) { zo[P + 1] = mu; zo[P + 2] = sd; }
+    int mine = sel[0];
+#pragma unroll
+    for (int a2 = 1; a2 < 4; ++a2)
+      if (e == a2) mine = sel[a2];
+    if (e < k) {
+      co[CO_IDX + e] = __int_as_float(mine);
+      if (ra.route_idx) ra.route_idx[(size_t)t * k + e] = mine;
+    }
+  }
+  // this lane's post row a = e / 4: its write-back scale
+  float my_s = sscale[0];
+#pragma unroll
+  for (int a2 = 1; a2 < 4; ++a2)
+    if ((e >> 2) == a2) my_s = sscale[a2];
+
   // gates
   co[CO_PRE + e] = e < N ? (unit_gates ? 1.f : sigmoid(zs[tok][e])) : 0.f;
   if constexpr (!GS) {
     (void)gram; (void)ngram; (void)gs_ceps;
     const int a = e >> 2, m = e & 3;
-    co[CO_POST + e] = (a < k && m < nc) ? (unit_gates ? 1.f : sigmoid(zs[tok][N + a * nc + m])) : 0.f;
+    const float h = (a < k && m < nc) ? (unit_gates ? 1.f : sigmoid(zs[tok][N + a * nc + m])) : 0.f;
+    co[CO_POST + e] = ROUTE ? h * my_s : h;
   } else {
     // Gram-Schmidt folded into the post coefficients (nc == 4)
     float gsum = 0.f;
@@ -302,7 +422,7 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
         h = fmaf(hp, f.T[c][m], h);
       }
     }
-    co[CO_POST + e] = h;
+    co[CO_POST + e] = ROUTE ? h * my_s : h;
   }
   // Sinkhorn on the k x k res logits
   {
@@ -322,14 +442,14 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
     }
     co[CO_RES + e] = M;
   }
-  co[48 + e] = e == 0 ? r : 0.f;
+  if (e < 4) co[CO_R + e] = e == 0 ? r : 0.f;      // [52, 56) may hold the active list
   if (z_out) {
 #pragma unroll
     for (int n = 0; n < 3; ++n) {
       const int p = e + 16 * n;
-      if (p < P) z_out[(size_t)t * (P + 1) + p] = zs[tok][p];
+      if (p < P) z_out[(size_t)t * zsv + p] = zs[tok][p];
     }
-    if (e == 0) z_out[(size_t)t * (P + 1) + P] = r;
+    if (e == 0) z_out[(size_t)t * zsv + P] = r;
   }
 }
 
@@ -343,10 +463,13 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
 // place) stays safe and every load batch overlaps the previous token's work.
 // FAST: N == 16 and k == 4 (all row and active-row loops compile-time);
 // otherwise rows i >= N and active slots a >= k are skipped at run time.
+// ROUTE: each token's active list comes from its coefficient record
+// (CO_IDX, uniform scalar loads two tokens ahead of their use in addresses)
+// instead of `act`.
 // ---------------------------------------------------------------------------
 struct Active { int id[4]; };
 
-template <typename E, int NCOMP, bool FAST>
+template <typename E, int NCOMP, bool FAST, bool ROUTE>
 __global__ __launch_bounds__(MIX_THREADS) void k_mix(
     const void* __restrict__ X, const void* __restrict__ out, const float* __restrict__ w4,
     const float* __restrict__ w8, const float* __restrict__ w12, const float* __restrict__ coef,
@@ -401,30 +524,46 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
     }
   }
 
+  // a token's active list
+  auto token_ids = [&](int s, int (&id)[4]) {
+    if constexpr (ROUTE) {
+      const int4 v = *reinterpret_cast<const int4*>(coef + (tok0 + s) * COEF_STRIDE + CO_IDX);
+      id[0] = v.x; id[1] = v.y; id[2] = v.z; id[3] = v.w;
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) id[b] = act.id[b];
+    }
+  };
   // prefetch buffers: the 16 state rows, the k active rows and the out row
   // of the next token (one buffer resource per token: offsets stay small)
   V xr[16], xa_r[4], ov;
-  auto load_token = [&](int s) {
+  auto load_token = [&](int s, const int (&id)[4]) {
     const rsrc_t rx = make_rsrc(Xb + (tok0 + s) * tokb, tokb);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (FULLN || i < NR) xr[i] = bload<E, MIX_CH>(rx, voff, (uint32_t)i * rowb);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
-      if (b < K) xa_r[b] = bload<E, MIX_CH>(rx, voff, (uint32_t)act.id[b] * rowb);
+      if (b < K) xa_r[b] = bload<E, MIX_CH>(rx, voff, (uint32_t)id[b] * rowb);
     ov = bload<E, MIX_CH>(rout, voff, (uint32_t)s * rowb);
   };
-  load_token(s0);
+  int id_a[4], id_b[4];            // active lists of the tokens after the current one
+  token_ids(s0, id_a);
+  load_token(s0, id_a);
+  token_ids(s0 + 1 < s1 ? s0 + 1 : s0, id_b);
 
   for (int s = s0; s < s1; ++s) {
     const size_t t = tok0 + s;
     V cx[16], cxa[4], co_out = ov;
+    int cid[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) { cid[b] = id_a[b]; id_a[b] = id_b[b]; }
 #pragma unroll
     for (int i = 0; i < 16; ++i) cx[i] = xr[i];
 #pragma unroll
     for (int b = 0; b < 4; ++b) cxa[b] = xa_r[b];
-    load_token(s + 1 < s1 ? s + 1 : s);          // next token (the last iteration reloads, harmlessly)
-
+    load_token(s + 1 < s1 ? s + 1 : s, id_a);    // next token (the last iteration reloads, harmlessly)
+    token_ids(s + 2 < s1 ? s + 2 : s1 - 1, id_b);
     // the token's coefficients: uniform 16-byte loads (scalar loads)
     const f32x4* c4 = reinterpret_cast<const f32x4*>(coef + t * COEF_STRIDE);
     float cpre[16], cpost[16], cres[16];
@@ -493,7 +632,7 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
             for (int m = 0; m < NCOMP; ++m) v = fmaf(cpost[a * 4 + m], u[m][ch], v);
             res[ch] = v;
           }
-          bstore<E, MIX_CH>(V::from_float(res), rxn, voff, (uint32_t)act.id[a] * rowb);
+          bstore<E, MIX_CH>(V::from_float(res), rxn, voff, (uint32_t)cid[a] * rowb);
           if (xact) bstore<E, MIX_CH>(cxa[a], rxs, voff, (uint32_t)a * rowb);
         }
       }
@@ -503,7 +642,7 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
           if (FULLN || i < NR) {
             bool is_act = false;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) is_act |= (b < K && i == act.id[b]);
+            for (int b = 0; b < 4; ++b) is_act |= (b < K && i == cid[b]);
             if (!is_act) bstore<E, MIX_CH>(cx[i], rxn, voff, (uint32_t)i * rowb);
           }
         }
@@ -516,10 +655,34 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
 // launchers
 // ---------------------------------------------------------------------------
 template <typename R>
-static void launch_pack_wt(const Plan& p, const void* W, void* Wf, hipStream_t st, xhc_timer* tm) {
+static void launch_pack_wt(const Plan& p, const void* W, void* Wf, hipStream_t st, xhc_timer* tm,
+                           const void* Wr = nullptr, RowOrder cand = RowOrder{0}) {
   TimedLaunch tl(tm, KID_PACK_WT, st);
   const int nks = (p.C + 31) / 32;
-  k_pack_wt<R><<<p.N * nks, 256, 0, st>>>(static_cast<const R*>(W), static_cast<R*>(Wf), p.C, p.P, p.NT, nks);
+  k_pack_wt<R><<<p.N * nks, 256, 0, st>>>(static_cast<const R*>(W), static_cast<R*>(Wf), p.C, p.P, p.NT, nks,
+                                          static_cast<const R*>(Wr), p.N, cand, p.ncand);
+}
+
+// The router's candidates (streams that are not fixed, ascending) and the
+// fixed slots' streams.
+static RouteArgs route_args(const Plan& p, const xhc_fwd_args* a, float* rcs) {
+  RouteArgs ra{};
+  ra.rcs = rcs;
+  ra.b_route = a->b_route;
+  ra.route_idx = a->route_idx;
+  ra.ncand = p.ncand;
+  ra.nfix = p.nfix;
+  ra.R = p.R;
+  for (int j = 0; j < 4; ++j) ra.fixed[j] = j < p.nfix ? a->active[j] : 0;
+  uint64_t bits = 0;
+  int n = 0;
+  for (int i = 0; i < p.N && p.R; ++i) {
+    bool fixed = false;
+    for (int j = 0; j < p.nfix; ++j) fixed |= a->active[j] == i;
+    if (!fixed) bits |= (uint64_t)i << (4 * n++);
+  }
+  ra.cand = RowOrder{bits};
+  return ra;
 }
 
 template <typename E>
@@ -530,9 +693,11 @@ static void launch_proj(const Plan& p, const StreamRows& src, const void* Wf, fl
 #define XHC_PROJ(NT, PU, PNS) \
   k_proj<E, NT, PU, PNS><<<nb, 64 * PROJ_WAVES, 0, st>>>(src, Wf, zpart, p.T, p.C, p.ZST, p.proj_tiles)
   if (p.SK >= 8) {
-    if (p.NT == 1) XHC_PROJ(1, 1, 6); else if (p.NT == 2) XHC_PROJ(2, 1, 6); else XHC_PROJ(3, 1, 6);
+    if (p.NT == 1) XHC_PROJ(1, 1, 6); else if (p.NT == 2) XHC_PROJ(2, 1, 6);
+    else if (p.NT == 3) XHC_PROJ(3, 1, 6); else XHC_PROJ(4, 1, 6);
   } else {
-    if (p.NT == 1) XHC_PROJ(1, 2, 4); else if (p.NT == 2) XHC_PROJ(2, 2, 4); else XHC_PROJ(3, 2, 4);
+    if (p.NT == 1) XHC_PROJ(1, 2, 4); else if (p.NT == 2) XHC_PROJ(2, 2, 4);
+    else if (p.NT == 3) XHC_PROJ(3, 2, 4); else XHC_PROJ(4, 2, 4);
   }
 #undef XHC_PROJ
 }
@@ -547,8 +712,14 @@ static int forward_impl(const Plan& p, const Plan& pn, const xhc_fwd_args* a, co
   const float* carry_in = ch ? static_cast<const float*>(ch->carry_in) : nullptr;
   const bool carry_out = ch && ch->W_next;
 
+  float* rcs = reinterpret_cast<float*>(ws + p.off_rcs);
+  const RouteArgs ra = route_args(p, a, rcs);
   if (!carry_in) {
-    launch_pack_wt<R>(p, a->W, Wt, st, tm);
+    if (p.R) {
+      TimedLaunch tl(tm, KID_RCOLSUM, st);
+      launch_route_colsum(p, a->W_route, rcs, st);
+    }
+    launch_pack_wt<R>(p, a->W, Wt, st, tm, p.R ? a->W_route : nullptr, ra.cand);
     launch_proj<E>(p, stream_rows(p, a->X, nullptr, a->active), Wt, zpart, st, tm);
   }
   float* gram = reinterpret_cast<float*>(ws + p.off_gram);
@@ -561,14 +732,17 @@ static int forward_impl(const Plan& p, const Plan& pn, const xhc_fwd_args* a, co
     const float* zp = carry_in ? carry_in : zpart;
     const int sk = carry_in ? p.mp_ncb : p.SK;
     const int unit = p.gate == XHC_GATE_UNIT;
-    if (p.gs)
-      k_coef<true><<<(p.T + 15) / 16, 256, 0, st>>>(zp, sk, p.ZST, NTP, nullptr, a->bias, coef, a->z_save, p.T, p.N,
-                                                    p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps, p.iters, unit, gram,
-                                                    p.b1_cblocks, p.gs_ceps);
-    else
-      k_coef<false><<<(p.T + 15) / 16, 256, 0, st>>>(zp, sk, p.ZST, NTP, nullptr, a->bias, coef, a->z_save, p.T,
-                                                     p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps, p.iters, unit,
-                                                     nullptr, 0, 0.f);
+#define XHC_COEF(GS, RT)                                                                                      \
+  k_coef<GS, RT><<<(p.T + 15) / 16, 256, 0, st>>>(zp, sk, p.ZST, NTP, nullptr, a->bias, coef, a->z_save, p.zsv, \
+                                                  p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps, p.iters,  \
+                                                  unit, GS ? gram : nullptr, GS ? p.b1_cblocks : 0,              \
+                                                  GS ? p.gs_ceps : 0.f, ra)
+    if (p.gs) {
+      if (p.R) XHC_COEF(true, true); else XHC_COEF(true, false);
+    } else {
+      if (p.R) XHC_COEF(false, true); else XHC_COEF(false, false);
+    }
+#undef XHC_COEF
   }
   if (carry_out) {
     // the next sublayer's weights in the MFMA fragment order, then the fused
@@ -581,18 +755,24 @@ static int forward_impl(const Plan& p, const Plan& pn, const xhc_fwd_args* a, co
   {
     TimedLaunch tl(tm, KID_MIX, st);
     Active act;
-    for (int b = 0; b < 4; ++b) act.id[b] = b < p.k ? a->active[b] : -1;
+    for (int b = 0; b < 4; ++b) act.id[b] = b < p.k && !p.R ? a->active[b] : -1;
     dim3 grid(p.mix_cblocks, p.B * p.mix_segs);
     const int in_place = a->X_new == a->X;
-#define XHC_MIX(NCOMP, FULLN)                                                                              \
-  k_mix<E, NCOMP, FULLN><<<grid, MIX_THREADS, 0, st>>>(a->X, a->out, a->w4, a->w8, a->w12, coef, a->X_new, \
-                                                       a->h_in, a->xact_save, p.S, p.C, p.N, p.k, act,      \
-                                                       in_place, p.mix_lseg, p.mix_segs)
+#define XHC_MIX(NCOMP, FULLN, RT)                                                                              \
+  k_mix<E, NCOMP, FULLN, RT><<<grid, MIX_THREADS, 0, st>>>(a->X, a->out, a->w4, a->w8, a->w12, coef, a->X_new, \
+                                                           a->h_in, a->xact_save, p.S, p.C, p.N, p.k, act,      \
+                                                           in_place, p.mix_lseg, p.mix_segs)
     const bool fast = p.N == 16 && p.k == 4;
-    if (p.nc == 4) {
-      if (fast) XHC_MIX(4, true); else XHC_MIX(4, false);
+    if (p.R) {
+      if (p.nc == 4) {
+        if (fast) XHC_MIX(4, true, true); else XHC_MIX(4, false, true);
+      } else {
+        if (fast) XHC_MIX(1, true, true); else XHC_MIX(1, false, true);
+      }
+    } else if (p.nc == 4) {
+      if (fast) XHC_MIX(4, true, false); else XHC_MIX(4, false, false);
     } else {
-      if (fast) XHC_MIX(1, true); else XHC_MIX(1, false);
+      if (fast) XHC_MIX(1, true, false); else XHC_MIX(1, false, false);
     }
 #undef XHC_MIX
   }
@@ -631,9 +811,10 @@ int launch_coef_bwd(const Plan& p, const void* X, const void* xact, const int32_
   }
   TimedLaunch tl(tm, KID_COEF, st);
   // the backward needs z (and r) only: its post coefficients come from z
-  k_coef<false><<<(p.T + 15) / 16, 256, 0, st>>>(zpart, p.SK, p.ZST, p.NT * 16, z_save, bias, coef, z_out, p.T,
-                                                 p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps, p.iters,
-                                                 p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f);
+  k_coef<false, false><<<(p.T + 15) / 16, 256, 0, st>>>(zpart, p.SK, p.ZST, p.NT * 16, z_save, bias, coef, z_out,
+                                                        p.zsv, p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps,
+                                                        p.iters, p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f,
+                                                        RouteArgs{});
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
 }
 

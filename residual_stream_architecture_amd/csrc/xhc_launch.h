@@ -12,7 +12,7 @@ namespace xhc {
 enum KernelId {
   KID_PACK_WT = 0, KID_PROJ, KID_COEF, KID_MIX,
   KID_PACK_WP, KID_BDOTS, KID_BCOEF, KID_BGRAD, KID_BREDUCE, KID_BXDOTS,
-  KID_MIXPROJ, KID_GRAM, KID_BDOTS_GS,
+  KID_MIXPROJ, KID_GRAM, KID_BDOTS_GS, KID_RCOLSUM, KID_RPASS, KID_RDWR,
   KID_COUNT
 };
 // Alias kept for the backward's coefficient recompute from z_save.
@@ -76,5 +76,7 @@ int launch_backward(const Plan& p, const xhc_bwd_args* a, void* ws, hipStream_t 
 // partials over channel blocks of B1_WAVES * B1_WAVE_CH.
 void launch_gram(const Plan& p, const void* out, const float* w4, const float* w8, const float* w12, float* gram,
                  hipStream_t st);
+// Router (xhc_route.hip): partial column sums of W_route, rcs[RCS_BLK][16].
+void launch_route_colsum(const Plan& p, const void* W_route, float* rcs, hipStream_t st);
 
 }  // namespace xhc

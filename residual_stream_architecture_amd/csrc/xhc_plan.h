@@ -14,8 +14,9 @@ namespace xhc {
 //   [16, 32)  H_post[a*4 + m]
 //   [32, 48)  H_res[a*4 + b]
 //   48        r (RMS of the flattened state)
+//   [52, 56)  with a router: the token's active list (stream ids as int bits)
 constexpr int COEF_STRIDE = 64;
-constexpr int CO_PRE = 0, CO_POST = 16, CO_RES = 32, CO_R = 48;
+constexpr int CO_PRE = 0, CO_POST = 16, CO_RES = 32, CO_R = 48, CO_IDX = 52;
 
 // Per-token backward dot records (floats):
 //   B1x, per channel block of BX_CB:   [0, 16)  dH_pre[i]      = <dh_in, X_i>
@@ -67,13 +68,37 @@ constexpr int rec_dzr0_half(int esz) { return 4 * 16 * 8 * esz; }
 constexpr int rec_dzr1_half(int esz) { return 4 * 16 * 4 * esz; }
 constexpr int rec_dzrt_half(int esz) { return 3 * 4 * 16 * 4 * esz; }
 
-constexpr int NT_MAX = 3;   // logit tiles of 16: P = N + k*nc + k*k <= 48
+// The same record with a router (routed backward): the projection's K is 64
+// (logits 0..47, then the router's 16 stream columns), so
+//   [REC_DZR0, ..)    dz/r logits 0..31 as above
+//   [RR_DZR1, ..)     logits 32..63 as a second K=32 step, p = 32 + 8g + e
+//   [RR_DZRT, ..)     four dW B-fragment tiles (logits 0..63)
+//   [RR_CO, ..)       fields [RRF_NF][t 16]: H_pre[16], gamma, the LayerNorm
+//                     term that every element of the token's dX receives
+// B2 copies REC_R_USED bytes of it; records are REC_R_BYTES apart.
+constexpr int RR_DZR1 = 2048, RR_DZRT = 4096, RR_CO = 8192;
+constexpr int RRF_PRE = 0, RRF_GAMMA = 16, RRF_CONST = 17, RRF_NF = 18;
+constexpr int REC_R_USED = RR_CO + RRF_NF * B2_TT * 4;
+constexpr int REC_R_BYTES = 10240;
+static_assert(REC_R_USED <= REC_R_BYTES, "routed record");
+
+constexpr int NT_MAX = 4;   // logit tiles of 16: P = N + k*nc + k*k <= 48, plus the router's tile
+constexpr int RCS_BLK = 32; // partial column sums of W_route (forward router)
+constexpr int DZ_R = 80;    // floats per token of the routed backward's dz record:
+                            // dz [0,48), drho [48,64), mean*drho/sd [64,80)
 
 struct Plan {
   int B, S, C, N, k, nc, P, NT, T, iters, dtype, gate;
   float eps;
   bool gs;            // Gram-Schmidt over the four components (nc == 4)
   float gs_ceps;      // C * gs_eps
+  int R;              // routed slots (0: fixed active list)
+  int nfix;           // fixed slots, k - R
+  int ncand;          // router candidates, N - nfix (<= 15)
+  int zsv;            // floats per token of z_save
+  int dzs;            // floats per token of the backward's dz record
+  int dwr;            // floats per row of the backward's dW partials
+  int rec_bytes;      // bytes per B2 tile record
   int64_t NC;
   int esz;            // bytes per storage element
   // forward
@@ -101,8 +126,9 @@ struct Plan {
   int mp_nbatch;      // token batches of 128
   size_t carry_bytes; // [mp_ncb][T][ZST] floats
   // workspace layout (byte offsets; every region 256-byte aligned)
-  size_t off_wt, off_zpart, off_coef, off_gram, fwd_bytes;
-  size_t off_zbuf, off_wp, off_dpart, off_dpa, off_dwpart, off_dz, off_rec, off_dwpart2, off_gss, bwd_bytes;
+  size_t off_wt, off_zpart, off_coef, off_gram, off_rcs, fwd_bytes;
+  size_t off_zbuf, off_wp, off_dpart, off_dpa, off_dwpart, off_dz, off_rec, off_dwpart2, off_gss;
+  size_t off_hres, off_pass, off_rred, bwd_bytes;
 };
 
 // Fills `p` from `d`; returns XHC_OK or an XHC_ERR_* code for an

@@ -11,6 +11,8 @@ standard_normal in float32):
     then, if grads=True, dX_new [T,N,C] * 1 and dh_in [T,C] * 1.
 In bf16 workloads X, out, W, dX_new and dh_in are rounded to bf16
 (round-to-nearest-even); the conv weights stay fp32; the bias is zero.
+A router's weights come from `make_router` (its own generator, seed + 7000):
+W_route [N*C,N] * 0.02, bf16-rounded in bf16 workloads; b_route is zero.
 """
 
 from dataclasses import dataclass
@@ -35,6 +37,7 @@ class Workload:
     eps: float = 1e-6
     gs: bool = False      # Gram-Schmidt over the write-back components
     alt: bool = False     # stack: even sublayers attention-side (one component, no TFA)
+    route: int = 0        # routed slots (the first k - route active streams are fixed)
 
     @property
     def T(self):
@@ -56,6 +59,8 @@ WORKLOADS = {
     "fwdbwd4096": Workload("fwdbwd4096", 2, 4096, 4096, 16, 4, 4, "bf16", "fwdbwd"),
     # the same with Gram-Schmidt over the four write-back components
     "fwdbwd4096_gs": Workload("fwdbwd4096_gs", 2, 4096, 4096, 16, 4, 4, "bf16", "fwdbwd", gs=True),
+    # the same with the router: streams 0 and 1 fixed, two chosen per token
+    "fwdbwd4096_route": Workload("fwdbwd4096_route", 2, 4096, 4096, 16, 4, 4, "bf16", "fwdbwd", route=2),
     # 48 stacked sublayer updates, state carried in HBM
     "stack48": Workload("stack48", 1, 8192, 7168, 16, 4, 4, "bf16", "stack", layers=48),
     # the same stack alternating attention-side sublayers (out only) with
@@ -122,6 +127,13 @@ def make_inputs(w: Workload, seed=0, grads=False, state=True):
         d["dX_new"] = _draw(rng, (T, N, C), 1.0, lowp)
         d["dh_in"] = _draw(rng, (T, C), 1.0, lowp)
     return d
+
+
+def make_router(w: Workload, seed=0):
+    """The router's weights: W_route [N*C, N] and a zero b_route."""
+    rng = np.random.default_rng(seed + 7000)
+    return dict(W_route=_draw(rng, (w.N * w.C, w.N), 0.02, w.dtype == "bf16"),
+                b_route=np.zeros(w.N, dtype=np.float32))
 
 
 def as_float(d, key):

@@ -26,14 +26,15 @@ class xhc_desc(ctypes.Structure):
                 ("N", ctypes.c_int32), ("k", ctypes.c_int32), ("ncomp", ctypes.c_int32),
                 ("sinkhorn_iters", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
-                ("gram_schmidt", ctypes.c_int32), ("gs_eps", ctypes.c_float)]
+                ("gram_schmidt", ctypes.c_int32), ("gs_eps", ctypes.c_float),
+                ("route", ctypes.c_int32)]
 
 
 class xhc_fwd_args(ctypes.Structure):
     _fields_ = [("X", _vp), ("out", _vp), ("w4", _vp), ("w8", _vp), ("w12", _vp),
                 ("W", _vp), ("bias", _vp), ("active", ctypes.POINTER(ctypes.c_int32)),
                 ("X_new", _vp), ("h_in", _vp), ("z_save", _vp), ("xact_save", _vp),
-                ("timer", _vp)]
+                ("timer", _vp), ("W_route", _vp), ("b_route", _vp), ("route_idx", _vp)]
 
 
 class xhc_bwd_args(ctypes.Structure):
@@ -41,7 +42,8 @@ class xhc_bwd_args(ctypes.Structure):
                 ("W", _vp), ("bias", _vp), ("active", ctypes.POINTER(ctypes.c_int32)),
                 ("z_save", _vp), ("dX_new", _vp), ("dh_in", _vp), ("dX", _vp), ("dout", _vp),
                 ("dW", _vp), ("db", _vp), ("dw4", _vp), ("dw8", _vp), ("dw12", _vp),
-                ("accumulate", ctypes.c_int32), ("timer", _vp)]
+                ("accumulate", ctypes.c_int32), ("timer", _vp),
+                ("W_route", _vp), ("route_idx", _vp), ("dW_route", _vp), ("db_route", _vp)]
 
 
 class xhc_chain_args(ctypes.Structure):
@@ -93,6 +95,8 @@ def _load():
     L.xhc_timer_read.restype = ctypes.c_int
     L.xhc_kernel_count.argtypes = []
     L.xhc_kernel_count.restype = ctypes.c_int
+    L.xhc_zsave_stride.argtypes = [ctypes.POINTER(xhc_desc)]
+    L.xhc_zsave_stride.restype = ctypes.c_int32
     L.xhc_kernel_name.argtypes = [ctypes.c_int]
     L.xhc_kernel_name.restype = ctypes.c_char_p
     return L
@@ -102,8 +106,13 @@ lib = _load()
 
 
 def make_desc(B, S, C, N, k, ncomp, dtype, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID,
-              gram_schmidt=False, gs_eps=1e-6):
-    return xhc_desc(B, S, C, N, k, ncomp, iters, eps, dtype, gate_mode, int(gram_schmidt), gs_eps)
+              gram_schmidt=False, gs_eps=1e-6, route=0):
+    return xhc_desc(B, S, C, N, k, ncomp, iters, eps, dtype, gate_mode, int(gram_schmidt), gs_eps, int(route))
+
+
+def zsave_stride(desc):
+    """Floats per token of z_save (logits, r and, with a router, its record)."""
+    return lib.xhc_zsave_stride(ctypes.byref(desc))
 
 
 def workspace_size(desc, phase):
@@ -185,7 +194,8 @@ def _active_array(active):
 def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None, bias=None,
             z_save=None, xact_save=None, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID,
             workspace=None, stream=None, timer=None, desc=None, carry_in=None, W_next=None,
-            carry_out=None, gram_schmidt=False, gs_eps=1e-6, desc_next=None):
+            carry_out=None, gram_schmidt=False, gs_eps=1e-6, desc_next=None, route=0, W_route=None,
+            b_route=None, route_idx=None):
     """xhc_forward on torch device tensors.  X [B*S,N,C], out [B*S,C], W [N*C,P].
 
     With carry_in, W_next or carry_out given, calls xhc_forward_chain: carry_in
@@ -193,16 +203,20 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
     None); W_next [N*C,P] with carry_out (xhc_carry_size bytes) forms the next
     sublayer's projection partials from X_new; desc_next (an xhc_desc) describes
     that sublayer when it differs from this one (k, ncomp, ...).  gram_schmidt=True
-    orthogonalises the write-back components (modified Gram-Schmidt, epsilon gs_eps)."""
+    orthogonalises the write-back components (modified Gram-Schmidt, epsilon gs_eps).
+    route=R > 0 chooses the last R active slots per token with the router
+    (W_route [N*C,N], b_route [N]); route_idx [B*S,k] int32 receives the
+    per-token active lists, and active then needs only its first k-R entries."""
     T, N, C = X.shape
     ncomp = 4 if w4 is not None else 1
     if desc is None:
         desc = make_desc(B, S, C, N, len(active), ncomp, _dtype_code(X), iters, eps, gate_mode,
-                         gram_schmidt, gs_eps)
+                         gram_schmidt, gs_eps, route)
     act = _active_array(active)
     args = xhc_fwd_args(_ptr(X), _ptr(out), _ptr(w4), _ptr(w8), _ptr(w12), _ptr(W), _ptr(bias),
                         ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(X_new), _ptr(h_in),
-                        _ptr(z_save), _ptr(xact_save), None if timer is None else timer.handle)
+                        _ptr(z_save), _ptr(xact_save), None if timer is None else timer.handle,
+                        _ptr(W_route), _ptr(b_route), _ptr(route_idx))
     ws, need = _workspace(desc, XHC_PHASE_FWD, X.device, workspace)
     if carry_in is None and W_next is None and carry_out is None and desc_next is None:
         rc = lib.xhc_forward(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
@@ -221,18 +235,21 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
 def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None, w4=None, w8=None,
              w12=None, bias=None, z_save=None, db=None, dw4=None, dw8=None, dw12=None, accumulate=False,
              iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID, workspace=None, stream=None, timer=None,
-             desc=None, gram_schmidt=False, gs_eps=1e-6):
-    """xhc_backward on torch device tensors."""
+             desc=None, gram_schmidt=False, gs_eps=1e-6, route=0, W_route=None, route_idx=None,
+             dW_route=None, db_route=None):
+    """xhc_backward on torch device tensors (with a router: the forward's
+    z_save and route_idx, and dW_route [N*C,N] / db_route [N] fp32 outputs)."""
     T, N, C = X.shape
     ncomp = 4 if w4 is not None else 1
     if desc is None:
         desc = make_desc(B, S, C, N, len(active), ncomp, _dtype_code(X), iters, eps, gate_mode,
-                         gram_schmidt, gs_eps)
+                         gram_schmidt, gs_eps, route)
     act = _active_array(active)
     args = xhc_bwd_args(_ptr(X), _ptr(xact), _ptr(out), _ptr(w4), _ptr(w8), _ptr(w12), _ptr(W), _ptr(bias),
                         ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(z_save), _ptr(dX_new),
                         _ptr(dh_in), _ptr(dX), _ptr(dout), _ptr(dW), _ptr(db), _ptr(dw4), _ptr(dw8),
-                        _ptr(dw12), int(bool(accumulate)), None if timer is None else timer.handle)
+                        _ptr(dw12), int(bool(accumulate)), None if timer is None else timer.handle,
+                        _ptr(W_route), _ptr(route_idx), _ptr(dW_route), _ptr(db_route))
     ws, need = _workspace(desc, XHC_PHASE_BWD, X.device, workspace)
     rc = lib.xhc_backward(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
                           _stream_handle(stream))

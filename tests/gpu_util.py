@@ -31,7 +31,7 @@ def to_host(t):
 def device_inputs(d, bf16):
     dev = {}
     for key, a in d.items():
-        if key in ("w4", "w8", "w12", "bias"):
+        if key in ("w4", "w8", "w12", "bias", "b_route"):
             dev[key] = torch.from_numpy(a).to(DEV)
         else:
             dev[key] = to_dev(a, bf16)

@@ -1,0 +1,168 @@
+"""GPU parity of the router (desc.route = R > 0: the first k - R active
+streams fixed, the other R slots chosen per token by sigmoid scores over the
+LayerNorm'd flattened state, the routed write-back scaled by the score)
+against the oracle, through the C ABI.
+
+The choice is an integer decided by floating point.  The library decides on
+fp32 scores, the oracle on fp64 ones, so near ties may go either way; the
+tests therefore check that every GPU choice is a valid top-R under the
+oracle's scores within a score tolerance, that it agrees with the oracle's
+own choice on all but a small share of tokens, and then compare every
+output with the oracle run on the GPU's choice.  With W_route = 0 the scores
+are exactly b_route in both, and the choice (ties included) must match bit
+for bit.
+
+Tolerances as in the other parity tests: fp32 max|err| <= 1e-4 + 1e-4 |ref|,
+bf16 <= 1e-2 + 1e-2 |ref|; pass-through rows bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import xhc_oracle as xo
+from residual_stream_architecture_amd import synth
+from residual_stream_architecture_amd import xhc
+from tests.gpu_util import check_close, device_inputs, host_inputs, say, to_host
+
+pytestmark = pytest.mark.gpu
+W_ = synth.Workload
+
+# name, workload (route = R), fixed streams
+CASES = [
+    ("tiny_f32", W_("r", 1, 64, 64, 16, 4, 4, "f32", "fwdbwd", route=2), [0, 1]),
+    ("ragged_bf16", W_("r", 2, 77, 136, 16, 4, 4, "bf16", "fwdbwd", route=2), [5, 12]),
+    ("n8_k3_r1_f32", W_("r", 3, 30, 40, 8, 3, 4, "f32", "fwdbwd", route=1), [6, 1]),
+    ("all_routed_n6_f32", W_("r", 2, 25, 48, 6, 4, 4, "f32", "fwdbwd", route=4), []),
+    ("fix1_r3_bf16", W_("r", 2, 41, 96, 16, 4, 4, "bf16", "fwdbwd", route=3), [7]),
+    ("nc1_bf16", W_("r", 2, 50, 64, 16, 4, 1, "bf16", "fwdbwd", route=2), [3, 9]),
+    ("gs_bf16", W_("r", 2, 77, 136, 16, 4, 4, "bf16", "fwdbwd", gs=True, route=2), [5, 12]),
+    ("wide_bf16", W_("r", 1, 130, 1040, 16, 4, 4, "bf16", "fwdbwd", route=2), [4, 5]),
+    ("edge_c8_s1_f32", W_("r", 4, 1, 8, 16, 4, 4, "f32", "fwdbwd", route=2), [0, 15]),
+]
+GS_EPS = 1e-6
+
+
+def tol(w):
+    return (1e-4, 1e-4) if w.dtype == "f32" else (1e-2, 1e-2)
+
+
+def inputs(w, seed, grads):
+    d = synth.make_inputs(w, seed=seed, grads=grads)
+    d.update(synth.make_router(w, seed))
+    return d
+
+
+def host_kw(h, w, fixed):
+    convs = (h["w4"], h["w8"], h["w12"]) if w.ncomp == 4 else ()
+    return dict(args=(h["X"], h["out"], h["W"], h["bias"], list(fixed) + [0] * w.route, convs),
+                kw=dict(B=w.B, S=w.S, iters=w.iters, eps=w.eps, gram_schmidt_on=w.gs, gs_eps=GS_EPS,
+                        route=w.route, W_route=h["W_route"], b_route=h["b_route"]))
+
+
+def run_forward(w, dev, fixed, in_place=False):
+    T, C = w.T, w.C
+    X = dev["X"].clone()
+    Xn = X if in_place else torch.empty_like(X)
+    h_in = torch.empty(T, C, dtype=X.dtype, device=X.device)
+    desc = xhc.make_desc(w.B, w.S, C, w.N, w.k, w.ncomp, xhc.XHC_BF16 if w.dtype == "bf16" else xhc.XHC_F32,
+                         w.iters, w.eps, gram_schmidt=w.gs, gs_eps=GS_EPS, route=w.route)
+    z_save = torch.empty(T, xhc.zsave_stride(desc), dtype=torch.float32, device=X.device)
+    ridx = torch.full((T, w.k), -1, dtype=torch.int32, device=X.device)
+    conv = dict(w4=dev["w4"], w8=dev["w8"], w12=dev["w12"]) if w.ncomp == 4 else {}
+    xhc.forward(X, dev["out"], dev["W"], list(fixed) + [0] * w.route, Xn, h_in, B=w.B, S=w.S,
+                bias=dev["bias"], z_save=z_save, desc=desc, W_route=dev["W_route"], b_route=dev["b_route"],
+                route_idx=ridx, **conv)
+    torch.cuda.synchronize()
+    return Xn, h_in, z_save, ridx.cpu().numpy().astype(np.int64), desc
+
+
+def check_choice(rho, idx, fixed, R, atol=2e-3, rtol=1e-3):
+    """Every token's list: the fixed streams, then R distinct candidates that
+    form a top-R (in order) under the reference scores within a tolerance.
+    Returns the number of tokens whose list differs from the exact choice."""
+    T, N = rho.shape
+    k = idx.shape[1]
+    nfix = k - R
+    assert (idx[:, :nfix] == np.asarray(fixed, dtype=np.int64)[None, :]).all(), "fixed slots"
+    cand = np.array([i for i in range(N) if i not in fixed])
+    routed = idx[:, nfix:]
+    assert np.isin(routed, cand).all(), "a routed slot holds a fixed or invalid stream"
+    assert all(len(set(r)) == R for r in routed), "repeated stream in a routed list"
+    t_ = np.arange(T)[:, None]
+    chosen_rho = rho[t_, routed]
+    slack = atol + rtol * np.abs(rho).max(axis=1)
+    # in order (non-increasing) within the slack
+    assert (np.diff(chosen_rho, axis=1) <= slack[:, None]).all(), "routed slots out of score order"
+    # no unchosen candidate scores above the lowest chosen one beyond the slack
+    mask = np.zeros((T, N), dtype=bool)
+    mask[:, cand] = True
+    mask[t_, routed] = False
+    best_left = np.where(mask, rho, -np.inf).max(axis=1)
+    assert (best_left <= chosen_rho.min(axis=1) + slack).all(), "a better candidate was left out"
+    exact = xo.route_select(rho, fixed, R)
+    return int((exact != idx).any(axis=1).sum())
+
+
+def compare_forward(w, h, fixed, Xn, h_in, z_save, idx, ref):
+    atol, rtol = tol(w)
+    T, N = w.T, w.N
+    Xn_h = to_host(Xn)
+    act = np.zeros((T, N), dtype=bool)
+    act[np.arange(T)[:, None], idx] = True
+    assert np.array_equal(Xn_h[~act], h["X"][~act]), "pass-through rows differ"
+    check_close("X_new[active]", Xn_h[act], ref["X_new"][act], atol, rtol)
+    check_close("h_in", to_host(h_in), ref["h_in"], atol, rtol)
+    zs = z_save.cpu().numpy().astype(np.float64)
+    P, k, R = w.P, w.k, w.route
+    check_close("z", zs[:, :P], ref["z"], 1e-3, 1e-3)
+    check_close("mean", zs[:, P + 1], ref["mu"], 1e-5, 1e-4)
+    check_close("sd", zs[:, P + 2], ref["sd"], 1e-5, 1e-4)
+    rec = zs[:, P + 3:P + 3 + 3 * R].reshape(T, R, 3)
+    check_close("rho[routed]", rec[:, :, 0], np.take_along_axis(ref["rho"], idx[:, k - R:], axis=1), 2e-3, 1e-3)
+
+
+@pytest.mark.parametrize("name,w,fixed", CASES, ids=[c[0] for c in CASES])
+def test_route_forward_parity(name, w, fixed):
+    say(f"[route forward] {name} B={w.B} S={w.S} C={w.C} N={w.N} k={w.k} R={w.route} nc={w.ncomp} "
+        f"gs={w.gs} {w.dtype}")
+    d = inputs(w, 0, False)
+    h = host_inputs(d)
+    dev = device_inputs(d, w.dtype == "bf16")
+    Xn, h_in, z_save, idx, _ = run_forward(w, dev, fixed)
+    hk = host_kw(h, w, fixed)
+    rt = xo.forward(*hk["args"], **hk["kw"])
+    differ = check_choice(rt["rho"], idx, fixed, w.route)
+    say(f"  tokens whose choice differs from the exact one (near ties): {differ} of {w.T}")
+    assert differ <= max(1, w.T // 100)
+    ref = xo.forward(*hk["args"], **hk["kw"], route_idx=idx)
+    compare_forward(w, h, fixed, Xn, h_in, z_save, idx, ref)
+
+
+def test_route_forward_in_place_matches_out_of_place():
+    w = CASES[1][1]
+    fixed = CASES[1][2]
+    say(f"[route forward in place] B={w.B} S={w.S} C={w.C}")
+    d = inputs(w, 1, False)
+    dev = device_inputs(d, True)
+    a = run_forward(w, dev, fixed, in_place=False)
+    b = run_forward(w, dev, fixed, in_place=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and (a[3] == b[3]).all()
+
+
+def test_route_ties_go_to_the_lower_stream():
+    # W_route = 0: every score is exactly b_route, so the choice (ties
+    # included) is decided exactly and must equal the oracle's
+    w = W_("r", 2, 33, 64, 16, 4, 4, "f32", "fwd", route=2)
+    fixed = [2, 11]
+    say(f"[route ties] B={w.B} S={w.S} C={w.C}")
+    d = inputs(w, 2, False)
+    d["W_route"] = np.zeros_like(d["W_route"])
+    d["b_route"] = np.array([0.5, 1.0, 9.0, 1.0, 0.25, 1.0, 0.5, 0.75, 1.0, 0.0, 0.5, 9.0, 0.75, 0.5, 1.0, 0.5],
+                            dtype=np.float32)
+    h = host_inputs(d)
+    dev = device_inputs(d, False)
+    Xn, h_in, z_save, idx, _ = run_forward(w, dev, fixed)
+    assert (idx == np.array([2, 11, 1, 3])[None, :]).all(), idx[:3]
+    hk = host_kw(h, w, fixed)
+    ref = xo.forward(*hk["args"], **hk["kw"])
+    assert (ref["idx"] == idx).all()
+    compare_forward(w, h, fixed, Xn, h_in, z_save, idx, ref)
