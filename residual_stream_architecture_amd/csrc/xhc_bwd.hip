@@ -52,19 +52,26 @@ struct RowTable { int stream[5][4]; };   // row group -> 4 stream ids (-1 = none
 // 8 waves' partials are summed in LDS in a fixed order (deterministic) into
 // the tile's result buffer, written out once at the end:
 //   dpa[cb][t][0..16) = dH_pre,  dpa[cb][t][16 + a*4 + b] = dH_res[a][b].
+// ROUTE: the active list is per token (route_idx, staged for the tile in
+// LDS), B2's Wp gets the router's columns (W_route, stream i at column
+// 48 + i) and the post gates of routed slots are scaled by their scores
+// s = sigmoid(rho) from z_save's router record, as in the forward.
 // ---------------------------------------------------------------------------
-template <typename E, typename R>
+template <typename E, typename R, bool ROUTE>
 __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const void* __restrict__ dXn,
                                                           const void* __restrict__ dhin, float* __restrict__ dpa,
                                                           int T, int C, int N, int k, Act4 act, int ncb,
                                                           const float* __restrict__ zin, float* __restrict__ hpost,
                                                           int P, int nc, int unit_gates, const R* __restrict__ W,
-                                                          R* __restrict__ Wp, int64_t NC) {
+                                                          R* __restrict__ Wp, int64_t NC, int zsv,
+                                                          const int32_t* __restrict__ ridx,
+                                                          const R* __restrict__ Wr, int nfix) {
   constexpr int EB = E::bytes;
   constexpr int RING = EB == 2 ? 4 : 2;
   static_assert(BX_GRP % RING == 0 && BX_TOK % BX_GRP == 0, "ring slots must be static in a group");
   __shared__ float red[BX_GRP][BX_WAVES][80];
   __shared__ float res[BX_TOK][BX_OUT];
+  __shared__ int tid_s[BX_TOK][4];            // ROUTE: the tile's active lists
 
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int cb = lb % ncb;
@@ -77,7 +84,8 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
   const int tn = min(BX_TOK, T - t0);
 
   // B2's projection operand: this workgroup's slice of W -> Wp [NC][64]
-  // (zero padded past P); nothing reads it before B2
+  // (zero padded past P; with a router columns 48.. hold W_route); nothing
+  // reads it before B2
   {
     const int64_t nwp = NC * 64;
     const int64_t per = (nwp + gridDim.x - 1) / gridDim.x;
@@ -85,16 +93,29 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
     for (int64_t idx = beg + threadIdx.x; idx < end; idx += 64 * BX_WAVES) {
       const int64_t j = idx >> 6;
       const int pp = (int)(idx & 63);
-      Wp[idx] = pp < P ? W[(size_t)j * P + pp] : R(0);
+      R v = pp < P ? W[(size_t)j * P + pp] : R(0);
+      if (ROUTE && pp >= 48) v = pp - 48 < N ? Wr[(size_t)j * N + (pp - 48)] : R(0);
+      Wp[idx] = v;
     }
+  }
+  if constexpr (ROUTE) {
+    for (int j = threadIdx.x; j < BX_TOK * 4; j += 64 * BX_WAVES) {
+      const int tt = j >> 2, a = j & 3;
+      int v = 0;
+      if (tt < tn && a < k) v = ridx[(size_t)(t0 + tt) * k + a];
+      tid_s[tt][a] = (unsigned)v < (unsigned)N ? v : 0;     // never a row outside the state
+    }
+    __syncthreads();
   }
   // the tile's post gates for B1 (H_post[a*4 + m], recomputed from the saved
   // logits as the forward computed them), written by channel block 0
   if (cb == 0) {
     for (int j = threadIdx.x; j < tn * 16; j += 64 * BX_WAVES) {
       const int tt = j >> 4, e = j & 15, a = e >> 2, m = e & 3;
+      const float* zt = zin + (size_t)(t0 + tt) * zsv;
       float h = 0.f;
-      if (a < k && m < nc) h = unit_gates ? 1.f : sigmoid(zin[(size_t)(t0 + tt) * (P + 1) + N + a * nc + m]);
+      if (a < k && m < nc) h = unit_gates ? 1.f : sigmoid(zt[N + a * nc + m]);
+      if (ROUTE && a >= nfix && a < k) h *= sigmoid(zt[P + 3 + 3 * (a - nfix)]);
       hpost[(size_t)(t0 + tt) * 16 + e] = h;
     }
   }
@@ -103,7 +124,7 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
   const bool arow = r < N;
   const void* abase = src.base[arow ? r : 0];
   const int64_t astr = src.stride[arow ? r : 0];
-  const int brow = (r >= 1 && r <= k) ? act.id[r - 1] : 0;
+  const int brow = (!ROUTE && r >= 1 && r <= k) ? act.id[r - 1] : 0;
   const void* bbase = r == 0 ? dhin : dXn;
   const int64_t bstr = r == 0 ? (int64_t)C : (int64_t)N * C;
   const int64_t boff = r == 0 ? 0 : (int64_t)brow * C;
@@ -120,12 +141,15 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
   // token t0 + tt (clamped to the tile) -> ring slot q; channels past C are
   // zeroed in A so that they add nothing
   auto load = [&](int tt, int q) {
-    const int64_t t = t0 + min(tt, tn - 1);
+    const int ttc = min(tt, tn - 1);
+    const int64_t t = t0 + ttc;
+    int64_t bo = boff;
+    if constexpr (ROUTE) bo = (r >= 1 && r <= k) ? (int64_t)tid_s[ttc][min(r - 1, 3)] * C : 0;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const V8<E> x = V8<E>::load(abase, (size_t)(t * astr + cofs[ks]));
       av[q][ks] = kv[ks] ? x : V8<E>::zero();
-      bv[q][ks] = V8<E>::load(bbase, (size_t)(t * bstr + boff + cofs[ks]));
+      bv[q][ks] = V8<E>::load(bbase, (size_t)(t * bstr + bo + cofs[ks]));
     }
   };
 
@@ -150,7 +174,7 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
         idx = o < N ? o : -1;                                  // D[i][0]
       } else {
         const int a = (o - 16) >> 2, b = (o - 16) & 3;
-        if (a < k && b < k) idx = (1 + a) * 16 + act.id[b];    // D[i_b][1 + a]
+        if (a < k && b < k) idx = (1 + a) * 16 + (ROUTE ? tid_s[tg + u][b] : act.id[b]);   // D[i_b][1 + a]
       }
       float sum = 0.f;
       if (idx >= 0) {
@@ -189,6 +213,8 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
 //   BD_GRAM    (forward) the Gram record only; G is not read
 // Dot records: dpart[cb][t][DOT_STRIDE] with <G_a, U_m> at 32 + 4a + m and
 // the Gram record at 0..10 (BD_GRAM: dpart[cb][t][16], Gram at 0..10).
+// ROUTE: the rows G_a come from each token's active list (route_idx; uniform
+// scalar loads one token ahead of the loads they address).
 // ---------------------------------------------------------------------------
 enum { BD_FULL = 0, BD_GSDOTS = 1, BD_GSGRAD = 2, BD_GRAM = 3 };
 constexpr int GRAM_SPLIT = 8;   // segments of the forward Gram pass per backward segment
@@ -222,13 +248,13 @@ __device__ inline int reduce16_slot(int lane) {
   return ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
 }
 
-template <typename E, int NCOMP, bool FAST, int MODE>
+template <typename E, int NCOMP, bool FAST, int MODE, bool ROUTE>
 __global__ __launch_bounds__(256) void k_bdots(
     StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin,
     const void* __restrict__ out, const float* __restrict__ w4, const float* __restrict__ w8,
     const float* __restrict__ w12, const float* __restrict__ hpost, const float* __restrict__ gsS,
     float* __restrict__ dpart, void* __restrict__ dout, float* __restrict__ dwpart, int T, int S, int C, int N,
-    int kk, Act4 act, int lseg, int segs_per_seq) {
+    int kk, Act4 act, int lseg, int segs_per_seq, const int32_t* __restrict__ ridx) {
   using V2 = Vec<E, B1_CH>;
   constexpr int EB = E::bytes;
   constexpr bool GS = MODE != BD_FULL;
@@ -303,14 +329,28 @@ __global__ __launch_bounds__(256) void k_bdots(
   // keeps PF tokens of loads in flight
   constexpr int PF = 3;
   V2 gq[PF + 1][4], oq[PF + 1];
+  int nid[4];                       // ROUTE: active list of the token loaded next
+#pragma unroll
+  for (int a = 0; a < 4; ++a) nid[a] = act.id[a < k ? a : 0];
+  auto next_ids = [&](int s) {
+    if constexpr (ROUTE && NEED_G) {
+      const size_t t = tok0 + min(s, S - 1);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int v = ridx[t * k + (a < k ? a : 0)];
+        nid[a] = (unsigned)v < (unsigned)NS ? v : 0;
+      }
+    }
+  };
   auto load_tok = [&](int s, int q) {
     const size_t t = tok0 + min(s, S - 1);
     if constexpr (NEED_G) {
       const rsrc_t rg = make_rsrc(static_cast<const char*>(dXn) + t * tokb, tokb);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) gq[q][a] = bload<E, B1_CH>(rg, voff, (uint32_t)act.id[a < k ? a : 0] * rowb);
+      for (int a = 0; a < 4; ++a) gq[q][a] = bload<E, B1_CH>(rg, voff, (uint32_t)nid[a] * rowb);
     }
     oq[q] = bload<E, B1_CH>(rout, voff, (uint32_t)min(s, S - 1) * rowb);
+    next_ids(s + 1);
   };
   // post coefficients (and Sg) of one token (uniform: scalar loads), one token ahead
   float Hn[4][4], Sn[4][4];
@@ -335,6 +375,7 @@ __global__ __launch_bounds__(256) void k_bdots(
       }
     }
   };
+  next_ids(s0);
 #pragma unroll
   for (int q = 0; q < PF; ++q) load_tok(s0 + q, q);
   load_h(s0);
@@ -562,14 +603,28 @@ __global__ __launch_bounds__(256) void k_bdots(
 // ---------------------------------------------------------------------------
 constexpr int BCOEF_TOK = 4;
 
-template <typename E, bool GS>
+// ROUTE: the routed slots' write-back scale s_a = sigmoid(rho_a) enters as
+// in the forward (the effective post coefficient is s_a H_post[a, m]); with
+// dq[a, m] the gradient of that coefficient, dH_post = s_a dq and
+// ds_a = sum_m H_post[a, m] dq[a, m], drho_a = ds_a s_a (1 - s_a).  The
+// LayerNorm backward, with dy = drho W_route^T, y = (x - mean) / sd,
+//   dx = dy / sd - mean(dy) / sd - (x - mean) mean(dy y) / sd^2,
+//   mean(dy) = sum_a drho_a colsum_a / NC,  mean(dy y) = sum_a drho_a (rho_a - b_a) / NC,
+// goes to B2 as: the router's logit columns of its record (drho / sd at
+// column 48 + stream), gamma += mean(dy y) / sd^2 and a constant
+// mean * mean(dy y) / sd^2 - mean(dy) / sd added to every element.  dz_out
+// (DZ_R floats per token) also gets drho and mean * drho / sd per stream for
+// db_route and for dW_route's mean term; hres gets H_res for the pass kernel.
+template <typename E, bool GS, bool ROUTE>
 __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int ncba, const float* __restrict__ dpart,
                                               int ncb, const float* __restrict__ zin,
                                               const float* __restrict__ bias,
                                               float* __restrict__ dz_out, void* __restrict__ rec,
                                               int T, int64_t Tpad, int N, int k, int nc,
                                               int P, float inv_nc_total, int iters, int unit_gates,
-                                              float gs_ceps, float* __restrict__ hpost, float* __restrict__ gss) {
+                                              float gs_ceps, float* __restrict__ hpost, float* __restrict__ gss,
+                                              int zsv, int dzstride, const int32_t* __restrict__ ridx, int nfix,
+                                              float* __restrict__ hres) {
   extern __shared__ float hist[];   // [BCOEF_TOK][iters+1][16]
   __shared__ float dzs[BCOEF_TOK][64];
   const int e = threadIdx.x & 15, tok = threadIdx.x >> 4;
@@ -588,7 +643,7 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
   }
   #pragma unroll 8
   for (int cb = 0; cb < ncb; ++cb) dpost += dpart[((size_t)cb * T + tc) * DOT_STRIDE + 32 + e];
-  const float* z = zin + tc * (P + 1);
+  const float* z = zin + tc * zsv;
   const float r = z[P];
 
   // gates (recomputed from the logits, as the forward computed them)
@@ -596,6 +651,25 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
   const bool post_ok = (e >> 2) < k && (e & 3) < nc;
   const float hp = pre_ok ? (unit_gates ? 1.f : sigmoid(z[e])) : 0.f;
   const float hq = post_ok ? (unit_gates ? 1.f : sigmoid(z[N + (e >> 2) * nc + (e & 3)])) : 0.f;
+  // routed slots' scores and write-back scales (1 for fixed slots)
+  float sa[4];
+  int sid[4];
+#pragma unroll
+  for (int a2 = 0; a2 < 4; ++a2) {
+    sa[a2] = 1.f;
+    sid[a2] = 0;
+    if constexpr (ROUTE) {
+      if (a2 >= nfix && a2 < k) sa[a2] = sigmoid(z[P + 3 + 3 * (a2 - nfix)]);
+      if (a2 < k) {
+        const int v = ridx[(size_t)tc * k + a2];
+        sid[a2] = (unsigned)v < (unsigned)N ? v : 0;
+      }
+    }
+  }
+  float my_s = sa[0];
+#pragma unroll
+  for (int a2 = 1; a2 < 4; ++a2)
+    if ((e >> 2) == a2) my_s = sa[a2];
   if constexpr (GS) {
     // the token's 16 lanes share one wave: gather its records
     float gsum = 0.f;
@@ -613,7 +687,7 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
           g[n][m] = g[m][n];
         }
         D[m][n] = __shfl(dpost, base + m * 4 + n, 64);
-        Hp[m][n] = __shfl(hq, base + m * 4 + n, 64);
+        Hp[m][n] = __shfl(hq, base + m * 4 + n, 64) * sa[m];    // the effective coefficients
       }
     GsFwd f;
     gs_forward(g, gs_ceps, f);
@@ -648,10 +722,39 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
   } else {
     (void)gs_ceps; (void)hpost; (void)gss;
   }
+  // dpost is now the gradient of the effective post coefficient s_a H_post
   float dz_pre = 0.f, dz_post = 0.f;
   if (!unit_gates) {
     dz_pre = pre_ok ? dpre * hp * (1.f - hp) : 0.f;
-    dz_post = post_ok ? dpost * hq * (1.f - hq) : 0.f;
+    dz_post = post_ok ? (ROUTE ? my_s * dpost : dpost) * hq * (1.f - hq) : 0.f;
+  }
+  // router: drho per slot, then per stream
+  float drs = 0.f, gam_r = 0.f, cst = 0.f;   // this lane's stream: drho; LN gamma and constant
+  float rmu = 0.f, rsd = 1.f;
+  if constexpr (ROUTE) {
+    float v = hq * dpost;                    // ds_a over the quad of lanes of row a
+    v += row_xor<1>(v);
+    v += row_xor<2>(v);
+    const int base = (threadIdx.x & 63) & ~15;
+    rmu = z[P + 1];
+    rsd = z[P + 2];
+    float m1 = 0.f, m2 = 0.f;
+#pragma unroll
+    for (int a2 = 0; a2 < 4; ++a2) {
+      const float ds = __shfl(v, base + 4 * a2, 64);
+      if (a2 >= nfix && a2 < k) {
+        const float dr = ds * sa[a2] * (1.f - sa[a2]);
+        const int j = a2 - nfix;
+        m1 = fmaf(dr, z[P + 5 + 3 * j], m1);
+        m2 = fmaf(dr, z[P + 4 + 3 * j], m2);
+        if (sid[a2] == e) drs += dr;
+      }
+    }
+    m1 *= inv_nc_total;
+    m2 *= inv_nc_total;
+    const float isd = 1.f / rsd;
+    gam_r = m2 * isd * isd;
+    cst = rmu * gam_r - m1 * isd;
   }
 
   // Sinkhorn backward
@@ -692,6 +795,7 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
     g = valid ? (gR - t2) / rs : 0.f;
   }
   const float dL = g * H[e];
+  if (ROUTE && tv) hres[t * 16 + e] = H[iters * 16 + e];
 
   // assemble dz in the logit column layout
   dzs[tok][e] = 0.f; dzs[tok][16 + e] = 0.f; dzs[tok][32 + e] = 0.f; dzs[tok][48 + e] = 0.f;
@@ -715,7 +819,11 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
   const float inv_r = 1.f / r;
   if (tv) {
 #pragma unroll
-    for (int n = 0; n < 3; ++n) dz_out[t * 48 + e + 16 * n] = dzs[tok][e + 16 * n];
+    for (int n = 0; n < 3; ++n) dz_out[t * dzstride + e + 16 * n] = dzs[tok][e + 16 * n];
+    if constexpr (ROUTE) {
+      dz_out[t * dzstride + 48 + e] = drs;
+      dz_out[t * dzstride + 64 + e] = rmu * drs / rsd;
+    }
   }
   // B2's tile record (layout next to REC_BYTES); t in [T, Tpad) is written
   // as zeros.  In bf16 mode dz/r is stored as hi and lo bf16 halves: the dz
@@ -723,39 +831,52 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
   // keep fp32 accuracy.
   if (t < Tpad) {
     constexpr int EB = E::bytes;
-    unsigned char* rb = static_cast<unsigned char*>(rec) + (size_t)(t / B2_TT) * REC_BYTES;
+    constexpr int NT_REC = ROUTE ? 4 : 3;
+    unsigned char* rb = static_cast<unsigned char*>(rec) + (size_t)(t / B2_TT) * (ROUTE ? REC_R_BYTES : REC_BYTES);
     const int tt = (int)(t % B2_TT);
 #pragma unroll
-    for (int n = 0; n < 3; ++n) {
-      const int p = e + 16 * n;                      // logits 0..47
-      const float v = tv ? dzs[tok][p] * inv_r : 0.f;
+    for (int n = 0; n < NT_REC; ++n) {
+      const int p = e + 16 * n;                      // logits 0..47 (router: 48..63 = drho / sd per stream)
+      const float v = tv ? (n < 3 ? dzs[tok][p] * inv_r : drs / rsd) : 0.f;
       size_t o_dzr, dzr_half;
       if (p < 32) {
         o_dzr = REC_DZR0 + ((size_t)(((p >> 3) * 16 + tt) * 8 + (p & 7))) * EB;
+        dzr_half = rec_dzr0_half(EB);
+      } else if (ROUTE) {
+        o_dzr = RR_DZR1 + ((size_t)((((p - 32) >> 3) * 16 + tt) * 8 + ((p - 32) & 7))) * EB;
         dzr_half = rec_dzr0_half(EB);
       } else {
         o_dzr = REC_DZR1 + ((size_t)((((p - 32) >> 2) * 16 + tt) * 4 + ((p - 32) & 3))) * EB;
         dzr_half = rec_dzr1_half(EB);
       }
       const int pt = p >> 4, rr = p & 15, gt = tt >> 2, e4 = tt & 3;
-      const size_t o_dzrt = REC_DZRT + ((size_t)((pt * 4 + gt) * 16 + rr) * 4 + e4) * EB;
+      const size_t o_dzrt = (ROUTE ? RR_DZRT : REC_DZRT) + ((size_t)((pt * 4 + gt) * 16 + rr) * 4 + e4) * EB;
+      const size_t dzrt_half = (size_t)NT_REC * 4 * 16 * 4 * EB;
       if constexpr (EB == 2) {
         __bf16 hi, lo;
         split_bf16(v, hi, lo);
         *reinterpret_cast<__bf16*>(rb + o_dzr) = hi;
         *reinterpret_cast<__bf16*>(rb + o_dzr + dzr_half) = lo;
         *reinterpret_cast<__bf16*>(rb + o_dzrt) = hi;
-        *reinterpret_cast<__bf16*>(rb + o_dzrt + rec_dzrt_half(EB)) = lo;
+        *reinterpret_cast<__bf16*>(rb + o_dzrt + dzrt_half) = lo;
       } else {
         *reinterpret_cast<float*>(rb + o_dzr) = v;
         *reinterpret_cast<float*>(rb + o_dzrt) = v;
       }
     }
-    float* rco = reinterpret_cast<float*>(rb + REC_CO);
-    rco[(RF_PRE + e) * B2_TT + tt] = tv ? hp : 0.f;
-    rco[(RF_RES + e) * B2_TT + tt] = tv ? H[iters * 16 + e] : 0.f;
-    if (e < REC_NF - RF_GAMMA)
-      rco[(RF_GAMMA + e) * B2_TT + tt] = (tv && e == 0) ? al * inv_nc_total * inv_r * inv_r : 0.f;
+    const float gam = al * inv_nc_total * inv_r * inv_r + gam_r;
+    if constexpr (ROUTE) {
+      float* rco = reinterpret_cast<float*>(rb + RR_CO);
+      rco[(RRF_PRE + e) * B2_TT + tt] = tv ? hp : 0.f;
+      if (e < RRF_NF - RRF_GAMMA)
+        rco[(RRF_GAMMA + e) * B2_TT + tt] = tv ? (e == 0 ? gam : e == 1 ? cst : 0.f) : 0.f;
+    } else {
+      float* rco = reinterpret_cast<float*>(rb + REC_CO);
+      rco[(RF_PRE + e) * B2_TT + tt] = tv ? hp : 0.f;
+      rco[(RF_RES + e) * B2_TT + tt] = tv ? H[iters * 16 + e] : 0.f;
+      if (e < REC_NF - RF_GAMMA)
+        rco[(RF_GAMMA + e) * B2_TT + tt] = (tv && e == 0) ? gam : 0.f;
+    }
   }
 }
 
@@ -779,6 +900,14 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
 // store issued after the loads it needs.  The active rows' upstream
 // gradients G_a are exchanged through LDS; all of a tile's rows are read (a
 // tile earlier) before any is written, so dX may alias dX_new.
+// ROUTE: the active rows differ per token, so the row groups are simply
+// streams 4g..4g+3, and a lane's "pass" row is either dX_new[t, i] (i not
+// active for its token) or pass[t][b] = sum_a H_res[a, b] G_a (i = i_b),
+// formed beforehand by k_route_pass; the choice is made per lane from the
+// token's active list (loaded one step ahead of the addresses it selects).
+// The projection's K is 64 (the router's logit columns 48.. carry
+// drho / sd), dX also receives the LayerNorm constant, and dW has a fourth
+// 16-column tile (the router's, rows of 64 partials).
 // ---------------------------------------------------------------------------
 template <typename E> struct B2Lds {
   static constexpr int EB = E::bytes;
@@ -787,20 +916,28 @@ template <typename E> struct B2Lds {
   static constexpr int ROWTILE = 4 * GSTRIDE;
 };
 
-template <typename E>
+template <typename E, bool ROUTE>
 __global__ __launch_bounds__(512) void k_bgrad(
     StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin, const void* __restrict__ Wp,
     const unsigned char* __restrict__ rec, int ntiles, void* dX, float* __restrict__ dwp, int T, int C, int N, int k,
-    RowTable rows, int nrg, int ncb, int tok_per_split) {
+    RowTable rows, int nrg, int ncb, int tok_per_split, const void* __restrict__ passbuf,
+    const int32_t* __restrict__ ridx) {
   constexpr bool BF = E::bytes == 2;
   constexpr int EB = E::bytes;
   using LY = B2Lds<E>;
+  constexpr int RUSED = ROUTE ? REC_R_USED : REC_USED;     // record bytes copied to LDS
+  constexpr int RSTRIDE = ROUTE ? REC_R_BYTES : REC_BYTES; // record bytes per tile
+  constexpr int RCO = ROUTE ? RR_CO : REC_CO;
+  constexpr int RDZRT = ROUTE ? RR_DZRT : REC_DZRT;
+  constexpr int NPT = ROUTE ? 4 : 3;                       // 16-logit tiles of dz/r
+  constexpr int F_PRE = ROUTE ? RRF_PRE : RF_PRE;
+  constexpr int F_GAMMA = ROUTE ? RRF_GAMMA : RF_GAMMA;
   constexpr int DHB = B2_TT * B2_CB * EB;              // dh_in block of one tile ([t][B2_CB])
-  constexpr int SBUF = REC_USED + DHB;                 // LDS bytes of one tile's shared operands
-  constexpr int NREC = (REC_USED + 1023) / 1024;       // wave-wide copies of the record (last one partial)
+  constexpr int SBUF = RUSED + DHB;                    // LDS bytes of one tile's shared operands
+  constexpr int NREC = (RUSED + 1023) / 1024;          // wave-wide copies of the record (last one partial)
   constexpr int NCH = NREC + DHB / 1024;
   constexpr int STEP = B2_TT * B2_SUB;
-  static_assert(REC_USED % 16 == 0 && DHB % 1024 == 0 && REC_USED <= REC_BYTES, "record copy split");
+  static_assert(RUSED % 16 == 0 && DHB % 1024 == 0 && RUSED <= RSTRIDE, "record copy split");
   __shared__ __attribute__((aligned(16))) unsigned char rbuf[2][B2_SUB][SBUF];
   __shared__ __attribute__((aligned(16))) unsigned char gsh[B2_SUB][B2_WAVES][LY::ROWTILE];   // dX_new rows
   __shared__ __attribute__((aligned(16))) unsigned char xsh[B2_SUB][B2_WAVES][LY::ROWTILE];   // X rows
@@ -816,7 +953,7 @@ __global__ __launch_bounds__(512) void k_bgrad(
   const int stream = rows.stream[rg][slot];
   const bool wv = stream >= 0;
   const int srow = wv ? stream : 0;
-  const bool active_grp = rg == 0;
+  const bool active_grp = !ROUTE && rg == 0;
   const int c0 = cb * B2_CB + chalf * B2_WAVE_CH;   // this wave's channels c0 .. c0+32
   const int64_t NCs = (int64_t)N * C;
   const size_t jbase = (size_t)srow * C + c0;
@@ -828,7 +965,8 @@ __global__ __launch_bounds__(512) void k_bgrad(
   // proj A operand: W rows, permuted: A row m of j-tile jt -> channel
   // 8*(m/4) + 4*jt + m%4 ; K = 48 logits as a K=32 step (wa) and a K=16
   // step (wb)
-  V8<E> wa[2];
+  // (ROUTE: K = 64 as two K=32 steps, wa and wc)
+  V8<E> wa[2], wc[2];
   Vec<E, 4> wb[2];
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt) {
@@ -836,15 +974,20 @@ __global__ __launch_bounds__(512) void k_bgrad(
     const bool ok = wv && c0 + ch < C;
     const size_t row = (ok ? jbase + ch : 0) * 64;
     const V8<E> va = V8<E>::load(Wp, row + 8 * g4);
-    const Vec<E, 4> vb = Vec<E, 4>::load(Wp, row + 32 + 4 * g4);
     wa[jt] = ok ? va : V8<E>::zero();
-    wb[jt] = ok ? vb : Vec<E, 4>::zero();
+    if constexpr (ROUTE) {
+      const V8<E> vc = V8<E>::load(Wp, row + 32 + 8 * g4);
+      wc[jt] = ok ? vc : V8<E>::zero();
+    } else {
+      const Vec<E, 4> vb = Vec<E, 4>::load(Wp, row + 32 + 4 * g4);
+      wb[jt] = ok ? vb : Vec<E, 4>::zero();
+    }
   }
-  f32x4 dwacc[2][3];
+  f32x4 dwacc[2][NPT];
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-    for (int pt = 0; pt < 3; ++pt) dwacc[jt][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int pt = 0; pt < NPT; ++pt) dwacc[jt][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const void* xbase = src.base[srow];
   const int64_t xstride = src.stride[srow];
@@ -862,21 +1005,21 @@ __global__ __launch_bounds__(512) void k_bgrad(
     for (int s = 0; s < B2_SUB; ++s) {
       const int ta = t0 + s * B2_TT;
       const int tile = ta / B2_TT;
-      const rsrc_t rrec = make_rsrc(rec + (size_t)tile * REC_BYTES, tile < ntiles ? REC_BYTES : 0u);
+      const rsrc_t rrec = make_rsrc(rec + (size_t)tile * RSTRIDE, tile < ntiles ? (uint32_t)RSTRIDE : 0u);
       const rsrc_t rdh = make_rsrc(static_cast<const char*>(dhin) + (size_t)ta * dhrowb,
                                    clamp_bytes(ta < T ? T - ta : 0, dhrowb));
 #pragma unroll
       for (int q = 0; q < (NCH + B2_WAVES - 1) / B2_WAVES; ++q) {
         const int c = wave + q * B2_WAVES;
         if (c < NREC) {
-          if (c * 1024 + lane * 16 < REC_USED)
+          if (c * 1024 + lane * 16 < RUSED)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rrec, (lds_void_t*)&rbuf[b][s][c * 1024], 16,
                                                      c * 1024 + lane * 16, 0, 0, 0);
         } else if (c < NCH) {
           constexpr int PPT = B2_CB * EB / 16;             // 16-byte pieces per token
           const int e = (c - NREC) * 64 + lane;
           const uint32_t voff = ((uint32_t)(e / PPT) * C + cb * B2_CB + (e % PPT) * (16 / EB)) * EB;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rdh, (lds_void_t*)&rbuf[b][s][REC_USED + (c - NREC) * 1024], 16,
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rdh, (lds_void_t*)&rbuf[b][s][RUSED + (c - NREC) * 1024], 16,
                                                    voff, 0, 0, 0);
         }
       }
@@ -884,10 +1027,32 @@ __global__ __launch_bounds__(512) void k_bgrad(
   };
   // own rows of the B2_SUB tiles from t0, through buffer resources based at
   // each tile (tokens past the end read zeros)
-  V8<E> xo[B2_SUB], dvo[B2_SUB];
+  V8<E> xo[B2_SUB], dvo[B2_SUB], pvo[B2_SUB];
   const uint32_t xrowb = (uint32_t)xstride * EB;
   const uint32_t vx = ((uint32_t)r16 * (uint32_t)xstride + clc) * EB;
   const uint32_t vd = (((uint32_t)r16 * N + srow) * (uint32_t)C + clc) * EB;
+  // ROUTE: this lane's tokens' active lists for the step loaded next, and
+  // per loaded tile whether the lane's row comes from `pass`
+  int nid[B2_SUB][4];
+  bool from_pass[B2_SUB];
+#pragma unroll
+  for (int s = 0; s < B2_SUB; ++s) {
+    from_pass[s] = false;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) nid[s][a] = -1;
+  }
+  auto load_ids = [&](int t0) {
+    if constexpr (ROUTE) {
+#pragma unroll
+      for (int s = 0; s < B2_SUB; ++s) {
+        const int ta = t0 + s * B2_TT + r16;
+        const size_t tc = (size_t)(ta < T ? ta : T - 1);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) nid[s][a] = a < k ? ridx[tc * k + a] : -1;
+      }
+    }
+  };
+  const uint32_t prowb = (uint32_t)k * C * EB;       // bytes of one token's pass rows
   auto load_own = [&](int t0) {
 #pragma unroll
     for (int s = 0; s < B2_SUB; ++s) {
@@ -896,7 +1061,21 @@ __global__ __launch_bounds__(512) void k_bgrad(
       const rsrc_t rx = make_rsrc(static_cast<const char*>(xbase) + (size_t)ta * xrowb, clamp_bytes(left, xrowb));
       const rsrc_t rd = make_rsrc(static_cast<const char*>(dXn) + (size_t)ta * tokb, clamp_bytes(left, tokb));
       xo[s] = bload<E, 8>(rx, vx, 0);
-      dvo[s] = bload<E, 8>(rd, vd, 0);
+      if constexpr (ROUTE) {
+        // the slot of this lane's stream in its token's list (-1: not active);
+        // the row not used is addressed out of range, which reads nothing
+        int slot = -1;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          if (nid[s][a] == srow) slot = a;
+        from_pass[s] = slot >= 0;
+        const rsrc_t rp = make_rsrc(static_cast<const char*>(passbuf) + (size_t)ta * prowb, clamp_bytes(left, prowb));
+        const uint32_t vp = (((uint32_t)r16 * k + (slot >= 0 ? slot : 0)) * (uint32_t)C + clc) * EB;
+        dvo[s] = bload<E, 8>(rd, from_pass[s] ? 0x80000000u : vd, 0);
+        pvo[s] = bload<E, 8>(rp, from_pass[s] ? vp : 0x80000000u, 0);
+      } else {
+        dvo[s] = bload<E, 8>(rd, vd, 0);
+      }
     }
   };
   // dX of finished tiles, by buffer stores based at each tile: an
@@ -915,7 +1094,9 @@ __global__ __launch_bounds__(512) void k_bgrad(
 
   if (tbeg < tfin) {
     dma(tbeg, 0);
+    load_ids(tbeg);
     load_own(tbeg);
+    load_ids(tbeg + STEP);
   }
   int buf = 0;
   for (int t0 = tbeg; t0 < tfin; t0 += STEP) {
@@ -928,7 +1109,8 @@ __global__ __launch_bounds__(512) void k_bgrad(
     for (int s = 0; s < B2_SUB; ++s) {
       const bool ok = t0 + s * B2_TT + r16 < T && cv;
       *reinterpret_cast<V8<E>*>(&xsh[s][wave][rowoff]) = ok ? xo[s] : V8<E>::zero();
-      *reinterpret_cast<V8<E>*>(&gsh[s][wave][rowoff]) = ok ? dvo[s] : V8<E>::zero();
+      const V8<E> own = (ROUTE && from_pass[s]) ? pvo[s] : dvo[s];
+      *reinterpret_cast<V8<E>*>(&gsh[s][wave][rowoff]) = ok ? own : V8<E>::zero();
     }
     store_res();
     {
@@ -937,6 +1119,7 @@ __global__ __launch_bounds__(512) void k_bgrad(
       const int tn = t0 + STEP < tfin ? t0 + STEP : t0;
       dma(tn, buf ^ 1);
       load_own(tn);
+      load_ids(tn + STEP);
     }
     res_t0 = t0;
     __syncthreads();
@@ -949,7 +1132,28 @@ __global__ __launch_bounds__(512) void k_bgrad(
 
       // ---- proj on MFMA: D[c][t], 2 j-tiles; K = 48 logits as 32 + 16 ----
       f32x4 pj[2];
-      {
+      if constexpr (ROUTE) {
+        V8<E> bz0, bz0l, bz2, bz2l;
+        const int off0 = REC_DZR0 + (g4 * 16 + r16) * 8 * EB;
+        const int off2 = RR_DZR1 + (g4 * 16 + r16) * 8 * EB;
+        bz0 = *reinterpret_cast<const V8<E>*>(rb + off0);
+        bz2 = *reinterpret_cast<const V8<E>*>(rb + off2);
+        if constexpr (BF) {
+          bz0l = *reinterpret_cast<const V8<E>*>(rb + off0 + rec_dzr0_half(EB));
+          bz2l = *reinterpret_cast<const V8<E>*>(rb + off2 + rec_dzr0_half(EB));
+        }
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mma32(wa[jt], bz0, acc);
+          acc = mma32(wc[jt], bz2, acc);
+          if constexpr (BF) {
+            acc = mma32(wa[jt], bz0l, acc);
+            acc = mma32(wc[jt], bz2l, acc);
+          }
+          pj[jt] = acc;
+        }
+      } else {
         V8<E> bz0, bz0l;
         Vec<E, 4> bz1, bz1l;
         {
@@ -976,9 +1180,10 @@ __global__ __launch_bounds__(512) void k_bgrad(
       }
       // ---- assemble dX for (token tk, channels cl..cl+8) ----
       {
-        const float* co = reinterpret_cast<const float*>(rb + REC_CO);
-        const float hpre = co[(RF_PRE + srow) * B2_TT + r16];
-        const float gam = co[RF_GAMMA * B2_TT + r16];
+        const float* co = reinterpret_cast<const float*>(rb + RCO);
+        const float hpre = co[(F_PRE + srow) * B2_TT + r16];
+        const float gam = co[F_GAMMA * B2_TT + r16];
+        const float cst = ROUTE ? co[RRF_CONST * B2_TT + r16] : 0.f;
         float pass[8];
         if (active_grp) {
 #pragma unroll
@@ -999,7 +1204,7 @@ __global__ __launch_bounds__(512) void k_bgrad(
           gv.to_float(pass);
         }
         const V8<E> hv =
-            *reinterpret_cast<const V8<E>*>(rb + REC_USED + (r16 * B2_CB + chalf * B2_WAVE_CH + 8 * g4) * EB);
+            *reinterpret_cast<const V8<E>*>(rb + RUSED + (r16 * B2_CB + chalf * B2_WAVE_CH + 8 * g4) * EB);
         const V8<E> xv = *reinterpret_cast<const V8<E>*>(&xsh[s][wave][rowoff]);
         float xf[8], hf[8], o[8];
         xv.to_float(xf);
@@ -1011,6 +1216,7 @@ __global__ __launch_bounds__(512) void k_bgrad(
           v = fmaf(hpre, hf[q], v);
           v += pj[jt][e];
           v = fmaf(-gam, xf[q], v);
+          if constexpr (ROUTE) v += cst;
           o[q] = v;
         }
         const V8<E> ov = V8<E>::from_float(o);
@@ -1027,12 +1233,12 @@ __global__ __launch_bounds__(512) void k_bgrad(
       }
       // ---- dW on MFMA: A = X^T (rows = channels, K = 16 tokens) ----
       {
-        Vec<E, 4> bh[3], bl[3];
+        Vec<E, 4> bh[NPT], bl[NPT];
 #pragma unroll
-        for (int pt = 0; pt < 3; ++pt) {
-          const int off = REC_DZRT + ((pt * 4 + g4) * 16 + r16) * 4 * EB;
+        for (int pt = 0; pt < NPT; ++pt) {
+          const int off = RDZRT + ((pt * 4 + g4) * 16 + r16) * 4 * EB;
           bh[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off);
-          if constexpr (BF) bl[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off + rec_dzrt_half(EB));
+          if constexpr (BF) bl[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off + NPT * 4 * 16 * 4 * EB);
         }
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
@@ -1052,7 +1258,7 @@ __global__ __launch_bounds__(512) void k_bgrad(
             for (int q = 0; q < 4; ++q) xa.x[q] = *reinterpret_cast<const float*>(colp + (4 * g4 + q) * 8 * EB);
           }
 #pragma unroll
-          for (int pt = 0; pt < 3; ++pt) {
+          for (int pt = 0; pt < NPT; ++pt) {
             dwacc[jt][pt] = mma16(xa, bh[pt], dwacc[jt][pt]);
             if constexpr (BF) dwacc[jt][pt] = mma16(xa, bl[pt], dwacc[jt][pt]);
           }
@@ -1071,9 +1277,9 @@ __global__ __launch_bounds__(512) void k_bgrad(
       for (int e = 0; e < 4; ++e) {
         const int ch = 16 * jt + 4 * g4 + e;
         if (c0 + ch < C) {
-          float* dst = dwp + ((size_t)ts * NCs + jbase + ch) * 48;
+          float* dst = dwp + ((size_t)ts * NCs + jbase + ch) * (NPT * 16);
 #pragma unroll
-          for (int pt = 0; pt < 3; ++pt) dst[16 * pt + r16] = dwacc[jt][pt][e];
+          for (int pt = 0; pt < NPT; ++pt) dst[16 * pt + r16] = dwacc[jt][pt][e];
         }
       }
   }
@@ -1087,15 +1293,38 @@ constexpr int RED_CONV_LANES = 4;   // threads per conv-weight gradient (quad, s
 // One launch for the three parameter-gradient reductions; workgroup ranges:
 //   [0, nb_dw)              dW[j][p] = sum over token splits (B2 partials)
 //   [nb_dw, nb_dw + P)      db[p]    = sum over tokens of dz (one block per p)
-//   [nb_dw + P, ...)        dconv    = sum over sequence segments (B1 partials),
+//   [nb_dw + P, .. + nb_conv) dconv  = sum over sequence segments (B1 partials),
 //                            4 threads per output, each summing every 4th segment
+//   [.., + 32)              router: db_route[i] = sum_t drho[t, i] (blocks 0..15)
+//                            and rred[i] = sum_t mean drho[t, i] / sd (16..31)
+// dwp rows hold dwr floats, dz records dzs floats.
 __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, int nsplit, int64_t NC, int P,
                                                 float* __restrict__ dW, const float* __restrict__ dz, int T,
                                                 float* __restrict__ db, const float* __restrict__ cpart, int nseg,
                                                 int C, float* __restrict__ dw4, float* __restrict__ dw8,
-                                                float* __restrict__ dw12, int nb_dw, int accumulate) {
+                                                float* __restrict__ dw12, int nb_dw, int accumulate, int dwr,
+                                                int dzs, int nb_conv, float* __restrict__ db_route,
+                                                float* __restrict__ rred, int N) {
   __shared__ float sm[256];
   const int bid = blockIdx.x;
+  if (bid >= nb_dw + P + nb_conv) {
+    const int q = bid - (nb_dw + P + nb_conv);
+    const int i = q & 15;
+    float s = 0.f;
+    #pragma unroll 8
+    for (int t = threadIdx.x; t < T; t += 256) s += dz[(size_t)t * dzs + (q < 16 ? 48 : 64) + i];
+    sm[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (threadIdx.x < w) sm[threadIdx.x] += sm[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0 && i < N) {
+      if (q >= 16) rred[i] = sm[0];
+      else if (db_route) db_route[i] = (accumulate ? db_route[i] : 0.f) + sm[0];
+    }
+    return;
+  }
   if (bid < nb_dw) {
     // four consecutive logits of one row per thread (P <= 48 and the
     // partial rows are 48 floats, so a group of 4 never crosses a row)
@@ -1107,7 +1336,7 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, i
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     #pragma unroll 8
     for (int q = 0; q < nsplit; ++q) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(dwp + ((size_t)q * NC + j) * 48 + p0);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(dwp + ((size_t)q * NC + j) * dwr + p0);
       s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
     }
     float* dst = dW + (size_t)j * P + p0;
@@ -1121,7 +1350,7 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, i
     const int p = bid - nb_dw;
     float s = 0.f;
     #pragma unroll 8
-    for (int t = threadIdx.x; t < T; t += 256) s += dz[(size_t)t * 48 + p];
+    for (int t = threadIdx.x; t < T; t += 256) s += dz[(size_t)t * dzs + p];
     sm[threadIdx.x] = s;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
@@ -1166,6 +1395,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
     zin = zbuf;
   }
 
+  const bool rt = p.R > 0;
   void* Wp = ws + p.off_wp;
   float* dpart = reinterpret_cast<float*>(ws + p.off_dpart);
   float* dpa = reinterpret_cast<float*>(ws + p.off_dpa);
@@ -1174,87 +1404,123 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   float* dz = reinterpret_cast<float*>(ws + p.off_dz);
   unsigned char* rec = reinterpret_cast<unsigned char*>(ws + p.off_rec);
   float* dwp = reinterpret_cast<float*>(ws + p.off_dwpart2);
+  float* hres = reinterpret_cast<float*>(ws + p.off_hres);
+  void* pass = ws + p.off_pass;
+  float* rred = reinterpret_cast<float*>(ws + p.off_rred);
+  const int32_t* ridx = rt ? a->route_idx : nullptr;
   const StreamRows src = stream_rows(p, a->X, a->xact, a->active);
   Act4 act;
-  for (int b = 0; b < 4; ++b) act.id[b] = b < p.k ? a->active[b] : 0;
+  for (int b = 0; b < 4; ++b) act.id[b] = b < p.k && !rt ? a->active[b] : 0;
 
   {
     TimedLaunch tl(tm, KID_BXDOTS, st);
-    k_bxdots<E, R><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(
-        src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, zin, hpost, p.P, p.nc,
-        p.gate == XHC_GATE_UNIT, static_cast<const R*>(a->W), static_cast<R*>(Wp), p.NC);
+#define XHC_BX(RT)                                                                                             \
+  k_bxdots<E, R, RT><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(                                      \
+      src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, zin, hpost, p.P, p.nc,               \
+      p.gate == XHC_GATE_UNIT, static_cast<const R*>(a->W), static_cast<R*>(Wp), p.NC, p.zsv, ridx,             \
+      static_cast<const R*>(rt ? a->W_route : nullptr), p.nfix)
+    if (rt) XHC_BX(true); else XHC_BX(false);
+#undef XHC_BX
   }
   float* gss = reinterpret_cast<float*>(ws + p.off_gss);        // [T][16] Sg (Gram-Schmidt)
   const dim3 b1grid(p.b1_cblocks, p.B * p.b1_segs);
   const bool fast = p.N == 16 && p.k == 4;
-#define XHC_BDOTS(NCOMP, FAST, MODE)                                                                              \
-  k_bdots<E, NCOMP, FAST, MODE><<<b1grid, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12,    \
-                                                        hpost, gss, dpart, a->dout, dwpart, p.T, p.S, p.C, p.N, p.k, \
-                                                        act, p.b1_lseg, p.b1_segs)
+#define XHC_BDOTS_G(GRID, NCOMP, FAST, MODE, LSEG, SEGS, RT)                                                    \
+  k_bdots<E, NCOMP, FAST, MODE, RT><<<GRID, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12, \
+                                                          hpost, gss, dpart, a->dout, dwpart, p.T, p.S, p.C, p.N,  \
+                                                          p.k, act, LSEG, SEGS, ridx)
+#define XHC_BDOTS(NCOMP, MODE)                                                                                 \
+  do {                                                                                                         \
+    if (rt) {                                                                                                  \
+      if (fast) XHC_BDOTS_G(b1grid, NCOMP, true, MODE, p.b1_lseg, p.b1_segs, true);                            \
+      else XHC_BDOTS_G(b1grid, NCOMP, false, MODE, p.b1_lseg, p.b1_segs, true);                                \
+    } else {                                                                                                   \
+      if (fast) XHC_BDOTS_G(b1grid, NCOMP, true, MODE, p.b1_lseg, p.b1_segs, false);                           \
+      else XHC_BDOTS_G(b1grid, NCOMP, false, MODE, p.b1_lseg, p.b1_segs, false);                               \
+    }                                                                                                          \
+  } while (0)
   {
     TimedLaunch tl(tm, KID_BDOTS, st);
     if (p.gs) {
       int lseg, segs;
       dots_segments(p, lseg, segs);
       const dim3 g2(p.b1_cblocks, p.B * segs);
-      if (fast)
-        k_bdots<E, 4, true, BD_GSDOTS><<<g2, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12,
-                                                           hpost, gss, dpart, a->dout, dwpart, p.T, p.S, p.C, p.N,
-                                                           p.k, act, lseg, segs);
-      else
-        k_bdots<E, 4, false, BD_GSDOTS><<<g2, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12,
-                                                            hpost, gss, dpart, a->dout, dwpart, p.T, p.S, p.C, p.N,
-                                                            p.k, act, lseg, segs);
+      if (rt) {
+        if (fast) XHC_BDOTS_G(g2, 4, true, BD_GSDOTS, lseg, segs, true);
+        else XHC_BDOTS_G(g2, 4, false, BD_GSDOTS, lseg, segs, true);
+      } else {
+        if (fast) XHC_BDOTS_G(g2, 4, true, BD_GSDOTS, lseg, segs, false);
+        else XHC_BDOTS_G(g2, 4, false, BD_GSDOTS, lseg, segs, false);
+      }
     } else if (p.nc == 4) {
-      if (fast) XHC_BDOTS(4, true, BD_FULL); else XHC_BDOTS(4, false, BD_FULL);
+      XHC_BDOTS(4, BD_FULL);
     } else {
-      if (fast) XHC_BDOTS(1, true, BD_FULL); else XHC_BDOTS(1, false, BD_FULL);
+      XHC_BDOTS(1, BD_FULL);
     }
   }
   {
     TimedLaunch tl(tm, KID_BCOEF, st);
     const int nb = (int)((p.Tpad + BCOEF_TOK - 1) / BCOEF_TOK);
     const size_t shm = (size_t)BCOEF_TOK * (p.iters + 1) * 16 * sizeof(float);
-    if (p.gs)
-      k_bcoef<E, true><<<nb, 64, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T,
-                                            p.Tpad, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.iters,
-                                            p.gate == XHC_GATE_UNIT, p.gs_ceps, hpost, gss);
-    else
-      k_bcoef<E, false><<<nb, 64, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T,
-                                             p.Tpad, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.iters,
-                                             p.gate == XHC_GATE_UNIT, 0.f, nullptr, nullptr);
+#define XHC_BCOEF(GS, RT)                                                                                       \
+  k_bcoef<E, GS, RT><<<nb, 64, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T,  \
+                                          p.Tpad, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.iters,            \
+                                          p.gate == XHC_GATE_UNIT, GS ? p.gs_ceps : 0.f, hpost,                \
+                                          GS ? gss : nullptr, p.zsv, p.dzs, ridx, p.nfix, hres)
+    if (p.gs) {
+      if (rt) XHC_BCOEF(true, true); else XHC_BCOEF(true, false);
+    } else {
+      if (rt) XHC_BCOEF(false, true); else XHC_BCOEF(false, false);
+    }
+#undef XHC_BCOEF
   }
   if (p.gs) {
     TimedLaunch tl(tm, KID_BDOTS_GS, st);
-    if (fast) XHC_BDOTS(4, true, BD_GSGRAD); else XHC_BDOTS(4, false, BD_GSGRAD);
+    XHC_BDOTS(4, BD_GSGRAD);
   }
 #undef XHC_BDOTS
+#undef XHC_BDOTS_G
+  if (rt) {
+    TimedLaunch tl(tm, KID_RPASS, st);
+    launch_route_pass(p, a->dX_new, ridx, hres, pass, st);
+  }
   {
     TimedLaunch tl(tm, KID_BGRAD, st);
     RowTable rows;
     for (int g = 0; g < 5; ++g)
       for (int w = 0; w < 4; ++w) rows.stream[g][w] = -1;
-    for (int w = 0; w < p.k; ++w) rows.stream[0][w] = a->active[w];
-    int nxt = 0;
-    for (int i = 0; i < p.N; ++i) {
-      bool is_act = false;
-      for (int b = 0; b < p.k; ++b) is_act |= a->active[b] == i;
-      if (is_act) continue;
-      rows.stream[1 + nxt / 4][nxt % 4] = i;
-      ++nxt;
+    if (rt) {
+      for (int i = 0; i < p.N; ++i) rows.stream[i / 4][i % 4] = i;
+    } else {
+      for (int w = 0; w < p.k; ++w) rows.stream[0][w] = a->active[w];
+      int nxt = 0;
+      for (int i = 0; i < p.N; ++i) {
+        bool is_act = false;
+        for (int b = 0; b < p.k; ++b) is_act |= a->active[b] == i;
+        if (is_act) continue;
+        rows.stream[1 + nxt / 4][nxt % 4] = i;
+        ++nxt;
+      }
     }
     const int nb = p.b2_rowgroups * p.b2_cblocks * p.b2_ts;
-    k_bgrad<E><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, (int)(p.Tpad / B2_TT), a->dX, dwp,
-                                             p.T, p.C, p.N, p.k,
-                                             rows, p.b2_rowgroups, p.b2_cblocks, p.b2_tok_per_split);
+#define XHC_BGRAD(RT)                                                                                          \
+  k_bgrad<E, RT><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, (int)(p.Tpad / B2_TT), a->dX, \
+                                               dwp, p.T, p.C, p.N, p.k, rows, p.b2_rowgroups, p.b2_cblocks,    \
+                                               p.b2_tok_per_split, pass, ridx)
+    if (rt) XHC_BGRAD(true); else XHC_BGRAD(false);
+#undef XHC_BGRAD
   }
   {
     TimedLaunch tl(tm, KID_BREDUCE, st);
     const int nb_dw = (int)((p.NC * ((p.P + 3) / 4) + 255) / 256);
     const int nb_conv = p.nc == 4 ? (int)(((int64_t)p.C * 24 * RED_CONV_LANES + 255) / 256) : 0;
-    k_reduce<<<nb_dw + p.P + nb_conv, 256, 0, st>>>(dwp, p.b2_ts, p.NC, p.P, a->dW, dz, p.T, a->db,
-                                                     p.nc == 4 ? dwpart : nullptr, p.B * p.b1_segs, p.C, a->dw4,
-                                                     a->dw8, a->dw12, nb_dw, a->accumulate);
+    k_reduce<<<nb_dw + p.P + nb_conv + (rt ? 32 : 0), 256, 0, st>>>(
+        dwp, p.b2_ts, p.NC, p.P, a->dW, dz, p.T, a->db, p.nc == 4 ? dwpart : nullptr, p.B * p.b1_segs, p.C, a->dw4,
+        a->dw8, a->dw12, nb_dw, a->accumulate, p.dwr, p.dzs, nb_conv, rt ? a->db_route : nullptr, rred, p.N);
+  }
+  if (rt) {
+    TimedLaunch tl(tm, KID_RDWR, st);
+    launch_route_dwr(p, dwp, rred, a->dW_route, a->accumulate, st);
   }
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
 }
@@ -1275,13 +1541,13 @@ void launch_gram(const Plan& p, const void* out, const float* w4, const float* w
   StreamRows none{};
   Act4 act{};
   if (p.dtype == XHC_BF16)
-    k_bdots<BF16, 4, false, BD_GRAM><<<grid, 256, 0, st>>>(none, nullptr, nullptr, out, w4, w8, w12, nullptr, nullptr,
-                                                           gram, nullptr, nullptr, p.T, p.S, p.C, p.N, p.k, act,
-                                                           lseg, segs);
+    k_bdots<BF16, 4, false, BD_GRAM, false><<<grid, 256, 0, st>>>(none, nullptr, nullptr, out, w4, w8, w12, nullptr,
+                                                                  nullptr, gram, nullptr, nullptr, p.T, p.S, p.C,
+                                                                  p.N, p.k, act, lseg, segs, nullptr);
   else
-    k_bdots<F32, 4, false, BD_GRAM><<<grid, 256, 0, st>>>(none, nullptr, nullptr, out, w4, w8, w12, nullptr, nullptr,
-                                                          gram, nullptr, nullptr, p.T, p.S, p.C, p.N, p.k, act,
-                                                          lseg, segs);
+    k_bdots<F32, 4, false, BD_GRAM, false><<<grid, 256, 0, st>>>(none, nullptr, nullptr, out, w4, w8, w12, nullptr,
+                                                                 nullptr, gram, nullptr, nullptr, p.T, p.S, p.C,
+                                                                 p.N, p.k, act, lseg, segs, nullptr);
 }
 
 int launch_backward(const Plan& p, const xhc_bwd_args* a, void* ws, hipStream_t st) {

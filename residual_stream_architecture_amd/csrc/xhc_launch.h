@@ -78,5 +78,11 @@ void launch_gram(const Plan& p, const void* out, const float* w4, const float* w
                  hipStream_t st);
 // Router (xhc_route.hip): partial column sums of W_route, rcs[RCS_BLK][16].
 void launch_route_colsum(const Plan& p, const void* W_route, float* rcs, hipStream_t st);
+// Router, backward: pass[t][b] = sum_a H_res[a, b] G_a, and dW_route from
+// B2's partials.
+void launch_route_pass(const Plan& p, const void* dXn, const int32_t* ridx, const float* hres, void* pass,
+                       hipStream_t st);
+void launch_route_dwr(const Plan& p, const float* dwp, const float* rred, float* dWr, int accumulate,
+                      hipStream_t st);
 
 }  // namespace xhc

@@ -17,6 +17,8 @@
 //                   term, for the dX assembly of rows chosen per token
 //   k_route_dwr     (backward) dW_route from the dX pass's partials minus
 //                   the LayerNorm mean's share
+#include <algorithm>
+
 #include "xhc_device.h"
 #include "xhc_launch.h"
 
@@ -53,6 +55,78 @@ void launch_route_colsum(const Plan& p, const void* W_route, float* rcs, hipStre
     k_route_colsum<uint16_t><<<RCS_BLK, 256, 0, st>>>(static_cast<const uint16_t*>(W_route), p.NC, p.N, rcs);
   else
     k_route_colsum<float><<<RCS_BLK, 256, 0, st>>>(static_cast<const float*>(W_route), p.NC, p.N, rcs);
+}
+
+// pass[t][b][c] = sum_a H_res[a, b] dX_new[t, i_a, c] for b < k (storage
+// type, [T][k][C]).  Thread = 8 channels of one token; H_res ([T][16], row a
+// at 4a) and the active list come from the coefficient backward's records.
+template <typename E>
+__global__ __launch_bounds__(256) void k_route_pass(const void* __restrict__ dXn, const int32_t* __restrict__ ridx,
+                                                    const float* __restrict__ hres, void* __restrict__ pass,
+                                                    int64_t T, int C, int N, int k) {
+  const int64_t nch = C / 8;
+  for (int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x; w < T * nch; w += (int64_t)gridDim.x * 256) {
+    const int64_t t = w / nch;
+    const int c = (int)(w - t * nch) * 8;
+    float g[4][8];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      int id = a < k ? ridx[t * k + a] : 0;
+      id = (unsigned)id < (unsigned)N ? id : 0;
+      V8<E>::load(dXn, (size_t)(t * N + id) * C + c).to_float(g[a]);
+      if (a >= k)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) g[a][q] = 0.f;
+    }
+    const float* h = hres + t * 16;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b < k) {
+        float o[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          float v = 0.f;
+#pragma unroll
+          for (int a = 0; a < 4; ++a) v = fmaf(a < k ? h[a * 4 + b] : 0.f, g[a][q], v);
+          o[q] = v;
+        }
+        V8<E>::from_float(o).store(pass, (size_t)(t * k + b) * C + c);
+      }
+    }
+  }
+}
+
+// dW_route[j][i] = sum over token splits of B2's router partials (column
+// 48 + i of its 64-float rows) - rred[i] (the LayerNorm mean's share:
+// sum_t mean_t drho[t, i] / sd_t, the same for every row j).
+__global__ __launch_bounds__(256) void k_route_dwr(const float* __restrict__ dwp, int nsplit, int64_t NC, int N,
+                                                   const float* __restrict__ rred, float* __restrict__ dWr,
+                                                   int accumulate) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= NC * N) return;
+  const int64_t j = g / N;
+  const int i = (int)(g - j * N);
+  float s = 0.f;
+  #pragma unroll 8
+  for (int q = 0; q < nsplit; ++q) s += dwp[((size_t)q * NC + j) * 64 + 48 + i];
+  s -= rred[i];
+  dWr[g] = (accumulate ? dWr[g] : 0.f) + s;
+}
+
+void launch_route_pass(const Plan& p, const void* dXn, const int32_t* ridx, const float* hres, void* pass,
+                       hipStream_t st) {
+  const int64_t work = (int64_t)p.T * (p.C / 8);
+  const int nb = (int)std::min<int64_t>((work + 255) / 256, 16384);
+  if (p.dtype == XHC_BF16)
+    k_route_pass<BF16><<<nb, 256, 0, st>>>(dXn, ridx, hres, pass, p.T, p.C, p.N, p.k);
+  else
+    k_route_pass<F32><<<nb, 256, 0, st>>>(dXn, ridx, hres, pass, p.T, p.C, p.N, p.k);
+}
+
+void launch_route_dwr(const Plan& p, const float* dwp, const float* rred, float* dWr, int accumulate,
+                      hipStream_t st) {
+  const int nb = (int)((p.NC * p.N + 255) / 256);
+  k_route_dwr<<<nb, 256, 0, st>>>(dwp, p.b2_ts, p.NC, p.N, rred, dWr, accumulate);
 }
 
 }  // namespace xhc

@@ -166,3 +166,67 @@ def test_route_ties_go_to_the_lower_stream():
     ref = xo.forward(*hk["args"], **hk["kw"])
     assert (ref["idx"] == idx).all()
     compare_forward(w, h, fixed, Xn, h_in, z_save, idx, ref)
+
+
+def run_backward(w, dev, fixed, X, z_save, ridx_dev, in_place_dx=False, accumulate=False, init=None):
+    T, N, C, P = w.T, w.N, w.C, w.P
+    dXn = dev["dX_new"].clone()
+    dX = dXn if in_place_dx else torch.empty_like(dXn)
+    f32 = dict(dtype=torch.float32, device=dXn.device)
+    out = dict(dX=dX, dout=torch.empty(T, C, dtype=dXn.dtype, device=dXn.device),
+               dW=torch.empty((N * C, P), **f32), db=torch.empty((P,), **f32),
+               dW_route=torch.empty((N * C, N), **f32), db_route=torch.empty((N,), **f32))
+    if w.ncomp == 4:
+        out.update({key: torch.empty((C, K), **f32) for key, K in (("dw4", 4), ("dw8", 8), ("dw12", 12))})
+    if init is not None:
+        for key, v in init.items():
+            out[key].copy_(v)
+    conv = dict(w4=dev["w4"], w8=dev["w8"], w12=dev["w12"]) if w.ncomp == 4 else {}
+    grads = {key: out[key] for key in ("dw4", "dw8", "dw12") if key in out}
+    xhc.backward(X, dev["out"], dev["W"], list(fixed) + [0] * w.route, dXn, dev["dh_in"], out["dX"], out["dout"],
+                 out["dW"], B=w.B, S=w.S, bias=dev["bias"], z_save=z_save, db=out["db"], iters=w.iters, eps=w.eps,
+                 gram_schmidt=w.gs, gs_eps=GS_EPS, route=w.route, W_route=dev["W_route"], route_idx=ridx_dev,
+                 dW_route=out["dW_route"], db_route=out["db_route"], accumulate=accumulate, **conv, **grads)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name,w,fixed", CASES, ids=[c[0] for c in CASES])
+def test_route_backward_parity(name, w, fixed):
+    say(f"[route backward] {name} B={w.B} S={w.S} C={w.C} N={w.N} k={w.k} R={w.route} nc={w.ncomp} "
+        f"gs={w.gs} {w.dtype}")
+    d = inputs(w, 1, True)
+    h = host_inputs(d)
+    dev = device_inputs(d, w.dtype == "bf16")
+    _, _, z_save, idx, _ = run_forward(w, dev, fixed)
+    ridx_dev = torch.from_numpy(idx.astype(np.int32)).to(dev["X"].device)
+    hk = host_kw(h, w, fixed)
+    g = xo.backward(*hk["args"], h["dX_new"], h["dh_in"], **hk["kw"], route_idx=idx)
+    res = run_backward(w, dev, fixed, dev["X"], z_save, ridx_dev)
+    atol, rtol = tol(w)
+    for key, ref in (("dX", g["dX"]), ("dout", g["dout"]), ("dW", g["dW"]), ("db", g["db"]),
+                     ("dW_route", g["dW_route"]), ("db_route", g["db_route"])):
+        check_close(key, to_host(res[key]), ref, atol, rtol)
+    for m, key in enumerate(["dw4", "dw8", "dw12"][:w.ncomp - 1]):
+        check_close(key, to_host(res[key]), g["dconv"][m], atol, rtol)
+    # deterministic, and dX may overwrite dX_new
+    res2 = run_backward(w, dev, fixed, dev["X"], z_save, ridx_dev)
+    for key in res:
+        assert torch.equal(res[key], res2[key]), f"{key} not deterministic"
+    res3 = run_backward(w, dev, fixed, dev["X"], z_save, ridx_dev, in_place_dx=True)
+    for key in res:
+        assert torch.equal(res[key], res3[key]), f"{key} differs with dX == dX_new"
+
+
+def test_route_backward_accumulates():
+    name, w, fixed = CASES[1]
+    say(f"[route backward accumulate] {name}")
+    d = inputs(w, 3, True)
+    dev = device_inputs(d, True)
+    _, _, z_save, idx, _ = run_forward(w, dev, fixed)
+    ridx_dev = torch.from_numpy(idx.astype(np.int32)).to(dev["X"].device)
+    base = run_backward(w, dev, fixed, dev["X"], z_save, ridx_dev)
+    init = {key: torch.full_like(base[key], 0.25) for key in ("dW", "db", "dW_route", "db_route", "dw4")}
+    acc = run_backward(w, dev, fixed, dev["X"], z_save, ridx_dev, accumulate=True, init=init)
+    for key in init:
+        assert torch.allclose(acc[key], base[key] + 0.25, rtol=1e-6, atol=1e-6), key
