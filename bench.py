@@ -61,10 +61,16 @@ def kernel_bytes(w, esz, save_rows=True):
                for the next sublayer)
       gram     (Gram-Schmidt) reads out C
       bdots_gs (Gram-Schmidt) reads G 4C + out C; writes dout C  6C
-    plus the projection weights (N*C x P) where a kernel reads them."""
+    With the router:
+      route_pass reads G 4C; writes the pass rows 4C               8C
+      bgrad    reads state 16C + dX_new 12C + pass rows 4C + dh_in C;
+               writes dX 16C                                    49C
+    plus the projection weights (N*C x P, and N*C x N for the router) where
+    a kernel reads them."""
     T, C, N, k, P = w.T, w.C, w.N, w.k, w.P
     unit = T * C * esz
-    wbytes = N * C * P * esz
+    rt = getattr(w, "route", 0)
+    wbytes = N * C * P * esz + (N * C * N * esz if rt else 0)
     gs = getattr(w, "gs", False)
     kb = {
         "proj": N * unit + wbytes,
@@ -77,13 +83,16 @@ def kernel_bytes(w, esz, save_rows=True):
     if gs:
         kb["gram"] = unit
         kb["bdots_gs"] = (k + 1 + 1) * unit
+    if rt:
+        kb["route_pass"] = 2 * k * unit
+        del kb["mixproj"]
     return kb
 
 
 # the source file that holds each kernel (the shared headers count for all)
 KERNEL_SOURCE = {"proj": "xhc_fwd.hip", "mix": "xhc_fwd.hip", "bxdots": "xhc_bwd.hip", "bdots": "xhc_bwd.hip",
                  "bgrad": "xhc_bwd.hip", "mixproj": "xhc_chain.hip", "gram": "xhc_bwd.hip",
-                 "bdots_gs": "xhc_bwd.hip"}
+                 "bdots_gs": "xhc_bwd.hip", "route_pass": "xhc_route.hip"}
 
 
 def source_digest(kernel=None):
@@ -150,14 +159,19 @@ def cpu_baseline(w, ntok):
         S = min(left, w.S)
         sw = synth.Workload("cpu-sample", 1, S, w.C, w.N, w.k, w.ncomp, w.dtype, "fwdbwd")
         d = synth.make_inputs(sw, seed=seq, grads=True)
+        rkw = {}
+        if w.route:
+            d.update(synth.make_router(sw, seq))
         h = {k: synth.as_float(d, k) for k in d}
         del d
+        if w.route:
+            rkw = dict(route=w.route, W_route=h["W_route"], b_route=h["b_route"])
         convs = (h["w4"], h["w8"], h["w12"])
         t = time.perf_counter()
         xo.forward(h["X"], h["out"], h["W"], h["bias"], active, convs, B=1, S=S, iters=w.iters, eps=w.eps,
-                   gram_schmidt_on=w.gs)
+                   gram_schmidt_on=w.gs, **rkw)
         xo.backward(h["X"], h["out"], h["W"], h["bias"], active, convs, h["dX_new"], h["dh_in"], B=1, S=S,
-                    iters=w.iters, eps=w.eps, gram_schmidt_on=w.gs)
+                    iters=w.iters, eps=w.eps, gram_schmidt_on=w.gs, **rkw)
         dt += time.perf_counter() - t
         del h
         left -= S
@@ -166,7 +180,8 @@ def cpu_baseline(w, ntok):
     return {"value": round(ntok / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"numpy fp64 oracle forward+backward over {ntok} tokens ({seq} sequence(s) of at most "
                       f"{w.S}) of the same workload (C={w.C}, N={w.N}, k={w.k}, TFA on"
-                      f"{', Gram-Schmidt on' if w.gs else ''}): {dt:.1f} s of compute; "
+                      f"{', Gram-Schmidt on' if w.gs else ''}{', router' if w.route else ''}): "
+                      f"{dt:.1f} s of compute; "
                       f"BLAS threads={threads}, host cpus={os.cpu_count()}"}
 
 
@@ -294,6 +309,9 @@ def main():
     print(f"# workload {w}", file=sys.stderr, flush=True)
 
     d = synth.make_inputs(w, seed=0, grads=True)
+    rt = w.route
+    if rt:
+        d.update(synth.make_router(w, 0))
 
     def dev(a):
         if a.dtype == np.uint16:
@@ -307,10 +325,10 @@ def main():
     W = dev(d["W"])
     bias = dev(d["bias"])
     convs = dict(w4=dev(d["w4"]), w8=dev(d["w8"]), w12=dev(d["w12"]))
+    route_in = dict(W_route=dev(d["W_route"]), b_route=dev(d["b_route"])) if rt else {}
     del d
     sdt = X.dtype
     h_in = torch.empty(T, C, dtype=sdt, device="cuda")
-    z_save = torch.empty(T, P + 1, device="cuda")
     xact = torch.empty(T, k, C, dtype=sdt, device="cuda")
     dX = torch.empty_like(dXn)
     dout = torch.empty(T, C, dtype=sdt, device="cuda")
@@ -319,16 +337,24 @@ def main():
     dws = dict(dw4=torch.empty(C, 4, device="cuda"), dw8=torch.empty(C, 8, device="cuda"),
                dw12=torch.empty(C, 12, device="cuda"))
     desc = xhc.make_desc(w.B, w.S, C, N, k, w.ncomp, xhc.XHC_BF16 if w.dtype == "bf16" else xhc.XHC_F32,
-                         w.iters, w.eps, gram_schmidt=w.gs)
+                         w.iters, w.eps, gram_schmidt=w.gs, route=rt)
+    z_save = torch.empty(T, xhc.zsave_stride(desc), device="cuda")
     ws_f = torch.empty(xhc.workspace_size(desc, 0), dtype=torch.uint8, device="cuda")
     ws_b = torch.empty(xhc.workspace_size(desc, 1), dtype=torch.uint8, device="cuda")
     active = synth.active_streams(0, N, k)
+    fwd_kw = dict(xact_save=xact)
+    bwd_kw = dict(xact=xact)
+    if rt:
+        ridx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        fwd_kw.update(route_idx=ridx, **route_in)
+        bwd_kw.update(W_route=route_in["W_route"], route_idx=ridx,
+                      dW_route=torch.empty(N * C, N, device="cuda"), db_route=torch.empty(N, device="cuda"))
 
     def step(timer=None):
-        xhc.forward(X, out, W, active, X, h_in, B=w.B, S=w.S, bias=bias, z_save=z_save, xact_save=xact,
-                    workspace=ws_f, timer=timer, desc=desc, **convs)
-        xhc.backward(X, out, W, active, dXn, dhin, dX, dout, dW, B=w.B, S=w.S, xact=xact, bias=bias,
-                     z_save=z_save, db=db, workspace=ws_b, timer=timer, desc=desc, **convs, **dws)
+        xhc.forward(X, out, W, active, X, h_in, B=w.B, S=w.S, bias=bias, z_save=z_save,
+                    workspace=ws_f, timer=timer, desc=desc, **convs, **fwd_kw)
+        xhc.backward(X, out, W, active, dXn, dhin, dX, dout, dW, B=w.B, S=w.S, bias=bias,
+                     z_save=z_save, db=db, workspace=ws_b, timer=timer, desc=desc, **convs, **dws, **bwd_kw)
 
     for _ in range(args.warmup):
         step()
@@ -389,6 +415,8 @@ def main():
     impl_step_c = 16 + 26 + 21 + 6 + 49                             # what the kernels above touch
     if w.gs:
         impl_step_c += 1 + 5                                        # gram pass, the dots pass of B1
+    if rt:
+        impl_step_c += 8                                            # the pass rows (written, read)
     step_bytes = alg_step_c * T * C * esz
     result = {
         "metric": METRIC,
@@ -405,7 +433,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"xHC sublayer fwd+bwd ({w.name}): B={w.B} S={w.S} C={C} N={N} k={k} "
                                f"TFA K=4/8/12{', Gram-Schmidt' if w.gs else ''}, 20 Sinkhorn iters, "
-                               f"in-place forward + backward",
+                               + (f"router: {k - rt} fixed + {rt} routed streams per token, " if rt else "")
+                               + "in-place forward + backward",
                    "global_batch": w.B, "seq_len": w.S},
         "step_hbm": {"alg_bytes_per_token_in_C": alg_step_c, "touched_bytes_per_token_in_C": impl_step_c,
                      "alg_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),

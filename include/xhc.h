@@ -146,8 +146,8 @@ typedef struct {
                           (and with a router its record), or NULL; the
                           backward needs it                                   */
   void* xact_save;     /* [T,k,C] the k active rows of X before the update
-                          (slot order), or NULL; the backward needs it after
-                          an in-place call without a router                   */
+                          (slot order: with a router, each token's list), or
+                          NULL; the backward needs it after an in-place call  */
   xhc_timer* timer;    /* NULL, or a timer from xhc_timer_create             */
   /* router (read only when desc->route > 0) */
   const void* W_route; /* [N*C,N] router weights, storage type, row i*C + c   */
@@ -178,8 +178,8 @@ typedef struct {
   int32_t accumulate;  /* 0: overwrite dW/db/dw* (and dW_route/db_route);
                           1: add to them                                      */
   xhc_timer* timer;
-  /* router (read only when desc->route > 0; then X must be the forward's
-     input, xact NULL and z_save the forward's) */
+  /* router (read only when desc->route > 0; then z_save must be the
+     forward's) */
   const void* W_route; /* [N*C,N]                                             */
   const int32_t* route_idx;  /* [T,k] the forward's per-token active list     */
   float* dW_route;     /* [N*C,N] fp32                                        */

@@ -109,7 +109,7 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.off_zpart = o;  o = align256(o + (size_t)q.SK * T * q.ZST * 4);
   q.off_coef = o;   o = align256(o + (size_t)T * COEF_STRIDE * 4);
   q.off_gram = o;   o = align256(o + (q.gs ? (size_t)q.b1_cblocks * T * 16 * 4 : 0));
-  q.off_rcs = o;    o = align256(o + (q.R ? (size_t)RCS_BLK * 16 * 4 : 0));
+  q.off_rcs = o;    o = align256(o + (q.R ? (size_t)(RCS_BLK + 1) * 16 * 4 : 0));
   q.fwd_bytes = o;
   // backward reuses the forward regions (projection recompute) and adds:
   q.off_zbuf = o;   o = align256(o + (size_t)T * q.zsv * 4);
@@ -245,7 +245,6 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
   if (p.R) {
     // the router's choice and scores come from the forward's records
     if (!a->z_save || !a->route_idx || !a->W_route || !a->dW_route) return XHC_ERR_NULL;
-    if (a->xact) return XHC_ERR_UNSUPPORTED;
   }
   int rc = check_active(p, a->active);
   if (rc) return rc;

@@ -65,7 +65,8 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
                                                           int P, int nc, int unit_gates, const R* __restrict__ W,
                                                           R* __restrict__ Wp, int64_t NC, int zsv,
                                                           const int32_t* __restrict__ ridx,
-                                                          const R* __restrict__ Wr, int nfix) {
+                                                          const R* __restrict__ Wr, int nfix,
+                                                          const void* __restrict__ xact) {
   constexpr int EB = E::bytes;
   constexpr int RING = EB == 2 ? 4 : 2;
   static_assert(BX_GRP % RING == 0 && BX_TOK % BX_GRP == 0, "ring slots must be static in a group");
@@ -144,10 +145,22 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
     const int ttc = min(tt, tn - 1);
     const int64_t t = t0 + ttc;
     int64_t bo = boff;
-    if constexpr (ROUTE) bo = (r >= 1 && r <= k) ? (int64_t)tid_s[ttc][min(r - 1, 3)] * C : 0;
+    const void* ab = abase;
+    int64_t ao = t * astr;
+    if constexpr (ROUTE) {
+      bo = (r >= 1 && r <= k) ? (int64_t)tid_s[ttc][min(r - 1, 3)] * C : 0;
+      if (xact) {
+        // after an in-place forward, stream r's old row is saved at its slot
+        int slot = -1;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          if (a < k && tid_s[ttc][a] == r) slot = a;
+        if (slot >= 0) { ab = xact; ao = (t * k + slot) * C; }
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const V8<E> x = V8<E>::load(abase, (size_t)(t * astr + cofs[ks]));
+      const V8<E> x = V8<E>::load(ab, (size_t)(ao + cofs[ks]));
       av[q][ks] = kv[ks] ? x : V8<E>::zero();
       bv[q][ks] = V8<E>::load(bbase, (size_t)(t * bstr + bo + cofs[ks]));
     }
@@ -917,11 +930,11 @@ template <typename E> struct B2Lds {
 };
 
 template <typename E, bool ROUTE>
-__global__ __launch_bounds__(512) void k_bgrad(
+__device__ __forceinline__ void bgrad_body(
     StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin, const void* __restrict__ Wp,
     const unsigned char* __restrict__ rec, int ntiles, void* dX, float* __restrict__ dwp, int T, int C, int N, int k,
     RowTable rows, int nrg, int ncb, int tok_per_split, const void* __restrict__ passbuf,
-    const int32_t* __restrict__ ridx) {
+    const int32_t* __restrict__ ridx, const void* __restrict__ xact) {
   constexpr bool BF = E::bytes == 2;
   constexpr int EB = E::bytes;
   using LY = B2Lds<E>;
@@ -1027,20 +1040,16 @@ __global__ __launch_bounds__(512) void k_bgrad(
   };
   // own rows of the B2_SUB tiles from t0, through buffer resources based at
   // each tile (tokens past the end read zeros)
-  V8<E> xo[B2_SUB], dvo[B2_SUB], pvo[B2_SUB];
+  V8<E> xo[B2_SUB], dvo[B2_SUB];
   const uint32_t xrowb = (uint32_t)xstride * EB;
   const uint32_t vx = ((uint32_t)r16 * (uint32_t)xstride + clc) * EB;
   const uint32_t vd = (((uint32_t)r16 * N + srow) * (uint32_t)C + clc) * EB;
-  // ROUTE: this lane's tokens' active lists for the step loaded next, and
-  // per loaded tile whether the lane's row comes from `pass`
+  // ROUTE: this lane's tokens' active lists for the step loaded next
   int nid[B2_SUB][4];
-  bool from_pass[B2_SUB];
 #pragma unroll
-  for (int s = 0; s < B2_SUB; ++s) {
-    from_pass[s] = false;
+  for (int s = 0; s < B2_SUB; ++s)
 #pragma unroll
     for (int a = 0; a < 4; ++a) nid[s][a] = -1;
-  }
   auto load_ids = [&](int t0) {
     if constexpr (ROUTE) {
 #pragma unroll
@@ -1052,7 +1061,6 @@ __global__ __launch_bounds__(512) void k_bgrad(
       }
     }
   };
-  const uint32_t prowb = (uint32_t)k * C * EB;       // bytes of one token's pass rows
   auto load_own = [&](int t0) {
 #pragma unroll
     for (int s = 0; s < B2_SUB; ++s) {
@@ -1060,19 +1068,26 @@ __global__ __launch_bounds__(512) void k_bgrad(
       const int left = ta < T ? T - ta : 0;
       const rsrc_t rx = make_rsrc(static_cast<const char*>(xbase) + (size_t)ta * xrowb, clamp_bytes(left, xrowb));
       const rsrc_t rd = make_rsrc(static_cast<const char*>(dXn) + (size_t)ta * tokb, clamp_bytes(left, tokb));
-      xo[s] = bload<E, 8>(rx, vx, 0);
+      if (!ROUTE) xo[s] = bload<E, 8>(rx, vx, 0);
       if constexpr (ROUTE) {
-        // the slot of this lane's stream in its token's list (-1: not active);
-        // the row not used is addressed out of range, which reads nothing
+        // the slot of this lane's stream in its token's list (-1: not
+        // active) picks the row: pass[t][slot] or dX_new[t][stream], read
+        // through a per-lane address (tokens past the end read token T-1;
+        // their values are masked when published)
         int slot = -1;
 #pragma unroll
         for (int a = 0; a < 4; ++a)
           if (nid[s][a] == srow) slot = a;
-        from_pass[s] = slot >= 0;
-        const rsrc_t rp = make_rsrc(static_cast<const char*>(passbuf) + (size_t)ta * prowb, clamp_bytes(left, prowb));
-        const uint32_t vp = (((uint32_t)r16 * k + (slot >= 0 ? slot : 0)) * (uint32_t)C + clc) * EB;
-        dvo[s] = bload<E, 8>(rd, from_pass[s] ? 0x80000000u : vd, 0);
-        pvo[s] = bload<E, 8>(rp, from_pass[s] ? vp : 0x80000000u, 0);
+        const size_t tk = (size_t)(ta + r16 < T ? ta + r16 : T - 1);
+        const char* src_row = slot >= 0
+            ? static_cast<const char*>(passbuf) + ((tk * k + slot) * (size_t)C + clc) * EB
+            : static_cast<const char*>(dXn) + ((tk * N + srow) * (size_t)C + clc) * EB;
+        dvo[s] = V8<E>::load(src_row, 0);
+        // the state row: saved at its slot after an in-place forward
+        const char* x_row = (xact && slot >= 0)
+            ? static_cast<const char*>(xact) + ((tk * k + slot) * (size_t)C + clc) * EB
+            : static_cast<const char*>(xbase) + (tk * (size_t)xstride + clc) * EB;
+        xo[s] = V8<E>::load(x_row, 0);
       } else {
         dvo[s] = bload<E, 8>(rd, vd, 0);
       }
@@ -1109,8 +1124,7 @@ __global__ __launch_bounds__(512) void k_bgrad(
     for (int s = 0; s < B2_SUB; ++s) {
       const bool ok = t0 + s * B2_TT + r16 < T && cv;
       *reinterpret_cast<V8<E>*>(&xsh[s][wave][rowoff]) = ok ? xo[s] : V8<E>::zero();
-      const V8<E> own = (ROUTE && from_pass[s]) ? pvo[s] : dvo[s];
-      *reinterpret_cast<V8<E>*>(&gsh[s][wave][rowoff]) = ok ? own : V8<E>::zero();
+      *reinterpret_cast<V8<E>*>(&gsh[s][wave][rowoff]) = ok ? dvo[s] : V8<E>::zero();
     }
     store_res();
     {
@@ -1285,6 +1299,26 @@ __global__ __launch_bounds__(512) void k_bgrad(
   }
 }
 
+// The B2 kernels: the fixed-list form, and the routed form held to four
+// waves per SIMD (at most 128 VGPRs) so that two workgroups share a CU.
+template <typename E>
+__global__ __launch_bounds__(512) void k_bgrad(
+    StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin, const void* __restrict__ Wp,
+    const unsigned char* __restrict__ rec, int ntiles, void* dX, float* __restrict__ dwp, int T, int C, int N, int k,
+    RowTable rows, int nrg, int ncb, int tok_per_split) {
+  bgrad_body<E, false>(src, dXn, dhin, Wp, rec, ntiles, dX, dwp, T, C, N, k, rows, nrg, ncb, tok_per_split, nullptr,
+                       nullptr, nullptr);
+}
+template <typename E>
+__global__ __launch_bounds__(512, 4) void k_bgrad_route(
+    StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin, const void* __restrict__ Wp,
+    const unsigned char* __restrict__ rec, int ntiles, void* dX, float* __restrict__ dwp, int T, int C, int N, int k,
+    RowTable rows, int nrg, int ncb, int tok_per_split, const void* __restrict__ passbuf,
+    const int32_t* __restrict__ ridx, const void* __restrict__ xact) {
+  bgrad_body<E, true>(src, dXn, dhin, Wp, rec, ntiles, dX, dwp, T, C, N, k, rows, nrg, ncb, tok_per_split, passbuf,
+                      ridx, xact);
+}
+
 // ---------------------------------------------------------------------------
 // Deterministic reductions (fixed order, no atomics).
 // ---------------------------------------------------------------------------
@@ -1408,7 +1442,8 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   void* pass = ws + p.off_pass;
   float* rred = reinterpret_cast<float*>(ws + p.off_rred);
   const int32_t* ridx = rt ? a->route_idx : nullptr;
-  const StreamRows src = stream_rows(p, a->X, a->xact, a->active);
+  // with a router the saved rows are mapped per token inside the kernels
+  const StreamRows src = stream_rows(p, a->X, rt ? nullptr : a->xact, a->active);
   Act4 act;
   for (int b = 0; b < 4; ++b) act.id[b] = b < p.k && !rt ? a->active[b] : 0;
 
@@ -1418,7 +1453,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   k_bxdots<E, R, RT><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(                                      \
       src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, zin, hpost, p.P, p.nc,               \
       p.gate == XHC_GATE_UNIT, static_cast<const R*>(a->W), static_cast<R*>(Wp), p.NC, p.zsv, ridx,             \
-      static_cast<const R*>(rt ? a->W_route : nullptr), p.nfix)
+      static_cast<const R*>(rt ? a->W_route : nullptr), p.nfix, rt ? a->xact : nullptr)
     if (rt) XHC_BX(true); else XHC_BX(false);
 #undef XHC_BX
   }
@@ -1503,12 +1538,14 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
       }
     }
     const int nb = p.b2_rowgroups * p.b2_cblocks * p.b2_ts;
-#define XHC_BGRAD(RT)                                                                                          \
-  k_bgrad<E, RT><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, (int)(p.Tpad / B2_TT), a->dX, \
-                                               dwp, p.T, p.C, p.N, p.k, rows, p.b2_rowgroups, p.b2_cblocks,    \
-                                               p.b2_tok_per_split, pass, ridx)
-    if (rt) XHC_BGRAD(true); else XHC_BGRAD(false);
-#undef XHC_BGRAD
+    if (rt)
+      k_bgrad_route<E><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, (int)(p.Tpad / B2_TT),
+                                                     a->dX, dwp, p.T, p.C, p.N, p.k, rows, p.b2_rowgroups,
+                                                     p.b2_cblocks, p.b2_tok_per_split, pass, ridx, a->xact);
+    else
+      k_bgrad<E><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, (int)(p.Tpad / B2_TT), a->dX,
+                                               dwp, p.T, p.C, p.N, p.k, rows, p.b2_rowgroups, p.b2_cblocks,
+                                               p.b2_tok_per_split);
   }
   {
     TimedLaunch tl(tm, KID_BREDUCE, st);

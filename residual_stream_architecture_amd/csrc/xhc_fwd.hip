@@ -247,7 +247,7 @@ __global__ __launch_bounds__(64 * PROJ_WAVES) void k_proj(StreamRows src, const 
 // record.
 // ---------------------------------------------------------------------------
 struct RouteArgs {
-  const float* rcs;       // [RCS_BLK][16] partial column sums of W_route
+  const float* rcs;       // [RCS_BLK + 1][16]: partial column sums of W_route, then the sums
   const float* b_route;   // [N] or NULL
   int32_t* route_idx;     // [T][k] or NULL
   RowOrder cand;          // candidate e -> stream id
@@ -270,12 +270,7 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
   float r = 0.f;
   float zr = 0.f, ssum = 0.f;   // ROUTE: raw x.Wr of candidate e (or sum(x) at e == ncand), sum(x^2)
   if constexpr (ROUTE) {
-    // W_route's column sums, in a fixed order
-    if (threadIdx.x < 16) {
-      float a = 0.f;
-      for (int b = 0; b < RCS_BLK; ++b) a += ra.rcs[b * 16 + threadIdx.x];
-      csum[threadIdx.x] = a;
-    }
+    if (threadIdx.x < 16) csum[threadIdx.x] = ra.rcs[RCS_BLK * 16 + threadIdx.x];   // W_route's column sums
   }
   if (zpart) {
     float ss = (tv && e < SK) ? zpart[((size_t)e * T + t) * ZST + NTP] : 0.f;

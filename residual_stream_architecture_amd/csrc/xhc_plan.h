@@ -83,7 +83,7 @@ constexpr int REC_R_BYTES = 10240;
 static_assert(REC_R_USED <= REC_R_BYTES, "routed record");
 
 constexpr int NT_MAX = 4;   // logit tiles of 16: P = N + k*nc + k*k <= 48, plus the router's tile
-constexpr int RCS_BLK = 32; // partial column sums of W_route (forward router)
+constexpr int RCS_BLK = 256; // partial column sums of W_route (forward router), then the sums
 constexpr int DZ_R = 80;    // floats per token of the routed backward's dz record:
                             // dz [0,48), drho [48,64), mean*drho/sd [64,80)
 

@@ -11,7 +11,8 @@
 // so the projection pass forms x.Wr and sum(x) on MFMA next to the other
 // logits, and only Wr's column sums are needed apart (k_route_colsum).
 //
-//   k_route_colsum  W_route [NC, N] -> partial column sums [RCS_BLK][16]
+//   k_route_colsum  W_route [NC, N] -> partial column sums [RCS_BLK][16],
+//                   then (k_route_colsum_fin) the column sums [16]
 //   k_route_pass    (backward) pass[t][b] = sum_a H_res[a, b] G_a, the
 //                   gradient that reaches active row b through the mixing
 //                   term, for the dX assembly of rows chosen per token
@@ -50,11 +51,27 @@ __global__ __launch_bounds__(256) void k_route_colsum(const R* __restrict__ Wr, 
   }
 }
 
+// rcs[RCS_BLK][i] (the partials) -> rcs[RCS_BLK * 16 + i], in block order.
+__global__ __launch_bounds__(256) void k_route_colsum_fin(float* __restrict__ rcs) {
+  __shared__ float part[16][17];
+  const int c = threadIdx.x & 15, rl = threadIdx.x >> 4;
+  float s = 0.f;
+  for (int b = rl; b < RCS_BLK; b += 16) s += rcs[b * 16 + c];
+  part[rl][c] = s;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float a = 0.f;
+    for (int q = 0; q < 16; ++q) a += part[q][threadIdx.x];
+    rcs[RCS_BLK * 16 + threadIdx.x] = a;
+  }
+}
+
 void launch_route_colsum(const Plan& p, const void* W_route, float* rcs, hipStream_t st) {
   if (p.dtype == XHC_BF16)
     k_route_colsum<uint16_t><<<RCS_BLK, 256, 0, st>>>(static_cast<const uint16_t*>(W_route), p.NC, p.N, rcs);
   else
     k_route_colsum<float><<<RCS_BLK, 256, 0, st>>>(static_cast<const float*>(W_route), p.NC, p.N, rcs);
+  k_route_colsum_fin<<<1, 256, 0, st>>>(rcs);
 }
 
 // pass[t][b][c] = sum_a H_res[a, b] dX_new[t, i_a, c] for b < k (storage

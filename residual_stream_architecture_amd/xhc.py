@@ -16,6 +16,8 @@ XHC_PHASE_FWD, XHC_PHASE_BWD = 0, 1
 ERRORS = {0: "XHC_OK", -1: "XHC_ERR_NULL", -2: "XHC_ERR_SHAPE", -3: "XHC_ERR_INDEX",
           -4: "XHC_ERR_ALIAS", -5: "XHC_ERR_ALIGN", -6: "XHC_ERR_UNSUPPORTED",
           -7: "XHC_ERR_WORKSPACE", -8: "XHC_ERR_HIP"}
+(XHC_OK, XHC_ERR_NULL, XHC_ERR_SHAPE, XHC_ERR_INDEX, XHC_ERR_ALIAS, XHC_ERR_ALIGN, XHC_ERR_UNSUPPORTED,
+ XHC_ERR_WORKSPACE, XHC_ERR_HIP) = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 _vp = ctypes.c_void_p
 _fp = ctypes.POINTER(ctypes.c_float)

@@ -248,3 +248,103 @@ def test_strerror():
     for c in range(0, -9, -1):
         assert xhc.strerror(c)
     assert "unknown" in xhc.strerror(-99)
+
+
+# ---------------------------------------------------------------------------
+# router (desc.route > 0)
+# ---------------------------------------------------------------------------
+
+def routed_fwd(desc):
+    a, act = good_fwd(desc, inplace=False)
+    a.W_route, a.b_route, a.route_idx = fake(20), fake(21), fake(22)
+    return a, act
+
+
+def routed_bwd(desc):
+    a, act = good_bwd(desc)
+    a.xact = None
+    a.W_route, a.route_idx, a.dW_route, a.db_route = fake(20), fake(22), fake(23), fake(24)
+    return a, act
+
+
+def test_route_descriptions():
+    assert xhc.validate(desc16(route=2), routed_fwd(desc16(route=2))[0], xhc.XHC_PHASE_FWD) == xhc.XHC_OK
+    assert xhc.validate(desc16(route=5), routed_fwd(desc16())[0], xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_SHAPE
+    assert xhc.validate(desc16(route=-1), routed_fwd(desc16())[0], xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_SHAPE
+    # 16 candidates (no fixed stream at N = 16) do not fit the router's logit tile
+    assert xhc.workspace_size(desc16(route=4), xhc.XHC_PHASE_FWD) == 0
+    assert xhc.validate(desc16(route=4), routed_fwd(desc16())[0], xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_UNSUPPORTED
+    d = desc16(N=12, route=4)
+    assert xhc.validate(d, routed_fwd(d)[0], xhc.XHC_PHASE_FWD) == xhc.XHC_OK
+
+
+def test_route_zsave_stride_and_workspace():
+    P = 16 + 16 + 16
+    assert xhc.zsave_stride(desc16()) == P + 1
+    assert xhc.zsave_stride(desc16(route=2)) == P + 3 + 6
+    assert xhc.zsave_stride(desc16(route=3)) == P + 3 + 9
+    assert xhc.zsave_stride(desc16(route=9)) == 0
+    for phase in (xhc.XHC_PHASE_FWD, xhc.XHC_PHASE_BWD):
+        assert xhc.workspace_size(desc16(route=2), phase) > xhc.workspace_size(desc16(), phase)
+
+
+def test_route_forward_error_paths():
+    d = desc16(route=2)
+    a, _ = routed_fwd(d)
+    a.W_route = None
+    assert xhc.validate(d, a, xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_NULL
+    # only the fixed prefix of `active` is read: repeats past it are fine
+    a, act = routed_fwd(d)
+    act[2] = act[3] = act[0]
+    assert xhc.validate(d, a, xhc.XHC_PHASE_FWD) == xhc.XHC_OK
+    act[1] = act[0]
+    assert xhc.validate(d, a, xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_INDEX
+    a, _ = routed_fwd(d)
+    a.route_idx = fake(22, 4)
+    assert xhc.validate(d, a, xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_ALIGN
+    a, _ = routed_fwd(d)
+    a.route_idx = a.h_in                            # an output overlapping another
+    assert xhc.validate(d, a, xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_ALIAS
+    a, _ = routed_fwd(d)
+    a.route_idx = a.W_route                         # an output overlapping an input
+    assert xhc.validate(d, a, xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_ALIAS
+    # the router needs neither b_route nor route_idx
+    a, _ = routed_fwd(d)
+    a.b_route, a.route_idx = None, None
+    assert xhc.validate(d, a, xhc.XHC_PHASE_FWD) == xhc.XHC_OK
+
+
+def test_route_backward_error_paths():
+    d = desc16(route=2)
+    assert xhc.validate(d, routed_bwd(d)[0], xhc.XHC_PHASE_BWD) == xhc.XHC_OK
+    for field in ("z_save", "route_idx", "W_route", "dW_route"):
+        a, _ = routed_bwd(d)
+        setattr(a, field, None)
+        assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_ERR_NULL, field
+    a, _ = routed_bwd(d)
+    a.db_route = None
+    assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_OK
+    a, _ = routed_bwd(d)
+    a.xact = fake(2)                                # after an in-place forward
+    assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_OK
+    a, _ = routed_bwd(d)
+    a.dW_route = a.dW
+    assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_ERR_ALIAS
+    a, _ = routed_bwd(d)
+    a.db_route = a.route_idx
+    assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_ERR_ALIAS
+
+
+def test_route_not_chained():
+    d = desc16(route=2)
+    a, _ = routed_fwd(d)
+    c = xhc.xhc_chain_args(None, fake(30), fake(31), None)
+    assert chain_call(d, a, c) == xhc.XHC_ERR_UNSUPPORTED
+    a, _ = good_fwd(desc16(), inplace=False)
+    c = xhc.xhc_chain_args(None, fake(30), fake(31), ctypes.pointer(desc16(route=2)))
+    assert chain_call(desc16(), a, c) == xhc.XHC_ERR_UNSUPPORTED
+
+
+def test_route_kernel_names():
+    names = xhc.kernel_names()
+    assert {"route_colsum", "route_pass", "route_dwr"} <= set(names)

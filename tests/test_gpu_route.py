@@ -58,7 +58,7 @@ def host_kw(h, w, fixed):
                         route=w.route, W_route=h["W_route"], b_route=h["b_route"]))
 
 
-def run_forward(w, dev, fixed, in_place=False):
+def run_forward(w, dev, fixed, in_place=False, xact=None):
     T, C = w.T, w.C
     X = dev["X"].clone()
     Xn = X if in_place else torch.empty_like(X)
@@ -70,7 +70,7 @@ def run_forward(w, dev, fixed, in_place=False):
     conv = dict(w4=dev["w4"], w8=dev["w8"], w12=dev["w12"]) if w.ncomp == 4 else {}
     xhc.forward(X, dev["out"], dev["W"], list(fixed) + [0] * w.route, Xn, h_in, B=w.B, S=w.S,
                 bias=dev["bias"], z_save=z_save, desc=desc, W_route=dev["W_route"], b_route=dev["b_route"],
-                route_idx=ridx, **conv)
+                route_idx=ridx, xact_save=xact, **conv)
     torch.cuda.synchronize()
     return Xn, h_in, z_save, ridx.cpu().numpy().astype(np.int64), desc
 
@@ -168,7 +168,7 @@ def test_route_ties_go_to_the_lower_stream():
     compare_forward(w, h, fixed, Xn, h_in, z_save, idx, ref)
 
 
-def run_backward(w, dev, fixed, X, z_save, ridx_dev, in_place_dx=False, accumulate=False, init=None):
+def run_backward(w, dev, fixed, X, z_save, ridx_dev, in_place_dx=False, accumulate=False, init=None, xact=None):
     T, N, C, P = w.T, w.N, w.C, w.P
     dXn = dev["dX_new"].clone()
     dX = dXn if in_place_dx else torch.empty_like(dXn)
@@ -186,7 +186,8 @@ def run_backward(w, dev, fixed, X, z_save, ridx_dev, in_place_dx=False, accumula
     xhc.backward(X, dev["out"], dev["W"], list(fixed) + [0] * w.route, dXn, dev["dh_in"], out["dX"], out["dout"],
                  out["dW"], B=w.B, S=w.S, bias=dev["bias"], z_save=z_save, db=out["db"], iters=w.iters, eps=w.eps,
                  gram_schmidt=w.gs, gs_eps=GS_EPS, route=w.route, W_route=dev["W_route"], route_idx=ridx_dev,
-                 dW_route=out["dW_route"], db_route=out["db_route"], accumulate=accumulate, **conv, **grads)
+                 dW_route=out["dW_route"], db_route=out["db_route"], accumulate=accumulate, xact=xact, **conv,
+                 **grads)
     torch.cuda.synchronize()
     return out
 
@@ -230,3 +231,23 @@ def test_route_backward_accumulates():
     acc = run_backward(w, dev, fixed, dev["X"], z_save, ridx_dev, accumulate=True, init=init)
     for key in init:
         assert torch.allclose(acc[key], base[key] + 0.25, rtol=1e-6, atol=1e-6), key
+
+
+@pytest.mark.parametrize("case", [1, 2, 6], ids=[CASES[i][0] for i in (1, 2, 6)])
+def test_route_backward_after_in_place_forward(case):
+    # the in-place forward keeps each token's old active rows (slot order);
+    # the backward from the updated state and those rows equals the one from
+    # the forward's input, bit for bit
+    name, w, fixed = CASES[case]
+    say(f"[route backward in place] {name}")
+    d = inputs(w, 4, True)
+    dev = device_inputs(d, w.dtype == "bf16")
+    _, _, z_save, idx, _ = run_forward(w, dev, fixed)
+    ridx_dev = torch.from_numpy(idx.astype(np.int32)).to(dev["X"].device)
+    ref = run_backward(w, dev, fixed, dev["X"], z_save, ridx_dev)
+    xact = torch.empty(w.T, w.k, w.C, dtype=dev["X"].dtype, device=dev["X"].device)
+    Xn, _, z2, idx2, _ = run_forward(w, dev, fixed, in_place=True, xact=xact)
+    assert (idx2 == idx).all() and torch.equal(z2, z_save)
+    got = run_backward(w, dev, fixed, Xn, z2, ridx_dev, xact=xact)
+    for key in ref:
+        assert torch.equal(got[key], ref[key]), key
