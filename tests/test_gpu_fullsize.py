@@ -244,3 +244,74 @@ def test_stack48_teacher_forced():
             check_close(f"L{layer} X_new[s={s}]", got[:, active], ref["X_new"][k0:, active], 1e-2, 1e-2)
             check_close(f"L{layer} h_in[s={s}]", to_host(h_in[s:s + n]), ref["h_in"][k0:], 1e-2, 1e-2)
         say(f" layer {layer} ok at {time.time() - t_start:.1f}s")
+
+
+@pytest.mark.timeout(600)
+def test_fwdbwd4096_route_sampled():
+    # the router at the full fwd+bwd size, in the launch configuration the
+    # benchmark times (in-place forward with the saved rows, then the
+    # backward).  Sampled blocks as in the Gram-Schmidt test; each block's
+    # choice is checked against the oracle's scores, then its outputs against
+    # the oracle run on the GPU's choice.
+    from tests.test_gpu_route import check_choice
+    w = synth.WORKLOADS["fwdbwd4096_route"]
+    say(f"[fullsize] fwdbwd4096_route B={w.B} S={w.S} C={w.C} R={w.route}")
+    d = synth.make_inputs(w, seed=0, grads=True)
+    d.update(synth.make_router(w, 0))
+    p = dev_params(d)
+    Wr = to_dev(d["W_route"], True)
+    br = torch.from_numpy(d["b_route"]).cuda()
+    X = to_dev(d["X"], True)
+    dXn = to_dev(d["dX_new"], True)
+    dhin = to_dev(d["dh_in"], True)
+    fixed = synth.active_streams(0, w.N, w.k)[:w.k - w.route]
+    active = fixed + [0] * w.route
+    T, N, C, P, k = w.T, w.N, w.C, w.P, w.k
+    desc = xhc.make_desc(w.B, w.S, C, N, k, 4, xhc.XHC_BF16, w.iters, w.eps, route=w.route)
+    h_in = torch.empty(T, C, dtype=torch.bfloat16, device="cuda")
+    z_save = torch.empty(T, xhc.zsave_stride(desc), device="cuda")
+    xact = torch.empty(T, k, C, dtype=torch.bfloat16, device="cuda")
+    ridx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    xhc.forward(X, p["out"], p["W"], active, X, h_in, B=w.B, S=w.S, bias=p["bias"], z_save=z_save, xact_save=xact,
+                desc=desc, W_route=Wr, b_route=br, route_idx=ridx, **conv_kw(p, 4))
+    dX = torch.empty_like(dXn)
+    dout = torch.empty(T, C, dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty(N * C, P, device="cuda")
+    dWr = torch.empty(N * C, N, device="cuda")
+    dws = dict(dw4=torch.empty(C, 4, device="cuda"), dw8=torch.empty(C, 8, device="cuda"),
+               dw12=torch.empty(C, 12, device="cuda"))
+    xhc.backward(X, p["out"], p["W"], active, dXn, dhin, dX, dout, dW, B=w.B, S=w.S, xact=xact, bias=p["bias"],
+                 z_save=z_save, desc=desc, W_route=Wr, route_idx=ridx, dW_route=dWr, **conv_kw(p, 4), **dws)
+    torch.cuda.synchronize()
+    idx = ridx.cpu().numpy().astype(np.int64)
+    Xh = synth.bf16_to_f32(d["X"])
+    outh, hW, hWr = synth.as_float(d, "out"), synth.as_float(d, "W"), synth.as_float(d, "W_route")
+    dXnh, dhinh = synth.bf16_to_f32(d["dX_new"]), synth.bf16_to_f32(d["dh_in"])
+    convs = (d["w4"], d["w8"], d["w12"])
+    Xn_h = None
+    n = 24
+    for (b, s) in sample_blocks(w, n):
+        lo, hi = max(0, s - LEAD), min(w.S, s + n + LEAD)
+        rows = slice(b * w.S + lo, b * w.S + hi)
+        kw = dict(B=1, S=hi - lo, iters=w.iters, eps=w.eps, route=w.route, W_route=hWr, b_route=d["b_route"])
+        own = xo.forward(Xh[rows], outh[rows], hW, d["bias"], active, convs, **kw)
+        differ = check_choice(own["rho"], idx[rows], fixed, w.route)
+        assert differ <= 1, f"block (b={b}, s={s}): {differ} tokens chose otherwise"
+        ref = xo.forward(Xh[rows], outh[rows], hW, d["bias"], active, convs, route_idx=idx[rows], **kw)
+        g = xo.backward(Xh[rows], outh[rows], hW, d["bias"], active, convs, dXnh[rows], dhinh[rows],
+                        route_idx=idx[rows], **kw)
+        k0, t0 = s - lo, b * w.S + s
+        got = to_host(X[t0:t0 + n])
+        act = np.zeros((n, N), dtype=bool)
+        act[np.arange(n)[:, None], idx[t0:t0 + n]] = True
+        assert np.array_equal(got[~act], Xh[t0:t0 + n][~act]), f"pass-through rows (b={b}, s={s})"
+        check_close(f"X_new[b={b},s={s}]", got[act], ref["X_new"][k0:k0 + n][act], 1e-2, 1e-2)
+        check_close(f"h_in[b={b},s={s}]", to_host(h_in[t0:t0 + n]), ref["h_in"][k0:k0 + n], 1e-2, 1e-2)
+        check_close(f"dX[b={b},s={s}]", to_host(dX[t0:t0 + n]), g["dX"][k0:k0 + n], 1e-2, 1e-2)
+        check_close(f"dout[b={b},s={s}]", to_host(dout[t0:t0 + n]), g["dout"][k0:k0 + n], 1e-2, 1e-2)
+    # the saved rows are the old active rows of each token's own list
+    xs = to_host(xact[:64])
+    assert np.array_equal(xs, Xh[np.arange(64)[:, None], idx[:64]])
+    # every fixed slot holds its stream, every routed list is valid
+    assert (idx[:, :w.k - w.route] == np.array(fixed)).all()
+    assert ((idx >= 0) & (idx < N)).all() and all(len(set(r)) == k for r in idx[::97])
