@@ -1056,8 +1056,13 @@ __device__ __forceinline__ void bgrad_body(
       for (int s = 0; s < B2_SUB; ++s) {
         const int ta = t0 + s * B2_TT + r16;
         const size_t tc = (size_t)(ta < T ? ta : T - 1);
+        if (k == 4) {                                  // the token's list in one 16-byte load
+          const int4 v = *reinterpret_cast<const int4*>(ridx + tc * 4);
+          nid[s][0] = v.x; nid[s][1] = v.y; nid[s][2] = v.z; nid[s][3] = v.w;
+        } else {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) nid[s][a] = a < k ? ridx[tc * k + a] : -1;
+          for (int a = 0; a < 4; ++a) nid[s][a] = a < k ? ridx[tc * k + a] : -1;
+        }
       }
     }
   };

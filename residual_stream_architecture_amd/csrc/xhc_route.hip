@@ -75,40 +75,41 @@ void launch_route_colsum(const Plan& p, const void* W_route, float* rcs, hipStre
 }
 
 // pass[t][b][c] = sum_a H_res[a, b] dX_new[t, i_a, c] for b < k (storage
-// type, [T][k][C]).  Thread = 8 channels of one token; H_res ([T][16], row a
-// at 4a) and the active list come from the coefficient backward's records.
+// type, [T][k][C]).  Workgroup = one token and a block of RP_CH channels
+// (8 per thread), so the token's active list and H_res ([T][16], row a at
+// 4a, from the coefficient backward) are uniform loads.
+constexpr int RP_CH = 256 * 8;
 template <typename E>
 __global__ __launch_bounds__(256) void k_route_pass(const void* __restrict__ dXn, const int32_t* __restrict__ ridx,
                                                     const float* __restrict__ hres, void* __restrict__ pass,
-                                                    int64_t T, int C, int N, int k) {
-  const int64_t nch = C / 8;
-  for (int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x; w < T * nch; w += (int64_t)gridDim.x * 256) {
-    const int64_t t = w / nch;
-    const int c = (int)(w - t * nch) * 8;
-    float g[4][8];
+                                                    int64_t T, int C, int N, int k, int ncb) {
+  const int64_t t = blockIdx.x / ncb;
+  const int c = (int)(blockIdx.x - t * ncb) * RP_CH + threadIdx.x * 8;
+  if (c >= C) return;
+  int id[4];
+  float h[16];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      int id = a < k ? ridx[t * k + a] : 0;
-      id = (unsigned)id < (unsigned)N ? id : 0;
-      V8<E>::load(dXn, (size_t)(t * N + id) * C + c).to_float(g[a]);
-      if (a >= k)
+  for (int a = 0; a < 4; ++a) {
+    const int v = a < k ? ridx[t * k + a] : 0;
+    id[a] = (unsigned)v < (unsigned)N ? v : 0;
+  }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) g[a][q] = 0.f;
-    }
-    const float* h = hres + t * 16;
+  for (int e = 0; e < 16; ++e) h[e] = (e >> 2) < k && (e & 3) < k ? hres[t * 16 + e] : 0.f;
+  float g[4][8];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (b < k) {
-        float o[8];
+  for (int a = 0; a < 4; ++a) V8<E>::load(dXn, (size_t)(t * N + id[a]) * C + c).to_float(g[a]);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          float v = 0.f;
+  for (int b = 0; b < 4; ++b) {
+    if (b < k) {
+      float o[8];
 #pragma unroll
-          for (int a = 0; a < 4; ++a) v = fmaf(a < k ? h[a * 4 + b] : 0.f, g[a][q], v);
-          o[q] = v;
-        }
-        V8<E>::from_float(o).store(pass, (size_t)(t * k + b) * C + c);
+      for (int q = 0; q < 8; ++q) {
+        float v = 0.f;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) v = fmaf(h[a * 4 + b], g[a][q], v);   // rows a >= k have H_res 0
+        o[q] = v;
       }
+      V8<E>::from_float(o).store(pass, (size_t)(t * k + b) * C + c);
     }
   }
 }
@@ -132,12 +133,12 @@ __global__ __launch_bounds__(256) void k_route_dwr(const float* __restrict__ dwp
 
 void launch_route_pass(const Plan& p, const void* dXn, const int32_t* ridx, const float* hres, void* pass,
                        hipStream_t st) {
-  const int64_t work = (int64_t)p.T * (p.C / 8);
-  const int nb = (int)std::min<int64_t>((work + 255) / 256, 16384);
+  const int ncb = (p.C + RP_CH - 1) / RP_CH;
+  const int64_t nb = (int64_t)p.T * ncb;
   if (p.dtype == XHC_BF16)
-    k_route_pass<BF16><<<nb, 256, 0, st>>>(dXn, ridx, hres, pass, p.T, p.C, p.N, p.k);
+    k_route_pass<BF16><<<nb, 256, 0, st>>>(dXn, ridx, hres, pass, p.T, p.C, p.N, p.k, ncb);
   else
-    k_route_pass<F32><<<nb, 256, 0, st>>>(dXn, ridx, hres, pass, p.T, p.C, p.N, p.k);
+    k_route_pass<F32><<<nb, 256, 0, st>>>(dXn, ridx, hres, pass, p.T, p.C, p.N, p.k, ncb);
 }
 
 void launch_route_dwr(const Plan& p, const float* dwp, const float* rred, float* dWr, int accumulate,
