@@ -15,34 +15,42 @@ from tests.gpu_util import device_inputs, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("gs", [False, True])
-def test_forward_backward_graph_replays_match_eager(gs):
-    w = synth.Workload("g", 2, 96, 256, 16, 4, 4, "bf16", "fwdbwd")
-    say(f"[graph] B={w.B} S={w.S} C={w.C} gram_schmidt={gs}")
+@pytest.mark.parametrize("gs,route", [(False, 0), (True, 0), (False, 2)])
+def test_forward_backward_graph_replays_match_eager(gs, route):
+    w = synth.Workload("g", 2, 96, 256, 16, 4, 4, "bf16", "fwdbwd", route=route)
+    say(f"[graph] B={w.B} S={w.S} C={w.C} gram_schmidt={gs} route={route}")
     d = synth.make_inputs(w, seed=21, grads=True)
+    if route:
+        d.update(synth.make_router(w, 21))
     dev = device_inputs(d, True)
     T, N, C, P = w.T, w.N, w.C, w.P
     active = [3, 7, 11, 15]
-    desc = xhc.make_desc(w.B, w.S, C, N, 4, 4, xhc.XHC_BF16, gram_schmidt=gs)
+    desc = xhc.make_desc(w.B, w.S, C, N, 4, 4, xhc.XHC_BF16, gram_schmidt=gs, route=route)
+    ridx = torch.empty(T, 4, dtype=torch.int32, device="cuda")
+    rkw_f = dict(W_route=dev["W_route"], b_route=dev["b_route"], route_idx=ridx) if route else {}
     ws_f = torch.empty(xhc.workspace_size(desc, 0), dtype=torch.uint8, device="cuda")
     ws_b = torch.empty(xhc.workspace_size(desc, 1), dtype=torch.uint8, device="cuda")
     conv = dict(w4=dev["w4"], w8=dev["w8"], w12=dev["w12"])
 
     def buffers():
-        return dict(Xn=torch.empty_like(dev["X"]), h_in=torch.empty(T, C, dtype=torch.bfloat16, device="cuda"),
-                    z=torch.empty(T, P + 1, device="cuda"), dX=torch.empty_like(dev["X"]),
-                    dout=torch.empty(T, C, dtype=torch.bfloat16, device="cuda"),
-                    dW=torch.empty(N * C, P, device="cuda"), db=torch.empty(P, device="cuda"),
-                    dw4=torch.empty(C, 4, device="cuda"), dw8=torch.empty(C, 8, device="cuda"),
-                    dw12=torch.empty(C, 12, device="cuda"))
+        b = dict(Xn=torch.empty_like(dev["X"]), h_in=torch.empty(T, C, dtype=torch.bfloat16, device="cuda"),
+                 z=torch.empty(T, xhc.zsave_stride(desc), device="cuda"), dX=torch.empty_like(dev["X"]),
+                 dout=torch.empty(T, C, dtype=torch.bfloat16, device="cuda"),
+                 dW=torch.empty(N * C, P, device="cuda"), db=torch.empty(P, device="cuda"),
+                 dw4=torch.empty(C, 4, device="cuda"), dw8=torch.empty(C, 8, device="cuda"),
+                 dw12=torch.empty(C, 12, device="cuda"))
+        if route:
+            b.update(dWr=torch.empty(N * C, N, device="cuda"), dbr=torch.empty(N, device="cuda"))
+        return b
 
     def step(b):
         # out of place, so that a replay starts from the same state
         xhc.forward(dev["X"], dev["out"], dev["W"], active, b["Xn"], b["h_in"], B=w.B, S=w.S, bias=dev["bias"],
-                    z_save=b["z"], workspace=ws_f, desc=desc, **conv)
+                    z_save=b["z"], workspace=ws_f, desc=desc, **conv, **rkw_f)
+        rkw_b = dict(W_route=dev["W_route"], route_idx=ridx, dW_route=b["dWr"], db_route=b["dbr"]) if route else {}
         xhc.backward(dev["X"], dev["out"], dev["W"], active, dev["dX_new"], dev["dh_in"], b["dX"], b["dout"],
                      b["dW"], B=w.B, S=w.S, bias=dev["bias"], z_save=b["z"], db=b["db"], dw4=b["dw4"],
-                     dw8=b["dw8"], dw12=b["dw12"], workspace=ws_b, desc=desc, **conv)
+                     dw8=b["dw8"], dw12=b["dw12"], workspace=ws_b, desc=desc, **conv, **rkw_b)
 
     eager = buffers()
     step(eager)
