@@ -121,6 +121,12 @@ typedef struct {
   int32_t route;            /* 0: the active list of every token is `active`;
                                R > 0: R routed slots (the retrospective's
                                setting is k = 4, R = 2)                     */
+  int32_t per_token_active; /* 1: the caller gives every token its own list
+                               in route_idx [T,k] (an input to both calls;
+                               no router, write-back unscaled; the lists
+                               must hold distinct streams, ids outside
+                               [0, N) are read as 0); requires route = 0 and
+                               is not chained.  0: off                      */
 } xhc_desc;
 
 /* Optional per-kernel timer (HIP events around every kernel a call
@@ -149,11 +155,13 @@ typedef struct {
                           (slot order: with a router, each token's list), or
                           NULL; the backward needs it after an in-place call  */
   xhc_timer* timer;    /* NULL, or a timer from xhc_timer_create             */
-  /* router (read only when desc->route > 0) */
+  /* router (read only when desc->route > 0; route_idx also with
+     desc->per_token_active) */
   const void* W_route; /* [N*C,N] router weights, storage type, row i*C + c   */
   const float* b_route;  /* [N] or NULL (zero)                                */
   int32_t* route_idx;  /* [T,k] per-token active list (output), or NULL; the
-                          backward needs it                                   */
+                          backward needs it.  With desc->per_token_active
+                          the caller's lists (input, required)               */
 } xhc_fwd_args;
 
 typedef struct {
@@ -179,9 +187,9 @@ typedef struct {
                           1: add to them                                      */
   xhc_timer* timer;
   /* router (read only when desc->route > 0; then z_save must be the
-     forward's) */
+     forward's; route_idx also with desc->per_token_active) */
   const void* W_route; /* [N*C,N]                                             */
-  const int32_t* route_idx;  /* [T,k] the forward's per-token active list     */
+  const int32_t* route_idx;  /* [T,k] the forward's per-token active lists    */
   float* dW_route;     /* [N*C,N] fp32                                        */
   float* db_route;     /* [N] fp32, or NULL                                   */
 } xhc_bwd_args;

@@ -82,6 +82,9 @@ shared with the GPU library and listed in the design notes):
       (s_a = 1 for a fixed slot).  The choice itself is discrete: only the
       chosen streams' scores receive a gradient, through s_a.  R = 0 is the
       fixed active list of O5.
+  O8  per-token active lists given by the caller (`active_tok`, [T, k]):
+      O5's write with token t's own list in place of `active`, s = 1, and
+      no router.  It is the form in which another router's choice enters.
 """
 
 import numpy as np
@@ -242,7 +245,7 @@ def router(Xf, W_route, b_route, active, R, eps, route_idx=None):
 
 def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
             gate_mode="sigmoid", gram_schmidt_on=False, gs_eps=1e-6,
-            route=0, W_route=None, b_route=None, route_idx=None):
+            route=0, W_route=None, b_route=None, route_idx=None, active_tok=None):
     """One xHC sublayer update, forward ([R-DRSW] write formula, O1-O5).
 
     X:      [B*S, N, C]  residual state before the update
@@ -256,6 +259,7 @@ def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
             write-back component
     route, W_route [N*C, N], b_route [N] or None, route_idx: the router of
             O7 (route = number of routed slots)
+    active_tok: [T, k] per-token active lists (O8), or None
 
     Returns a dict with X_new, h_in and the intermediates (z, r, H_pre,
     H_post, H_res, U, idx [T, k] the per-token active list, s [T, k] the
@@ -270,7 +274,7 @@ def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
     ncomp = 1 + len(conv_ws)
     P = n_logits(N, k, ncomp)
     assert T == B * S and out.shape == (T, C) and W.shape == (N * C, P)
-    fixed = list(active)[:k - route]          # with a router only the fixed prefix is read
+    fixed = list(active)[:k - route] if active_tok is None else []   # the host list entries that are read
     assert len(set(int(a) for a in fixed)) == len(fixed) and all(0 <= a < N for a in fixed)
     bias = np.zeros(P) if bias is None else np.asarray(bias, dtype=np.float64)
 
@@ -294,7 +298,7 @@ def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
         U, _ = gram_schmidt(U, gs_eps)
 
     # the per-token active list: fixed, or fixed + routed (O7)
-    rt = _route(X.reshape(T, N * C), active, route, W_route, b_route, eps, route_idx)
+    rt = _route(X.reshape(T, N * C), active, route, W_route, b_route, eps, route_idx, active_tok)
     idx, s = rt["idx"], rt["s"]
 
     # sparse write: only the k active streams are rewritten
@@ -309,11 +313,16 @@ def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
     return res
 
 
-def _route(Xf, active, route, W_route, b_route, eps, route_idx):
-    """The per-token active list and scales: O5's fixed list (route = 0) or
-    O7's router."""
+def _route(Xf, active, route, W_route, b_route, eps, route_idx, active_tok=None):
+    """The per-token active list and scales: O5's fixed list (route = 0),
+    O7's router, or O8's given lists."""
     T, NC = Xf.shape
     k = len(active)
+    if active_tok is not None:
+        assert not route
+        idx = np.asarray(active_tok, dtype=np.int64).reshape(T, k)
+        assert all(len(set(r)) == k for r in idx)
+        return dict(idx=idx, s=np.ones((T, k)))
     if not route:
         return dict(idx=np.tile(np.asarray(active, dtype=np.int64), (T, 1)), s=np.ones((T, k)))
     assert 0 < route <= k
@@ -398,7 +407,7 @@ def gram_schmidt_backward(U, gs_eps, dUt):
 
 def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
              iters=20, eps=1e-6, gate_mode="sigmoid", gram_schmidt_on=False, gs_eps=1e-6,
-             route=0, W_route=None, b_route=None, route_idx=None):
+             route=0, W_route=None, b_route=None, route_idx=None, active_tok=None):
     """Gradients of the forward above for upstream gradients dX_new, dh_in.
 
     Returns dict(dX [T,N,C], dout [T,C], dW [N*C,P], db [P],
@@ -429,7 +438,7 @@ def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
     U_raw = tfa_components(out, B, S, conv_ws)
     U = gram_schmidt(U_raw, gs_eps)[0] if gram_schmidt_on else U_raw
 
-    rt = _route(Xf, act, route, W_route, b_route, eps, route_idx)
+    rt = _route(Xf, act, route, W_route, b_route, eps, route_idx, active_tok)
     idx, s = rt["idx"], rt["s"]
     tok = np.arange(T)[:, None]
     G = dX_new[tok, idx, :]                                       # [T, k, C]

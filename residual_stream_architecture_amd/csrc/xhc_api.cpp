@@ -32,6 +32,8 @@ int make_plan(const xhc_desc* d, Plan* p) {
   if (d->route < 0 || d->route > d->k) return XHC_ERR_SHAPE;
   // the router's candidates and the LayerNorm sum share one logit tile
   if (d->route > 0 && d->N - (d->k - d->route) > 15) return XHC_ERR_UNSUPPORTED;
+  if (d->per_token_active != 0 && d->per_token_active != 1) return XHC_ERR_UNSUPPORTED;
+  if (d->per_token_active && d->route) return XHC_ERR_UNSUPPORTED;
 
   Plan& q = *p;
   q.B = d->B; q.S = d->S; q.C = d->C; q.N = d->N; q.k = d->k; q.nc = d->ncomp;
@@ -44,13 +46,14 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.gs = d->gram_schmidt == 1 && q.nc == 4;
   q.gs_ceps = q.gs ? (float)q.C * d->gs_eps : 0.f;
   q.R = d->route;
+  q.pt = q.R > 0 || d->per_token_active == 1;
   q.nfix = q.k - q.R;
   q.ncand = q.R ? q.N - q.nfix : 0;
   if (q.R) q.NT = 4;                       // tile 3: router candidates + sum(x)
   q.zsv = q.R ? q.P + 3 + 3 * q.R : q.P + 1;
-  q.dzs = q.R ? DZ_R : 48;
-  q.dwr = q.R ? 64 : 48;
-  q.rec_bytes = q.R ? REC_R_BYTES : REC_BYTES;
+  q.dzs = q.pt ? DZ_R : 48;
+  q.dwr = q.pt ? 64 : 48;
+  q.rec_bytes = q.pt ? REC_R_BYTES : REC_BYTES;
 
   // forward
   q.SK = q.N;
@@ -77,8 +80,8 @@ int make_plan(const xhc_desc* d, Plan* p) {
   }
   q.bx_cblocks = (int)cdiv(q.C, BX_CB);
   q.bx_tiles = (int)cdiv(T, BX_TOK);
-  // with a router the active rows change per token: all rows in groups of 4
-  q.b2_rowgroups = q.R ? (int)cdiv(q.N, 4) : 1 + (int)cdiv(q.N - q.k, 4);
+  // with per-token lists the active rows change per token: all rows in groups of 4
+  q.b2_rowgroups = q.pt ? (int)cdiv(q.N, 4) : 1 + (int)cdiv(q.N - q.k, 4);
   q.b2_cblocks = (int)cdiv(q.C, B2_CB);
   q.Tpad = cdiv(T, B2_TT) * B2_TT;
   {
@@ -121,9 +124,9 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.off_rec = o;    o = align256(o + (size_t)(q.Tpad / B2_TT) * q.rec_bytes);
   q.off_dwpart2 = o; o = align256(o + (size_t)q.b2_ts * q.NC * q.dwr * 4);
   q.off_gss = o;    o = align256(o + (q.gs ? (size_t)T * 16 * 4 : 0));
-  q.off_hres = o;   o = align256(o + (q.R ? (size_t)T * 16 * 4 : 0));
-  q.off_pass = o;   o = align256(o + (q.R ? (size_t)T * q.k * q.C * q.esz : 0));
-  q.off_rred = o;   o = align256(o + (q.R ? (size_t)16 * 4 : 0));
+  q.off_hres = o;   o = align256(o + (q.pt ? (size_t)T * 16 * 4 : 0));
+  q.off_pass = o;   o = align256(o + (q.pt ? (size_t)T * q.k * q.C * q.esz : 0));
+  q.off_rred = o;   o = align256(o + (q.pt ? (size_t)16 * 4 : 0));
   q.bwd_bytes = o;
   return XHC_OK;
 }
@@ -139,10 +142,12 @@ static bool overlap(Span a, Span b) {
 }
 static bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
 
-// The host active list: all k entries, or with a router the k - R fixed ones.
+// The host active list: all k entries, with a router the k - R fixed ones,
+// with the caller's per-token lists none.
 static int check_active(const Plan& p, const int32_t* act) {
-  if (!act) return XHC_ERR_NULL;
-  for (int a = 0; a < p.nfix; ++a) {
+  const int n = p.pt && !p.R ? 0 : p.nfix;
+  if (n && !act) return XHC_ERR_NULL;
+  for (int a = 0; a < n; ++a) {
     if (act[a] < 0 || act[a] >= p.N) return XHC_ERR_INDEX;
     for (int b = 0; b < a; ++b)
       if (act[a] == act[b]) return XHC_ERR_INDEX;
@@ -173,10 +178,11 @@ static int validate_fwd(const Plan& p, const xhc_fwd_args* a, bool need_W = true
   if (p.nc == 4 && (!a->w4 || !a->w8 || !a->w12)) return XHC_ERR_NULL;
   if (p.nc == 1 && has_conv) return XHC_ERR_UNSUPPORTED;
   if (p.R && !a->W_route) return XHC_ERR_NULL;
+  if (p.pt && !p.R && !a->route_idx) return XHC_ERR_NULL;
   int rc = check_active(p, a->active);
   if (rc) return rc;
   const void* ptrs[] = {a->X, a->out, a->w4, a->w8, a->w12, a->W, a->bias, a->X_new, a->h_in, a->z_save, a->xact_save,
-                        p.R ? a->W_route : nullptr, p.R ? a->b_route : nullptr, p.R ? a->route_idx : nullptr};
+                        p.R ? a->W_route : nullptr, p.R ? a->b_route : nullptr, p.pt ? a->route_idx : nullptr};
   for (const void* q : ptrs)
     if (misaligned(q)) return XHC_ERR_ALIGN;
   const size_t T = p.T, e = p.esz;
@@ -189,10 +195,12 @@ static int validate_fwd(const Plan& p, const xhc_fwd_args* a, bool need_W = true
   const Span xs = span(a->xact_save, a->xact_save ? T * p.k * p.C * e : 0);
   const Span Wr = span(p.R ? a->W_route : nullptr, (size_t)p.NC * p.N * e);
   const Span br = span(p.R ? a->b_route : nullptr, (size_t)p.N * 4);
-  const Span ri = span(p.R ? a->route_idx : nullptr, T * p.k * 4);
+  const Span ri = span(p.pt ? a->route_idx : nullptr, T * p.k * 4);
   if (a->X_new != a->X && overlap(X, Xn)) return XHC_ERR_ALIAS;
-  std::vector<Span> outs = {Xn, hin, zs, xs, ri};
+  const bool ri_out = p.R > 0;                  // the router writes the lists; given lists are read
+  std::vector<Span> outs = {Xn, hin, zs, xs};
   std::vector<Span> ins = {X, out, W, bias, w4, w8, w12, Wr, br};
+  (ri_out ? outs : ins).push_back(ri);
   if (any_overlap(outs, ins, Xn, X)) return XHC_ERR_ALIAS;
   return XHC_OK;
 }
@@ -201,7 +209,7 @@ static int validate_fwd(const Plan& p, const xhc_fwd_args* a, bool need_W = true
 // pn: the next sublayer's plan (== p without desc_next)
 static int validate_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const xhc_chain_args* c) {
   if (!c) return XHC_OK;
-  if (p.R || pn.R) return XHC_ERR_UNSUPPORTED;
+  if (p.pt || pn.pt) return XHC_ERR_UNSUPPORTED;
   if ((c->W_next == nullptr) != (c->carry_out == nullptr)) return XHC_ERR_NULL;
   if (misaligned(c->carry_in) || misaligned(c->carry_out) || misaligned(c->W_next)) return XHC_ERR_ALIGN;
   if (pn.B != p.B || pn.S != p.S || pn.C != p.C || pn.N != p.N || pn.dtype != p.dtype) return XHC_ERR_SHAPE;
@@ -246,11 +254,14 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
     // the router's choice and scores come from the forward's records
     if (!a->z_save || !a->route_idx || !a->W_route || !a->dW_route) return XHC_ERR_NULL;
   }
+  if (p.pt && !a->route_idx) return XHC_ERR_NULL;
+  // recomputing the logits maps saved rows by the host list: not per token
+  if (p.pt && a->xact && !a->z_save) return XHC_ERR_UNSUPPORTED;
   int rc = check_active(p, a->active);
   if (rc) return rc;
   const void* ptrs[] = {a->X, a->xact, a->out, a->w4, a->w8, a->w12, a->W, a->bias, a->z_save, a->dX_new,
                         a->dh_in, a->dX, a->dout, a->dW, a->db, a->dw4, a->dw8, a->dw12,
-                        p.R ? a->W_route : nullptr, p.R ? a->route_idx : nullptr,
+                        p.R ? a->W_route : nullptr, p.pt ? a->route_idx : nullptr,
                         p.R ? a->dW_route : nullptr, p.R ? a->db_route : nullptr};
   for (const void* q : ptrs)
     if (misaligned(q)) return XHC_ERR_ALIGN;
@@ -262,7 +273,7 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
              w12 = span(a->w12, a->w12 ? (size_t)p.C * 48 : 0);
   const Span zs = span(a->z_save, a->z_save ? T * p.zsv * 4 : 0);
   const Span Wr = span(p.R ? a->W_route : nullptr, (size_t)p.NC * p.N * e);
-  const Span ri = span(p.R ? a->route_idx : nullptr, T * p.k * 4);
+  const Span ri = span(p.pt ? a->route_idx : nullptr, T * p.k * 4);
   const Span dWr = span(p.R ? a->dW_route : nullptr, (size_t)p.NC * p.N * 4);
   const Span dbr = span(p.R ? a->db_route : nullptr, (size_t)p.N * 4);
   const Span dXn = span(a->dX_new, T * p.NC * e), dhin = span(a->dh_in, T * p.C * e);

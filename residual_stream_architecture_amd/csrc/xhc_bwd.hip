@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
       const int64_t j = idx >> 6;
       const int pp = (int)(idx & 63);
       R v = pp < P ? W[(size_t)j * P + pp] : R(0);
-      if (ROUTE && pp >= 48) v = pp - 48 < N ? Wr[(size_t)j * N + (pp - 48)] : R(0);
+      if (ROUTE && pp >= 48) v = (Wr && pp - 48 < N) ? Wr[(size_t)j * N + (pp - 48)] : R(0);
       Wp[idx] = v;
     }
   }
@@ -637,7 +637,7 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
                                               int P, float inv_nc_total, int iters, int unit_gates,
                                               float gs_ceps, float* __restrict__ hpost, float* __restrict__ gss,
                                               int zsv, int dzstride, const int32_t* __restrict__ ridx, int nfix,
-                                              float* __restrict__ hres) {
+                                              float* __restrict__ hres, int has_router) {
   extern __shared__ float hist[];   // [BCOEF_TOK][iters+1][16]
   __shared__ float dzs[BCOEF_TOK][64];
   const int e = threadIdx.x & 15, tok = threadIdx.x >> 4;
@@ -749,8 +749,10 @@ __global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int
     v += row_xor<1>(v);
     v += row_xor<2>(v);
     const int base = (threadIdx.x & 63) & ~15;
-    rmu = z[P + 1];
-    rsd = z[P + 2];
+    if (has_router) {                        // (given lists: no router record, no routed slots)
+      rmu = z[P + 1];
+      rsd = z[P + 2];
+    }
     float m1 = 0.f, m2 = 0.f;
 #pragma unroll
     for (int a2 = 0; a2 < 4; ++a2) {
@@ -1434,7 +1436,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
     zin = zbuf;
   }
 
-  const bool rt = p.R > 0;
+  const bool rt = p.pt;                      // per-token lists (router or caller)
   void* Wp = ws + p.off_wp;
   float* dpart = reinterpret_cast<float*>(ws + p.off_dpart);
   float* dpa = reinterpret_cast<float*>(ws + p.off_dpa);
@@ -1458,7 +1460,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   k_bxdots<E, R, RT><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(                                      \
       src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, zin, hpost, p.P, p.nc,               \
       p.gate == XHC_GATE_UNIT, static_cast<const R*>(a->W), static_cast<R*>(Wp), p.NC, p.zsv, ridx,             \
-      static_cast<const R*>(rt ? a->W_route : nullptr), p.nfix, rt ? a->xact : nullptr)
+      static_cast<const R*>(p.R ? a->W_route : nullptr), p.nfix, rt ? a->xact : nullptr)
     if (rt) XHC_BX(true); else XHC_BX(false);
 #undef XHC_BX
   }
@@ -1506,7 +1508,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   k_bcoef<E, GS, RT><<<nb, 64, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T,  \
                                           p.Tpad, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.iters,            \
                                           p.gate == XHC_GATE_UNIT, GS ? p.gs_ceps : 0.f, hpost,                \
-                                          GS ? gss : nullptr, p.zsv, p.dzs, ridx, p.nfix, hres)
+                                          GS ? gss : nullptr, p.zsv, p.dzs, ridx, p.nfix, hres, p.R > 0)
     if (p.gs) {
       if (rt) XHC_BCOEF(true, true); else XHC_BCOEF(true, false);
     } else {
@@ -1558,9 +1560,9 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
     const int nb_conv = p.nc == 4 ? (int)(((int64_t)p.C * 24 * RED_CONV_LANES + 255) / 256) : 0;
     k_reduce<<<nb_dw + p.P + nb_conv + (rt ? 32 : 0), 256, 0, st>>>(
         dwp, p.b2_ts, p.NC, p.P, a->dW, dz, p.T, a->db, p.nc == 4 ? dwpart : nullptr, p.B * p.b1_segs, p.C, a->dw4,
-        a->dw8, a->dw12, nb_dw, a->accumulate, p.dwr, p.dzs, nb_conv, rt ? a->db_route : nullptr, rred, p.N);
+        a->dw8, a->dw12, nb_dw, a->accumulate, p.dwr, p.dzs, nb_conv, p.R ? a->db_route : nullptr, rred, p.N);
   }
-  if (rt) {
+  if (p.R) {
     TimedLaunch tl(tm, KID_RDWR, st);
     launch_route_dwr(p, dwp, rred, a->dW_route, a->accumulate, st);
   }

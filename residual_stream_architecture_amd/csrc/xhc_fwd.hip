@@ -459,8 +459,9 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
 // FAST: N == 16 and k == 4 (all row and active-row loops compile-time);
 // otherwise rows i >= N and active slots a >= k are skipped at run time.
 // ROUTE: each token's active list comes from its coefficient record
-// (CO_IDX, uniform scalar loads two tokens ahead of their use in addresses)
-// instead of `act`.
+// (CO_IDX, written by the router) or from the caller's lists `ids` [T][k]
+// (ids outside [0, N) read as 0), by uniform scalar loads two tokens ahead
+// of their use in addresses, instead of `act`.
 // ---------------------------------------------------------------------------
 struct Active { int id[4]; };
 
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
     const void* __restrict__ X, const void* __restrict__ out, const float* __restrict__ w4,
     const float* __restrict__ w8, const float* __restrict__ w12, const float* __restrict__ coef,
     void* Xnew, void* __restrict__ hin, void* __restrict__ xact, int S, int C, int N, int k,
-    Active act, int in_place, int lseg, int segs_per_seq) {
+    Active act, int in_place, int lseg, int segs_per_seq, const int32_t* __restrict__ ids) {
   using V = Vec<E, MIX_CH>;
   constexpr int EB = E::bytes;
   const int craw = (blockIdx.x * MIX_THREADS + threadIdx.x) * MIX_CH;
@@ -522,8 +523,16 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
   // a token's active list
   auto token_ids = [&](int s, int (&id)[4]) {
     if constexpr (ROUTE) {
-      const int4 v = *reinterpret_cast<const int4*>(coef + (tok0 + s) * COEF_STRIDE + CO_IDX);
-      id[0] = v.x; id[1] = v.y; id[2] = v.z; id[3] = v.w;
+      if (ids) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int v = b < K ? ids[(tok0 + s) * K + b] : 0;
+          id[b] = (unsigned)v < (unsigned)NR ? v : 0;
+        }
+      } else {
+        const int4 v = *reinterpret_cast<const int4*>(coef + (tok0 + s) * COEF_STRIDE + CO_IDX);
+        id[0] = v.x; id[1] = v.y; id[2] = v.z; id[3] = v.w;
+      }
     } else {
 #pragma unroll
       for (int b = 0; b < 4; ++b) id[b] = act.id[b];
@@ -668,7 +677,7 @@ static RouteArgs route_args(const Plan& p, const xhc_fwd_args* a, float* rcs) {
   ra.ncand = p.ncand;
   ra.nfix = p.nfix;
   ra.R = p.R;
-  for (int j = 0; j < 4; ++j) ra.fixed[j] = j < p.nfix ? a->active[j] : 0;
+  for (int j = 0; j < 4; ++j) ra.fixed[j] = j < p.nfix && !(p.pt && !p.R) ? a->active[j] : 0;
   uint64_t bits = 0;
   int n = 0;
   for (int i = 0; i < p.N && p.R; ++i) {
@@ -750,15 +759,16 @@ static int forward_impl(const Plan& p, const Plan& pn, const xhc_fwd_args* a, co
   {
     TimedLaunch tl(tm, KID_MIX, st);
     Active act;
-    for (int b = 0; b < 4; ++b) act.id[b] = b < p.k && !p.R ? a->active[b] : -1;
+    for (int b = 0; b < 4; ++b) act.id[b] = b < p.k && !p.pt ? a->active[b] : -1;
     dim3 grid(p.mix_cblocks, p.B * p.mix_segs);
     const int in_place = a->X_new == a->X;
 #define XHC_MIX(NCOMP, FULLN, RT)                                                                              \
   k_mix<E, NCOMP, FULLN, RT><<<grid, MIX_THREADS, 0, st>>>(a->X, a->out, a->w4, a->w8, a->w12, coef, a->X_new, \
                                                            a->h_in, a->xact_save, p.S, p.C, p.N, p.k, act,      \
-                                                           in_place, p.mix_lseg, p.mix_segs)
+                                                           in_place, p.mix_lseg, p.mix_segs, ids)
     const bool fast = p.N == 16 && p.k == 4;
-    if (p.R) {
+    const int32_t* ids = p.pt && !p.R ? a->route_idx : nullptr;   // the caller's lists
+    if (p.pt) {
       if (p.nc == 4) {
         if (fast) XHC_MIX(4, true, true); else XHC_MIX(4, false, true);
       } else {

@@ -93,6 +93,7 @@ struct Plan {
   bool gs;            // Gram-Schmidt over the four components (nc == 4)
   float gs_ceps;      // C * gs_eps
   int R;              // routed slots (0: fixed active list)
+  bool pt;            // per-token active lists (the router's, or given by the caller)
   int nfix;           // fixed slots, k - R
   int ncand;          // router candidates, N - nfix (<= 15)
   int zsv;            // floats per token of z_save

@@ -29,7 +29,7 @@ class xhc_desc(ctypes.Structure):
                 ("sinkhorn_iters", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
                 ("gram_schmidt", ctypes.c_int32), ("gs_eps", ctypes.c_float),
-                ("route", ctypes.c_int32)]
+                ("route", ctypes.c_int32), ("per_token_active", ctypes.c_int32)]
 
 
 class xhc_fwd_args(ctypes.Structure):
@@ -108,8 +108,9 @@ lib = _load()
 
 
 def make_desc(B, S, C, N, k, ncomp, dtype, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID,
-              gram_schmidt=False, gs_eps=1e-6, route=0):
-    return xhc_desc(B, S, C, N, k, ncomp, iters, eps, dtype, gate_mode, int(gram_schmidt), gs_eps, int(route))
+              gram_schmidt=False, gs_eps=1e-6, route=0, per_token_active=False):
+    return xhc_desc(B, S, C, N, k, ncomp, iters, eps, dtype, gate_mode, int(gram_schmidt), gs_eps, int(route),
+                    int(per_token_active))
 
 
 def zsave_stride(desc):

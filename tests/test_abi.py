@@ -348,3 +348,28 @@ def test_route_not_chained():
 def test_route_kernel_names():
     names = xhc.kernel_names()
     assert {"route_colsum", "route_pass", "route_dwr"} <= set(names)
+
+
+def test_given_lists_validation():
+    d = desc16(per_token_active=1)
+    a, _ = good_fwd(d, inplace=False)
+    assert xhc.validate(d, a, xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_NULL          # the lists are required
+    a.route_idx = fake(22)
+    a.active = None                                                          # the host list is not read
+    assert xhc.validate(d, a, xhc.XHC_PHASE_FWD) == xhc.XHC_OK
+    a.route_idx = a.X_new                                                    # an input overlapping an output
+    assert xhc.validate(d, a, xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_ALIAS
+    assert xhc.validate(desc16(per_token_active=1, route=2), a, xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_UNSUPPORTED
+    assert xhc.validate(desc16(per_token_active=2), a, xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_UNSUPPORTED
+    b, _ = good_bwd(d)
+    assert xhc.validate(d, b, xhc.XHC_PHASE_BWD) == xhc.XHC_ERR_NULL
+    b.route_idx = fake(22)
+    assert xhc.validate(d, b, xhc.XHC_PHASE_BWD) == xhc.XHC_OK
+    b.z_save = None                                                          # xact without saved logits
+    assert xhc.validate(d, b, xhc.XHC_PHASE_BWD) == xhc.XHC_ERR_UNSUPPORTED
+    b.xact = None
+    assert xhc.validate(d, b, xhc.XHC_PHASE_BWD) == xhc.XHC_OK
+    a, _ = good_fwd(d, inplace=False)
+    a.route_idx = fake(22)
+    c = xhc.xhc_chain_args(None, fake(30), fake(31), None)
+    assert chain_call(d, a, c) == xhc.XHC_ERR_UNSUPPORTED

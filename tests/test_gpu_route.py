@@ -251,3 +251,77 @@ def test_route_backward_after_in_place_forward(case):
     got = run_backward(w, dev, fixed, Xn, z2, ridx_dev, xact=xact)
     for key in ref:
         assert torch.equal(got[key], ref[key]), key
+
+
+# ---------------------------------------------------------------------------
+# per-token lists given by the caller (desc.per_token_active = 1, reading O8)
+# ---------------------------------------------------------------------------
+
+GIVEN = [
+    ("given_bf16", W_("g", 2, 77, 136, 16, 4, 4, "bf16", "fwdbwd")),
+    ("given_k3_n7_f32", W_("g", 3, 30, 40, 7, 3, 4, "f32", "fwdbwd")),
+    ("given_gs_bf16", W_("g", 2, 61, 96, 16, 4, 4, "bf16", "fwdbwd", gs=True)),
+    ("given_nc1_bf16", W_("g", 2, 50, 64, 16, 4, 1, "bf16", "fwdbwd")),
+]
+
+
+def given_lists(w, seed):
+    r = np.random.default_rng(seed)
+    return np.stack([r.permutation(w.N)[:w.k] for _ in range(w.T)]).astype(np.int64)
+
+
+@pytest.mark.parametrize("name,w", GIVEN, ids=[c[0] for c in GIVEN])
+def test_given_lists_parity(name, w):
+    say(f"[given lists] {name} B={w.B} S={w.S} C={w.C} N={w.N} k={w.k} nc={w.ncomp} gs={w.gs} {w.dtype}")
+    d = synth.make_inputs(w, seed=5, grads=True)
+    h = host_inputs(d)
+    dev = device_inputs(d, w.dtype == "bf16")
+    lists = given_lists(w, 6)
+    lists_dev = torch.from_numpy(lists.astype(np.int32)).to(dev["X"].device)
+    T, N, C, P, k = w.T, w.N, w.C, w.P, w.k
+    desc = xhc.make_desc(w.B, w.S, C, N, k, w.ncomp, xhc.XHC_BF16 if w.dtype == "bf16" else xhc.XHC_F32,
+                         w.iters, w.eps, gram_schmidt=w.gs, gs_eps=GS_EPS, per_token_active=True)
+    conv = dict(w4=dev["w4"], w8=dev["w8"], w12=dev["w12"]) if w.ncomp == 4 else {}
+    convs = (h["w4"], h["w8"], h["w12"]) if w.ncomp == 4 else ()
+    kw = dict(B=w.B, S=w.S, iters=w.iters, eps=w.eps, gram_schmidt_on=w.gs, gs_eps=GS_EPS, active_tok=lists)
+    ref = xo.forward(h["X"], h["out"], h["W"], h["bias"], [0] * k, convs, **kw)
+    g = xo.backward(h["X"], h["out"], h["W"], h["bias"], [0] * k, convs, h["dX_new"], h["dh_in"], **kw)
+    atol, rtol = tol(w)
+    X = dev["X"].clone()
+    h_in = torch.empty(T, C, dtype=X.dtype, device=X.device)
+    z_save = torch.empty(T, P + 1, device=X.device)
+    xact = torch.empty(T, k, C, dtype=X.dtype, device=X.device)
+    xhc.forward(X, dev["out"], dev["W"], [0] * k, X, h_in, B=w.B, S=w.S, bias=dev["bias"], z_save=z_save,
+                xact_save=xact, desc=desc, route_idx=lists_dev, **conv)
+    torch.cuda.synchronize()
+    Xn_h = to_host(X)
+    act = np.zeros((T, N), dtype=bool)
+    act[np.arange(T)[:, None], lists] = True
+    assert np.array_equal(Xn_h[~act], h["X"][~act]), "pass-through rows differ"
+    check_close("X_new[active]", Xn_h[act], ref["X_new"][act], atol, rtol)
+    check_close("h_in", to_host(h_in), ref["h_in"], atol, rtol)
+    assert np.array_equal(to_host(xact), h["X"][np.arange(T)[:, None], lists]), "saved rows"
+
+    def run(Xs, xs, zs):
+        f32 = dict(dtype=torch.float32, device=X.device)
+        o = dict(dX=torch.empty_like(dev["dX_new"]), dout=torch.empty(T, C, dtype=X.dtype, device=X.device),
+                 dW=torch.empty((N * C, P), **f32), db=torch.empty((P,), **f32))
+        grads = {}
+        if w.ncomp == 4:
+            grads = {key: torch.empty((C, K), **f32) for key, K in (("dw4", 4), ("dw8", 8), ("dw12", 12))}
+        xhc.backward(Xs, dev["out"], dev["W"], [0] * k, dev["dX_new"], dev["dh_in"], o["dX"], o["dout"], o["dW"],
+                     B=w.B, S=w.S, xact=xs, bias=dev["bias"], z_save=zs, db=o["db"], desc=desc,
+                     route_idx=lists_dev, **conv, **grads)
+        torch.cuda.synchronize()
+        o.update(grads)
+        return o
+
+    res = run(X, xact, z_save)
+    for key, rf in (("dX", g["dX"]), ("dout", g["dout"]), ("dW", g["dW"]), ("db", g["db"])):
+        check_close(key, to_host(res[key]), rf, atol, rtol)
+    for m, key in enumerate(["dw4", "dw8", "dw12"][:w.ncomp - 1]):
+        check_close(key, to_host(res[key]), g["dconv"][m], atol, rtol)
+    # from the forward's input, with the logits recomputed: the same gradients
+    res2 = run(dev["X"], None, None)
+    for key in res:
+        assert np.allclose(to_host(res[key]), to_host(res2[key]), rtol=1e-5, atol=1e-6), key

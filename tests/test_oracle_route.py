@@ -188,3 +188,33 @@ def test_only_chosen_scores_receive_gradient():
     # and the per-token active lists hold distinct streams, fixed ones first
     assert (g["idx"][:, :2] == fixed).all()
     assert all(len(set(row)) == 4 for row in g["idx"])
+
+
+def test_given_lists_are_each_tokens_fixed_list():
+    # O8: a per-token list makes token t's update the fixed-list update with
+    # that list (the write of a token depends on its own list only; the TFA
+    # components and the dense read do not depend on the lists at all)
+    c = case(N=8, k=3, R=0, C=4, seed=9)
+    T = c["X"].shape[0]
+    r = np.random.default_rng(10)
+    lists = np.stack([r.permutation(8)[:3] for _ in range(T)])
+    f = xo.forward(c["X"], c["out"], c["W"], c["bias"], [0, 1, 2], tuple(c["convs"]), B=c["B"], S=c["S"],
+                   active_tok=lists)
+    g = xo.backward(c["X"], c["out"], c["W"], c["bias"], [0, 1, 2], tuple(c["convs"]), c["dX_new"], c["dh_in"],
+                    B=c["B"], S=c["S"], active_tok=lists)
+    dW = np.zeros_like(g["dW"])
+    for t in range(T):
+        lt = list(lists[t])
+        ft = xo.forward(c["X"], c["out"], c["W"], c["bias"], lt, tuple(c["convs"]), B=c["B"], S=c["S"])
+        np.testing.assert_array_equal(f["X_new"][t], ft["X_new"][t])
+        # the gradient of token t's own terms: token t's upstream gradient only
+        cc = dict(c)
+        cc["dX_new"] = np.zeros_like(c["dX_new"]); cc["dX_new"][t] = c["dX_new"][t]
+        cc["dh_in"] = np.zeros_like(c["dh_in"]); cc["dh_in"][t] = c["dh_in"][t]
+        gt = xo.backward(c["X"], c["out"], c["W"], c["bias"], lt, tuple(c["convs"]), cc["dX_new"], cc["dh_in"],
+                         B=c["B"], S=c["S"])
+        np.testing.assert_allclose(g["dX"][t], gt["dX"][t], rtol=1e-12, atol=1e-12)
+        dW += gt["dW"]
+    np.testing.assert_array_equal(f["h_in"], xo.forward(c["X"], c["out"], c["W"], c["bias"], [0, 1, 2],
+                                                       tuple(c["convs"]), B=c["B"], S=c["S"])["h_in"])
+    np.testing.assert_allclose(g["dW"], dW, rtol=1e-10, atol=1e-10)
