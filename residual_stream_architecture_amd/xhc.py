@@ -209,7 +209,9 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
     orthogonalises the write-back components (modified Gram-Schmidt, epsilon gs_eps).
     route=R > 0 chooses the last R active slots per token with the router
     (W_route [N*C,N], b_route [N]); route_idx [B*S,k] int32 receives the
-    per-token active lists, and active then needs only its first k-R entries."""
+    per-token active lists, and active then needs only its first k-R entries.
+    With desc.per_token_active = 1 (make_desc(..., per_token_active=True))
+    route_idx instead holds the caller's per-token lists, and active is not read."""
     T, N, C = X.shape
     ncomp = 4 if w4 is not None else 1
     if desc is None:
@@ -241,7 +243,8 @@ def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None,
              desc=None, gram_schmidt=False, gs_eps=1e-6, route=0, W_route=None, route_idx=None,
              dW_route=None, db_route=None):
     """xhc_backward on torch device tensors (with a router: the forward's
-    z_save and route_idx, and dW_route [N*C,N] / db_route [N] fp32 outputs)."""
+    z_save and route_idx, and dW_route [N*C,N] / db_route [N] fp32 outputs;
+    with per-token lists given by the caller: the same route_idx)."""
     T, N, C = X.shape
     ncomp = 4 if w4 is not None else 1
     if desc is None:
