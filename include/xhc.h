@@ -142,7 +142,8 @@ typedef struct {
   const void* W;       /* [N*C,P] projection weights, row i*C + c             */
   const float* bias;   /* [P] or NULL (zero)                                  */
   const int32_t* active; /* HOST [k] distinct stream ids; order binds row a.
-                          With route = R > 0 only the first k-R are read    */
+                          With route = R > 0 only the first k-R are read;
+                          with desc->per_token_active none (may be NULL)     */
   void* X_new;         /* [T,N,C]; == X: in place, only the k active rows are
                           written; otherwise must not overlap X and all N rows
                           are written (inactive rows copied bitwise)          */
@@ -174,7 +175,8 @@ typedef struct {
   const float* bias;   /* [P] or NULL                                         */
   const int32_t* active;  /* HOST [k], the forward's active list              */
   const float* z_save; /* [T, xhc_zsave_stride(desc)] from the forward, or
-                          NULL (recomputed; not with a router)                */
+                          NULL (recomputed; not with a router, nor with
+                          per-token lists and xact)                           */
   const void* dX_new;  /* [T,N,C] gradient w.r.t. X_new                       */
   const void* dh_in;   /* [T,C] gradient w.r.t. h_in                          */
   void* dX;            /* [T,N,C] gradient w.r.t. X; may be == dX_new, must
