@@ -1338,7 +1338,9 @@ constexpr int RED_CONV_LANES = 4;   // threads per conv-weight gradient (quad, s
 //                            4 threads per output, each summing every 4th segment
 //   [.., + 32)              router: db_route[i] = sum_t drho[t, i] (blocks 0..15)
 //                            and rred[i] = sum_t mean drho[t, i] / sd (16..31)
-// dwp rows hold dwr floats, dz records dzs floats.
+// dwp rows hold dwr floats, dz records dzs floats.  The launch runs the
+// few long-latency sums over tokens (db, router) first, so that they overlap
+// the bandwidth-bound dW blocks instead of trailing them.
 __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, int nsplit, int64_t NC, int P,
                                                 float* __restrict__ dW, const float* __restrict__ dz, int T,
                                                 float* __restrict__ db, const float* __restrict__ cpart, int nseg,
@@ -1347,7 +1349,11 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, i
                                                 int dzs, int nb_conv, float* __restrict__ db_route,
                                                 float* __restrict__ rred, int N) {
   __shared__ float sm[256];
-  const int bid = blockIdx.x;
+  const int nrt = (int)gridDim.x - (nb_dw + P + nb_conv);     // router sums (0 or 32)
+  const int nfirst = P + nrt;                                   // db and router blocks go first
+  int bid = blockIdx.x;
+  if (bid < nfirst) bid = bid < P ? nb_dw + bid : nb_dw + P + nb_conv + (bid - P);
+  else bid = bid - nfirst < nb_dw ? bid - nfirst : bid - nfirst + P;   // dW, then dconv
   if (bid >= nb_dw + P + nb_conv) {
     const int q = bid - (nb_dw + P + nb_conv);
     const int i = q & 15;
