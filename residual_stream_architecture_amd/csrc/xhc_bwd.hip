@@ -614,7 +614,7 @@ __global__ __launch_bounds__(256) void k_bdots(
 // and Sg to gss ([T][16] each), so that dU_m = sum_a Ht[a][m] G_a +
 // sum_n Sg[m][n] U_n.
 // ---------------------------------------------------------------------------
-constexpr int BCOEF_TOK = 4;
+constexpr int BCOEF_TOK = 16;   // tokens per workgroup (16 lanes each)
 
 // ROUTE: the routed slots' write-back scale s_a = sigmoid(rho_a) enters as
 // in the forward (the effective post coefficient is s_a H_post[a, m]); with
@@ -629,7 +629,7 @@ constexpr int BCOEF_TOK = 4;
 // (DZ_R floats per token) also gets drho and mean * drho / sd per stream for
 // db_route and for dW_route's mean term; hres gets H_res for the pass kernel.
 template <typename E, bool GS, bool ROUTE>
-__global__ __launch_bounds__(64) void k_bcoef(const float* __restrict__ dpa, int ncba, const float* __restrict__ dpart,
+__global__ __launch_bounds__(16 * BCOEF_TOK) void k_bcoef(const float* __restrict__ dpa, int ncba, const float* __restrict__ dpart,
                                               int ncb, const float* __restrict__ zin,
                                               const float* __restrict__ bias,
                                               float* __restrict__ dz_out, void* __restrict__ rec,
@@ -1511,7 +1511,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
     const int nb = (int)((p.Tpad + BCOEF_TOK - 1) / BCOEF_TOK);
     const size_t shm = (size_t)BCOEF_TOK * (p.iters + 1) * 16 * sizeof(float);
 #define XHC_BCOEF(GS, RT)                                                                                       \
-  k_bcoef<E, GS, RT><<<nb, 64, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T,  \
+  k_bcoef<E, GS, RT><<<nb, 16 * BCOEF_TOK, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T,  \
                                           p.Tpad, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.iters,            \
                                           p.gate == XHC_GATE_UNIT, GS ? p.gs_ceps : 0.f, hpost,                \
                                           GS ? gss : nullptr, p.zsv, p.dzs, ridx, p.nfix, hres, p.R > 0)
