@@ -45,9 +45,22 @@ __global__ __launch_bounds__(256) void k_pack_wt(const R* __restrict__ W, R* __r
   const int c0 = ks * 32;
   const int rows = min(32, C - c0);
   const R* src = W + ((size_t)i * C + c0) * P;
-  for (int idx = threadIdx.x; idx < 32 * P; idx += 256) {
-    const int rr = idx / P, pp = idx - (idx / P) * P;
-    tile[rr][pp] = rr < rows ? src[idx] : R(0);
+  // the rows * P source elements are one contiguous, 16-byte aligned run
+  // (C % 8 == 0 makes rows a multiple of 8): 16-byte loads; rows past C are 0
+  constexpr int VE = 16 / sizeof(R);
+  for (int v = threadIdx.x; v < rows * P / VE; v += 256) {
+    R val[VE];
+    __builtin_memcpy(val, src + (size_t)v * VE, 16);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const int idx = v * VE + e;
+      const int rr = idx / P;
+      tile[rr][idx - rr * P] = val[e];
+    }
+  }
+  for (int idx = rows * P + threadIdx.x; idx < 32 * P; idx += 256) {
+    const int rr = idx / P;
+    tile[rr][idx - rr * P] = R(0);
   }
   if (Wr) {
     const R* rsrc = Wr + ((size_t)i * C + c0) * N;
