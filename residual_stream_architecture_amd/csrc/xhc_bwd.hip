@@ -1046,12 +1046,31 @@ __device__ __forceinline__ void bgrad_body(
   const uint32_t xrowb = (uint32_t)xstride * EB;
   const uint32_t vx = ((uint32_t)r16 * (uint32_t)xstride + clc) * EB;
   const uint32_t vd = (((uint32_t)r16 * N + srow) * (uint32_t)C + clc) * EB;
-  // ROUTE: this lane's tokens' active lists for the step loaded next
-  int nid[B2_SUB][4];
+  // ROUTE: this lane's tokens' active lists for the step loaded next, and
+  // from them the slot of this lane's stream (-1: not active).  The slots
+  // are formed right after the top-of-step wait, before any memory operation
+  // of the step: a first use of the lists after this step's store and copies
+  // would make the compiler wait for all of them (loads and stores share one
+  // counter), exposing the copies' latency every step.
+  int nid[B2_SUB][4], nslot[B2_SUB];
 #pragma unroll
-  for (int s = 0; s < B2_SUB; ++s)
+  for (int s = 0; s < B2_SUB; ++s) {
+    nslot[s] = -1;
 #pragma unroll
     for (int a = 0; a < 4; ++a) nid[s][a] = -1;
+  }
+  auto form_slots = [&]() {
+    if constexpr (ROUTE) {
+#pragma unroll
+      for (int s = 0; s < B2_SUB; ++s) {
+        int slot = -1;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          if (nid[s][a] == srow) slot = a;
+        nslot[s] = slot;
+      }
+    }
+  };
   auto load_ids = [&](int t0) {
     if constexpr (ROUTE) {
 #pragma unroll
@@ -1081,10 +1100,7 @@ __device__ __forceinline__ void bgrad_body(
         // active) picks the row: pass[t][slot] or dX_new[t][stream], read
         // through a per-lane address (tokens past the end read token T-1;
         // their values are masked when published)
-        int slot = -1;
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          if (nid[s][a] == srow) slot = a;
+        const int slot = nslot[s];
         const size_t tk = (size_t)(ta + r16 < T ? ta + r16 : T - 1);
         const char* src_row = slot >= 0
             ? static_cast<const char*>(passbuf) + ((tk * k + slot) * (size_t)C + clc) * EB
@@ -1117,6 +1133,7 @@ __device__ __forceinline__ void bgrad_body(
   if (tbeg < tfin) {
     dma(tbeg, 0);
     load_ids(tbeg);
+    form_slots();
     load_own(tbeg);
     load_ids(tbeg + STEP);
   }
@@ -1125,6 +1142,7 @@ __device__ __forceinline__ void bgrad_body(
     // these tiles' copies and own loads (issued one iteration ago) have
     // landed; the other waves' copies are covered by the barrier below
     wait_vmcnt<0>();
+    form_slots();                    // (the next step's lists landed with them)
     // publish the own rows (zero outside the sequence or the channels), which
     // frees their registers for the next prefetch
 #pragma unroll
