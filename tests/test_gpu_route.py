@@ -51,20 +51,21 @@ def inputs(w, seed, grads):
     return d
 
 
-def host_kw(h, w, fixed):
+def host_kw(h, w, fixed, gate="sigmoid"):
     convs = (h["w4"], h["w8"], h["w12"]) if w.ncomp == 4 else ()
     return dict(args=(h["X"], h["out"], h["W"], h["bias"], list(fixed) + [0] * w.route, convs),
                 kw=dict(B=w.B, S=w.S, iters=w.iters, eps=w.eps, gram_schmidt_on=w.gs, gs_eps=GS_EPS,
-                        route=w.route, W_route=h["W_route"], b_route=h["b_route"]))
+                        route=w.route, W_route=h["W_route"], b_route=h["b_route"], gate_mode=gate))
 
 
-def run_forward(w, dev, fixed, in_place=False, xact=None):
+def run_forward(w, dev, fixed, in_place=False, xact=None, gate="sigmoid"):
     T, C = w.T, w.C
     X = dev["X"].clone()
     Xn = X if in_place else torch.empty_like(X)
     h_in = torch.empty(T, C, dtype=X.dtype, device=X.device)
     desc = xhc.make_desc(w.B, w.S, C, w.N, w.k, w.ncomp, xhc.XHC_BF16 if w.dtype == "bf16" else xhc.XHC_F32,
-                         w.iters, w.eps, gram_schmidt=w.gs, gs_eps=GS_EPS, route=w.route)
+                         w.iters, w.eps, gram_schmidt=w.gs, gs_eps=GS_EPS, route=w.route,
+                         gate_mode=xhc.XHC_GATE_UNIT if gate == "unit" else xhc.XHC_GATE_SIGMOID)
     z_save = torch.empty(T, xhc.zsave_stride(desc), dtype=torch.float32, device=X.device)
     ridx = torch.full((T, w.k), -1, dtype=torch.int32, device=X.device)
     conv = dict(w4=dev["w4"], w8=dev["w8"], w12=dev["w12"]) if w.ncomp == 4 else {}
@@ -168,7 +169,8 @@ def test_route_ties_go_to_the_lower_stream():
     compare_forward(w, h, fixed, Xn, h_in, z_save, idx, ref)
 
 
-def run_backward(w, dev, fixed, X, z_save, ridx_dev, in_place_dx=False, accumulate=False, init=None, xact=None):
+def run_backward(w, dev, fixed, X, z_save, ridx_dev, in_place_dx=False, accumulate=False, init=None, xact=None,
+                 gate="sigmoid"):
     T, N, C, P = w.T, w.N, w.C, w.P
     dXn = dev["dX_new"].clone()
     dX = dXn if in_place_dx else torch.empty_like(dXn)
@@ -186,6 +188,7 @@ def run_backward(w, dev, fixed, X, z_save, ridx_dev, in_place_dx=False, accumula
     xhc.backward(X, dev["out"], dev["W"], list(fixed) + [0] * w.route, dXn, dev["dh_in"], out["dX"], out["dout"],
                  out["dW"], B=w.B, S=w.S, bias=dev["bias"], z_save=z_save, db=out["db"], iters=w.iters, eps=w.eps,
                  gram_schmidt=w.gs, gs_eps=GS_EPS, route=w.route, W_route=dev["W_route"], route_idx=ridx_dev,
+                 gate_mode=xhc.XHC_GATE_UNIT if gate == "unit" else xhc.XHC_GATE_SIGMOID,
                  dW_route=out["dW_route"], db_route=out["db_route"], accumulate=accumulate, xact=xact, **conv,
                  **grads)
     torch.cuda.synchronize()
@@ -325,3 +328,26 @@ def test_given_lists_parity(name, w):
     res2 = run(dev["X"], None, None)
     for key in res:
         assert np.allclose(to_host(res[key]), to_host(res2[key]), rtol=1e-5, atol=1e-6), key
+
+
+def test_route_with_unit_gates():
+    # unit gates (H_pre = H_post = 1): the routed write-back is s times the
+    # plain sum of the components, and the router still gets its gradient
+    name, w, fixed = CASES[0]
+    say(f"[route unit gates] {name}")
+    d = inputs(w, 11, True)
+    h = host_inputs(d)
+    dev = device_inputs(d, False)
+    Xn, h_in, z_save, idx, _ = run_forward(w, dev, fixed, gate="unit")
+    hk = host_kw(h, w, fixed, gate="unit")
+    own = xo.forward(*hk["args"], **hk["kw"])
+    assert check_choice(own["rho"], idx, fixed, w.route) <= 1
+    ref = xo.forward(*hk["args"], **hk["kw"], route_idx=idx)
+    compare_forward(w, h, fixed, Xn, h_in, z_save, idx, ref)
+    ridx_dev = torch.from_numpy(idx.astype(np.int32)).to(dev["X"].device)
+    g = xo.backward(*hk["args"], h["dX_new"], h["dh_in"], **hk["kw"], route_idx=idx)
+    res = run_backward(w, dev, fixed, dev["X"], z_save, ridx_dev, gate="unit")
+    for key, rf in (("dX", g["dX"]), ("dout", g["dout"]), ("dW", g["dW"]), ("db", g["db"]),
+                    ("dW_route", g["dW_route"]), ("db_route", g["db_route"])):
+        check_close(key, to_host(res[key]), rf, 1e-4, 1e-4)
+    assert np.abs(g["db_route"]).max() > 1e-3
