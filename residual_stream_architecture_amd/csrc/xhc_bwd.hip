@@ -1225,18 +1225,24 @@ __device__ __forceinline__ void bgrad_body(
         const float cst = ROUTE ? co[RRF_CONST * B2_TT + r16] : 0.f;
         float pass[8];
         if (active_grp) {
+          // all four rows' reads first (rows past k were published as zeros
+          // and get coefficient 0), then the sums
+          V8<E> gv[4];
+          float hh[4];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            gv[a] = *reinterpret_cast<const V8<E>*>(&gsh[s][a + 4 * chalf][rowoff]);
+            const float h = co[(RF_RES + a * 4 + slot) * B2_TT + r16];
+            hh[a] = a < k ? h : 0.f;
+          }
 #pragma unroll
           for (int q = 0; q < 8; ++q) pass[q] = 0.f;
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
-            if (a < k) {
-              const float h = co[(RF_RES + a * 4 + slot) * B2_TT + r16];
-              const V8<E> gv = *reinterpret_cast<const V8<E>*>(&gsh[s][a + 4 * chalf][rowoff]);
-              float gf[8];
-              gv.to_float(gf);
+            float gf[8];
+            gv[a].to_float(gf);
 #pragma unroll
-              for (int q = 0; q < 8; ++q) pass[q] = fmaf(h, gf[q], pass[q]);
-            }
+            for (int q = 0; q < 8; ++q) pass[q] = fmaf(hh[a], gf[q], pass[q]);
           }
         } else {
           const V8<E> gv = *reinterpret_cast<const V8<E>*>(&gsh[s][wave][rowoff]);
