@@ -568,6 +568,16 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
   token_ids(s0, id_a);
   load_token(s0, id_a);
   token_ids(s0 + 1 < s1 ? s0 + 1 : s0, id_b);
+  // H_pre of the token processed next (uniform loads one token ahead: the
+  // dense read needs it first; H_post and H_res are loaded with the token
+  // and used after the convolutions)
+  f32x4 cn[4];
+  auto load_pre = [&](int s) {
+    const f32x4* c4 = reinterpret_cast<const f32x4*>(coef + (tok0 + s) * COEF_STRIDE);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cn[j] = c4[j];
+  };
+  load_pre(s0);
 
   for (int s = s0; s < s1; ++s) {
     const size_t t = tok0 + s;
@@ -581,15 +591,17 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
     for (int b = 0; b < 4; ++b) cxa[b] = xa_r[b];
     load_token(s + 1 < s1 ? s + 1 : s, id_a);    // next token (the last iteration reloads, harmlessly)
     token_ids(s + 2 < s1 ? s + 2 : s1 - 1, id_b);
-    // the token's coefficients: uniform 16-byte loads (scalar loads)
+    // the token's coefficients: H_pre loaded one token ahead, the rest now
+    // (uniform 16-byte loads)
     const f32x4* c4 = reinterpret_cast<const f32x4*>(coef + t * COEF_STRIDE);
     float cpre[16], cpost[16], cres[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f32x4 a0 = c4[j], a1 = c4[4 + j], a2 = c4[8 + j];
+      const f32x4 a0 = cn[j], a1 = c4[4 + j], a2 = c4[8 + j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) { cpre[4 * j + e] = a0[e]; cpost[4 * j + e] = a1[e]; cres[4 * j + e] = a2[e]; }
     }
+    load_pre(s + 1 < s1 ? s + 1 : s);
 #pragma unroll
     for (int j = 0; j < 11; ++j)
 #pragma unroll
