@@ -175,8 +175,8 @@ typedef struct {
   const float* bias;   /* [P] or NULL                                         */
   const int32_t* active;  /* HOST [k], the forward's active list              */
   const float* z_save; /* [T, xhc_zsave_stride(desc)] from the forward, or
-                          NULL (recomputed; not with a router, nor with
-                          per-token lists and xact)                           */
+                          NULL (recomputed; then not with xact when the lists
+                          are per token: router or given lists)              */
   const void* dX_new;  /* [T,N,C] gradient w.r.t. X_new                       */
   const void* dh_in;   /* [T,C] gradient w.r.t. h_in                          */
   void* dX;            /* [T,N,C] gradient w.r.t. X; may be == dX_new, must
@@ -188,12 +188,14 @@ typedef struct {
   int32_t accumulate;  /* 0: overwrite dW/db/dw* (and dW_route/db_route);
                           1: add to them                                      */
   xhc_timer* timer;
-  /* router (read only when desc->route > 0; then z_save must be the
-     forward's; route_idx also with desc->per_token_active) */
+  /* router (read only when desc->route > 0; route_idx also with
+     desc->per_token_active) */
   const void* W_route; /* [N*C,N]                                             */
   const int32_t* route_idx;  /* [T,k] the forward's per-token active lists    */
   float* dW_route;     /* [N*C,N] fp32                                        */
   float* db_route;     /* [N] fp32, or NULL                                   */
+  const float* b_route;  /* [N] or NULL (zero): read only to recompute the
+                          router's scores when z_save is NULL                 */
 } xhc_bwd_args;
 
 /* Bytes of device workspace the call needs (phase XHC_PHASE_FWD or

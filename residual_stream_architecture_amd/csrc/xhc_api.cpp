@@ -252,7 +252,7 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
   if (a->accumulate != 0 && a->accumulate != 1) return XHC_ERR_UNSUPPORTED;
   if (p.R) {
     // the router's choice and scores come from the forward's records
-    if (!a->z_save || !a->route_idx || !a->W_route || !a->dW_route) return XHC_ERR_NULL;
+    if (!a->route_idx || !a->W_route || !a->dW_route) return XHC_ERR_NULL;
   }
   if (p.pt && !a->route_idx) return XHC_ERR_NULL;
   // recomputing the logits maps saved rows by the host list: not per token
@@ -262,7 +262,8 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
   const void* ptrs[] = {a->X, a->xact, a->out, a->w4, a->w8, a->w12, a->W, a->bias, a->z_save, a->dX_new,
                         a->dh_in, a->dX, a->dout, a->dW, a->db, a->dw4, a->dw8, a->dw12,
                         p.R ? a->W_route : nullptr, p.pt ? a->route_idx : nullptr,
-                        p.R ? a->dW_route : nullptr, p.R ? a->db_route : nullptr};
+                        p.R ? a->dW_route : nullptr, p.R ? a->db_route : nullptr,
+                        p.R ? a->b_route : nullptr};
   for (const void* q : ptrs)
     if (misaligned(q)) return XHC_ERR_ALIGN;
   const size_t T = p.T, e = p.esz;
@@ -283,7 +284,8 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
              dw12 = span(a->dw12, a->dw12 ? (size_t)p.C * 48 : 0);
   if (a->dX != a->dX_new && overlap(dX, dXn)) return XHC_ERR_ALIAS;
   std::vector<Span> outs = {dX, dout, dW, db, dw4, dw8, dw12, dWr, dbr};
-  std::vector<Span> ins = {X, xact, out, W, bias, w4, w8, w12, zs, dXn, dhin, Wr, ri};
+  const Span br = span(p.R ? a->b_route : nullptr, (size_t)p.N * 4);
+  std::vector<Span> ins = {X, xact, out, W, bias, w4, w8, w12, zs, dXn, dhin, Wr, ri, br};
   if (any_overlap(outs, ins, dX, dXn)) return XHC_ERR_ALIAS;
   return XHC_OK;
 }

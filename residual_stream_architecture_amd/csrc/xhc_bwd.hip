@@ -1461,7 +1461,9 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
     // no saved logits: recompute them (projection and coefficient passes)
     float* zbuf = reinterpret_cast<float*>(ws + p.off_zbuf);
     float* coef = reinterpret_cast<float*>(ws + p.off_coef);
-    const int rc = launch_coef_bwd(p, a->X, a->xact, a->active, a->W, a->bias, nullptr, ws, coef, zbuf, st, tm);
+    const int rc = launch_coef_bwd(p, a->X, a->xact, a->active, a->W, a->bias, nullptr, ws, coef, zbuf, st, tm,
+                                   p.R ? a->W_route : nullptr, p.R ? a->b_route : nullptr,
+                                   p.R ? a->route_idx : nullptr);
     if (rc) return rc;
     zin = zbuf;
   }

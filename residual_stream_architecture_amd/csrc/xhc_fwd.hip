@@ -263,6 +263,8 @@ struct RouteArgs {
   const float* rcs;       // [RCS_BLK + 1][16]: partial column sums of W_route, then the sums
   const float* b_route;   // [N] or NULL
   int32_t* route_idx;     // [T][k] or NULL
+  const int32_t* force;   // [T][k] or NULL: take these routed streams instead of choosing
+                          // (the backward's recompute of a forward's records)
   RowOrder cand;          // candidate e -> stream id
   int ncand, nfix, R;
   int fixed[4];           // stream ids of the fixed slots
@@ -363,7 +365,18 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
         bv = take ? ov : bv;
         bl = take ? ol : bl;
       }
-      const int lw = bl & 15;                      // a candidate lane: R <= ncand
+      int lw = bl & 15;                            // a candidate lane: R <= ncand
+      if (ra.force) {
+        // the given stream's candidate lane (the lowest matching one; lane 0
+        // if the stream is no candidate, which a forward's list never holds)
+        int fs = ra.force[(size_t)t * k + ra.nfix + j];
+        int m = (cand && sid == fs) ? e : 16;
+        m = min(m, __float_as_int(row_xor<1>(__int_as_float(m))));
+        m = min(m, __float_as_int(row_xor<2>(__int_as_float(m))));
+        m = min(m, __float_as_int(row_xor<4>(__int_as_float(m))));
+        m = min(m, __float_as_int(row_xor<8>(__int_as_float(m))));
+        lw = m < 16 ? m : 0;
+      }
       const float rho_w = __shfl(rho, base + lw, 64);
       const float y_w = __shfl(ys, base + lw, 64);
       const float cs_w = __shfl(csm, base + lw, 64);
@@ -694,20 +707,22 @@ static void launch_pack_wt(const Plan& p, const void* W, void* Wf, hipStream_t s
 
 // The router's candidates (streams that are not fixed, ascending) and the
 // fixed slots' streams.
-static RouteArgs route_args(const Plan& p, const xhc_fwd_args* a, float* rcs) {
+static RouteArgs route_args(const Plan& p, const int32_t* active, const float* b_route, int32_t* route_idx,
+                            const int32_t* force, float* rcs) {
   RouteArgs ra{};
   ra.rcs = rcs;
-  ra.b_route = a->b_route;
-  ra.route_idx = a->route_idx;
+  ra.b_route = b_route;
+  ra.route_idx = route_idx;
+  ra.force = force;
   ra.ncand = p.ncand;
   ra.nfix = p.nfix;
   ra.R = p.R;
-  for (int j = 0; j < 4; ++j) ra.fixed[j] = j < p.nfix && !(p.pt && !p.R) ? a->active[j] : 0;
+  for (int j = 0; j < 4; ++j) ra.fixed[j] = j < p.nfix && !(p.pt && !p.R) ? active[j] : 0;
   uint64_t bits = 0;
   int n = 0;
   for (int i = 0; i < p.N && p.R; ++i) {
     bool fixed = false;
-    for (int j = 0; j < p.nfix; ++j) fixed |= a->active[j] == i;
+    for (int j = 0; j < p.nfix; ++j) fixed |= active[j] == i;
     if (!fixed) bits |= (uint64_t)i << (4 * n++);
   }
   ra.cand = RowOrder{bits};
@@ -742,7 +757,7 @@ static int forward_impl(const Plan& p, const Plan& pn, const xhc_fwd_args* a, co
   const bool carry_out = ch && ch->W_next;
 
   float* rcs = reinterpret_cast<float*>(ws + p.off_rcs);
-  const RouteArgs ra = route_args(p, a, rcs);
+  const RouteArgs ra = route_args(p, a->active, a->b_route, a->route_idx, nullptr, rcs);
   if (!carry_in) {
     if (p.R) {
       TimedLaunch tl(tm, KID_RCOLSUM, st);
@@ -821,30 +836,45 @@ int launch_forward_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, c
 }
 
 // Backward helper: coefficients either from a forward's z_save or, when it
-// is NULL, recomputed by the projection from the pre-update state.
+// is NULL, recomputed by the projection from the pre-update state.  With a
+// router the recompute also forms the router's record for the forward's
+// choice (force = its route_idx), so that it equals the forward's z_save.
 int launch_coef_bwd(const Plan& p, const void* X, const void* xact, const int32_t* active, const void* W,
                     const float* bias, const float* z_save, void* ws, float* coef, float* z_out,
-                    hipStream_t st, xhc_timer* tm) {
+                    hipStream_t st, xhc_timer* tm, const void* W_route, const float* b_route,
+                    const int32_t* force) {
   char* w = static_cast<char*>(ws);
   float* zpart = nullptr;
+  float* rcs = reinterpret_cast<float*>(w + p.off_rcs);
+  const RouteArgs ra = route_args(p, active, b_route, nullptr, force, rcs);
   if (!z_save) {
     void* Wt = w + p.off_wt;
     zpart = reinterpret_cast<float*>(w + p.off_zpart);
     const StreamRows src = stream_rows(p, X, xact, active);
+    if (p.R) {
+      TimedLaunch tl(tm, KID_RCOLSUM, st);
+      launch_route_colsum(p, W_route, rcs, st);
+    }
     if (p.dtype == XHC_BF16) {
-      launch_pack_wt<uint16_t>(p, W, Wt, st, tm);
+      launch_pack_wt<uint16_t>(p, W, Wt, st, tm, p.R ? W_route : nullptr, ra.cand);
       launch_proj<BF16>(p, src, Wt, zpart, st, tm);
     } else {
-      launch_pack_wt<float>(p, W, Wt, st, tm);
+      launch_pack_wt<float>(p, W, Wt, st, tm, p.R ? W_route : nullptr, ra.cand);
       launch_proj<F32>(p, src, Wt, zpart, st, tm);
     }
   }
   TimedLaunch tl(tm, KID_COEF, st);
-  // the backward needs z (and r) only: its post coefficients come from z
-  k_coef<false, false><<<(p.T + 15) / 16, 256, 0, st>>>(zpart, p.SK, p.ZST, p.NT * 16, z_save, bias, coef, z_out,
-                                                        p.zsv, p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps,
-                                                        p.iters, p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f,
-                                                        RouteArgs{});
+  // the backward needs z (and r, and the router's record) only: its post
+  // coefficients come from z
+  if (p.R && !z_save)
+    k_coef<false, true><<<(p.T + 15) / 16, 256, 0, st>>>(zpart, p.SK, p.ZST, p.NT * 16, nullptr, bias, coef, z_out,
+                                                         p.zsv, p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps,
+                                                         p.iters, p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f, ra);
+  else
+    k_coef<false, false><<<(p.T + 15) / 16, 256, 0, st>>>(zpart, p.SK, p.ZST, p.NT * 16, z_save, bias, coef, z_out,
+                                                          p.zsv, p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps,
+                                                          p.iters, p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f,
+                                                          RouteArgs{});
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
 }
 

@@ -70,7 +70,8 @@ void launch_mixproj(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const 
                     float* carry, hipStream_t st);
 int launch_coef_bwd(const Plan& p, const void* X, const void* xact, const int32_t* active, const void* W,
                     const float* bias, const float* z_save, void* ws, float* coef, float* z_out,
-                    hipStream_t st, xhc_timer* tm);
+                    hipStream_t st, xhc_timer* tm, const void* W_route, const float* b_route,
+                    const int32_t* force);
 int launch_backward(const Plan& p, const xhc_bwd_args* a, void* ws, hipStream_t st);
 // Gram-Schmidt's Gram records of the components (forward): gram[cb][t][16]
 // partials over channel blocks of B1_WAVES * B1_WAVE_CH.

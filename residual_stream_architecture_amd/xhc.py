@@ -45,7 +45,8 @@ class xhc_bwd_args(ctypes.Structure):
                 ("z_save", _vp), ("dX_new", _vp), ("dh_in", _vp), ("dX", _vp), ("dout", _vp),
                 ("dW", _vp), ("db", _vp), ("dw4", _vp), ("dw8", _vp), ("dw12", _vp),
                 ("accumulate", ctypes.c_int32), ("timer", _vp),
-                ("W_route", _vp), ("route_idx", _vp), ("dW_route", _vp), ("db_route", _vp)]
+                ("W_route", _vp), ("route_idx", _vp), ("dW_route", _vp), ("db_route", _vp),
+                ("b_route", _vp)]
 
 
 class xhc_chain_args(ctypes.Structure):
@@ -241,7 +242,7 @@ def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None,
              w12=None, bias=None, z_save=None, db=None, dw4=None, dw8=None, dw12=None, accumulate=False,
              iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID, workspace=None, stream=None, timer=None,
              desc=None, gram_schmidt=False, gs_eps=1e-6, route=0, W_route=None, route_idx=None,
-             dW_route=None, db_route=None):
+             dW_route=None, db_route=None, b_route=None):
     """xhc_backward on torch device tensors (with a router: the forward's
     z_save and route_idx, and dW_route [N*C,N] / db_route [N] fp32 outputs;
     with per-token lists given by the caller: the same route_idx)."""
@@ -255,7 +256,7 @@ def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None,
                         ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(z_save), _ptr(dX_new),
                         _ptr(dh_in), _ptr(dX), _ptr(dout), _ptr(dW), _ptr(db), _ptr(dw4), _ptr(dw8),
                         _ptr(dw12), int(bool(accumulate)), None if timer is None else timer.handle,
-                        _ptr(W_route), _ptr(route_idx), _ptr(dW_route), _ptr(db_route))
+                        _ptr(W_route), _ptr(route_idx), _ptr(dW_route), _ptr(db_route), _ptr(b_route))
     ws, need = _workspace(desc, XHC_PHASE_BWD, X.device, workspace)
     rc = lib.xhc_backward(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
                           _stream_handle(stream))

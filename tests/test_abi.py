@@ -317,10 +317,15 @@ def test_route_forward_error_paths():
 def test_route_backward_error_paths():
     d = desc16(route=2)
     assert xhc.validate(d, routed_bwd(d)[0], xhc.XHC_PHASE_BWD) == xhc.XHC_OK
-    for field in ("z_save", "route_idx", "W_route", "dW_route"):
+    for field in ("route_idx", "W_route", "dW_route"):
         a, _ = routed_bwd(d)
         setattr(a, field, None)
         assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_ERR_NULL, field
+    a, _ = routed_bwd(d)
+    a.z_save = None                                 # recomputed (b_route may be NULL: zero)
+    assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_OK
+    a.xact = fake(2)                                # but not from saved rows
+    assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_ERR_UNSUPPORTED
     a, _ = routed_bwd(d)
     a.db_route = None
     assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_OK

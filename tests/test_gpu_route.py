@@ -188,7 +188,7 @@ def run_backward(w, dev, fixed, X, z_save, ridx_dev, in_place_dx=False, accumula
     xhc.backward(X, dev["out"], dev["W"], list(fixed) + [0] * w.route, dXn, dev["dh_in"], out["dX"], out["dout"],
                  out["dW"], B=w.B, S=w.S, bias=dev["bias"], z_save=z_save, db=out["db"], iters=w.iters, eps=w.eps,
                  gram_schmidt=w.gs, gs_eps=GS_EPS, route=w.route, W_route=dev["W_route"], route_idx=ridx_dev,
-                 gate_mode=xhc.XHC_GATE_UNIT if gate == "unit" else xhc.XHC_GATE_SIGMOID,
+                 gate_mode=xhc.XHC_GATE_UNIT if gate == "unit" else xhc.XHC_GATE_SIGMOID, b_route=dev["b_route"],
                  dW_route=out["dW_route"], db_route=out["db_route"], accumulate=accumulate, xact=xact, **conv,
                  **grads)
     torch.cuda.synchronize()
@@ -220,6 +220,11 @@ def test_route_backward_parity(name, w, fixed):
     res3 = run_backward(w, dev, fixed, dev["X"], z_save, ridx_dev, in_place_dx=True)
     for key in res:
         assert torch.equal(res[key], res3[key]), f"{key} differs with dX == dX_new"
+    # without z_save the logits and the router's record are recomputed for
+    # the forward's choice: the same gradients, bit for bit
+    res4 = run_backward(w, dev, fixed, dev["X"], None, ridx_dev)
+    for key in res:
+        assert torch.equal(res[key], res4[key]), f"{key} differs when recomputed"
 
 
 def test_route_backward_accumulates():
