@@ -37,6 +37,9 @@ CASES = [
     ("gs_bf16", W_("r", 2, 77, 136, 16, 4, 4, "bf16", "fwdbwd", gs=True, route=2), [5, 12]),
     ("wide_bf16", W_("r", 1, 130, 1040, 16, 4, 4, "bf16", "fwdbwd", route=2), [4, 5]),
     ("edge_c8_s1_f32", W_("r", 4, 1, 8, 16, 4, 4, "f32", "fwdbwd", route=2), [0, 15]),
+    # one routed stream and nothing fixed: 15 candidates, the widest router tile
+    ("k1_n15_r1_f32", W_("r", 2, 37, 48, 15, 1, 4, "f32", "fwdbwd", route=1), []),
+    ("nc1_f32", W_("r", 2, 29, 56, 12, 3, 1, "f32", "fwdbwd", route=2), [4]),
 ]
 GS_EPS = 1e-6
 
