@@ -85,6 +85,18 @@ shared with the GPU library and listed in the design notes):
   O8  per-token active lists given by the caller (`active_tok`, [T, k]):
       O5's write with token t's own list in place of `active`, s = 1, and
       no router.  It is the form in which another router's choice enters.
+  O9  H_res from the active rows (optional, `hres_active`; [R-DRSW] credits
+      the sparse write with generating H_res at k^3 C instead of N^3 C, that
+      is from the k active rows only): the res logits are the RMS-normed
+      projection of the k*C active state alone,
+        xa = [X[t, i_0], .., X[t, i_{k-1}]] (length k*C),
+        r_act = sqrt(mean(xa^2) + eps),
+        L[a, b] = sum_{a'} sum_c X[t, i_{a'}, c] / r_act
+                  * W[i_{a'}*C + c, N + k*ncomp + a*k + b] + bias[...]
+      -- the rows of W that belong to the active streams, normalised by the
+      active state's own RMS.  The pre and post logits stay O1's (full state,
+      r).  W's res columns on the other streams' rows are not read, and
+      their gradient is zero.  With every stream active (k = N) this is O1.
 """
 
 import numpy as np
@@ -110,6 +122,24 @@ def rms_projection(Xf, W, bias, eps):
     xhat = Xf / r[:, None]
     z = xhat @ W + bias[None, :]
     return z, r, xhat
+
+
+def res_logits_active(X, W, bias, active, ncomp, eps):
+    """O9: the k x k res logits from the k active rows alone.
+
+    X: [T, N, C], W: [N*C, P].  Returns L [T, k, k], r_act [T], the normed
+    active state xa_hat [T, k*C] and the weights it multiplies W_act
+    [k*C, k*k] (the active streams' rows, in slot order, res columns).
+    """
+    T, N, C = X.shape
+    k = len(active)
+    res0 = N + k * ncomp
+    xa = X[:, list(active), :].reshape(T, k * C)
+    r_act = np.sqrt(np.mean(xa * xa, axis=1) + eps)
+    xa_hat = xa / r_act[:, None]
+    W_act = W.reshape(N, C, -1)[list(active)][:, :, res0:res0 + k * k].reshape(k * C, k * k)
+    L = xa_hat @ W_act + bias[None, res0:res0 + k * k]
+    return L.reshape(T, k, k), r_act, xa_hat, W_act
 
 
 def sigmoid(x):
@@ -245,7 +275,8 @@ def router(Xf, W_route, b_route, active, R, eps, route_idx=None):
 
 def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
             gate_mode="sigmoid", gram_schmidt_on=False, gs_eps=1e-6,
-            route=0, W_route=None, b_route=None, route_idx=None, active_tok=None):
+            route=0, W_route=None, b_route=None, route_idx=None, active_tok=None,
+            hres_active=False):
     """One xHC sublayer update, forward ([R-DRSW] write formula, O1-O5).
 
     X:      [B*S, N, C]  residual state before the update
@@ -260,10 +291,12 @@ def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
     route, W_route [N*C, N], b_route [N] or None, route_idx: the router of
             O7 (route = number of routed slots)
     active_tok: [T, k] per-token active lists (O8), or None
+    hres_active: the res logits from the active rows (O9; fixed list only)
 
     Returns a dict with X_new, h_in and the intermediates (z, r, H_pre,
     H_post, H_res, U, idx [T, k] the per-token active list, s [T, k] the
-    write-back scales, and with a router rho, mu, sd).
+    write-back scales, with a router rho, mu, sd, and with hres_active
+    r_act).
     """
     X = np.asarray(X, dtype=np.float64)
     out = np.asarray(out, dtype=np.float64)
@@ -280,6 +313,13 @@ def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
 
     # coefficients from the full flattened state (dense read of all streams)
     z, r, _ = rms_projection(X.reshape(T, N * C), W, bias, eps)
+    extra = {}
+    if hres_active:
+        # O9: the res logits from the active rows alone
+        assert not route and active_tok is None
+        La, r_act, _, _ = res_logits_active(X, W, bias, active, ncomp, eps)
+        z[:, N + k * ncomp:] = La.reshape(T, k * k)
+        extra["r_act"] = r_act
     z_pre, z_post, L = split_logits(z, N, k, ncomp)
     if gate_mode == "sigmoid":
         H_pre, H_post = sigmoid(z_pre), sigmoid(z_post)
@@ -310,6 +350,7 @@ def forward(X, out, W, bias, active, conv_ws, *, B, S, iters=20, eps=1e-6,
     res = dict(X_new=X_new, h_in=h_in, z=z, r=r, H_pre=H_pre,
                H_post=H_post, H_res=H_res, U=U)
     res.update(rt)
+    res.update(extra)
     return res
 
 
@@ -407,7 +448,8 @@ def gram_schmidt_backward(U, gs_eps, dUt):
 
 def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
              iters=20, eps=1e-6, gate_mode="sigmoid", gram_schmidt_on=False, gs_eps=1e-6,
-             route=0, W_route=None, b_route=None, route_idx=None, active_tok=None):
+             route=0, W_route=None, b_route=None, route_idx=None, active_tok=None,
+             hres_active=False):
     """Gradients of the forward above for upstream gradients dX_new, dh_in.
 
     Returns dict(dX [T,N,C], dout [T,C], dW [N*C,P], db [P],
@@ -429,6 +471,10 @@ def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
 
     Xf = X.reshape(T, N * C)
     z, r, xhat = rms_projection(Xf, W, bias, eps)
+    if hres_active:
+        assert not route and active_tok is None
+        La, r_act, xa_hat, W_act = res_logits_active(X, W, bias, act, ncomp, eps)
+        z[:, N + k * ncomp:] = La.reshape(T, k * k)
     z_pre, z_post, L = split_logits(z, N, k, ncomp)
     if gate_mode == "sigmoid":
         H_pre, H_post = sigmoid(z_pre), sigmoid(z_post)
@@ -470,11 +516,23 @@ def backward(X, out, W, bias, active, conv_ws, dX_new, dh_in, *, B, S,
 
     # through the RMS-normed projection
     db = dz.sum(axis=0)
-    dW = xhat.T @ dz
-    dxhat = dz @ W.T
+    dz_full = dz.copy()
+    if hres_active:
+        dz_full[:, N + k * ncomp:] = 0.0        # the res logits do not read the full state
+    dW = xhat.T @ dz_full
+    dxhat = dz_full @ W.T
     n = N * C
     dXf = (dxhat - xhat * (np.sum(dxhat * xhat, axis=1, keepdims=True) / n)) / r[:, None]
     dX += dXf.reshape(T, N, C)
+    if hres_active:
+        # O9: the res logits' RMS-normed projection of the active rows
+        res0 = N + k * ncomp
+        dLf = dz[:, res0:]
+        dWa = xa_hat.T @ dLf                                   # [k*C, k*k]
+        dW.reshape(N, C, P)[act, :, res0:] += dWa.reshape(k, C, k * k)
+        dxa = dLf @ W_act.T
+        dXa = (dxa - xa_hat * (np.sum(dxa * xa_hat, axis=1, keepdims=True) / (k * C))) / r_act[:, None]
+        dX[:, act, :] += dXa.reshape(T, k, C)
 
     # through the router's scales, then its LayerNorm (O7)
     extra = {}
