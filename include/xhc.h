@@ -74,8 +74,14 @@ enum {
   XHC_ERR_ALIGN = -5,        /* a pointer is not 16-byte aligned            */
   XHC_ERR_UNSUPPORTED = -6,  /* a mode the library does not implement       */
   XHC_ERR_WORKSPACE = -7,    /* workspace NULL or smaller than required     */
-  XHC_ERR_HIP = -8           /* a HIP call or kernel launch failed          */
+  XHC_ERR_HIP = -8,          /* a HIP call or kernel launch failed          */
+  XHC_ERR_SCRATCH = -9       /* xhc_forward_noalloc: the problem needs more
+                                scratch than XHC_NOALLOC_SCRATCH_BYTES      */
 };
+
+/* Size of the static device scratch array of xhc_forward_noalloc (64 MiB;
+ * each GPU the library runs on holds one until the process ends). */
+#define XHC_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* Problem description.  Supported: B, S >= 1; 1 <= k <= 4; k <= N <= 16;
  * ncomp in {1, 4} (4 = TFA on: out plus three causal convolutions; 1 = out
@@ -218,6 +224,23 @@ int xhc_validate(const xhc_desc* desc, const void* args, int phase);
  * shared with a concurrent call. */
 int xhc_forward(const xhc_desc* desc, const xhc_fwd_args* args,
                 void* workspace, size_t workspace_bytes, xhc_stream_t stream);
+
+/* xhc_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The scratch that xhc_forward keeps in
+ * the caller's workspace lives in a static device array of the library
+ * instead (XHC_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends);
+ * the call allocates and frees nothing.  Arguments and results are those of
+ * xhc_forward (same kernels); args->timer must be NULL (a timer creates HIP
+ * events: XHC_ERR_UNSUPPORTED).  A problem whose xhc_workspace_size(desc,
+ * XHC_PHASE_FWD) exceeds XHC_NOALLOC_SCRATCH_BYTES is refused with
+ * XHC_ERR_SCRATCH before anything is launched.  Every call on one GPU uses
+ * that GPU's one array, which keeps the last call's contents: calls that
+ * overlap in time on one GPU (other streams, other threads) race on it and
+ * must be serialised by the caller.  The first call on a device looks up
+ * that device's copy of the array (hipGetSymbolAddress, with the device
+ * current); a failure there is XHC_ERR_HIP. */
+int xhc_forward_noalloc(const xhc_desc* desc, const xhc_fwd_args* args, xhc_stream_t stream);
 
 /* Backward of xhc_forward: gradients of X, out, W, bias and the conv
  * weights from those of X_new and h_in, through the unrolled Sinkhorn.

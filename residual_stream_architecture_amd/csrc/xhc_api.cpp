@@ -290,6 +290,12 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
   return XHC_OK;
 }
 
+int prepare_forward(const xhc_desc* d, const xhc_fwd_args* a, Plan* p) {
+  int rc = make_plan(d, p);
+  if (rc) return rc;
+  return validate_fwd(*p, a);
+}
+
 }  // namespace xhc
 
 // ---------------------------------------------------------------------------
@@ -431,6 +437,7 @@ const char* xhc_strerror(int code) {
     case XHC_ERR_UNSUPPORTED: return "mode not supported";
     case XHC_ERR_WORKSPACE: return "workspace missing or too small";
     case XHC_ERR_HIP: return "HIP call or kernel launch failed";
+    case XHC_ERR_SCRATCH: return "problem needs more scratch than the library's static buffer holds";
     default: return "unknown xhc error";
   }
 }

@@ -135,5 +135,8 @@ struct Plan {
 // Fills `p` from `d`; returns XHC_OK or an XHC_ERR_* code for an
 // unsupported description.
 int make_plan(const xhc_desc* d, Plan* p);
+// make_plan, then the forward's argument checks (what xhc_validate does for
+// XHC_PHASE_FWD).
+int prepare_forward(const xhc_desc* d, const xhc_fwd_args* a, Plan* p);
 
 }  // namespace xhc

@@ -15,9 +15,10 @@ XHC_GATE_SIGMOID, XHC_GATE_UNIT = 0, 1
 XHC_PHASE_FWD, XHC_PHASE_BWD = 0, 1
 ERRORS = {0: "XHC_OK", -1: "XHC_ERR_NULL", -2: "XHC_ERR_SHAPE", -3: "XHC_ERR_INDEX",
           -4: "XHC_ERR_ALIAS", -5: "XHC_ERR_ALIGN", -6: "XHC_ERR_UNSUPPORTED",
-          -7: "XHC_ERR_WORKSPACE", -8: "XHC_ERR_HIP"}
+          -7: "XHC_ERR_WORKSPACE", -8: "XHC_ERR_HIP", -9: "XHC_ERR_SCRATCH"}
 (XHC_OK, XHC_ERR_NULL, XHC_ERR_SHAPE, XHC_ERR_INDEX, XHC_ERR_ALIAS, XHC_ERR_ALIGN, XHC_ERR_UNSUPPORTED,
- XHC_ERR_WORKSPACE, XHC_ERR_HIP) = 0, -1, -2, -3, -4, -5, -6, -7, -8
+ XHC_ERR_WORKSPACE, XHC_ERR_HIP, XHC_ERR_SCRATCH) = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+NOALLOC_SCRATCH_BYTES = 64 << 20      # XHC_NOALLOC_SCRATCH_BYTES
 
 _vp = ctypes.c_void_p
 _fp = ctypes.POINTER(ctypes.c_float)
@@ -78,6 +79,8 @@ def _load():
     L.xhc_validate.restype = ctypes.c_int
     L.xhc_forward.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_fwd_args), _vp, ctypes.c_size_t, _vp]
     L.xhc_forward.restype = ctypes.c_int
+    L.xhc_forward_noalloc.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_fwd_args), _vp]
+    L.xhc_forward_noalloc.restype = ctypes.c_int
     L.xhc_carry_size.argtypes = [ctypes.POINTER(xhc_desc)]
     L.xhc_carry_size.restype = ctypes.c_size_t
     L.xhc_forward_chain.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_fwd_args),
@@ -236,6 +239,26 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
                                ws.numel(), _stream_handle(stream))
     if rc:
         raise XhcError(rc, "xhc_forward_chain")
+
+
+def forward_noalloc(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None, bias=None,
+                    z_save=None, xact_save=None, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID, stream=None,
+                    desc=None, gram_schmidt=False, gs_eps=1e-6, route=0, W_route=None, b_route=None,
+                    route_idx=None):
+    """xhc_forward_noalloc: xhc_forward with the library's static scratch
+    array in place of a workspace (no device memory is allocated)."""
+    T, N, C = X.shape
+    ncomp = 4 if w4 is not None else 1
+    if desc is None:
+        desc = make_desc(B, S, C, N, len(active), ncomp, _dtype_code(X), iters, eps, gate_mode,
+                         gram_schmidt, gs_eps, route)
+    act = _active_array(active)
+    args = xhc_fwd_args(_ptr(X), _ptr(out), _ptr(w4), _ptr(w8), _ptr(w12), _ptr(W), _ptr(bias),
+                        ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(X_new), _ptr(h_in),
+                        _ptr(z_save), _ptr(xact_save), None, _ptr(W_route), _ptr(b_route), _ptr(route_idx))
+    rc = lib.xhc_forward_noalloc(ctypes.byref(desc), ctypes.byref(args), _stream_handle(stream))
+    if rc:
+        raise XhcError(rc, "xhc_forward_noalloc")
 
 
 def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None, w4=None, w8=None,

@@ -181,6 +181,26 @@ def test_calls_fail_before_launch_without_workspace():
     assert rc == -5
 
 
+def test_noalloc_refuses_before_launch():
+    # xhc_forward_noalloc checks everything before its first HIP call: the
+    # forward's validation, no timer, and a problem that fits its static
+    # scratch array (T = 24576 tokens at C = 4096 needs more than 64 MiB)
+    noalloc = xhc.lib.xhc_forward_noalloc
+    d = desc16()
+    a, keep = good_fwd(d)
+    a.X = None
+    assert noalloc(ctypes.byref(d), ctypes.byref(a), None) == xhc.XHC_ERR_NULL
+    a, keep = good_fwd(d)
+    a.timer = fake(30)
+    assert noalloc(ctypes.byref(d), ctypes.byref(a), None) == xhc.XHC_ERR_UNSUPPORTED
+    big = desc16(B=3, S=8192, C=4096)
+    assert xhc.workspace_size(big, 0) > xhc.NOALLOC_SCRATCH_BYTES
+    a, keep = good_fwd(big)
+    assert noalloc(ctypes.byref(big), ctypes.byref(a), None) == xhc.XHC_ERR_SCRATCH
+    # the headline workload's forward fits
+    assert xhc.workspace_size(desc16(B=2, S=4096, C=4096), 0) <= xhc.NOALLOC_SCRATCH_BYTES
+
+
 def good_chain():
     return xhc.xhc_chain_args(carry_in=fake(21), W_next=fake(22), carry_out=fake(23))
 
@@ -245,7 +265,7 @@ def test_chain_error_paths():
 
 
 def test_strerror():
-    for c in range(0, -9, -1):
+    for c in range(0, -10, -1):
         assert xhc.strerror(c)
     assert "unknown" in xhc.strerror(-99)
 
