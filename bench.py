@@ -43,6 +43,9 @@ def parse():
                     help="fwd+bwd: capture one step in a HIP graph (torch.cuda.CUDAGraph) and time its replays")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 2 GiB device copy (HBM counter calibration) and exit")
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the hand-written bandwidth probes (libxhc_probe.so: streaming read, copy, "
+                         "two reads + one write, and the per-token-row run patterns of the xHC kernels) and exit")
     return ap.parse_args()
 
 
@@ -141,6 +144,73 @@ def copy_probe(torch):
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t) / reps
     print(json.dumps({"copy_probe_bytes": 2 * n * 2, "ms": dt * 1e3, "GBps": 4 * n / dt / 1e9}), flush=True)
+
+
+PROBE_RUNS = (128, 256, 512, 1024)
+
+
+def bandwidth_probes(torch):
+    """Bandwidth of plain access patterns on this GPU, timed with events on
+    the launch stream (median of 10 launches after 3 warm-ups):
+      stream_*   contiguous streaming, every workgroup its own slice
+      rows_*     per-token rows of 128 KiB (the state of one token at
+                 N = 16, C = 4096, bf16) over 8192 tokens; each workgroup owns
+                 `run` bytes of every row of its token split -- 2r1w is the
+                 backward assembly kernel's mix (state and dX_new read, dX
+                 written), 1r the projection's and the backward dots' reads.
+    Bytes are the bytes each probe must move (reads + writes)."""
+    import ctypes
+    from residual_stream_architecture_amd import build as b
+    if not os.path.exists(b.PROBE_LIB):
+        raise SystemExit(f"{b.PROBE_LIB} is missing: build first")
+    L = ctypes.CDLL(b.PROBE_LIB)
+    vp = ctypes.c_void_p
+    L.xhc_probe_stream.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    L.xhc_probe_rows.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, vp, vp]
+    T, row = 8192, 16 * 4096 * 2
+    nbytes = T * row                                   # 1 GiB per buffer
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    for i, t in enumerate(bufs):
+        t.fill_(i + 1)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    a, bb, d = (t.data_ptr() for t in bufs)
+
+    def timed(fn, moved):
+        for _ in range(3):
+            rc = fn()
+            if rc:
+                raise RuntimeError(f"probe launch failed ({rc})")
+        times = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        times.sort()
+        med = times[len(times) // 2]
+        return {"bytes": moved, "us": round(med * 1e6, 1), "GBps": round(moved / med / 1e9, 1),
+                "frac_of_peak": round(moved / med / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    res = {}
+    for nr, nw, name in ((1, 0, "1r"), (1, 1, "1r1w"), (2, 1, "2r1w")):
+        for blocks in (1024, 4096):
+            res[f"stream_{name}_wg{blocks}"] = timed(
+                lambda: L.xhc_probe_stream(a, bb, d, nbytes, nr, nw, blocks, sink.data_ptr(), st.cuda_stream),
+                (nr + nw) * nbytes)
+    for nr, nw, name in ((1, 0, "1r"), (2, 1, "2r1w")):
+        for run in PROBE_RUNS:
+            splits = max(1, 2048 // (row // run))
+            res[f"rows_{name}_run{run}"] = timed(
+                lambda: L.xhc_probe_rows(a, bb, d, T, row, run, nr, nw, splits, sink.data_ptr(), st.cuda_stream),
+                (nr + nw) * nbytes)
+            res[f"rows_{name}_run{run}"]["grid"] = (row // run) * splits
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "hbm bandwidth of plain access patterns", "peak_GBps": HBM_PEAK_GBPS,
+                      "results": res}), flush=True)
 
 
 def cpu_baseline(w, ntok):
@@ -298,6 +368,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(torch)
+        return
+    if args.probe:
+        bandwidth_probes(torch)
         return
 
     w = synth.WORKLOADS[args.workload]

@@ -12,6 +12,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["xhc_api.cpp", "xhc_fwd.hip", "xhc_bwd.hip", "xhc_chain.hip", "xhc_route.hip", "xhc_noalloc.hip"]
 LIB = os.path.join(PKG, "libxhc.so")
+# bandwidth probes for the benchmark: a library of their own, not part of libxhc
+PROBE_SOURCE = "xhc_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libxhc_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
@@ -40,7 +43,7 @@ def build(verbose=False):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     objs = []
     cmds = []
-    for s in SOURCES:
+    for s in SOURCES + [PROBE_SOURCE]:
         obj = os.path.join(BUILD_DIR, s + ".o")
         objs.append(obj)
         cmds.append([hipcc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", obj])
@@ -48,10 +51,11 @@ def build(verbose=False):
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
-    _check_kernel_stubs(tmp)
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs[:-1]), (PROBE_LIB, objs[-1:])):
+        tmp = lib + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *lib_objs])
+        _check_kernel_stubs(tmp)
+        os.replace(tmp, lib)
     return LIB
 
 
