@@ -98,6 +98,16 @@ enum {
  * a zero component (zero conv weights) at 0.  With ncomp == 1 it is the
  * identity.  A description with gram_schmidt = 0 (a zero-filled tail) is the
  * form without it, which the pages use when the backbone trains with Muon.
+ * Accuracy: the library runs the procedure on each token's 4x4 Gram matrix
+ * of the raw components (fp32 sums over C), the same procedure in exact
+ * arithmetic.  Its error grows with the conditioning of that matrix: with
+ * nearly collinear components (cosines of 0.99 and more) and fp32 storage,
+ * X_new, h_in, dX and dout stay within 1e-4 + 1e-4 |ref| of an fp64
+ * reference, but the gradient of the post logits carries relative errors up
+ * to about 1e-3 on small entries, and dW, db and the conv-weight gradients
+ * (sums over tokens) are then within 1e-3 of each column's largest
+ * magnitude (about 1e-4 measured at cosine 0.999) rather than element by
+ * element.
  *
  * Router (route = R > 0; source: the retrospective's section "模型可以拥有
  * 16 条 streams，但每层只更新 4 条", the paragraphs on fixed and routed
@@ -114,7 +124,21 @@ enum {
  * + s_a sum_m H_post[a,m] U_m.  The choice is discrete: the gradient reaches
  * the chosen streams' scores through s only.  Supported with at most 15
  * candidate streams (N - (k-R) <= 15, so at N = 16 at least one fixed
- * stream) and 1 <= R <= k; not with the chained forward. */
+ * stream) and 1 <= R <= k; not with the chained forward.
+ *
+ * H_res from the active rows (hres_active = 1; source: the retrospective's
+ * section "模型可以拥有 16 条 streams，但每层只更新 4 条", which credits the
+ * sparse write with generating H_res at k^3 C instead of N^3 C cost): the
+ * k*k res logits are the RMS-normed projection of the k active rows alone,
+ *   xa = [X[t, i_0], .., X[t, i_{k-1}]],  r_act = sqrt(mean(xa^2) + rms_eps)
+ *   L[a, b] = sum_{a'} X[t, i_{a'}] / r_act . W[i_{a'}*C .. , res column
+ *             a*k + b] + bias
+ * (the active streams' rows of W, normalised by the active state's own
+ * RMS); the pre and post logits stay those of the full state.  W's res
+ * columns on the other streams' rows are not read, and xhc_backward writes
+ * zeros there in dW (or leaves them with accumulate = 1).  z_save then
+ * holds P + 2 floats per token: logits, r, r_act.  With k = N it is the
+ * default form. */
 typedef struct {
   int32_t B, S, C, N, k, ncomp;
   int32_t sinkhorn_iters;   /* Sinkhorn row+column steps (20 by default)    */
@@ -133,6 +157,10 @@ typedef struct {
                                must hold distinct streams, ids outside
                                [0, N) are read as 0); requires route = 0 and
                                is not chained.  0: off                      */
+  int32_t hres_active;      /* 1: H_res generated from the k active rows (see
+                               below); requires route = 0 and
+                               per_token_active = 0, and is not chained.
+                               0: off (every logit from the full state)     */
 } xhc_desc;
 
 /* Optional per-kernel timer (HIP events around every kernel a call
@@ -211,7 +239,8 @@ size_t xhc_workspace_size(const xhc_desc* desc, int phase);
 /* Floats per token of z_save: P + 1 (logits, r) without a router; with
  * route = R > 0, P + 3 + 3R: logits, r, the LayerNorm mean and sd, then per
  * routed slot its score rho, rho - b_route and the column sum of W_route of
- * the chosen stream.  0 for an invalid description.  Pure host code. */
+ * the chosen stream; with hres_active, P + 2: logits, r, r_act.  0 for an
+ * invalid description.  Pure host code. */
 int32_t xhc_zsave_stride(const xhc_desc* desc);
 
 /* Checks desc and args (an xhc_fwd_args* or xhc_bwd_args* per phase):

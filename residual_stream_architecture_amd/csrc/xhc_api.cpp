@@ -34,6 +34,8 @@ int make_plan(const xhc_desc* d, Plan* p) {
   if (d->route > 0 && d->N - (d->k - d->route) > 15) return XHC_ERR_UNSUPPORTED;
   if (d->per_token_active != 0 && d->per_token_active != 1) return XHC_ERR_UNSUPPORTED;
   if (d->per_token_active && d->route) return XHC_ERR_UNSUPPORTED;
+  if (d->hres_active != 0 && d->hres_active != 1) return XHC_ERR_UNSUPPORTED;
+  if (d->hres_active && (d->route || d->per_token_active)) return XHC_ERR_UNSUPPORTED;
 
   Plan& q = *p;
   q.B = d->B; q.S = d->S; q.C = d->C; q.N = d->N; q.k = d->k; q.nc = d->ncomp;
@@ -50,7 +52,8 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.nfix = q.k - q.R;
   q.ncand = q.R ? q.N - q.nfix : 0;
   if (q.R) q.NT = 4;                       // tile 3: router candidates + sum(x)
-  q.zsv = q.R ? q.P + 3 + 3 * q.R : q.P + 1;
+  q.hact = d->hres_active == 1;
+  q.zsv = q.R ? q.P + 3 + 3 * q.R : q.hact ? q.P + 2 : q.P + 1;
   q.dzs = q.pt ? DZ_R : 48;
   q.dwr = q.pt ? 64 : 48;
   q.rec_bytes = q.pt ? REC_R_BYTES : REC_BYTES;
@@ -210,6 +213,8 @@ static int validate_fwd(const Plan& p, const xhc_fwd_args* a, bool need_W = true
 static int validate_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const xhc_chain_args* c) {
   if (!c) return XHC_OK;
   if (p.pt || pn.pt) return XHC_ERR_UNSUPPORTED;
+  // the carried partials sum every stream of a channel block
+  if (p.hact || pn.hact) return XHC_ERR_UNSUPPORTED;
   if ((c->W_next == nullptr) != (c->carry_out == nullptr)) return XHC_ERR_NULL;
   if (misaligned(c->carry_in) || misaligned(c->carry_out) || misaligned(c->W_next)) return XHC_ERR_ALIGN;
   if (pn.B != p.B || pn.S != p.S || pn.C != p.C || pn.N != p.N || pn.dtype != p.dtype) return XHC_ERR_SHAPE;
@@ -253,6 +258,9 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
   if (p.R) {
     // the router's choice and scores come from the forward's records
     if (!a->route_idx || !a->W_route || !a->dW_route) return XHC_ERR_NULL;
+    // recomputing the scores needs the forward's b_route: a NULL here would
+    // silently stand for zero while the forward may have used another value
+    if (!a->z_save && !a->b_route) return XHC_ERR_NULL;
   }
   if (p.pt && !a->route_idx) return XHC_ERR_NULL;
   // recomputing the logits maps saved rows by the host list: not per token

@@ -637,7 +637,7 @@ __global__ __launch_bounds__(16 * BCOEF_TOK) void k_bcoef(const float* __restric
                                               int P, float inv_nc_total, int iters, int unit_gates,
                                               float gs_ceps, float* __restrict__ hpost, float* __restrict__ gss,
                                               int zsv, int dzstride, const int32_t* __restrict__ ridx, int nfix,
-                                              float* __restrict__ hres, int has_router) {
+                                              float* __restrict__ hres, int has_router, HresActive ha) {
   extern __shared__ float hist[];   // [BCOEF_TOK][iters+1][16]
   __shared__ float dzs[BCOEF_TOK][64];
   const int e = threadIdx.x & 15, tok = threadIdx.x >> 4;
@@ -658,6 +658,7 @@ __global__ __launch_bounds__(16 * BCOEF_TOK) void k_bcoef(const float* __restric
   for (int cb = 0; cb < ncb; ++cb) dpost += dpart[((size_t)cb * T + tc) * DOT_STRIDE + 32 + e];
   const float* z = zin + tc * zsv;
   const float r = z[P];
+  const float r_act = ha.mask ? z[P + 1] : r;     // hres_active: the res logits' normaliser
 
   // gates (recomputed from the logits, as the forward computed them)
   const bool pre_ok = e < N;
@@ -820,18 +821,27 @@ __global__ __launch_bounds__(16 * BCOEF_TOK) void k_bcoef(const float* __restric
   if (valid) dzs[tok][N + k * nc + a * k + b] = dL;
   __syncthreads();
 
-  // gamma = dz.(z - bias) / (N*C*r^2)
-  float al = 0.f;
+  // gamma = dz.(z - bias) / (N*C*r^2); with hres_active the res logits'
+  // share goes to gamma_act = dz_res.(z_res - bias) / (k*C*r_act^2), which
+  // only the active rows receive
+  float al = 0.f, al_act = 0.f;
 #pragma unroll
   for (int n = 0; n < 3; ++n) {
     const int p = e + 16 * n;
-    if (p < P) al = fmaf(dzs[tok][p], z[p] - (bias ? bias[p] : 0.f), al);
+    const float v = p < P ? dzs[tok][p] * (z[p] - (bias ? bias[p] : 0.f)) : 0.f;
+    if (ha.mask && p >= ha.res0 && p < ha.res1) al_act += v;
+    else al += v;
   }
   al += row_xor<1>(al);
   al += row_xor<2>(al);
   al += row_xor<4>(al);
   al += row_xor<8>(al);
+  al_act += row_xor<1>(al_act);
+  al_act += row_xor<2>(al_act);
+  al_act += row_xor<4>(al_act);
+  al_act += row_xor<8>(al_act);
   const float inv_r = 1.f / r;
+  const float inv_ra = 1.f / r_act;
   if (tv) {
 #pragma unroll
     for (int n = 0; n < 3; ++n) dz_out[t * dzstride + e + 16 * n] = dzs[tok][e + 16 * n];
@@ -852,7 +862,8 @@ __global__ __launch_bounds__(16 * BCOEF_TOK) void k_bcoef(const float* __restric
 #pragma unroll
     for (int n = 0; n < NT_REC; ++n) {
       const int p = e + 16 * n;                      // logits 0..47 (router: 48..63 = drho / sd per stream)
-      const float v = tv ? (n < 3 ? dzs[tok][p] * inv_r : drs / rsd) : 0.f;
+      const float inv_n = (ha.mask && p >= ha.res0 && p < ha.res1) ? inv_ra : inv_r;
+      const float v = tv ? (n < 3 ? dzs[tok][p] * inv_n : drs / rsd) : 0.f;
       size_t o_dzr, dzr_half;
       if (p < 32) {
         o_dzr = REC_DZR0 + ((size_t)(((p >> 3) * 16 + tt) * 8 + (p & 7))) * EB;
@@ -889,8 +900,9 @@ __global__ __launch_bounds__(16 * BCOEF_TOK) void k_bcoef(const float* __restric
       float* rco = reinterpret_cast<float*>(rb + REC_CO);
       rco[(RF_PRE + e) * B2_TT + tt] = tv ? hp : 0.f;
       rco[(RF_RES + e) * B2_TT + tt] = tv ? H[iters * 16 + e] : 0.f;
+      const float gam_act = al_act * ha.inv_kc * inv_ra * inv_ra;
       if (e < REC_NF - RF_GAMMA)
-        rco[(RF_GAMMA + e) * B2_TT + tt] = (tv && e == 0) ? gam : 0.f;
+        rco[(RF_GAMMA + e) * B2_TT + tt] = tv ? (e == 0 ? gam : e == 1 ? gam_act : 0.f) : 0.f;
     }
   }
 }
@@ -931,12 +943,23 @@ template <typename E> struct B2Lds {
   static constexpr int ROWTILE = 4 * GSTRIDE;
 };
 
+// LDS of the row-group body: the double-buffered tile records with the dh_in
+// blocks, then the published dX_new and X row tiles.
+template <typename E, bool ROUTE>
+constexpr int bgrad_sbuf() {
+  return (ROUTE ? REC_R_USED : REC_USED) + B2_TT * B2_CB * E::bytes;
+}
+template <typename E, bool ROUTE>
+constexpr int bgrad_lds_bytes() {
+  return 2 * B2_SUB * bgrad_sbuf<E, ROUTE>() + 2 * B2_SUB * B2_WAVES * B2Lds<E>::ROWTILE;
+}
+
 template <typename E, bool ROUTE>
 __device__ __forceinline__ void bgrad_body(
     StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin, const void* __restrict__ Wp,
     const unsigned char* __restrict__ rec, int ntiles, void* dX, float* __restrict__ dwp, int T, int C, int N, int k,
-    RowTable rows, int nrg, int ncb, int tok_per_split, const void* __restrict__ passbuf,
-    const int32_t* __restrict__ ridx, const void* __restrict__ xact) {
+    RowTable rows, int rg, int cb, int ts, int tok_per_split, const void* __restrict__ passbuf,
+    const int32_t* __restrict__ ridx, const void* __restrict__ xact, int wz0, int wz1, unsigned char* smem) {
   constexpr bool BF = E::bytes == 2;
   constexpr int EB = E::bytes;
   using LY = B2Lds<E>;
@@ -953,14 +976,13 @@ __device__ __forceinline__ void bgrad_body(
   constexpr int NCH = NREC + DHB / 1024;
   constexpr int STEP = B2_TT * B2_SUB;
   static_assert(RUSED % 16 == 0 && DHB % 1024 == 0 && RUSED <= RSTRIDE, "record copy split");
-  __shared__ __attribute__((aligned(16))) unsigned char rbuf[2][B2_SUB][SBUF];
-  __shared__ __attribute__((aligned(16))) unsigned char gsh[B2_SUB][B2_WAVES][LY::ROWTILE];   // dX_new rows
-  __shared__ __attribute__((aligned(16))) unsigned char xsh[B2_SUB][B2_WAVES][LY::ROWTILE];   // X rows
+  static_assert(SBUF == bgrad_sbuf<E, ROUTE>(), "LDS layout");
+  typedef unsigned char RbufT[B2_SUB][SBUF];
+  typedef unsigned char RowT[B2_WAVES][LY::ROWTILE];
+  RbufT* rbuf = reinterpret_cast<RbufT*>(smem);                                     // [2] tile records + dh_in
+  RowT* gsh = reinterpret_cast<RowT*>(smem + 2 * B2_SUB * SBUF);                    // [B2_SUB] dX_new rows
+  RowT* xsh = reinterpret_cast<RowT*>(smem + 2 * B2_SUB * SBUF + B2_SUB * sizeof(RowT));   // [B2_SUB] X rows
 
-  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int rg = lb % nrg;
-  const int cb = (lb / nrg) % ncb;
-  const int ts = lb / (nrg * ncb);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: rsrc and M0 stay scalar
   const int slot = wave & 3, chalf = wave >> 2;
@@ -996,6 +1018,23 @@ __device__ __forceinline__ void bgrad_body(
     } else {
       const Vec<E, 4> vb = Vec<E, 4>::load(Wp, row + 32 + 4 * g4);
       wb[jt] = ok ? vb : Vec<E, 4>::zero();
+    }
+  }
+  if (!ROUTE && !active_grp && wz0 < wz1) {
+    // hres_active: the res logits [wz0, wz1) do not read the untouched rows
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      float fa[8], fb[4];
+      wa[jt].to_float(fa);
+      wb[jt].to_float(fb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (8 * g4 + j >= wz0 && 8 * g4 + j < wz1) fa[j] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (32 + 4 * g4 + j >= wz0 && 32 + 4 * g4 + j < wz1) fb[j] = 0.f;
+      wa[jt] = V8<E>::from_float(fa);
+      wb[jt] = Vec<E, 4>::from_float(fb);
     }
   }
   f32x4 dwacc[2][NPT];
@@ -1205,23 +1244,28 @@ __device__ __forceinline__ void bgrad_body(
             bz1l = *reinterpret_cast<const Vec<E, 4>*>(rb + off1 + rec_dzr1_half(EB));
           }
         }
+        // the K = 32 and K = 16 steps accumulate apart and are added on the
+        // VALU: an MFMA of one shape accumulating onto the result of the
+        // other shape needs wait states that the compiler does not insert
+        // (such a chain gave timing-dependent wrong sums)
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          acc = mma32(wa[jt], bz0, acc);
-          acc = mma16(wb[jt], bz1, acc);
+          f32x4 a32 = {0.f, 0.f, 0.f, 0.f}, a16 = {0.f, 0.f, 0.f, 0.f};
+          a32 = mma32(wa[jt], bz0, a32);
+          a16 = mma16(wb[jt], bz1, a16);
           if constexpr (BF) {
-            acc = mma32(wa[jt], bz0l, acc);
-            acc = mma16(wb[jt], bz1l, acc);
+            a32 = mma32(wa[jt], bz0l, a32);
+            a16 = mma16(wb[jt], bz1l, a16);
           }
-          pj[jt] = acc;
+          pj[jt] = a32 + a16;
         }
       }
       // ---- assemble dX for (token tk, channels cl..cl+8) ----
       {
         const float* co = reinterpret_cast<const float*>(rb + RCO);
         const float hpre = co[(F_PRE + srow) * B2_TT + r16];
-        const float gam = co[F_GAMMA * B2_TT + r16];
+        // the active rows also take gamma_act (hres_active; 0 otherwise)
+        const float gam = co[F_GAMMA * B2_TT + r16] + ((!ROUTE && active_grp) ? co[(F_GAMMA + 1) * B2_TT + r16] : 0.f);
         const float cst = ROUTE ? co[RRF_CONST * B2_TT + r16] : 0.f;
         float pass[8];
         if (active_grp) {
@@ -1330,15 +1374,21 @@ __device__ __forceinline__ void bgrad_body(
   }
 }
 
-// The B2 kernels: the fixed-list form, and the routed form held to four
-// waves per SIMD (at most 128 VGPRs) so that two workgroups share a CU.
+// The B2 kernels: the fixed-list form and the routed form (every row group
+// in the row-group body), both held to four waves per SIMD (at most 128
+// VGPRs, no spills) so that two workgroups share a CU.
 template <typename E>
-__global__ __launch_bounds__(512) void k_bgrad(
+__global__ __launch_bounds__(512, 4) void k_bgrad(
     StreamRows src, const void* __restrict__ dXn, const void* __restrict__ dhin, const void* __restrict__ Wp,
     const unsigned char* __restrict__ rec, int ntiles, void* dX, float* __restrict__ dwp, int T, int C, int N, int k,
-    RowTable rows, int nrg, int ncb, int tok_per_split) {
-  bgrad_body<E, false>(src, dXn, dhin, Wp, rec, ntiles, dX, dwp, T, C, N, k, rows, nrg, ncb, tok_per_split, nullptr,
-                       nullptr, nullptr);
+    RowTable rows, int nrg, int ncb, int tok_per_split, int wz0, int wz1) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[bgrad_lds_bytes<E, false>()];
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int rg = lb % nrg;
+  const int cb = (lb / nrg) % ncb;
+  const int ts = lb / (nrg * ncb);
+  bgrad_body<E, false>(src, dXn, dhin, Wp, rec, ntiles, dX, dwp, T, C, N, k, rows, rg, cb, ts, tok_per_split,
+                       nullptr, nullptr, nullptr, wz0, wz1, smem);
 }
 template <typename E>
 __global__ __launch_bounds__(512, 4) void k_bgrad_route(
@@ -1346,8 +1396,13 @@ __global__ __launch_bounds__(512, 4) void k_bgrad_route(
     const unsigned char* __restrict__ rec, int ntiles, void* dX, float* __restrict__ dwp, int T, int C, int N, int k,
     RowTable rows, int nrg, int ncb, int tok_per_split, const void* __restrict__ passbuf,
     const int32_t* __restrict__ ridx, const void* __restrict__ xact) {
-  bgrad_body<E, true>(src, dXn, dhin, Wp, rec, ntiles, dX, dwp, T, C, N, k, rows, nrg, ncb, tok_per_split, passbuf,
-                      ridx, xact);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[bgrad_lds_bytes<E, true>()];
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int rg = lb % nrg;
+  const int cb = (lb / nrg) % ncb;
+  const int ts = lb / (nrg * ncb);
+  bgrad_body<E, true>(src, dXn, dhin, Wp, rec, ntiles, dX, dwp, T, C, N, k, rows, rg, cb, ts, tok_per_split, passbuf,
+                      ridx, xact, 0, 0, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1371,7 +1426,7 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, i
                                                 int C, float* __restrict__ dw4, float* __restrict__ dw8,
                                                 float* __restrict__ dw12, int nb_dw, int accumulate, int dwr,
                                                 int dzs, int nb_conv, float* __restrict__ db_route,
-                                                float* __restrict__ rred, int N) {
+                                                float* __restrict__ rred, int N, HresActive ha) {
   __shared__ float sm[256];
   const int nrt = (int)gridDim.x - (nb_dw + P + nb_conv);     // router sums (0 or 32)
   const int nfirst = P + nrt;                                   // db and router blocks go first
@@ -1411,9 +1466,13 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dwp, i
       s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
     }
     float* dst = dW + (size_t)j * P + p0;
+    // hres_active: the res columns of the untouched streams' rows get no gradient
+    const bool untouched = ha.mask && !((ha.mask >> (int)(j / C)) & 1u);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (p0 + e < P) dst[e] = (accumulate ? dst[e] : 0.f) + s[e];
+    for (int e = 0; e < 4; ++e) {
+      const bool zero = untouched && p0 + e >= ha.res0 && p0 + e < ha.res1;
+      if (p0 + e < P) dst[e] = (accumulate ? dst[e] : 0.f) + (zero ? 0.f : s[e]);
+    }
     return;
   }
   if (bid < nb_dw + P) {
@@ -1485,6 +1544,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   const StreamRows src = stream_rows(p, a->X, rt ? nullptr : a->xact, a->active);
   Act4 act;
   for (int b = 0; b < 4; ++b) act.id[b] = b < p.k && !rt ? a->active[b] : 0;
+  const HresActive ha = hres_active(p, a->active);
 
   {
     TimedLaunch tl(tm, KID_BXDOTS, st);
@@ -1540,7 +1600,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   k_bcoef<E, GS, RT><<<nb, 16 * BCOEF_TOK, shm, st>>>(dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T,  \
                                           p.Tpad, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.iters,            \
                                           p.gate == XHC_GATE_UNIT, GS ? p.gs_ceps : 0.f, hpost,                \
-                                          GS ? gss : nullptr, p.zsv, p.dzs, ridx, p.nfix, hres, p.R > 0)
+                                          GS ? gss : nullptr, p.zsv, p.dzs, ridx, p.nfix, hres, p.R > 0, ha)
     if (p.gs) {
       if (rt) XHC_BCOEF(true, true); else XHC_BCOEF(true, false);
     } else {
@@ -1576,15 +1636,17 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
         ++nxt;
       }
     }
-    const int nb = p.b2_rowgroups * p.b2_cblocks * p.b2_ts;
-    if (rt)
+    if (rt) {
+      const int nb = p.b2_rowgroups * p.b2_cblocks * p.b2_ts;
       k_bgrad_route<E><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, (int)(p.Tpad / B2_TT),
                                                      a->dX, dwp, p.T, p.C, p.N, p.k, rows, p.b2_rowgroups,
                                                      p.b2_cblocks, p.b2_tok_per_split, pass, ridx, a->xact);
-    else
+    } else {
+      const int nb = p.b2_rowgroups * p.b2_cblocks * p.b2_ts;
       k_bgrad<E><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, (int)(p.Tpad / B2_TT), a->dX,
                                                dwp, p.T, p.C, p.N, p.k, rows, p.b2_rowgroups, p.b2_cblocks,
-                                               p.b2_tok_per_split);
+                                               p.b2_tok_per_split, ha.res0, ha.mask ? ha.res1 : ha.res0);
+    }
   }
   {
     TimedLaunch tl(tm, KID_BREDUCE, st);
@@ -1592,7 +1654,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
     const int nb_conv = p.nc == 4 ? (int)(((int64_t)p.C * 24 * RED_CONV_LANES + 255) / 256) : 0;
     k_reduce<<<nb_dw + p.P + nb_conv + (rt ? 32 : 0), 256, 0, st>>>(
         dwp, p.b2_ts, p.NC, p.P, a->dW, dz, p.T, a->db, p.nc == 4 ? dwpart : nullptr, p.B * p.b1_segs, p.C, a->dw4,
-        a->dw8, a->dw12, nb_dw, a->accumulate, p.dwr, p.dzs, nb_conv, p.R ? a->db_route : nullptr, rred, p.N);
+        a->dw8, a->dw12, nb_dw, a->accumulate, p.dwr, p.dzs, nb_conv, p.R ? a->db_route : nullptr, rred, p.N, ha);
   }
   if (p.R) {
     TimedLaunch tl(tm, KID_RDWR, st);

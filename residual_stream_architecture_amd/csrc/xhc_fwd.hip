@@ -276,7 +276,7 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
                                               float* __restrict__ coef, float* __restrict__ z_out, int zsv, int T,
                                               int N, int k, int nc, int P, float inv_nc_total, float eps,
                                               int iters, int unit_gates, const float* __restrict__ gram,
-                                              int ngram, float gs_ceps, RouteArgs ra) {
+                                              int ngram, float gs_ceps, RouteArgs ra, HresActive ha) {
   __shared__ float zs[16][COEF_STRIDE];
   __shared__ float csum[16];
   const int e = threadIdx.x & 15, tok = threadIdx.x >> 4;
@@ -287,14 +287,24 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
   if constexpr (ROUTE) {
     if (threadIdx.x < 16) csum[threadIdx.x] = ra.rcs[RCS_BLK * 16 + threadIdx.x];   // W_route's column sums
   }
+  float r_act = 0.f;    // hres_active: RMS of the k active rows
   if (zpart) {
     float ss = (tv && e < SK) ? zpart[((size_t)e * T + t) * ZST + NTP] : 0.f;
+    // (with hres_active the splits are streams: the active ones' share)
+    float sa = ((ha.mask >> e) & 1u) ? ss : 0.f;
     ss += row_xor<1>(ss);
     ss += row_xor<2>(ss);
     ss += row_xor<4>(ss);
     ss += row_xor<8>(ss);
     ssum = ss;
     r = sqrtf(ss * inv_nc_total + eps);
+    if (ha.mask) {
+      sa += row_xor<1>(sa);
+      sa += row_xor<2>(sa);
+      sa += row_xor<4>(sa);
+      sa += row_xor<8>(sa);
+      r_act = sqrtf(sa * ha.inv_kc + eps);
+    }
     // all partial loads issued together (SK <= 16; clamped indices, masked
     // values), summed in split order
     constexpr int NZ = ROUTE ? 4 : 3;
@@ -302,6 +312,10 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
 #pragma unroll
     for (int n = 0; n < NZ; ++n) z[n] = 0.f;
     const int tcl = tv ? t : 0;
+    // hres_active: a res column sums the active streams' splits only
+    bool isres[NZ];
+#pragma unroll
+    for (int n = 0; n < NZ; ++n) isres[n] = ha.mask && e + 16 * n >= ha.res0 && e + 16 * n < ha.res1;
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       const float* zp = zpart + ((size_t)min(s, SK - 1) * T + tcl) * ZST;
@@ -309,13 +323,13 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
 #pragma unroll
       for (int n = 0; n < NZ; ++n) v[n] = zp[min(e + 16 * n, ZST - 1)];
 #pragma unroll
-      for (int n = 0; n < NZ; ++n) z[n] += s < SK ? v[n] : 0.f;
+      for (int n = 0; n < NZ; ++n) z[n] += (s < SK && (!isres[n] || ((ha.mask >> s) & 1u))) ? v[n] : 0.f;
     }
     if constexpr (ROUTE) zr = z[3];
 #pragma unroll
     for (int n = 0; n < 3; ++n) {
       const int p = e + 16 * n;
-      zs[tok][p] = (tv && p < P) ? z[n] / r + (bias ? bias[p] : 0.f) : 0.f;
+      zs[tok][p] = (tv && p < P) ? z[n] / (isres[n] ? r_act : r) + (bias ? bias[p] : 0.f) : 0.f;
     }
   } else {
     r = tv ? z_in[(size_t)t * zsv + P] : 1.f;
@@ -471,6 +485,7 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
       if (p < P) z_out[(size_t)t * zsv + p] = zs[tok][p];
     }
     if (e == 0) z_out[(size_t)t * zsv + P] = r;
+    if (ha.mask && e == 1) z_out[(size_t)t * zsv + P + 1] = r_act;
   }
 }
 
@@ -780,7 +795,7 @@ static int forward_impl(const Plan& p, const Plan& pn, const xhc_fwd_args* a, co
   k_coef<GS, RT><<<(p.T + 15) / 16, 256, 0, st>>>(zp, sk, p.ZST, NTP, nullptr, a->bias, coef, a->z_save, p.zsv, \
                                                   p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps, p.iters,  \
                                                   unit, GS ? gram : nullptr, GS ? p.b1_cblocks : 0,              \
-                                                  GS ? p.gs_ceps : 0.f, ra)
+                                                  GS ? p.gs_ceps : 0.f, ra, hres_active(p, a->active))
     if (p.gs) {
       if (p.R) XHC_COEF(true, true); else XHC_COEF(true, false);
     } else {
@@ -869,12 +884,13 @@ int launch_coef_bwd(const Plan& p, const void* X, const void* xact, const int32_
   if (p.R && !z_save)
     k_coef<false, true><<<(p.T + 15) / 16, 256, 0, st>>>(zpart, p.SK, p.ZST, p.NT * 16, nullptr, bias, coef, z_out,
                                                          p.zsv, p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps,
-                                                         p.iters, p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f, ra);
+                                                         p.iters, p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f, ra,
+                                                         HresActive{});
   else
     k_coef<false, false><<<(p.T + 15) / 16, 256, 0, st>>>(zpart, p.SK, p.ZST, p.NT * 16, z_save, bias, coef, z_out,
                                                           p.zsv, p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps,
                                                           p.iters, p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f,
-                                                          RouteArgs{});
+                                                          RouteArgs{}, hres_active(p, active));
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
 }
 

@@ -53,6 +53,17 @@ inline StreamRows stream_rows(const Plan& p, const void* X, const void* xact, co
   return s;
 }
 
+// The active-row form's description for the kernels (mask 0 when it is off).
+inline HresActive hres_active(const Plan& p, const int32_t* active) {
+  HresActive h{0u, 0, 0, 0.f};
+  if (!p.hact) return h;
+  for (int a = 0; a < p.k; ++a) h.mask |= 1u << active[a];
+  h.res0 = p.N + p.k * p.nc;
+  h.res1 = h.res0 + p.k * p.k;
+  h.inv_kc = 1.0f / ((float)p.k * (float)p.C);
+  return h;
+}
+
 // Order in which the fused write + next-projection pass visits the state
 // rows: the k active rows (in the order of `active`), then the other rows
 // ascending; entries past N repeat the first.  Slot s in bits 4s .. 4s+3.

@@ -57,7 +57,8 @@ constexpr int B2_TARGET_WG = 2048;  // B2 grid: four rounds of 2 workgroups per 
 //                     [half][g 4][t 16] x 4 elements, p = 32 + 4g + e
 //   [REC_DZRT, ..)    dz/r as the dW MFMA's B fragments:
 //                     [half][pt 3][g 4][r 16] x 4 elements, logit 16pt + r, token 4g + e
-//   [REC_CO, +2304)   coefficients [field 36][t 16] floats: H_pre[16], H_res[16], gamma
+//   [REC_CO, +2304)   coefficients [field 36][t 16] floats: H_pre[16], H_res[16], gamma,
+//                     gamma_act (the active rows' extra term with hres_active, else 0)
 // half = bf16 hi and lo parts (bf16 storage) or one fp32 part (fp32 storage);
 // each region has the same size in both storages.
 constexpr int REC_BYTES = 9216;
@@ -87,11 +88,20 @@ constexpr int RCS_BLK = 256; // partial column sums of W_route (forward router),
 constexpr int DZ_R = 80;    // floats per token of the routed backward's dz record:
                             // dz [0,48), drho [48,64), mean*drho/sd [64,80)
 
+// The res logits of the active-row form (hres_active): which logit columns
+// are res columns and which streams are active.
+struct HresActive {
+  unsigned mask;      // bit i: stream i is active (0: the form is off)
+  int res0, res1;     // res logit columns [res0, res1)
+  float inv_kc;       // 1 / (k*C)
+};
+
 struct Plan {
   int B, S, C, N, k, nc, P, NT, T, iters, dtype, gate;
   float eps;
   bool gs;            // Gram-Schmidt over the four components (nc == 4)
   float gs_ceps;      // C * gs_eps
+  bool hact;          // H_res generated from the k active rows (res logits normed by their RMS)
   int R;              // routed slots (0: fixed active list)
   bool pt;            // per-token active lists (the router's, or given by the caller)
   int nfix;           // fixed slots, k - R

@@ -30,7 +30,8 @@ class xhc_desc(ctypes.Structure):
                 ("sinkhorn_iters", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
                 ("gram_schmidt", ctypes.c_int32), ("gs_eps", ctypes.c_float),
-                ("route", ctypes.c_int32), ("per_token_active", ctypes.c_int32)]
+                ("route", ctypes.c_int32), ("per_token_active", ctypes.c_int32),
+                ("hres_active", ctypes.c_int32)]
 
 
 class xhc_fwd_args(ctypes.Structure):
@@ -112,9 +113,9 @@ lib = _load()
 
 
 def make_desc(B, S, C, N, k, ncomp, dtype, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID,
-              gram_schmidt=False, gs_eps=1e-6, route=0, per_token_active=False):
+              gram_schmidt=False, gs_eps=1e-6, route=0, per_token_active=False, hres_active=False):
     return xhc_desc(B, S, C, N, k, ncomp, iters, eps, dtype, gate_mode, int(gram_schmidt), gs_eps, int(route),
-                    int(per_token_active))
+                    int(per_token_active), int(hres_active))
 
 
 def zsave_stride(desc):
@@ -183,13 +184,20 @@ def _stream_handle(stream):
     return s.cuda_stream
 
 
-def _workspace(desc, phase, device, workspace):
+def _workspace(desc, phase, device, workspace, stream):
+    """The caller's workspace, or a fresh one.  A fresh one is allocated on
+    torch's current stream and freed when the call returns, while the
+    kernels may still run on `stream`: it is recorded on that stream, so the
+    caching allocator hands the block out again only after the stream's
+    work up to now has finished."""
     import torch
     need = workspace_size(desc, phase)
     if need == 0:
         raise XhcError(-2, "xhc_workspace_size")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        if stream is not None:
+            workspace.record_stream(stream)
     return workspace, need
 
 
@@ -226,7 +234,7 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
                         ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(X_new), _ptr(h_in),
                         _ptr(z_save), _ptr(xact_save), None if timer is None else timer.handle,
                         _ptr(W_route), _ptr(b_route), _ptr(route_idx))
-    ws, need = _workspace(desc, XHC_PHASE_FWD, X.device, workspace)
+    ws, need = _workspace(desc, XHC_PHASE_FWD, X.device, workspace, stream)
     if carry_in is None and W_next is None and carry_out is None and desc_next is None:
         rc = lib.xhc_forward(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
                              _stream_handle(stream))
@@ -268,7 +276,12 @@ def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None,
              dW_route=None, db_route=None, b_route=None):
     """xhc_backward on torch device tensors (with a router: the forward's
     z_save and route_idx, and dW_route [N*C,N] / db_route [N] fp32 outputs;
-    with per-token lists given by the caller: the same route_idx)."""
+    with per-token lists given by the caller: the same route_idx).
+
+    With a router and z_save=None the backward recomputes the router's
+    scores, and b_route must then be the forward's b_route: the library
+    refuses a missing one (XHC_ERR_NULL) rather than reading it as zero --
+    pass a zero tensor if the forward ran without one."""
     T, N, C = X.shape
     ncomp = 4 if w4 is not None else 1
     if desc is None:
@@ -280,7 +293,7 @@ def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None,
                         _ptr(dh_in), _ptr(dX), _ptr(dout), _ptr(dW), _ptr(db), _ptr(dw4), _ptr(dw8),
                         _ptr(dw12), int(bool(accumulate)), None if timer is None else timer.handle,
                         _ptr(W_route), _ptr(route_idx), _ptr(dW_route), _ptr(db_route), _ptr(b_route))
-    ws, need = _workspace(desc, XHC_PHASE_BWD, X.device, workspace)
+    ws, need = _workspace(desc, XHC_PHASE_BWD, X.device, workspace, stream)
     rc = lib.xhc_backward(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
                           _stream_handle(stream))
     if rc:

@@ -342,7 +342,9 @@ def test_route_backward_error_paths():
         setattr(a, field, None)
         assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_ERR_NULL, field
     a, _ = routed_bwd(d)
-    a.z_save = None                                 # recomputed (b_route may be NULL: zero)
+    a.z_save = None                                 # recomputed: needs the forward's b_route
+    assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_ERR_NULL
+    a.b_route = fake(25)
     assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_OK
     a.xact = fake(2)                                # but not from saved rows
     assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_ERR_UNSUPPORTED
@@ -398,3 +400,31 @@ def test_given_lists_validation():
     a.route_idx = fake(22)
     c = xhc.xhc_chain_args(None, fake(30), fake(31), None)
     assert chain_call(d, a, c) == xhc.XHC_ERR_UNSUPPORTED
+
+
+def test_hres_active_descriptions():
+    # H_res from the active rows: fixed lists only, not chained; z_save holds r_act too
+    d = desc16(hres_active=True)
+    a, keep = good_fwd(d)
+    assert xhc.validate(d, a, xhc.XHC_PHASE_FWD) == xhc.XHC_OK
+    b, keep2 = good_bwd(d)
+    assert xhc.validate(d, b, xhc.XHC_PHASE_BWD) == xhc.XHC_OK
+    P = 16 + 4 * 4 + 16
+    assert xhc.zsave_stride(d) == P + 2 and xhc.zsave_stride(desc16()) == P + 1
+    assert xhc.workspace_size(d, 0) == xhc.workspace_size(desc16(), 0)
+    for kw in (dict(route=2), dict(per_token_active=True)):
+        dd = desc16(hres_active=True, **kw)
+        assert xhc.workspace_size(dd, 0) == 0, kw
+        assert xhc.validate(dd, a, xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_UNSUPPORTED, kw
+    bad = desc16()
+    bad.hres_active = 2
+    assert xhc.validate(bad, a, xhc.XHC_PHASE_FWD) == xhc.XHC_ERR_UNSUPPORTED
+    # the carried partials sum every stream: no chain
+    a, keep = good_fwd(d, inplace=False)
+    c = good_chain()
+    # (no workspace: a call that passes every check stops at XHC_ERR_WORKSPACE)
+    assert chain_call(d, a, c) == xhc.XHC_ERR_UNSUPPORTED
+    dn = desc16()
+    assert chain_call(dn, a, c) == xhc.XHC_ERR_WORKSPACE
+    c.desc_next = ctypes.pointer(desc16(hres_active=True))
+    assert chain_call(dn, a, c) == xhc.XHC_ERR_UNSUPPORTED

@@ -213,23 +213,47 @@ def test_fwdbwd4096_gs_sampled():
 
 
 @pytest.mark.timeout(1200)
-def test_stack48_teacher_forced():
+@pytest.mark.parametrize("chained", [True, False], ids=["chained", "two_pass"])
+def test_stack48_teacher_forced(chained):
+    """All 48 sublayers of the stack, in the launch configuration the
+    benchmark times (chained: every sublayer after the first starts from the
+    projection partials the previous write pass carried out, and every
+    sublayer but the last carries them on).  Each layer is checked on
+    sampled blocks, teacher-forced from the GPU's own state before it: the
+    active rows and h_in within tolerance, the other rows bitwise, and the
+    saved logits and RMS (for a chained layer these come from the carry)."""
     w = synth.WORKLOADS["stack48"]
-    say(f"[fullsize] stack48 S={w.S} C={w.C} layers={w.layers}")
+    say(f"[fullsize] stack48 S={w.S} C={w.C} layers={w.layers} chained={chained}")
     t_start = time.time()
+    T, N, C, P = w.T, w.N, w.C, w.P
     X = to_dev(synth.make_inputs(w, seed=0)["X"], True)
     blocks = [(0, 0), (0, 4096), (0, w.S - 16)]
     n = 16
-    h_in = torch.empty(w.T, w.C, dtype=torch.bfloat16, device="cuda")
-    for layer in range(w.layers):
+    h_in = torch.empty(T, C, dtype=torch.bfloat16, device="cuda")
+    z_save = torch.empty(T, P + 1, device="cuda")
+    desc = xhc.make_desc(w.B, w.S, C, N, w.k, 4, xhc.XHC_BF16)
+    carries = [torch.empty(xhc.carry_size(desc) // 4, device="cuda") for _ in range(2)] if chained else None
+
+    def params(layer):
         d = synth.make_inputs(w, seed=synth.stack_layer_seed(layer), state=False)
-        p = dev_params(d)
+        return d, dev_params(d)
+
+    cur = params(0)
+    for layer in range(w.layers):
+        d, p = cur
+        nxt = params(layer + 1) if layer + 1 < w.layers else None
         active = synth.active_streams(layer, w.N, w.k)
         before = {}
         for (_, s) in blocks:
             lo = max(0, s - LEAD)
             before[s] = to_host(X[lo:s + n])
-        xhc.forward(X, p["out"], p["W"], active, X, h_in, B=w.B, S=w.S, bias=p["bias"], **conv_kw(p, 4))
+        extra = {}
+        if chained:
+            extra = dict(carry_in=carries[layer % 2] if layer > 0 else None,
+                         W_next=None if nxt is None else nxt[1]["W"],
+                         carry_out=None if nxt is None else carries[(layer + 1) % 2])
+        xhc.forward(X, p["out"], None if (chained and layer > 0) else p["W"], active, X, h_in, B=w.B, S=w.S,
+                    bias=p["bias"], z_save=z_save, desc=desc, **conv_kw(p, 4), **extra)
         torch.cuda.synchronize()
         outh, hW = synth.as_float(d, "out"), synth.as_float(d, "W")
         convs = (d["w4"], d["w8"], d["w12"])
@@ -243,7 +267,11 @@ def test_stack48_teacher_forced():
             assert np.array_equal(got[:, inactive], before[s][k0:, inactive]), f"layer {layer}: pass-through"
             check_close(f"L{layer} X_new[s={s}]", got[:, active], ref["X_new"][k0:, active], 1e-2, 1e-2)
             check_close(f"L{layer} h_in[s={s}]", to_host(h_in[s:s + n]), ref["h_in"][k0:], 1e-2, 1e-2)
+            zs = to_host(z_save[s:s + n])
+            check_close(f"L{layer} z[s={s}]", zs[:, :P], ref["z"][k0:], 1e-3, 1e-3)
+            check_close(f"L{layer} r[s={s}]", zs[:, P], ref["r"][k0:], 1e-5, 1e-4)
         say(f" layer {layer} ok at {time.time() - t_start:.1f}s")
+        cur = nxt
 
 
 @pytest.mark.timeout(600)

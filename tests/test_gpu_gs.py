@@ -30,6 +30,13 @@ CASES = [
     ("unit_f32", W_("g", 2, 25, 48, 6, 2, 4, "f32", "fwd"), [2, 5], "unit", "leaning"),
     ("edge_c8_s1_f32", W_("g", 4, 1, 8, 16, 4, 4, "f32", "fwd"), [0, 1, 2, 3], "sigmoid", "leaning"),
     ("edge_c8_s5_bf16", W_("g", 3, 5, 8, 4, 3, 4, "bf16", "fwd"), [3, 1, 2], "sigmoid", "leaning"),
+    # near-collinear components (the regime the retrospective's section on
+    # Gram-Schmidt is about): each conv component is the output plus a
+    # little of its neighbours, cosine with the output about 0.99 / 0.999
+    ("collinear99_f32", W_("g", 2, 96, 1024, 16, 4, 4, "f32", "fwd"), [0, 5, 10, 15], "sigmoid", "cos0.99"),
+    ("collinear999_f32", W_("g", 2, 96, 1024, 16, 4, 4, "f32", "fwd"), [2, 3, 4, 5], "sigmoid", "cos0.999"),
+    ("collinear99_bf16", W_("g", 2, 96, 1024, 16, 4, 4, "bf16", "fwd"), [1, 6, 11, 14], "sigmoid", "cos0.99"),
+    ("collinear999_bf16", W_("g", 2, 96, 1024, 16, 4, 4, "bf16", "fwd"), [8, 9, 10, 11], "sigmoid", "cos0.999"),
 ]
 
 
@@ -48,7 +55,26 @@ def make_case(w, seed, grads, convs_kind):
     elif convs_kind == "zero":
         for key in ("w4", "w8", "w12"):
             d[key] = np.zeros_like(d[key])
+    elif convs_kind.startswith("cos"):
+        # tap 1 on the current token, the others N(0, e^2) with e such that
+        # for independent tokens cos(U_0, U_m) = 1 / sqrt(1 + e^2 (K - 1))
+        cos = float(convs_kind[3:])
+        r = np.random.default_rng(seed + 200)
+        for key, K in (("w4", 4), ("w8", 8), ("w12", 12)):
+            e = np.sqrt((1.0 / cos ** 2 - 1.0) / (K - 1))
+            v = (r.standard_normal((w.C, K)) * e).astype(np.float32)
+            v[:, K - 1] = 1.0
+            d[key] = v
     return d
+
+
+def component_cosines(h, w):
+    """Largest and median cosine over tokens between the output and each conv
+    component (the oracle's TFA of the case's inputs)."""
+    U = xo.tfa_components(h["out"], w.B, w.S, conv_tuple(h))
+    cs = [np.sum(U[:, 0] * U[:, m], axis=1)
+          / (np.linalg.norm(U[:, 0], axis=1) * np.linalg.norm(U[:, m], axis=1) + 1e-30) for m in range(1, 4)]
+    return [(float(np.median(c)), float(np.max(c))) for c in cs]
 
 
 def gate_code(gate):
@@ -81,6 +107,8 @@ def test_gs_forward_parity(name, w, active, gate, cv):
     dev = device_inputs(d, w.dtype == "bf16")
     ref = xo.forward(h["X"], h["out"], h["W"], h["bias"], active, conv_tuple(h), B=w.B, S=w.S, iters=w.iters,
                      eps=w.eps, gate_mode=gate, gram_schmidt_on=True, gs_eps=GS_EPS)
+    if cv.startswith("cos"):
+        say(f"  cos(out, conv_m) median/max: {component_cosines(h, w)}")
     Xn, h_in, z_save, _ = run_forward(w, dev, active, gate)
     atol, rtol = tol(w)
     Xn_h = to_host(Xn)
@@ -124,10 +152,31 @@ def test_gs_backward_parity(name, w, active, gate, cv):
     res = run(Xn, xact, z_save)
     check_close("dX", to_host(res["dX"]), g["dX"], atol, rtol)
     check_close("dout", to_host(res["dout"]), g["dout"], atol, rtol)
-    check_close("dW", to_host(res["dW"]), g["dW"], atol, rtol)
-    check_close("db", to_host(res["db"]), g["db"], atol, rtol)
-    for m, key in enumerate(["dw4", "dw8", "dw12"]):
-        check_close(key, to_host(res[key]), g["dconv"][m], atol, rtol)
+    if cv.startswith("cos") and w.dtype == "f32":
+        # The stated limit of the coefficient form with nearly collinear
+        # components in fp32: the triangle T comes from the fp32 Gram record,
+        # and its error (about eps_fp32 cond(g)) times <G_a, U_m> reaches the
+        # post logits' gradient, and through Ht and Sg the components'
+        # gradient, of every token.  dX and dout stay at 1e-4; the sums over
+        # tokens dW, db and the conv-weight gradients are held to 1e-3 of each
+        # column's largest magnitude (db: of its largest entry) instead of
+        # element by element (measured: about 1e-4 at cosine 0.999).
+        for key, ref in (("dW", g["dW"]), ("db", g["db"]), ("dw4", g["dconv"][0]), ("dw8", g["dconv"][1]),
+                         ("dw12", g["dconv"][2])):
+            got = to_host(res[key])
+            if ref.ndim == 1:                 # db: one sum per logit, held to the largest
+                scale = np.abs(ref).max(keepdims=True)
+                err = np.abs(got - ref).max(keepdims=True)
+            else:
+                scale = np.abs(ref).reshape(-1, ref.shape[-1]).max(axis=0)
+                err = np.abs(got - ref).reshape(-1, ref.shape[-1]).max(axis=0)
+            say(f"  {key}: max err / column scale = {np.max(err / scale):.3e}")
+            assert (err <= 1e-3 * scale).all(), key
+    else:
+        check_close("dW", to_host(res["dW"]), g["dW"], atol, rtol)
+        check_close("db", to_host(res["db"]), g["db"], atol, rtol)
+        for m, key in enumerate(["dw4", "dw8", "dw12"]):
+            check_close(key, to_host(res[key]), g["dconv"][m], atol, rtol)
     # recomputed coefficients give the same gradients; a rerun is bitwise identical
     res2 = run(dev["X"], None, None)
     for key in res:

@@ -48,6 +48,17 @@ def tol(w):
     return (1e-4, 1e-4) if w.dtype == "f32" else (1e-2, 1e-2)
 
 
+def tol_logits(w):
+    """Tolerance of the intermediates (logits z, scores rho, and the score
+    slack of check_choice): the fp32 path sums in fp32 throughout, the bf16
+    one rounds its inputs to bf16 but still accumulates in fp32."""
+    return (1e-4, 1e-4) if w.dtype == "f32" else (1e-3, 1e-3)
+
+
+def slack(w):
+    return (2e-4, 1e-4) if w.dtype == "f32" else (2e-3, 1e-3)
+
+
 def inputs(w, seed, grads):
     d = synth.make_inputs(w, seed=seed, grads=grads)
     d.update(synth.make_router(w, seed))
@@ -117,11 +128,11 @@ def compare_forward(w, h, fixed, Xn, h_in, z_save, idx, ref):
     check_close("h_in", to_host(h_in), ref["h_in"], atol, rtol)
     zs = z_save.cpu().numpy().astype(np.float64)
     P, k, R = w.P, w.k, w.route
-    check_close("z", zs[:, :P], ref["z"], 1e-3, 1e-3)
+    check_close("z", zs[:, :P], ref["z"], *tol_logits(w))
     check_close("mean", zs[:, P + 1], ref["mu"], 1e-5, 1e-4)
     check_close("sd", zs[:, P + 2], ref["sd"], 1e-5, 1e-4)
     rec = zs[:, P + 3:P + 3 + 3 * R].reshape(T, R, 3)
-    check_close("rho[routed]", rec[:, :, 0], np.take_along_axis(ref["rho"], idx[:, k - R:], axis=1), 2e-3, 1e-3)
+    check_close("rho[routed]", rec[:, :, 0], np.take_along_axis(ref["rho"], idx[:, k - R:], axis=1), *slack(w))
 
 
 @pytest.mark.parametrize("name,w,fixed", CASES, ids=[c[0] for c in CASES])
@@ -134,7 +145,32 @@ def test_route_forward_parity(name, w, fixed):
     Xn, h_in, z_save, idx, _ = run_forward(w, dev, fixed)
     hk = host_kw(h, w, fixed)
     rt = xo.forward(*hk["args"], **hk["kw"])
-    differ = check_choice(rt["rho"], idx, fixed, w.route)
+    differ = check_choice(rt["rho"], idx, fixed, w.route, *slack(w))
+    say(f"  tokens whose choice differs from the exact one (near ties): {differ} of {w.T}")
+    assert differ <= max(1, w.T // 100)
+    ref = xo.forward(*hk["args"], **hk["kw"], route_idx=idx)
+    compare_forward(w, h, fixed, Xn, h_in, z_save, idx, ref)
+
+
+@pytest.mark.parametrize("case", [0, 1], ids=["tiny_f32", "ragged_bf16"])
+def test_route_offset_state(case):
+    # a state whose tokens have a mean far from zero next to their spread
+    # (X + 8): the router's LayerNorm subtracts a large mean, which a
+    # one-pass variance or an uncentred score sum would lose in fp32
+    name, w, fixed = CASES[case]
+    say(f"[route offset state] {name}")
+    d = inputs(w, 5, False)
+    if w.dtype == "bf16":
+        d["X"] = synth.bf16_bits(synth.bf16_to_f32(d["X"]) + np.float32(8.0))
+    else:
+        d["X"] = d["X"] + np.float32(8.0)
+    h = host_inputs(d)
+    dev = device_inputs(d, w.dtype == "bf16")
+    Xn, h_in, z_save, idx, _ = run_forward(w, dev, fixed)
+    hk = host_kw(h, w, fixed)
+    rt = xo.forward(*hk["args"], **hk["kw"])
+    assert np.abs(rt["mu"]).min() > 7.0
+    differ = check_choice(rt["rho"], idx, fixed, w.route, *slack(w))
     say(f"  tokens whose choice differs from the exact one (near ties): {differ} of {w.T}")
     assert differ <= max(1, w.T // 100)
     ref = xo.forward(*hk["args"], **hk["kw"], route_idx=idx)
@@ -349,7 +385,7 @@ def test_route_with_unit_gates():
     Xn, h_in, z_save, idx, _ = run_forward(w, dev, fixed, gate="unit")
     hk = host_kw(h, w, fixed, gate="unit")
     own = xo.forward(*hk["args"], **hk["kw"])
-    assert check_choice(own["rho"], idx, fixed, w.route) <= 1
+    assert check_choice(own["rho"], idx, fixed, w.route, *slack(w)) <= 1
     ref = xo.forward(*hk["args"], **hk["kw"], route_idx=idx)
     compare_forward(w, h, fixed, Xn, h_in, z_save, idx, ref)
     ridx_dev = torch.from_numpy(idx.astype(np.int32)).to(dev["X"].device)
