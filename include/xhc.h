@@ -63,7 +63,7 @@ typedef struct ihipStream_t* xhc_stream_t;   /* a hipStream_t */
 
 enum { XHC_F32 = 0, XHC_BF16 = 1 };
 enum { XHC_GATE_SIGMOID = 0, XHC_GATE_UNIT = 1 };
-enum { XHC_PHASE_FWD = 0, XHC_PHASE_BWD = 1 };
+enum { XHC_PHASE_FWD = 0, XHC_PHASE_BWD = 1, XHC_PHASE_PRE = 2, XHC_PHASE_POST = 3 };
 
 enum {
   XHC_OK = 0,
@@ -243,7 +243,8 @@ size_t xhc_workspace_size(const xhc_desc* desc, int phase);
  * invalid description.  Pure host code. */
 int32_t xhc_zsave_stride(const xhc_desc* desc);
 
-/* Checks desc and args (an xhc_fwd_args* or xhc_bwd_args* per phase):
+/* Checks desc and args (an xhc_fwd_args*, xhc_bwd_args*, xhc_pre_args* or
+ * xhc_post_args* for XHC_PHASE_FWD, _BWD, _PRE, _POST):
  * NULLs, shapes, indices, aliasing, alignment.  Pure host code, no HIP
  * call, usable without a GPU.  Returns XHC_OK or the first error found. */
 int xhc_validate(const xhc_desc* desc, const void* args, int phase);
@@ -320,6 +321,63 @@ size_t xhc_carry_size(const xhc_desc* desc);
 int xhc_forward_chain(const xhc_desc* desc, const xhc_fwd_args* args,
                       const xhc_chain_args* chain, void* workspace,
                       size_t workspace_bytes, xhc_stream_t stream);
+
+/* Split forward (source: the retrospective's section "把 N 调大以后，事情开始不
+ * 太对了": H_pre reads the sublayer's input, the sublayer F runs, H_post
+ * writes its output back -- in a model, out = F(h_in) exists only after the
+ * dense read).  xhc_forward_pre forms the coefficients and h_in;
+ * xhc_forward_post, given out, rewrites the k active rows in place.  The
+ * two calls in turn compute what xhc_forward computes in place (up to the
+ * order of fp32 sums), and the backward is xhc_backward (or its split form
+ * below) with the pre call's z_save.  Chained: the pre call of a sublayer
+ * whose next sublayer's weights W_next are given also forms that
+ * sublayer's projection partials over the rows this sublayer leaves
+ * untouched (they are read anyway), and the post call adds the rewritten
+ * rows' partials to the same carry; the next pre call starts from it
+ * (carry_in) instead of reading its state for the projection -- the
+ * dense-read correction of the retrospective's closing section, one state
+ * read per sublayer.  Not with a router or per-token lists, and hres_active
+ * not with a carry (XHC_ERR_UNSUPPORTED). */
+typedef struct {
+  const void* X;          /* [T,N,C] the state (read only)                     */
+  const void* W;          /* [N*C,P]; not read with carry_in                    */
+  const float* bias;      /* [P] or NULL (zero)                                 */
+  const int32_t* active;  /* HOST [k] distinct stream ids, as xhc_forward's     */
+  void* h_in;             /* [T,C] dense-read sublayer input                    */
+  float* z_save;          /* [T, xhc_zsave_stride(desc)] required: logits and r;
+                             xhc_forward_post and the backward read it          */
+  const void* carry_in;   /* NULL: project X here; else the carry that the
+                             previous sublayer's xhc_forward_post completed     */
+  const void* W_next;     /* NULL, or the next sublayer's W [N*C, P_next]       */
+  void* carry_out;        /* xhc_carry_size(next description) bytes iff W_next:
+                             receives the untouched rows' partials; may equal
+                             carry_in (consumed first)                          */
+  const xhc_desc* desc_next; /* HOST, the next sublayer's description, or NULL
+                             (the same); same B, S, C, N, dtype                 */
+  xhc_timer* timer;
+} xhc_pre_args;
+
+typedef struct {
+  void* X;                /* [T,N,C] the state the pre call read; its k active
+                             rows are rewritten in place                        */
+  const void* out;        /* [T,C] the sublayer output F(h_in)                  */
+  const float *w4, *w8, *w12;  /* TFA conv weights, NULL iff ncomp == 1         */
+  const int32_t* active;  /* HOST [k], the pre call's                           */
+  const float* z_save;    /* the pre call's z_save                              */
+  void* xact_save;        /* [T,k,C] the old active rows (for the backward), or NULL */
+  const void* W_next;     /* NULL, or the pre call's W_next                     */
+  void* carry_out;        /* the pre call's carry_out (the new rows' partials
+                             are added to it) iff W_next                        */
+  const xhc_desc* desc_next; /* as in the pre call                              */
+  xhc_timer* timer;
+} xhc_post_args;
+
+/* Workspace: xhc_workspace_size(desc, XHC_PHASE_FWD) bytes for either call
+ * (its contents need not survive between them).  Errors as xhc_forward. */
+int xhc_forward_pre(const xhc_desc* desc, const xhc_pre_args* args, void* workspace, size_t workspace_bytes,
+                    xhc_stream_t stream);
+int xhc_forward_post(const xhc_desc* desc, const xhc_post_args* args, void* workspace, size_t workspace_bytes,
+                     xhc_stream_t stream);
 
 /* Message of an XHC_* code (static string). */
 const char* xhc_strerror(int code);

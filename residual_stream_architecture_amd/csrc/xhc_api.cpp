@@ -249,6 +249,76 @@ static int validate_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, 
   return XHC_OK;
 }
 
+// Split forward (xhc_forward_pre / xhc_forward_post): pn is the next
+// sublayer's plan (== p without desc_next).
+static int check_split_modes(const Plan& p, const Plan& pn, bool carried) {
+  if (p.pt || pn.pt) return XHC_ERR_UNSUPPORTED;
+  // the carried partials sum every stream of a channel block
+  if (carried && (p.hact || pn.hact)) return XHC_ERR_UNSUPPORTED;
+  if (pn.B != p.B || pn.S != p.S || pn.C != p.C || pn.N != p.N || pn.dtype != p.dtype) return XHC_ERR_SHAPE;
+  return XHC_OK;
+}
+
+static int validate_pre(const Plan& p, const Plan& pn, const xhc_pre_args* a) {
+  if (!a) return XHC_ERR_NULL;
+  int rc = check_split_modes(p, pn, a->carry_in || a->W_next);
+  if (rc) return rc;
+  if (!a->X || !a->h_in || !a->z_save || (!a->carry_in && !a->W)) return XHC_ERR_NULL;
+  if ((a->W_next == nullptr) != (a->carry_out == nullptr)) return XHC_ERR_NULL;
+  rc = check_active(p, a->active);
+  if (rc) return rc;
+  const void* ptrs[] = {a->X, a->W, a->bias, a->h_in, a->z_save, a->carry_in, a->W_next, a->carry_out};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return XHC_ERR_ALIGN;
+  const size_t T = p.T, e = p.esz;
+  const Span X = span(a->X, T * p.NC * e), hin = span(a->h_in, T * p.C * e);
+  const Span W = span(a->W, a->W && !a->carry_in ? (size_t)p.NC * p.P * e : 0);
+  const Span bias = span(a->bias, a->bias ? (size_t)p.P * 4 : 0);
+  const Span zs = span(a->z_save, T * p.zsv * 4);
+  const Span cin = span(a->carry_in, a->carry_in ? p.carry_bytes : 0);
+  const Span Wn = span(a->W_next, a->W_next ? (size_t)pn.NC * pn.P * e : 0);
+  const Span cout = span(a->carry_out, a->carry_out ? pn.carry_bytes : 0);
+  // carry_out may be carry_in itself: the coefficients consume it first
+  const Span cout_chk = (a->carry_out && a->carry_out == a->carry_in) ? Span{nullptr, 0} : cout;
+  std::vector<Span> outs = {hin, zs, cout_chk};
+  std::vector<Span> ins = {X, W, bias, cin, Wn};
+  if (any_overlap(outs, ins, Span{nullptr, 0}, Span{nullptr, 0})) return XHC_ERR_ALIAS;
+  if (a->carry_out && a->carry_out == a->carry_in) {
+    for (const Span& o : {hin, zs})
+      if (overlap(cout, o)) return XHC_ERR_ALIAS;
+    for (const Span& i : {X, W, bias, Wn})
+      if (overlap(cout, i)) return XHC_ERR_ALIAS;
+  }
+  return XHC_OK;
+}
+
+static int validate_post(const Plan& p, const Plan& pn, const xhc_post_args* a) {
+  if (!a) return XHC_ERR_NULL;
+  int rc = check_split_modes(p, pn, a->W_next != nullptr);
+  if (rc) return rc;
+  if (!a->X || !a->out || !a->z_save) return XHC_ERR_NULL;
+  if (p.nc == 4 && (!a->w4 || !a->w8 || !a->w12)) return XHC_ERR_NULL;
+  if (p.nc == 1 && (a->w4 || a->w8 || a->w12)) return XHC_ERR_UNSUPPORTED;
+  if ((a->W_next == nullptr) != (a->carry_out == nullptr)) return XHC_ERR_NULL;
+  rc = check_active(p, a->active);
+  if (rc) return rc;
+  const void* ptrs[] = {a->X, a->out, a->w4, a->w8, a->w12, a->z_save, a->xact_save, a->W_next, a->carry_out};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return XHC_ERR_ALIGN;
+  const size_t T = p.T, e = p.esz;
+  const Span X = span(a->X, T * p.NC * e), out = span(a->out, T * p.C * e);
+  const Span w4 = span(a->w4, a->w4 ? (size_t)p.C * 16 : 0), w8 = span(a->w8, a->w8 ? (size_t)p.C * 32 : 0),
+             w12 = span(a->w12, a->w12 ? (size_t)p.C * 48 : 0);
+  const Span zs = span(a->z_save, T * p.zsv * 4);
+  const Span xs = span(a->xact_save, a->xact_save ? T * p.k * p.C * e : 0);
+  const Span Wn = span(a->W_next, a->W_next ? (size_t)pn.NC * pn.P * e : 0);
+  const Span cout = span(a->carry_out, a->carry_out ? pn.carry_bytes : 0);
+  std::vector<Span> outs = {X, xs, cout};
+  std::vector<Span> ins = {out, w4, w8, w12, zs, Wn};
+  if (any_overlap(outs, ins, Span{nullptr, 0}, Span{nullptr, 0})) return XHC_ERR_ALIAS;
+  return XHC_OK;
+}
+
 static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
   if (!a) return XHC_ERR_NULL;
   if (!a->X || !a->out || !a->W || !a->dX_new || !a->dh_in || !a->dX || !a->dout || !a->dW) return XHC_ERR_NULL;
@@ -352,12 +422,30 @@ size_t xhc_workspace_size(const xhc_desc* desc, int phase) {
   return 0;
 }
 
+// The next sublayer's plan of a split call (== p without desc_next).
+static int next_plan(const xhc::Plan& p, const xhc_desc* desc_next, xhc::Plan* pn) {
+  *pn = p;
+  if (!desc_next) return XHC_OK;
+  const int rc = xhc::make_plan(desc_next, pn);
+  return rc ? XHC_ERR_SHAPE : XHC_OK;
+}
+
 int xhc_validate(const xhc_desc* desc, const void* args, int phase) {
   xhc::Plan p;
   int rc = xhc::make_plan(desc, &p);
   if (rc) return rc;
   if (phase == XHC_PHASE_FWD) return xhc::validate_fwd(p, static_cast<const xhc_fwd_args*>(args));
   if (phase == XHC_PHASE_BWD) return xhc::validate_bwd(p, static_cast<const xhc_bwd_args*>(args));
+  if (phase == XHC_PHASE_PRE || phase == XHC_PHASE_POST) {
+    if (!args) return XHC_ERR_NULL;
+    const xhc_desc* dn = phase == XHC_PHASE_PRE ? static_cast<const xhc_pre_args*>(args)->desc_next
+                                                : static_cast<const xhc_post_args*>(args)->desc_next;
+    xhc::Plan pn;
+    rc = next_plan(p, dn, &pn);
+    if (rc) return rc;
+    return phase == XHC_PHASE_PRE ? xhc::validate_pre(p, pn, static_cast<const xhc_pre_args*>(args))
+                                  : xhc::validate_post(p, pn, static_cast<const xhc_post_args*>(args));
+  }
   return XHC_ERR_UNSUPPORTED;
 }
 
@@ -419,6 +507,38 @@ int xhc_forward_chain(const xhc_desc* desc, const xhc_fwd_args* args, const xhc_
   if (rc) return rc;
   clear_pending_hip_error();
   return xhc::launch_forward_chain(p, pn, args, chain, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+int xhc_forward_pre(const xhc_desc* desc, const xhc_pre_args* args, void* workspace, size_t workspace_bytes,
+                    xhc_stream_t stream) {
+  xhc::Plan p, pn;
+  int rc = xhc::make_plan(desc, &p);
+  if (rc) return rc;
+  if (!args) return XHC_ERR_NULL;
+  rc = next_plan(p, args->desc_next, &pn);
+  if (rc) return rc;
+  rc = xhc::validate_pre(p, pn, args);
+  if (rc) return rc;
+  rc = check_ws(p, workspace, workspace_bytes, p.fwd_bytes);
+  if (rc) return rc;
+  clear_pending_hip_error();
+  return xhc::launch_forward_pre(p, pn, args, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+int xhc_forward_post(const xhc_desc* desc, const xhc_post_args* args, void* workspace, size_t workspace_bytes,
+                     xhc_stream_t stream) {
+  xhc::Plan p, pn;
+  int rc = xhc::make_plan(desc, &p);
+  if (rc) return rc;
+  if (!args) return XHC_ERR_NULL;
+  rc = next_plan(p, args->desc_next, &pn);
+  if (rc) return rc;
+  rc = xhc::validate_post(p, pn, args);
+  if (rc) return rc;
+  rc = check_ws(p, workspace, workspace_bytes, p.fwd_bytes);
+  if (rc) return rc;
+  clear_pending_hip_error();
+  return xhc::launch_forward_post(p, pn, args, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
 int xhc_backward(const xhc_desc* desc, const xhc_bwd_args* args, void* workspace, size_t workspace_bytes,

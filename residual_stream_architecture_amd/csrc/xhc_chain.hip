@@ -37,6 +37,17 @@
 //   carry[cb][t][0 .. 16*NT)  = partial x'.W' over the block's channels
 //   carry[cb][t][16*NT]       = partial sum of x'^2
 // which k_coef of the next sublayer sums over the ncb channel blocks.
+//
+// MODE splits the pass for a sublayer whose output does not exist yet when
+// its input is formed (the split forward: out = F(h_in) runs in between):
+//   MP_FULL  the pass above;
+//   MP_PRE   the dense read only: every row is read, h_in is written, and
+//            the carry gets the untouched rows' partials (their values as
+//            read are the next state's); no state is written;
+//   MP_POST  the sparse write only: the k active rows are read and
+//            rewritten (TFA, new rows, xact_save), and their new values'
+//            partials are added to the carry the PRE pass wrote.
+// proj = 0 skips the projection (no next sublayer: no carry).
 #include "xhc_device.h"
 #include "xhc_launch.h"
 
@@ -47,6 +58,7 @@ constexpr int MP_TOK = 16 * MP_WAVES;     // tokens per workgroup
 constexpr int MP_RPS = 4;                 // state rows per step
 constexpr int MP_WSLOT = MP_RPS * 6144;   // W' bytes per step (NT = 3)
 constexpr int CL_STRIDE = 52;             // floats per token of the LDS coefficient rows
+constexpr int MP_FULL = MIX_FULL, MP_PRE = MIX_PRE, MP_POST = MIX_POST;
 
 // `out` n positions back: the lane's token is r of a 16-token tile, `cur`
 // holds the tile's values and `halo` those of the 16 tokens before it.
@@ -69,13 +81,13 @@ __device__ inline V8<E> window_back(const V8<E>& cur, const V8<E>& halo) {
   return o;
 }
 
-template <typename E, int NT, int NCOMP, bool FAST>
+template <typename E, int NT, int NCOMP, bool FAST, int MODE>
 __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     const void* __restrict__ X, const void* __restrict__ out, const float* __restrict__ w4,
     const float* __restrict__ w8, const float* __restrict__ w12, const float* __restrict__ coef,
     const void* __restrict__ Wf, void* Xnew, void* __restrict__ hin, void* __restrict__ xact,
     float* __restrict__ carry, RowOrder ro, int T, int S, int C, int N_, int k_, int in_place, int cpw,
-    int nch, int nbatch, int ZST) {
+    int nch, int nbatch, int ZST, int proj) {
   const int N = FAST ? 16 : N_;
   const int k = FAST ? 4 : k_;
   constexpr int EB = E::bytes;
@@ -99,11 +111,12 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
   const int r = lane & 15, g = lane >> 4;
   const int tb = bt * MP_TOK, t0 = tb + 16 * wave, t = t0 + r;
   const int spos = (t < T ? t : 0) % S;                 // position in the sequence
-  const int nq = (N + MP_RPS - 1) / MP_RPS;             // steps per chunk
+  // steps per chunk (the POST pass visits the k active rows only: one step)
+  const int nq = MODE == MP_POST ? 1 : (N + MP_RPS - 1) / MP_RPS;
   // bf16 chunks hold two K-steps; with four steps per chunk the active rows'
   // second K-step (TFA, new rows, their projection) moves to the third step,
   // so that the arithmetic of the first step is split over two steps
-  const bool split = KS == 2 && nq == 4;
+  const bool split = MODE == MP_FULL && KS == 2 && nq == 4;
   const int c0 = cb * cpw, c1 = min(c0 + cpw, nch);
   const int nsteps = (c1 - c0) * nq;
   const int nks = (C + 31) >> 5;                        // K-steps of the packed W'
@@ -195,7 +208,9 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
       if (pc < MP_RPS * PPR) {
         const int j = pc / PPR, o = pc - j * PPR;
         const int slot = q * MP_RPS + j;
-        if (slot < N && o * 1024 < valid_bytes) {
+        // PRE projects the untouched rows only, POST the active ones only
+        const bool wanted = MODE == MP_FULL || (MODE == MP_PRE ? slot >= k : slot < k);
+        if (proj && wanted && slot < N && o * 1024 < valid_bytes) {
           const unsigned char* src = static_cast<const unsigned char*>(Wf) +
                                      ((size_t)row_of(ro, slot) * nks + ksb) * NT * FB + o * 1024 + lane * 16;
           if (split && q == 0 && j < k && o >= PPR / 2)   // K-step 1 of an active row
@@ -220,6 +235,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
   auto dma_rows = [&](int c, int q) {
 #pragma unroll
     for (int j = 0; j < MP_RPS; ++j) {
+      if (MODE == MP_POST && j >= k) continue;       // untouched rows: not read by the POST pass
       const uint32_t soff = (uint32_t)row_of(ro, q * MP_RPS + j) * rowb;    // rows past N repeat a valid row
 #pragma unroll
       for (int u = 0; u < KS; ++u) {
@@ -268,9 +284,13 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
 
   // one row of the step: h_in from the old values, sum of squares and the
   // projection from `xv` (the row of the new state), K-step u
-  auto row_work = [&](const unsigned char* wfr, int u, int c, float hp, const V8<E>& xold, const V8<E>& xv) {
+  auto row_work = [&](const unsigned char* wfr, int u, int c, float hp, const V8<E>& xold, const V8<E>& xv,
+                      bool project) {
+    if constexpr (MODE != MP_POST) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) hacc[u][e] = fmaf(hp, xold.f(e), hacc[u][e]);
+      for (int e = 0; e < 8; ++e) hacc[u][e] = fmaf(hp, xold.f(e), hacc[u][e]);
+    }
+    if (!project) return;
     if constexpr (EB == 2) {
       // bf16 pairs: the products are exact in fp32
 #pragma unroll
@@ -285,7 +305,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
         ss = fmaf(y, y, ss);
       }
     }
-    if (c * KS + u < nks) {
+    if (proj && c * KS + u < nks) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const V8<E> wv = *reinterpret_cast<const V8<E>*>(wfr + n * FB + lane * 8 * EB);
@@ -369,7 +389,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
         const int row = row_of(ro, a);
         bstore<E, 8>(nv, rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
         if (xact) bstore<E, 8>(xs[a], rxs, lane_off(c, u, xsb), (uint32_t)a * rowb);
-        row_work(wact + a * wstride, u, c, co[row], xs[a], nv);
+        row_work(wact + a * wstride, u, c, co[row], xs[a], nv, true);
       }
     }
   };
@@ -384,7 +404,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     const int c = c0 + cq;
     const int s = cq * nq + q;
     wait_vmcnt<0>();
-    if constexpr (FIRST && NCOMP == 4) {
+    if constexpr (FIRST && NCOMP == 4 && MODE != MP_PRE) {
       if (nq == 1) __syncthreads();     // one step per chunk: every wave is done with the last conv weights
       store_conv(c);
     }
@@ -397,11 +417,11 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     } else if (cq + 1 < c1 - c0) {
       w_dma(s + 1);
       dma_rows(c + 1, 0);
-      if constexpr (NCOMP == 4) load_conv(c + 1);
+      if constexpr (NCOMP == 4 && MODE != MP_PRE) load_conv(c + 1);
     }
     const unsigned char* wsl = wst[s & 1];
 
-    if constexpr (FIRST) {
+    if constexpr (FIRST && MODE != MP_PRE) {
       if (split) {
         V8<E> xs0[4];
 #pragma unroll
@@ -423,21 +443,23 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
         if (cq + 1 < c1 - c0) load_out(c + 1);
       }
     }
-    // the step's other rows (untouched by the update)
+    // the step's other rows (untouched by the update); the PRE pass reads the
+    // active rows here too, for h_in only
 #pragma unroll
     for (int j = 0; j < MP_RPS; ++j) {
       const int slot = q * MP_RPS + j;
-      if (slot < N && (!FIRST || j >= k)) {
+      const bool untouched = !FIRST || j >= k;
+      if (MODE != MP_POST && slot < N && (untouched || MODE == MP_PRE)) {
         const int row = row_of(ro, slot);
         const float hp = co[row];
 #pragma unroll
         for (int u = 0; u < KS; ++u) {
-          row_work(wsl + j * SLOTB + u * NT * FB, u, c, hp, x[j][u], x[j][u]);
-          if (!in_place) bstore<E, 8>(x[j][u], rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
+          row_work(wsl + j * SLOTB + u * NT * FB, u, c, hp, x[j][u], x[j][u], untouched);
+          if (MODE == MP_FULL && !in_place) bstore<E, 8>(x[j][u], rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
         }
       }
     }
-    if (q + 1 == nq) {
+    if (MODE != MP_POST && q + 1 == nq) {
 #pragma unroll
       for (int u = 0; u < KS; ++u) {
         bstore<E, 8>(V8<E>::from_float(hacc[u]), rh, lane_off(c, u, rowb), 0);
@@ -447,11 +469,11 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     }
   };
 
-  if constexpr (NCOMP == 4) load_conv(c0);
+  if constexpr (NCOMP == 4 && MODE != MP_PRE) load_conv(c0);
   if (c1 > c0) {
     w_dma(0);
     dma_rows(c0, 0);
-    load_out(c0);
+    if constexpr (MODE != MP_PRE) load_out(c0);
   }
   for (int cq = 0; cq < c1 - c0; ++cq) {
     step(std::true_type{}, cq, 0);
@@ -461,11 +483,21 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
 
   ss += shfl_xor(ss, 16);
   ss += shfl_xor(ss, 32);
-  if (t < T) {
+  if (proj && t < T) {
     float* zp = carry + ((size_t)cb * T + t) * ZST;
+    if constexpr (MODE == MP_POST) {
+      // the PRE pass's partials (untouched rows) plus the new rows'
 #pragma unroll
-    for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(zp + 16 * n + 4 * g) = acc[n];
-    if (g == 0) zp[16 * NT] = ss;
+      for (int n = 0; n < NT; ++n) {
+        f32x4* dst = reinterpret_cast<f32x4*>(zp + 16 * n + 4 * g);
+        *dst = *dst + acc[n];
+      }
+      if (g == 0) zp[16 * NT] += ss;
+    } else {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(zp + 16 * n + 4 * g) = acc[n];
+      if (g == 0) zp[16 * NT] = ss;
+    }
   }
 }
 
@@ -473,38 +505,48 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
 // launcher
 // ---------------------------------------------------------------------------
 // pn: the next sublayer's plan; its tile count and partial-record stride
-// shape the projection and the carry.
+// shape the projection and the carry.  mode: MP_FULL, MP_PRE or MP_POST;
+// Wf == NULL: no projection (and no carry).
 template <typename E>
-static void launch_mixproj_e(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const float* coef,
+static void launch_mixproj_e(const Plan& p, const Plan& pn, int mode, const MixArgs& m, const float* coef,
                              const void* Wf, float* carry, hipStream_t st) {
   RowOrder ro{0};
   {
     bool used[16] = {false};
     int order[16], n = 0;
-    for (int b = 0; b < p.k; ++b) { order[n++] = a->active[b]; used[a->active[b]] = true; }
+    for (int b = 0; b < p.k; ++b) { order[n++] = m.active[b]; used[m.active[b]] = true; }
     for (int i = 0; i < p.N; ++i)
       if (!used[i]) order[n++] = i;
     for (; n < 16; ++n) order[n] = order[0];
     for (int i = 0; i < 16; ++i) ro.bits |= (uint64_t)order[i] << (4 * i);
   }
-  const int in_place = a->X_new == a->X;
+  const int in_place = m.X_new == m.X;
+  const int proj = Wf != nullptr;
+  const int NT = proj ? pn.NT : 1;
   const dim3 grid(p.mp_ncb * p.mp_nbatch);
-#define XHC_MP(NT, NC)                                                                                            \
-  k_mixproj<E, NT, NC, false><<<grid, 64 * MP_WAVES, 0, st>>>(a->X, a->out, a->w4, a->w8, a->w12, coef, Wf, a->X_new,    \
-                                                       a->h_in, a->xact_save, carry, ro, p.T, p.S, p.C, p.N, p.k, \
-                                                       in_place, p.mp_cpw, p.mp_nch, p.mp_nbatch, pn.ZST)
-  if (p.nc == 4) {
-    if (pn.NT == 3) XHC_MP(3, 4); else if (pn.NT == 2) XHC_MP(2, 4); else XHC_MP(1, 4);
+#define XHC_MP(NTV, NC, MODE)                                                                                     \
+  k_mixproj<E, NTV, NC, false, MODE><<<grid, 64 * MP_WAVES, 0, st>>>(                                             \
+      m.X, m.out, m.w4, m.w8, m.w12, coef, Wf, m.X_new, m.h_in, m.xact_save, carry, ro, p.T, p.S, p.C, p.N, p.k,   \
+      in_place, p.mp_cpw, p.mp_nch, p.mp_nbatch, pn.ZST, proj)
+#define XHC_MP_NT(NC, MODE)                                                                                       \
+  do {                                                                                                           \
+    if (NT == 3) XHC_MP(3, NC, MODE); else if (NT == 2) XHC_MP(2, NC, MODE); else XHC_MP(1, NC, MODE);           \
+  } while (0)
+  if (mode == MP_PRE) {
+    XHC_MP_NT(1, MP_PRE);                  // no write-back: the component count does not matter
+  } else if (mode == MP_POST) {
+    if (p.nc == 4) XHC_MP_NT(4, MP_POST); else XHC_MP_NT(1, MP_POST);
   } else {
-    if (pn.NT == 3) XHC_MP(3, 1); else if (pn.NT == 2) XHC_MP(2, 1); else XHC_MP(1, 1);
+    if (p.nc == 4) XHC_MP_NT(4, MP_FULL); else XHC_MP_NT(1, MP_FULL);
   }
+#undef XHC_MP_NT
 #undef XHC_MP
 }
 
-void launch_mixproj(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const float* coef, const void* Wf,
+void launch_mixproj(const Plan& p, const Plan& pn, int mode, const MixArgs& m, const float* coef, const void* Wf,
                     float* carry, hipStream_t st) {
-  if (p.dtype == XHC_BF16) launch_mixproj_e<BF16>(p, pn, a, coef, Wf, carry, st);
-  else launch_mixproj_e<F32>(p, pn, a, coef, Wf, carry, st);
+  if (p.dtype == XHC_BF16) launch_mixproj_e<BF16>(p, pn, mode, m, coef, Wf, carry, st);
+  else launch_mixproj_e<F32>(p, pn, mode, m, coef, Wf, carry, st);
 }
 
 }  // namespace xhc

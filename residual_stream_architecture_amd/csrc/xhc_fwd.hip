@@ -808,7 +808,8 @@ static int forward_impl(const Plan& p, const Plan& pn, const xhc_fwd_args* a, co
     // write pass with its projection
     launch_pack_wt<R>(pn, ch->W_next, Wt, st, tm);
     TimedLaunch tl(tm, KID_MIXPROJ, st);
-    launch_mixproj(p, pn, a, coef, Wt, static_cast<float*>(ch->carry_out), st);
+    const MixArgs m{a->X, a->out, a->w4, a->w8, a->w12, a->X_new, a->h_in, a->xact_save, a->active};
+    launch_mixproj(p, pn, MIX_FULL, m, coef, Wt, static_cast<float*>(ch->carry_out), st);
     return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
   }
   {
@@ -837,6 +838,84 @@ static int forward_impl(const Plan& p, const Plan& pn, const xhc_fwd_args* a, co
 #undef XHC_MIX
   }
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
+}
+
+// Split forward, first call: coefficients (from the state, or from the
+// previous sublayer's carried partials) and the dense read h_in; with a next
+// sublayer, also its projection partials over the rows this sublayer's
+// write leaves untouched.
+template <typename E, typename R>
+static int forward_pre_impl(const Plan& p, const Plan& pn, const xhc_pre_args* a, char* ws, hipStream_t st) {
+  xhc_timer* tm = a->timer;
+  void* Wt = ws + p.off_wt;
+  float* zpart = reinterpret_cast<float*>(ws + p.off_zpart);
+  float* coef = reinterpret_cast<float*>(ws + p.off_coef);
+  const float* carry_in = static_cast<const float*>(a->carry_in);
+  if (!carry_in) {
+    launch_pack_wt<R>(p, a->W, Wt, st, tm);
+    launch_proj<E>(p, stream_rows(p, a->X, nullptr, a->active), Wt, zpart, st, tm);
+  }
+  {
+    TimedLaunch tl(tm, KID_COEF, st);
+    const float* zp = carry_in ? carry_in : zpart;
+    const int sk = carry_in ? p.mp_ncb : p.SK;
+    k_coef<false, false><<<(p.T + 15) / 16, 256, 0, st>>>(zp, sk, p.ZST, p.NT * 16, nullptr, a->bias, coef, a->z_save,
+                                                          p.zsv, p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps,
+                                                          p.iters, p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f,
+                                                          RouteArgs{}, hres_active(p, a->active));
+  }
+  if (a->W_next) launch_pack_wt<R>(pn, a->W_next, Wt, st, tm);
+  {
+    TimedLaunch tl(tm, KID_MIXPROJ, st);
+    const MixArgs m{a->X, nullptr, nullptr, nullptr, nullptr, const_cast<void*>(a->X), a->h_in, nullptr, a->active};
+    launch_mixproj(p, pn, MIX_PRE, m, coef, a->W_next ? Wt : nullptr, static_cast<float*>(a->carry_out), st);
+  }
+  return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
+}
+
+// Split forward, second call: the coefficients again from the first call's
+// z_save, then the sparse write (in place); with a next sublayer, the new
+// rows' projection partials are added to the first call's carry.
+template <typename E, typename R>
+static int forward_post_impl(const Plan& p, const Plan& pn, const xhc_post_args* a, char* ws, hipStream_t st) {
+  xhc_timer* tm = a->timer;
+  void* Wt = ws + p.off_wt;
+  float* coef = reinterpret_cast<float*>(ws + p.off_coef);
+  float* gram = reinterpret_cast<float*>(ws + p.off_gram);
+  if (p.gs) {
+    TimedLaunch tl(tm, KID_GRAM, st);
+    launch_gram(p, a->out, a->w4, a->w8, a->w12, gram, st);
+  }
+  {
+    TimedLaunch tl(tm, KID_COEF, st);
+#define XHC_COEF_Z(GS)                                                                                          \
+  k_coef<GS, false><<<(p.T + 15) / 16, 256, 0, st>>>(nullptr, 0, p.ZST, p.NT * 16, a->z_save, nullptr, coef,       \
+                                                     nullptr, p.zsv, p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, \
+                                                     p.eps, p.iters, p.gate == XHC_GATE_UNIT, GS ? gram : nullptr, \
+                                                     GS ? p.b1_cblocks : 0, GS ? p.gs_ceps : 0.f, RouteArgs{},     \
+                                                     HresActive{})
+    if (p.gs) XHC_COEF_Z(true); else XHC_COEF_Z(false);
+#undef XHC_COEF_Z
+  }
+  if (a->W_next) launch_pack_wt<R>(pn, a->W_next, Wt, st, tm);
+  {
+    TimedLaunch tl(tm, KID_MIXPROJ, st);
+    const MixArgs m{a->X, a->out, a->w4, a->w8, a->w12, a->X, nullptr, a->xact_save, a->active};
+    launch_mixproj(p, pn, MIX_POST, m, coef, a->W_next ? Wt : nullptr, static_cast<float*>(a->carry_out), st);
+  }
+  return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
+}
+
+int launch_forward_pre(const Plan& p, const Plan& pn, const xhc_pre_args* a, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  if (p.dtype == XHC_BF16) return forward_pre_impl<BF16, uint16_t>(p, pn, a, w, st);
+  return forward_pre_impl<F32, float>(p, pn, a, w, st);
+}
+
+int launch_forward_post(const Plan& p, const Plan& pn, const xhc_post_args* a, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  if (p.dtype == XHC_BF16) return forward_post_impl<BF16, uint16_t>(p, pn, a, w, st);
+  return forward_post_impl<F32, float>(p, pn, a, w, st);
 }
 
 int launch_forward(const Plan& p, const xhc_fwd_args* a, void* ws, hipStream_t st) {

@@ -77,8 +77,23 @@ int launch_forward(const Plan& p, const xhc_fwd_args* a, void* ws, hipStream_t s
 // pn: the next sublayer's plan (its P, tile count and carry layout).
 int launch_forward_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const xhc_chain_args* c, void* ws,
                          hipStream_t st);
-void launch_mixproj(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const float* coef, const void* Wf,
+// The buffers of the fused write pass (xhc_chain.hip).
+struct MixArgs {
+  const void* X;
+  const void* out;
+  const float *w4, *w8, *w12;
+  void* X_new;
+  void* h_in;
+  void* xact_save;
+  const int32_t* active;
+};
+// Passes of k_mixproj: the whole write pass, its dense read only, its sparse write only.
+enum { MIX_FULL = 0, MIX_PRE = 1, MIX_POST = 2 };
+void launch_mixproj(const Plan& p, const Plan& pn, int mode, const MixArgs& m, const float* coef, const void* Wf,
                     float* carry, hipStream_t st);
+// Split forward (xhc_forward_pre / xhc_forward_post).
+int launch_forward_pre(const Plan& p, const Plan& pn, const xhc_pre_args* a, void* ws, hipStream_t st);
+int launch_forward_post(const Plan& p, const Plan& pn, const xhc_post_args* a, void* ws, hipStream_t st);
 int launch_coef_bwd(const Plan& p, const void* X, const void* xact, const int32_t* active, const void* W,
                     const float* bias, const float* z_save, void* ws, float* coef, float* z_out,
                     hipStream_t st, xhc_timer* tm, const void* W_route, const float* b_route,

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_PKG, "libxhc.so")
 
 XHC_F32, XHC_BF16 = 0, 1
 XHC_GATE_SIGMOID, XHC_GATE_UNIT = 0, 1
-XHC_PHASE_FWD, XHC_PHASE_BWD = 0, 1
+XHC_PHASE_FWD, XHC_PHASE_BWD, XHC_PHASE_PRE, XHC_PHASE_POST = 0, 1, 2, 3
 ERRORS = {0: "XHC_OK", -1: "XHC_ERR_NULL", -2: "XHC_ERR_SHAPE", -3: "XHC_ERR_INDEX",
           -4: "XHC_ERR_ALIAS", -5: "XHC_ERR_ALIGN", -6: "XHC_ERR_UNSUPPORTED",
           -7: "XHC_ERR_WORKSPACE", -8: "XHC_ERR_HIP", -9: "XHC_ERR_SCRATCH"}
@@ -56,6 +56,18 @@ class xhc_chain_args(ctypes.Structure):
                 ("desc_next", ctypes.POINTER(xhc_desc))]
 
 
+class xhc_pre_args(ctypes.Structure):
+    _fields_ = [("X", _vp), ("W", _vp), ("bias", _vp), ("active", ctypes.POINTER(ctypes.c_int32)),
+                ("h_in", _vp), ("z_save", _vp), ("carry_in", _vp), ("W_next", _vp), ("carry_out", _vp),
+                ("desc_next", ctypes.POINTER(xhc_desc)), ("timer", _vp)]
+
+
+class xhc_post_args(ctypes.Structure):
+    _fields_ = [("X", _vp), ("out", _vp), ("w4", _vp), ("w8", _vp), ("w12", _vp),
+                ("active", ctypes.POINTER(ctypes.c_int32)), ("z_save", _vp), ("xact_save", _vp),
+                ("W_next", _vp), ("carry_out", _vp), ("desc_next", ctypes.POINTER(xhc_desc)), ("timer", _vp)]
+
+
 class XhcError(RuntimeError):
     def __init__(self, code, what):
         super().__init__(f"{what}: {ERRORS.get(code, code)} ({lib.xhc_strerror(code).decode()})")
@@ -87,6 +99,12 @@ def _load():
     L.xhc_forward_chain.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_fwd_args),
                                     ctypes.POINTER(xhc_chain_args), _vp, ctypes.c_size_t, _vp]
     L.xhc_forward_chain.restype = ctypes.c_int
+    L.xhc_forward_pre.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_pre_args), _vp, ctypes.c_size_t,
+                                  _vp]
+    L.xhc_forward_pre.restype = ctypes.c_int
+    L.xhc_forward_post.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_post_args), _vp, ctypes.c_size_t,
+                                   _vp]
+    L.xhc_forward_post.restype = ctypes.c_int
     L.xhc_backward.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_bwd_args), _vp, ctypes.c_size_t, _vp]
     L.xhc_backward.restype = ctypes.c_int
     L.xhc_strerror.argtypes = [ctypes.c_int]
@@ -247,6 +265,42 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
                                ws.numel(), _stream_handle(stream))
     if rc:
         raise XhcError(rc, "xhc_forward_chain")
+
+
+def _desc_ptr(d):
+    return None if d is None else ctypes.pointer(d)
+
+
+def forward_pre(X, W, active, h_in, z_save, *, desc, bias=None, carry_in=None, W_next=None, carry_out=None,
+                desc_next=None, workspace=None, stream=None, timer=None):
+    """xhc_forward_pre: coefficients and the dense read h_in of the state X
+    (read only), z_save for the post call; with W_next/carry_out the next
+    sublayer's projection partials over this sublayer's untouched rows."""
+    act = _active_array(active)
+    args = xhc_pre_args(_ptr(X), _ptr(W), _ptr(bias), ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)),
+                        _ptr(h_in), _ptr(z_save), _ptr(carry_in), _ptr(W_next), _ptr(carry_out),
+                        _desc_ptr(desc_next), None if timer is None else timer.handle)
+    ws, need = _workspace(desc, XHC_PHASE_FWD, X.device, workspace, stream)
+    rc = lib.xhc_forward_pre(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
+                             _stream_handle(stream))
+    if rc:
+        raise XhcError(rc, "xhc_forward_pre")
+
+
+def forward_post(X, out, active, z_save, *, desc, w4=None, w8=None, w12=None, xact_save=None, W_next=None,
+                 carry_out=None, desc_next=None, workspace=None, stream=None, timer=None):
+    """xhc_forward_post: the sparse write of the pre call's sublayer, in place
+    in X, from its output `out` and the pre call's z_save; with W_next the
+    new rows' projection partials are added to the pre call's carry_out."""
+    act = _active_array(active)
+    args = xhc_post_args(_ptr(X), _ptr(out), _ptr(w4), _ptr(w8), _ptr(w12),
+                         ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(z_save), _ptr(xact_save),
+                         _ptr(W_next), _ptr(carry_out), _desc_ptr(desc_next), None if timer is None else timer.handle)
+    ws, need = _workspace(desc, XHC_PHASE_FWD, X.device, workspace, stream)
+    rc = lib.xhc_forward_post(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
+                              _stream_handle(stream))
+    if rc:
+        raise XhcError(rc, "xhc_forward_post")
 
 
 def forward_noalloc(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None, bias=None,

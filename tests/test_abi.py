@@ -428,3 +428,80 @@ def test_hres_active_descriptions():
     assert chain_call(dn, a, c) == xhc.XHC_ERR_WORKSPACE
     c.desc_next = ctypes.pointer(desc16(hres_active=True))
     assert chain_call(dn, a, c) == xhc.XHC_ERR_UNSUPPORTED
+
+
+def good_pre(desc, chained=False):
+    act = (ctypes.c_int32 * desc.k)(*range(desc.k))
+    a = xhc.xhc_pre_args(X=fake(1), W=fake(2), bias=None, active=ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)),
+                         h_in=fake(3), z_save=fake(4), carry_in=fake(5) if chained else None,
+                         W_next=fake(6) if chained else None, carry_out=fake(7) if chained else None)
+    return a, act
+
+
+def good_post(desc, chained=False):
+    act = (ctypes.c_int32 * desc.k)(*range(desc.k))
+    c4 = desc.ncomp == 4
+    a = xhc.xhc_post_args(X=fake(1), out=fake(8), w4=fake(9) if c4 else None, w8=fake(10) if c4 else None,
+                          w12=fake(11) if c4 else None, active=ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)),
+                          z_save=fake(4), xact_save=fake(12), W_next=fake(6) if chained else None,
+                          carry_out=fake(7) if chained else None)
+    return a, act
+
+
+def test_split_forward_validation():
+    d = desc16()
+    PRE, POST = xhc.XHC_PHASE_PRE, xhc.XHC_PHASE_POST
+    for chained in (False, True):
+        a, keep = good_pre(d, chained)
+        assert xhc.validate(d, a, PRE) == xhc.XHC_OK, chained
+        b, keep2 = good_post(d, chained)
+        assert xhc.validate(d, b, POST) == xhc.XHC_OK, chained
+    # z_save is required by both calls; W only without carry_in
+    a, keep = good_pre(d)
+    a.z_save = None
+    assert xhc.validate(d, a, PRE) == xhc.XHC_ERR_NULL
+    a, keep = good_pre(d)
+    a.W = None
+    assert xhc.validate(d, a, PRE) == xhc.XHC_ERR_NULL
+    a, keep = good_pre(d, chained=True)
+    a.W = None
+    assert xhc.validate(d, a, PRE) == xhc.XHC_OK
+    a.carry_out = None                                   # W_next without carry_out
+    assert xhc.validate(d, a, PRE) == xhc.XHC_ERR_NULL
+    a, keep = good_pre(d, chained=True)
+    a.carry_out = a.carry_in                             # the coefficients consume carry_in first
+    assert xhc.validate(d, a, PRE) == xhc.XHC_OK
+    a.carry_out = a.h_in
+    assert xhc.validate(d, a, PRE) == xhc.XHC_ERR_ALIAS
+    a, keep = good_pre(d)
+    a.h_in = a.X
+    assert xhc.validate(d, a, PRE) == xhc.XHC_ERR_ALIAS
+    b, keep = good_post(d)
+    b.z_save = None
+    assert xhc.validate(d, b, POST) == xhc.XHC_ERR_NULL
+    b, keep = good_post(d)
+    b.out = b.X
+    assert xhc.validate(d, b, POST) == xhc.XHC_ERR_ALIAS
+    b, keep = good_post(d, chained=True)
+    b.carry_out = b.z_save
+    assert xhc.validate(d, b, POST) == xhc.XHC_ERR_ALIAS
+    b, keep = good_post(d)
+    b.w8 = None
+    assert xhc.validate(d, b, POST) == xhc.XHC_ERR_NULL
+    # not with a router or given lists; hres_active only without a carry
+    assert xhc.validate(desc16(route=2), good_pre(desc16(route=2))[0], PRE) == xhc.XHC_ERR_UNSUPPORTED
+    dh = desc16(hres_active=True)
+    assert xhc.validate(dh, good_pre(dh)[0], PRE) == xhc.XHC_OK
+    assert xhc.validate(dh, good_pre(dh, chained=True)[0], PRE) == xhc.XHC_ERR_UNSUPPORTED
+    assert xhc.validate(dh, good_post(dh, chained=True)[0], POST) == xhc.XHC_ERR_UNSUPPORTED
+    # the next description must describe the same state
+    a, keep = good_pre(d, chained=True)
+    a.desc_next = ctypes.pointer(desc16(C=128))
+    assert xhc.validate(d, a, PRE) == xhc.XHC_ERR_SHAPE
+    a.desc_next = ctypes.pointer(desc16(ncomp=1))
+    assert xhc.validate(d, a, PRE) == xhc.XHC_OK
+    # calls stop before any launch without a workspace
+    a, keep = good_pre(d)
+    assert xhc.lib.xhc_forward_pre(ctypes.byref(d), ctypes.byref(a), None, 0, None) == xhc.XHC_ERR_WORKSPACE
+    b, keep = good_post(d)
+    assert xhc.lib.xhc_forward_post(ctypes.byref(d), ctypes.byref(b), None, 0, None) == xhc.XHC_ERR_WORKSPACE
