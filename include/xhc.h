@@ -63,7 +63,8 @@ typedef struct ihipStream_t* xhc_stream_t;   /* a hipStream_t */
 
 enum { XHC_F32 = 0, XHC_BF16 = 1 };
 enum { XHC_GATE_SIGMOID = 0, XHC_GATE_UNIT = 1 };
-enum { XHC_PHASE_FWD = 0, XHC_PHASE_BWD = 1, XHC_PHASE_PRE = 2, XHC_PHASE_POST = 3 };
+enum { XHC_PHASE_FWD = 0, XHC_PHASE_BWD = 1, XHC_PHASE_PRE = 2, XHC_PHASE_POST = 3,
+       XHC_PHASE_BWD_POST = 4, XHC_PHASE_BWD_PRE = 5 };
 
 enum {
   XHC_OK = 0,
@@ -232,8 +233,9 @@ typedef struct {
                           router's scores when z_save is NULL                 */
 } xhc_bwd_args;
 
-/* Bytes of device workspace the call needs (phase XHC_PHASE_FWD or
- * XHC_PHASE_BWD); 0 for an invalid description.  Pure host code. */
+/* Bytes of device workspace the call needs (phase XHC_PHASE_FWD for the
+ * forward calls, XHC_PHASE_BWD for the backward ones); 0 for an invalid
+ * description.  Pure host code. */
 size_t xhc_workspace_size(const xhc_desc* desc, int phase);
 
 /* Floats per token of z_save: P + 1 (logits, r) without a router; with
@@ -243,8 +245,9 @@ size_t xhc_workspace_size(const xhc_desc* desc, int phase);
  * invalid description.  Pure host code. */
 int32_t xhc_zsave_stride(const xhc_desc* desc);
 
-/* Checks desc and args (an xhc_fwd_args*, xhc_bwd_args*, xhc_pre_args* or
- * xhc_post_args* for XHC_PHASE_FWD, _BWD, _PRE, _POST):
+/* Checks desc and args (an xhc_fwd_args*, xhc_bwd_args*, xhc_pre_args*,
+ * xhc_post_args*, xhc_bwd_post_args* or xhc_bwd_pre_args* for
+ * XHC_PHASE_FWD, _BWD, _PRE, _POST, _BWD_POST, _BWD_PRE):
  * NULLs, shapes, indices, aliasing, alignment.  Pure host code, no HIP
  * call, usable without a GPU.  Returns XHC_OK or the first error found. */
 int xhc_validate(const xhc_desc* desc, const void* args, int phase);
@@ -378,6 +381,64 @@ int xhc_forward_pre(const xhc_desc* desc, const xhc_pre_args* args, void* worksp
                     xhc_stream_t stream);
 int xhc_forward_post(const xhc_desc* desc, const xhc_post_args* args, void* workspace, size_t workspace_bytes,
                      xhc_stream_t stream);
+
+/* Split backward, the reverse of the split forward (source: the same
+ * section; in backpropagation the gradient reaches the write-back first and
+ * the dense read last, with the sublayer's own backward between them).
+ * xhc_backward_post runs first: from dX_new and the pre call's z_save it
+ * forms dout (the gradient the sublayer's backward starts from), the conv-
+ * weight gradients, and the dots of the gradient of each rewritten row with
+ * each write-back component, which it leaves in the caller's bwd_state.
+ * The sublayer's backward then turns dout into dh_in, and xhc_backward_pre
+ * forms dX, dW and db from dX_new, dh_in and bwd_state.  The two calls in
+ * turn run the kernels of xhc_backward in its order and give the same
+ * results bit for bit (same z_save).  Not with Gram-Schmidt, a router or
+ * per-token lists (XHC_ERR_UNSUPPORTED): for those this library forms dout
+ * after the coefficient backward, which needs dh_in.  With accumulate = 1
+ * each call adds to the gradients it writes. */
+typedef struct {
+  const void* out;        /* [T,C] the sublayer output                          */
+  const float *w4, *w8, *w12;  /* TFA conv weights, NULL iff ncomp == 1         */
+  const int32_t* active;  /* HOST [k], the forward's active list                */
+  const float* z_save;    /* [T, xhc_zsave_stride(desc)] the forward's, required */
+  const void* dX_new;     /* [T,N,C] gradient w.r.t. X_new                      */
+  void* dout;             /* [T,C] gradient w.r.t. out                          */
+  float *dw4, *dw8, *dw12;  /* fp32 conv-weight gradients, NULL iff ncomp == 1  */
+  void* bwd_state;        /* xhc_bwd_state_size(desc) bytes, 16-byte aligned:
+                             written here, read by xhc_backward_pre            */
+  int32_t accumulate;     /* 0: overwrite dw*; 1: add to them                   */
+  xhc_timer* timer;
+} xhc_bwd_post_args;
+
+typedef struct {
+  const void* X;          /* [T,N,C] as in xhc_bwd_args                         */
+  const void* xact;       /* [T,k,C] or NULL, as in xhc_bwd_args                */
+  const void* W;          /* [N*C,P]                                            */
+  const float* bias;      /* [P] or NULL                                        */
+  const int32_t* active;  /* HOST [k], the forward's active list                */
+  const float* z_save;    /* the forward's z_save, required                     */
+  const void* dX_new;     /* [T,N,C] as given to xhc_backward_post              */
+  const void* dh_in;      /* [T,C] gradient w.r.t. h_in                         */
+  const void* bwd_state;  /* written by xhc_backward_post on the same problem   */
+  void* dX;               /* [T,N,C]; may be == dX_new, must not partially
+                             overlap it                                         */
+  float* dW;              /* [N*C,P] fp32                                       */
+  float* db;              /* [P] fp32, or NULL                                  */
+  int32_t accumulate;     /* 0: overwrite dW/db; 1: add to them                 */
+  xhc_timer* timer;
+} xhc_bwd_pre_args;
+
+/* Bytes of bwd_state (fp32 dot partials per token and channel block); 0 for
+ * an invalid description.  Pure host code. */
+size_t xhc_bwd_state_size(const xhc_desc* desc);
+
+/* Workspace: xhc_workspace_size(desc, XHC_PHASE_BWD) bytes for either call
+ * (its contents need not survive between them; bwd_state must).  Errors as
+ * xhc_backward. */
+int xhc_backward_post(const xhc_desc* desc, const xhc_bwd_post_args* args, void* workspace,
+                      size_t workspace_bytes, xhc_stream_t stream);
+int xhc_backward_pre(const xhc_desc* desc, const xhc_bwd_pre_args* args, void* workspace,
+                     size_t workspace_bytes, xhc_stream_t stream);
 
 /* Message of an XHC_* code (static string). */
 const char* xhc_strerror(int code);

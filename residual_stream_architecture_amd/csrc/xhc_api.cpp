@@ -131,6 +131,7 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.off_pass = o;   o = align256(o + (q.pt ? (size_t)T * q.k * q.C * q.esz : 0));
   q.off_rred = o;   o = align256(o + (q.pt ? (size_t)16 * 4 : 0));
   q.bwd_bytes = o;
+  q.state_bytes = (size_t)q.b1_cblocks * T * DOT_STRIDE * 4;
   return XHC_OK;
 }
 
@@ -368,6 +369,67 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
   return XHC_OK;
 }
 
+// Split backward (xhc_backward_post / xhc_backward_pre).
+static int check_split_bwd_modes(const Plan& p, int accumulate) {
+  if (p.pt || p.gs) return XHC_ERR_UNSUPPORTED;
+  if (accumulate != 0 && accumulate != 1) return XHC_ERR_UNSUPPORTED;
+  return XHC_OK;
+}
+
+static int validate_bwd_post(const Plan& p, const xhc_bwd_post_args* a) {
+  if (!a) return XHC_ERR_NULL;
+  int rc = check_split_bwd_modes(p, a->accumulate);
+  if (rc) return rc;
+  if (!a->out || !a->z_save || !a->dX_new || !a->dout || !a->bwd_state) return XHC_ERR_NULL;
+  if (p.nc == 4 && (!a->w4 || !a->w8 || !a->w12 || !a->dw4 || !a->dw8 || !a->dw12)) return XHC_ERR_NULL;
+  if (p.nc == 1 && (a->w4 || a->w8 || a->w12 || a->dw4 || a->dw8 || a->dw12)) return XHC_ERR_UNSUPPORTED;
+  rc = check_active(p, a->active);
+  if (rc) return rc;
+  const void* ptrs[] = {a->out, a->w4, a->w8, a->w12, a->z_save, a->dX_new, a->dout, a->dw4, a->dw8, a->dw12,
+                        a->bwd_state};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return XHC_ERR_ALIGN;
+  const size_t T = p.T, e = p.esz;
+  const Span out = span(a->out, T * p.C * e);
+  const Span w4 = span(a->w4, a->w4 ? (size_t)p.C * 16 : 0), w8 = span(a->w8, a->w8 ? (size_t)p.C * 32 : 0),
+             w12 = span(a->w12, a->w12 ? (size_t)p.C * 48 : 0);
+  const Span zs = span(a->z_save, T * p.zsv * 4);
+  const Span dXn = span(a->dX_new, T * p.NC * e), dout = span(a->dout, T * p.C * e);
+  const Span dw4 = span(a->dw4, a->dw4 ? (size_t)p.C * 16 : 0), dw8 = span(a->dw8, a->dw8 ? (size_t)p.C * 32 : 0),
+             dw12 = span(a->dw12, a->dw12 ? (size_t)p.C * 48 : 0);
+  const Span st = span(a->bwd_state, p.state_bytes);
+  std::vector<Span> outs = {dout, dw4, dw8, dw12, st};
+  std::vector<Span> ins = {out, w4, w8, w12, zs, dXn};
+  if (any_overlap(outs, ins, Span{nullptr, 0}, Span{nullptr, 0})) return XHC_ERR_ALIAS;
+  return XHC_OK;
+}
+
+static int validate_bwd_pre(const Plan& p, const xhc_bwd_pre_args* a) {
+  if (!a) return XHC_ERR_NULL;
+  int rc = check_split_bwd_modes(p, a->accumulate);
+  if (rc) return rc;
+  if (!a->X || !a->W || !a->z_save || !a->dX_new || !a->dh_in || !a->bwd_state || !a->dX || !a->dW)
+    return XHC_ERR_NULL;
+  rc = check_active(p, a->active);
+  if (rc) return rc;
+  const void* ptrs[] = {a->X, a->xact, a->W, a->bias, a->z_save, a->dX_new, a->dh_in, a->bwd_state, a->dX, a->dW,
+                        a->db};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return XHC_ERR_ALIGN;
+  const size_t T = p.T, e = p.esz;
+  const Span X = span(a->X, T * p.NC * e), xact = span(a->xact, a->xact ? T * p.k * p.C * e : 0);
+  const Span W = span(a->W, (size_t)p.NC * p.P * e), bias = span(a->bias, a->bias ? (size_t)p.P * 4 : 0);
+  const Span zs = span(a->z_save, T * p.zsv * 4), st = span(a->bwd_state, p.state_bytes);
+  const Span dXn = span(a->dX_new, T * p.NC * e), dhin = span(a->dh_in, T * p.C * e);
+  const Span dX = span(a->dX, T * p.NC * e);
+  const Span dW = span(a->dW, (size_t)p.NC * p.P * 4), db = span(a->db, a->db ? (size_t)p.P * 4 : 0);
+  if (a->dX != a->dX_new && overlap(dX, dXn)) return XHC_ERR_ALIAS;
+  std::vector<Span> outs = {dX, dW, db};
+  std::vector<Span> ins = {X, xact, W, bias, zs, dXn, dhin, st};
+  if (any_overlap(outs, ins, dX, dXn)) return XHC_ERR_ALIAS;
+  return XHC_OK;
+}
+
 int prepare_forward(const xhc_desc* d, const xhc_fwd_args* a, Plan* p) {
   int rc = make_plan(d, p);
   if (rc) return rc;
@@ -422,6 +484,12 @@ size_t xhc_workspace_size(const xhc_desc* desc, int phase) {
   return 0;
 }
 
+size_t xhc_bwd_state_size(const xhc_desc* desc) {
+  xhc::Plan p;
+  if (xhc::make_plan(desc, &p) != XHC_OK) return 0;
+  return p.state_bytes;
+}
+
 // The next sublayer's plan of a split call (== p without desc_next).
 static int next_plan(const xhc::Plan& p, const xhc_desc* desc_next, xhc::Plan* pn) {
   *pn = p;
@@ -436,6 +504,8 @@ int xhc_validate(const xhc_desc* desc, const void* args, int phase) {
   if (rc) return rc;
   if (phase == XHC_PHASE_FWD) return xhc::validate_fwd(p, static_cast<const xhc_fwd_args*>(args));
   if (phase == XHC_PHASE_BWD) return xhc::validate_bwd(p, static_cast<const xhc_bwd_args*>(args));
+  if (phase == XHC_PHASE_BWD_POST) return xhc::validate_bwd_post(p, static_cast<const xhc_bwd_post_args*>(args));
+  if (phase == XHC_PHASE_BWD_PRE) return xhc::validate_bwd_pre(p, static_cast<const xhc_bwd_pre_args*>(args));
   if (phase == XHC_PHASE_PRE || phase == XHC_PHASE_POST) {
     if (!args) return XHC_ERR_NULL;
     const xhc_desc* dn = phase == XHC_PHASE_PRE ? static_cast<const xhc_pre_args*>(args)->desc_next
@@ -552,6 +622,32 @@ int xhc_backward(const xhc_desc* desc, const xhc_bwd_args* args, void* workspace
   if (rc) return rc;
   clear_pending_hip_error();
   return xhc::launch_backward(p, args, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+int xhc_backward_post(const xhc_desc* desc, const xhc_bwd_post_args* args, void* workspace, size_t workspace_bytes,
+                      xhc_stream_t stream) {
+  xhc::Plan p;
+  int rc = xhc::make_plan(desc, &p);
+  if (rc) return rc;
+  rc = xhc::validate_bwd_post(p, args);
+  if (rc) return rc;
+  rc = check_ws(p, workspace, workspace_bytes, p.bwd_bytes);
+  if (rc) return rc;
+  clear_pending_hip_error();
+  return xhc::launch_backward_post(p, args, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+int xhc_backward_pre(const xhc_desc* desc, const xhc_bwd_pre_args* args, void* workspace, size_t workspace_bytes,
+                     xhc_stream_t stream) {
+  xhc::Plan p;
+  int rc = xhc::make_plan(desc, &p);
+  if (rc) return rc;
+  rc = xhc::validate_bwd_pre(p, args);
+  if (rc) return rc;
+  rc = check_ws(p, workspace, workspace_bytes, p.bwd_bytes);
+  if (rc) return rc;
+  clear_pending_hip_error();
+  return xhc::launch_backward_pre(p, args, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
 const char* xhc_strerror(int code) {

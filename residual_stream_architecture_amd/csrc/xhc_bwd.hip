@@ -228,6 +228,9 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
 // the Gram record at 0..10 (BD_GRAM: dpart[cb][t][16], Gram at 0..10).
 // ROUTE: the rows G_a come from each token's active list (route_idx; uniform
 // scalar loads one token ahead of the loads they address).
+// hpost holds each token's post coefficients (16 floats, a-major) every
+// hstride floats: B1x's [T][16] gate records, or the coefficient records of
+// the split backward's first call.
 // ---------------------------------------------------------------------------
 enum { BD_FULL = 0, BD_GSDOTS = 1, BD_GSGRAD = 2, BD_GRAM = 3 };
 constexpr int GRAM_SPLIT = 8;   // segments of the forward Gram pass per backward segment
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(256) void k_bdots(
     const void* __restrict__ out, const float* __restrict__ w4, const float* __restrict__ w8,
     const float* __restrict__ w12, const float* __restrict__ hpost, const float* __restrict__ gsS,
     float* __restrict__ dpart, void* __restrict__ dout, float* __restrict__ dwpart, int T, int S, int C, int N,
-    int kk, Act4 act, int lseg, int segs_per_seq, const int32_t* __restrict__ ridx) {
+    int kk, Act4 act, int lseg, int segs_per_seq, const int32_t* __restrict__ ridx, int hstride) {
   using V2 = Vec<E, B1_CH>;
   constexpr int EB = E::bytes;
   constexpr bool GS = MODE != BD_FULL;
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(256) void k_bdots(
   auto load_h = [&](int s) {
     if constexpr (NEED_H) {
       const size_t t = tok0 + min(s, S - 1);
-      const f32x4* hp = reinterpret_cast<const f32x4*>(hpost + t * 16);
+      const f32x4* hp = reinterpret_cast<const f32x4*>(hpost + t * hstride);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const f32x4 v = hp[a];
@@ -1562,7 +1565,7 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
 #define XHC_BDOTS_G(GRID, NCOMP, FAST, MODE, LSEG, SEGS, RT)                                                    \
   k_bdots<E, NCOMP, FAST, MODE, RT><<<GRID, 256, 0, st>>>(src, a->dX_new, a->dh_in, a->out, a->w4, a->w8, a->w12, \
                                                           hpost, gss, dpart, a->dout, dwpart, p.T, p.S, p.C, p.N,  \
-                                                          p.k, act, LSEG, SEGS, ridx)
+                                                          p.k, act, LSEG, SEGS, ridx, 16)
 #define XHC_BDOTS(NCOMP, MODE)                                                                                 \
   do {                                                                                                         \
     if (rt) {                                                                                                  \
@@ -1663,6 +1666,123 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Split backward.  xhc_backward_post (first in backpropagation): from dX_new
+// and the forward's z_save, the TFA backward -- dout, the conv-weight
+// gradients and the dots <G_a, U_m> -- with the dots left in the caller's
+// bwd_state.  xhc_backward_pre (after the sublayer's own backward has turned
+// dout into dh_in): the state dots, the coefficient backward from both sets
+// of dots, the dX assembly and dW, db.  Together the kernels and their
+// order are those of backward_impl.
+// ---------------------------------------------------------------------------
+template <typename E, typename R>
+static int backward_post_impl(const Plan& p, const xhc_bwd_post_args* a, char* ws, hipStream_t st) {
+  xhc_timer* tm = a->timer;
+  float* coef = reinterpret_cast<float*>(ws + p.off_coef);        // [T][64] coefficient records
+  float* dwpart = reinterpret_cast<float*>(ws + p.off_dwpart);
+  float* dpart = static_cast<float*>(a->bwd_state);
+  const int rc = launch_coef_saved(p, a->z_save, coef, st, tm);
+  if (rc) return rc;
+  const StreamRows src{};     // the rows of the state are not read here
+  Act4 act;
+  for (int b = 0; b < 4; ++b) act.id[b] = b < p.k ? a->active[b] : 0;
+  const dim3 b1grid(p.b1_cblocks, p.B * p.b1_segs);
+  const bool fast = p.N == 16 && p.k == 4;
+  {
+    TimedLaunch tl(tm, KID_BDOTS, st);
+#define XHC_BDP(NCOMP, FAST)                                                                                    \
+  k_bdots<E, NCOMP, FAST, BD_FULL, false><<<b1grid, 256, 0, st>>>(                                               \
+      src, a->dX_new, nullptr, a->out, a->w4, a->w8, a->w12, coef + CO_POST, nullptr, dpart, a->dout, dwpart,    \
+      p.T, p.S, p.C, p.N, p.k, act, p.b1_lseg, p.b1_segs, nullptr, COEF_STRIDE)
+    if (p.nc == 4) {
+      if (fast) XHC_BDP(4, true); else XHC_BDP(4, false);
+    } else {
+      if (fast) XHC_BDP(1, true); else XHC_BDP(1, false);
+    }
+#undef XHC_BDP
+  }
+  if (p.nc == 4) {
+    TimedLaunch tl(tm, KID_BREDUCE, st);
+    const int nb_conv = (int)(((int64_t)p.C * 24 * RED_CONV_LANES + 255) / 256);
+    k_reduce<<<p.P + nb_conv, 256, 0, st>>>(nullptr, 0, p.NC, p.P, nullptr, nullptr, p.T, nullptr, dwpart,
+                                           p.B * p.b1_segs, p.C, a->dw4, a->dw8, a->dw12, 0, a->accumulate, p.dwr,
+                                           p.dzs, nb_conv, nullptr, nullptr, p.N, HresActive{});
+  }
+  return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
+}
+
+template <typename E, typename R>
+static int backward_pre_impl(const Plan& p, const xhc_bwd_pre_args* a, char* ws, hipStream_t st) {
+  xhc_timer* tm = a->timer;
+  const float* zin = a->z_save;
+  void* Wp = ws + p.off_wp;
+  float* dpa = reinterpret_cast<float*>(ws + p.off_dpa);
+  float* hpost = reinterpret_cast<float*>(ws + p.off_coef);
+  float* dz = reinterpret_cast<float*>(ws + p.off_dz);
+  unsigned char* rec = reinterpret_cast<unsigned char*>(ws + p.off_rec);
+  float* dwp = reinterpret_cast<float*>(ws + p.off_dwpart2);
+  const float* dpart = static_cast<const float*>(a->bwd_state);
+  const StreamRows src = stream_rows(p, a->X, a->xact, a->active);
+  Act4 act;
+  for (int b = 0; b < 4; ++b) act.id[b] = b < p.k ? a->active[b] : 0;
+  const HresActive ha = hres_active(p, a->active);
+  {
+    TimedLaunch tl(tm, KID_BXDOTS, st);
+    k_bxdots<E, R, false><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(
+        src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, zin, hpost, p.P, p.nc,
+        p.gate == XHC_GATE_UNIT, static_cast<const R*>(a->W), static_cast<R*>(Wp), p.NC, p.zsv, nullptr, nullptr,
+        p.nfix, nullptr);
+  }
+  {
+    TimedLaunch tl(tm, KID_BCOEF, st);
+    const int nb = (int)((p.Tpad + BCOEF_TOK - 1) / BCOEF_TOK);
+    const size_t shm = (size_t)BCOEF_TOK * (p.iters + 1) * 16 * sizeof(float);
+    k_bcoef<E, false, false><<<nb, 16 * BCOEF_TOK, shm, st>>>(
+        dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T, p.Tpad, p.N, p.k, p.nc, p.P,
+        1.0f / (float)p.NC, p.iters, p.gate == XHC_GATE_UNIT, 0.f, hpost, nullptr, p.zsv, p.dzs, nullptr, p.nfix,
+        nullptr, 0, ha);
+  }
+  {
+    TimedLaunch tl(tm, KID_BGRAD, st);
+    RowTable rows;
+    for (int g = 0; g < 5; ++g)
+      for (int w = 0; w < 4; ++w) rows.stream[g][w] = -1;
+    for (int w = 0; w < p.k; ++w) rows.stream[0][w] = a->active[w];
+    int nxt = 0;
+    for (int i = 0; i < p.N; ++i) {
+      bool is_act = false;
+      for (int b = 0; b < p.k; ++b) is_act |= a->active[b] == i;
+      if (is_act) continue;
+      rows.stream[1 + nxt / 4][nxt % 4] = i;
+      ++nxt;
+    }
+    const int nb = p.b2_rowgroups * p.b2_cblocks * p.b2_ts;
+    k_bgrad<E><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, (int)(p.Tpad / B2_TT), a->dX, dwp,
+                                             p.T, p.C, p.N, p.k, rows, p.b2_rowgroups, p.b2_cblocks,
+                                             p.b2_tok_per_split, ha.res0, ha.mask ? ha.res1 : ha.res0);
+  }
+  {
+    TimedLaunch tl(tm, KID_BREDUCE, st);
+    const int nb_dw = (int)((p.NC * ((p.P + 3) / 4) + 255) / 256);
+    k_reduce<<<nb_dw + p.P, 256, 0, st>>>(dwp, p.b2_ts, p.NC, p.P, a->dW, dz, p.T, a->db, nullptr, 0, p.C, nullptr,
+                                          nullptr, nullptr, nb_dw, a->accumulate, p.dwr, p.dzs, 0, nullptr, nullptr,
+                                          p.N, ha);
+  }
+  return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
+}
+
+int launch_backward_post(const Plan& p, const xhc_bwd_post_args* a, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  if (p.dtype == XHC_BF16) return backward_post_impl<BF16, uint16_t>(p, a, w, st);
+  return backward_post_impl<F32, float>(p, a, w, st);
+}
+
+int launch_backward_pre(const Plan& p, const xhc_bwd_pre_args* a, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  if (p.dtype == XHC_BF16) return backward_pre_impl<BF16, uint16_t>(p, a, w, st);
+  return backward_pre_impl<F32, float>(p, a, w, st);
+}
+
 // Segments of the passes that write per-token records only (BD_GRAM,
 // BD_GSDOTS): GRAM_SPLIT times the backward's, as these passes need few
 // registers and more, shorter segments keep more waves in flight.
@@ -1681,11 +1801,11 @@ void launch_gram(const Plan& p, const void* out, const float* w4, const float* w
   if (p.dtype == XHC_BF16)
     k_bdots<BF16, 4, false, BD_GRAM, false><<<grid, 256, 0, st>>>(none, nullptr, nullptr, out, w4, w8, w12, nullptr,
                                                                   nullptr, gram, nullptr, nullptr, p.T, p.S, p.C,
-                                                                  p.N, p.k, act, lseg, segs, nullptr);
+                                                                  p.N, p.k, act, lseg, segs, nullptr, 16);
   else
     k_bdots<F32, 4, false, BD_GRAM, false><<<grid, 256, 0, st>>>(none, nullptr, nullptr, out, w4, w8, w12, nullptr,
                                                                  nullptr, gram, nullptr, nullptr, p.T, p.S, p.C,
-                                                                 p.N, p.k, act, lseg, segs, nullptr);
+                                                                 p.N, p.k, act, lseg, segs, nullptr, 16);
 }
 
 int launch_backward(const Plan& p, const xhc_bwd_args* a, void* ws, hipStream_t st) {

@@ -929,6 +929,17 @@ int launch_forward_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, c
   return forward_impl<F32, float>(p, pn, a, c, w, st, a->timer);
 }
 
+// Coefficient records from a forward's saved logits (no Gram-Schmidt, no
+// router): the split backward's post gates.
+int launch_coef_saved(const Plan& p, const float* z_save, float* coef, hipStream_t st, xhc_timer* tm) {
+  TimedLaunch tl(tm, KID_COEF, st);
+  k_coef<false, false><<<(p.T + 15) / 16, 256, 0, st>>>(nullptr, 0, p.ZST, p.NT * 16, z_save, nullptr, coef, nullptr,
+                                                        p.zsv, p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps,
+                                                        p.iters, p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f,
+                                                        RouteArgs{}, HresActive{});
+  return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
+}
+
 // Backward helper: coefficients either from a forward's z_save or, when it
 // is NULL, recomputed by the projection from the pre-update state.  With a
 // router the recompute also forms the router's record for the forward's

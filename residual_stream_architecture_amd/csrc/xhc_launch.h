@@ -99,6 +99,10 @@ int launch_coef_bwd(const Plan& p, const void* X, const void* xact, const int32_
                     hipStream_t st, xhc_timer* tm, const void* W_route, const float* b_route,
                     const int32_t* force);
 int launch_backward(const Plan& p, const xhc_bwd_args* a, void* ws, hipStream_t st);
+int launch_coef_saved(const Plan& p, const float* z_save, float* coef, hipStream_t st, xhc_timer* tm);
+// Split backward (xhc_backward_post, then xhc_backward_pre).
+int launch_backward_post(const Plan& p, const xhc_bwd_post_args* a, void* ws, hipStream_t st);
+int launch_backward_pre(const Plan& p, const xhc_bwd_pre_args* a, void* ws, hipStream_t st);
 // Gram-Schmidt's Gram records of the components (forward): gram[cb][t][16]
 // partials over channel blocks of B1_WAVES * B1_WAVE_CH.
 void launch_gram(const Plan& p, const void* out, const float* w4, const float* w8, const float* w12, float* gram,

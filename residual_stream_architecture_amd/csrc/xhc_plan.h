@@ -139,6 +139,7 @@ struct Plan {
   // workspace layout (byte offsets; every region 256-byte aligned)
   size_t off_wt, off_zpart, off_coef, off_gram, off_rcs, fwd_bytes;
   size_t off_zbuf, off_wp, off_dpart, off_dpa, off_dwpart, off_dz, off_rec, off_dwpart2, off_gss;
+  size_t state_bytes;     // bwd_state of the split backward: dot partials [b1_cblocks][T][DOT_STRIDE]
   size_t off_hres, off_pass, off_rred, bwd_bytes;
 };
 

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_PKG, "libxhc.so")
 XHC_F32, XHC_BF16 = 0, 1
 XHC_GATE_SIGMOID, XHC_GATE_UNIT = 0, 1
 XHC_PHASE_FWD, XHC_PHASE_BWD, XHC_PHASE_PRE, XHC_PHASE_POST = 0, 1, 2, 3
+XHC_PHASE_BWD_POST, XHC_PHASE_BWD_PRE = 4, 5
 ERRORS = {0: "XHC_OK", -1: "XHC_ERR_NULL", -2: "XHC_ERR_SHAPE", -3: "XHC_ERR_INDEX",
           -4: "XHC_ERR_ALIAS", -5: "XHC_ERR_ALIGN", -6: "XHC_ERR_UNSUPPORTED",
           -7: "XHC_ERR_WORKSPACE", -8: "XHC_ERR_HIP", -9: "XHC_ERR_SCRATCH"}
@@ -68,6 +69,18 @@ class xhc_post_args(ctypes.Structure):
                 ("W_next", _vp), ("carry_out", _vp), ("desc_next", ctypes.POINTER(xhc_desc)), ("timer", _vp)]
 
 
+class xhc_bwd_post_args(ctypes.Structure):
+    _fields_ = [("out", _vp), ("w4", _vp), ("w8", _vp), ("w12", _vp), ("active", ctypes.POINTER(ctypes.c_int32)),
+                ("z_save", _vp), ("dX_new", _vp), ("dout", _vp), ("dw4", _vp), ("dw8", _vp), ("dw12", _vp),
+                ("bwd_state", _vp), ("accumulate", ctypes.c_int32), ("timer", _vp)]
+
+
+class xhc_bwd_pre_args(ctypes.Structure):
+    _fields_ = [("X", _vp), ("xact", _vp), ("W", _vp), ("bias", _vp), ("active", ctypes.POINTER(ctypes.c_int32)),
+                ("z_save", _vp), ("dX_new", _vp), ("dh_in", _vp), ("bwd_state", _vp), ("dX", _vp), ("dW", _vp),
+                ("db", _vp), ("accumulate", ctypes.c_int32), ("timer", _vp)]
+
+
 class XhcError(RuntimeError):
     def __init__(self, code, what):
         super().__init__(f"{what}: {ERRORS.get(code, code)} ({lib.xhc_strerror(code).decode()})")
@@ -107,6 +120,14 @@ def _load():
     L.xhc_forward_post.restype = ctypes.c_int
     L.xhc_backward.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_bwd_args), _vp, ctypes.c_size_t, _vp]
     L.xhc_backward.restype = ctypes.c_int
+    L.xhc_bwd_state_size.argtypes = [ctypes.POINTER(xhc_desc)]
+    L.xhc_bwd_state_size.restype = ctypes.c_size_t
+    L.xhc_backward_post.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_bwd_post_args), _vp,
+                                    ctypes.c_size_t, _vp]
+    L.xhc_backward_post.restype = ctypes.c_int
+    L.xhc_backward_pre.argtypes = [ctypes.POINTER(xhc_desc), ctypes.POINTER(xhc_bwd_pre_args), _vp,
+                                   ctypes.c_size_t, _vp]
+    L.xhc_backward_pre.restype = ctypes.c_int
     L.xhc_strerror.argtypes = [ctypes.c_int]
     L.xhc_strerror.restype = ctypes.c_char_p
     L.xhc_timer_create.argtypes = []
@@ -147,6 +168,10 @@ def workspace_size(desc, phase):
 
 def carry_size(desc):
     return lib.xhc_carry_size(ctypes.byref(desc))
+
+
+def bwd_state_size(desc):
+    return lib.xhc_bwd_state_size(ctypes.byref(desc))
 
 
 def strerror(code):
@@ -352,6 +377,39 @@ def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None,
                           _stream_handle(stream))
     if rc:
         raise XhcError(rc, "xhc_backward")
+
+
+def backward_post(out, active, z_save, dX_new, dout, bwd_state, *, desc, w4=None, w8=None, w12=None, dw4=None,
+                  dw8=None, dw12=None, accumulate=False, workspace=None, stream=None, timer=None):
+    """xhc_backward_post: dout, the conv-weight gradients and the dot
+    partials (into bwd_state, a device buffer of bwd_state_size(desc) bytes)
+    from dX_new and the forward's z_save."""
+    act = _active_array(active)
+    args = xhc_bwd_post_args(_ptr(out), _ptr(w4), _ptr(w8), _ptr(w12),
+                             ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(z_save), _ptr(dX_new),
+                             _ptr(dout), _ptr(dw4), _ptr(dw8), _ptr(dw12), _ptr(bwd_state),
+                             int(bool(accumulate)), None if timer is None else timer.handle)
+    ws, need = _workspace(desc, XHC_PHASE_BWD, out.device, workspace, stream)
+    rc = lib.xhc_backward_post(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
+                               _stream_handle(stream))
+    if rc:
+        raise XhcError(rc, "xhc_backward_post")
+
+
+def backward_pre(X, W, active, z_save, dX_new, dh_in, bwd_state, dX, dW, *, desc, xact=None, bias=None, db=None,
+                 accumulate=False, workspace=None, stream=None, timer=None):
+    """xhc_backward_pre: dX, dW and db from dX_new, dh_in and the bwd_state
+    that xhc_backward_post left."""
+    act = _active_array(active)
+    args = xhc_bwd_pre_args(_ptr(X), _ptr(xact), _ptr(W), _ptr(bias),
+                            ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(z_save), _ptr(dX_new),
+                            _ptr(dh_in), _ptr(bwd_state), _ptr(dX), _ptr(dW), _ptr(db),
+                            int(bool(accumulate)), None if timer is None else timer.handle)
+    ws, need = _workspace(desc, XHC_PHASE_BWD, X.device, workspace, stream)
+    rc = lib.xhc_backward_pre(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
+                              _stream_handle(stream))
+    if rc:
+        raise XhcError(rc, "xhc_backward_pre")
 
 
 def validate(desc, args, phase):

@@ -505,3 +505,101 @@ def test_split_forward_validation():
     assert xhc.lib.xhc_forward_pre(ctypes.byref(d), ctypes.byref(a), None, 0, None) == xhc.XHC_ERR_WORKSPACE
     b, keep = good_post(d)
     assert xhc.lib.xhc_forward_post(ctypes.byref(d), ctypes.byref(b), None, 0, None) == xhc.XHC_ERR_WORKSPACE
+
+
+def good_bwd_post(desc):
+    act = (ctypes.c_int32 * desc.k)(*range(desc.k))
+    c4 = desc.ncomp == 4
+    a = xhc.xhc_bwd_post_args(
+        out=fake(3), w4=fake(4) if c4 else None, w8=fake(5) if c4 else None, w12=fake(6) if c4 else None,
+        active=ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), z_save=fake(8), dX_new=fake(9), dout=fake(12),
+        dw4=fake(15) if c4 else None, dw8=fake(16) if c4 else None, dw12=fake(17) if c4 else None,
+        bwd_state=fake(20), accumulate=0, timer=None)
+    return a, act
+
+
+def good_bwd_pre(desc):
+    act = (ctypes.c_int32 * desc.k)(*range(desc.k))
+    a = xhc.xhc_bwd_pre_args(
+        X=fake(1), xact=fake(2), W=fake(7), bias=None, active=ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)),
+        z_save=fake(8), dX_new=fake(9), dh_in=fake(10), bwd_state=fake(20), dX=fake(11), dW=fake(13), db=fake(14),
+        accumulate=0, timer=None)
+    return a, act
+
+
+def test_split_backward_validation():
+    d = desc16()
+    BP, BR = xhc.XHC_PHASE_BWD_POST, xhc.XHC_PHASE_BWD_PRE
+    a, keep = good_bwd_post(d)
+    assert xhc.validate(d, a, BP) == xhc.XHC_OK
+    b, keep2 = good_bwd_pre(d)
+    assert xhc.validate(d, b, BR) == xhc.XHC_OK
+    # the state: dot partials per channel block of the dots pass, token and dot slot
+    T = d.B * d.S
+    st = xhc.bwd_state_size(d)
+    assert st > 0 and st % (T * 48 * 4) == 0
+    assert xhc.bwd_state_size(desc16(C=4096)) > st
+    bad = desc16()
+    bad.N = 17
+    assert xhc.bwd_state_size(bad) == 0
+    # required pointers
+    for field in ("z_save", "dX_new", "dout", "bwd_state", "out", "dw8"):
+        a, keep = good_bwd_post(d)
+        setattr(a, field, None)
+        assert xhc.validate(d, a, BP) == xhc.XHC_ERR_NULL, field
+    for field in ("X", "W", "z_save", "dX_new", "dh_in", "bwd_state", "dX", "dW"):
+        b, keep = good_bwd_pre(d)
+        setattr(b, field, None)
+        assert xhc.validate(d, b, BR) == xhc.XHC_ERR_NULL, field
+    # xact and db are optional
+    b, keep = good_bwd_pre(d)
+    b.xact = None
+    b.db = None
+    assert xhc.validate(d, b, BR) == xhc.XHC_OK
+    # the state is an output of the first call and an input of the second
+    a, keep = good_bwd_post(d)
+    a.bwd_state = a.dX_new
+    assert xhc.validate(d, a, BP) == xhc.XHC_ERR_ALIAS
+    a, keep = good_bwd_post(d)
+    a.dout = fake(20, 64)
+    assert xhc.validate(d, a, BP) == xhc.XHC_ERR_ALIAS
+    b, keep = good_bwd_pre(d)
+    b.dW = fake(20, 256)
+    assert xhc.validate(d, b, BR) == xhc.XHC_ERR_ALIAS
+    # dX may be dX_new itself but not a part of it
+    b, keep = good_bwd_pre(d)
+    b.dX = b.dX_new
+    assert xhc.validate(d, b, BR) == xhc.XHC_OK
+    b.dX = fake(9, 256)
+    assert xhc.validate(d, b, BR) == xhc.XHC_ERR_ALIAS
+    # alignment, accumulate, indices
+    a, keep = good_bwd_post(d)
+    a.bwd_state = fake(20, 4)
+    assert xhc.validate(d, a, BP) == xhc.XHC_ERR_ALIGN
+    a, keep = good_bwd_post(d)
+    a.accumulate = 2
+    assert xhc.validate(d, a, BP) == xhc.XHC_ERR_UNSUPPORTED
+    b, keep = good_bwd_pre(d)
+    keep[1] = keep[0]
+    assert xhc.validate(d, b, BR) == xhc.XHC_ERR_INDEX
+    # ncomp = 1: no conv weights or their gradients
+    d1 = desc16(ncomp=1)
+    a, keep = good_bwd_post(d1)
+    assert xhc.validate(d1, a, BP) == xhc.XHC_OK
+    a.dw4 = fake(15)
+    assert xhc.validate(d1, a, BP) == xhc.XHC_ERR_UNSUPPORTED
+    # Gram-Schmidt, a router and per-token lists are not split; hres_active is
+    for kw in (dict(gram_schmidt=True), dict(route=2), dict(per_token_active=True)):
+        dd = desc16(**kw)
+        assert xhc.validate(dd, good_bwd_post(dd)[0], BP) == xhc.XHC_ERR_UNSUPPORTED, kw
+        assert xhc.validate(dd, good_bwd_pre(dd)[0], BR) == xhc.XHC_ERR_UNSUPPORTED, kw
+    dh = desc16(hres_active=True)
+    assert xhc.validate(dh, good_bwd_post(dh)[0], BP) == xhc.XHC_OK
+    assert xhc.validate(dh, good_bwd_pre(dh)[0], BR) == xhc.XHC_OK
+    # both need the backward's workspace and stop before any launch without it
+    assert xhc.workspace_size(d, BP) == 0 and xhc.workspace_size(d, BR) == 0
+    a, keep = good_bwd_post(d)
+    assert xhc.lib.xhc_backward_post(ctypes.byref(d), ctypes.byref(a), None, 0, None) == xhc.XHC_ERR_WORKSPACE
+    b, keep = good_bwd_pre(d)
+    assert xhc.lib.xhc_backward_pre(ctypes.byref(d), ctypes.byref(b), None, 0, None) == xhc.XHC_ERR_WORKSPACE
+    assert xhc.lib.xhc_backward_pre(ctypes.byref(d), None, None, 0, None) == xhc.XHC_ERR_NULL
