@@ -34,8 +34,12 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless a field says HOST.  The caller owns
- *     all memory; the library never allocates, frees or synchronises.  Work
- *     is enqueued asynchronously on `stream` (NULL = the null stream).
+ *     all memory; the library never allocates, frees or synchronises, with
+ *     two exceptions, both opt-in: a call that carries a timer (args->timer)
+ *     creates the HIP events it records, and xhc_timer_read waits for them
+ *     (see the timer calls at the end); xhc_forward_noalloc looks up its
+ *     static array once per device.  Work is enqueued asynchronously on
+ *     `stream` (NULL = the null stream).
  *   - Layouts are dense, row-major, C contiguous: X, X_new, dX_new, dX are
  *     [T, N, C]; out, h_in, dh_in, dout are [T, C]; W and dW are [N*C, P];
  *     w4/w8/w12 and their gradients are [C, 4], [C, 8], [C, 12].
@@ -88,6 +92,14 @@ enum {
  * ncomp in {1, 4} (4 = TFA on: out plus three causal convolutions; 1 = out
  * only, the mHC-style write-back); C >= 8 with C % 8 == 0;
  * 1 <= sinkhorn_iters <= 64; rms_eps >= 0; B*S*N*C < 2^31.
+ *
+ * The last bound keeps every element index of the state within 32 bits (the
+ * kernels address it through 32-bit buffer offsets); larger states are
+ * XHC_ERR_SHAPE.  Sequences do not interact, so a larger batch runs as
+ * several calls over groups of whole sequences, each with its pointers
+ * offset to the group's first token (B = the group's size); in the backward,
+ * accumulate = 1 on every call after the first sums dW, db and the conv
+ * gradients over the groups (up to the order of fp32 sums).
  *
  * Gram-Schmidt (gram_schmidt = 1; source: the retrospective's section
  * "Conv 带来了新信息，也带来了新的麻烦", which removes from each conv
@@ -444,9 +456,17 @@ int xhc_backward_pre(const xhc_desc* desc, const xhc_bwd_pre_args* args, void* w
 const char* xhc_strerror(int code);
 
 /* Timer: records HIP events around each kernel launched by calls that carry
- * it.  xhc_timer_read synchronises on the recorded events and returns the
- * summed milliseconds and launch count of the kernel named `kernel` (one of
- * the names xhc_kernel_name returns), or a negative code. */
+ * it, on the call's stream.  It is the one part of the library that creates
+ * HIP objects: a call that carries a timer creates (hipEventCreate) each
+ * event the first time the timer needs it and keeps it for reuse after
+ * xhc_timer_reset; xhc_timer_destroy destroys them.  A failed creation only
+ * drops that measurement.  xhc_timer_read blocks the calling thread until
+ * the recorded events of `kernel` have completed (hipEventSynchronize), then
+ * returns the summed milliseconds and launch count of the kernel named
+ * `kernel` (one of the names xhc_kernel_name returns), or a negative code.
+ * A timer is not for code under graph capture (event records would be
+ * captured) nor for xhc_forward_noalloc (XHC_ERR_UNSUPPORTED); it is not
+ * safe to share between threads. */
 xhc_timer* xhc_timer_create(void);
 void xhc_timer_destroy(xhc_timer* timer);
 void xhc_timer_reset(xhc_timer* timer);

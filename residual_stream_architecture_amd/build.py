@@ -59,6 +59,40 @@ def build(verbose=False):
     return LIB
 
 
+SAN_DIR = os.path.join(BUILD_DIR, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libxhc.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized():
+    """libxhc.so with its C-ABI layer (validation, planning, dispatch, timer:
+    xhc_api.cpp) compiled as plain host C++ under AddressSanitizer and
+    UBSan, linked with the kernels' objects of build(), into _build/san.
+    For the ABI tests on the CPU: load it with XHC_LIBRARY and the ASan
+    runtime preloaded (sanitized_env())."""
+    if not all(os.path.exists(os.path.join(BUILD_DIR, s + ".o")) for s in SOURCES[1:]):
+        build()
+    os.makedirs(SAN_DIR, exist_ok=True)
+    api_obj = os.path.join(SAN_DIR, "xhc_api.o")
+    _run(["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+          "-I" + os.path.join(ROOT, "include"), "-Wno-unused-result", *SAN_FLAGS,
+          "-c", os.path.join(CSRC, SOURCES[0]), "-o", api_obj])
+    objs = [os.path.join(BUILD_DIR, s + ".o") for s in SOURCES[1:]]
+    _run(["g++", "-shared", *SAN_FLAGS, "-o", SAN_LIB, api_obj, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+          "-Wl,-rpath,/opt/rocm/lib"])
+    return SAN_LIB
+
+
+def sanitized_env():
+    """Environment that loads SAN_LIB in a Python process (the interpreter
+    itself is not instrumented, so the ASan runtime is preloaded)."""
+    asan = subprocess.run(["g++", "-print-file-name=libasan.so"], stdout=subprocess.PIPE, text=True).stdout.strip()
+    env = dict(os.environ)
+    env.update(XHC_LIBRARY=SAN_LIB, LD_PRELOAD=asan, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    return env
+
+
 def _check_kernel_stubs(lib):
     """A kernel template whose host-side instantiation fails (a deferred
     device-code diagnostic) leaves its launch stub undefined: the library

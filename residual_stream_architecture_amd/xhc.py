@@ -8,7 +8,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libxhc.so")
+# XHC_LIBRARY names another build of the same library (a sanitised host build
+# for the ABI tests, say); by default the in-tree one.
+LIB_PATH = os.environ.get("XHC_LIBRARY") or os.path.join(_PKG, "libxhc.so")
 
 XHC_F32, XHC_BF16 = 0, 1
 XHC_GATE_SIGMOID, XHC_GATE_UNIT = 0, 1
