@@ -168,8 +168,9 @@ typedef struct {
                                in route_idx [T,k] (an input to both calls;
                                no router, write-back unscaled; the lists
                                must hold distinct streams, ids outside
-                               [0, N) are read as 0); requires route = 0 and
-                               is not chained.  0: off                      */
+                               [0, N) are read as 0, and the calls report
+                               such lists through args->status); requires
+                               route = 0 and is not chained.  0: off        */
   int32_t hres_active;      /* 1: H_res generated from the k active rows (see
                                below); requires route = 0 and
                                per_token_active = 0, and is not chained.
@@ -210,6 +211,10 @@ typedef struct {
   int32_t* route_idx;  /* [T,k] per-token active list (output), or NULL; the
                           backward needs it.  With desc->per_token_active
                           the caller's lists (input, required)               */
+  int32_t* status;     /* NULL, or device int32[2] (16-byte aligned) that the
+                          call checks given per-token lists into; see
+                          XHC_STATUS_*.  Left untouched without
+                          desc->per_token_active                              */
 } xhc_fwd_args;
 
 typedef struct {
@@ -243,7 +248,23 @@ typedef struct {
   float* db_route;     /* [N] fp32, or NULL                                   */
   const float* b_route;  /* [N] or NULL (zero): read only to recompute the
                           router's scores when z_save is NULL                 */
+  int32_t* status;     /* NULL, or device int32[2] as in xhc_fwd_args: the
+                          lists in route_idx are checked (router or given
+                          lists); left untouched with one list for all      */
 } xhc_bwd_args;
+
+/* Status word of per-token active lists.  A call given args->status and
+ * per-token lists checks every token's list on the device before its other
+ * kernels: for each token with an id outside [0, N) or an id that appears
+ * twice, it ORs XHC_STATUS_ID_RANGE and/or XHC_STATUS_ID_REPEAT into
+ * status[0] and adds 1 to status[1] (the number of such tokens).  The call
+ * never clears the word: zero it before the call (a fill kernel under graph
+ * capture) and read it once the stream has finished the call.  Results
+ * that depend on a flagged token (its own rows; in the backward also the
+ * sums over tokens -- dW, db, the conv-weight gradients -- and dout within
+ * the convolution window before it) are unspecified, but no access leaves
+ * the caller's buffers: an out-of-range id reads as stream 0. */
+enum { XHC_STATUS_ID_RANGE = 1, XHC_STATUS_ID_REPEAT = 2 };
 
 /* Bytes of device workspace the call needs (phase XHC_PHASE_FWD for the
  * forward calls, XHC_PHASE_BWD for the backward ones); 0 for an invalid

@@ -186,7 +186,8 @@ static int validate_fwd(const Plan& p, const xhc_fwd_args* a, bool need_W = true
   int rc = check_active(p, a->active);
   if (rc) return rc;
   const void* ptrs[] = {a->X, a->out, a->w4, a->w8, a->w12, a->W, a->bias, a->X_new, a->h_in, a->z_save, a->xact_save,
-                        p.R ? a->W_route : nullptr, p.R ? a->b_route : nullptr, p.pt ? a->route_idx : nullptr};
+                        p.R ? a->W_route : nullptr, p.R ? a->b_route : nullptr, p.pt ? a->route_idx : nullptr,
+                        p.pt && !p.R ? a->status : nullptr};
   for (const void* q : ptrs)
     if (misaligned(q)) return XHC_ERR_ALIGN;
   const size_t T = p.T, e = p.esz;
@@ -200,9 +201,10 @@ static int validate_fwd(const Plan& p, const xhc_fwd_args* a, bool need_W = true
   const Span Wr = span(p.R ? a->W_route : nullptr, (size_t)p.NC * p.N * e);
   const Span br = span(p.R ? a->b_route : nullptr, (size_t)p.N * 4);
   const Span ri = span(p.pt ? a->route_idx : nullptr, T * p.k * 4);
+  const Span stw = span(p.pt && !p.R ? a->status : nullptr, 8);
   if (a->X_new != a->X && overlap(X, Xn)) return XHC_ERR_ALIAS;
   const bool ri_out = p.R > 0;                  // the router writes the lists; given lists are read
-  std::vector<Span> outs = {Xn, hin, zs, xs};
+  std::vector<Span> outs = {Xn, hin, zs, xs, stw};
   std::vector<Span> ins = {X, out, W, bias, w4, w8, w12, Wr, br};
   (ri_out ? outs : ins).push_back(ri);
   if (any_overlap(outs, ins, Xn, X)) return XHC_ERR_ALIAS;
@@ -342,7 +344,7 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
                         a->dh_in, a->dX, a->dout, a->dW, a->db, a->dw4, a->dw8, a->dw12,
                         p.R ? a->W_route : nullptr, p.pt ? a->route_idx : nullptr,
                         p.R ? a->dW_route : nullptr, p.R ? a->db_route : nullptr,
-                        p.R ? a->b_route : nullptr};
+                        p.R ? a->b_route : nullptr, p.pt ? a->status : nullptr};
   for (const void* q : ptrs)
     if (misaligned(q)) return XHC_ERR_ALIGN;
   const size_t T = p.T, e = p.esz;
@@ -362,7 +364,8 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
   const Span dw4 = span(a->dw4, a->dw4 ? (size_t)p.C * 16 : 0), dw8 = span(a->dw8, a->dw8 ? (size_t)p.C * 32 : 0),
              dw12 = span(a->dw12, a->dw12 ? (size_t)p.C * 48 : 0);
   if (a->dX != a->dX_new && overlap(dX, dXn)) return XHC_ERR_ALIAS;
-  std::vector<Span> outs = {dX, dout, dW, db, dw4, dw8, dw12, dWr, dbr};
+  const Span stw = span(p.pt ? a->status : nullptr, 8);
+  std::vector<Span> outs = {dX, dout, dW, db, dw4, dw8, dw12, dWr, dbr, stw};
   const Span br = span(p.R ? a->b_route : nullptr, (size_t)p.N * 4);
   std::vector<Span> ins = {X, xact, out, W, bias, w4, w8, w12, zs, dXn, dhin, Wr, ri, br};
   if (any_overlap(outs, ins, dX, dXn)) return XHC_ERR_ALIAS;
@@ -458,7 +461,7 @@ struct xhc_timer {
 
 static const char* const kKernelNames[xhc::KID_COUNT] = {
     "pack_wt", "proj", "coef", "mix", "pack_wp", "bdots", "bcoef", "bgrad", "breduce", "bxdots", "mixproj", "gram",
-    "bdots_gs", "route_colsum", "route_pass", "route_dwr"};
+    "bdots_gs", "route_colsum", "route_pass", "route_dwr", "check_lists"};
 
 namespace xhc {
 void timer_mark(xhc_timer* tm, int kid, hipStream_t st, bool start) {

@@ -1518,6 +1518,10 @@ static void dots_segments(const Plan& p, int& lseg, int& segs);
 template <typename E, typename R>
 static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStream_t st) {
   xhc_timer* tm = a->timer;
+  if (p.pt && a->status) {
+    TimedLaunch tl(tm, KID_CHECK, st);
+    launch_check_lists(p, a->route_idx, a->status, st);
+  }
   const float* zin = a->z_save;
   if (!zin) {
     // no saved logits: recompute them (projection and coefficient passes)

@@ -773,6 +773,10 @@ static int forward_impl(const Plan& p, const Plan& pn, const xhc_fwd_args* a, co
 
   float* rcs = reinterpret_cast<float*>(ws + p.off_rcs);
   const RouteArgs ra = route_args(p, a->active, a->b_route, a->route_idx, nullptr, rcs);
+  if (p.pt && !p.R && a->status) {
+    TimedLaunch tl(tm, KID_CHECK, st);
+    launch_check_lists(p, a->route_idx, a->status, st);
+  }
   if (!carry_in) {
     if (p.R) {
       TimedLaunch tl(tm, KID_RCOLSUM, st);

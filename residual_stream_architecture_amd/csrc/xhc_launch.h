@@ -12,7 +12,7 @@ namespace xhc {
 enum KernelId {
   KID_PACK_WT = 0, KID_PROJ, KID_COEF, KID_MIX,
   KID_PACK_WP, KID_BDOTS, KID_BCOEF, KID_BGRAD, KID_BREDUCE, KID_BXDOTS,
-  KID_MIXPROJ, KID_GRAM, KID_BDOTS_GS, KID_RCOLSUM, KID_RPASS, KID_RDWR,
+  KID_MIXPROJ, KID_GRAM, KID_BDOTS_GS, KID_RCOLSUM, KID_RPASS, KID_RDWR, KID_CHECK,
   KID_COUNT
 };
 // Alias kept for the backward's coefficient recompute from z_save.
@@ -111,6 +111,7 @@ void launch_gram(const Plan& p, const void* out, const float* w4, const float* w
 void launch_route_colsum(const Plan& p, const void* W_route, float* rcs, hipStream_t st);
 // Router, backward: pass[t][b] = sum_a H_res[a, b] G_a, and dW_route from
 // B2's partials.
+void launch_check_lists(const Plan& p, const int32_t* ids, int32_t* status, hipStream_t st);
 void launch_route_pass(const Plan& p, const void* dXn, const int32_t* ridx, const float* hres, void* pass,
                        hipStream_t st);
 void launch_route_dwr(const Plan& p, const float* dwp, const float* rred, float* dWr, int accumulate,

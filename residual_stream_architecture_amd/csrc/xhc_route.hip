@@ -147,4 +147,36 @@ void launch_route_dwr(const Plan& p, const float* dwp, const float* rred, float*
   k_route_dwr<<<nb, 256, 0, st>>>(dwp, p.b2_ts, p.NC, p.N, rred, dWr, accumulate);
 }
 
+// Per-token active lists (the caller's, or the router's handed back to the
+// backward): one thread per token checks that its k ids lie in [0, N) and
+// are distinct.  A bad token ORs its findings into status[0] and counts
+// itself in status[1]; good tokens touch nothing, so the usual case costs
+// one read of the lists.
+__global__ __launch_bounds__(256) void k_check_lists(const int32_t* __restrict__ ids, int64_t T, int k, int N,
+                                                     int32_t* __restrict__ status) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int v[4];
+  int bad = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    v[b] = b < k ? ids[t * k + b] : 0;
+    if (b < k && (unsigned)v[b] >= (unsigned)N) bad |= XHC_STATUS_ID_RANGE;
+  }
+#pragma unroll
+  for (int b = 1; b < 4; ++b)
+#pragma unroll
+    for (int a = 0; a < b; ++a)
+      if (b < k && v[a] == v[b]) bad |= XHC_STATUS_ID_REPEAT;
+  if (bad) {
+    atomicOr(status, bad);
+    atomicAdd(status + 1, 1);
+  }
+}
+
+void launch_check_lists(const Plan& p, const int32_t* ids, int32_t* status, hipStream_t st) {
+  const int64_t nb = ((int64_t)p.T + 255) / 256;
+  k_check_lists<<<nb, 256, 0, st>>>(ids, p.T, p.k, p.N, status);
+}
+
 }  // namespace xhc

@@ -16,6 +16,7 @@ XHC_F32, XHC_BF16 = 0, 1
 XHC_GATE_SIGMOID, XHC_GATE_UNIT = 0, 1
 XHC_PHASE_FWD, XHC_PHASE_BWD, XHC_PHASE_PRE, XHC_PHASE_POST = 0, 1, 2, 3
 XHC_PHASE_BWD_POST, XHC_PHASE_BWD_PRE = 4, 5
+XHC_STATUS_ID_RANGE, XHC_STATUS_ID_REPEAT = 1, 2
 ERRORS = {0: "XHC_OK", -1: "XHC_ERR_NULL", -2: "XHC_ERR_SHAPE", -3: "XHC_ERR_INDEX",
           -4: "XHC_ERR_ALIAS", -5: "XHC_ERR_ALIGN", -6: "XHC_ERR_UNSUPPORTED",
           -7: "XHC_ERR_WORKSPACE", -8: "XHC_ERR_HIP", -9: "XHC_ERR_SCRATCH"}
@@ -41,7 +42,7 @@ class xhc_fwd_args(ctypes.Structure):
     _fields_ = [("X", _vp), ("out", _vp), ("w4", _vp), ("w8", _vp), ("w12", _vp),
                 ("W", _vp), ("bias", _vp), ("active", ctypes.POINTER(ctypes.c_int32)),
                 ("X_new", _vp), ("h_in", _vp), ("z_save", _vp), ("xact_save", _vp),
-                ("timer", _vp), ("W_route", _vp), ("b_route", _vp), ("route_idx", _vp)]
+                ("timer", _vp), ("W_route", _vp), ("b_route", _vp), ("route_idx", _vp), ("status", _vp)]
 
 
 class xhc_bwd_args(ctypes.Structure):
@@ -51,7 +52,7 @@ class xhc_bwd_args(ctypes.Structure):
                 ("dW", _vp), ("db", _vp), ("dw4", _vp), ("dw8", _vp), ("dw12", _vp),
                 ("accumulate", ctypes.c_int32), ("timer", _vp),
                 ("W_route", _vp), ("route_idx", _vp), ("dW_route", _vp), ("db_route", _vp),
-                ("b_route", _vp)]
+                ("b_route", _vp), ("status", _vp)]
 
 
 class xhc_chain_args(ctypes.Structure):
@@ -255,7 +256,7 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
             z_save=None, xact_save=None, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID,
             workspace=None, stream=None, timer=None, desc=None, carry_in=None, W_next=None,
             carry_out=None, gram_schmidt=False, gs_eps=1e-6, desc_next=None, route=0, W_route=None,
-            b_route=None, route_idx=None):
+            b_route=None, route_idx=None, status=None):
     """xhc_forward on torch device tensors.  X [B*S,N,C], out [B*S,C], W [N*C,P].
 
     With carry_in, W_next or carry_out given, calls xhc_forward_chain: carry_in
@@ -268,7 +269,9 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
     (W_route [N*C,N], b_route [N]); route_idx [B*S,k] int32 receives the
     per-token active lists, and active then needs only its first k-R entries.
     With desc.per_token_active = 1 (make_desc(..., per_token_active=True))
-    route_idx instead holds the caller's per-token lists, and active is not read."""
+    route_idx instead holds the caller's per-token lists, and active is not read;
+    status (int32 [2] on the device, zeroed by the caller) then receives the
+    XHC_STATUS_* flags and the count of tokens whose list is bad."""
     T, N, C = X.shape
     ncomp = 4 if w4 is not None else 1
     if desc is None:
@@ -278,7 +281,7 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
     args = xhc_fwd_args(_ptr(X), _ptr(out), _ptr(w4), _ptr(w8), _ptr(w12), _ptr(W), _ptr(bias),
                         ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(X_new), _ptr(h_in),
                         _ptr(z_save), _ptr(xact_save), None if timer is None else timer.handle,
-                        _ptr(W_route), _ptr(b_route), _ptr(route_idx))
+                        _ptr(W_route), _ptr(b_route), _ptr(route_idx), _ptr(status))
     ws, need = _workspace(desc, XHC_PHASE_FWD, X.device, workspace, stream)
     if carry_in is None and W_next is None and carry_out is None and desc_next is None:
         rc = lib.xhc_forward(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
@@ -333,7 +336,7 @@ def forward_post(X, out, active, z_save, *, desc, w4=None, w8=None, w12=None, xa
 def forward_noalloc(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None, bias=None,
                     z_save=None, xact_save=None, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID, stream=None,
                     desc=None, gram_schmidt=False, gs_eps=1e-6, route=0, W_route=None, b_route=None,
-                    route_idx=None):
+                    route_idx=None, status=None):
     """xhc_forward_noalloc: xhc_forward with the library's static scratch
     array in place of a workspace (no device memory is allocated)."""
     T, N, C = X.shape
@@ -344,7 +347,8 @@ def forward_noalloc(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w
     act = _active_array(active)
     args = xhc_fwd_args(_ptr(X), _ptr(out), _ptr(w4), _ptr(w8), _ptr(w12), _ptr(W), _ptr(bias),
                         ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(X_new), _ptr(h_in),
-                        _ptr(z_save), _ptr(xact_save), None, _ptr(W_route), _ptr(b_route), _ptr(route_idx))
+                        _ptr(z_save), _ptr(xact_save), None, _ptr(W_route), _ptr(b_route), _ptr(route_idx),
+                        _ptr(status))
     rc = lib.xhc_forward_noalloc(ctypes.byref(desc), ctypes.byref(args), _stream_handle(stream))
     if rc:
         raise XhcError(rc, "xhc_forward_noalloc")
@@ -354,7 +358,7 @@ def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None,
              w12=None, bias=None, z_save=None, db=None, dw4=None, dw8=None, dw12=None, accumulate=False,
              iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID, workspace=None, stream=None, timer=None,
              desc=None, gram_schmidt=False, gs_eps=1e-6, route=0, W_route=None, route_idx=None,
-             dW_route=None, db_route=None, b_route=None):
+             dW_route=None, db_route=None, b_route=None, status=None):
     """xhc_backward on torch device tensors (with a router: the forward's
     z_save and route_idx, and dW_route [N*C,N] / db_route [N] fp32 outputs;
     with per-token lists given by the caller: the same route_idx).
@@ -373,7 +377,8 @@ def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None,
                         ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(z_save), _ptr(dX_new),
                         _ptr(dh_in), _ptr(dX), _ptr(dout), _ptr(dW), _ptr(db), _ptr(dw4), _ptr(dw8),
                         _ptr(dw12), int(bool(accumulate)), None if timer is None else timer.handle,
-                        _ptr(W_route), _ptr(route_idx), _ptr(dW_route), _ptr(db_route), _ptr(b_route))
+                        _ptr(W_route), _ptr(route_idx), _ptr(dW_route), _ptr(db_route), _ptr(b_route),
+                        _ptr(status))
     ws, need = _workspace(desc, XHC_PHASE_BWD, X.device, workspace, stream)
     rc = lib.xhc_backward(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
                           _stream_handle(stream))

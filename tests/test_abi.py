@@ -603,3 +603,42 @@ def test_split_backward_validation():
     b, keep = good_bwd_pre(d)
     assert xhc.lib.xhc_backward_pre(ctypes.byref(d), ctypes.byref(b), None, 0, None) == xhc.XHC_ERR_WORKSPACE
     assert xhc.lib.xhc_backward_pre(ctypes.byref(d), None, None, 0, None) == xhc.XHC_ERR_NULL
+
+
+def test_status_word_of_given_lists():
+    F, Bw = xhc.XHC_PHASE_FWD, xhc.XHC_PHASE_BWD
+    d = desc16(per_token_active=True)
+    a, keep = good_fwd(d)
+    a.route_idx = fake(22)
+    assert xhc.validate(d, a, F) == xhc.XHC_OK
+    a.status = fake(30)
+    assert xhc.validate(d, a, F) == xhc.XHC_OK
+    a.status = fake(30, 4)
+    assert xhc.validate(d, a, F) == xhc.XHC_ERR_ALIGN
+    for other in ("route_idx", "X_new", "h_in", "z_save"):
+        a.status = getattr(a, other) + 16
+        assert xhc.validate(d, a, F) == xhc.XHC_ERR_ALIAS, other
+    b, keep2 = good_bwd(d)
+    b.route_idx = fake(22)
+    b.status = fake(30)
+    assert xhc.validate(d, b, Bw) == xhc.XHC_OK
+    b.status = b.route_idx
+    assert xhc.validate(d, b, Bw) == xhc.XHC_ERR_ALIAS
+    b.status = b.dW + 64
+    assert xhc.validate(d, b, Bw) == xhc.XHC_ERR_ALIAS
+    # with one list for every token the word is not read
+    d0 = desc16()
+    a, keep = good_fwd(d0)
+    a.status = fake(1, 4)
+    assert xhc.validate(d0, a, F) == xhc.XHC_OK
+    # the router's lists are its own in the forward and an input of the backward
+    dr = desc16(route=2)
+    a, keep = good_fwd(dr)
+    a.W_route, a.route_idx, a.status = fake(20), fake(22), fake(1, 4)
+    assert xhc.validate(dr, a, F) == xhc.XHC_OK
+    b, keep = good_bwd(dr)
+    b.W_route, b.route_idx, b.dW_route, b.status = fake(20), fake(22), fake(23), fake(30, 8)
+    assert xhc.validate(dr, b, Bw) == xhc.XHC_ERR_ALIGN
+    b.status = fake(30)
+    assert xhc.validate(dr, b, Bw) == xhc.XHC_OK
+    assert "check_lists" in xhc.kernel_names()
