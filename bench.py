@@ -160,6 +160,12 @@ def bandwidth_probes(torch):
                  `run` bytes of every row of its token split -- 2r1w is the
                  backward assembly kernel's mix (state and dX_new read, dX
                  written), 1r the projection's and the backward dots' reads.
+      frag_*     the same state as 16 rows of 8 KiB per token; each
+                 workgroup owns 1 KiB of every row of a 64-token tile, each
+                 wave 128 bytes, two 16-byte loads per lane and token: laid
+                 out as MFMA A fragments (one instruction covers 16 rows x 64
+                 bytes, half of each line) or as whole lines (8 rows x 128
+                 bytes per instruction).
     Bytes are the bytes each probe must move (reads + writes)."""
     import ctypes
     from residual_stream_architecture_amd import build as b
@@ -170,6 +176,7 @@ def bandwidth_probes(torch):
     L.xhc_probe_stream.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
     L.xhc_probe_rows.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, vp, vp]
+    L.xhc_probe_frag.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
     T, row = 8192, 16 * 4096 * 2
     nbytes = T * row                                   # 1 GiB per buffer
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(3)]
@@ -210,6 +217,9 @@ def bandwidth_probes(torch):
                 lambda: L.xhc_probe_rows(a, bb, d, T, row, run, nr, nw, splits, sink.data_ptr(), st.cuda_stream),
                 (nr + nw) * nbytes)
             res[f"rows_{name}_run{run}"]["grid"] = (row // run) * splits
+    for mode, name in ((0, "frag_1r_mfma_layout"), (1, "frag_1r_whole_lines")):
+        res[name] = timed(lambda: L.xhc_probe_frag(a, T, 16, row // 16, mode, sink.data_ptr(), st.cuda_stream),
+                          nbytes)
     torch.cuda.synchronize()
     print(json.dumps({"probe": "hbm bandwidth of plain access patterns", "peak_GBps": HBM_PEAK_GBPS,
                       "results": res}), flush=True)

@@ -13,6 +13,16 @@
 //       its split of the tokens and walks the tokens -- the pattern of the
 //       backward's assembly kernel (two reads, one write) and of the
 //       projection (one read) with run_bytes per workgroup and row
+//   xhc_probe_frag(a, T, rows, row_bytes, mode)
+//       T tokens of `rows` rows of row_bytes (the state, [T][N][C]); each
+//       workgroup of 8 waves owns 1 KiB of every row of a 64-token tile, each
+//       wave 128 bytes of it, read one token at a time with two 16-byte loads
+//       per lane.  mode 0 lays the loads out as MFMA A fragments (lane
+//       (r = lane % 16, g = lane / 16) reads row r at 16 g and 64 + 16 g: one
+//       instruction touches 16 rows x 64 bytes, half of each 128-byte line);
+//       mode 1 reads the same bytes with every instruction covering 8 rows x
+//       128 bytes (whole lines).  The pattern of the backward's state dots
+//       and, with tokens for rows, of the projection.
 //
 // Workgroups are mapped to logical blocks XCD by XCD (as in libxhc), so that
 // the blocks running on one XCD cover neighbouring columns of the same
@@ -118,6 +128,51 @@ int launch_rows_run(int run, const u32x4* a, const u32x4* b, u32x4* d, int T, in
   }
 }
 
+constexpr int FRAG_WAVES = 8;
+constexpr int FRAG_TOK = 64;
+constexpr int FRAG_RING = 4;
+
+template <int MODE>
+__global__ __launch_bounds__(64 * FRAG_WAVES) void k_frag(const unsigned char* __restrict__ a, int T, int rows,
+                                                         int row_bytes, int ncb, unsigned* __restrict__ sink) {
+  const int lb = xcd_block(blockIdx.x, gridDim.x);
+  const int cb = lb % ncb;
+  const int tile = lb / ncb;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = tile * FRAG_TOK;
+  const int tn = T - t0 < FRAG_TOK ? T - t0 : FRAG_TOK;
+  const int64_t tokb = (int64_t)rows * row_bytes;
+  const int base = cb * 1024 + wave * 128;
+  int off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int row, col;
+    if (MODE == 0) { row = lane & 15; col = 64 * i + 16 * (lane >> 4); }
+    else { row = 8 * i + (lane >> 3); col = 16 * (lane & 7); }
+    off[i] = (row < rows ? row : 0) * row_bytes + base + col;
+  }
+  unsigned acc = 0;
+  u32x4 v[FRAG_RING][2];
+  auto load = [&](int tt, int q) {
+    const int tc = tt < tn ? tt : tn - 1;
+    const unsigned char* p = a + (int64_t)(t0 + tc) * tokb;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) v[q][i] = *reinterpret_cast<const u32x4*>(p + off[i]);
+  };
+#pragma unroll
+  for (int q = 0; q < FRAG_RING - 1; ++q) load(q, q);
+  for (int tt = 0; tt < tn; tt += FRAG_RING) {
+#pragma unroll
+    for (int u = 0; u < FRAG_RING; ++u) {
+      load(tt + u + FRAG_RING - 1, (u + FRAG_RING - 1) % FRAG_RING);
+      if (tt + u < tn)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc ^= v[u][i][0] ^ v[u][i][1] ^ v[u][i][2] ^ v[u][i][3];
+    }
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -164,6 +219,20 @@ int xhc_probe_rows(const void* a, const void* b, void* d, int T, int row_bytes, 
   else if (!nwrite) rc = launch_rows_run<2, 0>(run_bytes, pa, pb, pd, T, row16, ncol, tps, (int)nblk, sink, st);
   else rc = launch_rows_run<2, 1>(run_bytes, pa, pb, pd, T, row16, ncol, tps, (int)nblk, sink, st);
   if (rc) return rc;
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// T tokens of `rows` (<= 16) rows of row_bytes (a multiple of 1024) each;
+// grid = row_bytes / 1024 column blocks x ceil(T / 64) token tiles.
+int xhc_probe_frag(const void* a, int T, int rows, int row_bytes, int mode, unsigned* sink, hipStream_t st) {
+  if (!a || T < 1 || rows < 1 || rows > 16 || row_bytes < 1024 || (row_bytes % 1024) || !sink) return -1;
+  if (mode != 0 && mode != 1) return -1;
+  const int ncb = row_bytes / 1024;
+  const int64_t nblk = (int64_t)ncb * ((T + FRAG_TOK - 1) / FRAG_TOK);
+  if (nblk > (1 << 30)) return -1;
+  const unsigned char* pa = static_cast<const unsigned char*>(a);
+  if (mode == 0) k_frag<0><<<(int)nblk, 64 * FRAG_WAVES, 0, st>>>(pa, T, rows, row_bytes, ncb, sink);
+  else k_frag<1><<<(int)nblk, 64 * FRAG_WAVES, 0, st>>>(pa, T, rows, row_bytes, ncb, sink);
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
