@@ -87,16 +87,33 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
   // B2's projection operand: this workgroup's slice of W -> Wp [NC][64]
   // (zero padded past P; with a router columns 48.. hold W_route); nothing
   // reads it before B2
+  // Each thread's PK elements are loaded together (clamped, always valid
+  // addresses) before any is stored: one memory latency per PK elements
+  // instead of one per element at the start of every workgroup.
   {
+    constexpr int PK = 8;
     const int64_t nwp = NC * 64;
     const int64_t per = (nwp + gridDim.x - 1) / gridDim.x;
     const int64_t beg = (int64_t)lb * per, end = min(beg + per, nwp);
-    for (int64_t idx = beg + threadIdx.x; idx < end; idx += 64 * BX_WAVES) {
-      const int64_t j = idx >> 6;
-      const int pp = (int)(idx & 63);
-      R v = pp < P ? W[(size_t)j * P + pp] : R(0);
-      if (ROUTE && pp >= 48) v = (Wr && pp - 48 < N) ? Wr[(size_t)j * N + (pp - 48)] : R(0);
-      Wp[idx] = v;
+    for (int64_t i0 = beg + threadIdx.x; i0 < end; i0 += (int64_t)64 * BX_WAVES * PK) {
+      R w[PK], wr[PK];
+#pragma unroll
+      for (int u = 0; u < PK; ++u) {
+        const int64_t idx = i0 + (int64_t)u * 64 * BX_WAVES;
+        const int64_t j = min(idx >> 6, NC - 1);
+        const int pp = (int)(idx & 63);
+        w[u] = W[(size_t)j * P + min(pp, P - 1)];
+        // (given per-token lists run this path without a router: no W_route)
+        if constexpr (ROUTE) wr[u] = Wr ? Wr[(size_t)j * N + min(max(pp - 48, 0), N - 1)] : R(0);
+      }
+#pragma unroll
+      for (int u = 0; u < PK; ++u) {
+        const int64_t idx = i0 + (int64_t)u * 64 * BX_WAVES;
+        const int pp = (int)(idx & 63);
+        R x = pp < P ? w[u] : R(0);
+        if (ROUTE && pp >= 48) x = pp - 48 < N ? wr[u] : R(0);
+        if (idx < end) Wp[idx] = x;
+      }
     }
   }
   if constexpr (ROUTE) {
@@ -139,8 +156,10 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
   }
 
   V8<E> av[RING][2], bv[RING][2];
-  // token t0 + tt (clamped to the tile) -> ring slot q; channels past C are
-  // zeroed in A so that they add nothing
+  // token t0 + tt (clamped to the tile) -> ring slot q.  The ring holds the
+  // loads as they arrive: channels past C are zeroed in A at the MFMA, not
+  // here, since a select on a prefetched value would make the loop wait
+  // for it where the ring is carried to the next group
   auto load = [&](int tt, int q) {
     const int ttc = min(tt, tn - 1);
     const int64_t t = t0 + ttc;
@@ -160,34 +179,55 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const V8<E> x = V8<E>::load(ab, (size_t)(ao + cofs[ks]));
-      av[q][ks] = kv[ks] ? x : V8<E>::zero();
+      av[q][ks] = V8<E>::load(ab, (size_t)(ao + cofs[ks]));
       bv[q][ks] = V8<E>::load(bbase, (size_t)(t * bstr + bo + cofs[ks]));
     }
   };
 
+  // this thread's entry of the cross-wave sums: D[i][0] = dH_pre[i] for
+  // o < 16, D[i_b][1 + a] = dH_res[a][b] after (fixed lists: formed here
+  // once -- indexing the by-value list with a run-time index reads the
+  // kernel arguments from memory, and that load's wait in the loop would
+  // also wait for the whole prefetch ring)
+  int red_idx = -1;
+  {
+    const int o = threadIdx.x % BX_OUT;
+    if (o < 16) {
+      red_idx = o < N ? o : -1;
+    } else if (!ROUTE) {
+      const int a = (o - 16) >> 2, b = (o - 16) & 3;
+      int ib = act.id[0];
+#pragma unroll
+      for (int bb = 1; bb < 4; ++bb)
+        if (b == bb) ib = act.id[bb];
+      red_idx = (a < k && b < k) ? (1 + a) * 16 + ib : -1;
+    }
+  }
 #pragma unroll
   for (int q = 0; q < RING - 1; ++q) load(q, q);
-  for (int tg = 0; tg < tn; tg += BX_GRP) {
+  // every group of the tile runs (a short last tile works on copies of its
+  // last token, whose sums are not written out), fully unrolled: at the head
+  // of a loop the compiler cannot tell which ring slot each outstanding load
+  // fills and waits for all of them, which drained the ring once per group
+#pragma unroll
+  for (int tg = 0; tg < BX_TOK; tg += BX_GRP) {
 #pragma unroll
     for (int u = 0; u < BX_GRP; ++u) {
       const int q = u % RING;
       load(tg + u + RING - 1, (u + RING - 1) % RING);
       f32x4 d = {0.f, 0.f, 0.f, 0.f};
-      d = mma32(av[q][0], bv[q][0], d);
-      d = mma32(av[q][1], bv[q][1], d);
+      d = mma32(kv[0] ? av[q][0] : V8<E>::zero(), bv[q][0], d);
+      d = mma32(kv[1] ? av[q][1] : V8<E>::zero(), bv[q][1], d);
       // lane (r, g) holds D[4g + e][r]: column r, rows 4g..4g+3
       if (r <= 4) *reinterpret_cast<f32x4*>(&red[u][wave][r * 16 + 4 * g]) = d;
     }
     __syncthreads();
     if (threadIdx.x < BX_GRP * BX_OUT) {
       const int u = threadIdx.x / BX_OUT, o = threadIdx.x % BX_OUT;
-      int idx = -1;
-      if (o < 16) {
-        idx = o < N ? o : -1;                                  // D[i][0]
-      } else {
+      int idx = red_idx;
+      if (ROUTE && o >= 16) {
         const int a = (o - 16) >> 2, b = (o - 16) & 3;
-        if (a < k && b < k) idx = (1 + a) * 16 + (ROUTE ? tid_s[tg + u][b] : act.id[b]);   // D[i_b][1 + a]
+        idx = (a < k && b < k) ? (1 + a) * 16 + tid_s[tg + u][b] : -1;   // D[i_b][1 + a]
       }
       float sum = 0.f;
       if (idx >= 0) {
@@ -1203,7 +1243,9 @@ __device__ __forceinline__ void bgrad_body(
       load_ids(tn + STEP);
     }
     res_t0 = t0;
-    __syncthreads();
+    // the published rows and this step's copies (waited above) are visible
+    // to every wave; the next step's copies and loads stay in flight
+    lds_barrier();
 #pragma unroll
     for (int s = 0; s < B2_SUB; ++s) {
       __builtin_amdgcn_sched_barrier(0);      // keep the tiles' live ranges apart
@@ -1357,7 +1399,7 @@ __device__ __forceinline__ void bgrad_body(
         }
       }
     }
-    __syncthreads();          // every read of this step's buffers and row tiles is done
+    lds_barrier();            // every read of this step's buffers and row tiles is done
     buf ^= 1;
   }
   store_res();

@@ -144,6 +144,20 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
 }
 
+// Workgroup barrier for data the waves exchange through LDS.  It waits for
+// this wave's own LDS accesses (lgkmcnt) and nothing else, then meets the
+// other waves.  __syncthreads() also waits for every global load this wave
+// has in flight: its fence counts an LDS-DMA copy as an LDS write, and
+// copies and loads share one counter, so a prefetch issued before it would
+// land before the barrier instead of behind the work that follows.  Copies
+// that the other side of the barrier reads must be waited for explicitly
+// (wait_vmcnt) before calling this.  The memory clobber keeps the compiler
+// from moving memory accesses across the barrier.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0); vmcnt and expcnt left alone (gfx9 encoding)
+  asm volatile("s_barrier" ::: "memory");
+}
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // rows * row_bytes as a buffer size, saturated below 4 GiB
 __device__ inline uint32_t clamp_bytes(int rows, uint32_t row_bytes) {
