@@ -189,6 +189,7 @@ class Timer:
     """Per-kernel HIP-event timer (xhc_timer)."""
 
     def __init__(self):
+        self._lib = lib                  # kept: module globals may be gone when a timer dies at exit
         self.handle = lib.xhc_timer_create()
 
     def reset(self):
@@ -202,8 +203,8 @@ class Timer:
         return ms.value, n.value
 
     def __del__(self):
-        if getattr(self, "handle", None):
-            lib.xhc_timer_destroy(self.handle)
+        if getattr(self, "handle", None) and getattr(self, "_lib", None) is not None:
+            self._lib.xhc_timer_destroy(self.handle)
             self.handle = None
 
 
