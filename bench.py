@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-chain", action="store_true",
                     help="stacked workloads: project every sublayer's state in its own pass instead of "
                          "carrying the projection from the previous sublayer's write pass")
+    ap.add_argument("--split", action="store_true",
+                    help="fwd+bwd: build the step from the split calls (xhc_forward_pre, xhc_forward_post, "
+                         "xhc_backward_post, xhc_backward_pre) instead of xhc_forward and xhc_backward")
     ap.add_argument("--graph", action="store_true",
                     help="fwd+bwd: capture one step in a HIP graph (torch.cuda.CUDAGraph) and time its replays")
     ap.add_argument("--copy-probe", action="store_true",
@@ -441,6 +444,22 @@ def main():
         xhc.backward(X, out, W, active, dXn, dhin, dX, dout, dW, B=w.B, S=w.S, bias=bias,
                      z_save=z_save, db=db, workspace=ws_b, timer=timer, desc=desc, **convs, **dws, **bwd_kw)
 
+    if args.split:
+        # the same step from the split calls: the sublayer's output and dh_in
+        # stand ready (synthetic), so the calls run back to back
+        if rt or w.gs:
+            raise SystemExit("--split: not with the router or Gram-Schmidt (the split calls refuse them)")
+        bwd_state = torch.empty(xhc.bwd_state_size(desc) // 4, dtype=torch.float32, device="cuda")
+
+        def step(timer=None):
+            xhc.forward_pre(X, W, active, h_in, z_save, desc=desc, bias=bias, workspace=ws_f, timer=timer)
+            xhc.forward_post(X, out, active, z_save, desc=desc, xact_save=xact, workspace=ws_f, timer=timer,
+                             **convs)
+            xhc.backward_post(out, active, z_save, dXn, dout, bwd_state, desc=desc, workspace=ws_b, timer=timer,
+                              **convs, **dws)
+            xhc.backward_pre(X, W, active, z_save, dXn, dhin, bwd_state, dX, dW, desc=desc, xact=xact, bias=bias,
+                             db=db, workspace=ws_b, timer=timer)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -481,6 +500,8 @@ def main():
             step(timer)
         torch.cuda.synchronize()
         kb = kernel_bytes(w, esz)
+        if args.split:
+            kb.pop("mixproj", None)      # the pre and post passes move different bytes under one name
         for name in xhc.kernel_names():
             ms, n = timer.read(name)
             if n:
@@ -539,7 +560,8 @@ def main():
         "config": {"workload": f"xHC sublayer fwd+bwd ({w.name}): B={w.B} S={w.S} C={C} N={N} k={k} "
                                f"TFA K=4/8/12{', Gram-Schmidt' if w.gs else ''}, 20 Sinkhorn iters, "
                                + (f"router: {k - rt} fixed + {rt} routed streams per token, " if rt else "")
-                               + "in-place forward + backward",
+                               + ("split calls (forward pre, post; backward post, pre)" if args.split
+                                  else "in-place forward + backward"),
                    "global_batch": w.B, "seq_len": w.S},
         "step_hbm": step_hbm,
         "kernels": kernels,

@@ -82,3 +82,68 @@ def test_forward_backward_graph_replays_match_eager(gs, route):
     for key in eager:
         assert torch.equal(other[key], eager[key]), key
     assert np.isfinite(eager["dW"].cpu().numpy()).all()
+
+
+def test_split_calls_graph_replays_match_eager():
+    """The split forward and backward (pre, post; backward post, pre) captured
+    in one graph: the state is copied in first (a copy kernel), since the post
+    call rewrites it in place."""
+    w = synth.Workload("gs", 2, 96, 256, 16, 4, 4, "bf16", "fwdbwd")
+    say(f"[graph split] B={w.B} S={w.S} C={w.C}")
+    d = synth.make_inputs(w, seed=23, grads=True)
+    dev = device_inputs(d, True)
+    T, N, C, P = w.T, w.N, w.C, w.P
+    active = [1, 6, 11, 12]
+    desc = xhc.make_desc(w.B, w.S, C, N, 4, 4, xhc.XHC_BF16)
+    ws_f = torch.empty(xhc.workspace_size(desc, 0), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(xhc.workspace_size(desc, 1), dtype=torch.uint8, device="cuda")
+    conv = dict(w4=dev["w4"], w8=dev["w8"], w12=dev["w12"])
+
+    def buffers():
+        return dict(X=torch.empty_like(dev["X"]), h_in=torch.empty(T, C, dtype=torch.bfloat16, device="cuda"),
+                    z=torch.empty(T, xhc.zsave_stride(desc), device="cuda"),
+                    xact=torch.empty(T, 4, C, dtype=torch.bfloat16, device="cuda"),
+                    st=torch.empty(xhc.bwd_state_size(desc) // 4, device="cuda"), dX=torch.empty_like(dev["X"]),
+                    dout=torch.empty(T, C, dtype=torch.bfloat16, device="cuda"),
+                    dW=torch.empty(N * C, P, device="cuda"), db=torch.empty(P, device="cuda"),
+                    dw4=torch.empty(C, 4, device="cuda"), dw8=torch.empty(C, 8, device="cuda"),
+                    dw12=torch.empty(C, 12, device="cuda"))
+
+    def step(b):
+        b["X"].copy_(dev["X"])
+        xhc.forward_pre(b["X"], dev["W"], active, b["h_in"], b["z"], desc=desc, bias=dev["bias"], workspace=ws_f)
+        xhc.forward_post(b["X"], dev["out"], active, b["z"], desc=desc, xact_save=b["xact"], workspace=ws_f,
+                         **conv)
+        xhc.backward_post(dev["out"], active, b["z"], dev["dX_new"], b["dout"], b["st"], desc=desc, workspace=ws_b,
+                          dw4=b["dw4"], dw8=b["dw8"], dw12=b["dw12"], **conv)
+        xhc.backward_pre(b["X"], dev["W"], active, b["z"], dev["dX_new"], dev["dh_in"], b["st"], b["dX"], b["dW"],
+                         desc=desc, xact=b["xact"], bias=dev["bias"], db=b["db"], workspace=ws_b)
+
+    eager = buffers()
+    step(eager)
+    torch.cuda.synchronize()
+    static = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(static)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(static)
+    torch.cuda.synchronize()
+    other = buffers()
+    for rep in range(3):
+        for t in static.values():
+            t.zero_()
+        step(other)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key in eager:
+            if key == "st":
+                continue                    # the state's unused dot slots are never written
+            assert torch.equal(static[key], eager[key]), f"replay {rep}: {key} differs from the eager result"
+        say(f"  replay {rep} bitwise equal")
+    assert np.isfinite(eager["dW"].cpu().numpy()).all()
