@@ -215,7 +215,9 @@ def test_stack48_teacher_forced(chained):
     sublayer but the last carries them on).  Each layer is checked on
     sampled blocks, teacher-forced from the GPU's own state before it: the
     active rows and h_in within tolerance, the other rows bitwise, and the
-    saved logits and RMS (for a chained layer these come from the carry)."""
+    saved logits and RMS (for a chained layer these come from the carry).
+    The first, a middle and the last layer are checked on every token the
+    same way."""
     w = synth.WORKLOADS["stack48"]
     say(f"[fullsize] stack48 S={w.S} C={w.C} layers={w.layers} chained={chained}")
     t_start = time.time()
@@ -241,6 +243,8 @@ def test_stack48_teacher_forced(chained):
         for (_, s) in blocks:
             lo = max(0, s - LEAD)
             before[s] = to_host(X[lo:s + n])
+        full = layer in (0, w.layers // 2, w.layers - 1)
+        X_full = X.clone() if full else None
         extra = {}
         if chained:
             extra = dict(carry_in=carries[layer % 2] if layer > 0 else None,
@@ -264,6 +268,18 @@ def test_stack48_teacher_forced(chained):
             zs = to_host(z_save[s:s + n])
             check_close(f"L{layer} z[s={s}]", zs[:, :P], ref["z"][k0:], 1e-3, 1e-3)
             check_close(f"L{layer} r[s={s}]", zs[:, P], ref["r"][k0:], 1e-5, 1e-4)
+        if full:
+            inactive = [i for i in range(w.N) if i not in active]
+            assert torch.equal(X[:, inactive], X_full[:, inactive]), f"layer {layer}: pass-through"
+            ref = xo.forward(to_host(X_full), outh, hW, d["bias"], active, convs, B=1, S=w.S, iters=w.iters,
+                             eps=w.eps)
+            del X_full
+            check_close(f"L{layer} X_new[all]", to_host(X[:, active]), ref["X_new"][:, active], 1e-2, 1e-2)
+            check_close(f"L{layer} h_in[all]", to_host(h_in), ref["h_in"], 1e-2, 1e-2)
+            zs = to_host(z_save)
+            check_close(f"L{layer} z[all]", zs[:, :P], ref["z"], 1e-3, 1e-3)
+            check_close(f"L{layer} r[all]", zs[:, P], ref["r"], 1e-5, 1e-4)
+            del ref, zs
         say(f" layer {layer} ok at {time.time() - t_start:.1f}s")
         cur = nxt
 
