@@ -381,14 +381,15 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
         }
       }
     }
+    // new and saved rows are stored non-temporal, as in the mix kernel
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       if (a < k) {
         V8<E> nv;
         __builtin_memcpy(&nv, &nvw[a][0], sizeof(nv));
         const int row = row_of(ro, a);
-        bstore<E, 8>(nv, rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
-        if (xact) bstore<E, 8>(xs[a], rxs, lane_off(c, u, xsb), (uint32_t)a * rowb);
+        bstore<E, 8, CP_NT>(nv, rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
+        if (xact) bstore<E, 8, CP_NT>(xs[a], rxs, lane_off(c, u, xsb), (uint32_t)a * rowb);
         row_work(wact + a * wstride, u, c, co[row], xs[a], nv, true);
       }
     }
@@ -455,7 +456,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
 #pragma unroll
         for (int u = 0; u < KS; ++u) {
           row_work(wsl + j * SLOTB + u * NT * FB, u, c, hp, x[j][u], x[j][u], untouched);
-          if (MODE == MP_FULL && !in_place) bstore<E, 8>(x[j][u], rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
+          if (MODE == MP_FULL && !in_place) bstore<E, 8, CP_NT>(x[j][u], rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
         }
       }
     }

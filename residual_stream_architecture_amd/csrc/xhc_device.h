@@ -204,28 +204,35 @@ __device__ inline Vec<E, W> bload(rsrc_t r, uint32_t voff, uint32_t soff) {
   return v;
 }
 
-template <typename E, int W>
+// Cache policy of a buffer store: CP_NT marks the line non-temporal (the
+// store streams to memory instead of sitting dirty in the caches).  It pays
+// where each instruction writes whole 128-byte lines that no later kernel of
+// the pass reads soon; a line written in halves by two waves is slower.
+constexpr int CP_DEFAULT = 0;
+constexpr int CP_NT = 2;
+
+template <typename E, int W, int CP = CP_DEFAULT>
 __device__ inline void bstore(const Vec<E, W>& v, rsrc_t r, uint32_t voff, uint32_t soff) {
   constexpr int B = W * E::bytes;
   if constexpr (B == 4) {
     unsigned x;
     __builtin_memcpy(&x, &v, 4);
-    __builtin_amdgcn_raw_buffer_store_b32(x, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(x, r, voff, soff, CP);
   } else if constexpr (B == 8) {
     u32x2 x;
     __builtin_memcpy(&x, &v, 8);
-    __builtin_amdgcn_raw_buffer_store_b64(x, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(x, r, voff, soff, CP);
   } else if constexpr (B == 16) {
     u32x4 x;
     __builtin_memcpy(&x, &v, 16);
-    __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, CP);
   } else {
     static_assert(B == 32, "vector width");
     u32x4 x0, x1;
     __builtin_memcpy(&x0, &v, 16);
     __builtin_memcpy(&x1, reinterpret_cast<const char*>(&v) + 16, 16);
-    __builtin_amdgcn_raw_buffer_store_b128(x0, r, voff, soff, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(x1, r, voff + 16, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(x0, r, voff, soff, CP);
+    __builtin_amdgcn_raw_buffer_store_b128(x1, r, voff + 16, soff, CP);
   }
 }
 

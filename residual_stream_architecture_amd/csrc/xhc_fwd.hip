@@ -668,6 +668,9 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
         u[1][ch] = s4; u[2][ch] = s8; u[3][ch] = s12;
       }
     }
+    // The state rows (new, copied, saved) are stored non-temporal: a wave
+    // writes whole lines of them, and their next reader is a later pass.
+    // h_in keeps the default policy, as the sublayer reads it next.
     if (cv) {
       float xa[4][MIX_CH];
 #pragma unroll
@@ -689,8 +692,8 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
             for (int m = 0; m < NCOMP; ++m) v = fmaf(cpost[a * 4 + m], u[m][ch], v);
             res[ch] = v;
           }
-          bstore<E, MIX_CH>(V::from_float(res), rxn, voff, (uint32_t)cid[a] * rowb);
-          if (xact) bstore<E, MIX_CH>(cxa[a], rxs, voff, (uint32_t)a * rowb);
+          bstore<E, MIX_CH, CP_NT>(V::from_float(res), rxn, voff, (uint32_t)cid[a] * rowb);
+          if (xact) bstore<E, MIX_CH, CP_NT>(cxa[a], rxs, voff, (uint32_t)a * rowb);
         }
       }
       if (!in_place) {                             // out of place: copy the untouched rows
@@ -700,7 +703,7 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
             bool is_act = false;
 #pragma unroll
             for (int b = 0; b < 4; ++b) is_act |= (b < K && i == cid[b]);
-            if (!is_act) bstore<E, MIX_CH>(cx[i], rxn, voff, (uint32_t)i * rowb);
+            if (!is_act) bstore<E, MIX_CH, CP_NT>(cx[i], rxn, voff, (uint32_t)i * rowb);
           }
         }
       }
