@@ -960,12 +960,15 @@ __global__ __launch_bounds__(16 * BCOEF_TOK) void k_bcoef(const float* __restric
 
 // ---------------------------------------------------------------------------
 // B2.  Workgroup = (row group, B2_CB = 64 channels, token split), 8 waves:
-// wave w handles row w%4 of the group on channel half w/4, so the two halves
-// of every 128-byte line of a bf16 row are read by two waves of one
-// workgroup in the same tile.  Per tile of B2_TT = 16 tokens:
+// wave w computes row w%4 of the group on channel half w/4.  Its loads and
+// stores instead cover token half w/4 of the tile in whole 128-byte lines
+// (both channel halves), exchanged with the other wave of the row through
+// the LDS row tiles: an instruction that reads or writes half lines, the
+// other half coming from another wave, moves HBM data markedly slower.
+// Per tile of B2_TT = 16 tokens:
 //   proj[c][t] = sum_p W[i*C+c, p] dz_r[t, p] on MFMA (dz/r as bf16 hi + lo),
 //   with A rows permuted so that lane (t = lane%16, g = lane/16) ends up
-//   owning channels 8g..8g+8 of token t -- the layout of its own loads;
+//   owning channels 8g..8g+8 of token t -- the layout of its row tile slots;
 //   dX = pass + H_pre dh_in + proj - X gamma;
 //   dW[i*C+c][p] += sum_t X[t, c] dz_r[t, p] on MFMA (K = the tile's tokens,
 //   A = X^T through LDS).
@@ -975,7 +978,8 @@ __global__ __launch_bounds__(16 * BCOEF_TOK) void k_bcoef(const float* __restric
 // prefetches its own state, dX_new and dh_in pieces one tile ahead.  A
 // tile's dX is stored at the start of the next iteration, ahead of that
 // iteration's prefetch, so the wait at the top of the loop never waits on a
-// store issued after the loads it needs.  The active rows' upstream
+// store issued after the loads it needs (the routed form stores the first
+// tile of a step as soon as it is done).  The active rows' upstream
 // gradients G_a are exchanged through LDS; all of a tile's rows are read (a
 // tile earlier) before any is written, so dX may alias dX_new.
 // ROUTE: the active rows differ per token, so the row groups are simply
@@ -1131,11 +1135,24 @@ __device__ __forceinline__ void bgrad_body(
     }
   };
   // own rows of the B2_SUB tiles from t0, through buffer resources based at
-  // each tile (tokens past the end read zeros)
+  // each tile (tokens past the end read zeros).  Without the router, the two
+  // waves of a row split its tile by tokens rather than by channel halves
+  // when loading, so that every load instruction covers whole lines: lane
+  // (token lt = 8 chalf + lane/8, piece lp = lane%8) reads channels
+  // cb*B2_CB + 8 lp .. + 8 and publishes them into the row tile of the wave
+  // that owns that half, at that wave's slot for (token lt, group lp%4).
+  // The routed form loads each lane's own slot (its rows differ per token).
   V8<E> xo[B2_SUB], dvo[B2_SUB];
   const uint32_t xrowb = (uint32_t)xstride * EB;
-  const uint32_t vx = ((uint32_t)r16 * (uint32_t)xstride + clc) * EB;
-  const uint32_t vd = (((uint32_t)r16 * N + srow) * (uint32_t)C + clc) * EB;
+  const int lt = ROUTE ? r16 : 8 * chalf + (lane >> 3);
+  const int lp = lane & 7;
+  const int lc = ROUTE ? cl : cb * B2_CB + 8 * lp;
+  const bool lcv = wv && lc < C;
+  const int lcc = lcv ? lc : 0;
+  const int pubw = ROUTE ? wave : slot + 4 * (lp >> 2);
+  const int puboff = ROUTE ? g4 * LY::GSTRIDE + r16 * 8 * EB : (lp & 3) * LY::GSTRIDE + lt * 8 * EB;
+  const uint32_t vx = ((uint32_t)lt * (uint32_t)xstride + lcc) * EB;
+  const uint32_t vd = (((uint32_t)lt * N + srow) * (uint32_t)C + lcc) * EB;
   // ROUTE: this lane's tokens' active lists for the step loaded next, and
   // from them the slot of this lane's stream (-1: not active).  The slots
   // are formed right after the top-of-step wait, before any memory operation
@@ -1208,15 +1225,31 @@ __device__ __forceinline__ void bgrad_body(
   };
   // dX of finished tiles, by buffer stores based at each tile: an
   // out-of-range offset (ragged token or channel tail, or no tile yet) is
-  // dropped by the hardware.  The last tile of a step is stored at the top
-  // of the next step, ahead of its prefetch.
+  // dropped by the hardware.
+  // Without the router, a tile's dX goes out in whole lines, in the load
+  // mapping: each wave leaves its dX in its own X row tile (the tile's dW
+  // runs first, so the X values are no longer needed), and after the step's closing barrier each lane stores
+  // the piece (token lt, piece lp) it loaded, both tiles at the top of the
+  // next step, ahead of the prefetch.  It reads them before it publishes
+  // the next rows into the same places (the other wave of the row writes
+  // only the other token half).  The whole-line stores are non-temporal:
+  // dX is not read again in the pass.
+  // With the router, the last tile of a step is stored at the top of the
+  // next step from registers (res) and the first one as soon as it is done.
   V8<E> res = V8<E>::zero();
   uint32_t res_off = 0x80000000u;
   int res_t0 = 0;
   auto store_res = [&]() {
-    const rsrc_t rdx =
-        make_rsrc(static_cast<char*>(dX) + (size_t)(res_t0 + (B2_SUB - 1) * B2_TT) * tokb, (uint32_t)B2_TT * tokb);
-    bstore<E, 8>(res, rdx, res_off, 0);
+    if constexpr (ROUTE) {
+      const rsrc_t rdx =
+          make_rsrc(static_cast<char*>(dX) + (size_t)(res_t0 + (B2_SUB - 1) * B2_TT) * tokb, (uint32_t)B2_TT * tokb);
+      bstore<E, 8>(res, rdx, res_off, 0);
+    }
+  };
+  auto staged = [&](int s) { return *reinterpret_cast<const V8<E>*>(&xsh[s][pubw][puboff]); };
+  auto store_staged = [&](const V8<E>& v, int ta, bool have) {
+    const rsrc_t rdx = make_rsrc(static_cast<char*>(dX) + (size_t)ta * tokb, (uint32_t)B2_TT * tokb);
+    bstore<E, 8, CP_NT>(v, rdx, (have && ta + lt < T && lcv) ? vd : 0x80000000u, 0);
   };
   const int rowoff = g4 * LY::GSTRIDE + r16 * 8 * EB;      // this lane's slot in a row tile
 
@@ -1228,18 +1261,23 @@ __device__ __forceinline__ void bgrad_body(
     load_ids(tbeg + STEP);
   }
   int buf = 0;
+  int last_t0 = tbeg;
   for (int t0 = tbeg; t0 < tfin; t0 += STEP) {
     // these tiles' copies and own loads (issued one iteration ago) have
     // landed; the other waves' copies are covered by the barrier below
     wait_vmcnt<0>();
     form_slots();                    // (the next step's lists landed with them)
     // publish the own rows (zero outside the sequence or the channels), which
-    // frees their registers for the next prefetch
+    // frees their registers for the next prefetch; without the router, each
+    // tile's place first gives up the previous step's staged dX
 #pragma unroll
     for (int s = 0; s < B2_SUB; ++s) {
-      const bool ok = t0 + s * B2_TT + r16 < T && cv;
-      *reinterpret_cast<V8<E>*>(&xsh[s][wave][rowoff]) = ok ? xo[s] : V8<E>::zero();
-      *reinterpret_cast<V8<E>*>(&gsh[s][wave][rowoff]) = ok ? dvo[s] : V8<E>::zero();
+      V8<E> d;
+      if constexpr (!ROUTE) d = staged(s);
+      const bool ok = t0 + s * B2_TT + lt < T && lcv;
+      *reinterpret_cast<V8<E>*>(&xsh[s][pubw][puboff]) = ok ? xo[s] : V8<E>::zero();
+      *reinterpret_cast<V8<E>*>(&gsh[s][pubw][puboff]) = ok ? dvo[s] : V8<E>::zero();
+      if constexpr (!ROUTE) store_staged(d, t0 - STEP + s * B2_TT, t0 > tbeg);
     }
     store_res();
     {
@@ -1261,6 +1299,39 @@ __device__ __forceinline__ void bgrad_body(
       const bool tv = tk < T;
       const unsigned char* rb = rbuf[buf][s];
 
+      // ---- dW on MFMA: A = X^T (rows = channels, K = 16 tokens) ----
+      {
+        Vec<E, 4> bh[NPT], bl[NPT];
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) {
+          const int off = RDZRT + ((pt * 4 + g4) * 16 + r16) * 4 * EB;
+          bh[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off);
+          if constexpr (BF) bl[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off + NPT * 4 * 16 * 4 * EB);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          // channel cc = 16*jt + r16 of tokens 4*g4 .. 4*g4+3: entry [cc/8][t], element cc%8
+          const int cc = 16 * jt + r16;
+          const unsigned char* colp = &xsh[s][wave][(cc >> 3) * LY::GSTRIDE + (cc & 7) * EB];
+          Vec<E, 4> xa;
+          if constexpr (BF) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const unsigned lo16 = *reinterpret_cast<const uint16_t*>(colp + (4 * g4 + 2 * q) * 8 * EB);
+              const unsigned hi16 = *reinterpret_cast<const uint16_t*>(colp + (4 * g4 + 2 * q + 1) * 8 * EB);
+              xa.w[q] = lo16 | (hi16 << 16);
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xa.x[q] = *reinterpret_cast<const float*>(colp + (4 * g4 + q) * 8 * EB);
+          }
+#pragma unroll
+          for (int pt = 0; pt < NPT; ++pt) {
+            dwacc[jt][pt] = mma16(xa, bh[pt], dwacc[jt][pt]);
+            if constexpr (BF) dwacc[jt][pt] = mma16(xa, bl[pt], dwacc[jt][pt]);
+          }
+        }
+      }
       // ---- proj on MFMA: D[c][t], 2 j-tiles; K = 48 logits as 32 + 16 ----
       f32x4 pj[2];
       if constexpr (ROUTE) {
@@ -1362,55 +1433,37 @@ __device__ __forceinline__ void bgrad_body(
           o[q] = v;
         }
         const V8<E> ov = V8<E>::from_float(o);
-        const uint32_t off = (tv && cv) ? ((uint32_t)r16 * N + srow) * (uint32_t)C * EB + cl * EB : 0x80000000u;
-        if (s + 1 < B2_SUB) {
-          // stored now: it completes well before the next top-of-loop wait
-          const rsrc_t rdx =
-              make_rsrc(static_cast<char*>(dX) + (size_t)(t0 + s * B2_TT) * tokb, (uint32_t)B2_TT * tokb);
-          bstore<E, 8>(ov, rdx, off, 0);
-        } else {
-          res = ov;          // the last tile's store is issued at the top of the next step
-          res_off = off;
-        }
-      }
-      // ---- dW on MFMA: A = X^T (rows = channels, K = 16 tokens) ----
-      {
-        Vec<E, 4> bh[NPT], bl[NPT];
-#pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) {
-          const int off = RDZRT + ((pt * 4 + g4) * 16 + r16) * 4 * EB;
-          bh[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off);
-          if constexpr (BF) bl[pt] = *reinterpret_cast<const Vec<E, 4>*>(rb + off + NPT * 4 * 16 * 4 * EB);
-        }
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          // channel cc = 16*jt + r16 of tokens 4*g4 .. 4*g4+3: entry [cc/8][t], element cc%8
-          const int cc = 16 * jt + r16;
-          const unsigned char* colp = &xsh[s][wave][(cc >> 3) * LY::GSTRIDE + (cc & 7) * EB];
-          Vec<E, 4> xa;
-          if constexpr (BF) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const unsigned lo16 = *reinterpret_cast<const uint16_t*>(colp + (4 * g4 + 2 * q) * 8 * EB);
-              const unsigned hi16 = *reinterpret_cast<const uint16_t*>(colp + (4 * g4 + 2 * q + 1) * 8 * EB);
-              xa.w[q] = lo16 | (hi16 << 16);
-            }
+        if constexpr (ROUTE) {
+          const uint32_t off = (tv && cv) ? ((uint32_t)r16 * N + srow) * (uint32_t)C * EB + cl * EB : 0x80000000u;
+          if (s + 1 < B2_SUB) {
+            // stored now: it completes well before the next top-of-loop wait
+            const rsrc_t rdx =
+                make_rsrc(static_cast<char*>(dX) + (size_t)(t0 + s * B2_TT) * tokb, (uint32_t)B2_TT * tokb);
+            bstore<E, 8>(ov, rdx, off, 0);
           } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) xa.x[q] = *reinterpret_cast<const float*>(colp + (4 * g4 + q) * 8 * EB);
+            res = ov;          // the last tile's store is issued at the top of the next step
+            res_off = off;
           }
-#pragma unroll
-          for (int pt = 0; pt < NPT; ++pt) {
-            dwacc[jt][pt] = mma16(xa, bh[pt], dwacc[jt][pt]);
-            if constexpr (BF) dwacc[jt][pt] = mma16(xa, bl[pt], dwacc[jt][pt]);
-          }
+        } else {
+          // staged in this wave's X row tile, over the value just read (the
+          // tile's dW, above, has read the rest of it)
+          *reinterpret_cast<V8<E>*>(&xsh[s][wave][rowoff]) = ov;
         }
       }
     }
-    lds_barrier();            // every read of this step's buffers and row tiles is done
+    // every read of this step's buffers and row tiles is done, and the staged
+    // dX is visible to the other wave of the row
+    lds_barrier();
     buf ^= 1;
+    last_t0 = t0;
   }
   store_res();
+  if constexpr (!ROUTE) {
+    if (tbeg < tfin) {
+#pragma unroll
+      for (int s = 0; s < B2_SUB; ++s) store_staged(staged(s), last_t0 + s * B2_TT, true);
+    }
+  }
   // dW partial rows: D row 4*g4+e of j-tile jt = channel 16*jt + 4*g4 + e
   if (wv) {
 #pragma unroll
