@@ -1135,7 +1135,8 @@ __device__ __forceinline__ void bgrad_body(
     }
   };
   // own rows of the B2_SUB tiles from t0, through buffer resources based at
-  // each tile (tokens past the end read zeros).  Without the router, the two
+  // each tile (tokens past the end read zeros).  These are the pass's last
+  // reads of the state and of dX_new: non-temporal.  Without the router, the two
   // waves of a row split its tile by tokens rather than by channel halves
   // when loading, so that every load instruction covers whole lines: lane
   // (token lt = 8 chalf + lane/8, piece lp = lane%8) reads channels
@@ -1201,7 +1202,7 @@ __device__ __forceinline__ void bgrad_body(
       const int left = ta < T ? T - ta : 0;
       const rsrc_t rx = make_rsrc(static_cast<const char*>(xbase) + (size_t)ta * xrowb, clamp_bytes(left, xrowb));
       const rsrc_t rd = make_rsrc(static_cast<const char*>(dXn) + (size_t)ta * tokb, clamp_bytes(left, tokb));
-      if (!ROUTE) xo[s] = bload<E, 8>(rx, vx, 0);
+      if (!ROUTE) xo[s] = bload<E, 8, CP_NT>(rx, vx, 0);
       if constexpr (ROUTE) {
         // the slot of this lane's stream in its token's list (-1: not
         // active) picks the row: pass[t][slot] or dX_new[t][stream], read
@@ -1219,7 +1220,7 @@ __device__ __forceinline__ void bgrad_body(
             : static_cast<const char*>(xbase) + (tk * (size_t)xstride + clc) * EB;
         xo[s] = V8<E>::load(x_row, 0);
       } else {
-        dvo[s] = bload<E, 8>(rd, vd, 0);
+        dvo[s] = bload<E, 8, CP_NT>(rd, vd, 0);
       }
     }
   };

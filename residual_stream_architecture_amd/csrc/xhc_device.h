@@ -181,35 +181,35 @@ __device__ inline rsrc_t make_rsrc_u(const void* base, uint32_t bytes) {
   return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), n);
 }
 
-template <typename E, int W>
-__device__ inline Vec<E, W> bload(rsrc_t r, uint32_t voff, uint32_t soff) {
-  constexpr int B = W * E::bytes;
-  Vec<E, W> v;
-  if constexpr (B == 4) {
-    const unsigned x = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-    __builtin_memcpy(&v, &x, 4);
-  } else if constexpr (B == 8) {
-    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-    __builtin_memcpy(&v, &x, 8);
-  } else if constexpr (B == 16) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    __builtin_memcpy(&v, &x, 16);
-  } else {
-    static_assert(B == 32, "vector width");
-    const u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    const u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, 0);
-    __builtin_memcpy(&v, &x0, 16);
-    __builtin_memcpy(reinterpret_cast<char*>(&v) + 16, &x1, 16);
-  }
-  return v;
-}
-
-// Cache policy of a buffer store: CP_NT marks the line non-temporal (the
+// Cache policy of a buffer access: CP_NT marks the line non-temporal (the
 // store streams to memory instead of sitting dirty in the caches).  It pays
 // where each instruction writes whole 128-byte lines that no later kernel of
 // the pass reads soon; a line written in halves by two waves is slower.
 constexpr int CP_DEFAULT = 0;
 constexpr int CP_NT = 2;
+
+template <typename E, int W, int CP = CP_DEFAULT>
+__device__ inline Vec<E, W> bload(rsrc_t r, uint32_t voff, uint32_t soff) {
+  constexpr int B = W * E::bytes;
+  Vec<E, W> v;
+  if constexpr (B == 4) {
+    const unsigned x = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, CP);
+    __builtin_memcpy(&v, &x, 4);
+  } else if constexpr (B == 8) {
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, CP);
+    __builtin_memcpy(&v, &x, 8);
+  } else if constexpr (B == 16) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, CP);
+    __builtin_memcpy(&v, &x, 16);
+  } else {
+    static_assert(B == 32, "vector width");
+    const u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, CP);
+    const u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, CP);
+    __builtin_memcpy(&v, &x0, 16);
+    __builtin_memcpy(reinterpret_cast<char*>(&v) + 16, &x1, 16);
+  }
+  return v;
+}
 
 template <typename E, int W, int CP = CP_DEFAULT>
 __device__ inline void bstore(const Vec<E, W>& v, rsrc_t r, uint32_t voff, uint32_t soff) {

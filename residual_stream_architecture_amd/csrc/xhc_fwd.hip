@@ -580,13 +580,15 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
     }
   };
   // prefetch buffers: the 16 state rows, the k active rows and the out row
-  // of the next token (one buffer resource per token: offsets stay small)
+  // of the next token (one buffer resource per token: offsets stay small).
+  // The 16 rows are the forward's last read of the state: non-temporal (the
+  // active rows' second read follows at once and keeps the default).
   V xr[16], xa_r[4], ov;
   auto load_token = [&](int s, const int (&id)[4]) {
     const rsrc_t rx = make_rsrc(Xb + (tok0 + s) * tokb, tokb);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (FULLN || i < NR) xr[i] = bload<E, MIX_CH>(rx, voff, (uint32_t)i * rowb);
+      if (FULLN || i < NR) xr[i] = bload<E, MIX_CH, CP_NT>(rx, voff, (uint32_t)i * rowb);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       if (b < K) xa_r[b] = bload<E, MIX_CH>(rx, voff, (uint32_t)id[b] * rowb);
