@@ -142,7 +142,8 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
   const bool arow = r < N;
   const void* abase = src.base[arow ? r : 0];
   const int64_t astr = src.stride[arow ? r : 0];
-  const int brow = (!ROUTE && r >= 1 && r <= k) ? act.id[r - 1] : 0;
+  // (columns past k repeat G_0's row: their loads touch no further lines)
+  const int brow = (!ROUTE && r >= 1) ? act.id[r <= k ? r - 1 : 0] : 0;
   const void* bbase = r == 0 ? dhin : dXn;
   const int64_t bstr = r == 0 ? (int64_t)C : (int64_t)N * C;
   const int64_t boff = r == 0 ? 0 : (int64_t)brow * C;
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
     const void* ab = abase;
     int64_t ao = t * astr;
     if constexpr (ROUTE) {
-      bo = (r >= 1 && r <= k) ? (int64_t)tid_s[ttc][min(r - 1, 3)] * C : 0;
+      bo = r >= 1 ? (int64_t)tid_s[ttc][r <= k ? min(r - 1, 3) : 0] * C : 0;
       if (xact) {
         // after an in-place forward, stream r's old row is saved at its slot
         int slot = -1;
@@ -1049,9 +1050,7 @@ __device__ __forceinline__ void bgrad_body(
   const int c0 = cb * B2_CB + chalf * B2_WAVE_CH;   // this wave's channels c0 .. c0+32
   const int64_t NCs = (int64_t)N * C;
   const size_t jbase = (size_t)srow * C + c0;
-  const int cl = c0 + 8 * g4;                        // this lane's 8 channels
-  const bool cv = wv && cl < C;
-  const int clc = cl < C ? cl : 0;
+  const int cl = c0 + 8 * g4;                        // this lane's 8 channels (in the row tiles)
   const uint32_t tokb = (uint32_t)N * C * EB;        // bytes of one token's state
 
   // proj A operand: W rows, permuted: A row m of j-tile jt -> channel
@@ -1134,24 +1133,23 @@ __device__ __forceinline__ void bgrad_body(
       }
     }
   };
-  // own rows of the B2_SUB tiles from t0, through buffer resources based at
-  // each tile (tokens past the end read zeros).  These are the pass's last
-  // reads of the state and of dX_new: non-temporal.  Without the router, the two
-  // waves of a row split its tile by tokens rather than by channel halves
-  // when loading, so that every load instruction covers whole lines: lane
-  // (token lt = 8 chalf + lane/8, piece lp = lane%8) reads channels
+  // own rows of the B2_SUB tiles from t0 (tokens past the end read zeros,
+  // or are masked when published).  These are the pass's last reads of the
+  // state, of dX_new and of the pass rows: non-temporal.  The two waves of a
+  // row split its tile by tokens rather than by channel halves when loading,
+  // so that every load instruction covers whole lines: lane (token
+  // lt = 8 chalf + lane/8, piece lp = lane%8) reads channels
   // cb*B2_CB + 8 lp .. + 8 and publishes them into the row tile of the wave
   // that owns that half, at that wave's slot for (token lt, group lp%4).
-  // The routed form loads each lane's own slot (its rows differ per token).
   V8<E> xo[B2_SUB], dvo[B2_SUB];
   const uint32_t xrowb = (uint32_t)xstride * EB;
-  const int lt = ROUTE ? r16 : 8 * chalf + (lane >> 3);
+  const int lt = 8 * chalf + (lane >> 3);
   const int lp = lane & 7;
-  const int lc = ROUTE ? cl : cb * B2_CB + 8 * lp;
+  const int lc = cb * B2_CB + 8 * lp;
   const bool lcv = wv && lc < C;
   const int lcc = lcv ? lc : 0;
-  const int pubw = ROUTE ? wave : slot + 4 * (lp >> 2);
-  const int puboff = ROUTE ? g4 * LY::GSTRIDE + r16 * 8 * EB : (lp & 3) * LY::GSTRIDE + lt * 8 * EB;
+  const int pubw = slot + 4 * (lp >> 2);
+  const int puboff = (lp & 3) * LY::GSTRIDE + lt * 8 * EB;
   const uint32_t vx = ((uint32_t)lt * (uint32_t)xstride + lcc) * EB;
   const uint32_t vd = (((uint32_t)lt * N + srow) * (uint32_t)C + lcc) * EB;
   // ROUTE: this lane's tokens' active lists for the step loaded next, and
@@ -1179,18 +1177,21 @@ __device__ __forceinline__ void bgrad_body(
       }
     }
   };
+  // (the routed loads go through buffer resources based at each tile, with
+  // 32-bit per-lane offsets; a list of a token past the end reads zeros)
   auto load_ids = [&](int t0) {
     if constexpr (ROUTE) {
 #pragma unroll
       for (int s = 0; s < B2_SUB; ++s) {
-        const int ta = t0 + s * B2_TT + r16;
-        const size_t tc = (size_t)(ta < T ? ta : T - 1);
+        const int ta = t0 + s * B2_TT;
+        const rsrc_t ri = make_rsrc(ridx + (size_t)ta * k, clamp_bytes(ta < T ? T - ta : 0, (uint32_t)k * 4));
         if (k == 4) {                                  // the token's list in one 16-byte load
-          const int4 v = *reinterpret_cast<const int4*>(ridx + tc * 4);
-          nid[s][0] = v.x; nid[s][1] = v.y; nid[s][2] = v.z; nid[s][3] = v.w;
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ri, (uint32_t)lt * 16, 0, 0);
+          nid[s][0] = (int)v[0]; nid[s][1] = (int)v[1]; nid[s][2] = (int)v[2]; nid[s][3] = (int)v[3];
         } else {
 #pragma unroll
-          for (int a = 0; a < 4; ++a) nid[s][a] = a < k ? ridx[tc * k + a] : -1;
+          for (int a = 0; a < 4; ++a)
+            nid[s][a] = a < k ? (int)__builtin_amdgcn_raw_buffer_load_b32(ri, ((uint32_t)lt * k + a) * 4, 0, 0) : -1;
         }
       }
     }
@@ -1209,16 +1210,16 @@ __device__ __forceinline__ void bgrad_body(
         // through a per-lane address (tokens past the end read token T-1;
         // their values are masked when published)
         const int slot = nslot[s];
-        const size_t tk = (size_t)(ta + r16 < T ? ta + r16 : T - 1);
+        const size_t tk = (size_t)(ta + lt < T ? ta + lt : T - 1);
         const char* src_row = slot >= 0
-            ? static_cast<const char*>(passbuf) + ((tk * k + slot) * (size_t)C + clc) * EB
-            : static_cast<const char*>(dXn) + ((tk * N + srow) * (size_t)C + clc) * EB;
-        dvo[s] = V8<E>::load(src_row, 0);
+            ? static_cast<const char*>(passbuf) + ((tk * k + slot) * (size_t)C + lcc) * EB
+            : static_cast<const char*>(dXn) + ((tk * N + srow) * (size_t)C + lcc) * EB;
+        dvo[s] = V8<E>::load_nt(src_row, 0);
         // the state row: saved at its slot after an in-place forward
         const char* x_row = (xact && slot >= 0)
-            ? static_cast<const char*>(xact) + ((tk * k + slot) * (size_t)C + clc) * EB
-            : static_cast<const char*>(xbase) + (tk * (size_t)xstride + clc) * EB;
-        xo[s] = V8<E>::load(x_row, 0);
+            ? static_cast<const char*>(xact) + ((tk * k + slot) * (size_t)C + lcc) * EB
+            : static_cast<const char*>(xbase) + (tk * (size_t)xstride + lcc) * EB;
+        xo[s] = V8<E>::load_nt(x_row, 0);
       } else {
         dvo[s] = bload<E, 8, CP_NT>(rd, vd, 0);
       }
@@ -1226,27 +1227,14 @@ __device__ __forceinline__ void bgrad_body(
   };
   // dX of finished tiles, by buffer stores based at each tile: an
   // out-of-range offset (ragged token or channel tail, or no tile yet) is
-  // dropped by the hardware.
-  // Without the router, a tile's dX goes out in whole lines, in the load
-  // mapping: each wave leaves its dX in its own X row tile (the tile's dW
-  // runs first, so the X values are no longer needed), and after the step's closing barrier each lane stores
-  // the piece (token lt, piece lp) it loaded, both tiles at the top of the
-  // next step, ahead of the prefetch.  It reads them before it publishes
-  // the next rows into the same places (the other wave of the row writes
-  // only the other token half).  The whole-line stores are non-temporal:
-  // dX is not read again in the pass.
-  // With the router, the last tile of a step is stored at the top of the
-  // next step from registers (res) and the first one as soon as it is done.
-  V8<E> res = V8<E>::zero();
-  uint32_t res_off = 0x80000000u;
-  int res_t0 = 0;
-  auto store_res = [&]() {
-    if constexpr (ROUTE) {
-      const rsrc_t rdx =
-          make_rsrc(static_cast<char*>(dX) + (size_t)(res_t0 + (B2_SUB - 1) * B2_TT) * tokb, (uint32_t)B2_TT * tokb);
-      bstore<E, 8>(res, rdx, res_off, 0);
-    }
-  };
+  // dropped by the hardware.  A tile's dX goes out in whole lines, in the
+  // load mapping: each wave leaves its dX in its own X row tile (the tile's
+  // dW runs first, so the X values are no longer needed), and after the
+  // step's closing barrier each lane stores the piece (token lt, piece lp)
+  // it loaded, both tiles at the top of the next step, ahead of the
+  // prefetch.  It reads them before it publishes the next rows into the
+  // same places (the other wave of the row writes only the other token
+  // half).  The stores are non-temporal: dX is not read again in the pass.
   auto staged = [&](int s) { return *reinterpret_cast<const V8<E>*>(&xsh[s][pubw][puboff]); };
   auto store_staged = [&](const V8<E>& v, int ta, bool have) {
     const rsrc_t rdx = make_rsrc(static_cast<char*>(dX) + (size_t)ta * tokb, (uint32_t)B2_TT * tokb);
@@ -1269,18 +1257,16 @@ __device__ __forceinline__ void bgrad_body(
     wait_vmcnt<0>();
     form_slots();                    // (the next step's lists landed with them)
     // publish the own rows (zero outside the sequence or the channels), which
-    // frees their registers for the next prefetch; without the router, each
-    // tile's place first gives up the previous step's staged dX
+    // frees their registers for the next prefetch; each tile's place first
+    // gives up the previous step's staged dX
 #pragma unroll
     for (int s = 0; s < B2_SUB; ++s) {
-      V8<E> d;
-      if constexpr (!ROUTE) d = staged(s);
+      const V8<E> d = staged(s);
       const bool ok = t0 + s * B2_TT + lt < T && lcv;
       *reinterpret_cast<V8<E>*>(&xsh[s][pubw][puboff]) = ok ? xo[s] : V8<E>::zero();
       *reinterpret_cast<V8<E>*>(&gsh[s][pubw][puboff]) = ok ? dvo[s] : V8<E>::zero();
-      if constexpr (!ROUTE) store_staged(d, t0 - STEP + s * B2_TT, t0 > tbeg);
+      store_staged(d, t0 - STEP + s * B2_TT, t0 > tbeg);
     }
-    store_res();
     {
       // next tiles' loads; the last step reloads itself so that every wave
       // issues the same memory operations in every iteration
@@ -1289,15 +1275,12 @@ __device__ __forceinline__ void bgrad_body(
       load_own(tn);
       load_ids(tn + STEP);
     }
-    res_t0 = t0;
     // the published rows and this step's copies (waited above) are visible
     // to every wave; the next step's copies and loads stay in flight
     lds_barrier();
 #pragma unroll
     for (int s = 0; s < B2_SUB; ++s) {
       __builtin_amdgcn_sched_barrier(0);      // keep the tiles' live ranges apart
-      const int tk = t0 + s * B2_TT + r16;
-      const bool tv = tk < T;
       const unsigned char* rb = rbuf[buf][s];
 
       // ---- dW on MFMA: A = X^T (rows = channels, K = 16 tokens) ----
@@ -1385,7 +1368,7 @@ __device__ __forceinline__ void bgrad_body(
           pj[jt] = a32 + a16;
         }
       }
-      // ---- assemble dX for (token tk, channels cl..cl+8) ----
+      // ---- assemble dX for (token t0 + s*B2_TT + r16, channels cl..cl+8) ----
       {
         const float* co = reinterpret_cast<const float*>(rb + RCO);
         const float hpre = co[(F_PRE + srow) * B2_TT + r16];
@@ -1433,23 +1416,9 @@ __device__ __forceinline__ void bgrad_body(
           if constexpr (ROUTE) v += cst;
           o[q] = v;
         }
-        const V8<E> ov = V8<E>::from_float(o);
-        if constexpr (ROUTE) {
-          const uint32_t off = (tv && cv) ? ((uint32_t)r16 * N + srow) * (uint32_t)C * EB + cl * EB : 0x80000000u;
-          if (s + 1 < B2_SUB) {
-            // stored now: it completes well before the next top-of-loop wait
-            const rsrc_t rdx =
-                make_rsrc(static_cast<char*>(dX) + (size_t)(t0 + s * B2_TT) * tokb, (uint32_t)B2_TT * tokb);
-            bstore<E, 8>(ov, rdx, off, 0);
-          } else {
-            res = ov;          // the last tile's store is issued at the top of the next step
-            res_off = off;
-          }
-        } else {
-          // staged in this wave's X row tile, over the value just read (the
-          // tile's dW, above, has read the rest of it)
-          *reinterpret_cast<V8<E>*>(&xsh[s][wave][rowoff]) = ov;
-        }
+        // staged in this wave's X row tile, over the value just read (the
+        // tile's dW, above, has read the rest of it)
+        *reinterpret_cast<V8<E>*>(&xsh[s][wave][rowoff]) = V8<E>::from_float(o);
       }
     }
     // every read of this step's buffers and row tiles is done, and the staged
@@ -1458,12 +1427,9 @@ __device__ __forceinline__ void bgrad_body(
     buf ^= 1;
     last_t0 = t0;
   }
-  store_res();
-  if constexpr (!ROUTE) {
-    if (tbeg < tfin) {
+  if (tbeg < tfin) {
 #pragma unroll
-      for (int s = 0; s < B2_SUB; ++s) store_staged(staged(s), last_t0 + s * B2_TT, true);
-    }
+    for (int s = 0; s < B2_SUB; ++s) store_staged(staged(s), last_t0 + s * B2_TT, true);
   }
   // dW partial rows: D row 4*g4+e of j-tile jt = channel 16*jt + 4*g4 + e
   if (wv) {

@@ -46,6 +46,15 @@ template <int W> struct Vec<BF16, W> {
     }
     return v;
   }
+  // a whole vector of 8, read non-temporal (the data's last use in a pass)
+  __device__ static Vec load_nt(const void* base, size_t elem) {
+    static_assert(W == 8, "non-temporal loads of 16 bytes");
+    const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const uint16_t*>(base) + elem));
+    Vec v;
+    v.w[0] = r[0]; v.w[1] = r[1]; v.w[2] = r[2]; v.w[3] = r[3];
+    return v;
+  }
   __device__ void store(void* base, size_t elem) const {
     uint16_t* p = reinterpret_cast<uint16_t*>(base) + elem;
     if constexpr (W == 8) {
@@ -97,6 +106,17 @@ template <int W> struct Vec<F32, W> {
       typedef float f32x2 __attribute__((ext_vector_type(2)));
       f32x2 r = *reinterpret_cast<const f32x2*>(p);
       v.x[0] = r[0]; v.x[1] = r[1];
+    }
+    return v;
+  }
+  __device__ static Vec load_nt(const void* base, size_t elem) {
+    static_assert(W % 4 == 0, "non-temporal loads of 16 bytes");
+    const float* p = reinterpret_cast<const float*>(base) + elem;
+    Vec v;
+#pragma unroll
+    for (int q = 0; q < W; q += 4) {
+      const f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + q));
+      v.x[q] = r[0]; v.x[q + 1] = r[1]; v.x[q + 2] = r[2]; v.x[q + 3] = r[3];
     }
     return v;
   }
@@ -156,6 +176,23 @@ __device__ inline void wait_vmcnt() {
 __device__ inline void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0); vmcnt and expcnt left alone (gfx9 encoding)
   asm volatile("s_barrier" ::: "memory");
+}
+
+// Bitwise OR of two vectors, one of them zero: picks the other without a
+// per-lane branch (two loads of which one reads nothing, then the OR).
+template <int W>
+__device__ inline Vec<BF16, W> vor(const Vec<BF16, W>& a, const Vec<BF16, W>& b) {
+  Vec<BF16, W> v;
+#pragma unroll
+  for (int j = 0; j < W / 2; ++j) v.w[j] = a.w[j] | b.w[j];
+  return v;
+}
+template <int W>
+__device__ inline Vec<F32, W> vor(const Vec<F32, W>& a, const Vec<F32, W>& b) {
+  Vec<F32, W> v;
+#pragma unroll
+  for (int j = 0; j < W; ++j) v.x[j] = __uint_as_float(__float_as_uint(a.x[j]) | __float_as_uint(b.x[j]));
+  return v;
 }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
