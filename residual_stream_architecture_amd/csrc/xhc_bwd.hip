@@ -41,6 +41,25 @@ struct RowTable { int stream[5][4]; };   // row group -> 4 stream ids (-1 = none
 // ---------------------------------------------------------------------------
 
 // ---------------------------------------------------------------------------
+// Post gates for B1: hpost[t][a*4 + m] = H_post[a][m], recomputed from the
+// saved logits as the forward computed them (routed slots scaled by their
+// scores), zero past k and nc.  One thread per entry.
+// ---------------------------------------------------------------------------
+template <bool ROUTE>
+__global__ __launch_bounds__(256) void k_post_gates(const float* __restrict__ zin, float* __restrict__ hpost, int T,
+                                                    int N, int k, int P, int nc, int unit_gates, int zsv, int nfix) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= (int64_t)T * 16) return;
+  const int64_t t = j >> 4;
+  const int e = (int)(j & 15), a = e >> 2, m = e & 3;
+  const float* zt = zin + (size_t)t * zsv;
+  float h = 0.f;
+  if (a < k && m < nc) h = unit_gates ? 1.f : sigmoid(zt[N + a * nc + m]);
+  if (ROUTE && a >= nfix && a < k) h *= sigmoid(zt[P + 3 + 3 * (a - nfix)]);
+  hpost[j] = h;
+}
+
+// ---------------------------------------------------------------------------
 // B1x.  The backward's state dots on MFMA.  Workgroup = (channel block of
 // BX_CB = 8 x 64 channels, tile of BX_TOK tokens); wave w owns channels
 // cb*BX_CB + 64w .. +64 (two K=32 steps).  Per token:
@@ -60,13 +79,10 @@ struct RowTable { int stream[5][4]; };   // row group -> 4 stream ids (-1 = none
 template <typename E, typename R, bool ROUTE>
 __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const void* __restrict__ dXn,
                                                           const void* __restrict__ dhin, float* __restrict__ dpa,
-                                                          int T, int C, int N, int k, Act4 act, int ncb,
-                                                          const float* __restrict__ zin, float* __restrict__ hpost,
-                                                          int P, int nc, int unit_gates, const R* __restrict__ W,
-                                                          R* __restrict__ Wp, int64_t NC, int zsv,
+                                                          int T, int C, int N, int k, Act4 act, int ncb, int P,
+                                                          const R* __restrict__ W, R* __restrict__ Wp, int64_t NC,
                                                           const int32_t* __restrict__ ridx,
-                                                          const R* __restrict__ Wr, int nfix,
-                                                          const void* __restrict__ xact) {
+                                                          const R* __restrict__ Wr, const void* __restrict__ xact) {
   constexpr int EB = E::bytes;
   constexpr int RING = EB == 2 ? 4 : 2;
   static_assert(BX_GRP % RING == 0 && BX_TOK % BX_GRP == 0, "ring slots must be static in a group");
@@ -124,18 +140,6 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
       tid_s[tt][a] = (unsigned)v < (unsigned)N ? v : 0;     // never a row outside the state
     }
     __syncthreads();
-  }
-  // the tile's post gates for B1 (H_post[a*4 + m], recomputed from the saved
-  // logits as the forward computed them), written by channel block 0
-  if (cb == 0) {
-    for (int j = threadIdx.x; j < tn * 16; j += 64 * BX_WAVES) {
-      const int tt = j >> 4, e = j & 15, a = e >> 2, m = e & 3;
-      const float* zt = zin + (size_t)(t0 + tt) * zsv;
-      float h = 0.f;
-      if (a < k && m < nc) h = unit_gates ? 1.f : sigmoid(zt[N + a * nc + m]);
-      if (ROUTE && a >= nfix && a < k) h *= sigmoid(zt[P + 3 + 3 * (a - nfix)]);
-      hpost[(size_t)(t0 + tt) * 16 + e] = h;
-    }
   }
 
   // A row r = stream r; B column r = dh_in (r = 0) or G_{r-1}
@@ -1623,16 +1627,6 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   for (int b = 0; b < 4; ++b) act.id[b] = b < p.k && !rt ? a->active[b] : 0;
   const HresActive ha = hres_active(p, a->active);
 
-  {
-    TimedLaunch tl(tm, KID_BXDOTS, st);
-#define XHC_BX(RT)                                                                                             \
-  k_bxdots<E, R, RT><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(                                      \
-      src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, zin, hpost, p.P, p.nc,               \
-      p.gate == XHC_GATE_UNIT, static_cast<const R*>(a->W), static_cast<R*>(Wp), p.NC, p.zsv, ridx,             \
-      static_cast<const R*>(p.R ? a->W_route : nullptr), p.nfix, rt ? a->xact : nullptr)
-    if (rt) XHC_BX(true); else XHC_BX(false);
-#undef XHC_BX
-  }
   float* gss = reinterpret_cast<float*>(ws + p.off_gss);        // [T][16] Sg (Gram-Schmidt)
   const dim3 b1grid(p.b1_cblocks, p.B * p.b1_segs);
   const bool fast = p.N == 16 && p.k == 4;
@@ -1650,6 +1644,20 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
       else XHC_BDOTS_G(b1grid, NCOMP, false, MODE, p.b1_lseg, p.b1_segs, false);                               \
     }                                                                                                          \
   } while (0)
+  // The TFA backward runs first: it is bound by arithmetic rather than by
+  // memory, so the write-back of whatever ran before the call drains while
+  // it runs instead of slowing the state dots.  Its post gates come from
+  // their own small kernel (with Gram-Schmidt, the first pass needs none).
+  if (!p.gs) {
+    TimedLaunch tl(tm, KID_POSTG, st);
+    const int nb = (int)(((int64_t)p.T * 16 + 255) / 256);
+    if (rt)
+      k_post_gates<true><<<nb, 256, 0, st>>>(zin, hpost, p.T, p.N, p.k, p.P, p.nc, p.gate == XHC_GATE_UNIT,
+                                             p.zsv, p.nfix);
+    else
+      k_post_gates<false><<<nb, 256, 0, st>>>(zin, hpost, p.T, p.N, p.k, p.P, p.nc, p.gate == XHC_GATE_UNIT,
+                                              p.zsv, p.nfix);
+  }
   {
     TimedLaunch tl(tm, KID_BDOTS, st);
     if (p.gs) {
@@ -1668,6 +1676,15 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
     } else {
       XHC_BDOTS(1, BD_FULL);
     }
+  }
+  {
+    TimedLaunch tl(tm, KID_BXDOTS, st);
+#define XHC_BX(RT)                                                                                             \
+  k_bxdots<E, R, RT><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(                                      \
+      src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, p.P, static_cast<const R*>(a->W),   \
+      static_cast<R*>(Wp), p.NC, ridx, static_cast<const R*>(p.R ? a->W_route : nullptr), rt ? a->xact : nullptr)
+    if (rt) XHC_BX(true); else XHC_BX(false);
+#undef XHC_BX
   }
   {
     TimedLaunch tl(tm, KID_BCOEF, st);
@@ -1803,9 +1820,8 @@ static int backward_pre_impl(const Plan& p, const xhc_bwd_pre_args* a, char* ws,
   {
     TimedLaunch tl(tm, KID_BXDOTS, st);
     k_bxdots<E, R, false><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(
-        src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, zin, hpost, p.P, p.nc,
-        p.gate == XHC_GATE_UNIT, static_cast<const R*>(a->W), static_cast<R*>(Wp), p.NC, p.zsv, nullptr, nullptr,
-        p.nfix, nullptr);
+        src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, p.P, static_cast<const R*>(a->W),
+        static_cast<R*>(Wp), p.NC, nullptr, nullptr, nullptr);
   }
   {
     TimedLaunch tl(tm, KID_BCOEF, st);
