@@ -405,20 +405,34 @@ __global__ __launch_bounds__(256) void k_bdots(
   };
   // One buffer resource per row read, sized to the row, or to nothing for a
   // position past the sequence: lanes past C and such positions read zeros,
-  // with no per-value selects in the token loop.
+  // with no per-value selects in the token loop.  The second Gram-Schmidt
+  // pass holds more uniform values (Sg), and there the extra resources
+  // spill scalar registers: it reads through one resource per token and
+  // masks the values instead (ZMASK).
+  constexpr bool ZMASK = MODE == BD_GSGRAD;
   const uint32_t voffr = (uint32_t)clraw * EB;
   auto load_tok = [&](int s, int q) {
     const bool lv = s < S;
     const size_t t = tok0 + min(s, S - 1);
-    if constexpr (NEED_G) {
+    if constexpr (ZMASK) {
+      if constexpr (NEED_G) {
+        const rsrc_t rg = make_rsrc(static_cast<const char*>(dXn) + t * tokb, tokb);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const rsrc_t rg = make_rsrc(static_cast<const char*>(dXn) + t * tokb + (size_t)nid[a] * rowb, lv ? rowb : 0u);
-        gq[q][a] = bload<E, B1_CH>(rg, voffr, 0);
+        for (int a = 0; a < 4; ++a) gq[q][a] = bload<E, B1_CH>(rg, voff, (uint32_t)nid[a] * rowb);
       }
+      oq[q] = bload<E, B1_CH>(rout, voff, (uint32_t)min(s, S - 1) * rowb);
+    } else {
+      if constexpr (NEED_G) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const rsrc_t rg =
+              make_rsrc(static_cast<const char*>(dXn) + t * tokb + (size_t)nid[a] * rowb, lv ? rowb : 0u);
+          gq[q][a] = bload<E, B1_CH>(rg, voffr, 0);
+        }
+      }
+      const rsrc_t ro = make_rsrc(static_cast<const char*>(out) + t * rowb, lv ? rowb : 0u);
+      oq[q] = bload<E, B1_CH>(ro, voffr, 0);
     }
-    const rsrc_t ro = make_rsrc(static_cast<const char*>(out) + t * rowb, lv ? rowb : 0u);
-    oq[q] = bload<E, B1_CH>(ro, voffr, 0);
     next_ids(s + 1);
   };
   // post coefficients (and Sg) of one token (uniform: scalar loads), one token ahead
@@ -484,7 +498,7 @@ __global__ __launch_bounds__(256) void k_bdots(
         if constexpr (NEED_G) {
           gq[q][a].to_float(G[a]);
         }
-        if (!NEED_G || !(a < k)) {
+        if (!NEED_G || !(a < k && (!ZMASK || (cv && live)))) {
 #pragma unroll
           for (int ch = 0; ch < B1_CH; ++ch) G[a][ch] = 0.f;
         }
@@ -500,7 +514,7 @@ __global__ __launch_bounds__(256) void k_bdots(
         for (int ch = 0; ch < B1_CH; ++ch) U[m][ch] = 0.f;
       if (need_u) {
 #pragma unroll
-        for (int ch = 0; ch < B1_CH; ++ch) win[(j + 11) % 12][ch] = of[ch];
+        for (int ch = 0; ch < B1_CH; ++ch) win[(j + 11) % 12][ch] = (!ZMASK || cv) ? of[ch] : 0.f;
 #pragma unroll
         for (int ch = 0; ch < B1_CH; ++ch) {
           U[0][ch] = win[(j + 11) % 12][ch];
@@ -568,7 +582,7 @@ __global__ __launch_bounds__(256) void k_bdots(
                 float e = 0.f;
 #pragma unroll
                 for (int n = 0; n < 4; ++n) e = fmaf(Sg[m][n], U[n][ch], e);
-                d += live ? e : 0.f;     // U of a position past the sequence still sees real ones
+                d += (live && (!ZMASK || cv)) ? e : 0.f;   // U past the sequence still sees real ones
               }
             }
             dU[m][ch] = d;
