@@ -461,7 +461,7 @@ struct xhc_timer {
 
 static const char* const kKernelNames[xhc::KID_COUNT] = {
     "pack_wt", "proj", "coef", "mix", "pack_wp", "bdots", "bcoef", "bgrad", "breduce", "bxdots", "mixproj", "gram",
-    "bdots_gs", "route_colsum", "route_pass", "route_dwr", "check_lists", "post_gates"};
+    "bdots_gs", "route_colsum", "route_pass", "route_dwr", "check_lists", "bwd_prep"};
 
 namespace xhc {
 void timer_mark(xhc_timer* tm, int kid, hipStream_t st, bool start) {

@@ -40,23 +40,69 @@ struct RowTable { int stream[5][4]; };   // row group -> 4 stream ids (-1 = none
 // W [NC, P] -> Wp [NC, 64], columns p >= P zero.
 // ---------------------------------------------------------------------------
 
+// B2's projection operand, elements [beg, end) of Wp [NC][64] from W [NC][P]
+// (zero padded past P; with a router columns 48.. hold W_route), by `nth`
+// threads of which this is `tid`.  Each thread's PK elements are loaded
+// together (clamped, always valid addresses) before any is stored: one
+// memory latency per PK elements instead of one per element.
+template <typename R, bool ROUTE>
+__device__ inline void pack_wp(const R* __restrict__ W, R* __restrict__ Wp, const R* __restrict__ Wr, int P, int N,
+                               int64_t NC, int64_t beg, int64_t end, int tid, int nth) {
+  constexpr int PK = 8;
+  for (int64_t i0 = beg + tid; i0 < end; i0 += (int64_t)nth * PK) {
+    R w[PK], wr[PK];
+#pragma unroll
+    for (int u = 0; u < PK; ++u) {
+      const int64_t idx = i0 + (int64_t)u * nth;
+      const int64_t j = min(idx >> 6, NC - 1);
+      const int pp = (int)(idx & 63);
+      w[u] = W[(size_t)j * P + min(pp, P - 1)];
+      // (given per-token lists run this path without a router: no W_route)
+      if constexpr (ROUTE) wr[u] = Wr ? Wr[(size_t)j * N + min(max(pp - 48, 0), N - 1)] : R(0);
+    }
+#pragma unroll
+    for (int u = 0; u < PK; ++u) {
+      const int64_t idx = i0 + (int64_t)u * nth;
+      const int pp = (int)(idx & 63);
+      R x = pp < P ? w[u] : R(0);
+      if (ROUTE && pp >= 48) x = pp - 48 < N ? wr[u] : R(0);
+      if (idx < end) Wp[idx] = x;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Post gates for B1: hpost[t][a*4 + m] = H_post[a][m], recomputed from the
-// saved logits as the forward computed them (routed slots scaled by their
-// scores), zero past k and nc.  One thread per entry.
+// The backward's preparation, ahead of the TFA backward:
+//   blocks [0, nbg): post gates for B1, hpost[t][a*4 + m] = H_post[a][m],
+//     recomputed from the saved logits as the forward computed them (routed
+//     slots scaled by their scores), zero past k and nc; one thread per
+//     entry (none when hpost is NULL);
+//   the other blocks: B2's projection operand Wp (pack_wp), which nothing
+//     reads before B2.
+// Both are small; in one launch they cost one launch.
 // ---------------------------------------------------------------------------
-template <bool ROUTE>
-__global__ __launch_bounds__(256) void k_post_gates(const float* __restrict__ zin, float* __restrict__ hpost, int T,
-                                                    int N, int k, int P, int nc, int unit_gates, int zsv, int nfix) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j >= (int64_t)T * 16) return;
-  const int64_t t = j >> 4;
-  const int e = (int)(j & 15), a = e >> 2, m = e & 3;
-  const float* zt = zin + (size_t)t * zsv;
-  float h = 0.f;
-  if (a < k && m < nc) h = unit_gates ? 1.f : sigmoid(zt[N + a * nc + m]);
-  if (ROUTE && a >= nfix && a < k) h *= sigmoid(zt[P + 3 + 3 * (a - nfix)]);
-  hpost[j] = h;
+template <typename R, bool ROUTE>
+__global__ __launch_bounds__(256) void k_bwd_prep(const float* __restrict__ zin, float* __restrict__ hpost, int T,
+                                                  int N, int k, int P, int nc, int unit_gates, int zsv, int nfix,
+                                                  int nbg, const R* __restrict__ W, R* __restrict__ Wp,
+                                                  const R* __restrict__ Wr, int64_t NC) {
+  if ((int)blockIdx.x < nbg) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= (int64_t)T * 16) return;
+    const int64_t t = j >> 4;
+    const int e = (int)(j & 15), a = e >> 2, m = e & 3;
+    const float* zt = zin + (size_t)t * zsv;
+    float h = 0.f;
+    if (a < k && m < nc) h = unit_gates ? 1.f : sigmoid(zt[N + a * nc + m]);
+    if (ROUTE && a >= nfix && a < k) h *= sigmoid(zt[P + 3 + 3 * (a - nfix)]);
+    hpost[j] = h;
+  } else {
+    const int nbp = (int)gridDim.x - nbg, bp = (int)blockIdx.x - nbg;
+    const int64_t nwp = NC * 64;
+    const int64_t per = (nwp + nbp - 1) / nbp;
+    const int64_t beg = (int64_t)bp * per, end = min(beg + per, nwp);
+    pack_wp<R, ROUTE>(W, Wp, Wr, P, N, NC, beg, end, threadIdx.x, 256);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -82,7 +128,8 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
                                                           int T, int C, int N, int k, Act4 act, int ncb, int P,
                                                           const R* __restrict__ W, R* __restrict__ Wp, int64_t NC,
                                                           const int32_t* __restrict__ ridx,
-                                                          const R* __restrict__ Wr, const void* __restrict__ xact) {
+                                                          const R* __restrict__ Wr, const void* __restrict__ xact,
+                                                          int pack) {
   constexpr int EB = E::bytes;
   constexpr int RING = EB == 2 ? 4 : 2;
   static_assert(BX_GRP % RING == 0 && BX_TOK % BX_GRP == 0, "ring slots must be static in a group");
@@ -100,37 +147,13 @@ __global__ __launch_bounds__(64 * BX_WAVES) void k_bxdots(StreamRows src, const 
   const int t0 = tile * BX_TOK;
   const int tn = min(BX_TOK, T - t0);
 
-  // B2's projection operand: this workgroup's slice of W -> Wp [NC][64]
-  // (zero padded past P; with a router columns 48.. hold W_route); nothing
-  // reads it before B2
-  // Each thread's PK elements are loaded together (clamped, always valid
-  // addresses) before any is stored: one memory latency per PK elements
-  // instead of one per element at the start of every workgroup.
-  {
-    constexpr int PK = 8;
+  // B2's projection operand, this workgroup's slice of it (when the
+  // backward's preparation kernel has not packed it)
+  if (pack) {
     const int64_t nwp = NC * 64;
     const int64_t per = (nwp + gridDim.x - 1) / gridDim.x;
     const int64_t beg = (int64_t)lb * per, end = min(beg + per, nwp);
-    for (int64_t i0 = beg + threadIdx.x; i0 < end; i0 += (int64_t)64 * BX_WAVES * PK) {
-      R w[PK], wr[PK];
-#pragma unroll
-      for (int u = 0; u < PK; ++u) {
-        const int64_t idx = i0 + (int64_t)u * 64 * BX_WAVES;
-        const int64_t j = min(idx >> 6, NC - 1);
-        const int pp = (int)(idx & 63);
-        w[u] = W[(size_t)j * P + min(pp, P - 1)];
-        // (given per-token lists run this path without a router: no W_route)
-        if constexpr (ROUTE) wr[u] = Wr ? Wr[(size_t)j * N + min(max(pp - 48, 0), N - 1)] : R(0);
-      }
-#pragma unroll
-      for (int u = 0; u < PK; ++u) {
-        const int64_t idx = i0 + (int64_t)u * 64 * BX_WAVES;
-        const int pp = (int)(idx & 63);
-        R x = pp < P ? w[u] : R(0);
-        if (ROUTE && pp >= 48) x = pp - 48 < N ? wr[u] : R(0);
-        if (idx < end) Wp[idx] = x;
-      }
-    }
+    pack_wp<R, ROUTE>(W, Wp, Wr, P, N, NC, beg, end, threadIdx.x, 64 * BX_WAVES);
   }
   if constexpr (ROUTE) {
     for (int j = threadIdx.x; j < BX_TOK * 4; j += 64 * BX_WAVES) {
@@ -1660,17 +1683,22 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
   } while (0)
   // The TFA backward runs first: it is bound by arithmetic rather than by
   // memory, so the write-back of whatever ran before the call drains while
-  // it runs instead of slowing the state dots.  Its post gates come from
-  // their own small kernel (with Gram-Schmidt, the first pass needs none).
-  if (!p.gs) {
-    TimedLaunch tl(tm, KID_POSTG, st);
-    const int nb = (int)(((int64_t)p.T * 16 + 255) / 256);
+  // it runs instead of slowing the state dots.  Its post gates (with
+  // Gram-Schmidt the first pass needs none) and B2's projection operand come
+  // from one small preparation kernel ahead of it.
+  {
+    TimedLaunch tl(tm, KID_BPREP, st);
+    const int nbg = p.gs ? 0 : (int)(((int64_t)p.T * 16 + 255) / 256);
+    const int nbp = (int)std::min<int64_t>(4096, (p.NC * 64 + 2047) / 2048);   // one round of PK loads each
+    const R* Wr = static_cast<const R*>(p.R ? a->W_route : nullptr);
     if (rt)
-      k_post_gates<true><<<nb, 256, 0, st>>>(zin, hpost, p.T, p.N, p.k, p.P, p.nc, p.gate == XHC_GATE_UNIT,
-                                             p.zsv, p.nfix);
+      k_bwd_prep<R, true><<<nbg + nbp, 256, 0, st>>>(zin, p.gs ? nullptr : hpost, p.T, p.N, p.k, p.P, p.nc,
+                                                     p.gate == XHC_GATE_UNIT, p.zsv, p.nfix, nbg,
+                                                     static_cast<const R*>(a->W), static_cast<R*>(Wp), Wr, p.NC);
     else
-      k_post_gates<false><<<nb, 256, 0, st>>>(zin, hpost, p.T, p.N, p.k, p.P, p.nc, p.gate == XHC_GATE_UNIT,
-                                              p.zsv, p.nfix);
+      k_bwd_prep<R, false><<<nbg + nbp, 256, 0, st>>>(zin, p.gs ? nullptr : hpost, p.T, p.N, p.k, p.P, p.nc,
+                                                      p.gate == XHC_GATE_UNIT, p.zsv, p.nfix, nbg,
+                                                      static_cast<const R*>(a->W), static_cast<R*>(Wp), Wr, p.NC);
   }
   {
     TimedLaunch tl(tm, KID_BDOTS, st);
@@ -1696,7 +1724,8 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
 #define XHC_BX(RT)                                                                                             \
   k_bxdots<E, R, RT><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(                                      \
       src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, p.P, static_cast<const R*>(a->W),   \
-      static_cast<R*>(Wp), p.NC, ridx, static_cast<const R*>(p.R ? a->W_route : nullptr), rt ? a->xact : nullptr)
+      static_cast<R*>(Wp), p.NC, ridx, static_cast<const R*>(p.R ? a->W_route : nullptr), rt ? a->xact : nullptr, \
+      0)
     if (rt) XHC_BX(true); else XHC_BX(false);
 #undef XHC_BX
   }
@@ -1835,7 +1864,7 @@ static int backward_pre_impl(const Plan& p, const xhc_bwd_pre_args* a, char* ws,
     TimedLaunch tl(tm, KID_BXDOTS, st);
     k_bxdots<E, R, false><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(
         src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, p.P, static_cast<const R*>(a->W),
-        static_cast<R*>(Wp), p.NC, nullptr, nullptr, nullptr);
+        static_cast<R*>(Wp), p.NC, nullptr, nullptr, nullptr, 1);
   }
   {
     TimedLaunch tl(tm, KID_BCOEF, st);

@@ -12,7 +12,7 @@ namespace xhc {
 enum KernelId {
   KID_PACK_WT = 0, KID_PROJ, KID_COEF, KID_MIX,
   KID_PACK_WP, KID_BDOTS, KID_BCOEF, KID_BGRAD, KID_BREDUCE, KID_BXDOTS,
-  KID_MIXPROJ, KID_GRAM, KID_BDOTS_GS, KID_RCOLSUM, KID_RPASS, KID_RDWR, KID_CHECK, KID_POSTG,
+  KID_MIXPROJ, KID_GRAM, KID_BDOTS_GS, KID_RCOLSUM, KID_RPASS, KID_RDWR, KID_CHECK, KID_BPREP,
   KID_COUNT
 };
 // Alias kept for the backward's coefficient recompute from z_save.
