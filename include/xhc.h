@@ -135,9 +135,9 @@ enum {
  * the choice is made on fp32 scores), and its write-back term is scaled by
  * s = sigmoid(rho):  X_new[t, i_a] = sum_b H_res[a,b] X[t, i_b]
  * + s_a sum_m H_post[a,m] U_m.  The choice is discrete: the gradient reaches
- * the chosen streams' scores through s only.  Supported with at most 15
- * candidate streams (N - (k-R) <= 15, so at N = 16 at least one fixed
- * stream) and 1 <= R <= k; not with the chained forward.
+ * the chosen streams' scores through s only.  Supported with 1 <= R <= k
+ * (R = k: no fixed stream, all N streams are candidates); not with the
+ * chained forward.
  *
  * H_res from the active rows (hres_active = 1; source: the retrospective's
  * section "模型可以拥有 16 条 streams，但每层只更新 4 条", which credits the

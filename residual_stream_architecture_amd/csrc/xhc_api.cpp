@@ -30,8 +30,6 @@ int make_plan(const xhc_desc* d, Plan* p) {
   const int64_t T = (int64_t)d->B * d->S;
   if (T * d->N * (int64_t)d->C >= ((int64_t)1 << 31)) return XHC_ERR_SHAPE;
   if (d->route < 0 || d->route > d->k) return XHC_ERR_SHAPE;
-  // the router's candidates and the LayerNorm sum share one logit tile
-  if (d->route > 0 && d->N - (d->k - d->route) > 15) return XHC_ERR_UNSUPPORTED;
   if (d->per_token_active != 0 && d->per_token_active != 1) return XHC_ERR_UNSUPPORTED;
   if (d->per_token_active && d->route) return XHC_ERR_UNSUPPORTED;
   if (d->hres_active != 0 && d->hres_active != 1) return XHC_ERR_UNSUPPORTED;
@@ -51,7 +49,7 @@ int make_plan(const xhc_desc* d, Plan* p) {
   q.pt = q.R > 0 || d->per_token_active == 1;
   q.nfix = q.k - q.R;
   q.ncand = q.R ? q.N - q.nfix : 0;
-  if (q.R) q.NT = 4;                       // tile 3: router candidates + sum(x)
+  if (q.R) q.NT = 4;                       // tile 3: the router's candidate columns
   q.hact = d->hres_active == 1;
   q.zsv = q.R ? q.P + 3 + 3 * q.R : q.hact ? q.P + 2 : q.P + 1;
   q.dzs = q.pt ? DZ_R : 48;

@@ -28,14 +28,9 @@ namespace xhc {
 // of W, read coalesced into LDS, and the NT fragments are written from there
 // as 8-element vectors.
 // With a router (Wr != NULL, NT == 4) logit tile 3 holds the router's
-// candidate columns, column 48 + e = Wr column cand(e) for e < ncand, then a
-// column of ones (its dot with the state row is the row's sum, for the
-// LayerNorm mean), then zeros.
+// candidate columns, column 48 + e = Wr column cand(e) for e < ncand (up to
+// all 16 streams), then zeros.
 // ---------------------------------------------------------------------------
-template <typename R> __device__ inline R one_of();
-template <> __device__ inline uint16_t one_of<uint16_t>() { return (uint16_t)0x3F80u; }   // bf16 1.0
-template <> __device__ inline float one_of<float>() { return 1.0f; }
-
 template <typename R>
 __global__ __launch_bounds__(256) void k_pack_wt(const R* __restrict__ W, R* __restrict__ Wf, int C, int P, int NT,
                                                  int nks, const R* __restrict__ Wr, int N, RowOrder cand,
@@ -67,7 +62,7 @@ __global__ __launch_bounds__(256) void k_pack_wt(const R* __restrict__ W, R* __r
     for (int idx = threadIdx.x; idx < 32 * 16; idx += 256) {
       const int rr = idx >> 4, e = idx & 15;
       R v = R(0);
-      if (rr < rows) v = e < ncand ? rsrc[(size_t)rr * N + row_of(cand, e)] : e == ncand ? one_of<R>() : R(0);
+      if (rr < rows && e < ncand) v = rsrc[(size_t)rr * N + row_of(cand, e)];
       tile[rr][48 + e] = v;
     }
   }
@@ -98,7 +93,9 @@ __global__ __launch_bounds__(256) void k_pack_wt(const R* __restrict__ W, R* __r
 // Stream rows come from `src` (the state, or after an in-place forward the
 // saved active rows for the active streams).
 // Output zpart[split][t][0..16NT) = sum_c X[t,split,c] W[split*C+c, p],
-//        zpart[split][t][16NT]    = sum_c X[t,split,c]^2.
+//        zpart[split][t][16NT]    = sum_c X[t,split,c]^2,
+// and with the router's tile (NT == 4)
+//        zpart[split][t][16NT+1]  = sum_c X[t,split,c]   (for the LayerNorm mean).
 // ---------------------------------------------------------------------------
 // PU K-steps per stage, PNS stages in the ring: one K-step in a six-deep ring
 // when the grid has several workgroups per CU (N >= 8 stream splits), two in
@@ -144,6 +141,8 @@ __global__ __launch_bounds__(64 * PROJ_WAVES) void k_proj(StreamRows src, const 
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[f][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss[2] = {0.f, 0.f};
+  constexpr bool SUMX = NT == 4;                     // the router's LayerNorm needs sum(x)
+  float sx[2] = {0.f, 0.f};
 
   V8<E> a[PNS][PU][2];
   // stage j -> ring slot q: W copies, then this lane's state pieces.  Stages
@@ -188,7 +187,11 @@ __global__ __launch_bounds__(64 * PROJ_WAVES) void k_proj(StreamRows src, const 
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { const float v = a[q][u][f].f(j); ss[f] = fmaf(v, v, ss[f]); }
+        for (int j = 0; j < 8; ++j) {
+          const float v = a[q][u][f].f(j);
+          ss[f] = fmaf(v, v, ss[f]);
+          if constexpr (SUMX) sx[f] += v;
+        }
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[f][n] = mma32(a[q][u][f], b[n], acc[f][n]);
       }
@@ -226,6 +229,10 @@ __global__ __launch_bounds__(64 * PROJ_WAVES) void k_proj(StreamRows src, const 
   for (int f = 0; f < 2; ++f) {
     ss[f] += shfl_xor(ss[f], 16);
     ss[f] += shfl_xor(ss[f], 32);
+    if constexpr (SUMX) {
+      sx[f] += shfl_xor(sx[f], 16);
+      sx[f] += shfl_xor(sx[f], 32);
+    }
   }
   float* zp = zpart + (size_t)split * T * ZST;
 #pragma unroll
@@ -238,7 +245,10 @@ __global__ __launch_bounds__(64 * PROJ_WAVES) void k_proj(StreamRows src, const 
         for (int n = 0; n < NT; ++n) zp[(size_t)tt * ZST + 16 * n + r] = acc[f][n][e];
       }
     }
-    if (g == 0 && tv[f]) zp[(size_t)(tbase + 16 * f + r) * ZST + 16 * NT] = ss[f];
+    if (g == 0 && tv[f]) {
+      zp[(size_t)(tbase + 16 * f + r) * ZST + 16 * NT] = ss[f];
+      if constexpr (SUMX) zp[(size_t)(tbase + 16 * f + r) * ZST + 16 * NT + 1] = sx[f];
+    }
   }
 }
 
@@ -252,7 +262,7 @@ __global__ __launch_bounds__(64 * PROJ_WAVES) void k_proj(StreamRows src, const 
 // partials, and the post coefficients become H_post T (u~ = T U, see
 // xhc_gs.h), so the write pass combines the raw components.
 // ROUTE (projection partials only): logit tile 3 holds x.Wr for the router's
-// candidates and sum(x); the token's scores, its top-R choice (R argmax
+// candidates, and each split's record sum(x) after sum(x^2); the token's scores, its top-R choice (R argmax
 // rounds over the 16 lanes on fp32 scores, equal scores to the lower
 // candidate, that is the lower stream id) and the scaling of the routed
 // slots' post coefficients by s = sigmoid(rho) happen here; the active list
@@ -283,7 +293,7 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
   const int t = blockIdx.x * 16 + tok;
   const bool tv = t < T;
   float r = 0.f;
-  float zr = 0.f, ssum = 0.f;   // ROUTE: raw x.Wr of candidate e (or sum(x) at e == ncand), sum(x^2)
+  float zr = 0.f, ssum = 0.f, xsum = 0.f;   // ROUTE: raw x.Wr of candidate e, sum(x^2), sum(x)
   if constexpr (ROUTE) {
     if (threadIdx.x < 16) csum[threadIdx.x] = ra.rcs[RCS_BLK * 16 + threadIdx.x];   // W_route's column sums
   }
@@ -298,6 +308,14 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
     ss += row_xor<8>(ss);
     ssum = ss;
     r = sqrtf(ss * inv_nc_total + eps);
+    if constexpr (ROUTE) {
+      float sx = (tv && e < SK) ? zpart[((size_t)e * T + t) * ZST + NTP + 1] : 0.f;
+      sx += row_xor<1>(sx);
+      sx += row_xor<2>(sx);
+      sx += row_xor<4>(sx);
+      sx += row_xor<8>(sx);
+      xsum = sx;
+    }
     if (ha.mask) {
       sa += row_xor<1>(sa);
       sa += row_xor<2>(sa);
@@ -351,7 +369,7 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
   if constexpr (ROUTE) {
     const int base = (threadIdx.x & 63) & ~15;
     const float inv_nc = inv_nc_total;
-    const float mu = __shfl(zr, base + ra.ncand, 64) * inv_nc;
+    const float mu = xsum * inv_nc;
     const float var = fmaxf(ssum * inv_nc - mu * mu, 0.f);
     const float sd = sqrtf(var + eps);
     const bool cand = e < ra.ncand;

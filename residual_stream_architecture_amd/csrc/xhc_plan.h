@@ -105,7 +105,7 @@ struct Plan {
   int R;              // routed slots (0: fixed active list)
   bool pt;            // per-token active lists (the router's, or given by the caller)
   int nfix;           // fixed slots, k - R
-  int ncand;          // router candidates, N - nfix (<= 15)
+  int ncand;          // router candidates, N - nfix (<= 16)
   int zsv;            // floats per token of z_save
   int dzs;            // floats per token of the backward's dz record
   int dwr;            // floats per row of the backward's dW partials

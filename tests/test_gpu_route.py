@@ -37,9 +37,12 @@ CASES = [
     ("gs_bf16", W_("r", 2, 77, 136, 16, 4, 4, "bf16", "fwdbwd", gs=True, route=2), [5, 12]),
     ("wide_bf16", W_("r", 1, 130, 1040, 16, 4, 4, "bf16", "fwdbwd", route=2), [4, 5]),
     ("edge_c8_s1_f32", W_("r", 4, 1, 8, 16, 4, 4, "f32", "fwdbwd", route=2), [0, 15]),
-    # one routed stream and nothing fixed: 15 candidates, the widest router tile
+    # one routed stream and nothing fixed: 15 candidates
     ("k1_n15_r1_f32", W_("r", 2, 37, 48, 15, 1, 4, "f32", "fwdbwd", route=1), []),
     ("nc1_f32", W_("r", 2, 29, 56, 12, 3, 1, "f32", "fwdbwd", route=2), [4]),
+    # nothing fixed at N = 16: all 16 streams are candidates (a full router tile)
+    ("all_routed_n16_f32", W_("r", 2, 45, 64, 16, 4, 4, "f32", "fwdbwd", route=4), []),
+    ("all_routed_n16_bf16", W_("r", 2, 77, 136, 16, 2, 4, "bf16", "fwdbwd", route=2), []),
 ]
 GS_EPS = 1e-6
 
@@ -152,7 +155,7 @@ def test_route_forward_parity(name, w, fixed):
     compare_forward(w, h, fixed, Xn, h_in, z_save, idx, ref)
 
 
-@pytest.mark.parametrize("case", [0, 1], ids=["tiny_f32", "ragged_bf16"])
+@pytest.mark.parametrize("case", [0, 1, 11], ids=["tiny_f32", "ragged_bf16", "all_routed_n16_f32"])
 def test_route_offset_state(case):
     # a state whose tokens have a mean far from zero next to their spread
     # (X + 8): the router's LayerNorm subtracts a large mean, which a
