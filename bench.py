@@ -447,18 +447,22 @@ def main():
     if args.split:
         # the same step from the split calls: the sublayer's output and dh_in
         # stand ready (synthetic), so the calls run back to back
-        if rt or w.gs:
-            raise SystemExit("--split: not with the router or Gram-Schmidt (the split calls refuse them)")
+        if w.gs:
+            raise SystemExit("--split: not with Gram-Schmidt (the split backward refuses it)")
         bwd_state = torch.empty(xhc.bwd_state_size(desc) // 4, dtype=torch.float32, device="cuda")
+        pre_kw = dict(route_idx=ridx, **route_in) if rt else {}
+        lists_kw = dict(route_idx=ridx) if rt else {}
+        bpre_kw = {key: bwd_kw[key] for key in ("W_route", "route_idx", "dW_route", "db_route")} if rt else {}
 
         def step(timer=None):
-            xhc.forward_pre(X, W, active, h_in, z_save, desc=desc, bias=bias, workspace=ws_f, timer=timer)
+            xhc.forward_pre(X, W, active, h_in, z_save, desc=desc, bias=bias, workspace=ws_f, timer=timer,
+                            **pre_kw)
             xhc.forward_post(X, out, active, z_save, desc=desc, xact_save=xact, workspace=ws_f, timer=timer,
-                             **convs)
+                             **convs, **lists_kw)
             xhc.backward_post(out, active, z_save, dXn, dout, bwd_state, desc=desc, workspace=ws_b, timer=timer,
-                              **convs, **dws)
+                              **convs, **dws, **lists_kw)
             xhc.backward_pre(X, W, active, z_save, dXn, dhin, bwd_state, dX, dW, desc=desc, xact=xact, bias=bias,
-                             db=db, workspace=ws_b, timer=timer)
+                             db=db, workspace=ws_b, timer=timer, **bpre_kw)
 
     for _ in range(args.warmup):
         step()
@@ -502,6 +506,8 @@ def main():
         kb = kernel_bytes(w, esz)
         if args.split:
             kb.pop("mixproj", None)      # the pre and post passes move different bytes under one name
+            if rt:
+                kb.pop("mix", None)      # the routed post pass moves each token's rows only, not 26C
         for name in xhc.kernel_names():
             ms, n = timer.read(name)
             if n:

@@ -372,8 +372,15 @@ int xhc_forward_chain(const xhc_desc* desc, const xhc_fwd_args* args,
  * rows' partials to the same carry; the next pre call starts from it
  * (carry_in) instead of reading its state for the projection -- the
  * dense-read correction of the retrospective's closing section, one state
- * read per sublayer.  Not with a router or per-token lists, and hres_active
- * not with a carry (XHC_ERR_UNSUPPORTED). */
+ * read per sublayer.  hres_active not with a carry (XHC_ERR_UNSUPPORTED).
+ *
+ * With per-token lists (a router, desc->route > 0, or the caller's,
+ * desc->per_token_active) there is no carry (XHC_ERR_UNSUPPORTED with
+ * W_next or carry_in).  The pre call then runs the router, saves its record
+ * in z_save and its choice in route_idx; its dense read does not depend on
+ * the lists.  The post call takes route_idx and rewrites each token's own
+ * rows: it reads only those rows and `out` (the routed slots' write-back
+ * scaled by the saved scores, as xhc_forward does). */
 typedef struct {
   const void* X;          /* [T,N,C] the state (read only)                     */
   const void* W;          /* [N*C,P]; not read with carry_in                    */
@@ -391,6 +398,14 @@ typedef struct {
   const xhc_desc* desc_next; /* HOST, the next sublayer's description, or NULL
                              (the same); same B, S, C, N, dtype                 */
   xhc_timer* timer;
+  /* per-token lists (read only with desc->route > 0 or per_token_active) */
+  const void* W_route;    /* [N*C,N] router weights, with a router              */
+  const float* b_route;   /* [N] or NULL (zero)                                 */
+  int32_t* route_idx;     /* [T,k]: the router's lists (output, required: the
+                             post call and the backward read them), or the
+                             caller's given lists (input)                       */
+  int32_t* status;        /* NULL, or device int32[2]: given lists are checked
+                             into it (XHC_STATUS_*)                             */
 } xhc_pre_args;
 
 typedef struct {
@@ -406,6 +421,8 @@ typedef struct {
                              are added to it) iff W_next                        */
   const xhc_desc* desc_next; /* as in the pre call                              */
   xhc_timer* timer;
+  const int32_t* route_idx; /* [T,k] the pre call's lists; required with a
+                             router or given lists, otherwise not read          */
 } xhc_post_args;
 
 /* Workspace: xhc_workspace_size(desc, XHC_PHASE_FWD) bytes for either call
@@ -425,10 +442,11 @@ int xhc_forward_post(const xhc_desc* desc, const xhc_post_args* args, void* work
  * The sublayer's backward then turns dout into dh_in, and xhc_backward_pre
  * forms dX, dW and db from dX_new, dh_in and bwd_state.  The two calls in
  * turn run the kernels of xhc_backward in its order and give the same
- * results bit for bit (same z_save).  Not with Gram-Schmidt, a router or
- * per-token lists (XHC_ERR_UNSUPPORTED): for those this library forms dout
- * after the coefficient backward, which needs dh_in.  With accumulate = 1
- * each call adds to the gradients it writes. */
+ * results bit for bit (same z_save).  With a router or given lists both
+ * calls take the forward's route_idx, and the second also the router's
+ * weights and gradients.  Not with Gram-Schmidt (XHC_ERR_UNSUPPORTED): there
+ * this library forms dout after the coefficient backward, which needs
+ * dh_in.  With accumulate = 1 each call adds to the gradients it writes. */
 typedef struct {
   const void* out;        /* [T,C] the sublayer output                          */
   const float *w4, *w8, *w12;  /* TFA conv weights, NULL iff ncomp == 1         */
@@ -441,6 +459,10 @@ typedef struct {
                              written here, read by xhc_backward_pre            */
   int32_t accumulate;     /* 0: overwrite dw*; 1: add to them                   */
   xhc_timer* timer;
+  const int32_t* route_idx; /* [T,k] the forward's per-token lists; required
+                             with a router or given lists, otherwise not read   */
+  int32_t* status;        /* NULL, or device int32[2]: the lists in route_idx
+                             are checked into it (XHC_STATUS_*)                 */
 } xhc_bwd_post_args;
 
 typedef struct {
@@ -457,8 +479,13 @@ typedef struct {
                              overlap it                                         */
   float* dW;              /* [N*C,P] fp32                                       */
   float* db;              /* [P] fp32, or NULL                                  */
-  int32_t accumulate;     /* 0: overwrite dW/db; 1: add to them                 */
+  int32_t accumulate;     /* 0: overwrite dW/db (and dW_route/db_route); 1: add */
   xhc_timer* timer;
+  /* per-token lists (read only with desc->route > 0 or per_token_active) */
+  const void* W_route;    /* [N*C,N], with a router                             */
+  const int32_t* route_idx; /* [T,k] the forward's per-token lists, required   */
+  float* dW_route;        /* [N*C,N] fp32, with a router                        */
+  float* db_route;        /* [N] fp32, or NULL                                  */
 } xhc_bwd_pre_args;
 
 /* Bytes of bwd_state (fp32 dot partials per token and channel block); 0 for

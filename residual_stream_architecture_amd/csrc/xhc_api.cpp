@@ -253,7 +253,8 @@ static int validate_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, 
 // Split forward (xhc_forward_pre / xhc_forward_post): pn is the next
 // sublayer's plan (== p without desc_next).
 static int check_split_modes(const Plan& p, const Plan& pn, bool carried) {
-  if (p.pt || pn.pt) return XHC_ERR_UNSUPPORTED;
+  // per-token lists: the carried partials would need each token's own rows
+  if (carried && (p.pt || pn.pt)) return XHC_ERR_UNSUPPORTED;
   // the carried partials sum every stream of a channel block
   if (carried && (p.hact || pn.hact)) return XHC_ERR_UNSUPPORTED;
   if (pn.B != p.B || pn.S != p.S || pn.C != p.C || pn.N != p.N || pn.dtype != p.dtype) return XHC_ERR_SHAPE;
@@ -266,9 +267,13 @@ static int validate_pre(const Plan& p, const Plan& pn, const xhc_pre_args* a) {
   if (rc) return rc;
   if (!a->X || !a->h_in || !a->z_save || (!a->carry_in && !a->W)) return XHC_ERR_NULL;
   if ((a->W_next == nullptr) != (a->carry_out == nullptr)) return XHC_ERR_NULL;
+  if (p.R && !a->W_route) return XHC_ERR_NULL;
+  if (p.pt && !a->route_idx) return XHC_ERR_NULL;
   rc = check_active(p, a->active);
   if (rc) return rc;
-  const void* ptrs[] = {a->X, a->W, a->bias, a->h_in, a->z_save, a->carry_in, a->W_next, a->carry_out};
+  const void* ptrs[] = {a->X, a->W, a->bias, a->h_in, a->z_save, a->carry_in, a->W_next, a->carry_out,
+                        p.R ? a->W_route : nullptr, p.R ? a->b_route : nullptr, p.pt ? a->route_idx : nullptr,
+                        p.pt && !p.R ? a->status : nullptr};
   for (const void* q : ptrs)
     if (misaligned(q)) return XHC_ERR_ALIGN;
   const size_t T = p.T, e = p.esz;
@@ -281,8 +286,13 @@ static int validate_pre(const Plan& p, const Plan& pn, const xhc_pre_args* a) {
   const Span cout = span(a->carry_out, a->carry_out ? pn.carry_bytes : 0);
   // carry_out may be carry_in itself: the coefficients consume it first
   const Span cout_chk = (a->carry_out && a->carry_out == a->carry_in) ? Span{nullptr, 0} : cout;
-  std::vector<Span> outs = {hin, zs, cout_chk};
-  std::vector<Span> ins = {X, W, bias, cin, Wn};
+  const Span Wr = span(p.R ? a->W_route : nullptr, (size_t)p.NC * p.N * e);
+  const Span br = span(p.R ? a->b_route : nullptr, (size_t)p.N * 4);
+  const Span ri = span(p.pt ? a->route_idx : nullptr, T * p.k * 4);
+  const Span stw = span(p.pt && !p.R ? a->status : nullptr, 8);
+  std::vector<Span> outs = {hin, zs, cout_chk, stw};
+  std::vector<Span> ins = {X, W, bias, cin, Wn, Wr, br};
+  (p.R ? outs : ins).push_back(ri);            // the router writes the lists; given lists are read
   if (any_overlap(outs, ins, Span{nullptr, 0}, Span{nullptr, 0})) return XHC_ERR_ALIAS;
   if (a->carry_out && a->carry_out == a->carry_in) {
     for (const Span& o : {hin, zs})
@@ -301,9 +311,11 @@ static int validate_post(const Plan& p, const Plan& pn, const xhc_post_args* a) 
   if (p.nc == 4 && (!a->w4 || !a->w8 || !a->w12)) return XHC_ERR_NULL;
   if (p.nc == 1 && (a->w4 || a->w8 || a->w12)) return XHC_ERR_UNSUPPORTED;
   if ((a->W_next == nullptr) != (a->carry_out == nullptr)) return XHC_ERR_NULL;
+  if (p.pt && !a->route_idx) return XHC_ERR_NULL;
   rc = check_active(p, a->active);
   if (rc) return rc;
-  const void* ptrs[] = {a->X, a->out, a->w4, a->w8, a->w12, a->z_save, a->xact_save, a->W_next, a->carry_out};
+  const void* ptrs[] = {a->X, a->out, a->w4, a->w8, a->w12, a->z_save, a->xact_save, a->W_next, a->carry_out,
+                        p.pt ? a->route_idx : nullptr};
   for (const void* q : ptrs)
     if (misaligned(q)) return XHC_ERR_ALIGN;
   const size_t T = p.T, e = p.esz;
@@ -314,8 +326,9 @@ static int validate_post(const Plan& p, const Plan& pn, const xhc_post_args* a) 
   const Span xs = span(a->xact_save, a->xact_save ? T * p.k * p.C * e : 0);
   const Span Wn = span(a->W_next, a->W_next ? (size_t)pn.NC * pn.P * e : 0);
   const Span cout = span(a->carry_out, a->carry_out ? pn.carry_bytes : 0);
+  const Span ri = span(p.pt ? a->route_idx : nullptr, T * p.k * 4);
   std::vector<Span> outs = {X, xs, cout};
-  std::vector<Span> ins = {out, w4, w8, w12, zs, Wn};
+  std::vector<Span> ins = {out, w4, w8, w12, zs, Wn, ri};
   if (any_overlap(outs, ins, Span{nullptr, 0}, Span{nullptr, 0})) return XHC_ERR_ALIAS;
   return XHC_OK;
 }
@@ -372,7 +385,7 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
 
 // Split backward (xhc_backward_post / xhc_backward_pre).
 static int check_split_bwd_modes(const Plan& p, int accumulate) {
-  if (p.pt || p.gs) return XHC_ERR_UNSUPPORTED;
+  if (p.gs) return XHC_ERR_UNSUPPORTED;
   if (accumulate != 0 && accumulate != 1) return XHC_ERR_UNSUPPORTED;
   return XHC_OK;
 }
@@ -384,10 +397,11 @@ static int validate_bwd_post(const Plan& p, const xhc_bwd_post_args* a) {
   if (!a->out || !a->z_save || !a->dX_new || !a->dout || !a->bwd_state) return XHC_ERR_NULL;
   if (p.nc == 4 && (!a->w4 || !a->w8 || !a->w12 || !a->dw4 || !a->dw8 || !a->dw12)) return XHC_ERR_NULL;
   if (p.nc == 1 && (a->w4 || a->w8 || a->w12 || a->dw4 || a->dw8 || a->dw12)) return XHC_ERR_UNSUPPORTED;
+  if (p.pt && !a->route_idx) return XHC_ERR_NULL;
   rc = check_active(p, a->active);
   if (rc) return rc;
   const void* ptrs[] = {a->out, a->w4, a->w8, a->w12, a->z_save, a->dX_new, a->dout, a->dw4, a->dw8, a->dw12,
-                        a->bwd_state};
+                        a->bwd_state, p.pt ? a->route_idx : nullptr, p.pt ? a->status : nullptr};
   for (const void* q : ptrs)
     if (misaligned(q)) return XHC_ERR_ALIGN;
   const size_t T = p.T, e = p.esz;
@@ -399,8 +413,10 @@ static int validate_bwd_post(const Plan& p, const xhc_bwd_post_args* a) {
   const Span dw4 = span(a->dw4, a->dw4 ? (size_t)p.C * 16 : 0), dw8 = span(a->dw8, a->dw8 ? (size_t)p.C * 32 : 0),
              dw12 = span(a->dw12, a->dw12 ? (size_t)p.C * 48 : 0);
   const Span st = span(a->bwd_state, p.state_bytes);
-  std::vector<Span> outs = {dout, dw4, dw8, dw12, st};
-  std::vector<Span> ins = {out, w4, w8, w12, zs, dXn};
+  const Span ri = span(p.pt ? a->route_idx : nullptr, T * p.k * 4);
+  const Span stw = span(p.pt ? a->status : nullptr, 8);
+  std::vector<Span> outs = {dout, dw4, dw8, dw12, st, stw};
+  std::vector<Span> ins = {out, w4, w8, w12, zs, dXn, ri};
   if (any_overlap(outs, ins, Span{nullptr, 0}, Span{nullptr, 0})) return XHC_ERR_ALIAS;
   return XHC_OK;
 }
@@ -411,10 +427,13 @@ static int validate_bwd_pre(const Plan& p, const xhc_bwd_pre_args* a) {
   if (rc) return rc;
   if (!a->X || !a->W || !a->z_save || !a->dX_new || !a->dh_in || !a->bwd_state || !a->dX || !a->dW)
     return XHC_ERR_NULL;
+  if (p.R && (!a->W_route || !a->dW_route)) return XHC_ERR_NULL;
+  if (p.pt && !a->route_idx) return XHC_ERR_NULL;
   rc = check_active(p, a->active);
   if (rc) return rc;
   const void* ptrs[] = {a->X, a->xact, a->W, a->bias, a->z_save, a->dX_new, a->dh_in, a->bwd_state, a->dX, a->dW,
-                        a->db};
+                        a->db, p.R ? a->W_route : nullptr, p.pt ? a->route_idx : nullptr,
+                        p.R ? a->dW_route : nullptr, p.R ? a->db_route : nullptr};
   for (const void* q : ptrs)
     if (misaligned(q)) return XHC_ERR_ALIGN;
   const size_t T = p.T, e = p.esz;
@@ -425,8 +444,12 @@ static int validate_bwd_pre(const Plan& p, const xhc_bwd_pre_args* a) {
   const Span dX = span(a->dX, T * p.NC * e);
   const Span dW = span(a->dW, (size_t)p.NC * p.P * 4), db = span(a->db, a->db ? (size_t)p.P * 4 : 0);
   if (a->dX != a->dX_new && overlap(dX, dXn)) return XHC_ERR_ALIAS;
-  std::vector<Span> outs = {dX, dW, db};
-  std::vector<Span> ins = {X, xact, W, bias, zs, dXn, dhin, st};
+  const Span Wr = span(p.R ? a->W_route : nullptr, (size_t)p.NC * p.N * e);
+  const Span ri = span(p.pt ? a->route_idx : nullptr, T * p.k * 4);
+  const Span dWr = span(p.R ? a->dW_route : nullptr, (size_t)p.NC * p.N * 4);
+  const Span dbr = span(p.R ? a->db_route : nullptr, (size_t)p.N * 4);
+  std::vector<Span> outs = {dX, dW, db, dWr, dbr};
+  std::vector<Span> ins = {X, xact, W, bias, zs, dXn, dhin, st, Wr, ri};
   if (any_overlap(outs, ins, dX, dXn)) return XHC_ERR_ALIAS;
   return XHC_OK;
 }

@@ -1812,27 +1812,51 @@ static int backward_impl(const Plan& p, const xhc_bwd_args* a, char* ws, hipStre
 template <typename E, typename R>
 static int backward_post_impl(const Plan& p, const xhc_bwd_post_args* a, char* ws, hipStream_t st) {
   xhc_timer* tm = a->timer;
-  float* coef = reinterpret_cast<float*>(ws + p.off_coef);        // [T][64] coefficient records
+  const bool rt = p.pt;                        // per-token lists (router or caller)
+  float* coef = reinterpret_cast<float*>(ws + p.off_coef);        // [T][64] records, or [T][16] post gates
   float* dwpart = reinterpret_cast<float*>(ws + p.off_dwpart);
   float* dpart = static_cast<float*>(a->bwd_state);
-  const int rc = launch_coef_saved(p, a->z_save, coef, st, tm);
-  if (rc) return rc;
+  const int32_t* ridx = rt ? a->route_idx : nullptr;
+  const float* hpost = coef + CO_POST;
+  int hstride = COEF_STRIDE;
+  if (rt) {
+    if (a->status) {
+      TimedLaunch tl(tm, KID_CHECK, st);
+      launch_check_lists(p, a->route_idx, a->status, st);
+    }
+    // the post gates as the full backward forms them (routed slots scaled
+    // by their saved scores); no projection operand to pack here
+    TimedLaunch tl(tm, KID_BPREP, st);
+    const int nbg = (int)(((int64_t)p.T * 16 + 255) / 256);
+    k_bwd_prep<R, true><<<nbg, 256, 0, st>>>(a->z_save, coef, p.T, p.N, p.k, p.P, p.nc, p.gate == XHC_GATE_UNIT,
+                                             p.zsv, p.nfix, nbg, nullptr, nullptr, nullptr, p.NC);
+    hpost = coef;
+    hstride = 16;
+  } else {
+    const int rc = launch_coef_saved(p, a->z_save, coef, st, tm);
+    if (rc) return rc;
+  }
   const StreamRows src{};     // the rows of the state are not read here
   Act4 act;
-  for (int b = 0; b < 4; ++b) act.id[b] = b < p.k ? a->active[b] : 0;
+  for (int b = 0; b < 4; ++b) act.id[b] = b < p.k && !rt ? a->active[b] : 0;
   const dim3 b1grid(p.b1_cblocks, p.B * p.b1_segs);
   const bool fast = p.N == 16 && p.k == 4;
   {
     TimedLaunch tl(tm, KID_BDOTS, st);
-#define XHC_BDP(NCOMP, FAST)                                                                                    \
-  k_bdots<E, NCOMP, FAST, BD_FULL, false><<<b1grid, 256, 0, st>>>(                                               \
-      src, a->dX_new, nullptr, a->out, a->w4, a->w8, a->w12, coef + CO_POST, nullptr, dpart, a->dout, dwpart,    \
-      p.T, p.S, p.C, p.N, p.k, act, p.b1_lseg, p.b1_segs, nullptr, COEF_STRIDE)
+#define XHC_BDP(NCOMP, FAST, RT)                                                                                \
+  k_bdots<E, NCOMP, FAST, BD_FULL, RT><<<b1grid, 256, 0, st>>>(                                                  \
+      src, a->dX_new, nullptr, a->out, a->w4, a->w8, a->w12, hpost, nullptr, dpart, a->dout, dwpart, p.T, p.S,   \
+      p.C, p.N, p.k, act, p.b1_lseg, p.b1_segs, ridx, hstride)
+#define XHC_BDP_RT(NCOMP, FAST)                                                                                 \
+  do {                                                                                                         \
+    if (rt) XHC_BDP(NCOMP, FAST, true); else XHC_BDP(NCOMP, FAST, false);                                       \
+  } while (0)
     if (p.nc == 4) {
-      if (fast) XHC_BDP(4, true); else XHC_BDP(4, false);
+      if (fast) XHC_BDP_RT(4, true); else XHC_BDP_RT(4, false);
     } else {
-      if (fast) XHC_BDP(1, true); else XHC_BDP(1, false);
+      if (fast) XHC_BDP_RT(1, true); else XHC_BDP_RT(1, false);
     }
+#undef XHC_BDP_RT
 #undef XHC_BDP
   }
   if (p.nc == 4) {
@@ -1848,6 +1872,7 @@ static int backward_post_impl(const Plan& p, const xhc_bwd_post_args* a, char* w
 template <typename E, typename R>
 static int backward_pre_impl(const Plan& p, const xhc_bwd_pre_args* a, char* ws, hipStream_t st) {
   xhc_timer* tm = a->timer;
+  const bool rt = p.pt;                        // per-token lists (router or caller)
   const float* zin = a->z_save;
   void* Wp = ws + p.off_wp;
   float* dpa = reinterpret_cast<float*>(ws + p.off_dpa);
@@ -1855,51 +1880,78 @@ static int backward_pre_impl(const Plan& p, const xhc_bwd_pre_args* a, char* ws,
   float* dz = reinterpret_cast<float*>(ws + p.off_dz);
   unsigned char* rec = reinterpret_cast<unsigned char*>(ws + p.off_rec);
   float* dwp = reinterpret_cast<float*>(ws + p.off_dwpart2);
+  float* hres = reinterpret_cast<float*>(ws + p.off_hres);
+  void* pass = ws + p.off_pass;
+  float* rred = reinterpret_cast<float*>(ws + p.off_rred);
   const float* dpart = static_cast<const float*>(a->bwd_state);
-  const StreamRows src = stream_rows(p, a->X, a->xact, a->active);
+  const int32_t* ridx = rt ? a->route_idx : nullptr;
+  // with per-token lists the saved rows are mapped per token inside the kernels
+  const StreamRows src = stream_rows(p, a->X, rt ? nullptr : a->xact, a->active);
   Act4 act;
-  for (int b = 0; b < 4; ++b) act.id[b] = b < p.k ? a->active[b] : 0;
+  for (int b = 0; b < 4; ++b) act.id[b] = b < p.k && !rt ? a->active[b] : 0;
   const HresActive ha = hres_active(p, a->active);
   {
     TimedLaunch tl(tm, KID_BXDOTS, st);
-    k_bxdots<E, R, false><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(
-        src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, p.P, static_cast<const R*>(a->W),
-        static_cast<R*>(Wp), p.NC, nullptr, nullptr, nullptr, 1);
+#define XHC_BX(RT)                                                                                             \
+  k_bxdots<E, R, RT><<<p.bx_cblocks * p.bx_tiles, 64 * BX_WAVES, 0, st>>>(                                      \
+      src, a->dX_new, a->dh_in, dpa, p.T, p.C, p.N, p.k, act, p.bx_cblocks, p.P, static_cast<const R*>(a->W),   \
+      static_cast<R*>(Wp), p.NC, ridx, static_cast<const R*>(p.R ? a->W_route : nullptr), rt ? a->xact : nullptr, \
+      1)
+    if (rt) XHC_BX(true); else XHC_BX(false);
+#undef XHC_BX
   }
   {
     TimedLaunch tl(tm, KID_BCOEF, st);
     const int nb = (int)((p.Tpad + BCOEF_TOK - 1) / BCOEF_TOK);
     const size_t shm = (size_t)BCOEF_TOK * (p.iters + 1) * 16 * sizeof(float);
-    k_bcoef<E, false, false><<<nb, 16 * BCOEF_TOK, shm, st>>>(
-        dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T, p.Tpad, p.N, p.k, p.nc, p.P,
-        1.0f / (float)p.NC, p.iters, p.gate == XHC_GATE_UNIT, 0.f, hpost, nullptr, p.zsv, p.dzs, nullptr, p.nfix,
-        nullptr, 0, ha);
+#define XHC_BCOEF(RT)                                                                                           \
+  k_bcoef<E, false, RT><<<nb, 16 * BCOEF_TOK, shm, st>>>(                                                        \
+      dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T, p.Tpad, p.N, p.k, p.nc, p.P,           \
+      1.0f / (float)p.NC, p.iters, p.gate == XHC_GATE_UNIT, 0.f, hpost, nullptr, p.zsv, p.dzs, ridx, p.nfix,   \
+      hres, p.R > 0, ha)
+    if (rt) XHC_BCOEF(true); else XHC_BCOEF(false);
+#undef XHC_BCOEF
+  }
+  if (rt) {
+    TimedLaunch tl(tm, KID_RPASS, st);
+    launch_route_pass(p, a->dX_new, ridx, hres, pass, st);
   }
   {
     TimedLaunch tl(tm, KID_BGRAD, st);
     RowTable rows;
     for (int g = 0; g < 5; ++g)
       for (int w = 0; w < 4; ++w) rows.stream[g][w] = -1;
-    for (int w = 0; w < p.k; ++w) rows.stream[0][w] = a->active[w];
-    int nxt = 0;
-    for (int i = 0; i < p.N; ++i) {
-      bool is_act = false;
-      for (int b = 0; b < p.k; ++b) is_act |= a->active[b] == i;
-      if (is_act) continue;
-      rows.stream[1 + nxt / 4][nxt % 4] = i;
-      ++nxt;
-    }
     const int nb = p.b2_rowgroups * p.b2_cblocks * p.b2_ts;
-    k_bgrad<E><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, (int)(p.Tpad / B2_TT), a->dX, dwp,
-                                             p.T, p.C, p.N, p.k, rows, p.b2_rowgroups, p.b2_cblocks,
-                                             p.b2_tok_per_split, ha.res0, ha.mask ? ha.res1 : ha.res0);
+    if (rt) {
+      for (int i = 0; i < p.N; ++i) rows.stream[i / 4][i % 4] = i;
+      k_bgrad_route<E><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, (int)(p.Tpad / B2_TT),
+                                                     a->dX, dwp, p.T, p.C, p.N, p.k, rows, p.b2_rowgroups,
+                                                     p.b2_cblocks, p.b2_tok_per_split, pass, ridx, a->xact);
+    } else {
+      for (int w = 0; w < p.k; ++w) rows.stream[0][w] = a->active[w];
+      int nxt = 0;
+      for (int i = 0; i < p.N; ++i) {
+        bool is_act = false;
+        for (int b = 0; b < p.k; ++b) is_act |= a->active[b] == i;
+        if (is_act) continue;
+        rows.stream[1 + nxt / 4][nxt % 4] = i;
+        ++nxt;
+      }
+      k_bgrad<E><<<nb, 64 * B2_WAVES, 0, st>>>(src, a->dX_new, a->dh_in, Wp, rec, (int)(p.Tpad / B2_TT), a->dX,
+                                               dwp, p.T, p.C, p.N, p.k, rows, p.b2_rowgroups, p.b2_cblocks,
+                                               p.b2_tok_per_split, ha.res0, ha.mask ? ha.res1 : ha.res0);
+    }
   }
   {
     TimedLaunch tl(tm, KID_BREDUCE, st);
     const int nb_dw = (int)((p.NC * ((p.P + 3) / 4) + 255) / 256);
-    k_reduce<<<nb_dw + p.P, 256, 0, st>>>(dwp, p.b2_ts, p.NC, p.P, a->dW, dz, p.T, a->db, nullptr, 0, p.C, nullptr,
-                                          nullptr, nullptr, nb_dw, a->accumulate, p.dwr, p.dzs, 0, nullptr, nullptr,
-                                          p.N, ha);
+    k_reduce<<<nb_dw + p.P + (rt ? 32 : 0), 256, 0, st>>>(
+        dwp, p.b2_ts, p.NC, p.P, a->dW, dz, p.T, a->db, nullptr, 0, p.C, nullptr, nullptr, nullptr, nb_dw,
+        a->accumulate, p.dwr, p.dzs, 0, p.R ? a->db_route : nullptr, rred, p.N, ha);
+  }
+  if (p.R) {
+    TimedLaunch tl(tm, KID_RDWR, st);
+    launch_route_dwr(p, dwp, rred, a->dW_route, a->accumulate, st);
   }
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
 }

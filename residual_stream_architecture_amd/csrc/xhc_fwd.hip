@@ -521,10 +521,13 @@ __global__ __launch_bounds__(256) void k_coef(const float* __restrict__ zpart, i
 // (CO_IDX, written by the router) or from the caller's lists `ids` [T][k]
 // (ids outside [0, N) read as 0), by uniform scalar loads two tokens ahead
 // of their use in addresses, instead of `act`.
+// POST (the split forward's second call, in place): only the sparse write --
+// each token's k active rows and `out` are read, h_in is neither formed nor
+// written (hin is not used).
 // ---------------------------------------------------------------------------
 struct Active { int id[4]; };
 
-template <typename E, int NCOMP, bool FAST, bool ROUTE>
+template <typename E, int NCOMP, bool FAST, bool ROUTE, bool POST = false>
 __global__ __launch_bounds__(MIX_THREADS) void k_mix(
     const void* __restrict__ X, const void* __restrict__ out, const float* __restrict__ w4,
     const float* __restrict__ w8, const float* __restrict__ w12, const float* __restrict__ coef,
@@ -604,9 +607,11 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
   V xr[16], xa_r[4], ov;
   auto load_token = [&](int s, const int (&id)[4]) {
     const rsrc_t rx = make_rsrc(Xb + (tok0 + s) * tokb, tokb);
+    if constexpr (!POST) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (FULLN || i < NR) xr[i] = bload<E, MIX_CH, CP_NT>(rx, voff, (uint32_t)i * rowb);
+      for (int i = 0; i < 16; ++i)
+        if (FULLN || i < NR) xr[i] = bload<E, MIX_CH, CP_NT>(rx, voff, (uint32_t)i * rowb);
+    }
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       if (b < K) xa_r[b] = bload<E, MIX_CH>(rx, voff, (uint32_t)id[b] * rowb);
@@ -633,8 +638,10 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
     int cid[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) { cid[b] = id_a[b]; id_a[b] = id_b[b]; }
+    if constexpr (!POST) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) cx[i] = xr[i];
+      for (int i = 0; i < 16; ++i) cx[i] = xr[i];
+    }
 #pragma unroll
     for (int b = 0; b < 4; ++b) cxa[b] = xa_r[b];
     load_token(s + 1 < s1 ? s + 1 : s, id_a);    // next token (the last iteration reloads, harmlessly)
@@ -657,21 +664,23 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
     co_out.to_float(win[11]);
 
     // dense read
-    float hacc[MIX_CH];
+    if constexpr (!POST) {
+      float hacc[MIX_CH];
 #pragma unroll
-    for (int ch = 0; ch < MIX_CH; ++ch) hacc[ch] = 0.f;
+      for (int ch = 0; ch < MIX_CH; ++ch) hacc[ch] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (FULLN || i < NR) {
-        float xf[MIX_CH];
-        cx[i].to_float(xf);
-        const float hp = cpre[i];
+      for (int i = 0; i < 16; ++i) {
+        if (FULLN || i < NR) {
+          float xf[MIX_CH];
+          cx[i].to_float(xf);
+          const float hp = cpre[i];
 #pragma unroll
-        for (int ch = 0; ch < MIX_CH; ++ch) hacc[ch] = fmaf(hp, xf[ch], hacc[ch]);
+          for (int ch = 0; ch < MIX_CH; ++ch) hacc[ch] = fmaf(hp, xf[ch], hacc[ch]);
+        }
       }
+      const rsrc_t rh = make_rsrc(static_cast<char*>(hin) + t * rowb, rowb);
+      if (cv) bstore<E, MIX_CH>(V::from_float(hacc), rh, voff, 0);
     }
-    const rsrc_t rh = make_rsrc(static_cast<char*>(hin) + t * rowb, rowb);
-    if (cv) bstore<E, MIX_CH>(V::from_float(hacc), rh, voff, 0);
 
     float u[4][MIX_CH];
 #pragma unroll
@@ -716,7 +725,7 @@ __global__ __launch_bounds__(MIX_THREADS) void k_mix(
           if (xact) bstore<E, MIX_CH, CP_NT>(cxa[a], rxs, voff, (uint32_t)a * rowb);
         }
       }
-      if (!in_place) {                             // out of place: copy the untouched rows
+      if (!POST && !in_place) {                    // out of place: copy the untouched rows
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           if (FULLN || i < NR) {
@@ -877,24 +886,37 @@ static int forward_pre_impl(const Plan& p, const Plan& pn, const xhc_pre_args* a
   void* Wt = ws + p.off_wt;
   float* zpart = reinterpret_cast<float*>(ws + p.off_zpart);
   float* coef = reinterpret_cast<float*>(ws + p.off_coef);
-  const float* carry_in = static_cast<const float*>(a->carry_in);
+  float* rcs = reinterpret_cast<float*>(ws + p.off_rcs);
+  const float* carry_in = static_cast<const float*>(a->carry_in);   // never with per-token lists
+  const RouteArgs ra = route_args(p, a->active, a->b_route, a->route_idx, nullptr, rcs);
+  if (p.pt && !p.R && a->status) {
+    TimedLaunch tl(tm, KID_CHECK, st);
+    launch_check_lists(p, a->route_idx, a->status, st);
+  }
   if (!carry_in) {
-    launch_pack_wt<R>(p, a->W, Wt, st, tm);
+    if (p.R) {
+      TimedLaunch tl(tm, KID_RCOLSUM, st);
+      launch_route_colsum(p, a->W_route, rcs, st);
+    }
+    launch_pack_wt<R>(p, a->W, Wt, st, tm, p.R ? a->W_route : nullptr, ra.cand);
     launch_proj<E>(p, stream_rows(p, a->X, nullptr, a->active), Wt, zpart, st, tm);
   }
   {
     TimedLaunch tl(tm, KID_COEF, st);
     const float* zp = carry_in ? carry_in : zpart;
     const int sk = carry_in ? p.mp_ncb : p.SK;
-    k_coef<false, false><<<(p.T + 15) / 16, 256, 0, st>>>(zp, sk, p.ZST, p.NT * 16, nullptr, a->bias, coef, a->z_save,
-                                                          p.zsv, p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps,
-                                                          p.iters, p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f,
-                                                          RouteArgs{}, hres_active(p, a->active));
+#define XHC_COEF_PRE(RT)                                                                                          k_coef<false, RT><<<(p.T + 15) / 16, 256, 0, st>>>(zp, sk, p.ZST, p.NT * 16, nullptr, a->bias, coef, a->z_save,                                                       p.zsv, p.T, p.N, p.k, p.nc, p.P, 1.0f / (float)p.NC, p.eps,                                                        p.iters, p.gate == XHC_GATE_UNIT, nullptr, 0, 0.f,                                                                 RT ? ra : RouteArgs{}, hres_active(p, a->active))
+    if (p.R) XHC_COEF_PRE(true); else XHC_COEF_PRE(false);
+#undef XHC_COEF_PRE
   }
   if (a->W_next) launch_pack_wt<R>(pn, a->W_next, Wt, st, tm);
   {
     TimedLaunch tl(tm, KID_MIXPROJ, st);
-    const MixArgs m{a->X, nullptr, nullptr, nullptr, nullptr, const_cast<void*>(a->X), a->h_in, nullptr, a->active};
+    // the dense read visits every row once, whatever the lists: with
+    // per-token lists any row order serves
+    static const int32_t kOrder[4] = {0, 1, 2, 3};
+    const MixArgs m{a->X, nullptr, nullptr, nullptr, nullptr, const_cast<void*>(a->X), a->h_in, nullptr,
+                    p.pt ? kOrder : a->active};
     launch_mixproj(p, pn, MIX_PRE, m, coef, a->W_next ? Wt : nullptr, static_cast<float*>(a->carry_out), st);
   }
   return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
@@ -923,6 +945,28 @@ static int forward_post_impl(const Plan& p, const Plan& pn, const xhc_post_args*
                                                      HresActive{})
     if (p.gs) XHC_COEF_Z(true); else XHC_COEF_Z(false);
 #undef XHC_COEF_Z
+    // the router's write-back scales, from the saved scores
+    if (p.R) launch_route_scale_post(p, a->z_save, coef, st);
+  }
+  if (p.pt) {
+    // per-token lists (no carry): the sparse write of each token's own rows,
+    // which it reads with `out` and nothing else
+    TimedLaunch tl(tm, KID_MIX, st);
+    Active act;
+    for (int b = 0; b < 4; ++b) act.id[b] = -1;
+    const dim3 grid(p.mix_cblocks, p.B * p.mix_segs);
+#define XHC_MIX_POST(NCOMP, FULLN)                                                                              \
+  k_mix<E, NCOMP, FULLN, true, true><<<grid, MIX_THREADS, 0, st>>>(a->X, a->out, a->w4, a->w8, a->w12, coef, a->X, \
+                                                                   nullptr, a->xact_save, p.S, p.C, p.N, p.k, act, \
+                                                                   1, p.mix_lseg, p.mix_segs, a->route_idx)
+    const bool fast = p.N == 16 && p.k == 4;
+    if (p.nc == 4) {
+      if (fast) XHC_MIX_POST(4, true); else XHC_MIX_POST(4, false);
+    } else {
+      if (fast) XHC_MIX_POST(1, true); else XHC_MIX_POST(1, false);
+    }
+#undef XHC_MIX_POST
+    return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
   }
   if (a->W_next) launch_pack_wt<R>(pn, a->W_next, Wt, st, tm);
   {

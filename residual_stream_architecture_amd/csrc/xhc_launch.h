@@ -116,5 +116,8 @@ void launch_route_pass(const Plan& p, const void* dXn, const int32_t* ridx, cons
                        hipStream_t st);
 void launch_route_dwr(const Plan& p, const float* dwp, const float* rred, float* dWr, int accumulate,
                       hipStream_t st);
+// Router, split forward: the routed slots' post coefficients of records
+// rebuilt from z_save, times sigmoid of their saved scores.
+void launch_route_scale_post(const Plan& p, const float* z_save, float* coef, hipStream_t st);
 
 }  // namespace xhc

@@ -8,8 +8,9 @@
 // scaled by its score, and the score's gradient flows only through that
 // scale.  With y = (x - mean) / sd the router's logits are
 //   rho = y.Wr + b = (x.Wr - mean * colsum(Wr)) / sd + b,
-// so the projection pass forms x.Wr and sum(x) on MFMA next to the other
-// logits, and only Wr's column sums are needed apart (k_route_colsum).
+// so the projection pass forms x.Wr on MFMA next to the other logits (and
+// sum(x) beside sum(x^2)), and only Wr's column sums are needed apart
+// (k_route_colsum).
 //
 //   k_route_colsum  W_route [NC, N] -> partial column sums [RCS_BLK][16],
 //                   then (k_route_colsum_fin) the column sums [16]
@@ -18,6 +19,9 @@
 //                   term, for the dX assembly of rows chosen per token
 //   k_route_dwr     (backward) dW_route from the dX pass's partials minus
 //                   the LayerNorm mean's share
+//   k_route_scale_post (split forward, second call) the routed slots' post
+//                   coefficients of a record rebuilt from saved logits,
+//                   scaled by the saved scores as the router scaled them
 #include <algorithm>
 
 #include "xhc_device.h"
@@ -177,6 +181,28 @@ __global__ __launch_bounds__(256) void k_check_lists(const int32_t* __restrict__
 void launch_check_lists(const Plan& p, const int32_t* ids, int32_t* status, hipStream_t st) {
   const int64_t nb = ((int64_t)p.T + 255) / 256;
   k_check_lists<<<nb, 256, 0, st>>>(ids, p.T, p.k, p.N, status);
+}
+
+// The split forward's second call rebuilds the coefficient records from the
+// first call's saved logits; the routed slots' post coefficients are then
+// scaled by s = sigmoid(rho) of the score saved for that slot (z_save's
+// router record: rho of routed slot j at P + 3 + 3j), the same product the
+// router formed.  One thread per (token, post entry a*4 + m).
+__global__ __launch_bounds__(256) void k_route_scale_post(float* __restrict__ coef, const float* __restrict__ zin,
+                                                          int64_t T, int zsv, int P, int nfix, int k) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= T * 16) return;
+  const int64_t t = j >> 4;
+  const int e = (int)(j & 15), a = e >> 2;
+  if (a < nfix || a >= k) return;
+  float* c = coef + (size_t)t * COEF_STRIDE + CO_POST + e;
+  *c = *c * sigmoid(zin[(size_t)t * zsv + P + 3 + 3 * (a - nfix)]);
+}
+
+void launch_route_scale_post(const Plan& p, const float* z_save, float* coef, hipStream_t st) {
+  const int64_t n = (int64_t)p.T * 16;
+  k_route_scale_post<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(coef, z_save, (int64_t)p.T, p.zsv, p.P, p.nfix,
+                                                                  p.k);
 }
 
 }  // namespace xhc

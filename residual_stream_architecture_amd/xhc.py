@@ -63,25 +63,29 @@ class xhc_chain_args(ctypes.Structure):
 class xhc_pre_args(ctypes.Structure):
     _fields_ = [("X", _vp), ("W", _vp), ("bias", _vp), ("active", ctypes.POINTER(ctypes.c_int32)),
                 ("h_in", _vp), ("z_save", _vp), ("carry_in", _vp), ("W_next", _vp), ("carry_out", _vp),
-                ("desc_next", ctypes.POINTER(xhc_desc)), ("timer", _vp)]
+                ("desc_next", ctypes.POINTER(xhc_desc)), ("timer", _vp),
+                ("W_route", _vp), ("b_route", _vp), ("route_idx", _vp), ("status", _vp)]
 
 
 class xhc_post_args(ctypes.Structure):
     _fields_ = [("X", _vp), ("out", _vp), ("w4", _vp), ("w8", _vp), ("w12", _vp),
                 ("active", ctypes.POINTER(ctypes.c_int32)), ("z_save", _vp), ("xact_save", _vp),
-                ("W_next", _vp), ("carry_out", _vp), ("desc_next", ctypes.POINTER(xhc_desc)), ("timer", _vp)]
+                ("W_next", _vp), ("carry_out", _vp), ("desc_next", ctypes.POINTER(xhc_desc)), ("timer", _vp),
+                ("route_idx", _vp)]
 
 
 class xhc_bwd_post_args(ctypes.Structure):
     _fields_ = [("out", _vp), ("w4", _vp), ("w8", _vp), ("w12", _vp), ("active", ctypes.POINTER(ctypes.c_int32)),
                 ("z_save", _vp), ("dX_new", _vp), ("dout", _vp), ("dw4", _vp), ("dw8", _vp), ("dw12", _vp),
-                ("bwd_state", _vp), ("accumulate", ctypes.c_int32), ("timer", _vp)]
+                ("bwd_state", _vp), ("accumulate", ctypes.c_int32), ("timer", _vp),
+                ("route_idx", _vp), ("status", _vp)]
 
 
 class xhc_bwd_pre_args(ctypes.Structure):
     _fields_ = [("X", _vp), ("xact", _vp), ("W", _vp), ("bias", _vp), ("active", ctypes.POINTER(ctypes.c_int32)),
                 ("z_save", _vp), ("dX_new", _vp), ("dh_in", _vp), ("bwd_state", _vp), ("dX", _vp), ("dW", _vp),
-                ("db", _vp), ("accumulate", ctypes.c_int32), ("timer", _vp)]
+                ("db", _vp), ("accumulate", ctypes.c_int32), ("timer", _vp),
+                ("W_route", _vp), ("route_idx", _vp), ("dW_route", _vp), ("db_route", _vp)]
 
 
 class XhcError(RuntimeError):
@@ -303,14 +307,19 @@ def _desc_ptr(d):
 
 
 def forward_pre(X, W, active, h_in, z_save, *, desc, bias=None, carry_in=None, W_next=None, carry_out=None,
-                desc_next=None, workspace=None, stream=None, timer=None):
+                desc_next=None, workspace=None, stream=None, timer=None, W_route=None, b_route=None,
+                route_idx=None, status=None):
     """xhc_forward_pre: coefficients and the dense read h_in of the state X
     (read only), z_save for the post call; with W_next/carry_out the next
-    sublayer's projection partials over this sublayer's untouched rows."""
+    sublayer's projection partials over this sublayer's untouched rows.
+    With a router (desc.route > 0) W_route/b_route are read and route_idx
+    [B*S,k] int32 receives the per-token lists; with desc.per_token_active
+    route_idx holds the caller's lists (status: optional int32[2] check)."""
     act = _active_array(active)
     args = xhc_pre_args(_ptr(X), _ptr(W), _ptr(bias), ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)),
                         _ptr(h_in), _ptr(z_save), _ptr(carry_in), _ptr(W_next), _ptr(carry_out),
-                        _desc_ptr(desc_next), None if timer is None else timer.handle)
+                        _desc_ptr(desc_next), None if timer is None else timer.handle,
+                        _ptr(W_route), _ptr(b_route), _ptr(route_idx), _ptr(status))
     ws, need = _workspace(desc, XHC_PHASE_FWD, X.device, workspace, stream)
     rc = lib.xhc_forward_pre(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
                              _stream_handle(stream))
@@ -319,14 +328,16 @@ def forward_pre(X, W, active, h_in, z_save, *, desc, bias=None, carry_in=None, W
 
 
 def forward_post(X, out, active, z_save, *, desc, w4=None, w8=None, w12=None, xact_save=None, W_next=None,
-                 carry_out=None, desc_next=None, workspace=None, stream=None, timer=None):
+                 carry_out=None, desc_next=None, workspace=None, stream=None, timer=None, route_idx=None):
     """xhc_forward_post: the sparse write of the pre call's sublayer, in place
     in X, from its output `out` and the pre call's z_save; with W_next the
-    new rows' projection partials are added to the pre call's carry_out."""
+    new rows' projection partials are added to the pre call's carry_out.
+    With per-token lists (router or given) route_idx is the pre call's."""
     act = _active_array(active)
     args = xhc_post_args(_ptr(X), _ptr(out), _ptr(w4), _ptr(w8), _ptr(w12),
                          ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(z_save), _ptr(xact_save),
-                         _ptr(W_next), _ptr(carry_out), _desc_ptr(desc_next), None if timer is None else timer.handle)
+                         _ptr(W_next), _ptr(carry_out), _desc_ptr(desc_next), None if timer is None else timer.handle,
+                         _ptr(route_idx))
     ws, need = _workspace(desc, XHC_PHASE_FWD, X.device, workspace, stream)
     rc = lib.xhc_forward_post(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
                               _stream_handle(stream))
@@ -388,15 +399,18 @@ def backward(X, out, W, active, dX_new, dh_in, dX, dout, dW, *, B, S, xact=None,
 
 
 def backward_post(out, active, z_save, dX_new, dout, bwd_state, *, desc, w4=None, w8=None, w12=None, dw4=None,
-                  dw8=None, dw12=None, accumulate=False, workspace=None, stream=None, timer=None):
+                  dw8=None, dw12=None, accumulate=False, workspace=None, stream=None, timer=None, route_idx=None,
+                  status=None):
     """xhc_backward_post: dout, the conv-weight gradients and the dot
     partials (into bwd_state, a device buffer of bwd_state_size(desc) bytes)
-    from dX_new and the forward's z_save."""
+    from dX_new and the forward's z_save (and, with per-token lists, its
+    route_idx; status: optional int32[2] check of the lists)."""
     act = _active_array(active)
     args = xhc_bwd_post_args(_ptr(out), _ptr(w4), _ptr(w8), _ptr(w12),
                              ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(z_save), _ptr(dX_new),
                              _ptr(dout), _ptr(dw4), _ptr(dw8), _ptr(dw12), _ptr(bwd_state),
-                             int(bool(accumulate)), None if timer is None else timer.handle)
+                             int(bool(accumulate)), None if timer is None else timer.handle,
+                             _ptr(route_idx), _ptr(status))
     ws, need = _workspace(desc, XHC_PHASE_BWD, out.device, workspace, stream)
     rc = lib.xhc_backward_post(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
                                _stream_handle(stream))
@@ -405,14 +419,17 @@ def backward_post(out, active, z_save, dX_new, dout, bwd_state, *, desc, w4=None
 
 
 def backward_pre(X, W, active, z_save, dX_new, dh_in, bwd_state, dX, dW, *, desc, xact=None, bias=None, db=None,
-                 accumulate=False, workspace=None, stream=None, timer=None):
+                 accumulate=False, workspace=None, stream=None, timer=None, W_route=None, route_idx=None,
+                 dW_route=None, db_route=None):
     """xhc_backward_pre: dX, dW and db from dX_new, dh_in and the bwd_state
-    that xhc_backward_post left."""
+    that xhc_backward_post left; with a router also dW_route [N*C,N] and
+    db_route [N] (fp32), from W_route and the forward's route_idx."""
     act = _active_array(active)
     args = xhc_bwd_pre_args(_ptr(X), _ptr(xact), _ptr(W), _ptr(bias),
                             ctypes.cast(act, ctypes.POINTER(ctypes.c_int32)), _ptr(z_save), _ptr(dX_new),
                             _ptr(dh_in), _ptr(bwd_state), _ptr(dX), _ptr(dW), _ptr(db),
-                            int(bool(accumulate)), None if timer is None else timer.handle)
+                            int(bool(accumulate)), None if timer is None else timer.handle,
+                            _ptr(W_route), _ptr(route_idx), _ptr(dW_route), _ptr(db_route))
     ws, need = _workspace(desc, XHC_PHASE_BWD, X.device, workspace, stream)
     rc = lib.xhc_backward_pre(ctypes.byref(desc), ctypes.byref(args), ws.data_ptr(), ws.numel(),
                               _stream_handle(stream))

@@ -488,8 +488,37 @@ def test_split_forward_validation():
     b, keep = good_post(d)
     b.w8 = None
     assert xhc.validate(d, b, POST) == xhc.XHC_ERR_NULL
-    # not with a router or given lists; hres_active only without a carry
-    assert xhc.validate(desc16(route=2), good_pre(desc16(route=2))[0], PRE) == xhc.XHC_ERR_UNSUPPORTED
+    # per-token lists (a router or given lists) and hres_active only without a carry
+    for kw in (dict(route=2), dict(route=4), dict(per_token_active=True)):
+        dd = desc16(**kw)
+        a, keep = good_pre(dd)
+        assert xhc.validate(dd, a, PRE) == xhc.XHC_ERR_NULL, kw            # no route_idx
+        a.route_idx = fake(22)
+        if kw.get("route"):
+            assert xhc.validate(dd, a, PRE) == xhc.XHC_ERR_NULL, kw        # no W_route
+            a.W_route = fake(20)
+        assert xhc.validate(dd, a, PRE) == xhc.XHC_OK, kw
+        a.route_idx = a.h_in                                            # lists overlapping h_in
+        assert xhc.validate(dd, a, PRE) == xhc.XHC_ERR_ALIAS, kw
+        a, keep = good_pre(dd, chained=True)
+        a.route_idx, a.W_route = fake(22), fake(20)
+        assert xhc.validate(dd, a, PRE) == xhc.XHC_ERR_UNSUPPORTED, kw
+        b, keep = good_post(dd)
+        assert xhc.validate(dd, b, POST) == xhc.XHC_ERR_NULL, kw
+        b.route_idx = fake(22)
+        assert xhc.validate(dd, b, POST) == xhc.XHC_OK, kw
+        b.route_idx = b.X + 64                                          # the lists are an input
+        assert xhc.validate(dd, b, POST) == xhc.XHC_ERR_ALIAS, kw
+        b, keep = good_post(dd, chained=True)
+        b.route_idx = fake(22)
+        assert xhc.validate(dd, b, POST) == xhc.XHC_ERR_UNSUPPORTED, kw
+    # given lists with a status word (the router's lists are its own output)
+    dg = desc16(per_token_active=True)
+    a, keep = good_pre(dg)
+    a.route_idx, a.status = fake(22), fake(30)
+    assert xhc.validate(dg, a, PRE) == xhc.XHC_OK
+    a.status = fake(30, 4)
+    assert xhc.validate(dg, a, PRE) == xhc.XHC_ERR_ALIGN
     dh = desc16(hres_active=True)
     assert xhc.validate(dh, good_pre(dh)[0], PRE) == xhc.XHC_OK
     assert xhc.validate(dh, good_pre(dh, chained=True)[0], PRE) == xhc.XHC_ERR_UNSUPPORTED
@@ -588,11 +617,30 @@ def test_split_backward_validation():
     assert xhc.validate(d1, a, BP) == xhc.XHC_OK
     a.dw4 = fake(15)
     assert xhc.validate(d1, a, BP) == xhc.XHC_ERR_UNSUPPORTED
-    # Gram-Schmidt, a router and per-token lists are not split; hres_active is
-    for kw in (dict(gram_schmidt=True), dict(route=2), dict(per_token_active=True)):
+    # Gram-Schmidt is not split; a router, per-token lists and hres_active are
+    dd = desc16(gram_schmidt=True)
+    assert xhc.validate(dd, good_bwd_post(dd)[0], BP) == xhc.XHC_ERR_UNSUPPORTED
+    assert xhc.validate(dd, good_bwd_pre(dd)[0], BR) == xhc.XHC_ERR_UNSUPPORTED
+    for kw in (dict(route=2), dict(per_token_active=True)):
         dd = desc16(**kw)
-        assert xhc.validate(dd, good_bwd_post(dd)[0], BP) == xhc.XHC_ERR_UNSUPPORTED, kw
-        assert xhc.validate(dd, good_bwd_pre(dd)[0], BR) == xhc.XHC_ERR_UNSUPPORTED, kw
+        a, keep = good_bwd_post(dd)
+        assert xhc.validate(dd, a, BP) == xhc.XHC_ERR_NULL, kw             # no route_idx
+        a.route_idx = fake(22)
+        assert xhc.validate(dd, a, BP) == xhc.XHC_OK, kw
+        a.status = fake(30)
+        assert xhc.validate(dd, a, BP) == xhc.XHC_OK, kw
+        a.status = a.route_idx
+        assert xhc.validate(dd, a, BP) == xhc.XHC_ERR_ALIAS, kw
+        b, keep = good_bwd_pre(dd)
+        assert xhc.validate(dd, b, BR) == xhc.XHC_ERR_NULL, kw
+        b.route_idx = fake(22)
+        if kw.get("route"):
+            assert xhc.validate(dd, b, BR) == xhc.XHC_ERR_NULL, kw         # no W_route, dW_route
+            b.W_route, b.dW_route = fake(20), fake(23)
+        assert xhc.validate(dd, b, BR) == xhc.XHC_OK, kw
+        if kw.get("route"):
+            b.db_route = b.dW_route                                     # two outputs overlapping
+            assert xhc.validate(dd, b, BR) == xhc.XHC_ERR_ALIAS, kw
     dh = desc16(hres_active=True)
     assert xhc.validate(dh, good_bwd_post(dh)[0], BP) == xhc.XHC_OK
     assert xhc.validate(dh, good_bwd_pre(dh)[0], BR) == xhc.XHC_OK
