@@ -444,9 +444,11 @@ int xhc_forward_post(const xhc_desc* desc, const xhc_post_args* args, void* work
  * turn run the kernels of xhc_backward in its order and give the same
  * results bit for bit (same z_save).  With a router or given lists both
  * calls take the forward's route_idx, and the second also the router's
- * weights and gradients.  Not with Gram-Schmidt (XHC_ERR_UNSUPPORTED): there
- * this library forms dout after the coefficient backward, which needs
- * dh_in.  With accumulate = 1 each call adds to the gradients it writes. */
+ * weights and gradients.  With Gram-Schmidt the first call also runs the
+ * part of the coefficient backward that the gradient through the
+ * orthogonalisation needs (it reads the component dots and the saved
+ * logits only), and the second call runs the whole coefficient backward.
+ * With accumulate = 1 each call adds to the gradients it writes. */
 typedef struct {
   const void* out;        /* [T,C] the sublayer output                          */
   const float *w4, *w8, *w12;  /* TFA conv weights, NULL iff ncomp == 1         */

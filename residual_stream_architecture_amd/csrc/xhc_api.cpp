@@ -385,7 +385,7 @@ static int validate_bwd(const Plan& p, const xhc_bwd_args* a) {
 
 // Split backward (xhc_backward_post / xhc_backward_pre).
 static int check_split_bwd_modes(const Plan& p, int accumulate) {
-  if (p.gs) return XHC_ERR_UNSUPPORTED;
+  (void)p;
   if (accumulate != 0 && accumulate != 1) return XHC_ERR_UNSUPPORTED;
   return XHC_OK;
 }

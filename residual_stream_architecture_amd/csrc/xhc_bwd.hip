@@ -1817,48 +1817,88 @@ static int backward_post_impl(const Plan& p, const xhc_bwd_post_args* a, char* w
   float* dwpart = reinterpret_cast<float*>(ws + p.off_dwpart);
   float* dpart = static_cast<float*>(a->bwd_state);
   const int32_t* ridx = rt ? a->route_idx : nullptr;
-  const float* hpost = coef + CO_POST;
-  int hstride = COEF_STRIDE;
-  if (rt) {
-    if (a->status) {
-      TimedLaunch tl(tm, KID_CHECK, st);
-      launch_check_lists(p, a->route_idx, a->status, st);
-    }
-    // the post gates as the full backward forms them (routed slots scaled
-    // by their saved scores); no projection operand to pack here
-    TimedLaunch tl(tm, KID_BPREP, st);
-    const int nbg = (int)(((int64_t)p.T * 16 + 255) / 256);
-    k_bwd_prep<R, true><<<nbg, 256, 0, st>>>(a->z_save, coef, p.T, p.N, p.k, p.P, p.nc, p.gate == XHC_GATE_UNIT,
-                                             p.zsv, p.nfix, nbg, nullptr, nullptr, nullptr, p.NC);
-    hpost = coef;
-    hstride = 16;
-  } else {
-    const int rc = launch_coef_saved(p, a->z_save, coef, st, tm);
-    if (rc) return rc;
+  if (rt && a->status) {
+    TimedLaunch tl(tm, KID_CHECK, st);
+    launch_check_lists(p, a->route_idx, a->status, st);
   }
   const StreamRows src{};     // the rows of the state are not read here
   Act4 act;
   for (int b = 0; b < 4; ++b) act.id[b] = b < p.k && !rt ? a->active[b] : 0;
   const dim3 b1grid(p.b1_cblocks, p.B * p.b1_segs);
   const bool fast = p.N == 16 && p.k == 4;
-  {
-    TimedLaunch tl(tm, KID_BDOTS, st);
-#define XHC_BDP(NCOMP, FAST, RT)                                                                                \
-  k_bdots<E, NCOMP, FAST, BD_FULL, RT><<<b1grid, 256, 0, st>>>(                                                  \
-      src, a->dX_new, nullptr, a->out, a->w4, a->w8, a->w12, hpost, nullptr, dpart, a->dout, dwpart, p.T, p.S,   \
-      p.C, p.N, p.k, act, p.b1_lseg, p.b1_segs, ridx, hstride)
-#define XHC_BDP_RT(NCOMP, FAST)                                                                                 \
+#define XHC_BDP(GRID, NCOMP, FAST, MODE, LSEG, SEGS, RT, HP, GSS, HSTRIDE)                                      \
+  k_bdots<E, NCOMP, FAST, MODE, RT><<<GRID, 256, 0, st>>>(src, a->dX_new, nullptr, a->out, a->w4, a->w8, a->w12, \
+                                                          HP, GSS, dpart, a->dout, dwpart, p.T, p.S, p.C, p.N,   \
+                                                          p.k, act, LSEG, SEGS, ridx, HSTRIDE)
+#define XHC_BDP_RT(GRID, NCOMP, MODE, LSEG, SEGS, HP, GSS, HSTRIDE)                                             \
   do {                                                                                                         \
-    if (rt) XHC_BDP(NCOMP, FAST, true); else XHC_BDP(NCOMP, FAST, false);                                       \
+    if (rt) {                                                                                                  \
+      if (fast) XHC_BDP(GRID, NCOMP, true, MODE, LSEG, SEGS, true, HP, GSS, HSTRIDE);                          \
+      else XHC_BDP(GRID, NCOMP, false, MODE, LSEG, SEGS, true, HP, GSS, HSTRIDE);                              \
+    } else {                                                                                                   \
+      if (fast) XHC_BDP(GRID, NCOMP, true, MODE, LSEG, SEGS, false, HP, GSS, HSTRIDE);                         \
+      else XHC_BDP(GRID, NCOMP, false, MODE, LSEG, SEGS, false, HP, GSS, HSTRIDE);                             \
+    }                                                                                                          \
   } while (0)
-    if (p.nc == 4) {
-      if (fast) XHC_BDP_RT(4, true); else XHC_BDP_RT(4, false);
-    } else {
-      if (fast) XHC_BDP_RT(1, true); else XHC_BDP_RT(1, false);
+  if (p.gs) {
+    // Gram-Schmidt: the gradient through T needs the full-C dots <G_a, U_m>
+    // and the Gram record (first pass, into bwd_state), then Ht = H_post T
+    // and Sg from the coefficient backward's Gram-Schmidt part -- which reads
+    // only those dots and the saved logits, not the state dots that need
+    // dh_in -- and dout from the second pass.  The coefficient backward runs
+    // here with no state-dot blocks for those records alone (its dz and
+    // tile records are formed again, in full, by xhc_backward_pre).
+    float* hpost = coef;
+    float* gss = reinterpret_cast<float*>(ws + p.off_gss);
+    {
+      TimedLaunch tl(tm, KID_BDOTS, st);
+      int lseg, segs;
+      dots_segments(p, lseg, segs);
+      const dim3 g2(p.b1_cblocks, p.B * segs);
+      XHC_BDP_RT(g2, 4, BD_GSDOTS, lseg, segs, hpost, gss, 16);
     }
+    {
+      TimedLaunch tl(tm, KID_BCOEF, st);
+      float* dpa = reinterpret_cast<float*>(ws + p.off_dpa);
+      float* dz = reinterpret_cast<float*>(ws + p.off_dz);
+      unsigned char* rec = reinterpret_cast<unsigned char*>(ws + p.off_rec);
+      float* hres = reinterpret_cast<float*>(ws + p.off_hres);
+      const int nb = (int)((p.Tpad + BCOEF_TOK - 1) / BCOEF_TOK);
+      const size_t shm = (size_t)BCOEF_TOK * (p.iters + 1) * 16 * sizeof(float);
+#define XHC_BCOEF_GS(RT)                                                                                        \
+  k_bcoef<E, true, RT><<<nb, 16 * BCOEF_TOK, shm, st>>>(                                                         \
+      dpa, 0, dpart, p.b1_cblocks, a->z_save, nullptr, dz, rec, p.T, p.Tpad, p.N, p.k, p.nc, p.P,                \
+      1.0f / (float)p.NC, p.iters, p.gate == XHC_GATE_UNIT, p.gs_ceps, hpost, gss, p.zsv, p.dzs, ridx, p.nfix, \
+      hres, p.R > 0, HresActive{})
+      if (rt) XHC_BCOEF_GS(true); else XHC_BCOEF_GS(false);
+#undef XHC_BCOEF_GS
+    }
+    {
+      TimedLaunch tl(tm, KID_BDOTS_GS, st);
+      XHC_BDP_RT(b1grid, 4, BD_GSGRAD, p.b1_lseg, p.b1_segs, hpost, gss, 16);
+    }
+  } else {
+    const float* hpost = coef + CO_POST;
+    int hstride = COEF_STRIDE;
+    if (rt) {
+      // the post gates as the full backward forms them (routed slots scaled
+      // by their saved scores); no projection operand to pack here
+      TimedLaunch tl(tm, KID_BPREP, st);
+      const int nbg = (int)(((int64_t)p.T * 16 + 255) / 256);
+      k_bwd_prep<R, true><<<nbg, 256, 0, st>>>(a->z_save, coef, p.T, p.N, p.k, p.P, p.nc, p.gate == XHC_GATE_UNIT,
+                                               p.zsv, p.nfix, nbg, nullptr, nullptr, nullptr, p.NC);
+      hpost = coef;
+      hstride = 16;
+    } else {
+      const int rc = launch_coef_saved(p, a->z_save, coef, st, tm);
+      if (rc) return rc;
+    }
+    TimedLaunch tl(tm, KID_BDOTS, st);
+    if (p.nc == 4) XHC_BDP_RT(b1grid, 4, BD_FULL, p.b1_lseg, p.b1_segs, hpost, nullptr, hstride);
+    else XHC_BDP_RT(b1grid, 1, BD_FULL, p.b1_lseg, p.b1_segs, hpost, nullptr, hstride);
+  }
 #undef XHC_BDP_RT
 #undef XHC_BDP
-  }
   if (p.nc == 4) {
     TimedLaunch tl(tm, KID_BREDUCE, st);
     const int nb_conv = (int)(((int64_t)p.C * 24 * RED_CONV_LANES + 255) / 256);
@@ -1904,12 +1944,17 @@ static int backward_pre_impl(const Plan& p, const xhc_bwd_pre_args* a, char* ws,
     TimedLaunch tl(tm, KID_BCOEF, st);
     const int nb = (int)((p.Tpad + BCOEF_TOK - 1) / BCOEF_TOK);
     const size_t shm = (size_t)BCOEF_TOK * (p.iters + 1) * 16 * sizeof(float);
-#define XHC_BCOEF(RT)                                                                                           \
-  k_bcoef<E, false, RT><<<nb, 16 * BCOEF_TOK, shm, st>>>(                                                        \
+    float* gss = reinterpret_cast<float*>(ws + p.off_gss);
+#define XHC_BCOEF(GS, RT)                                                                                       \
+  k_bcoef<E, GS, RT><<<nb, 16 * BCOEF_TOK, shm, st>>>(                                                           \
       dpa, p.bx_cblocks, dpart, p.b1_cblocks, zin, a->bias, dz, rec, p.T, p.Tpad, p.N, p.k, p.nc, p.P,           \
-      1.0f / (float)p.NC, p.iters, p.gate == XHC_GATE_UNIT, 0.f, hpost, nullptr, p.zsv, p.dzs, ridx, p.nfix,   \
-      hres, p.R > 0, ha)
-    if (rt) XHC_BCOEF(true); else XHC_BCOEF(false);
+      1.0f / (float)p.NC, p.iters, p.gate == XHC_GATE_UNIT, GS ? p.gs_ceps : 0.f, hpost, GS ? gss : nullptr,    \
+      p.zsv, p.dzs, ridx, p.nfix, hres, p.R > 0, ha)
+    if (p.gs) {
+      if (rt) XHC_BCOEF(true, true); else XHC_BCOEF(true, false);
+    } else {
+      if (rt) XHC_BCOEF(false, true); else XHC_BCOEF(false, false);
+    }
 #undef XHC_BCOEF
   }
   if (rt) {

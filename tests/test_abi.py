@@ -617,10 +617,10 @@ def test_split_backward_validation():
     assert xhc.validate(d1, a, BP) == xhc.XHC_OK
     a.dw4 = fake(15)
     assert xhc.validate(d1, a, BP) == xhc.XHC_ERR_UNSUPPORTED
-    # Gram-Schmidt is not split; a router, per-token lists and hres_active are
+    # Gram-Schmidt, a router, per-token lists and hres_active are split
     dd = desc16(gram_schmidt=True)
-    assert xhc.validate(dd, good_bwd_post(dd)[0], BP) == xhc.XHC_ERR_UNSUPPORTED
-    assert xhc.validate(dd, good_bwd_pre(dd)[0], BR) == xhc.XHC_ERR_UNSUPPORTED
+    assert xhc.validate(dd, good_bwd_post(dd)[0], BP) == xhc.XHC_OK
+    assert xhc.validate(dd, good_bwd_pre(dd)[0], BR) == xhc.XHC_OK
     for kw in (dict(route=2), dict(per_token_active=True)):
         dd = desc16(**kw)
         a, keep = good_bwd_post(dd)

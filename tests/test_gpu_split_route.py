@@ -17,7 +17,9 @@ xhc_backward_pre (dX, dW, the router's gradients).
   on h_in, against the oracle given that output.
 - The split backward runs xhc_backward's kernels in its order: its results
   equal xhc_backward's bit for bit, from the forward's input and from an
-  in-place forward's state and saved rows."""
+  in-place forward's state and saved rows.  That holds with Gram-Schmidt
+  too (one list for every token, the router, given lists), where the first
+  call also runs the orthogonalisation's part of the coefficient backward."""
 import numpy as np
 import pytest
 import torch
@@ -33,10 +35,9 @@ pytestmark = pytest.mark.gpu
 W_ = synth.Workload
 
 # routed cases of the router tests: 2 fixed + 2 routed, ragged, 1 fixed + 3
-# routed, Gram-Schmidt (forward only: the split backward does not take it),
-# one component, nothing fixed at N = 16
+# routed, Gram-Schmidt, one component, nothing fixed at N = 16
 FWD_CASES = [0, 1, 4, 6, 10, 12]
-BWD_CASES = [0, 1, 4, 5, 10, 11, 12]
+BWD_CASES = [0, 1, 4, 5, 6, 10, 11, 12]
 
 
 def desc_of(w, given=False):
@@ -143,8 +144,6 @@ def split_backward(w, dev, fixed, desc, X, xact, z_save, ridx, routed=True):
 @pytest.mark.parametrize("case", BWD_CASES, ids=[CASES[i][0] for i in BWD_CASES])
 def test_split_route_backward_bitwise(case):
     name, w, fixed = CASES[case]
-    if w.gs:
-        pytest.skip("the split backward does not take Gram-Schmidt")
     say(f"[split route backward] {name} B={w.B} S={w.S} C={w.C} N={w.N} k={w.k} R={w.route} {w.dtype}")
     d = inputs(w, 1, True)
     h = host_inputs(d)
@@ -171,11 +170,12 @@ def test_split_route_backward_bitwise(case):
         check_close(key, to_host(got[key]), rf, atol, rtol)
 
 
-def test_split_given_lists():
+@pytest.mark.parametrize("gs", [False, True], ids=["plain", "gram_schmidt"])
+def test_split_given_lists(gs):
     # caller-given per-token lists: the split pair forward and backward
     # against xhc_forward / xhc_backward with the same lists, bit for bit
-    w = W_("g", 2, 77, 136, 16, 4, 4, "bf16", "fwdbwd")
-    say(f"[split given lists] B={w.B} S={w.S} C={w.C}")
+    w = W_("g", 2, 77, 136, 16, 4, 4, "bf16", "fwdbwd", gs=gs)
+    say(f"[split given lists] B={w.B} S={w.S} C={w.C} gs={gs}")
     d = synth.make_inputs(w, seed=5, grads=True)
     d.update(synth.make_router(w, 5))
     dev = device_inputs(d, True)
@@ -205,3 +205,42 @@ def test_split_given_lists():
     got = split_backward(w, dev, [], desc, X, xact, z_save, ld, routed=False)
     for key in got:
         assert torch.equal(got[key], ref[key]), f"{key} differs from xhc_backward's"
+
+
+@pytest.mark.parametrize("name,w,active", [
+    ("gs_ragged_bf16", W_("s", 2, 77, 136, 16, 4, 4, "bf16", "fwdbwd", gs=True), [5, 12, 0, 9]),
+    ("gs_k3_f32", W_("s", 2, 41, 72, 11, 3, 4, "f32", "fwdbwd", gs=True), [10, 2, 6]),
+], ids=["gs_ragged_bf16", "gs_k3_f32"])
+def test_split_gram_schmidt_backward_bitwise(name, w, active):
+    # one list for every token, Gram-Schmidt on: the split pair equals
+    # xhc_backward bit for bit, and the oracle within tolerance
+    say(f"[split gram-schmidt backward] {name} B={w.B} S={w.S} C={w.C} N={w.N} k={w.k} {w.dtype}")
+    d = synth.make_inputs(w, seed=3, grads=True)
+    h = host_inputs(d)
+    dev = device_inputs(d, w.dtype == "bf16")
+    desc = desc_of(w)
+    T, N, C, P, k = w.T, w.N, w.C, w.P, w.k
+    X = dev["X"].clone()
+    h_in = torch.empty(T, C, dtype=X.dtype, device=X.device)
+    z_save = torch.empty(T, xhc.zsave_stride(desc), device=X.device)
+    xact = torch.empty(T, k, C, dtype=X.dtype, device=X.device)
+    xhc.forward(X, dev["out"], dev["W"], active, X, h_in, B=w.B, S=w.S, bias=dev["bias"], z_save=z_save,
+                xact_save=xact, desc=desc, **conv_kw(dev, w))
+    f32 = dict(dtype=torch.float32, device=X.device)
+    ref = dict(dX=torch.empty_like(dev["dX_new"]), dout=torch.empty(T, C, dtype=X.dtype, device=X.device),
+               dW=torch.empty((N * C, P), **f32), db=torch.empty((P,), **f32))
+    grads = {key: torch.empty((C, K), **f32) for key, K in (("dw4", 4), ("dw8", 8), ("dw12", 12))}
+    xhc.backward(X, dev["out"], dev["W"], active, dev["dX_new"], dev["dh_in"], ref["dX"], ref["dout"], ref["dW"],
+                 B=w.B, S=w.S, xact=xact, bias=dev["bias"], z_save=z_save, db=ref["db"], desc=desc,
+                 **conv_kw(dev, w), **grads)
+    torch.cuda.synchronize()
+    ref.update(grads)
+    got = split_backward(w, dev, active, desc, X, xact, z_save, None, routed=False)
+    for key in got:
+        assert torch.equal(got[key], ref[key]), f"{key} differs from xhc_backward's"
+    convs = (h["w4"], h["w8"], h["w12"])
+    g = xo.backward(h["X"], h["out"], h["W"], h["bias"], active, convs, h["dX_new"], h["dh_in"], B=w.B, S=w.S,
+                    iters=w.iters, eps=w.eps, gram_schmidt_on=True, gs_eps=GS_EPS)
+    atol, rtol = tol(w)
+    for key in ("dX", "dout"):
+        check_close(key, to_host(got[key]), g[key], atol, rtol)
