@@ -307,7 +307,13 @@ def forward_bench(args, w, np, torch, synth, xhc):
                          w12=torch.randn(C, 12, generator=g, device="cuda") * 0.02)
             p.update(W=(torch.randn(N * C, Pl, generator=g, device="cuda") * 0.02).to(sdt),
                      bias=torch.zeros(Pl, device="cuda"))
-        desc = xhc.make_desc(w.B, w.S, C, N, k, nc, code, w.iters, w.eps, gram_schmidt=w.gs)
+        if w.route and w.layers > 1:
+            # the router's weights of the sublayer (its fixed streams: the
+            # first k - R of its rotating set)
+            p.update(W_route=(torch.randn(N * C, N, generator=g, device="cuda") * 0.02).to(sdt),
+                     b_route=torch.zeros(N, device="cuda"),
+                     route_idx=torch.empty(T, k, dtype=torch.int32, device="cuda"))
+        desc = xhc.make_desc(w.B, w.S, C, N, k, nc, code, w.iters, w.eps, gram_schmidt=w.gs, route=w.route)
         layers.append((p, synth.active_streams(l, N, k), desc, nc))
     del d
     h_in = torch.empty(T, C, dtype=sdt, device="cuda")
@@ -325,6 +331,10 @@ def forward_bench(args, w, np, torch, synth, xhc):
                              W_next=None if last else layers[l + 1][0]["W"],
                              carry_out=None if last else carries[(l + 1) % 2],
                              desc_next=None if last else layers[l + 1][2])
+                if w.route and not last:
+                    extra.update(W_route_next=layers[l + 1][0]["W_route"], active_next=layers[l + 1][1])
+            if w.route:
+                extra.update(W_route=p["W_route"], b_route=p["b_route"], route_idx=p["route_idx"])
             xhc.forward(X, p["out"], p["W"], active, X, h_in, B=w.B, S=w.S, bias=p["bias"], workspace=ws_f,
                         timer=timer, desc=desc, **conv, **extra)
 
@@ -343,6 +353,10 @@ def forward_bench(args, w, np, torch, synth, xhc):
         step(timer)
     torch.cuda.synchronize()
     kb = kernel_bytes(w, esz, save_rows=False)
+    if w.route:
+        # the stack's fused pass moves the same 22C per token with the router
+        # (a token's routed rows are read twice, the second time from L2)
+        kb["mixproj"] = (N + 1 + 1 + k) * T * C * esz + N * C * (P + N) * esz
     for name in xhc.kernel_names():
         ms, n = timer.read(name)
         if n:
@@ -361,6 +375,8 @@ def forward_bench(args, w, np, torch, synth, xhc):
               "config": {"workload": f"{w.name}: B={w.B} S={w.S} C={C} N={N} k={k} ncomp={w.ncomp} "
                                      f"layers={w.layers}"
                                      + (" (even sublayers attention-side: ncomp=1)" if w.alt else "")
+                                     + (f" router: {k - w.route} fixed + {w.route} routed streams per token"
+                                        if w.route else "")
                                      + ", in-place forward"
                                      + (", chained projection" if chain else "")},
               "layer_tokens_per_s": round(T * w.layers * args.steps / elapsed, 1),

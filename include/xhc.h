@@ -136,8 +136,8 @@ enum {
  * s = sigmoid(rho):  X_new[t, i_a] = sum_b H_res[a,b] X[t, i_b]
  * + s_a sum_m H_post[a,m] U_m.  The choice is discrete: the gradient reaches
  * the chosen streams' scores through s only.  Supported with 1 <= R <= k
- * (R = k: no fixed stream, all N streams are candidates); not with the
- * chained forward.
+ * (R = k: no fixed stream, all N streams are candidates); chained as
+ * xhc_chain_args states.
  *
  * H_res from the active rows (hres_active = 1; source: the retrospective's
  * section "模型可以拥有 16 条 streams，但每层只更新 4 条", which credits the
@@ -170,7 +170,8 @@ typedef struct {
                                must hold distinct streams, ids outside
                                [0, N) are read as 0, and the calls report
                                such lists through args->status); requires
-                               route = 0 and is not chained.  0: off        */
+                               route = 0; chained as xhc_chain_args
+                               states.  0: off                              */
   int32_t hres_active;      /* 1: H_res generated from the k active rows (see
                                below); requires route = 0 and
                                per_token_active = 0, and is not chained.
@@ -327,7 +328,16 @@ int xhc_backward(const xhc_desc* desc, const xhc_bwd_args* args,
  * sublayer's projection partials (x'.W' and sum x'^2 over each block of
  * channels, x' = X_new as stored), and the next call starts from them
  * instead of reading its state a second time.  Results equal those of
- * xhc_forward called layer by layer, up to the order of fp32 sums. */
+ * xhc_forward called layer by layer, up to the order of fp32 sums.
+ *
+ * Per-token lists (a router, desc->route > 0, or given lists) chain at N = 16
+ * and k = 4, in place, with route = 2 (two fixed, two routed slots), route =
+ * 4 or given lists (XHC_ERR_UNSUPPORTED otherwise): the pass reads each
+ * token's own active rows and projects the new state row by row, the
+ * routed rows' new values in place of the values it read.  A next sublayer
+ * with a router gets its router's logits and sum(x') in the carry too; the
+ * call then needs that sublayer's W_route_next and (with fixed slots) its
+ * active_next. */
 typedef struct {
   const void* carry_in;   /* NULL: project X here as xhc_forward does; else the
                              carry_out of the previous call, whose X_new is
@@ -342,6 +352,10 @@ typedef struct {
                              NULL: the same as this call's.  W_next is then
                              [N*C, P of desc_next].  XHC_ERR_SHAPE when B, S,
                              C, N or dtype differ from this call's          */
+  const void* W_route_next;  /* [N*C,N] the next sublayer's router weights, iff
+                             it has a router (and W_next is given)           */
+  const int32_t* active_next; /* HOST [k] the next sublayer's active list (its
+                             fixed slots are read), with a router there      */
 } xhc_chain_args;
 
 /* Bytes of one carry buffer (fp32 partials per token and channel block);

@@ -213,16 +213,29 @@ static int validate_fwd(const Plan& p, const xhc_fwd_args* a, bool need_W = true
 // pn: the next sublayer's plan (== p without desc_next)
 static int validate_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, const xhc_chain_args* c) {
   if (!c) return XHC_OK;
-  if (p.pt || pn.pt) return XHC_ERR_UNSUPPORTED;
+  if (p.pt) {
+    // per-token lists: the full pass at N = 16, k = 4, in place, with two or
+    // four slots chosen per token
+    const int rts = p.R ? p.R : p.k;
+    if (p.N != 16 || p.k != 4 || a->X_new != a->X || (rts != 2 && rts != 4)) return XHC_ERR_UNSUPPORTED;
+  }
   // the carried partials sum every stream of a channel block
   if (p.hact || pn.hact) return XHC_ERR_UNSUPPORTED;
   if ((c->W_next == nullptr) != (c->carry_out == nullptr)) return XHC_ERR_NULL;
   if (misaligned(c->carry_in) || misaligned(c->carry_out) || misaligned(c->W_next)) return XHC_ERR_ALIGN;
+  if (c->W_next && pn.R) {
+    // the next sublayer's router columns and candidate order
+    if (!c->W_route_next) return XHC_ERR_NULL;
+    if (misaligned(c->W_route_next)) return XHC_ERR_ALIGN;
+    const int rc = check_active(pn, c->active_next);
+    if (rc) return rc;
+  }
   if (pn.B != p.B || pn.S != p.S || pn.C != p.C || pn.N != p.N || pn.dtype != p.dtype) return XHC_ERR_SHAPE;
   const size_t T = p.T, e = p.esz;
   const Span cin = span(c->carry_in, c->carry_in ? p.carry_bytes : 0);
   const Span cout = span(c->carry_out, c->carry_out ? pn.carry_bytes : 0);
   const Span Wn = span(c->W_next, c->W_next ? (size_t)pn.NC * pn.P * e : 0);
+  const Span Wrn = span(c->W_next && pn.R ? c->W_route_next : nullptr, (size_t)pn.NC * pn.N * e);
   const Span X = span(a->X, T * p.NC * e), Xn = span(a->X_new, T * p.NC * e);
   const Span out = span(a->out, T * p.C * e), hin = span(a->h_in, T * p.C * e);
   const Span W = span(a->W, a->W ? (size_t)p.NC * p.P * e : 0);
@@ -231,21 +244,22 @@ static int validate_chain(const Plan& p, const Plan& pn, const xhc_fwd_args* a, 
              w12 = span(a->w12, a->w12 ? (size_t)p.C * 48 : 0);
   const Span zs = span(a->z_save, a->z_save ? T * p.zsv * 4 : 0);
   const Span xs = span(a->xact_save, a->xact_save ? T * p.k * p.C * e : 0);
-  const Span outs[] = {Xn, hin, zs, xs};
-  const Span ins[] = {X, out, W, bias, w4, w8, w12};
+  const Span ri = span(p.pt ? a->route_idx : nullptr, T * p.k * 4);
+  const Span outs[] = {Xn, hin, zs, xs, p.R ? ri : Span{nullptr, 0}};
+  const Span ins[] = {X, out, W, bias, w4, w8, w12, p.R ? Span{nullptr, 0} : ri};
   // carry_out: an output (carry_in identical to it is permitted)
   if (c->carry_out) {
     for (const Span& o : outs)
       if (overlap(cout, o)) return XHC_ERR_ALIAS;
     for (const Span& i : ins)
       if (overlap(cout, i)) return XHC_ERR_ALIAS;
-    if (overlap(cout, Wn)) return XHC_ERR_ALIAS;
+    if (overlap(cout, Wn) || overlap(cout, Wrn)) return XHC_ERR_ALIAS;
     if (c->carry_in && c->carry_in != c->carry_out && overlap(cout, cin)) return XHC_ERR_ALIAS;
   }
   // carry_in and W_next: inputs, no overlap with the call's outputs
   for (const Span& o : outs) {
     if (overlap(cin, o)) return XHC_ERR_ALIAS;
-    if (overlap(Wn, o)) return XHC_ERR_ALIAS;
+    if (overlap(Wn, o) || overlap(Wrn, o)) return XHC_ERR_ALIAS;
   }
   return XHC_OK;
 }

@@ -48,6 +48,19 @@
 //            rewritten (TFA, new rows, xact_save), and their new values'
 //            partials are added to the carry the PRE pass wrote.
 // proj = 0 skips the projection (no next sublayer: no carry).
+//
+// RTS > 0 (MP_FULL, in place, N = 16, k = 4): per-token lists, the last RTS
+// of the k slots chosen per token (a router's record, CO_IDX, or the
+// caller's lists `ids`), the first 4 - RTS fixed.  The first step of a chunk
+// reads each token's own rows (the lane's row offset in its LDS-DMA
+// address), forms and stores the new rows and adds the fixed rows' share of
+// the projection; h_in gets every active row's old value there.  The walk
+// then visits the rows that are not fixed (rt.cand, ascending) in steps of
+// four; a lane takes the new value of a row that is routed for its token
+// (held from the first step) and the value as read otherwise, and adds to
+// h_in only rows that are not its token's.  With a next sublayer that routes
+// (NT == 4: its router's columns form the fourth tile) the pass also sums x'
+// for that router's LayerNorm mean: carry[cb][t][16*NT + 1].
 #include "xhc_device.h"
 #include "xhc_launch.h"
 
@@ -59,6 +72,19 @@ constexpr int MP_RPS = 4;                 // state rows per step
 constexpr int MP_WSLOT = MP_RPS * 6144;   // W' bytes per step (NT = 3)
 constexpr int CL_STRIDE = 52;             // floats per token of the LDS coefficient rows
 constexpr int MP_FULL = MIX_FULL, MP_PRE = MIX_PRE, MP_POST = MIX_POST;
+
+// LDS of the active rows' held K-step-1 fragments, which only a pass that
+// spreads the active rows' work over two steps uses (see `split`): declared
+// in that pass only, so that a pass with a fourth logit tile fits in LDS.
+template <bool ON> struct HeldFragments {
+  __device__ static unsigned char* get() { return nullptr; }
+};
+template <> struct HeldFragments<true> {
+  __device__ static unsigned char* get() {
+    __shared__ __attribute__((aligned(16))) unsigned char b[MP_RPS * 3 * 1024];
+    return b;
+  }
+};
 
 // `out` n positions back: the lane's token is r of a 16-token tile, `cur`
 // holds the tile's values and `halo` those of the 16 tokens before it.
@@ -81,25 +107,31 @@ __device__ inline V8<E> window_back(const V8<E>& cur, const V8<E>& halo) {
   return o;
 }
 
-template <typename E, int NT, int NCOMP, bool FAST, int MODE>
+template <typename E, int NT, int NCOMP, bool FAST, int MODE, int RTS = 0>
 __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     const void* __restrict__ X, const void* __restrict__ out, const float* __restrict__ w4,
     const float* __restrict__ w8, const float* __restrict__ w12, const float* __restrict__ coef,
     const void* __restrict__ Wf, void* Xnew, void* __restrict__ hin, void* __restrict__ xact,
     float* __restrict__ carry, RowOrder ro, int T, int S, int C, int N_, int k_, int in_place, int cpw,
-    int nch, int nbatch, int ZST, int proj) {
+    int nch, int nbatch, int ZST, int proj, MixRoute rt) {
+  // per-token lists: the full pass; the launcher admits them at N = 16, k = 4
+  static_assert(RTS == 0 || (MODE == MP_FULL && RTS <= 4), "per-token lists: the full pass");
   const int N = FAST ? 16 : N_;
   const int k = FAST ? 4 : k_;
+  constexpr int NFIX = 4 - RTS;              // with per-token lists: the fixed slots
   constexpr int EB = E::bytes;
   constexpr int KS = EB == 2 ? 2 : 1;        // MFMA K-steps of 32 channels per chunk
   constexpr int CW = 32 * KS;                // channels per chunk
   constexpr int FB = 512 * EB;               // bytes of one W' fragment
   constexpr int SLOTB = KS * NT * FB;        // W' bytes of one row and chunk
   constexpr int PPR = SLOTB / 1024;          // 1 KiB copies per row
-  static_assert(MP_RPS * SLOTB <= MP_WSLOT && SLOTB % 1024 == 0, "W' step slot");
-  __shared__ __attribute__((aligned(16))) unsigned char wst[2][MP_WSLOT];
-  // the active rows' K-step-1 fragments, kept from a chunk's first step to its third
-  __shared__ __attribute__((aligned(16))) unsigned char wa1[MP_RPS * 3 * 1024];
+  constexpr int WSLOT = MP_RPS * SLOTB;      // W' bytes of one step
+  static_assert(SLOTB % 1024 == 0, "W' step slot");
+  // the spreading of the active rows' work over two steps (below) holds
+  // their K-step-1 fragments from a chunk's first step to its third
+  constexpr bool SPLIT_OK = RTS == 0 && NT <= 3;
+  __shared__ __attribute__((aligned(16))) unsigned char wst[2][WSLOT];
+  unsigned char* const wa1 = HeldFragments<SPLIT_OK>::get();
   __shared__ __attribute__((aligned(16))) float cwl[24][64];
   __shared__ __attribute__((aligned(16))) float cl[MP_TOK][CL_STRIDE];
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[MP_WAVES][MP_RPS * 1024 * KS * (EB / 2)];
@@ -111,12 +143,23 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
   const int r = lane & 15, g = lane >> 4;
   const int tb = bt * MP_TOK, t0 = tb + 16 * wave, t = t0 + r;
   const int spos = (t < T ? t : 0) % S;                 // position in the sequence
-  // steps per chunk (the POST pass visits the k active rows only: one step)
-  const int nq = MODE == MP_POST ? 1 : (N + MP_RPS - 1) / MP_RPS;
+  // steps per chunk (the POST pass visits the k active rows only: one step;
+  // with per-token lists the active rows, then the rows that are not fixed)
+  const int nq = RTS ? 1 + (rt.ncand + MP_RPS - 1) / MP_RPS : MODE == MP_POST ? 1 : (N + MP_RPS - 1) / MP_RPS;
   // bf16 chunks hold two K-steps; with four steps per chunk the active rows'
   // second K-step (TFA, new rows, their projection) moves to the third step,
   // so that the arithmetic of the first step is split over two steps
-  const bool split = MODE == MP_FULL && KS == 2 && nq == 4;
+  const bool split = SPLIT_OK && MODE == MP_FULL && KS == 2 && nq == 4;
+  // with per-token lists: the token's routed rows (slots NFIX ..), read once
+  int rid[4] = {0, 0, 0, 0};
+  if constexpr (RTS > 0) {
+    const int tt = t < T ? t : T - 1;
+#pragma unroll
+    for (int a = NFIX; a < 4; ++a) {
+      const int v = rt.ids ? rt.ids[(size_t)tt * 4 + a] : __float_as_int(coef[(size_t)tt * COEF_STRIDE + CO_IDX + a]);
+      rid[a] = (unsigned)v < 16u ? v : 0;
+    }
+  }
   const int c0 = cb * cpw, c1 = min(c0 + cpw, nch);
   const int nsteps = (c1 - c0) * nq;
   const int nks = (C + 31) >> 5;                        // K-steps of the packed W'
@@ -197,6 +240,26 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     }
   };
 
+  // the state row of step q's slot j, and whether the step projects it:
+  // with per-token lists the first step projects the fixed rows only (the
+  // routed ones differ per token) and the walk the rows that are not fixed
+  auto step_row = [&](int q, int j, bool& projected) -> int {
+    if constexpr (RTS > 0) {
+      if (q == 0) {
+        projected = j < NFIX;
+        return row_of(ro, j < NFIX ? j : 0);
+      }
+      const int sl = (q - 1) * MP_RPS + j;
+      projected = sl < rt.ncand;
+      return row_of(rt.cand, sl < rt.ncand ? sl : rt.ncand - 1);
+    } else {
+      const int slot = q * MP_RPS + j;
+      // PRE projects the untouched rows only, POST the active ones only
+      projected = slot < N && (MODE == MP_FULL || (MODE == MP_PRE ? slot >= k : slot < k));
+      return row_of(ro, slot);      // rows past N repeat a valid row
+    }
+  };
+
   // W' fragments of step s's rows -> wst[s & 1][slot j][u][n]
   auto w_dma = [&](int s) {
     const int cq = s / nq, q = s - cq * nq, c = c0 + cq;
@@ -207,12 +270,11 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
       const int pc = wave + MP_WAVES * i;
       if (pc < MP_RPS * PPR) {
         const int j = pc / PPR, o = pc - j * PPR;
-        const int slot = q * MP_RPS + j;
-        // PRE projects the untouched rows only, POST the active ones only
-        const bool wanted = MODE == MP_FULL || (MODE == MP_PRE ? slot >= k : slot < k);
-        if (proj && wanted && slot < N && o * 1024 < valid_bytes) {
+        bool wanted;
+        const int wrow = step_row(q, j, wanted);
+        if (proj && wanted && o * 1024 < valid_bytes) {
           const unsigned char* src = static_cast<const unsigned char*>(Wf) +
-                                     ((size_t)row_of(ro, slot) * nks + ksb) * NT * FB + o * 1024 + lane * 16;
+                                     ((size_t)wrow * nks + ksb) * NT * FB + o * 1024 + lane * 16;
           if (split && q == 0 && j < k && o >= PPR / 2)   // K-step 1 of an active row
             __builtin_amdgcn_global_load_lds((const gbl_void_t*)src,
                                              (lds_void_t*)&wa1[j * (PPR / 2) * 1024 + (o - PPR / 2) * 1024], 16, 0, 0);
@@ -236,10 +298,20 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
 #pragma unroll
     for (int j = 0; j < MP_RPS; ++j) {
       if (MODE == MP_POST && j >= k) continue;       // untouched rows: not read by the POST pass
-      const uint32_t soff = (uint32_t)row_of(ro, q * MP_RPS + j) * rowb;    // rows past N repeat a valid row
+      bool unused;
+      uint32_t soff = (uint32_t)step_row(q, j, unused) * rowb;
+      // with per-token lists the first step's routed slots read the
+      // lane's own row: its offset goes into the lane's address
+      uint32_t vrow = 0;
+      if constexpr (RTS > 0) {
+        if (q == 0 && j >= NFIX) {
+          soff = 0;
+          vrow = (uint32_t)rid[j] * rowb;
+        }
+      }
 #pragma unroll
       for (int u = 0; u < KS; ++u) {
-        const uint32_t vo = lane_off(c, u, tokb);
+        const uint32_t vo = lane_off(c, u, tokb) + vrow;
 #pragma unroll
         for (int pp = 0; pp < PP; ++pp)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)&xbuf[wave][((j * KS + u) * PP + pp) * 1024], 16,
@@ -275,12 +347,16 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
+  float sx = 0.f;                             // sum of x' (NT == 4: for the next router's mean)
   float hacc[KS][8];
 #pragma unroll
   for (int u = 0; u < KS; ++u)
 #pragma unroll
     for (int e = 0; e < 8; ++e) hacc[u][e] = 0.f;
   const float* co = &cl[16 * wave + r][0];
+  // with per-token lists: the new values of the token's routed rows (slots
+  // NFIX ..), from a chunk's first step to the walk that projects them
+  V8<E> nvr[4][KS];
 
   // one row of the step: h_in from the old values, sum of squares and the
   // projection from `xv` (the row of the new state), K-step u
@@ -297,12 +373,17 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
       for (int d = 0; d < 4; ++d) {
         const bf16x2 p2 = __builtin_bit_cast(bf16x2, xv.w[d]);
         ss = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, ss, false);
+        if constexpr (NT == 4) {
+          const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+          sx = __builtin_amdgcn_fdot2_f32_bf16(p2, one2, sx, false);
+        }
       }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float y = xv.f(e);
         ss = fmaf(y, y, ss);
+        if constexpr (NT == 4) sx += y;
       }
     }
     if (proj && c * KS + u < nks) {
@@ -387,10 +468,21 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
       if (a < k) {
         V8<E> nv;
         __builtin_memcpy(&nv, &nvw[a][0], sizeof(nv));
-        const int row = row_of(ro, a);
-        bstore<E, 8, CP_NT>(nv, rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
         if (xact) bstore<E, 8, CP_NT>(xs[a], rxs, lane_off(c, u, xsb), (uint32_t)a * rowb);
-        row_work(wact + a * wstride, u, c, co[row], xs[a], nv, true);
+        if (RTS > 0 && a >= NFIX) {
+          // a row of the token's own: stored at the lane's row, its old value
+          // into h_in with the token's coefficient, its new value held for
+          // the walk, which projects it
+          bstore<E, 8, CP_NT>(nv, rxn, lane_off(c, u, tokb) + (uint32_t)rid[a] * rowb, 0);
+          const float hp = co[rid[a]];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hacc[u][e] = fmaf(hp, xs[a].f(e), hacc[u][e]);
+          nvr[a][u] = nv;
+        } else {
+          const int row = row_of(ro, a);
+          bstore<E, 8, CP_NT>(nv, rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
+          row_work(wact + a * wstride, u, c, co[row], xs[a], nv, true);
+        }
       }
     }
   };
@@ -444,13 +536,40 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
         if (cq + 1 < c1 - c0) load_out(c + 1);
       }
     }
+    // the walk with per-token lists: the rows that are not fixed; the
+    // token's routed rows take their held new values, and their old ones
+    // are already in h_in
+    if constexpr (RTS > 0 && !FIRST) {
+#pragma unroll
+      for (int j = 0; j < MP_RPS; ++j) {
+        const int sl = (q - 1) * MP_RPS + j;
+        if (sl < rt.ncand) {
+          const int row = row_of(rt.cand, sl);
+          bool mine = false;
+#pragma unroll
+          for (int a = NFIX; a < 4; ++a) mine |= rid[a] == row;
+          const float hp = mine ? 0.f : co[row];
+#pragma unroll
+          for (int u = 0; u < KS; ++u) {
+            V8<E> xv = x[j][u];
+#pragma unroll
+            for (int a = NFIX; a < 4; ++a) {
+              if (rid[a] == row) {
+                xv = nvr[a][u];
+              }
+            }
+            row_work(wsl + j * SLOTB + u * NT * FB, u, c, hp, x[j][u], xv, true);
+          }
+        }
+      }
+    }
     // the step's other rows (untouched by the update); the PRE pass reads the
     // active rows here too, for h_in only
 #pragma unroll
     for (int j = 0; j < MP_RPS; ++j) {
       const int slot = q * MP_RPS + j;
       const bool untouched = !FIRST || j >= k;
-      if (MODE != MP_POST && slot < N && (untouched || MODE == MP_PRE)) {
+      if (RTS == 0 && MODE != MP_POST && slot < N && (untouched || MODE == MP_PRE)) {
         const int row = row_of(ro, slot);
         const float hp = co[row];
 #pragma unroll
@@ -484,6 +603,10 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
 
   ss += shfl_xor(ss, 16);
   ss += shfl_xor(ss, 32);
+  if constexpr (NT == 4) {
+    sx += shfl_xor(sx, 16);
+    sx += shfl_xor(sx, 32);
+  }
   if (proj && t < T) {
     float* zp = carry + ((size_t)cb * T + t) * ZST;
     if constexpr (MODE == MP_POST) {
@@ -494,10 +617,12 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
         *dst = *dst + acc[n];
       }
       if (g == 0) zp[16 * NT] += ss;
+      if (NT == 4 && g == 0) zp[16 * NT + 1] += sx;
     } else {
 #pragma unroll
       for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(zp + 16 * n + 4 * g) = acc[n];
       if (g == 0) zp[16 * NT] = ss;
+      if (NT == 4 && g == 0) zp[16 * NT + 1] = sx;
     }
   }
 }
@@ -510,44 +635,75 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
 // Wf == NULL: no projection (and no carry).
 template <typename E>
 static void launch_mixproj_e(const Plan& p, const Plan& pn, int mode, const MixArgs& m, const float* coef,
-                             const void* Wf, float* carry, hipStream_t st) {
+                             const void* Wf, float* carry, hipStream_t st, const int32_t* ids) {
   RowOrder ro{0};
+  MixRoute rt{};
+  // with per-token lists the host list holds the fixed slots only (none for
+  // the caller's lists)
+  const bool per_token = p.pt && mode == MP_FULL;   // the split passes visit rows alike for every token
+  const int nfix = per_token ? (p.R ? p.nfix : 0) : p.k;
   {
     bool used[16] = {false};
     int order[16], n = 0;
-    for (int b = 0; b < p.k; ++b) { order[n++] = m.active[b]; used[m.active[b]] = true; }
+    for (int b = 0; b < nfix; ++b) { order[n++] = m.active[b]; used[m.active[b]] = true; }
+    uint64_t cbits = 0;
     for (int i = 0; i < p.N; ++i)
-      if (!used[i]) order[n++] = i;
+      if (!used[i]) {
+        cbits |= (uint64_t)i << (4 * rt.ncand++);
+        order[n++] = i;
+      }
     for (; n < 16; ++n) order[n] = order[0];
     for (int i = 0; i < 16; ++i) ro.bits |= (uint64_t)order[i] << (4 * i);
+    rt.cand = RowOrder{cbits};
+    rt.ids = per_token && !p.R ? ids : nullptr;
   }
   const int in_place = m.X_new == m.X;
   const int proj = Wf != nullptr;
   const int NT = proj ? pn.NT : 1;
   const dim3 grid(p.mp_ncb * p.mp_nbatch);
-#define XHC_MP(NTV, NC, MODE)                                                                                     \
-  k_mixproj<E, NTV, NC, false, MODE><<<grid, 64 * MP_WAVES, 0, st>>>(                                             \
+#define XHC_MP_R(NTV, NC, MODE, RTS)                                                                              \
+  k_mixproj<E, NTV, NC, false, MODE, RTS><<<grid, 64 * MP_WAVES, 0, st>>>(                                        \
       m.X, m.out, m.w4, m.w8, m.w12, coef, Wf, m.X_new, m.h_in, m.xact_save, carry, ro, p.T, p.S, p.C, p.N, p.k,   \
-      in_place, p.mp_cpw, p.mp_nch, p.mp_nbatch, pn.ZST, proj)
+      in_place, p.mp_cpw, p.mp_nch, p.mp_nbatch, pn.ZST, proj, rt)
+#define XHC_MP(NTV, NC, MODE) XHC_MP_R(NTV, NC, MODE, 0)
 #define XHC_MP_NT(NC, MODE)                                                                                       \
   do {                                                                                                           \
     if (NT == 3) XHC_MP(3, NC, MODE); else if (NT == 2) XHC_MP(2, NC, MODE); else XHC_MP(1, NC, MODE);           \
   } while (0)
-  if (mode == MP_PRE) {
+  // a fourth logit tile (the next sublayer's router) in the full pass only:
+  // the split passes are not chained with per-token lists
+  if (per_token) {
+    // per-token lists (the full pass, in place, N = 16, k = 4, so the next
+    // sublayer has at least three logit tiles): two or four slots per token
+    const int rts = 4 - nfix;
+#define XHC_MP_RT(NC)                                                                                             \
+  do {                                                                                                           \
+    if (rts == 2) {                                                                                              \
+      if (NT == 4) XHC_MP_R(4, NC, MP_FULL, 2); else XHC_MP_R(3, NC, MP_FULL, 2);                               \
+    } else {                                                                                                     \
+      if (NT == 4) XHC_MP_R(4, NC, MP_FULL, 4); else XHC_MP_R(3, NC, MP_FULL, 4);                               \
+    }                                                                                                            \
+  } while (0)
+    if (p.nc == 4) XHC_MP_RT(4); else XHC_MP_RT(1);
+#undef XHC_MP_RT
+  } else if (mode == MP_PRE) {
     XHC_MP_NT(1, MP_PRE);                  // no write-back: the component count does not matter
   } else if (mode == MP_POST) {
     if (p.nc == 4) XHC_MP_NT(4, MP_POST); else XHC_MP_NT(1, MP_POST);
+  } else if (NT == 4) {
+    if (p.nc == 4) XHC_MP(4, 4, MP_FULL); else XHC_MP(4, 1, MP_FULL);
   } else {
     if (p.nc == 4) XHC_MP_NT(4, MP_FULL); else XHC_MP_NT(1, MP_FULL);
   }
 #undef XHC_MP_NT
 #undef XHC_MP
+#undef XHC_MP_R
 }
 
 void launch_mixproj(const Plan& p, const Plan& pn, int mode, const MixArgs& m, const float* coef, const void* Wf,
-                    float* carry, hipStream_t st) {
-  if (p.dtype == XHC_BF16) launch_mixproj_e<BF16>(p, pn, mode, m, coef, Wf, carry, st);
-  else launch_mixproj_e<F32>(p, pn, mode, m, coef, Wf, carry, st);
+                    float* carry, hipStream_t st, const int32_t* ids) {
+  if (p.dtype == XHC_BF16) launch_mixproj_e<BF16>(p, pn, mode, m, coef, Wf, carry, st, ids);
+  else launch_mixproj_e<F32>(p, pn, mode, m, coef, Wf, carry, st, ids);
 }
 
 }  // namespace xhc

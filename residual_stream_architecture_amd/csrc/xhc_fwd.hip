@@ -809,11 +809,13 @@ static int forward_impl(const Plan& p, const Plan& pn, const xhc_fwd_args* a, co
     TimedLaunch tl(tm, KID_CHECK, st);
     launch_check_lists(p, a->route_idx, a->status, st);
   }
+  // the router's column sums (for its LayerNorm mean), also when the
+  // logits come carried from the previous sublayer
+  if (p.R) {
+    TimedLaunch tl(tm, KID_RCOLSUM, st);
+    launch_route_colsum(p, a->W_route, rcs, st);
+  }
   if (!carry_in) {
-    if (p.R) {
-      TimedLaunch tl(tm, KID_RCOLSUM, st);
-      launch_route_colsum(p, a->W_route, rcs, st);
-    }
     launch_pack_wt<R>(p, a->W, Wt, st, tm, p.R ? a->W_route : nullptr, ra.cand);
     launch_proj<E>(p, stream_rows(p, a->X, nullptr, a->active), Wt, zpart, st, tm);
   }
@@ -840,12 +842,15 @@ static int forward_impl(const Plan& p, const Plan& pn, const xhc_fwd_args* a, co
 #undef XHC_COEF
   }
   if (carry_out) {
-    // the next sublayer's weights in the MFMA fragment order, then the fused
-    // write pass with its projection
-    launch_pack_wt<R>(pn, ch->W_next, Wt, st, tm);
+    // the next sublayer's weights in the MFMA fragment order (with its
+    // router's candidate columns in the fourth tile, ordered by its own
+    // fixed list), then the fused write pass with its projection
+    const RowOrder cand_next =
+        pn.R ? route_args(pn, ch->active_next, nullptr, nullptr, nullptr, nullptr).cand : RowOrder{0};
+    launch_pack_wt<R>(pn, ch->W_next, Wt, st, tm, pn.R ? ch->W_route_next : nullptr, cand_next);
     TimedLaunch tl(tm, KID_MIXPROJ, st);
     const MixArgs m{a->X, a->out, a->w4, a->w8, a->w12, a->X_new, a->h_in, a->xact_save, a->active};
-    launch_mixproj(p, pn, MIX_FULL, m, coef, Wt, static_cast<float*>(ch->carry_out), st);
+    launch_mixproj(p, pn, MIX_FULL, m, coef, Wt, static_cast<float*>(ch->carry_out), st, a->route_idx);
     return hipGetLastError() == hipSuccess ? XHC_OK : XHC_ERR_HIP;
   }
   {

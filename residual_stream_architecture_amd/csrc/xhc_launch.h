@@ -89,8 +89,15 @@ struct MixArgs {
 };
 // Passes of k_mixproj: the whole write pass, its dense read only, its sparse write only.
 enum { MIX_FULL = 0, MIX_PRE = 1, MIX_POST = 2 };
+// Per-token lists in the fused pass: the rows that are not fixed (ascending)
+// and the caller's lists (NULL: the router's, from the coefficient records).
+struct MixRoute {
+  RowOrder cand;
+  int ncand;
+  const int32_t* ids;
+};
 void launch_mixproj(const Plan& p, const Plan& pn, int mode, const MixArgs& m, const float* coef, const void* Wf,
-                    float* carry, hipStream_t st);
+                    float* carry, hipStream_t st, const int32_t* ids = nullptr);
 // Split forward (xhc_forward_pre / xhc_forward_post).
 int launch_forward_pre(const Plan& p, const Plan& pn, const xhc_pre_args* a, void* ws, hipStream_t st);
 int launch_forward_post(const Plan& p, const Plan& pn, const xhc_post_args* a, void* ws, hipStream_t st);

@@ -66,6 +66,9 @@ WORKLOADS = {
     # the same stack alternating attention-side sublayers (out only) with
     # MLP-side ones (TFA), as the pages place TFA after the MLP/MoE only
     "stack48_alt": Workload("stack48_alt", 1, 8192, 7168, 16, 4, 4, "bf16", "stack", layers=48, alt=True),
+    # the same stack with the router in every sublayer: the first two streams
+    # of the rotating set fixed, two chosen per token
+    "stack48_route": Workload("stack48_route", 1, 8192, 7168, 16, 4, 4, "bf16", "stack", layers=48, route=2),
 }
 
 

@@ -57,7 +57,8 @@ class xhc_bwd_args(ctypes.Structure):
 
 class xhc_chain_args(ctypes.Structure):
     _fields_ = [("carry_in", _vp), ("W_next", _vp), ("carry_out", _vp),
-                ("desc_next", ctypes.POINTER(xhc_desc))]
+                ("desc_next", ctypes.POINTER(xhc_desc)), ("W_route_next", _vp),
+                ("active_next", ctypes.POINTER(ctypes.c_int32))]
 
 
 class xhc_pre_args(ctypes.Structure):
@@ -261,7 +262,7 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
             z_save=None, xact_save=None, iters=20, eps=1e-6, gate_mode=XHC_GATE_SIGMOID,
             workspace=None, stream=None, timer=None, desc=None, carry_in=None, W_next=None,
             carry_out=None, gram_schmidt=False, gs_eps=1e-6, desc_next=None, route=0, W_route=None,
-            b_route=None, route_idx=None, status=None):
+            b_route=None, route_idx=None, status=None, W_route_next=None, active_next=None):
     """xhc_forward on torch device tensors.  X [B*S,N,C], out [B*S,C], W [N*C,P].
 
     With carry_in, W_next or carry_out given, calls xhc_forward_chain: carry_in
@@ -276,7 +277,9 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
     With desc.per_token_active = 1 (make_desc(..., per_token_active=True))
     route_idx instead holds the caller's per-token lists, and active is not read;
     status (int32 [2] on the device, zeroed by the caller) then receives the
-    XHC_STATUS_* flags and the count of tokens whose list is bad."""
+    XHC_STATUS_* flags and the count of tokens whose list is bad.
+    In a chain whose next sublayer has a router, W_route_next [N*C,N] and
+    active_next (its host active list) give that router's columns."""
     T, N, C = X.shape
     ncomp = 4 if w4 is not None else 1
     if desc is None:
@@ -294,8 +297,10 @@ def forward(X, out, W, active, X_new, h_in, *, B, S, w4=None, w8=None, w12=None,
         if rc:
             raise XhcError(rc, "xhc_forward")
         return
+    act_next = _active_array(active_next) if active_next is not None else None
     chain = xhc_chain_args(_ptr(carry_in), _ptr(W_next), _ptr(carry_out),
-                           None if desc_next is None else ctypes.pointer(desc_next))
+                           None if desc_next is None else ctypes.pointer(desc_next), _ptr(W_route_next),
+                           None if act_next is None else ctypes.cast(act_next, ctypes.POINTER(ctypes.c_int32)))
     rc = lib.xhc_forward_chain(ctypes.byref(desc), ctypes.byref(args), ctypes.byref(chain), ws.data_ptr(),
                                ws.numel(), _stream_handle(stream))
     if rc:

@@ -362,14 +362,48 @@ def test_route_backward_error_paths():
     assert xhc.validate(d, a, xhc.XHC_PHASE_BWD) == xhc.XHC_ERR_ALIAS
 
 
-def test_route_not_chained():
+def test_route_chain_validation():
+    W, NUL, UNS, WS = xhc.XHC_OK, xhc.XHC_ERR_NULL, xhc.XHC_ERR_UNSUPPORTED, xhc.XHC_ERR_WORKSPACE
+    nxt = (ctypes.c_int32 * 4)(4, 9, 0, 0)
+    nxt_p = ctypes.cast(nxt, ctypes.POINTER(ctypes.c_int32))
     d = desc16(route=2)
+    # out of place: the routed pass rewrites each token's own rows in place only
     a, _ = routed_fwd(d)
-    c = xhc.xhc_chain_args(None, fake(30), fake(31), None)
-    assert chain_call(d, a, c) == xhc.XHC_ERR_UNSUPPORTED
-    a, _ = good_fwd(desc16(), inplace=False)
-    c = xhc.xhc_chain_args(None, fake(30), fake(31), ctypes.pointer(desc16(route=2)))
-    assert chain_call(desc16(), a, c) == xhc.XHC_ERR_UNSUPPORTED
+    c = xhc.xhc_chain_args(None, fake(30), fake(31), None, fake(32), nxt_p)
+    assert chain_call(d, a, c) == UNS
+    a.X_new = a.X
+    # a valid routed chain passes validation and stops at the missing workspace
+    assert chain_call(d, a, c) == WS
+    c.W_route_next = None                            # the next router's columns are required
+    assert chain_call(d, a, c) == NUL
+    c.W_route_next = fake(32)
+    c.active_next = None                             # and its fixed streams
+    assert chain_call(d, a, c) == NUL
+    dup = (ctypes.c_int32 * 4)(3, 3, 0, 0)
+    c.active_next = ctypes.cast(dup, ctypes.POINTER(ctypes.c_int32))
+    assert chain_call(d, a, c) == xhc.XHC_ERR_INDEX
+    c.active_next = nxt_p
+    c.W_route_next = a.X_new + 64                    # an input overlapping an output
+    assert chain_call(d, a, c) == xhc.XHC_ERR_ALIAS
+    # two or four per-token slots at N = 16, k = 4 only
+    for kw in (dict(route=1), dict(route=3), dict(route=2, N=12)):
+        dd = desc16(**kw)
+        a, _ = routed_fwd(dd)
+        a.X_new = a.X
+        c = xhc.xhc_chain_args(None, fake(30), fake(31), None, fake(32), nxt_p)
+        assert chain_call(dd, a, c) == UNS, kw
+    # a fixed-list sublayer whose next sublayer routes
+    a, _ = good_fwd(desc16())
+    c = xhc.xhc_chain_args(None, fake(30), fake(31), ctypes.pointer(desc16(route=2)), None, nxt_p)
+    assert chain_call(desc16(), a, c) == NUL
+    c.W_route_next = fake(32)
+    assert chain_call(desc16(), a, c) == WS
+    # given lists chain too (four per-token slots)
+    dg = desc16(per_token_active=True)
+    a, _ = good_fwd(dg)
+    a.route_idx = fake(22)
+    c = xhc.xhc_chain_args(None, fake(30), fake(31), None, None, None)
+    assert chain_call(dg, a, c) == WS
 
 
 def test_route_kernel_names():
