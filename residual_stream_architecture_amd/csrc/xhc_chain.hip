@@ -73,18 +73,6 @@ constexpr int MP_WSLOT = MP_RPS * 6144;   // W' bytes per step (NT = 3)
 constexpr int CL_STRIDE = 52;             // floats per token of the LDS coefficient rows
 constexpr int MP_FULL = MIX_FULL, MP_PRE = MIX_PRE, MP_POST = MIX_POST;
 
-// LDS of the active rows' held K-step-1 fragments, which only a pass that
-// spreads the active rows' work over two steps uses (see `split`): declared
-// in that pass only, so that a pass with a fourth logit tile fits in LDS.
-template <bool ON> struct HeldFragments {
-  __device__ static unsigned char* get() { return nullptr; }
-};
-template <> struct HeldFragments<true> {
-  __device__ static unsigned char* get() {
-    __shared__ __attribute__((aligned(16))) unsigned char b[MP_RPS * 3 * 1024];
-    return b;
-  }
-};
 
 // `out` n positions back: the lane's token is r of a 16-token tile, `cur`
 // holds the tile's values and `halo` those of the 16 tokens before it.
@@ -130,8 +118,13 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
   // the spreading of the active rows' work over two steps (below) holds
   // their K-step-1 fragments from a chunk's first step to its third
   constexpr bool SPLIT_OK = RTS == 0 && NT <= 3;
-  __shared__ __attribute__((aligned(16))) unsigned char wst[2][WSLOT];
-  unsigned char* const wa1 = HeldFragments<SPLIT_OK>::get();
+  // the W' ring, then (only in a pass that spreads the active rows' work)
+  // the active rows' held K-step-1 fragments: a pass with a fourth logit
+  // tile has no room for them in LDS
+  constexpr int HELD = SPLIT_OK ? MP_RPS * 3 * 1024 : 0;
+  __shared__ __attribute__((aligned(16))) unsigned char wbuf[2 * WSLOT + HELD];
+  unsigned char (*const wst)[WSLOT] = reinterpret_cast<unsigned char (*)[WSLOT]>(wbuf);
+  unsigned char* const wa1 = wbuf + 2 * WSLOT;
   __shared__ __attribute__((aligned(16))) float cwl[24][64];
   __shared__ __attribute__((aligned(16))) float cl[MP_TOK][CL_STRIDE];
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[MP_WAVES][MP_RPS * 1024 * KS * (EB / 2)];
@@ -271,7 +264,15 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
       if (pc < MP_RPS * PPR) {
         const int j = pc / PPR, o = pc - j * PPR;
         bool wanted;
-        const int wrow = step_row(q, j, wanted);
+        int wrow;
+        if constexpr (RTS > 0) {
+          wrow = step_row(q, j, wanted);
+        } else {
+          const int slot = q * MP_RPS + j;
+          // PRE projects the untouched rows only, POST the active ones only
+          wanted = slot < N && (MODE == MP_FULL || (MODE == MP_PRE ? slot >= k : slot < k));
+          wrow = row_of(ro, slot);
+        }
         if (proj && wanted && o * 1024 < valid_bytes) {
           const unsigned char* src = static_cast<const unsigned char*>(Wf) +
                                      ((size_t)wrow * nks + ksb) * NT * FB + o * 1024 + lane * 16;
@@ -298,8 +299,11 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
 #pragma unroll
     for (int j = 0; j < MP_RPS; ++j) {
       if (MODE == MP_POST && j >= k) continue;       // untouched rows: not read by the POST pass
-      bool unused;
-      uint32_t soff = (uint32_t)step_row(q, j, unused) * rowb;
+      uint32_t soff = (uint32_t)row_of(ro, q * MP_RPS + j) * rowb;    // rows past N repeat a valid row
+      if constexpr (RTS > 0) {
+        bool unused;
+        soff = (uint32_t)step_row(q, j, unused) * rowb;
+      }
       // with per-token lists the first step's routed slots read the
       // lane's own row: its offset goes into the lane's address
       uint32_t vrow = 0;
@@ -468,12 +472,12 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
       if (a < k) {
         V8<E> nv;
         __builtin_memcpy(&nv, &nvw[a][0], sizeof(nv));
-        if (xact) bstore<E, 8, CP_NT>(xs[a], rxs, lane_off(c, u, xsb), (uint32_t)a * rowb);
         if (RTS > 0 && a >= NFIX) {
           // a row of the token's own: stored at the lane's row, its old value
           // into h_in with the token's coefficient, its new value held for
           // the walk, which projects it
           bstore<E, 8, CP_NT>(nv, rxn, lane_off(c, u, tokb) + (uint32_t)rid[a] * rowb, 0);
+          if (xact) bstore<E, 8, CP_NT>(xs[a], rxs, lane_off(c, u, xsb), (uint32_t)a * rowb);
           const float hp = co[rid[a]];
 #pragma unroll
           for (int e = 0; e < 8; ++e) hacc[u][e] = fmaf(hp, xs[a].f(e), hacc[u][e]);
@@ -481,6 +485,7 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
         } else {
           const int row = row_of(ro, a);
           bstore<E, 8, CP_NT>(nv, rxn, lane_off(c, u, tokb), (uint32_t)row * rowb);
+          if (xact) bstore<E, 8, CP_NT>(xs[a], rxs, lane_off(c, u, xsb), (uint32_t)a * rowb);
           row_work(wact + a * wstride, u, c, co[row], xs[a], nv, true);
         }
       }
