@@ -69,10 +69,8 @@ namespace xhc {
 constexpr int MP_WAVES = 8;
 constexpr int MP_TOK = 16 * MP_WAVES;     // tokens per workgroup
 constexpr int MP_RPS = 4;                 // state rows per step
-constexpr int MP_WSLOT = MP_RPS * 6144;   // W' bytes per step (NT = 3)
 constexpr int CL_STRIDE = 52;             // floats per token of the LDS coefficient rows
 constexpr int MP_FULL = MIX_FULL, MP_PRE = MIX_PRE, MP_POST = MIX_POST;
-
 
 // `out` n positions back: the lane's token is r of a 16-token tile, `cur`
 // holds the tile's values and `halo` those of the 16 tokens before it.
@@ -233,24 +231,17 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
     }
   };
 
-  // the state row of step q's slot j, and whether the step projects it:
-  // with per-token lists the first step projects the fixed rows only (the
-  // routed ones differ per token) and the walk the rows that are not fixed
+  // with per-token lists: the state row of step q's slot j, and whether the
+  // step projects it -- the first step the fixed rows only (the routed ones
+  // differ per token), the walk the rows that are not fixed
   auto step_row = [&](int q, int j, bool& projected) -> int {
-    if constexpr (RTS > 0) {
-      if (q == 0) {
-        projected = j < NFIX;
-        return row_of(ro, j < NFIX ? j : 0);
-      }
-      const int sl = (q - 1) * MP_RPS + j;
-      projected = sl < rt.ncand;
-      return row_of(rt.cand, sl < rt.ncand ? sl : rt.ncand - 1);
-    } else {
-      const int slot = q * MP_RPS + j;
-      // PRE projects the untouched rows only, POST the active ones only
-      projected = slot < N && (MODE == MP_FULL || (MODE == MP_PRE ? slot >= k : slot < k));
-      return row_of(ro, slot);      // rows past N repeat a valid row
+    if (q == 0) {
+      projected = j < NFIX;
+      return row_of(ro, j < NFIX ? j : 0);
     }
+    const int sl = (q - 1) * MP_RPS + j;
+    projected = sl < rt.ncand;
+    return row_of(rt.cand, sl < rt.ncand ? sl : rt.ncand - 1);
   };
 
   // W' fragments of step s's rows -> wst[s & 1][slot j][u][n]
