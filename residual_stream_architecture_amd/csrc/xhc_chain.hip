@@ -290,6 +290,9 @@ __global__ __launch_bounds__(64 * MP_WAVES) void k_mixproj(
 #pragma unroll
     for (int j = 0; j < MP_RPS; ++j) {
       if (MODE == MP_POST && j >= k) continue;       // untouched rows: not read by the POST pass
+      // with per-token lists the walk's last step may hold fewer rows than
+      // slots: the empty slots are neither loaded nor read
+      if (RTS > 0 && q > 0 && (q - 1) * MP_RPS + j >= rt.ncand) continue;
       uint32_t soff = (uint32_t)row_of(ro, q * MP_RPS + j) * rowb;    // rows past N repeat a valid row
       if constexpr (RTS > 0) {
         bool unused;
