@@ -41,14 +41,19 @@ CASES = [
     # the stack's channel count (112 chunks of 64 channels in 16 blocks)
     ("stack_c7168_bf16", W_("c", 1, 160, 7168, 16, 4, 4, "bf16", "fwd", route=2),
      [(2, [0, 1]), (2, [4, 5]), (2, [8, 9]), (2, [12, 13])]),
+    # Gram-Schmidt over the components in every sublayer
+    ("gram_schmidt_bf16", W_("c", 2, 45, 136, 16, 4, 4, "bf16", "fwd", route=2, gs=True),
+     [(2, [3, 7]), ("given", []), (2, [6, 12])]),
 ]
 
 
 def layer_desc(w, kind):
     dt = xhc.XHC_BF16 if w.dtype == "bf16" else xhc.XHC_F32
     if kind == "given":
-        return xhc.make_desc(w.B, w.S, w.C, w.N, w.k, w.ncomp, dt, w.iters, w.eps, per_token_active=True)
-    return xhc.make_desc(w.B, w.S, w.C, w.N, w.k, w.ncomp, dt, w.iters, w.eps, route=kind)
+        return xhc.make_desc(w.B, w.S, w.C, w.N, w.k, w.ncomp, dt, w.iters, w.eps, per_token_active=True,
+                             gram_schmidt=w.gs, gs_eps=GS_EPS)
+    return xhc.make_desc(w.B, w.S, w.C, w.N, w.k, w.ncomp, dt, w.iters, w.eps, route=kind, gram_schmidt=w.gs,
+                         gs_eps=GS_EPS)
 
 
 def layer_inputs(w, l):
@@ -106,7 +111,7 @@ def test_chained_routed_stack(name, w, layers):
         # the oracle from the GPU's state before the sublayer
         h = host[l]
         convs = (h["w4"], h["w8"], h["w12"])
-        base = dict(B=w.B, S=w.S, iters=w.iters, eps=w.eps)
+        base = dict(B=w.B, S=w.S, iters=w.iters, eps=w.eps, gram_schmidt_on=w.gs, gs_eps=GS_EPS)
         if kind == "given":
             idx = given[l].astype(np.int64)
             ref = xo.forward(x_before, h["out"], h["W"], h["bias"], [0] * k, convs, active_tok=idx, **base)
